@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""SSD forward throughput on one MI355X, with the dominant kernel's roofline position
+and the fp64 oracle timed on the host cores beside it.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mamba2_2p7b]
+
+One step is one pass of the whole forward (chunk_cumsum -> chunk_state -> state_passing
+-> chunk_scan) over one batch of synthetic inputs already resident in HBM.  Inside the
+timed region each kernel is bracketed by HIP events on the stream it runs on, which
+gives every kernel's average duration; the step time itself comes from the host clock
+between two device synchronisations.  Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SSD fwd tokens/sec on 1 MI355X; MFMA util % and HBM GB/s vs peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mamba2_2p7b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="rough budget for the oracle CPU baseline")
+    return ap.parse_args()
+
+
+def host_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def cpu_baseline(w, inputs, budget_s):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the same workload:
+    the first batch element, as many heads as fit the time budget (whole sequences).
+    Tokens/s is scaled to the metric's unit: heads/H of a token per (step, head)."""
+    import numpy as np
+    import oracle
+    from mamba_ssd_chunked_03_amd.workloads import head_slice
+
+    nthreads = host_threads()
+
+    def sample(nh):
+        g_of = [h // (w.nheads // w.ngroups) for h in range(nh)]
+        sl = [head_slice(inputs, w, 0, h) for h in range(nh)]
+        cat = lambda k, ax: np.concatenate([s[k].double().numpy() for s in sl], axis=ax)
+        x, dt, A, D = cat("x", 2), cat("dt", 2), cat("A", 0), cat("D", 0)
+        B = np.concatenate([inputs["B"][0:1, :, g:g + 1].double().numpy() for g in g_of], axis=2)
+        C = np.concatenate([inputs["C"][0:1, :, g:g + 1].double().numpy() for g in g_of], axis=2)
+        init = None
+        if inputs["init_state"] is not None:
+            init = inputs["init_state"][0:1, :nh].double().numpy()
+        return dict(x=x, dt=dt, A=A, B=B, C=C, D=D, init_state=init)
+
+    # probe with one head per thread to size the sample, then time the sample
+    nh = min(w.nheads, nthreads)
+    s = sample(nh)
+    t0 = time.perf_counter()
+    oracle.ssd_ref(**s, nthreads=nthreads)
+    probe = time.perf_counter() - t0
+    rounds = max(1, int(budget_s / max(probe, 1e-3)))
+    nh = min(w.nheads, nh * rounds)
+    s = sample(nh)
+    used = oracle.threads_used(1, nh, nthreads)
+    t0 = time.perf_counter()
+    oracle.ssd_ref(**s, nthreads=nthreads)
+    el = time.perf_counter() - t0
+    tokens = w.seqlen * nh / w.nheads
+    return {"value": tokens / el, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"batch element 0 of {w.batch}, heads 0..{nh - 1} of {w.nheads}, "
+                      f"full T={w.seqlen} (fp64 token recurrence, {el:.2f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each GPU would run its own shard; see DESIGN.md). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mamba_ssd_chunked_03_amd import binding, roofline
+    from mamba_ssd_chunked_03_amd.workloads import WORKLOADS, generate
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"[bench] {w.describe()}: generating inputs")
+    cpu_inputs = generate(w)
+    d_in = {k: (None if v is None else v.to(dev)) for k, v in cpu_inputs.items()}
+    dims = binding.SsdDims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups)
+    Q = w.chunk_len
+    ws = torch.empty(binding.ssd_fwd_workspace_size(dims, Q), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(d_in["x"])
+    fin = torch.empty((w.batch, w.nheads, w.dstate, w.headdim), dtype=torch.float32, device=dev)
+
+    # the stage buffers inside the workspace, exactly as ssd_fwd lays them out
+    nC = w.nchunks
+    f32 = torch.float32
+    chunk_n = w.batch * w.nheads * nC * Q
+    state_n = w.batch * w.nheads * nC * w.headdim * w.dstate
+    rnd = lambda b: (b + 255) // 256 * 256
+    offs = [0]
+    for nbytes in (chunk_n * 4, chunk_n * 4, state_n * 4):
+        offs.append(offs[-1] + rnd(nbytes))
+    view = lambda off, n, shape: ws[off:off + n * 4].view(f32).view(shape)
+    cshape = (w.batch, w.nheads, nC, Q)
+    sshape = (w.batch, w.nheads, nC, w.headdim, w.dstate)
+    dtc, cs = view(offs[0], chunk_n, cshape), view(offs[1], chunk_n, cshape)
+    S, E = view(offs[2], state_n, sshape), view(offs[3], state_n, sshape)
+
+    def fwd():
+        binding.ssd_fwd(d_in["x"], d_in["dt"], d_in["A"], d_in["B"], d_in["C"], d_in["D"], Q,
+                        init_state=d_in["init_state"], y=y, final_state=fin, workspace=ws)
+
+    def staged(ev):
+        ev[0].record()
+        binding.ssd_chunk_cumsum(dims, Q, d_in["dt"], d_in["A"], dtc, cs)
+        ev[1].record()
+        binding.ssd_chunk_state(dims, Q, d_in["x"], d_in["B"], dtc, cs, S)
+        ev[2].record()
+        binding.ssd_state_passing(dims, Q, S, cs, init_state=d_in["init_state"],
+                                  entry_states=E, final_state=fin)
+        ev[3].record()
+        binding.ssd_chunk_scan(dims, Q, d_in["x"], d_in["B"], d_in["C"], dtc, cs, d_in["D"], E, y=y)
+        ev[4].record()
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    y_ref = y.clone()
+    ev_steps = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        staged(ev_steps[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    if not torch.equal(y, y_ref):
+        log("[bench] WARNING: staged calls and ssd_fwd differ")
+    if not torch.isfinite(y.float()).all():
+        log("[bench] WARNING: non-finite output")
+
+    names = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_scan"]
+    per = {n: 0.0 for n in names}
+    for ev in ev_steps:
+        for i, n in enumerate(names):
+            per[n] += ev[i].elapsed_time(ev[i + 1]) / args.steps   # ms
+    costs = {c.name: c for c in roofline.kernel_costs(
+        w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, Q, w.dtype,
+        init_state=w.init_state, final_state=True)}
+    kernels = {}
+    for n in names:
+        t = per[n] * 1e-3
+        c = costs[n]
+        gbs = c.bytes / t / 1e9
+        tfl = c.flops / t / 1e12
+        kernels[n] = {"avg_us": round(per[n] * 1e3, 2), "alg_bytes": int(c.bytes),
+                      "alg_flops": int(c.flops), "hbm_GBps": round(gbs, 1),
+                      "hbm_frac": round(gbs / roofline.PEAK_HBM_GBPS, 4),
+                      "mfma_TFLOPs": round(tfl, 2),
+                      "mfma_frac": round(tfl / roofline.PEAK_MFMA_TFLOPS["bf16"], 4)}
+    dom = max(names, key=lambda n: per[n])
+    dk = kernels[dom]
+    roof = {"bound": "hbm", "kernel": dom, "achieved": dk["hbm_GBps"],
+            "peak": roofline.PEAK_HBM_GBPS, "unit": "GB/s", "frac": dk["hbm_frac"],
+            "traffic": None}
+
+    ms_step = elapsed / args.steps * 1e3
+    tokens_per_s = w.tokens * args.steps / elapsed
+    result = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen,
+                   "nheads": w.nheads, "headdim": w.headdim, "dstate": w.dstate,
+                   "ngroups": w.ngroups, "chunk_len": Q, "input_dtype": w.dtype,
+                   "init_state": w.init_state, "parallelism": "single_gpu"},
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (fp64 oracle)")
+        result["cpu_baseline"] = cpu_baseline(w, cpu_inputs, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

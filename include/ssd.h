@@ -1,0 +1,148 @@
+/*
+ * ssd.h -- libssd: the Mamba-2 SSD (state space dual) layer forward on AMD MI355X (gfx950).
+ *
+ * The operation ("Mamba-2: Attention's Distant Cousin", docsaid.org, sections "Writing an
+ * SSM as a Matrix" and "Reducing A to a Single Number"; structured summary of arXiv
+ * 2405.21060, section "The SSD Layer: Formal Definition"): for every batch element b and
+ * head h, a scalar-decay selective SSM with an N x P state S,
+ *
+ *     S_t = exp(dt[b,t,h] * A[h]) * S_{t-1} + dt[b,t,h] * B[b,t,g] x[b,t,h]^T
+ *     y[b,t,h] = C[b,t,g]^T S_t + D[h] * x[b,t,h]
+ *
+ * where g = h / (H / G) is the B/C group of head h (heads share B and C within a group,
+ * summary section "The Mamba-2 Architecture", head patterns) and S_{-1} is init_state.
+ * Equivalently y = M x per head with M = L o (C B^T), L the 1-semiseparable decay mask.
+ *
+ * It is computed by the block decomposition of M into chunks of chunk_len steps
+ * (summary section "The Block-Decomposition SSD Algorithm", stages 0 to 5), as four
+ * kernels that ssd_fwd runs in order on one stream, each also exported on its own:
+ *   ssd_chunk_cumsum   stage 0: chunk-local inclusive prefix sums of dt*A (log decays)
+ *   ssd_chunk_state    stage 2: every chunk's final state from a zero start
+ *   ssd_state_passing  stage 3: the 1-SS scan over chunks that carries states across them
+ *   ssd_chunk_scan     stages 1, 4, 5: the masked quadratic form inside each chunk plus
+ *                      the carried state read out by C, plus the D skip
+ *
+ * Conventions for every entry point
+ *   - Pointers are device pointers (hipMalloc'd or equivalent), row-major and
+ *     contiguous.  x, B, C, y, dt_chunk, cs, the state buffers and the workspace must be
+ *     16-byte aligned; dt, A, D, init_state and final_state 4-byte aligned (else
+ *     SSD_ERR_ALIGN).  The caller owns every buffer.  The
+ *     library allocates nothing and keeps no state between calls, so calls on different
+ *     streams are independent; calls that share output or workspace buffers race.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.  Work is
+ *     enqueued asynchronously; a return of SSD_OK means "enqueued".
+ *   - Arguments are validated before any launch; on an error nothing is enqueued.
+ *   - Values are not checked: dt >= 0 and A <= 0 (so every decay lies in (0, 1]) are the
+ *     caller's contract.  Other values still give the same arithmetic, but a positive
+ *     dt*A sum inside a chunk can overflow exp.
+ *   - Supported sizes: chunk_len in {64, 128, 256}; dstate N in {16, 32, 64, 128, 256};
+ *     headdim P in {16, 32, 64, 128}; ngroups G >= 1 dividing nheads H; any seqlen
+ *     T >= 0 (the last chunk may be partial); batch >= 0; B*T*H*P < 2^31 elements per
+ *     tensor.  dtype SSD_F32 or SSD_BF16 for x, B, C and y; dt, A, D and the states are
+ *     always fp32.
+ *
+ * Tensor layouts
+ *   x, y           [batch][seqlen][nheads][headdim]       in `dtype`
+ *   dt             [batch][seqlen][nheads]                fp32
+ *   A, D           [nheads]                               fp32
+ *   B, C           [batch][seqlen][ngroups][dstate]       in `dtype`
+ *   init_state, final_state  [batch][nheads][dstate][headdim]   fp32
+ *   dt_chunk, cs   [batch][nheads][nchunks][chunk_len]    fp32, nchunks = ceil(T/chunk_len)
+ *   chunk states, entry states  [batch][nheads][nchunks][headdim][dstate]   fp32
+ *     (note: headdim-major, the transpose of the N x P state of the formulas)
+ */
+#ifndef LIBSSD_SSD_H
+#define LIBSSD_SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL = 1,        /* a required pointer is NULL */
+    SSD_ERR_DIMS = 2,        /* a size is negative, zero where it must not be, too large,
+                                or nheads is not a multiple of ngroups */
+    SSD_ERR_UNSUPPORTED = 3, /* chunk_len, dstate, headdim or dtype outside the supported set */
+    SSD_ERR_ALIGN = 4,       /* a pointer is not aligned as the conventions require */
+    SSD_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than ssd_fwd_workspace_size() */
+    SSD_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+} ssd_status;
+
+typedef struct {
+    int64_t batch;   /* B */
+    int64_t seqlen;  /* T */
+    int64_t nheads;  /* H */
+    int64_t headdim; /* P */
+    int64_t dstate;  /* N */
+    int64_t ngroups; /* G */
+} ssd_dims;
+
+/* Human-readable name of a status code (a static string; never NULL). */
+const char* ssd_status_string(ssd_status status);
+
+/* Bytes of device workspace ssd_fwd needs for these sizes (0 if the sizes are invalid).
+ * It holds dt_chunk, cs, the chunk states and the entry states, each 256-byte aligned. */
+size_t ssd_fwd_workspace_size(const ssd_dims* dims, int chunk_len);
+
+/* The whole SSD forward: y and (optionally) final_state from x, dt, A, B, C, D and an
+ * optional init_state.  Runs the four stage kernels below on `stream`.
+ *   init_state   NULL for a zero initial state
+ *   final_state  NULL to skip writing the state after the last step
+ *   workspace    device buffer of at least ssd_fwd_workspace_size(dims, chunk_len) bytes;
+ *                its contents on return are the stage intermediates (see the stage calls)
+ * Errors: SSD_ERR_NULL, SSD_ERR_DIMS, SSD_ERR_UNSUPPORTED, SSD_ERR_ALIGN,
+ * SSD_ERR_WORKSPACE before any launch; SSD_ERR_HIP if a launch fails. */
+ssd_status ssd_fwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const float* dt,
+                   const float* A, const void* B, const void* C, const float* D,
+                   int chunk_len, const float* init_state, void* y, float* final_state,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage 0 (summary section "The Block-Decomposition SSD Algorithm", step 0, and the log
+ * form of the 1-SS mask entries a_j ... a_{i+1}): for every (b, h, chunk c) and
+ * position i < chunk_len, with t = c*chunk_len + i,
+ *     dt_chunk[b][h][c][i] = dt[b][t][h]                (0 when t >= T)
+ *     cs[b][h][c][i]       = sum_{k <= i} dt_chunk[b][h][c][k] * A[h]
+ * so positions past a partial last chunk repeat the chunk's last prefix sum. */
+ssd_status ssd_chunk_cumsum(const ssd_dims* dims, int chunk_len, const float* dt,
+                            const float* A, float* dt_chunk, float* cs, void* stream);
+
+/* Stage 2 (same section, "Compute chunk-final states"): the state at the end of every
+ * chunk when the chunk starts from zero, i.e. from the chunk's own inputs only:
+ *     states[b][h][c][p][n] = sum_i exp(cs[c][Q-1] - cs[c][i]) * dt_chunk[c][i]
+ *                                   * B[b][cQ+i][g][n] * x[b][cQ+i][h][p]
+ * (sum over the chunk's valid positions i).  dt_chunk and cs come from ssd_chunk_cumsum. */
+ssd_status ssd_chunk_state(const ssd_dims* dims, ssd_dtype dtype, int chunk_len,
+                           const void* x, const void* B, const float* dt_chunk,
+                           const float* cs, float* states, void* stream);
+
+/* Stage 3 (same section, "Propagate states between chunks"): the sequential 1-SS scan
+ * over chunks.  With E_0 = init_state (zeros if NULL),
+ *     entry_states[c] = E_c,   E_{c+1} = exp(cs[c][Q-1]) * E_c + states[c]
+ * and final_state = E_nchunks (the state after the last step; NULL to skip).
+ * entry_states may not alias states (SSD_ERR_DIMS).  init_state/final_state use the
+ * [N][P] layout, states/entry_states the [P][N] one. */
+ssd_status ssd_state_passing(const ssd_dims* dims, int chunk_len, const float* states,
+                             const float* cs, const float* init_state, float* entry_states,
+                             float* final_state, void* stream);
+
+/* Stages 1, 4 and 5 (same section: intra-chunk outputs, inter-chunk outputs, combine):
+ * for every position j of chunk c (t = cQ + j < T),
+ *     y[b][t][h][p] = sum_{i <= j} (C_j . B_i) exp(cs[j] - cs[i]) dt_chunk[i] x[cQ+i][p]
+ *                   + exp(cs[j]) sum_n C_j[n] entry_states[c][p][n]
+ *                   + D[h] x[b][t][h][p]
+ * with C_j = C[b][cQ+j][g], B_i = B[b][cQ+i][g]. */
+ssd_status ssd_chunk_scan(const ssd_dims* dims, ssd_dtype dtype, int chunk_len,
+                          const void* x, const void* B, const void* C, const float* dt_chunk,
+                          const float* cs, const float* D, const float* entry_states, void* y,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBSSD_SSD_H */

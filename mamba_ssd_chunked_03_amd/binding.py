@@ -1,0 +1,192 @@
+"""ctypes binding for libssd.so (include/ssd.h), with the same entry point names.
+
+Argument marshalling only: shapes are read off the tensors, output tensors are
+allocated with torch when the caller passes none, and device pointers plus the current
+HIP stream go to the C ABI.  Every step of the computation runs in libssd's kernels;
+there is no fallback of any kind: if libssd.so is missing the first call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd.so")
+
+SSD_F32, SSD_BF16 = 0, 1
+_DTYPE_CODE = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}
+EXPORTED = ("ssd_status_string", "ssd_fwd_workspace_size", "ssd_fwd", "ssd_chunk_cumsum",
+            "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan")
+
+
+class SsdDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64)]
+
+    def tuple(self):
+        return (self.batch, self.seqlen, self.nheads, self.headdim, self.dstate, self.ngroups)
+
+
+class SsdError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(msg)
+        self.code = code
+
+
+_LIB = None
+
+
+def library(path=LIB_PATH):
+    """Load libssd.so (once).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None and path == LIB_PATH:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m mamba_ssd_chunked_03_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    vp, fp, i, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    dims = ctypes.POINTER(SsdDims)
+    lib.ssd_status_string.restype = ctypes.c_char_p
+    lib.ssd_status_string.argtypes = [i]
+    lib.ssd_fwd_workspace_size.restype = sz
+    lib.ssd_fwd_workspace_size.argtypes = [dims, i]
+    lib.ssd_fwd.restype = i
+    lib.ssd_fwd.argtypes = [dims, i, vp, fp, fp, vp, vp, fp, i, fp, vp, fp, vp, sz, vp]
+    lib.ssd_chunk_cumsum.restype = i
+    lib.ssd_chunk_cumsum.argtypes = [dims, i, fp, fp, fp, fp, vp]
+    lib.ssd_chunk_state.restype = i
+    lib.ssd_chunk_state.argtypes = [dims, i, i, vp, vp, fp, fp, fp, vp]
+    lib.ssd_state_passing.restype = i
+    lib.ssd_state_passing.argtypes = [dims, i, fp, fp, fp, fp, fp, vp]
+    lib.ssd_chunk_scan.restype = i
+    lib.ssd_chunk_scan.argtypes = [dims, i, i, vp, vp, vp, fp, fp, fp, fp, vp, vp]
+    if path == LIB_PATH:
+        _LIB = lib
+    return lib
+
+
+def status_string(code):
+    return library().ssd_status_string(int(code)).decode()
+
+
+def _check(code):
+    if code != 0:
+        raise SsdError(code, status_string(code))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def dims_of(x, B):
+    b, t, h, p = x.shape
+    return SsdDims(b, t, h, p, B.shape[3], B.shape[2])
+
+
+def nchunks(seqlen, chunk_len):
+    return (seqlen + chunk_len - 1) // chunk_len
+
+
+def _need(t, name, dtype=None, device=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def ssd_fwd_workspace_size(dims, chunk_len):
+    return int(library().ssd_fwd_workspace_size(ctypes.byref(dims), int(chunk_len)))
+
+
+def ssd_fwd(x, dt, A, B, C, D, chunk_len, init_state=None, y=None, final_state=None,
+            workspace=None, want_final=True, stream=None):
+    """y, final_state = SSD(x, dt, A, B, C, D) on the GPU through libssd.ssd_fwd.
+
+    x [B,T,H,P] and B/C [B,T,G,N] in fp32 or bf16; dt [B,T,H], A [H], D [H] fp32;
+    init_state [B,H,N,P] fp32 or None.  Returns (y, final_state or None)."""
+    dev = x.device
+    f32 = torch.float32
+    _need(x, "x", device=dev)
+    code = _DTYPE_CODE.get(x.dtype)
+    if code is None:
+        raise TypeError(f"x must be fp32 or bf16, got {x.dtype}")
+    for t, n in ((B, "B"), (C, "C")):
+        _need(t, n, x.dtype, dev)
+    for t, n in ((dt, "dt"), (A, "A"), (D, "D")):
+        _need(t, n, f32, dev)
+    if init_state is not None:
+        _need(init_state, "init_state", f32, dev)
+    d = dims_of(x, B)
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", x.dtype, dev)
+    if final_state is None and want_final:
+        final_state = torch.empty((d.batch, d.nheads, d.dstate, d.headdim), dtype=f32, device=dev)
+    if workspace is None:
+        ws = ssd_fwd_workspace_size(d, chunk_len)
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+    _check(library().ssd_fwd(ctypes.byref(d), code, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                             _ptr(D), int(chunk_len), _ptr(init_state), _ptr(y),
+                             _ptr(final_state), _ptr(workspace), workspace.numel(),
+                             _stream(dev, stream)))
+    return y, final_state
+
+
+def ssd_chunk_cumsum(dims, chunk_len, dt, A, dt_chunk=None, cs=None, stream=None):
+    dev = dt.device
+    nC = nchunks(dims.seqlen, chunk_len)
+    shape = (dims.batch, dims.nheads, nC, chunk_len)
+    dt_chunk = torch.empty(shape, dtype=torch.float32, device=dev) if dt_chunk is None else dt_chunk
+    cs = torch.empty(shape, dtype=torch.float32, device=dev) if cs is None else cs
+    _check(library().ssd_chunk_cumsum(ctypes.byref(dims), int(chunk_len), _ptr(dt), _ptr(A),
+                                      _ptr(dt_chunk), _ptr(cs), _stream(dev, stream)))
+    return dt_chunk, cs
+
+
+def _state_shape(dims, chunk_len):
+    return (dims.batch, dims.nheads, nchunks(dims.seqlen, chunk_len), dims.headdim, dims.dstate)
+
+
+def ssd_chunk_state(dims, chunk_len, x, B, dt_chunk, cs, states=None, stream=None):
+    dev = x.device
+    if states is None:
+        states = torch.empty(_state_shape(dims, chunk_len), dtype=torch.float32, device=dev)
+    _check(library().ssd_chunk_state(ctypes.byref(dims), _DTYPE_CODE[x.dtype], int(chunk_len),
+                                     _ptr(x), _ptr(B), _ptr(dt_chunk), _ptr(cs), _ptr(states),
+                                     _stream(dev, stream)))
+    return states
+
+
+def ssd_state_passing(dims, chunk_len, states, cs, init_state=None, entry_states=None,
+                      final_state=None, want_final=True, stream=None):
+    dev = cs.device
+    if entry_states is None:
+        entry_states = torch.empty(_state_shape(dims, chunk_len), dtype=torch.float32, device=dev)
+    if final_state is None and want_final:
+        final_state = torch.empty((dims.batch, dims.nheads, dims.dstate, dims.headdim),
+                                  dtype=torch.float32, device=dev)
+    _check(library().ssd_state_passing(ctypes.byref(dims), int(chunk_len), _ptr(states), _ptr(cs),
+                                       _ptr(init_state), _ptr(entry_states), _ptr(final_state),
+                                       _stream(dev, stream)))
+    return entry_states, final_state
+
+
+def ssd_chunk_scan(dims, chunk_len, x, B, C, dt_chunk, cs, D, entry_states, y=None, stream=None):
+    dev = x.device
+    y = torch.empty_like(x) if y is None else y
+    _check(library().ssd_chunk_scan(ctypes.byref(dims), _DTYPE_CODE[x.dtype], int(chunk_len),
+                                    _ptr(x), _ptr(B), _ptr(C), _ptr(dt_chunk), _ptr(cs), _ptr(D),
+                                    _ptr(entry_states), _ptr(y), _stream(dev, stream)))
+    return y

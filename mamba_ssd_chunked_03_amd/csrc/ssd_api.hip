@@ -1,0 +1,208 @@
+// ssd_api.hip -- libssd's C ABI: argument validation, workspace layout and dispatch.
+//
+// Every entry point validates all of its arguments before enqueuing anything, returns a
+// status code (no exceptions cross the ABI) and never synchronises.  Dispatch: bf16
+// inputs take the MFMA kernels when the shape has an instantiation, everything else the
+// fp32 VALU kernels.
+#include <string.h>
+
+#include "ssd_internal.h"
+
+using ssd::Shape;
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;  // int indexing inside kernels
+
+bool supported_chunk(int q) { return q == 64 || q == 128 || q == 256; }
+bool supported_dstate(int64_t n) { return n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
+bool supported_headdim(int64_t p) { return p == 16 || p == 32 || p == 64 || p == 128; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+ssd_status make_shape(const ssd_dims* d, int chunk_len, Shape* s) {
+    if (!d) return SSD_ERR_NULL;
+    if (d->batch < 0 || d->seqlen < 0 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 ||
+        d->ngroups < 1 || d->nheads % d->ngroups != 0)
+        return SSD_ERR_DIMS;
+    if (!supported_chunk(chunk_len) || !supported_dstate(d->dstate) ||
+        !supported_headdim(d->headdim))
+        return SSD_ERR_UNSUPPORTED;
+    const int64_t nC = (d->seqlen + chunk_len - 1) / chunk_len;
+    const int64_t bt = d->batch * (nC * chunk_len);
+    if (d->batch > kMaxElems || d->seqlen > kMaxElems || d->nheads > 65536 ||
+        bt * d->nheads * d->headdim >= kMaxElems || bt * d->ngroups * d->dstate >= kMaxElems ||
+        d->batch * d->nheads * nC * d->headdim * d->dstate >= kMaxElems)
+        return SSD_ERR_DIMS;
+    s->B = (int)d->batch;
+    s->T = (int)d->seqlen;
+    s->H = (int)d->nheads;
+    s->P = (int)d->headdim;
+    s->N = (int)d->dstate;
+    s->G = (int)d->ngroups;
+    s->Q = chunk_len;
+    s->nC = (int)nC;
+    return SSD_OK;
+}
+
+bool valid_dtype(ssd_dtype t) { return t == SSD_F32 || t == SSD_BF16; }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Workspace {
+    float *dtc, *cs, *states, *entry;
+};
+
+size_t workspace_bytes(const Shape& s, Workspace* w, char* base) {
+    const size_t chunk_elems = (size_t)s.B * s.H * s.nC * s.Q;
+    const size_t state_elems = (size_t)s.B * s.H * s.nC * s.P * s.N;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char* p = base ? base + off : nullptr;
+        off += round_up(bytes);
+        return (float*)p;
+    };
+    Workspace ws;
+    ws.dtc = take(chunk_elems * sizeof(float));
+    ws.cs = take(chunk_elems * sizeof(float));
+    ws.states = take(state_elems * sizeof(float));
+    ws.entry = take(state_elems * sizeof(float));
+    if (w) *w = ws;
+    return off;
+}
+
+ssd_status hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
+
+bool any_misaligned(std::initializer_list<const void*> ptrs) {
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return true;
+    return false;
+}
+
+// fp32 tensors read one element at a time (dt, A, D, init_state, final_state)
+bool any_misaligned4(std::initializer_list<const void*> ptrs) {
+    for (const void* p : ptrs)
+        if (p && ((uintptr_t)p & 3u) != 0) return true;
+    return false;
+}
+
+ssd_status run_chunk_state(const Shape& s, ssd_dtype dtype, const void* x, const void* B,
+                           const float* dtc, const float* cs, float* states, hipStream_t st) {
+    if (dtype == SSD_BF16 && ssd::chunk_state_mfma_supported(s))
+        return hip_status(ssd::launch_chunk_state_mfma(s, x, B, dtc, cs, states, st));
+    return hip_status(ssd::launch_chunk_state_valu(s, dtype, x, B, dtc, cs, states, st));
+}
+
+ssd_status run_chunk_scan(const Shape& s, ssd_dtype dtype, const void* x, const void* B,
+                          const void* C, const float* dtc, const float* cs, const float* D,
+                          const float* entry, void* y, hipStream_t st) {
+    if (dtype == SSD_BF16 && ssd::chunk_scan_mfma_supported(s))
+        return hip_status(ssd::launch_chunk_scan_mfma(s, x, B, C, dtc, cs, D, entry, y, st));
+    return hip_status(ssd::launch_chunk_scan_valu(s, dtype, x, B, C, dtc, cs, D, entry, y, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ssd_status_string(ssd_status status) {
+    switch (status) {
+        case SSD_OK: return "SSD_OK";
+        case SSD_ERR_NULL: return "SSD_ERR_NULL: a required pointer is NULL";
+        case SSD_ERR_DIMS: return "SSD_ERR_DIMS: sizes out of range or nheads % ngroups != 0";
+        case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: chunk_len/dstate/headdim/dtype not supported";
+        case SSD_ERR_ALIGN: return "SSD_ERR_ALIGN: a pointer is not aligned as required";
+        case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing or too small";
+        case SSD_ERR_HIP: return "SSD_ERR_HIP: the HIP runtime reported a launch error";
+    }
+    return "SSD_ERR_UNKNOWN";
+}
+
+size_t ssd_fwd_workspace_size(const ssd_dims* dims, int chunk_len) {
+    Shape s;
+    if (make_shape(dims, chunk_len, &s) != SSD_OK) return 0;
+    return workspace_bytes(s, nullptr, nullptr);
+}
+
+ssd_status ssd_chunk_cumsum(const ssd_dims* dims, int chunk_len, const float* dt, const float* A,
+                            float* dt_chunk, float* cs, void* stream) {
+    Shape s;
+    ssd_status r = make_shape(dims, chunk_len, &s);
+    if (r != SSD_OK) return r;
+    if ((size_t)s.B * s.T > 0 && (!dt || !A || !dt_chunk || !cs)) return SSD_ERR_NULL;
+    if (any_misaligned({dt_chunk, cs}) || any_misaligned4({dt, A})) return SSD_ERR_ALIGN;
+    return hip_status(ssd::launch_chunk_cumsum(s, dt, A, dt_chunk, cs, (hipStream_t)stream));
+}
+
+ssd_status ssd_chunk_state(const ssd_dims* dims, ssd_dtype dtype, int chunk_len, const void* x,
+                           const void* B, const float* dt_chunk, const float* cs, float* states,
+                           void* stream) {
+    Shape s;
+    ssd_status r = make_shape(dims, chunk_len, &s);
+    if (r != SSD_OK) return r;
+    if (!valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
+    if ((size_t)s.B * s.T > 0 && (!x || !B || !dt_chunk || !cs || !states)) return SSD_ERR_NULL;
+    if (any_misaligned({x, B, dt_chunk, cs, states})) return SSD_ERR_ALIGN;
+    return run_chunk_state(s, dtype, x, B, dt_chunk, cs, states, (hipStream_t)stream);
+}
+
+ssd_status ssd_state_passing(const ssd_dims* dims, int chunk_len, const float* states,
+                             const float* cs, const float* init_state, float* entry_states,
+                             float* final_state, void* stream) {
+    Shape s;
+    ssd_status r = make_shape(dims, chunk_len, &s);
+    if (r != SSD_OK) return r;
+    if ((size_t)s.B * s.T > 0 && (!states || !cs || !entry_states)) return SSD_ERR_NULL;
+    if (any_misaligned({states, cs, entry_states}) || any_misaligned4({init_state, final_state}))
+        return SSD_ERR_ALIGN;
+    if (states && states == entry_states && s.nC > 0) return SSD_ERR_DIMS;
+    return hip_status(ssd::launch_state_passing(s, states, cs, init_state, entry_states,
+                                                final_state, (hipStream_t)stream));
+}
+
+ssd_status ssd_chunk_scan(const ssd_dims* dims, ssd_dtype dtype, int chunk_len, const void* x,
+                          const void* B, const void* C, const float* dt_chunk, const float* cs,
+                          const float* D, const float* entry_states, void* y, void* stream) {
+    Shape s;
+    ssd_status r = make_shape(dims, chunk_len, &s);
+    if (r != SSD_OK) return r;
+    if (!valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
+    if ((size_t)s.B * s.T > 0 && (!x || !B || !C || !dt_chunk || !cs || !D || !entry_states || !y))
+        return SSD_ERR_NULL;
+    if (any_misaligned({x, B, C, dt_chunk, cs, entry_states, y}) || any_misaligned4({D}))
+        return SSD_ERR_ALIGN;
+    return run_chunk_scan(s, dtype, x, B, C, dt_chunk, cs, D, entry_states, y, (hipStream_t)stream);
+}
+
+ssd_status ssd_fwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const float* dt,
+                   const float* A, const void* B, const void* C, const float* D, int chunk_len,
+                   const float* init_state, void* y, float* final_state, void* workspace,
+                   size_t workspace_bytes_given, void* stream) {
+    Shape s;
+    ssd_status r = make_shape(dims, chunk_len, &s);
+    if (r != SSD_OK) return r;
+    if (!valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
+    const bool has_tokens = (size_t)s.B * s.T > 0;
+    if (has_tokens && (!x || !dt || !A || !B || !C || !D || !y)) return SSD_ERR_NULL;
+    if (any_misaligned({x, B, C, y, workspace}) ||
+        any_misaligned4({dt, A, D, init_state, final_state}))
+        return SSD_ERR_ALIGN;
+    Workspace ws;
+    const size_t need = workspace_bytes(s, &ws, (char*)workspace);
+    if (need > 0 && (!workspace || workspace_bytes_given < need)) return SSD_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    if (s.B == 0) return SSD_OK;
+    if (has_tokens) {
+        r = hip_status(ssd::launch_chunk_cumsum(s, dt, A, ws.dtc, ws.cs, st));
+        if (r != SSD_OK) return r;
+        r = run_chunk_state(s, dtype, x, B, ws.dtc, ws.cs, ws.states, st);
+        if (r != SSD_OK) return r;
+    }
+    // with T == 0 this only copies init_state (or zeros) to final_state
+    r = hip_status(ssd::launch_state_passing(s, ws.states, ws.cs, init_state, ws.entry,
+                                             final_state, st));
+    if (r != SSD_OK || !has_tokens) return r;
+    return run_chunk_scan(s, dtype, x, B, C, ws.dtc, ws.cs, D, ws.entry, y, st);
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// ssd_internal.h -- shapes, element access and kernel launchers shared by libssd's
+// translation units.  Not part of the public ABI (that is include/ssd.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssd.h"
+
+namespace ssd {
+
+// Problem shape after validation; every size fits in int.
+struct Shape {
+    int B, T, H, P, N, G, Q, nC;
+    int heads_per_group() const { return H / G; }
+};
+
+// ---- element access ---------------------------------------------------------------
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(__bf16 v) { return (float)v; }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float v) { return (__bf16)v; }
+
+// ---- launchers (each returns the launch status) -------------------------------------
+hipError_t launch_chunk_cumsum(const Shape& s, const float* dt, const float* A, float* dtc,
+                               float* cs, hipStream_t st);
+hipError_t launch_state_passing(const Shape& s, const float* states, const float* cs,
+                                const float* init, float* entry, float* final_state,
+                                hipStream_t st);
+
+// Plain fp32-accumulate VALU kernels: any supported size, fp32 or bf16 inputs.
+hipError_t launch_chunk_state_valu(const Shape& s, ssd_dtype dt, const void* x, const void* Bm,
+                                   const float* dtc, const float* cs, float* states,
+                                   hipStream_t st);
+hipError_t launch_chunk_scan_valu(const Shape& s, ssd_dtype dt, const void* x, const void* Bm,
+                                  const void* Cm, const float* dtc, const float* cs,
+                                  const float* D, const float* entry, void* y, hipStream_t st);
+
+// bf16 MFMA kernels (gfx950 v_mfma_f32_16x16x32_bf16); *_supported says whether a shape
+// has an instantiation.
+bool chunk_state_mfma_supported(const Shape& s);
+hipError_t launch_chunk_state_mfma(const Shape& s, const void* x, const void* Bm,
+                                   const float* dtc, const float* cs, float* states,
+                                   hipStream_t st);
+bool chunk_scan_mfma_supported(const Shape& s);
+hipError_t launch_chunk_scan_mfma(const Shape& s, const void* x, const void* Bm, const void* Cm,
+                                  const float* dtc, const float* cs, const float* D,
+                                  const float* entry, void* y, hipStream_t st);
+
+}  // namespace ssd

@@ -1,0 +1,92 @@
+// state_passing.hip -- stage 3 of the block decomposition: carry states across chunks.
+//
+// Structured summary of arXiv 2405.21060, section "The Block-Decomposition SSD
+// Algorithm", stage 3 ("Propagate states between chunks"): the true state after chunk c
+// is a 1-SS matrix applied to the sequence of chunk states, i.e. the scalar recurrence
+// (section "The 1-Semiseparable Matrix", equation 7) run over chunks with the chunk's
+// total decay as the scalar:
+//     E_0 = init,   E_{c+1} = exp(cs[c][Q-1]) * E_c + S_c,   final = E_nC.
+// The pages' subscripts for this chunk decay are garbled; this is the reading that
+// reproduces the token recurrence (checked against the oracle's boundary states).
+//
+// Every (b, h, p, n) element is an independent lane of a length-nC sequential scan.  A
+// workgroup of 256 threads covers 1024 elements of one (b, h) state, four consecutive
+// elements (one 16-byte load) per thread.  The loads of kUnroll chunks are issued before
+// the dependent multiply-adds so that several requests per thread are in flight; the
+// kernel is bound by HBM (it reads S and writes E once each).
+#include "ssd_internal.h"
+
+namespace ssd {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;
+
+__device__ __forceinline__ float4 fma4(float a, float4 s, float4 v) {
+    return make_float4(fmaf(a, s.x, v.x), fmaf(a, s.y, v.y), fmaf(a, s.z, v.z), fmaf(a, s.w, v.w));
+}
+
+__global__ __launch_bounds__(kThreads) void state_passing_kernel(
+    const float* __restrict__ states, const float* __restrict__ cs,
+    const float* __restrict__ init, float* __restrict__ entry, float* __restrict__ final_state,
+    int nC, int Q, int P, int N, int tiles_per_state) {
+    const int NP = N * P;
+    const int bh = blockIdx.x / tiles_per_state;
+    const int tile = blockIdx.x % tiles_per_state;
+    const int e = (tile * kThreads + threadIdx.x) * 4;  // element in the [P][N] state
+    if (e >= NP) return;
+    const int p = e / N, n = e % N;  // N % 4 == 0, so the four elements share p
+
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (init) {
+        const float* in = init + (size_t)bh * NP;  // [N][P]
+        s = make_float4(in[(n + 0) * P + p], in[(n + 1) * P + p], in[(n + 2) * P + p],
+                        in[(n + 3) * P + p]);
+    }
+    const size_t base = (size_t)bh * nC * NP + e;
+    const float* csl = cs + (size_t)bh * nC * Q + (Q - 1);  // each chunk's total log decay
+
+    int c = 0;
+    for (; c + kUnroll <= nC; c += kUnroll) {
+        float4 v[kUnroll];
+        float a[kUnroll];
+#pragma unroll
+        for (int k = 0; k < kUnroll; ++k) {
+            v[k] = *reinterpret_cast<const float4*>(states + base + (size_t)(c + k) * NP);
+            a[k] = csl[(size_t)(c + k) * Q];
+        }
+#pragma unroll
+        for (int k = 0; k < kUnroll; ++k) {
+            *reinterpret_cast<float4*>(entry + base + (size_t)(c + k) * NP) = s;
+            s = fma4(expf(a[k]), s, v[k]);
+        }
+    }
+    for (; c < nC; ++c) {
+        const float4 v = *reinterpret_cast<const float4*>(states + base + (size_t)c * NP);
+        *reinterpret_cast<float4*>(entry + base + (size_t)c * NP) = s;
+        s = fma4(expf(csl[(size_t)c * Q]), s, v);
+    }
+    if (final_state) {
+        float* out = final_state + (size_t)bh * NP;  // [N][P]
+        out[(n + 0) * P + p] = s.x;
+        out[(n + 1) * P + p] = s.y;
+        out[(n + 2) * P + p] = s.z;
+        out[(n + 3) * P + p] = s.w;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_state_passing(const Shape& s, const float* states, const float* cs,
+                                const float* init, float* entry, float* final_state,
+                                hipStream_t st) {
+    const int NP = s.N * s.P;
+    const int tiles = (NP + kThreads * 4 - 1) / (kThreads * 4);
+    const unsigned blocks = (unsigned)((size_t)s.B * s.H * tiles);
+    if (blocks == 0) return hipSuccess;
+    state_passing_kernel<<<blocks, kThreads, 0, st>>>(states, cs, init, entry, final_state, s.nC,
+                                                     s.Q, s.P, s.N, tiles);
+    return hipGetLastError();
+}
+
+}  // namespace ssd

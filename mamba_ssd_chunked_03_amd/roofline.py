@@ -1,0 +1,57 @@
+"""Algorithmic FLOP and byte counts of the four stage kernels, and the MI355X peaks.
+
+"Algorithmic" means what the method must do, not what a kernel issues: every input is
+read once and every output written once per launch; the quadratic part counts only the
+causal half of each Q x Q diagonal block (the method never needs the upper triangle),
+and C B^T is counted once per (batch, group, chunk) because the heads of a group share
+it.  Bytes use the dtype sizes of the boundary (x, B, C, y in the input dtype; dt, cs
+and the states in fp32).
+"""
+from dataclasses import dataclass
+
+# MI355X published peaks (dense; no sparsity).
+PEAK_HBM_GBPS = 8000.0
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3, "fp64": 78.6}
+
+
+@dataclass
+class KernelCost:
+    name: str
+    bytes: float
+    flops: float
+
+
+def kernel_costs(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len, dtype="bf16",
+                 init_state=False, final_state=True):
+    B, T, H, P, N, G, Q = batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len
+    e = 2 if dtype == "bf16" else 4
+    nC = (T + Q - 1) // Q
+    chunk_f32 = B * H * nC * Q * 4          # dt_chunk or cs
+    state_f32 = B * H * nC * P * N * 4      # chunk states or entry states
+    io_xy = B * T * H * P * e               # x or y
+    io_bc = B * T * G * N * e               # B or C
+    st1 = B * H * N * P * 4                 # init or final state
+    cumsum = KernelCost("chunk_cumsum", B * T * H * 4 + H * 4 + 2 * chunk_f32, 2.0 * B * T * H)
+    state = KernelCost("chunk_state", io_xy + io_bc + 2 * chunk_f32 + state_f32,
+                       2.0 * B * H * T * N * P)
+    passing = KernelCost("state_passing",
+                         2 * state_f32 + B * H * nC * 4 + (st1 if init_state else 0)
+                         + (st1 if final_state else 0),
+                         2.0 * B * H * nC * N * P)
+    # intra-chunk: sum over rows j of (j+1) MACs x P, per (b, h, chunk); C B^T likewise
+    # per (b, g, chunk) over N; off-chunk: Q x N x P MACs per (b, h, chunk)
+    full, rem = divmod(T, Q)
+    tri = full * Q * (Q + 1) + rem * (rem + 1)          # sum of 2*(j+1) over valid rows
+    scan = KernelCost("chunk_scan",
+                      2 * io_xy + 2 * io_bc + 2 * chunk_f32 + state_f32 + H * 4,
+                      B * H * tri * P + B * G * tri * N + 2.0 * B * H * T * N * P)
+    return [cumsum, state, passing, scan]
+
+
+def compulsory_bytes(batch, seqlen, nheads, headdim, dstate, ngroups, dtype="bf16",
+                     init_state=False, final_state=True):
+    e = 2 if dtype == "bf16" else 4
+    B, T, H, P, N, G = batch, seqlen, nheads, headdim, dstate, ngroups
+    st1 = B * H * N * P * 4
+    return (2 * B * T * H * P * e + 2 * B * T * G * N * e + B * T * H * 4 + 2 * H * 4
+            + (st1 if init_state else 0) + (st1 if final_state else 0))

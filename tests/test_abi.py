@@ -1,0 +1,99 @@
+"""The C-ABI library builds, loads and exports what include/ssd.h declares (CPU only).
+
+Only validation paths are called here: every call below fails its argument checks before
+any HIP call, so no GPU is needed.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mamba_ssd_chunked_03_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libssd.so is not built (run __graft_entry__.build())")
+    return binding.library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(binding.EXPORTED)
+    for name in names:
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {binding.LIB_PATH}").read()
+    for name in names:
+        assert re.search(rf"\bT {name}\b", out), f"{name} not exported as a function"
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        s = binding.status_string(code)
+        assert s.startswith("SSD_")
+    assert binding.status_string(99) == "SSD_ERR_UNKNOWN"
+
+
+def D(b=1, t=256, h=2, p=16, n=16, g=1):
+    return binding.SsdDims(b, t, h, p, n, g)
+
+
+def test_workspace_size(lib):
+    d = D(4, 4096, 80, 64, 128, 1)
+    ws = binding.ssd_fwd_workspace_size(d, 256)
+    nC = 16
+    chunk = 4 * 80 * nC * 256 * 4
+    state = 4 * 80 * nC * 64 * 128 * 4
+    assert ws == 2 * chunk + 2 * state
+    # ragged T rounds the chunk count up
+    assert binding.ssd_fwd_workspace_size(D(1, 1000, 4, 64, 128, 1), 256) == \
+        2 * (4 * 4 * 256 * 4) + 2 * (4 * 4 * 64 * 128 * 4)
+    assert binding.ssd_fwd_workspace_size(D(1, 0, 2, 16, 16, 1), 64) == 0
+    for bad, q in ((D(h=3, g=2), 64), (D(p=24), 64), (D(n=48), 64), (D(), 32), (D(b=-1), 64)):
+        assert binding.ssd_fwd_workspace_size(bad, q) == 0
+
+
+def _fwd(lib, d, dtype=0, q=64, ptrs=None, ws_bytes=1 << 30):
+    p = dict(x=16, dt=16, A=16, B=16, C=16, D=16, init=None, y=16, final=None, ws=16)
+    p.update(ptrs or {})
+    v = {k: (None if val is None else ctypes.c_void_p(val)) for k, val in p.items()}
+    return lib.ssd_fwd(ctypes.byref(d), dtype, v["x"], v["dt"], v["A"], v["B"], v["C"], v["D"], q,
+                       v["init"], v["y"], v["final"], v["ws"], ws_bytes, None)
+
+
+def test_validation_errors_before_any_launch(lib):
+    assert _fwd(lib, D(h=3, g=2)) == 2                     # H % G
+    assert _fwd(lib, D(t=-5)) == 2
+    assert _fwd(lib, D(p=0)) == 2
+    assert _fwd(lib, D(p=48)) == 3                         # unsupported head dim
+    assert _fwd(lib, D(n=512)) == 3
+    assert _fwd(lib, D(), q=100) == 3                      # unsupported chunk
+    assert _fwd(lib, D(), dtype=7) == 3
+    assert _fwd(lib, D(), ptrs=dict(x=None)) == 1
+    assert _fwd(lib, D(), ptrs=dict(C=None)) == 1
+    assert _fwd(lib, D(), ptrs=dict(x=0x1008)) == 4        # 8-byte aligned only
+    assert _fwd(lib, D(), ptrs=dict(dt=0x1002)) == 4
+    assert _fwd(lib, D(), ptrs=dict(ws=None)) == 5
+    assert _fwd(lib, D(), ws_bytes=10) == 5
+    assert _fwd(lib, D(b=1 << 20, t=1 << 20)) == 2          # index range
+    # stage entry points validate the same way
+    assert lib.ssd_chunk_cumsum(ctypes.byref(D(p=40)), 64, None, None, None, None, None) == 3
+    assert lib.ssd_chunk_cumsum(ctypes.byref(D()), 64, None, None, None, None, None) == 1
+    assert lib.ssd_chunk_state(ctypes.byref(D()), 1, 64, None, None, None, None, None, None) == 1
+    assert lib.ssd_state_passing(ctypes.byref(D()), 64, ctypes.c_void_p(64), ctypes.c_void_p(64),
+                                 None, ctypes.c_void_p(64), None, None) == 2   # aliasing
+    assert lib.ssd_chunk_scan(ctypes.byref(D()), 1, 128, None, None, None, None, None, None,
+                              None, None, None) == 1
+    assert lib.ssd_fwd(None, 0, None, None, None, None, None, None, 64, None, None, None, None,
+                       0, None) == 1

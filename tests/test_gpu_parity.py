@@ -1,0 +1,235 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, on the GPU.
+
+Whole-tensor rel-L2 against the oracle on small cases (several chunks and ragged tails);
+at the full model-shaped sizes, whole (batch, head) sequences sampled across the tensor
+are checked against the oracle run on just those sequences.  Per-stage tests feed each
+kernel oracle-made inputs so that a mistake is pinned to its stage.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mamba_ssd_chunked_03_amd import binding
+from mamba_ssd_chunked_03_amd.workloads import (LONG_CTX, MAMBA2_130M, MAMBA2_2P7B, NSWEEP, STRESS,
+                                                TINY_FP32, Workload, generate, variants)
+from parity import (TOL, check_sampled, gpu_fwd, np64, oracle_fwd, rel_l2, say, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    binding.library()
+    torch.cuda.init()
+    return torch.device("cuda:0")
+
+
+SMALL = [TINY_FP32] + list(STRESS.values())
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_fwd_matches_oracle_small(w):
+    say(f"[fwd small] {w.describe()}")
+    cpu = generate(w)
+    y, fin = gpu_fwd(to_device(cpu), w.chunk_len)
+    y_ref, f_ref = oracle_fwd(cpu)
+    ey, ef = rel_l2(np64(y), y_ref), rel_l2(np64(fin), f_ref)
+    say(f"    rel_l2 y={ey:.3e} final={ef:.3e}")
+    assert ey <= TOL[w.dtype]
+    assert ef <= TOL[w.dtype]
+
+
+MODEL = [MAMBA2_130M, MAMBA2_2P7B, *NSWEEP, LONG_CTX]
+
+
+@pytest.mark.parametrize("w", MODEL, ids=[w.name for w in MODEL])
+def test_fwd_matches_oracle_full_size_sampled(w):
+    say(f"[fwd full size] {w.describe()}")
+    cpu = generate(w)
+    y, fin = gpu_fwd(to_device(cpu), w.chunk_len)
+    assert torch.isfinite(y.float()).all()
+    ey, ef = check_sampled(w, cpu, y, fin, count=4)
+    say(f"    sampled rel_l2 y={ey:.3e} final={ef:.3e}")
+    assert ey <= TOL[w.dtype]
+    assert ef <= TOL[w.dtype]
+
+
+def test_tiny_fp32_whole_output():
+    """The fp32 workload compared on every output, at the fp32 bound."""
+    w = TINY_FP32
+    cpu = generate(w)
+    y, fin = gpu_fwd(to_device(cpu), w.chunk_len)
+    y_ref, f_ref = oracle_fwd(cpu)
+    assert rel_l2(np64(y), y_ref) <= 1e-4
+    assert rel_l2(np64(fin), f_ref) <= 1e-4
+    # element-wise: no single output is far off either
+    err = np.abs(np64(y) - y_ref).max() / np.abs(y_ref).max()
+    assert err < 1e-4
+
+
+# ------------------------------------------------------------------ stage by stage
+
+STAGE_CASES = [STRESS["slow_decay_fp32"], STRESS["slow_decay"], STRESS["ragged_250_q64"],
+               STRESS["ragged_1000"]]
+
+
+def _dims(w):
+    return binding.SsdDims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups)
+
+
+@pytest.mark.parametrize("w", STAGE_CASES, ids=[w.name for w in STAGE_CASES])
+def test_stage_chunk_cumsum(w):
+    say(f"[stage cumsum] {w.describe()}")
+    cpu = generate(w)
+    dv = to_device(cpu)
+    dtc, cs = binding.ssd_chunk_cumsum(_dims(w), w.chunk_len, dv["dt"], dv["A"])
+    torch.cuda.synchronize()
+    ref = oracle.chunk_cumsum(np64(cpu["dt"]), np64(cpu["A"]), w.chunk_len)
+    # dt copied exactly; zero past the end of the sequence
+    Q, T = w.chunk_len, w.seqlen
+    dt_pad = np.zeros((w.batch, w.nchunks * Q, w.nheads))
+    dt_pad[:, :T] = np64(cpu["dt"])
+    dt_ref = dt_pad.reshape(w.batch, w.nchunks, Q, w.nheads).transpose(0, 3, 1, 2)
+    np.testing.assert_array_equal(np64(dtc), dt_ref)
+    # fp32 prefix sums: error relative to the running sum of |dt*A| (all terms share a sign)
+    mag = np.abs(ref).max()
+    assert np.abs(np64(cs) - ref).max() <= 2e-6 * max(mag, 1e-30)
+
+
+@pytest.mark.parametrize("w", STAGE_CASES, ids=[w.name for w in STAGE_CASES])
+def test_stage_chunk_state(w):
+    say(f"[stage chunk_state] {w.describe()}")
+    cpu = generate(w)
+    dv = to_device(cpu)
+    d = _dims(w)
+    dtc, cs = binding.ssd_chunk_cumsum(d, w.chunk_len, dv["dt"], dv["A"])
+    S = binding.ssd_chunk_state(d, w.chunk_len, dv["x"], dv["B"], dtc, cs)
+    torch.cuda.synchronize()
+    c = {k: np64(v) for k, v in cpu.items()}
+    ref = oracle.chunk_states(c["x"], c["dt"], c["A"], c["B"], c["C"], c["D"], w.chunk_len)
+    e = rel_l2(np64(S).swapaxes(-1, -2), ref)
+    say(f"    rel_l2 S={e:.3e}")
+    assert e <= (1e-5 if w.dtype == "fp32" else TOL[w.dtype])
+
+
+@pytest.mark.parametrize("w", STAGE_CASES, ids=[w.name for w in STAGE_CASES])
+def test_stage_state_passing(w):
+    """Fed the oracle's chunk states and log decays (rounded to fp32), the scan must give
+    the oracle's entry states and final state."""
+    say(f"[stage state_passing] {w.describe()}")
+    cpu = generate(w)
+    c = {k: np64(v) for k, v in cpu.items()}
+    S = oracle.chunk_states(c["x"], c["dt"], c["A"], c["B"], c["C"], c["D"], w.chunk_len)
+    cs = oracle.chunk_cumsum(c["dt"], c["A"], w.chunk_len)
+    ent_ref, fin_ref = oracle.entry_states(c["x"], c["dt"], c["A"], c["B"], c["C"], c["D"],
+                                           w.chunk_len, init_state=c["init_state"])
+    dev = "cuda"
+    S_d = torch.from_numpy(S.swapaxes(-1, -2).copy()).float().to(dev)
+    cs_d = torch.from_numpy(cs).float().to(dev)
+    init = None if cpu["init_state"] is None else cpu["init_state"].to(dev)
+    ent, fin = binding.ssd_state_passing(_dims(w), w.chunk_len, S_d, cs_d, init_state=init)
+    torch.cuda.synchronize()
+    e1 = rel_l2(np64(ent).swapaxes(-1, -2), ent_ref)
+    e2 = rel_l2(np64(fin), fin_ref)
+    say(f"    rel_l2 entry={e1:.3e} final={e2:.3e}")
+    assert e1 <= 1e-5 and e2 <= 1e-5
+
+
+@pytest.mark.parametrize("w", STAGE_CASES, ids=[w.name for w in STAGE_CASES])
+def test_stage_chunk_scan(w):
+    """Fed the oracle's log decays and entry states, the chunk scan must give the
+    oracle's y."""
+    say(f"[stage chunk_scan] {w.describe()}")
+    cpu = generate(w)
+    c = {k: np64(v) for k, v in cpu.items()}
+    cs = oracle.chunk_cumsum(c["dt"], c["A"], w.chunk_len)
+    ent, _ = oracle.entry_states(c["x"], c["dt"], c["A"], c["B"], c["C"], c["D"], w.chunk_len,
+                                 init_state=c["init_state"])
+    y_ref, _ = oracle_fwd(cpu)
+    dv = to_device(cpu)
+    d = _dims(w)
+    dtc, _ = binding.ssd_chunk_cumsum(d, w.chunk_len, dv["dt"], dv["A"])
+    cs_d = torch.from_numpy(cs).float().cuda()
+    ent_d = torch.from_numpy(ent.swapaxes(-1, -2).copy()).float().cuda()
+    y = binding.ssd_chunk_scan(d, w.chunk_len, dv["x"], dv["B"], dv["C"], dtc, cs_d, dv["D"], ent_d)
+    torch.cuda.synchronize()
+    e = rel_l2(np64(y), y_ref)
+    say(f"    rel_l2 y={e:.3e}")
+    assert e <= TOL[w.dtype]
+
+
+# ------------------------------------------------------------------ invariants
+
+def test_chunk_length_does_not_change_the_result():
+    base = variants(STRESS["slow_decay"], seqlen=1000)
+    cpu = generate(base)
+    y_ref, f_ref = oracle_fwd(cpu)
+    dv = to_device(cpu)
+    outs = []
+    for q in (64, 128, 256):
+        say(f"[chunk invariance] Q={q}")
+        y, fin = gpu_fwd(dv, q)
+        assert rel_l2(np64(y), y_ref) <= TOL["bf16"]
+        assert rel_l2(np64(fin), f_ref) <= TOL["bf16"]
+        outs.append(np64(y))
+    assert rel_l2(outs[0], outs[2]) <= TOL["bf16"]
+
+
+def test_deterministic_run_to_run():
+    w = STRESS["slow_decay"]
+    dv = to_device(generate(w))
+    say("[determinism]")
+    y1, f1 = gpu_fwd(dv, w.chunk_len)
+    y2, f2 = gpu_fwd(dv, w.chunk_len)
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_split_run_resumes_from_final_state(dtype):
+    """Two segments, the second starting from the first's final state, reproduce one
+    run over the whole sequence (the state hand-off of sequence parallelism)."""
+    w = variants(STRESS["slow_decay"], dtype=dtype, seqlen=768, batch=1)
+    cpu = generate(w)
+    dv = to_device(cpu)
+    say(f"[split run] {dtype}")
+    y_full, f_full = gpu_fwd(dv, w.chunk_len)
+    T1 = 300   # not a chunk multiple
+    first = {k: (v[:, :T1].contiguous() if k in ("x", "dt", "B", "C") else v) for k, v in dv.items()}
+    ya, fa = gpu_fwd(first, w.chunk_len)
+    second = {k: (v[:, T1:].contiguous() if k in ("x", "dt", "B", "C") else v) for k, v in dv.items()}
+    second["init_state"] = fa
+    yb, fb = gpu_fwd(second, w.chunk_len)
+    y_ref, f_ref = oracle_fwd(cpu)
+    y_split = np.concatenate([np64(ya), np64(yb)], axis=1)
+    assert rel_l2(y_split, y_ref) <= TOL[dtype]
+    assert rel_l2(np64(fb), f_ref) <= TOL[dtype]
+    assert rel_l2(y_split, np64(y_full)) <= TOL[dtype]
+
+
+def test_empty_sequence_and_empty_batch():
+    say("[empty]")
+    w = Workload("t0", 2, 0, 2, 32, 32, 1, 64, init_state=True)
+    cpu = generate(w)
+    dv = to_device(cpu)
+    y, fin = gpu_fwd(dv, 64)
+    assert y.numel() == 0
+    assert torch.equal(fin, dv["init_state"])
+    dv["init_state"] = None
+    y, fin = gpu_fwd(dv, 64)
+    assert torch.count_nonzero(fin) == 0
+    w = Workload("b0", 0, 64, 2, 32, 32, 1, 64)
+    dv = to_device(generate(w))
+    y, fin = gpu_fwd(dv, 64)
+    assert y.numel() == 0 and fin.numel() == 0
+
+
+def test_bad_arguments_raise():
+    w = TINY_FP32
+    dv = to_device(generate(w))
+    with pytest.raises(binding.SsdError) as ei:
+        binding.ssd_fwd(dv["x"], dv["dt"], dv["A"], dv["B"], dv["C"], dv["D"], 96)
+    assert ei.value.code == 3
+    with pytest.raises(TypeError):
+        binding.ssd_fwd(dv["x"], dv["dt"].double(), dv["A"], dv["B"], dv["C"], dv["D"], 64)
