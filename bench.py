@@ -51,43 +51,44 @@ def host_threads():
 
 def cpu_baseline(w, inputs, budget_s):
     """Time the fp64 oracle (as it stands) on a bounded sample of the same workload:
-    the first batch element, as many heads as fit the time budget (whole sequences).
-    Tokens/s is scaled to the metric's unit: heads/H of a token per (step, head)."""
-    import numpy as np
+    whole batch elements when at least one fits the time budget (all of them when the
+    whole workload fits), else the first heads (whole groups) of batch element 0.  Every
+    sampled (batch, head) sequence runs over the full T.  Tokens/s is scaled to the
+    metric's unit: one (batch, head) sequence is 1/H of each of its T tokens."""
     import oracle
-    from mamba_ssd_chunked_03_amd.workloads import head_slice
 
     nthreads = host_threads()
+    hpg = w.nheads // w.ngroups
 
-    def sample(nh):
-        g_of = [h // (w.nheads // w.ngroups) for h in range(nh)]
-        sl = [head_slice(inputs, w, 0, h) for h in range(nh)]
-        cat = lambda k, ax: np.concatenate([s[k].double().numpy() for s in sl], axis=ax)
-        x, dt, A, D = cat("x", 2), cat("dt", 2), cat("A", 0), cat("D", 0)
-        B = np.concatenate([inputs["B"][0:1, :, g:g + 1].double().numpy() for g in g_of], axis=2)
-        C = np.concatenate([inputs["C"][0:1, :, g:g + 1].double().numpy() for g in g_of], axis=2)
-        init = None
-        if inputs["init_state"] is not None:
-            init = inputs["init_state"][0:1, :nh].double().numpy()
-        return dict(x=x, dt=dt, A=A, B=B, C=C, D=D, init_state=init)
+    def sample(nb, nh):
+        g = (nh + hpg - 1) // hpg
+        pick = lambda t, hs: None if t is None else t[:nb, :, :hs].double().numpy()
+        init = inputs["init_state"]
+        return dict(x=pick(inputs["x"], nh), dt=pick(inputs["dt"], nh),
+                    A=inputs["A"][:nh].double().numpy(), B=pick(inputs["B"], g),
+                    C=pick(inputs["C"], g), D=inputs["D"][:nh].double().numpy(),
+                    init_state=None if init is None else init[:nb, :nh].double().numpy())
 
-    # probe with one head per thread to size the sample, then time the sample
-    nh = min(w.nheads, nthreads)
-    s = sample(nh)
-    t0 = time.perf_counter()
-    oracle.ssd_ref(**s, nthreads=nthreads)
-    probe = time.perf_counter() - t0
-    rounds = max(1, int(budget_s / max(probe, 1e-3)))
-    nh = min(w.nheads, nh * rounds)
-    s = sample(nh)
-    used = oracle.threads_used(1, nh, nthreads)
-    t0 = time.perf_counter()
-    oracle.ssd_ref(**s, nthreads=nthreads)
-    el = time.perf_counter() - t0
-    tokens = w.seqlen * nh / w.nheads
-    return {"value": tokens / el, "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": f"batch element 0 of {w.batch}, heads 0..{nh - 1} of {w.nheads}, "
-                      f"full T={w.seqlen} (fp64 token recurrence, {el:.2f} s)"}
+    def timed(nb, nh):
+        s = sample(nb, nh)
+        t0 = time.perf_counter()
+        oracle.ssd_ref(**s, nthreads=nthreads)
+        return time.perf_counter() - t0
+
+    probe = timed(1, w.nheads)          # one whole batch element
+    if probe * 2 <= budget_s:
+        nb, nh = max(1, min(w.batch, int(budget_s / max(probe, 1e-3)))), w.nheads
+    else:
+        nb = 1
+        nh = max(hpg, int(w.nheads * budget_s / probe) // hpg * hpg)
+        nh = min(nh, w.nheads)
+    el = timed(nb, nh)
+    used = oracle.threads_used(nb, nh, nthreads)
+    tokens = w.seqlen * nb * nh / w.nheads
+    return {"value": round(tokens / el, 1), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"batch elements 0..{nb - 1} of {w.batch}, heads 0..{nh - 1} of "
+                      f"{w.nheads}, full T={w.seqlen} ({nb * nh} fp64 token-recurrence "
+                      f"sequences, {el:.2f} s)"}
 
 
 def main():
@@ -193,7 +194,7 @@ def main():
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
+        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen,
                    "nheads": w.nheads, "headdim": w.headdim, "dstate": w.dstate,
                    "ngroups": w.ngroups, "chunk_len": Q, "input_dtype": w.dtype,

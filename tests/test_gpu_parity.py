@@ -233,3 +233,28 @@ def test_bad_arguments_raise():
     assert ei.value.code == 3
     with pytest.raises(TypeError):
         binding.ssd_fwd(dv["x"], dv["dt"].double(), dv["A"], dv["B"], dv["C"], dv["D"], 64)
+
+
+# ------------------------------------------------------------------ MFMA instantiations
+
+SWEEP = [  # (headdim P, dstate N, chunk Q, groups)
+    (16, 64, 64, 1), (32, 32, 128, 2), (64, 256, 256, 1), (128, 128, 128, 2),
+    (128, 256, 64, 1), (16, 256, 128, 2), (64, 64, 256, 2), (128, 32, 256, 1),
+    (32, 128, 64, 1), (64, 128, 128, 1), (128, 64, 256, 2), (16, 16, 64, 1),
+]
+
+
+@pytest.mark.parametrize("shape", SWEEP, ids=[f"P{p}_N{n}_Q{q}_G{g}" for p, n, q, g in SWEEP])
+def test_shape_sweep_matches_oracle(shape):
+    """Every kernel instantiation family (and the VALU fallback for N=16), with a ragged
+    tail, slow decay and an init state."""
+    P, N, Q, G = shape
+    w = Workload(f"sweep_P{P}_N{N}_Q{Q}", 1, 2 * Q + 37, 2, P, N, G, Q, init_state=True,
+                 log_neg_a_range=(np.log(0.005), np.log(0.05)))
+    say(f"[sweep] {w.describe()}")
+    cpu = generate(w)
+    y, fin = gpu_fwd(to_device(cpu), Q)
+    y_ref, f_ref = oracle_fwd(cpu)
+    ey, ef = rel_l2(np64(y), y_ref), rel_l2(np64(fin), f_ref)
+    say(f"    rel_l2 y={ey:.3e} final={ef:.3e}")
+    assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
