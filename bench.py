@@ -35,6 +35,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="rough budget for the oracle CPU baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (3 times), to calibrate the "
+                         "HBM byte counters against a known traffic, and exit")
     return ap.parse_args()
 
 
@@ -100,6 +103,16 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_MiB": args.copy_calibration,
+                          "read_bytes_per_copy": 4 * n, "write_bytes_per_copy": 4 * n}))
+        return
     from mamba_ssd_chunked_03_amd import binding, roofline
     from mamba_ssd_chunked_03_amd.workloads import WORKLOADS, generate
 
@@ -123,11 +136,14 @@ def main():
     offs = [0]
     for nbytes in (chunk_n * 4, chunk_n * 4, state_n * 4):
         offs.append(offs[-1] + rnd(nbytes))
-    view = lambda off, n, shape: ws[off:off + n * 4].view(f32).view(shape)
+    def view(off, n, shape, dtype=f32):
+        esz = torch.tensor([], dtype=dtype).element_size()
+        return ws[off:off + n * esz].view(dtype).view(shape)
     cshape = (w.batch, w.nheads, nC, Q)
     sshape = (w.batch, w.nheads, nC, w.headdim, w.dstate)
     dtc, cs = view(offs[0], chunk_n, cshape), view(offs[1], chunk_n, cshape)
-    S, E = view(offs[2], state_n, sshape), view(offs[3], state_n, sshape)
+    S = view(offs[2], state_n, sshape)
+    E = view(offs[3], state_n, sshape, d_in["x"].dtype)   # entry states in the input dtype
 
     def fwd():
         binding.ssd_fwd(d_in["x"], d_in["dt"], d_in["A"], d_in["B"], d_in["C"], d_in["D"], Q,

@@ -48,8 +48,10 @@
  *   B, C           [batch][seqlen][ngroups][dstate]       in `dtype`
  *   init_state, final_state  [batch][nheads][dstate][headdim]   fp32
  *   dt_chunk, cs   [batch][nheads][nchunks][chunk_len]    fp32, nchunks = ceil(T/chunk_len)
- *   chunk states, entry states  [batch][nheads][nchunks][headdim][dstate]   fp32
- *     (note: headdim-major, the transpose of the N x P state of the formulas)
+ *   chunk states   [batch][nheads][nchunks][headdim][dstate]   fp32
+ *   entry states   [batch][nheads][nchunks][headdim][dstate]   in `dtype` (the chunk scan
+ *                  consumes them as operands of that dtype; the carried state is fp32)
+ *     (state buffers are headdim-major: the transpose of the N x P state of the formulas)
  */
 #ifndef LIBSSD_SSD_H
 #define LIBSSD_SSD_H
@@ -86,8 +88,9 @@ typedef struct {
 /* Human-readable name of a status code (a static string; never NULL). */
 const char* ssd_status_string(ssd_status status);
 
-/* Bytes of device workspace ssd_fwd needs for these sizes (0 if the sizes are invalid).
- * It holds dt_chunk, cs, the chunk states and the entry states, each 256-byte aligned. */
+/* Bytes of device workspace ssd_fwd needs for these sizes, for either dtype (0 if the
+ * sizes are invalid).  It holds dt_chunk, cs, the chunk states and the entry states, each
+ * 256-byte aligned, in that order. */
 size_t ssd_fwd_workspace_size(const ssd_dims* dims, int chunk_len);
 
 /* The whole SSD forward: y and (optionally) final_state from x, dt, A, B, C, D and an
@@ -122,24 +125,25 @@ ssd_status ssd_chunk_state(const ssd_dims* dims, ssd_dtype dtype, int chunk_len,
                            const float* cs, float* states, void* stream);
 
 /* Stage 3 (same section, "Propagate states between chunks"): the sequential 1-SS scan
- * over chunks.  With E_0 = init_state (zeros if NULL),
+ * over chunks.  With E_0 = init_state (zeros if NULL), carried in fp32,
  *     entry_states[c] = E_c,   E_{c+1} = exp(cs[c][Q-1]) * E_c + states[c]
- * and final_state = E_nchunks (the state after the last step; NULL to skip).
- * entry_states may not alias states (SSD_ERR_DIMS).  init_state/final_state use the
- * [N][P] layout, states/entry_states the [P][N] one. */
-ssd_status ssd_state_passing(const ssd_dims* dims, int chunk_len, const float* states,
-                             const float* cs, const float* init_state, float* entry_states,
-                             float* final_state, void* stream);
+ * and final_state = E_nchunks (the state after the last step, fp32; NULL to skip).
+ * entry_states are written in `dtype` (bf16: rounded to nearest even).  entry_states may
+ * not alias states (SSD_ERR_DIMS).  init_state/final_state use the [N][P] layout,
+ * states/entry_states the [P][N] one. */
+ssd_status ssd_state_passing(const ssd_dims* dims, ssd_dtype dtype, int chunk_len,
+                             const float* states, const float* cs, const float* init_state,
+                             void* entry_states, float* final_state, void* stream);
 
 /* Stages 1, 4 and 5 (same section: intra-chunk outputs, inter-chunk outputs, combine):
  * for every position j of chunk c (t = cQ + j < T),
  *     y[b][t][h][p] = sum_{i <= j} (C_j . B_i) exp(cs[j] - cs[i]) dt_chunk[i] x[cQ+i][p]
  *                   + exp(cs[j]) sum_n C_j[n] entry_states[c][p][n]
  *                   + D[h] x[b][t][h][p]
- * with C_j = C[b][cQ+j][g], B_i = B[b][cQ+i][g]. */
+ * with C_j = C[b][cQ+j][g], B_i = B[b][cQ+i][g]; entry_states are read in `dtype`. */
 ssd_status ssd_chunk_scan(const ssd_dims* dims, ssd_dtype dtype, int chunk_len,
                           const void* x, const void* B, const void* C, const float* dt_chunk,
-                          const float* cs, const float* D, const float* entry_states, void* y,
+                          const float* cs, const float* D, const void* entry_states, void* y,
                           void* stream);
 
 #ifdef __cplusplus

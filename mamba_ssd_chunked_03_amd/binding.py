@@ -58,7 +58,7 @@ def library(path=LIB_PATH):
     lib.ssd_chunk_state.restype = i
     lib.ssd_chunk_state.argtypes = [dims, i, i, vp, vp, fp, fp, fp, vp]
     lib.ssd_state_passing.restype = i
-    lib.ssd_state_passing.argtypes = [dims, i, fp, fp, fp, fp, fp, vp]
+    lib.ssd_state_passing.argtypes = [dims, i, i, fp, fp, fp, vp, fp, vp]
     lib.ssd_chunk_scan.restype = i
     lib.ssd_chunk_scan.argtypes = [dims, i, i, vp, vp, vp, fp, fp, fp, fp, vp, vp]
     if path == LIB_PATH:
@@ -170,15 +170,17 @@ def ssd_chunk_state(dims, chunk_len, x, B, dt_chunk, cs, states=None, stream=Non
 
 
 def ssd_state_passing(dims, chunk_len, states, cs, init_state=None, entry_states=None,
-                      final_state=None, want_final=True, stream=None):
+                      final_state=None, want_final=True, entry_dtype=torch.float32, stream=None):
+    """Entry states come back in entry_dtype (fp32 or bf16); final_state is fp32."""
     dev = cs.device
     if entry_states is None:
-        entry_states = torch.empty(_state_shape(dims, chunk_len), dtype=torch.float32, device=dev)
+        entry_states = torch.empty(_state_shape(dims, chunk_len), dtype=entry_dtype, device=dev)
     if final_state is None and want_final:
         final_state = torch.empty((dims.batch, dims.nheads, dims.dstate, dims.headdim),
                                   dtype=torch.float32, device=dev)
-    _check(library().ssd_state_passing(ctypes.byref(dims), int(chunk_len), _ptr(states), _ptr(cs),
-                                       _ptr(init_state), _ptr(entry_states), _ptr(final_state),
+    _check(library().ssd_state_passing(ctypes.byref(dims), _DTYPE_CODE[entry_states.dtype],
+                                       int(chunk_len), _ptr(states), _ptr(cs), _ptr(init_state),
+                                       _ptr(entry_states), _ptr(final_state),
                                        _stream(dev, stream)))
     return entry_states, final_state
 

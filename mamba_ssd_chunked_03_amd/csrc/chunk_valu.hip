@@ -94,7 +94,7 @@ template <typename Tin>
 __global__ __launch_bounds__(kThreads) void chunk_scan_valu_kernel(
     const Tin* __restrict__ x, const Tin* __restrict__ Bm, const Tin* __restrict__ Cm,
     const float* __restrict__ dtc, const float* __restrict__ cs, const float* __restrict__ D,
-    const float* __restrict__ entry, Tin* __restrict__ y, int T, int H, int G, int P, int N,
+    const Tin* __restrict__ entry, Tin* __restrict__ y, int T, int H, int G, int P, int N,
     int Q, int nC) {
     __shared__ float gm[kRows][256];
     __shared__ float cj[kRows][256];
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_valu_kernel(
         gm[r][i] = v;
     }
     __syncthreads();
-    const float* E = entry + ((size_t)(b * H + h) * nC + c) * P * N;
+    const Tin* E = entry + ((size_t)(b * H + h) * nC + c) * P * N;
     const float dh = D[h];
     for (int e = threadIdx.x; e < kRows * P; e += kThreads) {
         const int r = e / P, p = e % P;
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_valu_kernel(
         for (int i = 0; i <= j; ++i)
             acc = fmaf(gm[r][i], to_f32(x[((size_t)(b * T + t0 + i) * H + h) * P + p]), acc);
         float off = 0.f;
-        for (int n = 0; n < N; ++n) off = fmaf(cj[r][n], E[(size_t)p * N + n], off);
+        for (int n = 0; n < N; ++n) off = fmaf(cj[r][n], to_f32(E[(size_t)p * N + n]), off);
         const float xv = to_f32(x[((size_t)(b * T + t) * H + h) * P + p]);
         acc += expf(cs[cbase + j]) * off + dh * xv;
         y[((size_t)(b * T + t) * H + h) * P + p] = from_f32<Tin>(acc);
@@ -169,16 +169,16 @@ hipError_t launch_chunk_state_valu(const Shape& s, ssd_dtype dt, const void* x, 
 
 hipError_t launch_chunk_scan_valu(const Shape& s, ssd_dtype dt, const void* x, const void* Bm,
                                   const void* Cm, const float* dtc, const float* cs,
-                                  const float* D, const float* entry, void* y, hipStream_t st) {
+                                  const float* D, const void* entry, void* y, hipStream_t st) {
     const unsigned blocks = (unsigned)((size_t)s.B * s.H * s.nC * (s.Q / kRows));
     if (blocks == 0) return hipSuccess;
     if (dt == SSD_F32)
         chunk_scan_valu_kernel<float><<<blocks, kThreads, 0, st>>>(
-            (const float*)x, (const float*)Bm, (const float*)Cm, dtc, cs, D, entry, (float*)y, s.T,
+            (const float*)x, (const float*)Bm, (const float*)Cm, dtc, cs, D, (const float*)entry, (float*)y, s.T,
             s.H, s.G, s.P, s.N, s.Q, s.nC);
     else
         chunk_scan_valu_kernel<__bf16><<<blocks, kThreads, 0, st>>>(
-            (const __bf16*)x, (const __bf16*)Bm, (const __bf16*)Cm, dtc, cs, D, entry, (__bf16*)y,
+            (const __bf16*)x, (const __bf16*)Bm, (const __bf16*)Cm, dtc, cs, D, (const __bf16*)entry, (__bf16*)y,
             s.T, s.H, s.G, s.P, s.N, s.Q, s.nC);
     return hipGetLastError();
 }

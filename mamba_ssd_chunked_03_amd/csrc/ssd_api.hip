@@ -50,7 +50,8 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Workspace {
-    float *dtc, *cs, *states, *entry;
+    float *dtc, *cs, *states;
+    void* entry;  // entry states, in the input dtype
 };
 
 size_t workspace_bytes(const Shape& s, Workspace* w, char* base) {
@@ -66,7 +67,7 @@ size_t workspace_bytes(const Shape& s, Workspace* w, char* base) {
     ws.dtc = take(chunk_elems * sizeof(float));
     ws.cs = take(chunk_elems * sizeof(float));
     ws.states = take(state_elems * sizeof(float));
-    ws.entry = take(state_elems * sizeof(float));
+    ws.entry = take(state_elems * sizeof(float));  // fp32 size: enough for either dtype
     if (w) *w = ws;
     return off;
 }
@@ -95,7 +96,7 @@ ssd_status run_chunk_state(const Shape& s, ssd_dtype dtype, const void* x, const
 
 ssd_status run_chunk_scan(const Shape& s, ssd_dtype dtype, const void* x, const void* B,
                           const void* C, const float* dtc, const float* cs, const float* D,
-                          const float* entry, void* y, hipStream_t st) {
+                          const void* entry, void* y, hipStream_t st) {
     if (dtype == SSD_BF16 && ssd::chunk_scan_mfma_supported(s))
         return hip_status(ssd::launch_chunk_scan_mfma(s, x, B, C, dtc, cs, D, entry, y, st));
     return hip_status(ssd::launch_chunk_scan_valu(s, dtype, x, B, C, dtc, cs, D, entry, y, st));
@@ -146,23 +147,24 @@ ssd_status ssd_chunk_state(const ssd_dims* dims, ssd_dtype dtype, int chunk_len,
     return run_chunk_state(s, dtype, x, B, dt_chunk, cs, states, (hipStream_t)stream);
 }
 
-ssd_status ssd_state_passing(const ssd_dims* dims, int chunk_len, const float* states,
-                             const float* cs, const float* init_state, float* entry_states,
-                             float* final_state, void* stream) {
+ssd_status ssd_state_passing(const ssd_dims* dims, ssd_dtype dtype, int chunk_len,
+                             const float* states, const float* cs, const float* init_state,
+                             void* entry_states, float* final_state, void* stream) {
     Shape s;
     ssd_status r = make_shape(dims, chunk_len, &s);
     if (r != SSD_OK) return r;
+    if (!valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
     if ((size_t)s.B * s.T > 0 && (!states || !cs || !entry_states)) return SSD_ERR_NULL;
     if (any_misaligned({states, cs, entry_states}) || any_misaligned4({init_state, final_state}))
         return SSD_ERR_ALIGN;
-    if (states && states == entry_states && s.nC > 0) return SSD_ERR_DIMS;
-    return hip_status(ssd::launch_state_passing(s, states, cs, init_state, entry_states,
+    if (states && (const void*)states == entry_states && s.nC > 0) return SSD_ERR_DIMS;
+    return hip_status(ssd::launch_state_passing(s, dtype, states, cs, init_state, entry_states,
                                                 final_state, (hipStream_t)stream));
 }
 
 ssd_status ssd_chunk_scan(const ssd_dims* dims, ssd_dtype dtype, int chunk_len, const void* x,
                           const void* B, const void* C, const float* dt_chunk, const float* cs,
-                          const float* D, const float* entry_states, void* y, void* stream) {
+                          const float* D, const void* entry_states, void* y, void* stream) {
     Shape s;
     ssd_status r = make_shape(dims, chunk_len, &s);
     if (r != SSD_OK) return r;
@@ -199,7 +201,7 @@ ssd_status ssd_fwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const f
         if (r != SSD_OK) return r;
     }
     // with T == 0 this only copies init_state (or zeros) to final_state
-    r = hip_status(ssd::launch_state_passing(s, ws.states, ws.cs, init_state, ws.entry,
+    r = hip_status(ssd::launch_state_passing(s, dtype, ws.states, ws.cs, init_state, ws.entry,
                                              final_state, st));
     if (r != SSD_OK || !has_tokens) return r;
     return run_chunk_scan(s, dtype, x, B, C, ws.dtc, ws.cs, D, ws.entry, y, st);

@@ -25,17 +25,19 @@ template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float v) { return
 // ---- launchers (each returns the launch status) -------------------------------------
 hipError_t launch_chunk_cumsum(const Shape& s, const float* dt, const float* A, float* dtc,
                                float* cs, hipStream_t st);
-hipError_t launch_state_passing(const Shape& s, const float* states, const float* cs,
-                                const float* init, float* entry, float* final_state,
-                                hipStream_t st);
+// entry states are written in entry_dtype (fp32 or bf16); the carried state is fp32
+hipError_t launch_state_passing(const Shape& s, ssd_dtype entry_dtype, const float* states,
+                                const float* cs, const float* init, void* entry,
+                                float* final_state, hipStream_t st);
 
 // Plain fp32-accumulate VALU kernels: any supported size, fp32 or bf16 inputs.
 hipError_t launch_chunk_state_valu(const Shape& s, ssd_dtype dt, const void* x, const void* Bm,
                                    const float* dtc, const float* cs, float* states,
                                    hipStream_t st);
+// entry states are read in the input dtype
 hipError_t launch_chunk_scan_valu(const Shape& s, ssd_dtype dt, const void* x, const void* Bm,
                                   const void* Cm, const float* dtc, const float* cs,
-                                  const float* D, const float* entry, void* y, hipStream_t st);
+                                  const float* D, const void* entry, void* y, hipStream_t st);
 
 // bf16 MFMA kernels (gfx950 v_mfma_f32_16x16x32_bf16); *_supported says whether a shape
 // has an instantiation.
@@ -46,6 +48,6 @@ hipError_t launch_chunk_state_mfma(const Shape& s, const void* x, const void* Bm
 bool chunk_scan_mfma_supported(const Shape& s);
 hipError_t launch_chunk_scan_mfma(const Shape& s, const void* x, const void* Bm, const void* Cm,
                                   const float* dtc, const float* cs, const float* D,
-                                  const float* entry, void* y, hipStream_t st);
+                                  const void* entry, void* y, hipStream_t st);
 
 }  // namespace ssd

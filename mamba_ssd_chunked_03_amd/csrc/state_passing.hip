@@ -26,9 +26,25 @@ __device__ __forceinline__ float4 fma4(float a, float4 s, float4 v) {
     return make_float4(fmaf(a, s.x, v.x), fmaf(a, s.y, v.y), fmaf(a, s.z, v.z), fmaf(a, s.w, v.w));
 }
 
+__device__ __forceinline__ void store4(float* dst, float4 v) {
+    *reinterpret_cast<float4*>(dst) = v;
+}
+__device__ __forceinline__ void store4(__bf16* dst, float4 v) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 o;
+    o[0] = (__bf16)v.x;
+    o[1] = (__bf16)v.y;
+    o[2] = (__bf16)v.z;
+    o[3] = (__bf16)v.w;
+    *reinterpret_cast<bf16x4*>(dst) = o;
+}
+
+// TE: element type of the entry states (fp32, or bf16 when the consumer is the bf16 MFMA
+// chunk scan, which rounds them to bf16 anyway); the running state stays fp32.
+template <typename TE>
 __global__ __launch_bounds__(kThreads) void state_passing_kernel(
     const float* __restrict__ states, const float* __restrict__ cs,
-    const float* __restrict__ init, float* __restrict__ entry, float* __restrict__ final_state,
+    const float* __restrict__ init, TE* __restrict__ entry, float* __restrict__ final_state,
     int nC, int Q, int P, int N, int tiles_per_state) {
     const int NP = N * P;
     const int bh = blockIdx.x / tiles_per_state;
@@ -57,13 +73,13 @@ __global__ __launch_bounds__(kThreads) void state_passing_kernel(
         }
 #pragma unroll
         for (int k = 0; k < kUnroll; ++k) {
-            *reinterpret_cast<float4*>(entry + base + (size_t)(c + k) * NP) = s;
+            store4(entry + base + (size_t)(c + k) * NP, s);
             s = fma4(expf(a[k]), s, v[k]);
         }
     }
     for (; c < nC; ++c) {
         const float4 v = *reinterpret_cast<const float4*>(states + base + (size_t)c * NP);
-        *reinterpret_cast<float4*>(entry + base + (size_t)c * NP) = s;
+        store4(entry + base + (size_t)c * NP, s);
         s = fma4(expf(csl[(size_t)c * Q]), s, v);
     }
     if (final_state) {
@@ -77,15 +93,19 @@ __global__ __launch_bounds__(kThreads) void state_passing_kernel(
 
 }  // namespace
 
-hipError_t launch_state_passing(const Shape& s, const float* states, const float* cs,
-                                const float* init, float* entry, float* final_state,
-                                hipStream_t st) {
+hipError_t launch_state_passing(const Shape& s, ssd_dtype entry_dtype, const float* states,
+                                const float* cs, const float* init, void* entry,
+                                float* final_state, hipStream_t st) {
     const int NP = s.N * s.P;
     const int tiles = (NP + kThreads * 4 - 1) / (kThreads * 4);
     const unsigned blocks = (unsigned)((size_t)s.B * s.H * tiles);
     if (blocks == 0) return hipSuccess;
-    state_passing_kernel<<<blocks, kThreads, 0, st>>>(states, cs, init, entry, final_state, s.nC,
-                                                     s.Q, s.P, s.N, tiles);
+    if (entry_dtype == SSD_BF16)
+        state_passing_kernel<__bf16><<<blocks, kThreads, 0, st>>>(
+            states, cs, init, (__bf16*)entry, final_state, s.nC, s.Q, s.P, s.N, tiles);
+    else
+        state_passing_kernel<float><<<blocks, kThreads, 0, st>>>(
+            states, cs, init, (float*)entry, final_state, s.nC, s.Q, s.P, s.N, tiles);
     return hipGetLastError();
 }
 

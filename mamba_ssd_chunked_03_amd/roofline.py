@@ -27,7 +27,8 @@ def kernel_costs(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len, dty
     e = 2 if dtype == "bf16" else 4
     nC = (T + Q - 1) // Q
     chunk_f32 = B * H * nC * Q * 4          # dt_chunk or cs
-    state_f32 = B * H * nC * P * N * 4      # chunk states or entry states
+    state_f32 = B * H * nC * P * N * 4      # chunk states (fp32)
+    entry = B * H * nC * P * N * e          # entry states, in the input dtype
     io_xy = B * T * H * P * e               # x or y
     io_bc = B * T * G * N * e               # B or C
     st1 = B * H * N * P * 4                 # init or final state
@@ -35,7 +36,7 @@ def kernel_costs(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len, dty
     state = KernelCost("chunk_state", io_xy + io_bc + 2 * chunk_f32 + state_f32,
                        2.0 * B * H * T * N * P)
     passing = KernelCost("state_passing",
-                         2 * state_f32 + B * H * nC * 4 + (st1 if init_state else 0)
+                         state_f32 + entry + B * H * nC * 4 + (st1 if init_state else 0)
                          + (st1 if final_state else 0),
                          2.0 * B * H * nC * N * P)
     # intra-chunk: sum over rows j of (j+1) MACs x P, per (b, h, chunk); C B^T likewise
@@ -43,7 +44,7 @@ def kernel_costs(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len, dty
     full, rem = divmod(T, Q)
     tri = full * Q * (Q + 1) + rem * (rem + 1)          # sum of 2*(j+1) over valid rows
     scan = KernelCost("chunk_scan",
-                      2 * io_xy + 2 * io_bc + 2 * chunk_f32 + state_f32 + H * 4,
+                      2 * io_xy + 2 * io_bc + 2 * chunk_f32 + entry + H * 4,
                       B * H * tri * P + B * G * tri * N + 2.0 * B * H * T * N * P)
     return [cumsum, state, passing, scan]
 

@@ -91,8 +91,12 @@ def test_validation_errors_before_any_launch(lib):
     assert lib.ssd_chunk_cumsum(ctypes.byref(D(p=40)), 64, None, None, None, None, None) == 3
     assert lib.ssd_chunk_cumsum(ctypes.byref(D()), 64, None, None, None, None, None) == 1
     assert lib.ssd_chunk_state(ctypes.byref(D()), 1, 64, None, None, None, None, None, None) == 1
-    assert lib.ssd_state_passing(ctypes.byref(D()), 64, ctypes.c_void_p(64), ctypes.c_void_p(64),
-                                 None, ctypes.c_void_p(64), None, None) == 2   # aliasing
+    assert lib.ssd_state_passing(ctypes.byref(D()), 0, 64, ctypes.c_void_p(64),
+                                 ctypes.c_void_p(64), None, ctypes.c_void_p(64), None,
+                                 None) == 2   # aliasing
+    assert lib.ssd_state_passing(ctypes.byref(D()), 5, 64, ctypes.c_void_p(64),
+                                 ctypes.c_void_p(64), None, ctypes.c_void_p(128), None,
+                                 None) == 3   # dtype
     assert lib.ssd_chunk_scan(ctypes.byref(D()), 1, 128, None, None, None, None, None, None,
                               None, None, None) == 1
     assert lib.ssd_fwd(None, 0, None, None, None, None, None, None, 64, None, None, None, None,

@@ -129,12 +129,15 @@ def test_stage_state_passing(w):
     S_d = torch.from_numpy(S.swapaxes(-1, -2).copy()).float().to(dev)
     cs_d = torch.from_numpy(cs).float().to(dev)
     init = None if cpu["init_state"] is None else cpu["init_state"].to(dev)
-    ent, fin = binding.ssd_state_passing(_dims(w), w.chunk_len, S_d, cs_d, init_state=init)
+    ent, fin = binding.ssd_state_passing(_dims(w), w.chunk_len, S_d, cs_d, init_state=init,
+                                         entry_dtype=cpu["x"].dtype)
     torch.cuda.synchronize()
     e1 = rel_l2(np64(ent).swapaxes(-1, -2), ent_ref)
     e2 = rel_l2(np64(fin), fin_ref)
     say(f"    rel_l2 entry={e1:.3e} final={e2:.3e}")
-    assert e1 <= 1e-5 and e2 <= 1e-5
+    # entry states carried in fp32, stored in the input dtype (bf16 adds one rounding)
+    assert e1 <= (1e-5 if w.dtype == "fp32" else 4e-3)
+    assert e2 <= 1e-5
 
 
 @pytest.mark.parametrize("w", STAGE_CASES, ids=[w.name for w in STAGE_CASES])
@@ -152,7 +155,7 @@ def test_stage_chunk_scan(w):
     d = _dims(w)
     dtc, _ = binding.ssd_chunk_cumsum(d, w.chunk_len, dv["dt"], dv["A"])
     cs_d = torch.from_numpy(cs).float().cuda()
-    ent_d = torch.from_numpy(ent.swapaxes(-1, -2).copy()).float().cuda()
+    ent_d = torch.from_numpy(ent.swapaxes(-1, -2).copy()).to(cpu["x"].dtype).cuda()
     y = binding.ssd_chunk_scan(d, w.chunk_len, dv["x"], dv["B"], dv["C"], dtc, cs_d, dv["D"], ent_d)
     torch.cuda.synchronize()
     e = rel_l2(np64(y), y_ref)
