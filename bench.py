@@ -134,8 +134,9 @@ def main():
     state_n = w.batch * w.nheads * nC * w.headdim * w.dstate
     rnd = lambda b: (b + 255) // 256 * 256
     offs = [0]
-    for nbytes in (chunk_n * 4, chunk_n * 4, state_n * 4):
+    for nbytes in (chunk_n * 4, chunk_n * 4, state_n * 4, state_n * 4):
         offs.append(offs[-1] + rnd(nbytes))
+    gram_n = binding.ssd_chunk_gram_size(dims, d_in["x"].dtype, Q)
     def view(off, n, shape, dtype=f32):
         esz = torch.tensor([], dtype=dtype).element_size()
         return ws[off:off + n * esz].view(dtype).view(shape)
@@ -144,6 +145,7 @@ def main():
     dtc, cs = view(offs[0], chunk_n, cshape), view(offs[1], chunk_n, cshape)
     S = view(offs[2], state_n, sshape)
     E = view(offs[3], state_n, sshape, d_in["x"].dtype)   # entry states in the input dtype
+    gram = ws[offs[4]:offs[4] + gram_n]                     # C B^T blocks (bf16 path)
 
     def fwd():
         binding.ssd_fwd(d_in["x"], d_in["dt"], d_in["A"], d_in["B"], d_in["C"], d_in["D"], Q,
@@ -158,15 +160,18 @@ def main():
         binding.ssd_state_passing(dims, Q, S, cs, init_state=d_in["init_state"],
                                   entry_states=E, final_state=fin)
         ev[3].record()
-        binding.ssd_chunk_scan(dims, Q, d_in["x"], d_in["B"], d_in["C"], dtc, cs, d_in["D"], E, y=y)
+        binding.ssd_chunk_gram(dims, Q, d_in["B"], d_in["C"], gram)
         ev[4].record()
+        binding.ssd_chunk_scan(dims, Q, d_in["x"], d_in["B"], d_in["C"], dtc, cs, d_in["D"], E,
+                               gram=gram, y=y)
+        ev[5].record()
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         fwd()
     torch.cuda.synchronize()
     y_ref = y.clone()
-    ev_steps = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    ev_steps = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -179,14 +184,16 @@ def main():
     if not torch.isfinite(y.float()).all():
         log("[bench] WARNING: non-finite output")
 
-    names = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_scan"]
+    names = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_gram", "chunk_scan"]
     per = {n: 0.0 for n in names}
     for ev in ev_steps:
         for i, n in enumerate(names):
             per[n] += ev[i].elapsed_time(ev[i + 1]) / args.steps   # ms
     costs = {c.name: c for c in roofline.kernel_costs(
         w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, Q, w.dtype,
-        init_state=w.init_state, final_state=True)}
+        init_state=w.init_state, final_state=True, gram_bytes=gram_n)}
+    if "chunk_gram" not in costs:   # no separate gram launch on this path
+        names.remove("chunk_gram")
     kernels = {}
     for n in names:
         t = per[n] * 1e-3

@@ -19,6 +19,8 @@
  *   ssd_chunk_cumsum   stage 0: chunk-local inclusive prefix sums of dt*A (log decays)
  *   ssd_chunk_state    stage 2: every chunk's final state from a zero start
  *   ssd_state_passing  stage 3: the 1-SS scan over chunks that carries states across them
+ *   ssd_chunk_gram     stage 1, first half: the causal blocks of C B^T of every chunk,
+ *                      once per group (bf16 MFMA path only; a no-op elsewhere)
  *   ssd_chunk_scan     stages 1, 4, 5: the masked quadratic form inside each chunk plus
  *                      the carried state read out by C, plus the D skip
  *
@@ -89,8 +91,8 @@ typedef struct {
 const char* ssd_status_string(ssd_status status);
 
 /* Bytes of device workspace ssd_fwd needs for these sizes, for either dtype (0 if the
- * sizes are invalid).  It holds dt_chunk, cs, the chunk states and the entry states, each
- * 256-byte aligned, in that order. */
+ * sizes are invalid).  It holds dt_chunk, cs, the chunk states, the entry states and the
+ * C B^T blocks (ssd_chunk_gram_size for SSD_BF16), each 256-byte aligned, in that order. */
 size_t ssd_fwd_workspace_size(const ssd_dims* dims, int chunk_len);
 
 /* The whole SSD forward: y and (optionally) final_state from x, dt, A, B, C, D and an
@@ -135,16 +137,36 @@ ssd_status ssd_state_passing(const ssd_dims* dims, ssd_dtype dtype, int chunk_le
                              const float* states, const float* cs, const float* init_state,
                              void* entry_states, float* final_state, void* stream);
 
+/* Bytes of the `gram` buffer that ssd_chunk_gram fills and ssd_chunk_scan reads for these
+ * sizes and dtype; 0 where the chunk scan does not use one (SSD_F32, or invalid sizes). */
+size_t ssd_chunk_gram_size(const ssd_dims* dims, ssd_dtype dtype, int chunk_len);
+
+/* Stage 1, first half (same section, "Compute the diagonal blocks", and summary section
+ * "The Mamba-2 Architecture": B and C are shared by the heads of a group, so C B^T is
+ * too): for every (b, g, chunk c), the causal 32 x 32 blocks (row block >= column block)
+ * of the chunk's Q x Q matrix G[j][i] = C_j . B_i, rounded to bf16, with rows and
+ * columns past the end of a partial chunk set to zero.  The buffer's layout is private to
+ * the library: it holds the blocks as the chunk scan's matrix-core operands, is
+ * ssd_chunk_gram_size bytes long and is only meant to be passed to ssd_chunk_scan with
+ * the same dims, dtype and chunk_len.  With no gram buffer for these sizes (size 0) the
+ * call does nothing and returns SSD_OK; otherwise B, C and gram must be non-NULL and
+ * 16-byte aligned. */
+ssd_status ssd_chunk_gram(const ssd_dims* dims, ssd_dtype dtype, int chunk_len,
+                          const void* B, const void* C, void* gram, void* stream);
+
 /* Stages 1, 4 and 5 (same section: intra-chunk outputs, inter-chunk outputs, combine):
  * for every position j of chunk c (t = cQ + j < T),
  *     y[b][t][h][p] = sum_{i <= j} (C_j . B_i) exp(cs[j] - cs[i]) dt_chunk[i] x[cQ+i][p]
  *                   + exp(cs[j]) sum_n C_j[n] entry_states[c][p][n]
  *                   + D[h] x[b][t][h][p]
- * with C_j = C[b][cQ+j][g], B_i = B[b][cQ+i][g]; entry_states are read in `dtype`. */
+ * with C_j = C[b][cQ+j][g], B_i = B[b][cQ+i][g]; entry_states are read in `dtype`.
+ * gram is the buffer ssd_chunk_gram filled from the same B and C (the bf16 path takes
+ * C_j . B_i from it, rounded to bf16, and does not read B); where
+ * ssd_chunk_gram_size is 0 it is ignored and may be NULL. */
 ssd_status ssd_chunk_scan(const ssd_dims* dims, ssd_dtype dtype, int chunk_len,
                           const void* x, const void* B, const void* C, const float* dt_chunk,
-                          const float* cs, const float* D, const void* entry_states, void* y,
-                          void* stream);
+                          const float* cs, const float* D, const void* entry_states,
+                          const void* gram, void* y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -15,7 +15,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd.so")
 SSD_F32, SSD_BF16 = 0, 1
 _DTYPE_CODE = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}
 EXPORTED = ("ssd_status_string", "ssd_fwd_workspace_size", "ssd_fwd", "ssd_chunk_cumsum",
-            "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan")
+            "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_gram_size", "ssd_chunk_gram",
+            "ssd_chunk_scan")
 
 
 class SsdDims(ctypes.Structure):
@@ -59,8 +60,12 @@ def library(path=LIB_PATH):
     lib.ssd_chunk_state.argtypes = [dims, i, i, vp, vp, fp, fp, fp, vp]
     lib.ssd_state_passing.restype = i
     lib.ssd_state_passing.argtypes = [dims, i, i, fp, fp, fp, vp, fp, vp]
+    lib.ssd_chunk_gram_size.restype = sz
+    lib.ssd_chunk_gram_size.argtypes = [dims, i, i]
+    lib.ssd_chunk_gram.restype = i
+    lib.ssd_chunk_gram.argtypes = [dims, i, i, vp, vp, vp, vp]
     lib.ssd_chunk_scan.restype = i
-    lib.ssd_chunk_scan.argtypes = [dims, i, i, vp, vp, vp, fp, fp, fp, fp, vp, vp]
+    lib.ssd_chunk_scan.argtypes = [dims, i, i, vp, vp, vp, fp, fp, fp, vp, vp, vp, vp]
     if path == LIB_PATH:
         _LIB = lib
     return lib
@@ -185,10 +190,31 @@ def ssd_state_passing(dims, chunk_len, states, cs, init_state=None, entry_states
     return entry_states, final_state
 
 
-def ssd_chunk_scan(dims, chunk_len, x, B, C, dt_chunk, cs, D, entry_states, y=None, stream=None):
+def ssd_chunk_gram_size(dims, dtype, chunk_len):
+    return int(library().ssd_chunk_gram_size(ctypes.byref(dims), _DTYPE_CODE[dtype],
+                                             int(chunk_len)))
+
+
+def ssd_chunk_gram(dims, chunk_len, B, C, gram=None, stream=None):
+    """The C B^T blocks ssd_chunk_scan reads (a uint8 buffer; empty where none is used)."""
+    dev = B.device
+    if gram is None:
+        gram = torch.empty(ssd_chunk_gram_size(dims, B.dtype, chunk_len), dtype=torch.uint8,
+                           device=dev)
+    _check(library().ssd_chunk_gram(ctypes.byref(dims), _DTYPE_CODE[B.dtype], int(chunk_len),
+                                    _ptr(B), _ptr(C), _ptr(gram) if gram.numel() else None,
+                                    _stream(dev, stream)))
+    return gram
+
+
+def ssd_chunk_scan(dims, chunk_len, x, B, C, dt_chunk, cs, D, entry_states, gram=None, y=None,
+                   stream=None):
+    """gram: the buffer ssd_chunk_gram filled from the same B and C (needed where
+    ssd_chunk_gram_size is non-zero)."""
     dev = x.device
     y = torch.empty_like(x) if y is None else y
+    gp = _ptr(gram) if gram is not None and gram.numel() else None
     _check(library().ssd_chunk_scan(ctypes.byref(dims), _DTYPE_CODE[x.dtype], int(chunk_len),
                                     _ptr(x), _ptr(B), _ptr(C), _ptr(dt_chunk), _ptr(cs), _ptr(D),
-                                    _ptr(entry_states), _ptr(y), _stream(dev, stream)))
+                                    _ptr(entry_states), gp, _ptr(y), _stream(dev, stream)))
     return y

@@ -1,0 +1,499 @@
+// chunk_scan_mfma.hip -- stages 1, 4 and 5 of the block decomposition on gfx950 bf16 MFMA.
+//
+// Summary of arXiv 2405.21060, section "The Block-Decomposition SSD Algorithm": inside a
+// chunk the output is the quadratic (attention-like) form of the dual, Y = (L o C B^T) X
+// (section "The Scalar-Identity SSM", equation 16); the state carried into the chunk is
+// read out by C and decayed (stage 4); the two add up (stage 5).  Per chunk row j and
+// head h, with cs the chunk-local prefix sums of dt*A:
+//     y[j] = sum_{i<=j} (C_j . B_i) exp(cs_j - cs_i) dt_i x[i] + exp(cs_j) C_j . E + D x[j]
+//
+// Two kernels:
+//   chunk_gram   C B^T once per (batch, group, chunk): the heads of a group share B and C
+//                (summary section "The Mamba-2 Architecture", head patterns), so the Gram
+//                blocks are computed once and kept, rounded to bf16, in a small workspace
+//                laid out as the per-lane MFMA fragments the scan consumes.
+//   chunk_scan   persistent: a workgroup per CU walks a run of (batch, head, chunk) items
+//                with a double-buffered LDS, copying the next item's x and entry state
+//                from HBM while it computes the current one (details at the kernel).  The
+//                MFMA operands that run over time come out of LDS through transpose reads;
+//                the output is kept transposed, Y^T[p][j], so the Gram block for (row
+//                tile, 32-step block), masked and decayed in registers, is directly the B
+//                operand of X^T Gm^T.  The decay is masked before exponentiation (never a
+//                positive exponent); blocks wholly below a tile factor it at the block end
+//                e as exp(cs_j - cs_e) exp(cs_e - cs_i), both factors <= 1, so they need
+//                one exp per lane instead of one per element.
+#include "mfma_common.h"
+#include "ssd_internal.h"
+
+namespace ssd {
+namespace {
+
+using namespace mfma;
+
+// pair index of (16-row tile t, 32-step block ib <= t/2) in tile-major order
+__host__ __device__ constexpr int pair_base(int t) {
+    return (t & 1) ? (t / 2 + 1) * (t / 2 + 1) : (t / 2) * (t / 2 + 1);
+}
+__host__ __device__ constexpr int npairs(int Q) { return pair_base(Q / 16); }
+
+
+// ============================================================================ chunk_gram
+// gram[unit][pair][lane] (16 bytes): for lane l of tile t, block ib, column j = 16t + l%16
+// and g = l/16, the bf16 values C_j . B_i for i = 32ib + 4g + {0..3}, 32ib + 16 + 4g + {0..3}.
+// One wave per (unit, pair): all of its loads are independent and issued together.
+template <int Q, int N>
+__global__ __launch_bounds__(256) void chunk_gram_kernel(const __bf16* __restrict__ Bm,
+                                                         const __bf16* __restrict__ Cm,
+                                                         uint4* __restrict__ gram, int T, int G,
+                                                         int nC) {
+    constexpr int NK = N / 32;
+    constexpr int WPU = (npairs(Q) + 3) / 4;  // workgroups per unit
+    const int unit = blockIdx.x / WPU;
+    const int pr = (blockIdx.x % WPU) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (pr >= npairs(Q)) return;  // whole wave
+    int t = 0;
+    while (pair_base(t + 1) <= pr) ++t;
+    const int ib = pr - pair_base(t);
+    const int c = unit % nC;
+    const int b = unit / nC / G;
+    const int g = (unit / nC) % G;
+    const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int t0 = c * Q;
+    const int Lc = min(Q, T - t0);
+    const unsigned rowb = (unsigned)(G * N * 2);
+    const size_t base = ((size_t)(b * T + t0) * G + g) * N;
+    const __amdgpu_buffer_rsrc_t br = make_rsrc(Bm + base, (unsigned)Lc * rowb);
+    const __amdgpu_buffer_rsrc_t cr = make_rsrc(Cm + base, (unsigned)Lc * rowb);
+    const unsigned jrow = (unsigned)(t * 16 + l16) * rowb;
+    const unsigned irow = (unsigned)(ib * KB + l16) * rowb;
+    bf16x8 cf[NK], b0[NK], b1[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+        const unsigned col = (32 * kk + 8 * g4) * 2u;
+        cf[kk] = __builtin_bit_cast(bf16x8, buf_load16(cr, jrow + col));
+        b0[kk] = __builtin_bit_cast(bf16x8, buf_load16(br, irow + col));
+        b1[kk] = __builtin_bit_cast(bf16x8, buf_load16(br, irow + 16 * rowb + col));
+    }
+    f32x4 g0 = f32x4{0.f, 0.f, 0.f, 0.f}, g1 = g0;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+        g0 = mfma16(b0[kk], cf[kk], g0);
+        g1 = mfma16(b1[kk], cf[kk], g1);
+    }
+    gram[((size_t)unit * npairs(Q) + pr) * 64 + lane] =
+        make_uint4(pack_bf16(g0[0], g0[1]), pack_bf16(g0[2], g0[3]), pack_bf16(g1[0], g1[1]),
+                   pack_bf16(g1[2], g1[3]));
+}
+
+// ============================================================================ chunk_scan
+// Persistent and software-pipelined: each workgroup walks a contiguous run of (unit, head)
+// items, consecutive heads of one unit first.  Wave w of the NT/2 waves owns the 16-row
+// tiles w and NT-1-w (the same share of the causal triangle for every wave).  While the
+// unit stays the same, a wave keeps its tiles' C rows and Gram fragments in registers, so
+// the compute needs no global loads at all; meanwhile the next item's x, entry state, cs
+// and dt are copied from HBM into the other half of a double-buffered LDS.  The copies are
+// issued through inline asm so that the compiler does not make later LDS reads wait for
+// them; the one wait that is needed (the next item's copies, not the stores of the item
+// just finished) is explicit: vector memory operations complete in issue order, so waiting
+// until only this item's stores are outstanding means that everything before them landed.
+template <int Q, int N, int P>
+struct ScanCfg {
+    static constexpr int NT = Q / 16;   // 16-row tiles per chunk
+    static constexpr int NW = NT / 2;   // waves per workgroup
+    static constexpr int NTH = NW * 64;
+    static constexpr int NB = Q / KB;   // 32-step blocks per chunk
+    static constexpr int NB0 = NT / 4;  // most blocks the first tile of a wave has
+    static constexpr int PT = P / 16, NK = N / 32, PPR = P / 8, NPR = N / 8;
+    static constexpr unsigned XB = Q * P * 2, EB = P * N * 2, FB = Q * 4;
+    static constexpr unsigned ITEM = XB + EB + 2 * FB;  // x, entry state, cs, dt
+    static constexpr unsigned TAIL = 2 * FB;            // cs*log2(e), block-end weights
+    static constexpr int NBUF = (2 * ITEM + TAIL <= 160u * 1024u) ? 2 : 1;
+    static constexpr unsigned LDS = NBUF * ITEM + TAIL;
+    static constexpr int STORES = 2 * PT;  // y stores per wave per item
+};
+
+// 16 bytes per lane from a buffer resource into LDS at lds + 16 * lane (opaque to the
+// compiler's wait-count tracking; callers wait explicitly)
+__device__ __forceinline__ void dma16(u32x4 r, uint32_t lds, uint32_t voff) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(lds)
+                 : "memory");
+}
+// raw buffer resource words: base, stride 0, size in bytes (reads past it return zeros)
+__device__ __forceinline__ u32x4 raw_rsrc(const void* base, unsigned bytes) {
+    const uint64_t a = (uint64_t)base;
+    return u32x4{(unsigned)a, (unsigned)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+template <int Q, int N, int P>
+__device__ __forceinline__ void issue_item(const __bf16* x, const __bf16* E, const float* cs,
+                                           const float* dtc, int slot, int hpg, int T, int H,
+                                           int G, int nC, uint32_t lds, int wave, int lane) {
+    using C_ = ScanCfg<Q, N, P>;
+    const int unit = slot / hpg;
+    const int c = unit % nC, g = (unit / nC) % G, b = unit / nC / G;
+    const int h = g * hpg + slot % hpg;
+    const int Lc = min(Q, T - c * Q);
+    const unsigned rowb = (unsigned)(H * P * 2);
+    const u32x4 xr = raw_rsrc(x + ((size_t)(b * T + c * Q) * H + h) * P, (unsigned)Lc * rowb);
+    constexpr int XI = Q * C_::PPR / 64;
+#pragma unroll
+    for (int k = wave; k < XI; k += C_::NW) {
+        const int m = k * 64 + lane;  // LDS piece
+        const int r = m / C_::PPR, sl = m % C_::PPR;
+        dma16(xr, lds + k * 1024, (unsigned)r * rowb + (unsigned)(sl ^ (r & (C_::PPR - 1))) * 16u);
+    }
+    const size_t sb = (size_t)(b * H + h) * nC + c;
+    const u32x4 er = raw_rsrc(E + sb * P * N, C_::EB);
+    constexpr int EI = P * C_::NPR / 64;
+#pragma unroll
+    for (int k = wave; k < EI; k += C_::NW) {
+        const int m = k * 64 + lane;
+        const int p = m / C_::NPR, sl = m % C_::NPR;
+        dma16(er, lds + C_::XB + k * 1024,
+              (unsigned)(p * N + (sl ^ (p & (C_::NPR - 1))) * 8) * 2u);
+    }
+    if (wave == 0 && lane < Q / 4)
+        dma16(raw_rsrc(cs + sb * Q, C_::FB), lds + C_::XB + C_::EB, lane * 16u);
+    if (wave == (C_::NW > 1 ? 1 : 0) && lane < Q / 4)
+        dma16(raw_rsrc(dtc + sb * Q, C_::FB), lds + C_::XB + C_::EB + C_::FB, lane * 16u);
+}
+
+template <int Q, int N, int P>
+__global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kernel(
+    const __bf16* __restrict__ x, const __bf16* __restrict__ Cm, const float* __restrict__ dtc,
+    const float* __restrict__ cs, const float* __restrict__ D, const __bf16* __restrict__ E,
+    const uint4* __restrict__ gram, __bf16* __restrict__ y, int T, int H, int G, int nC,
+    int nslots) {
+    using C_ = ScanCfg<Q, N, P>;
+    constexpr int PT = C_::PT, NK = C_::NK, PPR = C_::PPR, NPR = C_::NPR, NB = C_::NB,
+                  NB0 = C_::NB0;
+    static_assert(N % 32 == 0 && P % 16 == 0 && Q % 64 == 0, "tile shape");
+    extern __shared__ __align__(16) unsigned char smem[];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+    float* s_c2 = reinterpret_cast<float*>(smem + C_::NBUF * C_::ITEM);
+    float* s_v = s_c2 + Q;  // exp(cs_e - cs_i) dt_i, e = end of i's block
+
+    // this workgroup's items: a contiguous run, neighbouring runs on the same XCD (the GPU
+    // deals consecutive workgroups round-robin to its 8 XCDs)
+    const int nwg = gridDim.x;
+    const int wp = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+    const int per = (nslots + nwg - 1) / nwg;
+    const int lo = wp * per, hi = min(nslots, lo + per);
+    if (lo >= hi) return;  // whole workgroup
+
+    const int hpg = H / G;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int tile0 = wave, tile1 = C_::NT - 1 - wave;
+    const int nblk0 = tile0 / 2 + 1, nblk1 = tile1 / 2 + 1;
+    const int j0 = tile0 * 16 + l16, j1 = tile1 * 16 + l16;
+    const unsigned rowb = (unsigned)(H * P * 2);
+    const unsigned crow = (unsigned)(G * N * 2);
+
+    // loop-invariant LDS offsets inside one buffer.  x^T operand of block ib: rows
+    // 32 ib + 4 g4 + l16 / 4 (and + 16), column p * 16 + 4 (l16 % 4); the swizzle depends
+    // only on the row mod PPR, which a whole block does not change.
+    unsigned xoff[PT];
+#pragma unroll
+    for (int p = 0; p < PT; ++p) xoff[p] = swz_off(4 * g4 + (l16 >> 2), p * 16 + 4 * (l16 & 3), PPR);
+    constexpr unsigned XBLK = KB * PPR * 16;   // bytes of 32 rows of x
+    constexpr unsigned XHALF = 16 * PPR * 16;  // bytes of 16 rows
+
+    bf16x8 cf0[NK], cf1[NK];  // C rows j0, j1 of the current unit
+    uint4 gf0[NB0], gf1[NB];  // Gram fragments of (tile0, ib), (tile1, ib)
+    int cur_unit = -1;
+
+    issue_item<Q, N, P>(x, E, cs, dtc, lo, hpg, T, H, G, nC, lds0, wave, lane);
+#pragma unroll 1
+    for (int sl = lo; sl < hi; ++sl) {
+        const int n = sl - lo;
+        const int buf = (C_::NBUF == 2) ? (n & 1) : 0;
+        unsigned char* bx = smem + buf * C_::ITEM;
+        const float* b_cs = reinterpret_cast<const float*>(bx + C_::XB + C_::EB);
+        const float* b_dt = b_cs + Q;
+        // this item's copies have landed once only the previous item's stores are pending
+        if (n == 0 || C_::NBUF == 1)
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::STORES) : "memory");
+
+        const int unit = sl / hpg;
+        const int c = unit % nC, g = (unit / nC) % G, b = unit / nC / G;
+        const int h = g * hpg + sl % hpg;
+        const int t0 = c * Q;
+        const int Lc = min(Q, T - t0);
+        if (tid < Q) {
+            const float ci = b_cs[tid];
+            s_c2[tid] = ci * kLog2e;
+            s_v[tid] = exp2_fast((b_cs[tid | (KB - 1)] - ci) * kLog2e) * b_dt[tid];
+        }
+        if (unit != cur_unit) {  // C rows and Gram fragments of the new unit
+            cur_unit = unit;
+            const __amdgpu_buffer_rsrc_t cr =
+                make_rsrc(Cm + ((size_t)(b * T + t0) * G + g) * N, (unsigned)Lc * crow);
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                const unsigned col = (32 * kk + 8 * g4) * 2u;
+                cf0[kk] = __builtin_bit_cast(bf16x8, buf_load16(cr, (unsigned)j0 * crow + col));
+                cf1[kk] = __builtin_bit_cast(bf16x8, buf_load16(cr, (unsigned)j1 * crow + col));
+            }
+            // fragments past a tile's last block read outside the buffer: zeros
+            const __amdgpu_buffer_rsrc_t gr = make_rsrc(
+                gram + (size_t)unit * npairs(Q) * 64, (unsigned)(npairs(Q) * 64 * 16));
+            const unsigned go0 = (unsigned)(pair_base(tile0) * 64 + lane) * 16u;
+            const unsigned go1 = (unsigned)(pair_base(tile1) * 64 + lane) * 16u;
+#pragma unroll
+            for (int i = 0; i < NB0; ++i)
+                gf0[i] = buf_load16(gr, i < nblk0 ? go0 + i * 1024u : 0x40000000u);
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+                gf1[i] = buf_load16(gr, i < nblk1 ? go1 + i * 1024u : 0x40000000u);
+            // wait here (vmcnt 0, as a compiler-visible wait) rather than at each first use,
+            // where the wait would also cover the next item's copies issued below
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+        }
+        lds_barrier();
+        if (C_::NBUF == 2 && sl + 1 < hi)
+            issue_item<Q, N, P>(x, E, cs, dtc, sl + 1, hpg, T, H, G, nC,
+                                lds0 + (buf ^ 1) * C_::ITEM, wave, lane);
+
+        // stage 4: the entry state read out by C, then decayed from the chunk start
+        f32x4 acc0[PT], acc1[PT];
+#pragma unroll
+        for (int p = 0; p < PT; ++p) acc0[p] = acc1[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const unsigned char* be = bx + C_::XB;
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+#pragma unroll
+            for (int p = 0; p < PT; ++p) {
+                const bf16x8 ea = *reinterpret_cast<const bf16x8*>(
+                    be + swz_off(p * 16 + l16, 32 * kk + 8 * g4, NPR));
+                acc0[p] = mfma16(ea, cf0[kk], acc0[p]);
+                acc1[p] = mfma16(ea, cf1[kk], acc1[p]);
+            }
+        }
+        const float csj0 = s_c2[j0], csj1 = s_c2[j1];
+        {
+            const float sc0 = exp2_fast(csj0), sc1 = exp2_fast(csj1);
+#pragma unroll
+            for (int p = 0; p < PT; ++p) {
+                acc0[p] *= sc0;
+                acc1[p] *= sc1;
+            }
+        }
+
+        // stage 1: masked quadratic form, one 32-step block at a time
+#pragma unroll
+        for (int ib = 0; ib < NB; ++ib) {
+            if (ib >= nblk1) break;  // nblk1 >= nblk0
+            bf16x8 xa[PT];
+#pragma unroll
+            for (int p = 0; p < PT; ++p) {
+                const unsigned char* xp = bx + xoff[p] + ib * XBLK;
+                const uint2 lo2 = lds_read_tr16(xp);
+                const uint2 hi2 = lds_read_tr16(xp + XHALF);
+                xa[p] = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+            }
+            const int i0 = ib * KB + 4 * g4;
+            // masked, decayed Gram block of one tile -> MFMA operand
+            auto block = [&](const uint4 gv4, int nblk, int j, float csj) -> bf16x8 {
+                float m[8];
+                if (ib < nblk - 1) {  // wholly below the tile: decay factored at block end
+                    const float f = exp2_fast(csj - s_c2[ib * KB + KB - 1]);
+                    const float4 va = *reinterpret_cast<const float4*>(&s_v[i0]);
+                    const float4 vb = *reinterpret_cast<const float4*>(&s_v[i0 + 16]);
+                    m[0] = bf16_lo(gv4.x) * (va.x * f); m[1] = bf16_hi(gv4.x) * (va.y * f);
+                    m[2] = bf16_lo(gv4.y) * (va.z * f); m[3] = bf16_hi(gv4.y) * (va.w * f);
+                    m[4] = bf16_lo(gv4.z) * (vb.x * f); m[5] = bf16_hi(gv4.z) * (vb.y * f);
+                    m[6] = bf16_lo(gv4.w) * (vb.z * f); m[7] = bf16_hi(gv4.w) * (vb.w * f);
+                } else {  // the diagonal block: mask above the diagonal through the exponent
+                    const float4 ca = *reinterpret_cast<const float4*>(&s_c2[i0]);
+                    const float4 cb = *reinterpret_cast<const float4*>(&s_c2[i0 + 16]);
+                    const float4 da = *reinterpret_cast<const float4*>(&b_dt[i0]);
+                    const float4 db = *reinterpret_cast<const float4*>(&b_dt[i0 + 16]);
+                    const float cav[4] = {ca.x, ca.y, ca.z, ca.w}, cbv[4] = {cb.x, cb.y, cb.z, cb.w};
+                    const float dav[4] = {da.x, da.y, da.z, da.w}, dbv[4] = {db.x, db.y, db.z, db.w};
+                    const float gv[8] = {bf16_lo(gv4.x), bf16_hi(gv4.x), bf16_lo(gv4.y),
+                                         bf16_hi(gv4.y), bf16_lo(gv4.z), bf16_hi(gv4.z),
+                                         bf16_lo(gv4.w), bf16_hi(gv4.w)};
+                    const float ninf = -__builtin_inff();
+                    const int jr = j - i0;  // k-slot q is at or below the diagonal iff q <= jr
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float ea = q <= jr ? csj - cav[q] : ninf;
+                        const float ec = 16 + q <= jr ? csj - cbv[q] : ninf;
+                        m[q] = gv[q] * exp2_fast(ea) * dav[q];
+                        m[4 + q] = gv[4 + q] * exp2_fast(ec) * dbv[q];
+                    }
+                }
+                return __builtin_bit_cast(
+                    bf16x8, make_uint4(pack_bf16(m[0], m[1]), pack_bf16(m[2], m[3]),
+                                       pack_bf16(m[4], m[5]), pack_bf16(m[6], m[7])));
+            };
+            if (ib < NB0 && ib < nblk0) {
+                const bf16x8 bm = block(gf0[ib < NB0 ? ib : 0], nblk0, j0, csj0);
+#pragma unroll
+                for (int p = 0; p < PT; ++p) acc0[p] = mfma16(xa[p], bm, acc0[p]);
+            }
+            {
+                const bf16x8 bm = block(gf1[ib], nblk1, j1, csj1);
+#pragma unroll
+                for (int p = 0; p < PT; ++p) acc1[p] = mfma16(xa[p], bm, acc1[p]);
+            }
+        }
+
+        // stage 5 and the skip: lane holds y[j][p*16 + 4*g4 + 0..3]; rows past the end of
+        // the sequence fall outside the buffer resource and are dropped
+        const float dh = D[h];
+        const __amdgpu_buffer_rsrc_t yr =
+            make_rsrc(y + ((size_t)(b * T + t0) * H + h) * P, (unsigned)Lc * rowb);
+        auto store_tile = [&](const f32x4* acc, int j) {
+#pragma unroll
+            for (int p = 0; p < PT; ++p) {
+                const int p0 = p * 16 + 4 * g4;
+                const uint2 xv = *reinterpret_cast<const uint2*>(bx + swz_off(j, p0, PPR));
+                uint2 out;
+                out.x = pack_bf16(acc[p][0] + dh * bf16_lo(xv.x), acc[p][1] + dh * bf16_hi(xv.x));
+                out.y = pack_bf16(acc[p][2] + dh * bf16_lo(xv.y), acc[p][3] + dh * bf16_hi(xv.y));
+                buf_store8(yr, (unsigned)j * rowb + p0 * 2u, out);
+            }
+        };
+        store_tile(acc0, j0);
+        store_tile(acc1, j1);
+        if (C_::NBUF == 1 && sl + 1 < hi) {
+            lds_barrier();  // every wave is done with the buffer
+            issue_item<Q, N, P>(x, E, cs, dtc, sl + 1, hpg, T, H, G, nC, lds0, wave, lane);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- dispatch
+
+template <int Q, int N, int P>
+hipError_t launch_scan_t(const Shape& s, const void* x, const void* Cm, const float* dtc,
+                         const float* cs, const float* D, const void* E, const void* gram,
+                         void* y, hipStream_t st) {
+    using C_ = ScanCfg<Q, N, P>;
+    const auto kern = chunk_scan_mfma_kernel<Q, N, P>;
+    // per device: allow the dynamic LDS size, and size the persistent grid to what is
+    // resident at once (a multiple of 8 workgroups, one run of items each)
+    static int grid_of[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (grid_of[dev] == 0) {
+        e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)C_::LDS);
+        if (e != hipSuccess) return e;
+        int ncu = 0, occ = 0;
+        e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, C_::NTH, C_::LDS);
+        if (e != hipSuccess) return e;
+        grid_of[dev] = ((ncu * (occ > 0 ? occ : 1)) / 8 > 0 ? (ncu * (occ > 0 ? occ : 1)) / 8 : 1) * 8;
+    }
+    const int nslots = s.B * s.G * s.nC * (s.H / s.G);
+    kern<<<grid_of[dev], C_::NTH, C_::LDS, st>>>(
+        (const __bf16*)x, (const __bf16*)Cm, dtc, cs, D, (const __bf16*)E, (const uint4*)gram,
+        (__bf16*)y, s.T, s.H, s.G, s.nC, nslots);
+    return hipGetLastError();
+}
+
+template <int Q, int N>
+hipError_t launch_gram_t(const Shape& s, const void* Bm, const void* Cm, void* gram,
+                         hipStream_t st) {
+    const unsigned blocks = (unsigned)((size_t)s.B * s.G * s.nC * ((npairs(Q) + 3) / 4));
+    chunk_gram_kernel<Q, N><<<blocks, 256, 0, st>>>((const __bf16*)Bm, (const __bf16*)Cm,
+                                                     (uint4*)gram, s.T, s.G, s.nC);
+    return hipGetLastError();
+}
+
+using ScanFn = hipError_t (*)(const Shape&, const void*, const void*, const float*, const float*,
+                              const float*, const void*, const void*, void*, hipStream_t);
+using GramFn = hipError_t (*)(const Shape&, const void*, const void*, void*, hipStream_t);
+
+template <int Q, int N>
+ScanFn pick_scan_qn(const Shape& s) {
+    switch (s.P) {
+        case 16: return launch_scan_t<Q, N, 16>;
+        case 32: return launch_scan_t<Q, N, 32>;
+        case 64: return launch_scan_t<Q, N, 64>;
+        case 128: return launch_scan_t<Q, N, 128>;
+    }
+    return nullptr;
+}
+template <int Q>
+ScanFn pick_scan_q(const Shape& s) {
+    switch (s.N) {
+        case 32: return pick_scan_qn<Q, 32>(s);
+        case 64: return pick_scan_qn<Q, 64>(s);
+        case 128: return pick_scan_qn<Q, 128>(s);
+        case 256: return pick_scan_qn<Q, 256>(s);
+    }
+    return nullptr;
+}
+template <int Q>
+GramFn pick_gram_q(const Shape& s) {
+    switch (s.N) {
+        case 32: return launch_gram_t<Q, 32>;
+        case 64: return launch_gram_t<Q, 64>;
+        case 128: return launch_gram_t<Q, 128>;
+        case 256: return launch_gram_t<Q, 256>;
+    }
+    return nullptr;
+}
+
+bool scan_offsets_fit(const Shape& s) {
+    // buffer resources address one chunk of x / y (and B, C) with 32-bit byte offsets
+    return (size_t)s.Q * s.H * s.P * 2 < ((size_t)1 << 31) &&
+           (size_t)s.Q * s.G * s.N * 2 < ((size_t)1 << 31);
+}
+
+ScanFn pick_scan(const Shape& s) {
+    if (!scan_offsets_fit(s)) return nullptr;
+    switch (s.Q) {
+        case 64: return pick_scan_q<64>(s);
+        case 128: return pick_scan_q<128>(s);
+        case 256: return pick_scan_q<256>(s);
+    }
+    return nullptr;
+}
+GramFn pick_gram(const Shape& s) {
+    if (!scan_offsets_fit(s)) return nullptr;
+    switch (s.Q) {
+        case 64: return pick_gram_q<64>(s);
+        case 128: return pick_gram_q<128>(s);
+        case 256: return pick_gram_q<256>(s);
+    }
+    return nullptr;
+}
+
+}  // namespace
+
+bool chunk_scan_mfma_supported(const Shape& s) { return pick_scan(s) != nullptr; }
+
+size_t chunk_gram_bytes(const Shape& s) {
+    if (!chunk_scan_mfma_supported(s)) return 0;
+    return (size_t)s.B * s.G * s.nC * npairs(s.Q) * 64 * 16;
+}
+
+hipError_t launch_chunk_gram(const Shape& s, const void* Bm, const void* Cm, void* gram,
+                             hipStream_t st) {
+    GramFn f = pick_gram(s);
+    if (!f) return hipErrorInvalidValue;
+    if ((size_t)s.B * s.G * s.nC == 0) return hipSuccess;
+    return f(s, Bm, Cm, gram, st);
+}
+
+hipError_t launch_chunk_scan_mfma(const Shape& s, const void* x, const void* Cm, const float* dtc,
+                                  const float* cs, const float* D, const void* entry,
+                                  const void* gram, void* y, hipStream_t st) {
+    ScanFn f = pick_scan(s);
+    if (!f) return hipErrorInvalidValue;
+    if ((size_t)s.B * s.G * s.nC == 0) return hipSuccess;
+    return f(s, x, Cm, dtc, cs, D, entry, gram, y, st);
+}
+
+}  // namespace ssd

@@ -52,6 +52,7 @@ size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Workspace {
     float *dtc, *cs, *states;
     void* entry;  // entry states, in the input dtype
+    void* gram;   // C B^T blocks of the MFMA chunk scan (empty where unused)
 };
 
 size_t workspace_bytes(const Shape& s, Workspace* w, char* base) {
@@ -68,6 +69,7 @@ size_t workspace_bytes(const Shape& s, Workspace* w, char* base) {
     ws.cs = take(chunk_elems * sizeof(float));
     ws.states = take(state_elems * sizeof(float));
     ws.entry = take(state_elems * sizeof(float));  // fp32 size: enough for either dtype
+    ws.gram = take(ssd::chunk_gram_bytes(s));
     if (w) *w = ws;
     return off;
 }
@@ -94,11 +96,15 @@ ssd_status run_chunk_state(const Shape& s, ssd_dtype dtype, const void* x, const
     return hip_status(ssd::launch_chunk_state_valu(s, dtype, x, B, dtc, cs, states, st));
 }
 
+bool uses_gram(const Shape& s, ssd_dtype dtype) {
+    return dtype == SSD_BF16 && ssd::chunk_scan_mfma_supported(s);
+}
+
 ssd_status run_chunk_scan(const Shape& s, ssd_dtype dtype, const void* x, const void* B,
                           const void* C, const float* dtc, const float* cs, const float* D,
-                          const void* entry, void* y, hipStream_t st) {
-    if (dtype == SSD_BF16 && ssd::chunk_scan_mfma_supported(s))
-        return hip_status(ssd::launch_chunk_scan_mfma(s, x, B, C, dtc, cs, D, entry, y, st));
+                          const void* entry, const void* gram, void* y, hipStream_t st) {
+    if (uses_gram(s, dtype))
+        return hip_status(ssd::launch_chunk_scan_mfma(s, x, C, dtc, cs, D, entry, gram, y, st));
     return hip_status(ssd::launch_chunk_scan_valu(s, dtype, x, B, C, dtc, cs, D, entry, y, st));
 }
 
@@ -162,18 +168,39 @@ ssd_status ssd_state_passing(const ssd_dims* dims, ssd_dtype dtype, int chunk_le
                                                 final_state, (hipStream_t)stream));
 }
 
+size_t ssd_chunk_gram_size(const ssd_dims* dims, ssd_dtype dtype, int chunk_len) {
+    Shape s;
+    if (make_shape(dims, chunk_len, &s) != SSD_OK || !valid_dtype(dtype)) return 0;
+    return uses_gram(s, dtype) ? ssd::chunk_gram_bytes(s) : 0;
+}
+
+ssd_status ssd_chunk_gram(const ssd_dims* dims, ssd_dtype dtype, int chunk_len, const void* B,
+                          const void* C, void* gram, void* stream) {
+    Shape s;
+    ssd_status r = make_shape(dims, chunk_len, &s);
+    if (r != SSD_OK) return r;
+    if (!valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
+    if (!uses_gram(s, dtype) || (size_t)s.B * s.T == 0) return SSD_OK;  // nothing to compute
+    if (!B || !C || !gram) return SSD_ERR_NULL;
+    if (any_misaligned({B, C, gram})) return SSD_ERR_ALIGN;
+    return hip_status(ssd::launch_chunk_gram(s, B, C, gram, (hipStream_t)stream));
+}
+
 ssd_status ssd_chunk_scan(const ssd_dims* dims, ssd_dtype dtype, int chunk_len, const void* x,
                           const void* B, const void* C, const float* dt_chunk, const float* cs,
-                          const float* D, const void* entry_states, void* y, void* stream) {
+                          const float* D, const void* entry_states, const void* gram, void* y,
+                          void* stream) {
     Shape s;
     ssd_status r = make_shape(dims, chunk_len, &s);
     if (r != SSD_OK) return r;
     if (!valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
     if ((size_t)s.B * s.T > 0 && (!x || !B || !C || !dt_chunk || !cs || !D || !entry_states || !y))
         return SSD_ERR_NULL;
-    if (any_misaligned({x, B, C, dt_chunk, cs, entry_states, y}) || any_misaligned4({D}))
+    if ((size_t)s.B * s.T > 0 && uses_gram(s, dtype) && !gram) return SSD_ERR_NULL;
+    if (any_misaligned({x, B, C, dt_chunk, cs, entry_states, gram, y}) || any_misaligned4({D}))
         return SSD_ERR_ALIGN;
-    return run_chunk_scan(s, dtype, x, B, C, dt_chunk, cs, D, entry_states, y, (hipStream_t)stream);
+    return run_chunk_scan(s, dtype, x, B, C, dt_chunk, cs, D, entry_states, gram, y,
+                          (hipStream_t)stream);
 }
 
 ssd_status ssd_fwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const float* dt,
@@ -204,7 +231,11 @@ ssd_status ssd_fwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const f
     r = hip_status(ssd::launch_state_passing(s, dtype, ws.states, ws.cs, init_state, ws.entry,
                                              final_state, st));
     if (r != SSD_OK || !has_tokens) return r;
-    return run_chunk_scan(s, dtype, x, B, C, ws.dtc, ws.cs, D, ws.entry, y, st);
+    if (uses_gram(s, dtype)) {
+        r = hip_status(ssd::launch_chunk_gram(s, B, C, ws.gram, st));
+        if (r != SSD_OK) return r;
+    }
+    return run_chunk_scan(s, dtype, x, B, C, ws.dtc, ws.cs, D, ws.entry, ws.gram, y, st);
 }
 
 }  // extern "C"

@@ -46,8 +46,12 @@ hipError_t launch_chunk_state_mfma(const Shape& s, const void* x, const void* Bm
                                    const float* dtc, const float* cs, float* states,
                                    hipStream_t st);
 bool chunk_scan_mfma_supported(const Shape& s);
-hipError_t launch_chunk_scan_mfma(const Shape& s, const void* x, const void* Bm, const void* Cm,
-                                  const float* dtc, const float* cs, const float* D,
-                                  const void* entry, void* y, hipStream_t st);
+// bytes of the C B^T blocks the MFMA chunk scan reads (0 where the shape has no MFMA scan)
+size_t chunk_gram_bytes(const Shape& s);
+hipError_t launch_chunk_gram(const Shape& s, const void* Bm, const void* Cm, void* gram,
+                             hipStream_t st);
+hipError_t launch_chunk_scan_mfma(const Shape& s, const void* x, const void* Cm, const float* dtc,
+                                  const float* cs, const float* D, const void* entry,
+                                  const void* gram, void* y, hipStream_t st);
 
 }  // namespace ssd

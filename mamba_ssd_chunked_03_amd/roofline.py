@@ -5,7 +5,9 @@ read once and every output written once per launch; the quadratic part counts on
 causal half of each Q x Q diagonal block (the method never needs the upper triangle),
 and C B^T is counted once per (batch, group, chunk) because the heads of a group share
 it.  Bytes use the dtype sizes of the boundary (x, B, C, y in the input dtype; dt, cs
-and the states in fp32).
+and the states in fp32).  Where the chunk scan takes C B^T from a separate chunk_gram
+launch (gram_bytes > 0: the bf16 matrix-core path), that launch reads B and C and writes
+the gram blocks once, and the scan reads them once in place of B.
 """
 from dataclasses import dataclass
 
@@ -22,7 +24,7 @@ class KernelCost:
 
 
 def kernel_costs(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len, dtype="bf16",
-                 init_state=False, final_state=True):
+                 init_state=False, final_state=True, gram_bytes=0):
     B, T, H, P, N, G, Q = batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len
     e = 2 if dtype == "bf16" else 4
     nC = (T + Q - 1) // Q
@@ -43,9 +45,16 @@ def kernel_costs(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len, dty
     # per (b, g, chunk) over N; off-chunk: Q x N x P MACs per (b, h, chunk)
     full, rem = divmod(T, Q)
     tri = full * Q * (Q + 1) + rem * (rem + 1)          # sum of 2*(j+1) over valid rows
+    gram_flops = B * G * tri * N
+    if gram_bytes:
+        gram = KernelCost("chunk_gram", 2 * io_bc + gram_bytes, gram_flops)
+        scan = KernelCost("chunk_scan",
+                          2 * io_xy + io_bc + gram_bytes + 2 * chunk_f32 + entry + H * 4,
+                          B * H * tri * P + 2.0 * B * H * T * N * P)
+        return [cumsum, state, passing, gram, scan]
     scan = KernelCost("chunk_scan",
                       2 * io_xy + 2 * io_bc + 2 * chunk_f32 + entry + H * 4,
-                      B * H * tri * P + B * G * tri * N + 2.0 * B * H * T * N * P)
+                      B * H * tri * P + gram_flops + 2.0 * B * H * T * N * P)
     return [cumsum, state, passing, scan]
 
 

@@ -8,6 +8,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from mamba_ssd_chunked_03_amd import binding
 
@@ -55,10 +56,19 @@ def test_workspace_size(lib):
     nC = 16
     chunk = 4 * 80 * nC * 256 * 4
     state = 4 * 80 * nC * 64 * 128 * 4
-    assert ws == 2 * chunk + 2 * state
+    # C B^T blocks: per (batch, group, chunk) the 72 causal (16-row tile, 32-step block)
+    # pairs of a 256-step chunk, 64 lanes x 16 bytes each
+    pairs = sum(t // 2 + 1 for t in range(256 // 16))
+    assert pairs == 72
+    gram = 4 * 1 * nC * pairs * 64 * 16
+    assert ws == 2 * chunk + 2 * state + gram
+    assert binding.ssd_chunk_gram_size(d, torch.bfloat16, 256) == gram
+    assert binding.ssd_chunk_gram_size(d, torch.float32, 256) == 0
+    assert binding.ssd_chunk_gram_size(D(1, 1000, 4, 64, 128, 2), torch.bfloat16, 64) == \
+        1 * 2 * 16 * sum(t // 2 + 1 for t in range(4)) * 1024
     # ragged T rounds the chunk count up
     assert binding.ssd_fwd_workspace_size(D(1, 1000, 4, 64, 128, 1), 256) == \
-        2 * (4 * 4 * 256 * 4) + 2 * (4 * 4 * 64 * 128 * 4)
+        2 * (4 * 4 * 256 * 4) + 2 * (4 * 4 * 64 * 128 * 4) + 4 * pairs * 1024
     assert binding.ssd_fwd_workspace_size(D(1, 0, 2, 16, 16, 1), 64) == 0
     for bad, q in ((D(h=3, g=2), 64), (D(p=24), 64), (D(n=48), 64), (D(), 32), (D(b=-1), 64)):
         assert binding.ssd_fwd_workspace_size(bad, q) == 0
@@ -98,6 +108,22 @@ def test_validation_errors_before_any_launch(lib):
                                  ctypes.c_void_p(64), None, ctypes.c_void_p(128), None,
                                  None) == 3   # dtype
     assert lib.ssd_chunk_scan(ctypes.byref(D()), 1, 128, None, None, None, None, None, None,
-                              None, None, None) == 1
+                              None, None, None, None) == 1
+    # bf16 scan needs its gram buffer; fp32 ignores it
+    ok = [ctypes.c_void_p(256)] * 7
+    mf = D(p=64, n=64)   # a shape with a matrix-core scan
+    assert lib.ssd_chunk_scan(ctypes.byref(mf), 1, 64, *ok, None, ctypes.c_void_p(256),
+                              None) == 1
+    assert lib.ssd_chunk_scan(ctypes.byref(mf), 1, 64, *ok, ctypes.c_void_p(264),
+                              ctypes.c_void_p(256), None) == 4
+    assert lib.ssd_chunk_gram(ctypes.byref(mf), 1, 64, None, None, None, None) == 1
+    assert lib.ssd_chunk_gram(ctypes.byref(mf), 1, 64, ctypes.c_void_p(8), ctypes.c_void_p(256),
+                              ctypes.c_void_p(256), None) == 4
+    assert lib.ssd_chunk_gram(ctypes.byref(D(p=40)), 1, 64, None, None, None, None) == 3
+    # no gram buffer for fp32, dstate 16 or an empty sequence: nothing to do
+    assert lib.ssd_chunk_gram(ctypes.byref(mf), 0, 64, None, None, None, None) == 0
+    assert lib.ssd_chunk_gram(ctypes.byref(D()), 1, 64, None, None, None, None) == 0
+    assert lib.ssd_chunk_gram(ctypes.byref(D(t=0, p=64, n=64)), 1, 64, None, None, None,
+                              None) == 0
     assert lib.ssd_fwd(None, 0, None, None, None, None, None, None, 64, None, None, None, None,
                        0, None) == 1

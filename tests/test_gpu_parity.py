@@ -156,7 +156,9 @@ def test_stage_chunk_scan(w):
     dtc, _ = binding.ssd_chunk_cumsum(d, w.chunk_len, dv["dt"], dv["A"])
     cs_d = torch.from_numpy(cs).float().cuda()
     ent_d = torch.from_numpy(ent.swapaxes(-1, -2).copy()).to(cpu["x"].dtype).cuda()
-    y = binding.ssd_chunk_scan(d, w.chunk_len, dv["x"], dv["B"], dv["C"], dtc, cs_d, dv["D"], ent_d)
+    gram = binding.ssd_chunk_gram(d, w.chunk_len, dv["B"], dv["C"])
+    y = binding.ssd_chunk_scan(d, w.chunk_len, dv["x"], dv["B"], dv["C"], dtc, cs_d, dv["D"], ent_d,
+                               gram=gram)
     torch.cuda.synchronize()
     e = rel_l2(np64(y), y_ref)
     say(f"    rel_l2 y={e:.3e}")
