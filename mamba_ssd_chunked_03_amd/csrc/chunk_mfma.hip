@@ -3,58 +3,197 @@
 // Summary of arXiv 2405.21060, section "The Block-Decomposition SSD Algorithm", stage 2
 // (the linear-attention contraction order of equation 15):
 //     S[n][p] = sum_i B[i][n] x'[i][p],   x'[i][p] = exp(cs_last - cs_i) dt_i x[i][p]
-// x' is formed in fp32 and rounded once to bf16.  v_mfma_f32_16x16x32_bf16 contracts over
-// time, which runs along the slow (row) dimension of B and x in HBM, so 32-step slices
-// are staged through LDS in a transposed [feature][time] layout (two time steps packed
-// per 32-bit LDS word), double-buffered through registers.  One workgroup (4 waves) per
-// (b, h, chunk); wave w owns state rows n in [w N/4, (w+1) N/4) and all of p.
+// with fp32 accumulation.  v_mfma_f32_16x16x32_bf16 contracts over time, which runs along
+// the slow (row) dimension of B and x in HBM, so both operands pass through LDS.
+//
+// Two kernels:
+//   chunk_state_pipe_kernel (N = 128, P <= 64): persistent and pipelined.  A workgroup per
+//     CU walks a run of (unit, head) items, a unit being one (batch, group, chunk).  The
+//     unit's B chunk is copied into LDS once and read out through transpose reads into
+//     register fragments (one 16-row n-tile per wave, all 32-step blocks), after which
+//     the next unit's B is copied in behind it.  Each item's x, cs and dt are copied into
+//     a double-buffered LDS while the previous item computes.  The per-step weight
+//     exp(cs_last - cs_i) dt_i is applied to the B fragments (rounded to bf16 once per
+//     item), and x^T comes out of LDS through transpose reads.
+//   chunk_state_mfma_kernel (other shapes): one workgroup per (b, h, chunk); 32-step slices
+//     of B and x are transposed through registers into LDS ([feature][time], two time
+//     steps per 32-bit word) and double-buffered; x' is formed in fp32 and rounded once.
+#include "mfma_common.h"
 #include "ssd_internal.h"
 
 namespace ssd {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+using namespace mfma;
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr int KB = 32;  // time steps per LDS slice = k of one MFMA
 constexpr int LDT = KB + 8;  // row stride (bf16) of the transposed [feature][time] slices
-
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float exp2_fast(float v) { return __builtin_amdgcn_exp2f(v); }
-
-// Workgroup barrier for data exchanged through LDS only.  __syncthreads() is a full
-// workgroup fence that also waits for every outstanding global load and store
-// (vmcnt(0)), which would drain the register prefetch of the next slice or head at
-// every barrier; here only this wave's LDS operations are waited for.  The empty asm
-// with a memory clobber keeps the compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// two fp32 -> packed bf16 pair (round to nearest even), as one 32-bit word
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-    bf16x2 p;
-    p[0] = (__bf16)lo;
-    p[1] = (__bf16)hi;
-    return __builtin_bit_cast(uint32_t, p);
-}
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// v if keep, else zeros -- per component, so that it stays a register select
-__device__ __forceinline__ uint4 keep_or_zero(bool keep, uint4 v) {
-    return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
-}
 
 // element k (0..7) of a 16-byte vector of bf16, as raw 16 bits in the low half
 __device__ __forceinline__ uint32_t bits_of(const uint4& v, int k) {
     const uint32_t w = k < 2 ? v.x : k < 4 ? v.y : k < 6 ? v.z : v.w;
     return (k & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+// ============================================================================ pipelined
+template <int Q, int N, int P>
+struct StateCfg {
+    static constexpr int NW = N / 16;  // waves: one 16-row n-tile each
+    static constexpr int NTH = NW * 64;
+    static constexpr int NB = Q / KB;
+    static constexpr int PT = P / 16, PPR = P / 8, NPR = N / 8;
+    static constexpr unsigned XB = Q * P * 2, BB = Q * N * 2, FB = Q * 4;
+    static constexpr unsigned ITEM = XB + 2 * FB;  // x, cs, dt
+    static constexpr unsigned LDS = BB + 2 * ITEM + FB;
+    static constexpr int STORES = PT;  // state stores per wave per item
+};
+
+template <int Q, int N, int P>
+__device__ __forceinline__ void state_issue_x(const __bf16* x, const float* cs, const float* dtc,
+                                              int slot, int hpg, int T, int H, int G, int nC,
+                                              uint32_t lds, int wave, int lane) {
+    using C_ = StateCfg<Q, N, P>;
+    const int unit = slot / hpg;
+    const int c = unit % nC, g = (unit / nC) % G, b = unit / nC / G;
+    const int h = g * hpg + slot % hpg;
+    const int Lc = min(Q, T - c * Q);
+    const unsigned rowb = (unsigned)(H * P * 2);
+    const u32x4 xr = raw_rsrc(x + ((size_t)(b * T + c * Q) * H + h) * P, (unsigned)Lc * rowb);
+    constexpr int XI = Q * C_::PPR / 64;
+#pragma unroll
+    for (int k = wave; k < XI; k += C_::NW) {
+        const int m = k * 64 + lane;
+        const int r = m / C_::PPR, sl = m % C_::PPR;
+        dma16(xr, lds + k * 1024, (unsigned)r * rowb + (unsigned)(sl ^ (r & (C_::PPR - 1))) * 16u);
+    }
+    const size_t sb = ((size_t)(b * H + h) * nC + c) * Q;
+    if (wave == 0 && lane < Q / 4) dma16(raw_rsrc(cs + sb, C_::FB), lds + C_::XB, lane * 16u);
+    if (wave == 1 && lane < Q / 4) dma16(raw_rsrc(dtc + sb, C_::FB), lds + C_::XB + C_::FB, lane * 16u);
+}
+
+template <int Q, int N, int P>
+__device__ __forceinline__ void state_issue_b(const __bf16* Bm, int unit, int T, int G, int nC,
+                                              uint32_t lds, int wave, int lane) {
+    using C_ = StateCfg<Q, N, P>;
+    const int c = unit % nC, g = (unit / nC) % G, b = unit / nC / G;
+    const int Lc = min(Q, T - c * Q);
+    const unsigned rowb = (unsigned)(G * N * 2);
+    const u32x4 br = raw_rsrc(Bm + ((size_t)(b * T + c * Q) * G + g) * N, (unsigned)Lc * rowb);
+    constexpr int BI = Q * C_::NPR / 64;
+#pragma unroll
+    for (int k = wave; k < BI; k += C_::NW) {
+        const int m = k * 64 + lane;
+        const int r = m / C_::NPR, sl = m % C_::NPR;
+        dma16(br, lds + k * 1024, (unsigned)r * rowb + (unsigned)(sl ^ (r & (C_::NPR - 1))) * 16u);
+    }
+}
+
+template <int Q, int N, int P>
+__global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_kernel(
+    const __bf16* __restrict__ x, const __bf16* __restrict__ Bm, const float* __restrict__ dtc,
+    const float* __restrict__ cs, float* __restrict__ states, int T, int H, int G, int nC,
+    int nslots) {
+    using C_ = StateCfg<Q, N, P>;
+    constexpr int NB = C_::NB, PT = C_::PT, PPR = C_::PPR, NPR = C_::NPR;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const uint32_t lds0 = lds_addr(smem);
+    unsigned char* const sB = smem;                    // B chunk of the next unit, [time][n]
+    unsigned char* const sX = smem + C_::BB;           // two item buffers: x, cs, dt
+    float* const s_w = reinterpret_cast<float*>(smem + C_::BB + 2 * C_::ITEM);
+
+    // a contiguous run of items per workgroup, neighbouring runs on the same XCD
+    const int nwg = gridDim.x;
+    const int wp = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+    const int per = (nslots + nwg - 1) / nwg;
+    const int lo = wp * per, hi = min(nslots, lo + per);
+    if (lo >= hi) return;
+
+    const int hpg = H / G;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+
+    // transpose-read offsets (rows 4 g4 + l16 / 4 of a 32-step block, column 4 (l16 % 4)
+    // within a 16-wide tile); the swizzle depends only on the row mod pieces-per-row
+    const unsigned boff = swz_off(4 * g4 + (l16 >> 2), wave * 16 + 4 * (l16 & 3), NPR);
+    unsigned xoff[PT];
+#pragma unroll
+    for (int p = 0; p < PT; ++p) xoff[p] = swz_off(4 * g4 + (l16 >> 2), p * 16 + 4 * (l16 & 3), PPR);
+    constexpr unsigned BBLK = KB * NPR * 16, BHALF = 16 * NPR * 16;
+    constexpr unsigned XBLK = KB * PPR * 16, XHALF = 16 * PPR * 16;
+
+    bf16x8 bt[NB];  // B^T fragments of this wave's n-tile, every 32-step block
+    int cur_unit = -1;
+
+    state_issue_b<Q, N, P>(Bm, lo / hpg, T, G, nC, lds0, wave, lane);
+    state_issue_x<Q, N, P>(x, cs, dtc, lo, hpg, T, H, G, nC, lds0 + C_::BB, wave, lane);
+#pragma unroll 1
+    for (int sl = lo; sl < hi; ++sl) {
+        const int n = sl - lo;
+        const int buf = n & 1;
+        const unsigned char* bx = sX + buf * C_::ITEM;
+        const float* b_cs = reinterpret_cast<const float*>(bx + C_::XB);
+        const float* b_dt = b_cs + Q;
+        // this item's copies have landed once only the previous item's stores are pending
+        if (n == 0)
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::STORES) : "memory");
+        const int unit = sl / hpg;
+        if (unit != cur_unit) {  // the B region holds this unit: take this wave's fragments
+            cur_unit = unit;
+#pragma unroll
+            for (int ib = 0; ib < NB; ++ib) {
+                const unsigned char* bp = sB + boff + ib * BBLK;
+                const uint2 lo2 = lds_read_tr16(bp);
+                const uint2 hi2 = lds_read_tr16(bp + BHALF);
+                bt[ib] = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+            }
+            lds_barrier();  // every wave holds its fragments: the region is free
+            const int nxt = (unit + 1) * hpg;
+            if (nxt < hi) state_issue_b<Q, N, P>(Bm, unit + 1, T, G, nC, lds0, wave, lane);
+        }
+        if (tid < Q) {
+            const float ci = b_cs[tid];
+            s_w[tid] = exp2_fast((b_cs[Q - 1] - ci) * kLog2e) * b_dt[tid];
+        }
+        lds_barrier();
+        if (sl + 1 < hi)
+            state_issue_x<Q, N, P>(x, cs, dtc, sl + 1, hpg, T, H, G, nC,
+                                   lds0 + C_::BB + (buf ^ 1) * C_::ITEM, wave, lane);
+
+        f32x4 acc[PT];
+#pragma unroll
+        for (int p = 0; p < PT; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ib = 0; ib < NB; ++ib) {
+            // B^T fragment weighted by exp(cs_last - cs_i) dt_i over its k-slots
+            const int i0 = ib * KB + 4 * g4;
+            const float4 wa = *reinterpret_cast<const float4*>(&s_w[i0]);
+            const float4 wb = *reinterpret_cast<const float4*>(&s_w[i0 + 16]);
+            const uint4 r = __builtin_bit_cast(uint4, bt[ib]);
+            const bf16x8 a = __builtin_bit_cast(
+                bf16x8, make_uint4(pack_bf16(bf16_lo(r.x) * wa.x, bf16_hi(r.x) * wa.y),
+                                   pack_bf16(bf16_lo(r.y) * wa.z, bf16_hi(r.y) * wa.w),
+                                   pack_bf16(bf16_lo(r.z) * wb.x, bf16_hi(r.z) * wb.y),
+                                   pack_bf16(bf16_lo(r.w) * wb.z, bf16_hi(r.w) * wb.w)));
+#pragma unroll
+            for (int p = 0; p < PT; ++p) {
+                const unsigned char* xp = bx + xoff[p] + ib * XBLK;
+                const uint2 lo2 = lds_read_tr16(xp);
+                const uint2 hi2 = lds_read_tr16(xp + XHALF);
+                acc[p] = mfma16(a, __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y)),
+                                acc[p]);
+            }
+        }
+        // lane holds S[n = wave*16 + 4*g4 + r][p = pt*16 + l16]; layout [p][n]
+        const int c = unit % nC, g = (unit / nC) % G, b = unit / nC / G;
+        const int h = g * hpg + sl % hpg;
+        float* out = states + ((size_t)(b * H + h) * nC + c) * P * N;
+#pragma unroll
+        for (int p = 0; p < PT; ++p)
+            *reinterpret_cast<float4*>(out + (size_t)(p * 16 + l16) * N + wave * 16 + 4 * g4) =
+                make_float4(acc[p][0], acc[p][1], acc[p][2], acc[p][3]);
+    }
 }
 
 // ============================================================================ chunk_state
@@ -197,20 +336,6 @@ hipError_t launch_state_t(const Shape& s, const void* x, const void* Bm, const f
     return hipGetLastError();
 }
 
-// Heads of one (batch, group, chunk) unit are split into `ranges` workgroups so that the
-// grid covers the GPU's 256 CUs at least once, keeping >= 4 heads per workgroup where the
-// group has that many (each workgroup pays one C B^T setup for its range).
-inline void scan_split(const Shape& s, int* heads_per_wg, int* ranges) {
-    const long units = (long)s.B * s.G * s.nC;
-    const int hpg = s.H / s.G;
-    int want = (int)((256 + units - 1) / units);  // >= 256 pairs = 2 workgroups per CU
-    int maxr = hpg / 4 > 0 ? hpg / 4 : 1;
-    int r = want < maxr ? want : maxr;
-    if (r < 1) r = 1;
-    *heads_per_wg = (hpg + r - 1) / r;
-    *ranges = (hpg + *heads_per_wg - 1) / *heads_per_wg;
-}
-
 #define SSD_FOR_P(F, Q, N)                                   \
     switch (s.P) {                                           \
         case 16: return F<Q, N, 16>;                         \
@@ -233,7 +358,61 @@ StateFn pick_state_q(const Shape& s) {
     return nullptr;
 }
 
+template <int Q, int N, int P>
+hipError_t launch_state_pipe_t(const Shape& s, const void* x, const void* Bm, const float* dtc,
+                               const float* cs, float* states, hipStream_t st) {
+    using C_ = StateCfg<Q, N, P>;
+    const auto kern = chunk_state_pipe_kernel<Q, N, P>;
+    static int grid_of[64];  // per device: resident workgroups, a multiple of 8
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (grid_of[dev] == 0) {
+        e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)C_::LDS);
+        if (e != hipSuccess) return e;
+        int ncu = 0, occ = 0;
+        e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, C_::NTH, C_::LDS);
+        if (e != hipSuccess) return e;
+        const int g8 = (ncu * (occ > 0 ? occ : 1)) / 8;
+        grid_of[dev] = (g8 > 0 ? g8 : 1) * 8;
+    }
+    const int nslots = s.B * s.G * s.nC * (s.H / s.G);
+    kern<<<grid_of[dev], C_::NTH, C_::LDS, st>>>((const __bf16*)x, (const __bf16*)Bm, dtc, cs,
+                                                  states, s.T, s.H, s.G, s.nC, nslots);
+    return hipGetLastError();
+}
+
+template <int Q>
+StateFn pick_state_pipe_q(const Shape& s) {
+    if (s.N != 128) return nullptr;
+    switch (s.P) {
+        case 16: return launch_state_pipe_t<Q, 128, 16>;
+        case 32: return launch_state_pipe_t<Q, 128, 32>;
+        case 64: return launch_state_pipe_t<Q, 128, 64>;
+    }
+    return nullptr;
+}
+
+bool state_offsets_fit(const Shape& s) {
+    // buffer resources address one chunk of x and B with 32-bit byte offsets
+    return (size_t)s.Q * s.H * s.P * 2 < ((size_t)1 << 31) &&
+           (size_t)s.Q * s.G * s.N * 2 < ((size_t)1 << 31);
+}
+
 StateFn pick_state(const Shape& s) {
+    if (state_offsets_fit(s)) {
+        StateFn f = nullptr;
+        switch (s.Q) {
+            case 64: f = pick_state_pipe_q<64>(s); break;
+            case 128: f = pick_state_pipe_q<128>(s); break;
+            case 256: f = pick_state_pipe_q<256>(s); break;
+        }
+        if (f) return f;
+    }
     switch (s.Q) {
         case 64: return pick_state_q<64>(s);
         case 128: return pick_state_q<128>(s);

@@ -112,18 +112,6 @@ struct ScanCfg {
     static constexpr int STORES = 2 * PT;  // y stores per wave per item
 };
 
-// 16 bytes per lane from a buffer resource into LDS at lds + 16 * lane (opaque to the
-// compiler's wait-count tracking; callers wait explicitly)
-__device__ __forceinline__ void dma16(u32x4 r, uint32_t lds, uint32_t voff) {
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(lds)
-                 : "memory");
-}
-// raw buffer resource words: base, stride 0, size in bytes (reads past it return zeros)
-__device__ __forceinline__ u32x4 raw_rsrc(const void* base, unsigned bytes) {
-    const uint64_t a = (uint64_t)base;
-    return u32x4{(unsigned)a, (unsigned)(a >> 32) & 0xffffu, bytes, 0x00020000u};
-}
-
 template <int Q, int N, int P>
 __device__ __forceinline__ void issue_item(const __bf16* x, const __bf16* E, const float* cs,
                                            const float* dtc, int slot, int hpg, int T, int H,

@@ -90,6 +90,24 @@ __device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
     return __builtin_bit_cast(uint2, v);
 }
 
+// Copies into LDS issued through inline asm: 16 bytes per lane from a buffer resource
+// into LDS at lds + 16 * lane.  The compiler does not see these as writes to LDS, so it
+// never makes later LDS reads wait for them; callers wait explicitly (s_waitcnt vmcnt)
+// and barrier before reading what they copied.
+__device__ __forceinline__ void dma16(u32x4 r, uint32_t lds, uint32_t voff) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(lds)
+                 : "memory");
+}
+// raw buffer resource words: base, stride 0, size in bytes (reads past it return zeros)
+__device__ __forceinline__ u32x4 raw_rsrc(const void* base, unsigned bytes) {
+    const uint64_t a = (uint64_t)base;
+    return u32x4{(unsigned)a, (unsigned)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+// LDS byte address of a pointer into shared memory
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char*)p;
+}
+
 // Row-major bf16 matrices in LDS are stored as rows of 16-byte pieces with the piece
 // index XOR-swizzled by the row (piece c of row r sits at slot c ^ (r % pieces_per_row)),
 // which spreads the column reads of consecutive rows over the LDS banks.  Byte offset of
