@@ -156,40 +156,44 @@ def main():
         binding.ssd_fwd(d_in["x"], d_in["dt"], d_in["A"], d_in["B"], d_in["C"], d_in["D"], Q,
                         init_state=d_in["init_state"], y=y, final_state=fin, workspace=ws)
 
+    # the same calls ssd_fwd makes, one stage at a time, with an event between stages
     def staged(ev):
         ev[0].record()
         binding.ssd_chunk_cumsum(dims, Q, d_in["dt"], d_in["A"], dtc, cs)
         ev[1].record()
-        binding.ssd_chunk_state(dims, Q, d_in["x"], d_in["B"], dtc, cs, S)
+        binding.ssd_chunk_state(dims, Q, d_in["x"], d_in["B"], dtc, cs, S, C=d_in["C"], gram=gram)
         ev[2].record()
         binding.ssd_state_passing(dims, Q, S, cs, init_state=d_in["init_state"],
                                   entry_states=E, final_state=fin)
         ev[3].record()
-        binding.ssd_chunk_gram(dims, Q, d_in["B"], d_in["C"], gram)
-        ev[4].record()
         binding.ssd_chunk_scan(dims, Q, d_in["x"], d_in["B"], d_in["C"], dtc, cs, d_in["D"], E,
                                gram=gram, y=y)
-        ev[5].record()
+        ev[4].record()
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         fwd()
     torch.cuda.synchronize()
     y_ref = y.clone()
-    ev_steps = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    # the timed steps: whole forward passes, back to back
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fwd()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # per-stage durations (HIP events on the launch stream), for the roofline
+    ev_steps = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     for k in range(args.steps):
         staged(ev_steps[k])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
     if not torch.equal(y, y_ref):
         log("[bench] WARNING: staged calls and ssd_fwd differ")
     if not torch.isfinite(y.float()).all():
         log("[bench] WARNING: non-finite output")
 
-    names = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_gram", "chunk_scan"]
+    names = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_scan"]
     per = {n: 0.0 for n in names}
     for ev in ev_steps:
         for i, n in enumerate(names):
@@ -197,8 +201,6 @@ def main():
     costs = {c.name: c for c in roofline.kernel_costs(
         w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, Q, w.dtype,
         init_state=w.init_state, final_state=True, gram_bytes=gram_n)}
-    if "chunk_gram" not in costs:   # no separate gram launch on this path
-        names.remove("chunk_gram")
     kernels = {}
     for n in names:
         t = per[n] * 1e-3

@@ -15,9 +15,10 @@
  *
  * It is computed by the block decomposition of M into chunks of chunk_len steps
  * (summary section "The Block-Decomposition SSD Algorithm", stages 0 to 5), as four
- * kernels that ssd_fwd runs in order on one stream, each also exported on its own:
+ * stage calls that ssd_fwd makes in order on one stream, each also exported on its own:
  *   ssd_chunk_cumsum   stage 0: chunk-local inclusive prefix sums of dt*A (log decays)
- *   ssd_chunk_state    stage 2: every chunk's final state from a zero start
+ *   ssd_chunk_state    stage 2: every chunk's final state from a zero start (and, given a
+ *                      gram buffer, the first half of stage 1 below in the same pass)
  *   ssd_state_passing  stage 3: the 1-SS scan over chunks that carries states across them
  *   ssd_chunk_gram     stage 1, first half: the causal blocks of C B^T of every chunk,
  *                      once per group (bf16 MFMA path only; a no-op elsewhere)
@@ -121,10 +122,15 @@ ssd_status ssd_chunk_cumsum(const ssd_dims* dims, int chunk_len, const float* dt
  * chunk when the chunk starts from zero, i.e. from the chunk's own inputs only:
  *     states[b][h][c][p][n] = sum_i exp(cs[c][Q-1] - cs[c][i]) * dt_chunk[c][i]
  *                                   * B[b][cQ+i][g][n] * x[b][cQ+i][h][p]
- * (sum over the chunk's valid positions i).  dt_chunk and cs come from ssd_chunk_cumsum. */
+ * (sum over the chunk's valid positions i).  dt_chunk and cs come from ssd_chunk_cumsum.
+ * gram: NULL, or a buffer of ssd_chunk_gram_size bytes that is also filled exactly as
+ * ssd_chunk_gram(dims, dtype, chunk_len, B, C, gram) would fill it (C is then required;
+ * where ssd_chunk_gram_size is 0 both are ignored).  The states kernel already holds each
+ * chunk's B, so for some shapes the blocks come from the same pass. */
 ssd_status ssd_chunk_state(const ssd_dims* dims, ssd_dtype dtype, int chunk_len,
                            const void* x, const void* B, const float* dt_chunk,
-                           const float* cs, float* states, void* stream);
+                           const float* cs, float* states, const void* C, void* gram,
+                           void* stream);
 
 /* Stage 3 (same section, "Propagate states between chunks"): the sequential 1-SS scan
  * over chunks.  With E_0 = init_state (zeros if NULL), carried in fp32,

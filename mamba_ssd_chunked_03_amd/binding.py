@@ -57,7 +57,7 @@ def library(path=LIB_PATH):
     lib.ssd_chunk_cumsum.restype = i
     lib.ssd_chunk_cumsum.argtypes = [dims, i, fp, fp, fp, fp, vp]
     lib.ssd_chunk_state.restype = i
-    lib.ssd_chunk_state.argtypes = [dims, i, i, vp, vp, fp, fp, fp, vp]
+    lib.ssd_chunk_state.argtypes = [dims, i, i, vp, vp, fp, fp, fp, vp, vp, vp]
     lib.ssd_state_passing.restype = i
     lib.ssd_state_passing.argtypes = [dims, i, i, fp, fp, fp, vp, fp, vp]
     lib.ssd_chunk_gram_size.restype = sz
@@ -164,13 +164,17 @@ def _state_shape(dims, chunk_len):
     return (dims.batch, dims.nheads, nchunks(dims.seqlen, chunk_len), dims.headdim, dims.dstate)
 
 
-def ssd_chunk_state(dims, chunk_len, x, B, dt_chunk, cs, states=None, stream=None):
+def ssd_chunk_state(dims, chunk_len, x, B, dt_chunk, cs, states=None, C=None, gram=None,
+                    stream=None):
+    """Chunk states; given C and a gram buffer (ssd_chunk_gram_size bytes) it also fills the
+    C B^T blocks that ssd_chunk_scan reads, as ssd_chunk_gram would."""
     dev = x.device
     if states is None:
         states = torch.empty(_state_shape(dims, chunk_len), dtype=torch.float32, device=dev)
+    gp = _ptr(gram) if gram is not None and gram.numel() else None
     _check(library().ssd_chunk_state(ctypes.byref(dims), _DTYPE_CODE[x.dtype], int(chunk_len),
                                      _ptr(x), _ptr(B), _ptr(dt_chunk), _ptr(cs), _ptr(states),
-                                     _stream(dev, stream)))
+                                     _ptr(C), gp, _stream(dev, stream)))
     return states
 
 

@@ -5,63 +5,89 @@
 // "The 1-Semiseparable Matrix": entries a_j ... a_{i+1} become exp(cs_j - cs_i) with
 // cs the running sum of log a = dt*A inside the chunk.
 //
-// One workgroup of Q threads per (b, h, chunk).  Thread i reads dt[b, cQ+i, h] (all H
-// heads of a chunk read the same cache lines, so L2 serves the strided reads), writes the
-// chunk-major copy dt_chunk[b][h][c][i] that the later kernels read contiguously, and the
-// inclusive prefix sum of dt*A over the chunk: a wave-level shuffle scan, then the
-// wave totals through LDS.  HBM-bound and tiny (two fp32 values per token and head).
+// One workgroup of 256 threads per (b, chunk, block of 16 heads).  dt is [B][T][H], so a
+// chunk's steps for a block of heads are Q rows of 64 contiguous bytes: the workgroup
+// reads them coalesced into an LDS tile [head][time], then each wave takes whole heads:
+// a lane holds Q/64 consecutive steps, scans them serially, and a 64-wide shuffle scan
+// adds the carry of the lanes before it.  It writes the chunk-major copy
+// dt_chunk[b][h][c][i] that the later kernels read contiguously, and the inclusive prefix
+// sum cs of dt*A over the chunk, both as contiguous rows.
 #include "ssd_internal.h"
 
 namespace ssd {
 namespace {
 
+constexpr int kHB = 16;  // heads per workgroup
+
 template <int Q>
-__global__ __launch_bounds__(Q) void chunk_cumsum_kernel(const float* __restrict__ dt,
-                                                          const float* __restrict__ A,
-                                                          float* __restrict__ dtc,
-                                                          float* __restrict__ cs, int T, int H,
-                                                          int nC) {
-    constexpr int kWaves = Q / 64;
-    __shared__ float wave_sum[kWaves];
-    const int c = blockIdx.x % nC;
-    const int bh = blockIdx.x / nC;
-    const int h = bh % H;
-    const int b = bh / H;
-    const int i = threadIdx.x;
-    const int t = c * Q + i;
-    const float v = t < T ? dt[((size_t)b * T + t) * H + h] : 0.0f;
-    float run = v * A[h];
-    // inclusive scan inside the 64-wide wave
-    const int lane = i & 63;
+__global__ __launch_bounds__(256) void chunk_cumsum_kernel(const float* __restrict__ dt,
+                                                           const float* __restrict__ A,
+                                                           float* __restrict__ dtc,
+                                                           float* __restrict__ cs, int T, int H,
+                                                           int nC) {
+    constexpr int E = Q / 64;       // steps per lane
+    constexpr int LD = Q + 4;       // padded row: 16-byte aligned, conflict-free writes
+    __shared__ __align__(16) float tile[kHB][LD];
+    const int hblocks = (H + kHB - 1) / kHB;
+    const int hb = blockIdx.x % hblocks;
+    const int bc = blockIdx.x / hblocks;
+    const int c = bc % nC;
+    const int b = bc / nC;
+    const int h0 = hb * kHB;
+    const int nh = min(kHB, H - h0);
+    const int t0 = c * Q;
+    const int Lc = min(Q, T - t0);
+    const int tid = threadIdx.x;
+    const float* src = dt + ((size_t)b * T + t0) * H + h0;
+#pragma unroll  // all loads in flight at once: the kernel is latency-bound
+    for (int e = tid; e < Q * kHB; e += 256) {
+        const int t = e / kHB, hh = e % kHB;
+        tile[hh][t] = (t < Lc && hh < nh) ? src[(size_t)t * H + hh] : 0.0f;
+    }
+    __syncthreads();
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int hh = wave; hh < nh; hh += 4) {
+        const int h = h0 + hh;
+        const float a = A[h];
+        float v[E], run[E];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(run, off, 64);
-        if (lane >= off) run += o;
+        for (int k = 0; k < E; ++k) v[k] = tile[hh][lane * E + k];
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            acc += v[k] * a;
+            run[k] = acc;
+        }
+        // exclusive carry from the lanes before this one
+        float incl = acc;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float o = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += o;
+        }
+        const float carry = incl - acc;
+        const size_t o = (((size_t)b * H + h) * nC + c) * Q + lane * E;
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            dtc[o + k] = v[k];
+            cs[o + k] = run[k] + carry;
+        }
     }
-    if (kWaves > 1) {
-        if (lane == 63) wave_sum[i >> 6] = run;
-        __syncthreads();
-        float carry = 0.0f;
-        for (int w = 0; w < (i >> 6); ++w) carry += wave_sum[w];
-        run += carry;
-    }
-    const size_t o = ((size_t)bh * nC + c) * Q + i;
-    dtc[o] = v;
-    cs[o] = run;
 }
 
 }  // namespace
 
 hipError_t launch_chunk_cumsum(const Shape& s, const float* dt, const float* A, float* dtc,
                                float* cs, hipStream_t st) {
-    const unsigned blocks = (unsigned)((size_t)s.B * s.H * s.nC);
+    const size_t hblocks = (size_t)(s.H + kHB - 1) / kHB;
+    const unsigned blocks = (unsigned)((size_t)s.B * s.nC * hblocks);
     if (blocks == 0) return hipSuccess;
     switch (s.Q) {
         case 64:
-            chunk_cumsum_kernel<64><<<blocks, 64, 0, st>>>(dt, A, dtc, cs, s.T, s.H, s.nC);
+            chunk_cumsum_kernel<64><<<blocks, 256, 0, st>>>(dt, A, dtc, cs, s.T, s.H, s.nC);
             break;
         case 128:
-            chunk_cumsum_kernel<128><<<blocks, 128, 0, st>>>(dt, A, dtc, cs, s.T, s.H, s.nC);
+            chunk_cumsum_kernel<128><<<blocks, 256, 0, st>>>(dt, A, dtc, cs, s.T, s.H, s.nC);
             break;
         case 256:
             chunk_cumsum_kernel<256><<<blocks, 256, 0, st>>>(dt, A, dtc, cs, s.T, s.H, s.nC);

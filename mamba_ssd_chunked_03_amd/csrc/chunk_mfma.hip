@@ -15,6 +15,9 @@
 //     a double-buffered LDS while the previous item computes.  The per-step weight
 //     exp(cs_last - cs_i) dt_i is applied to the B fragments (rounded to bf16 once per
 //     item), and x^T comes out of LDS through transpose reads.
+//     At Q = 256 the workgroup that meets a unit's first head also writes the unit's
+//     C B^T blocks for the chunk scan (what chunk_gram does): the B chunk is already in
+//     LDS, so only C rows are read (wave w: row tiles w and 15 - w, the blocks below them).
 //   chunk_state_mfma_kernel (other shapes): one workgroup per (b, h, chunk); 32-step slices
 //     of B and x are transposed through registers into LDS ([feature][time], two time
 //     steps per 32-bit word) and double-buffered; x' is formed in fp32 and rounded once.
@@ -87,11 +90,17 @@ __device__ __forceinline__ void state_issue_b(const __bf16* Bm, int unit, int T,
     }
 }
 
+// pair index of (16-row tile t, 32-step block ib <= t/2) in tile-major order (the chunk
+// scan's layout of the C B^T blocks)
+__device__ __forceinline__ int gram_pair_base(int t) {
+    return (t & 1) ? (t / 2 + 1) * (t / 2 + 1) : (t / 2) * (t / 2 + 1);
+}
+
 template <int Q, int N, int P>
 __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ Bm, const float* __restrict__ dtc,
-    const float* __restrict__ cs, float* __restrict__ states, int T, int H, int G, int nC,
-    int nslots) {
+    const float* __restrict__ cs, float* __restrict__ states, const __bf16* __restrict__ Cm,
+    uint4* __restrict__ gram, int T, int H, int G, int nC, int nslots) {
     using C_ = StateCfg<Q, N, P>;
     constexpr int NB = C_::NB, PT = C_::PT, PPR = C_::PPR, NPR = C_::NPR;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -147,6 +156,51 @@ __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_ker
                 const uint2 lo2 = lds_read_tr16(bp);
                 const uint2 hi2 = lds_read_tr16(bp + BHALF);
                 bt[ib] = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+            }
+            constexpr bool kGram = (Q == 256 && N == 128);
+            if (kGram && gram != nullptr && sl == unit * hpg) {
+                // C B^T blocks of this unit (this workgroup holds its first head): wave w
+                // takes row tiles w and 15 - w and every block at or below them
+                const int c = unit % nC, g = (unit / nC) % G, b = unit / nC / G;
+                const int Lc = min(Q, T - c * Q);
+                const unsigned crow = (unsigned)(G * N * 2);
+                const __amdgpu_buffer_rsrc_t cr =
+                    make_rsrc(Cm + ((size_t)(b * T + c * Q) * G + g) * N, (unsigned)Lc * crow);
+                constexpr int NK = N / 32, NPAIR = 72;
+                const int ta = wave, tb = 15 - wave;
+                const int na = ta / 2 + 1, nb = tb / 2 + 1;
+                bf16x8 ca[NK], cb[NK];
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) {
+                    const unsigned col = (32 * kk + 8 * g4) * 2u;
+                    ca[kk] = __builtin_bit_cast(bf16x8, buf_load16(cr, (unsigned)(ta * 16 + l16) * crow + col));
+                    cb[kk] = __builtin_bit_cast(bf16x8, buf_load16(cr, (unsigned)(tb * 16 + l16) * crow + col));
+                }
+                uint4* gu = gram + (size_t)unit * NPAIR * 64 + lane;
+#pragma unroll 1
+                for (int ib = 0; ib < nb; ++ib) {
+                    bf16x8 r0[NK], r1[NK];  // B rows 32 ib + l16 and + 16, n-slice kk
+#pragma unroll
+                    for (int kk = 0; kk < NK; ++kk) {
+                        r0[kk] = *reinterpret_cast<const bf16x8*>(
+                            sB + swz_off(ib * KB + l16, 32 * kk + 8 * g4, NPR));
+                        r1[kk] = *reinterpret_cast<const bf16x8*>(
+                            sB + swz_off(ib * KB + 16 + l16, 32 * kk + 8 * g4, NPR));
+                    }
+                    auto emit = [&](const bf16x8* cc, int t) {
+                        f32x4 g0 = f32x4{0.f, 0.f, 0.f, 0.f}, g1 = g0;
+#pragma unroll
+                        for (int kk = 0; kk < NK; ++kk) {
+                            g0 = mfma16(r0[kk], cc[kk], g0);
+                            g1 = mfma16(r1[kk], cc[kk], g1);
+                        }
+                        gu[(size_t)(gram_pair_base(t) + ib) * 64] =
+                            make_uint4(pack_bf16(g0[0], g0[1]), pack_bf16(g0[2], g0[3]),
+                                       pack_bf16(g1[0], g1[1]), pack_bf16(g1[2], g1[3]));
+                    };
+                    if (ib < na) emit(ca, ta);
+                    emit(cb, tb);
+                }
             }
             lds_barrier();  // every wave holds its fragments: the region is free
             const int nxt = (unit + 1) * hpg;
@@ -329,7 +383,7 @@ __global__ __launch_bounds__(256) void chunk_state_mfma_kernel(
 
 template <int Q, int N, int P>
 hipError_t launch_state_t(const Shape& s, const void* x, const void* Bm, const float* dtc,
-                          const float* cs, float* states, hipStream_t st) {
+                          const float* cs, float* states, const void*, void*, hipStream_t st) {
     const unsigned blocks = (unsigned)((size_t)s.B * s.H * s.nC);
     chunk_state_mfma_kernel<Q, N, P><<<blocks, 256, 0, st>>>(
         (const __bf16*)x, (const __bf16*)Bm, dtc, cs, states, s.T, s.H, s.G, s.nC);
@@ -346,7 +400,7 @@ hipError_t launch_state_t(const Shape& s, const void* x, const void* Bm, const f
     break;
 
 using StateFn = hipError_t (*)(const Shape&, const void*, const void*, const float*, const float*,
-                               float*, hipStream_t);
+                               float*, const void*, void*, hipStream_t);
 
 template <int Q>
 StateFn pick_state_q(const Shape& s) {
@@ -360,7 +414,8 @@ StateFn pick_state_q(const Shape& s) {
 
 template <int Q, int N, int P>
 hipError_t launch_state_pipe_t(const Shape& s, const void* x, const void* Bm, const float* dtc,
-                               const float* cs, float* states, hipStream_t st) {
+                               const float* cs, float* states, const void* Cm, void* gram,
+                               hipStream_t st) {
     using C_ = StateCfg<Q, N, P>;
     const auto kern = chunk_state_pipe_kernel<Q, N, P>;
     static int grid_of[64];  // per device: resident workgroups, a multiple of 8
@@ -382,7 +437,8 @@ hipError_t launch_state_pipe_t(const Shape& s, const void* x, const void* Bm, co
     }
     const int nslots = s.B * s.G * s.nC * (s.H / s.G);
     kern<<<grid_of[dev], C_::NTH, C_::LDS, st>>>((const __bf16*)x, (const __bf16*)Bm, dtc, cs,
-                                                  states, s.T, s.H, s.G, s.nC, nslots);
+                                                  states, (const __bf16*)Cm, (uint4*)gram, s.T,
+                                                  s.H, s.G, s.nC, nslots);
     return hipGetLastError();
 }
 
@@ -425,13 +481,18 @@ StateFn pick_state(const Shape& s) {
 
 bool chunk_state_mfma_supported(const Shape& s) { return pick_state(s) != nullptr; }
 
+bool chunk_state_writes_gram(const Shape& s) {
+    return state_offsets_fit(s) && s.Q == 256 && s.N == 128 && pick_state_pipe_q<256>(s) != nullptr;
+}
+
 hipError_t launch_chunk_state_mfma(const Shape& s, const void* x, const void* Bm,
                                    const float* dtc, const float* cs, float* states,
-                                   hipStream_t st) {
+                                   const void* Cm, void* gram, hipStream_t st) {
     StateFn f = pick_state(s);
     if (!f) return hipErrorInvalidValue;
     if ((size_t)s.B * s.H * s.nC == 0) return hipSuccess;
-    return f(s, x, Bm, dtc, cs, states, st);
+    const bool fuse = gram != nullptr && Cm != nullptr && chunk_state_writes_gram(s);
+    return f(s, x, Bm, dtc, cs, states, fuse ? Cm : nullptr, fuse ? gram : nullptr, st);
 }
 
 }  // namespace ssd

@@ -107,7 +107,16 @@ struct ScanCfg {
     static constexpr unsigned XB = Q * P * 2, EB = P * N * 2, FB = Q * 4;
     static constexpr unsigned ITEM = XB + EB + 2 * FB;  // x, entry state, cs, dt
     static constexpr unsigned TAIL = 2 * FB;            // cs*log2(e), block-end weights
-    static constexpr int NBUF = (2 * ITEM + TAIL <= 160u * 1024u) ? 2 : 1;
+    // copy instructions per wave per item: PT for x (Q P / 512 over Q / 32 waves), the
+    // entry state's share, and cs / dt on waves 0 / 1
+    static constexpr int EI = P * NPR / 64;
+    static constexpr bool EVEN = EI % NW == 0;
+    static constexpr int DMA_LO = PT + EI / NW, DMA_HI = DMA_LO + 1;
+    // three buffers (copies two items ahead) where they fit and the per-wave copy counts
+    // are known, else two, else one
+    static constexpr int NBUF = (EVEN && 3 * ITEM + TAIL <= 160u * 1024u) ? 3
+                              : (2 * ITEM + TAIL <= 160u * 1024u)         ? 2
+                                                                          : 1;
     static constexpr unsigned LDS = NBUF * ITEM + TAIL;
     static constexpr int STORES = 2 * PT;  // y stores per wave per item
 };
@@ -179,12 +188,6 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
     const unsigned rowb = (unsigned)(H * P * 2);
     const unsigned crow = (unsigned)(G * N * 2);
 
-    // loop-invariant LDS offsets inside one buffer.  x^T operand of block ib: rows
-    // 32 ib + 4 g4 + l16 / 4 (and + 16), column p * 16 + 4 (l16 % 4); the swizzle depends
-    // only on the row mod PPR, which a whole block does not change.
-    unsigned xoff[PT];
-#pragma unroll
-    for (int p = 0; p < PT; ++p) xoff[p] = swz_off(4 * g4 + (l16 >> 2), p * 16 + 4 * (l16 & 3), PPR);
     constexpr unsigned XBLK = KB * PPR * 16;   // bytes of 32 rows of x
     constexpr unsigned XHALF = 16 * PPR * 16;  // bytes of 16 rows
 
@@ -193,24 +196,71 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
     int cur_unit = -1;
 
     issue_item<Q, N, P>(x, E, cs, dtc, lo, hpg, T, H, G, nC, lds0, wave, lane);
+    if (C_::NBUF == 3 && lo + 1 < hi)
+        issue_item<Q, N, P>(x, E, cs, dtc, lo + 1, hpg, T, H, G, nC, lds0 + C_::ITEM, wave, lane);
+    int buf = 0;  // buffer of the current item
 #pragma unroll 1
     for (int sl = lo; sl < hi; ++sl) {
         const int n = sl - lo;
-        const int buf = (C_::NBUF == 2) ? (n & 1) : 0;
         unsigned char* bx = smem + buf * C_::ITEM;
         const float* b_cs = reinterpret_cast<const float*>(bx + C_::XB + C_::EB);
         const float* b_dt = b_cs + Q;
-        // this item's copies have landed once only the previous item's stores are pending
-        if (n == 0 || C_::NBUF == 1)
+        // This item's copies have landed once only what was issued after them is pending:
+        // with three buffers the next item's copies and the previous item's stores, with
+        // two the previous item's stores.
+        if (C_::NBUF == 3) {
+            const bool more = sl + 1 < hi;
+            if (n == 0 && !more)
+                asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+            else if (n == 0 && wave < 2)
+                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::DMA_HI) : "memory");
+            else if (n == 0)
+                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::DMA_LO) : "memory");
+            else if (!more)
+                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::STORES) : "memory");
+            else if (wave < 2)
+                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::DMA_HI + C_::STORES)
+                             : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::DMA_LO + C_::STORES)
+                             : "memory");
+        } else if (n == 0 || C_::NBUF == 1) {
             asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        else
+        } else {
             asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::STORES) : "memory");
+        }
 
         const int unit = sl / hpg;
         const int c = unit % nC, g = (unit / nC) % G, b = unit / nC / G;
         const int h = g * hpg + sl % hpg;
         const int t0 = c * Q;
         const int Lc = min(Q, T - t0);
+        // block counts re-read each item (opaque copies): the compiler would otherwise
+        // hoist every block's branch condition out of the loop into spilled SGPR masks
+        // Lane-derived offsets and masks are recomputed every item from an opaque copy of
+        // the lane id, and the block counts re-read: otherwise the compiler hoists them
+        // (and every block's branch condition and diagonal mask) out of the loop, and the
+        // registers they hold push the kernel into spills.
+        int nb0 = nblk0, nb1 = nblk1, ln = lane;
+        asm volatile("" : "+s"(nb0), "+s"(nb1), "+v"(ln));
+        const int ql16 = ln & 15, qg4 = ln >> 4;
+        // x^T operand of block ib: rows 32 ib + 4 g4 + l16 / 4 (and + 16), column
+        // p * 16 + 4 (l16 % 4); the swizzle depends only on the row mod PPR, which a whole
+        // block does not change
+        unsigned xoff[PT];
+#pragma unroll
+        for (int p = 0; p < PT; ++p)
+            xoff[p] = swz_off(4 * qg4 + (ql16 >> 2), p * 16 + 4 * (ql16 & 3), PPR);
+        // diagonal-block mask of each tile as 8 bits: k-slot k (steps 4 g4 + k and
+        // 16 + 4 g4 + k - 4 of the block) is at or below row j iff bit k is set
+        auto diag_bits = [&](int tile) {
+            const int jr = 16 * (tile & 1) + ql16 - 4 * qg4;
+            unsigned m = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) m |= (unsigned)((k < 4 ? k : 12 + k) <= jr) << k;
+            return m;
+        };
+        const unsigned db0 = diag_bits(tile0), db1 = diag_bits(tile1);
         if (tid < Q) {
             const float ci = b_cs[tid];
             s_c2[tid] = ci * kLog2e;
@@ -242,6 +292,11 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
             __builtin_amdgcn_s_waitcnt(0x0F70);
         }
         lds_barrier();
+        if (C_::NBUF == 3 && sl + 2 < hi) {  // into the buffer of the previous item
+            const int b2 = buf == 0 ? 2 : buf - 1;
+            issue_item<Q, N, P>(x, E, cs, dtc, sl + 2, hpg, T, H, G, nC, lds0 + b2 * C_::ITEM,
+                                wave, lane);
+        }
         if (C_::NBUF == 2 && sl + 1 < hi)
             issue_item<Q, N, P>(x, E, cs, dtc, sl + 1, hpg, T, H, G, nC,
                                 lds0 + (buf ^ 1) * C_::ITEM, wave, lane);
@@ -274,7 +329,7 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
         // stage 1: masked quadratic form, one 32-step block at a time
 #pragma unroll
         for (int ib = 0; ib < NB; ++ib) {
-            if (ib >= nblk1) break;  // nblk1 >= nblk0
+            if (ib >= nb1) break;  // nb1 >= nb0
             bf16x8 xa[PT];
 #pragma unroll
             for (int p = 0; p < PT; ++p) {
@@ -285,7 +340,7 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
             }
             const int i0 = ib * KB + 4 * g4;
             // masked, decayed Gram block of one tile -> MFMA operand
-            auto block = [&](const uint4 gv4, int nblk, int j, float csj) -> bf16x8 {
+            auto block = [&](const uint4 gv4, int nblk, unsigned dbits, float csj) -> bf16x8 {
                 float m[8];
                 if (ib < nblk - 1) {  // wholly below the tile: decay factored at block end
                     const float f = exp2_fast(csj - s_c2[ib * KB + KB - 1]);
@@ -305,12 +360,17 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
                     const float gv[8] = {bf16_lo(gv4.x), bf16_hi(gv4.x), bf16_lo(gv4.y),
                                          bf16_hi(gv4.y), bf16_lo(gv4.z), bf16_hi(gv4.z),
                                          bf16_lo(gv4.w), bf16_hi(gv4.w)};
-                    const float ninf = -__builtin_inff();
-                    const int jr = j - i0;  // k-slot q is at or below the diagonal iff q <= jr
+                    // exponent -inf above the diagonal: bit k of dbits, sign-extended to a
+                    // full mask, selects between the exponent and -inf bit by bit
+                    const unsigned ninf = 0xff800000u;
+                    unsigned dbl = dbits;  // opaque here too: masks are made where used
+                    asm volatile("" : "+v"(dbl));
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const float ea = q <= jr ? csj - cav[q] : ninf;
-                        const float ec = 16 + q <= jr ? csj - cbv[q] : ninf;
+                        const unsigned ma = (unsigned)__builtin_amdgcn_sbfe((int)dbl, q, 1);
+                        const unsigned mc = (unsigned)__builtin_amdgcn_sbfe((int)dbl, 4 + q, 1);
+                        const float ea = __uint_as_float((__float_as_uint(csj - cav[q]) & ma) | (ninf & ~ma));
+                        const float ec = __uint_as_float((__float_as_uint(csj - cbv[q]) & mc) | (ninf & ~mc));
                         m[q] = gv[q] * exp2_fast(ea) * dav[q];
                         m[4 + q] = gv[4 + q] * exp2_fast(ec) * dbv[q];
                     }
@@ -319,13 +379,13 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
                     bf16x8, make_uint4(pack_bf16(m[0], m[1]), pack_bf16(m[2], m[3]),
                                        pack_bf16(m[4], m[5]), pack_bf16(m[6], m[7])));
             };
-            if (ib < NB0 && ib < nblk0) {
-                const bf16x8 bm = block(gf0[ib < NB0 ? ib : 0], nblk0, j0, csj0);
+            if (ib < NB0 && ib < nb0) {
+                const bf16x8 bm = block(gf0[ib < NB0 ? ib : 0], nb0, db0, csj0);
 #pragma unroll
                 for (int p = 0; p < PT; ++p) acc0[p] = mfma16(xa[p], bm, acc0[p]);
             }
             {
-                const bf16x8 bm = block(gf1[ib], nblk1, j1, csj1);
+                const bf16x8 bm = block(gf1[ib], nb1, db1, csj1);
 #pragma unroll
                 for (int p = 0; p < PT; ++p) acc1[p] = mfma16(xa[p], bm, acc1[p]);
             }
@@ -353,6 +413,7 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
             lds_barrier();  // every wave is done with the buffer
             issue_item<Q, N, P>(x, E, cs, dtc, sl + 1, hpg, T, H, G, nC, lds0, wave, lane);
         }
+        buf = (C_::NBUF == 1) ? 0 : (buf + 1 == C_::NBUF ? 0 : buf + 1);
     }
 }
 

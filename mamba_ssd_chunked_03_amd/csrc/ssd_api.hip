@@ -89,15 +89,25 @@ bool any_misaligned4(std::initializer_list<const void*> ptrs) {
     return false;
 }
 
-ssd_status run_chunk_state(const Shape& s, ssd_dtype dtype, const void* x, const void* B,
-                           const float* dtc, const float* cs, float* states, hipStream_t st) {
-    if (dtype == SSD_BF16 && ssd::chunk_state_mfma_supported(s))
-        return hip_status(ssd::launch_chunk_state_mfma(s, x, B, dtc, cs, states, st));
-    return hip_status(ssd::launch_chunk_state_valu(s, dtype, x, B, dtc, cs, states, st));
-}
-
 bool uses_gram(const Shape& s, ssd_dtype dtype) {
     return dtype == SSD_BF16 && ssd::chunk_scan_mfma_supported(s);
+}
+
+// chunk states; with C and gram given (and a gram buffer in use for the shape) also the
+// chunk scan's C B^T blocks, in the same launch where the kernel can, else right after
+ssd_status run_chunk_state(const Shape& s, ssd_dtype dtype, const void* x, const void* B,
+                           const float* dtc, const float* cs, float* states, const void* C,
+                           void* gram, hipStream_t st) {
+    const bool want_gram = C != nullptr && gram != nullptr && uses_gram(s, dtype);
+    if (dtype == SSD_BF16 && ssd::chunk_state_mfma_supported(s)) {
+        ssd_status r = hip_status(ssd::launch_chunk_state_mfma(
+            s, x, B, dtc, cs, states, want_gram ? C : nullptr, want_gram ? gram : nullptr, st));
+        if (r != SSD_OK || !want_gram || ssd::chunk_state_writes_gram(s)) return r;
+    } else {
+        ssd_status r = hip_status(ssd::launch_chunk_state_valu(s, dtype, x, B, dtc, cs, states, st));
+        if (r != SSD_OK || !want_gram) return r;
+    }
+    return hip_status(ssd::launch_chunk_gram(s, B, C, gram, st));
 }
 
 ssd_status run_chunk_scan(const Shape& s, ssd_dtype dtype, const void* x, const void* B,
@@ -143,14 +153,17 @@ ssd_status ssd_chunk_cumsum(const ssd_dims* dims, int chunk_len, const float* dt
 
 ssd_status ssd_chunk_state(const ssd_dims* dims, ssd_dtype dtype, int chunk_len, const void* x,
                            const void* B, const float* dt_chunk, const float* cs, float* states,
-                           void* stream) {
+                           const void* C, void* gram, void* stream) {
     Shape s;
     ssd_status r = make_shape(dims, chunk_len, &s);
     if (r != SSD_OK) return r;
     if (!valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
     if ((size_t)s.B * s.T > 0 && (!x || !B || !dt_chunk || !cs || !states)) return SSD_ERR_NULL;
-    if (any_misaligned({x, B, dt_chunk, cs, states})) return SSD_ERR_ALIGN;
-    return run_chunk_state(s, dtype, x, B, dt_chunk, cs, states, (hipStream_t)stream);
+    const bool want_gram = gram != nullptr && uses_gram(s, dtype);
+    if ((size_t)s.B * s.T > 0 && want_gram && !C) return SSD_ERR_NULL;
+    if (any_misaligned({x, B, dt_chunk, cs, states, C, gram})) return SSD_ERR_ALIGN;
+    return run_chunk_state(s, dtype, x, B, dt_chunk, cs, states, want_gram ? C : nullptr,
+                           want_gram ? gram : nullptr, (hipStream_t)stream);
 }
 
 ssd_status ssd_state_passing(const ssd_dims* dims, ssd_dtype dtype, int chunk_len,
@@ -224,17 +237,13 @@ ssd_status ssd_fwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const f
     if (has_tokens) {
         r = hip_status(ssd::launch_chunk_cumsum(s, dt, A, ws.dtc, ws.cs, st));
         if (r != SSD_OK) return r;
-        r = run_chunk_state(s, dtype, x, B, ws.dtc, ws.cs, ws.states, st);
+        r = run_chunk_state(s, dtype, x, B, ws.dtc, ws.cs, ws.states, C, ws.gram, st);
         if (r != SSD_OK) return r;
     }
     // with T == 0 this only copies init_state (or zeros) to final_state
     r = hip_status(ssd::launch_state_passing(s, dtype, ws.states, ws.cs, init_state, ws.entry,
                                              final_state, st));
     if (r != SSD_OK || !has_tokens) return r;
-    if (uses_gram(s, dtype)) {
-        r = hip_status(ssd::launch_chunk_gram(s, B, C, ws.gram, st));
-        if (r != SSD_OK) return r;
-    }
     return run_chunk_scan(s, dtype, x, B, C, ws.dtc, ws.cs, D, ws.entry, ws.gram, y, st);
 }
 

@@ -42,9 +42,12 @@ hipError_t launch_chunk_scan_valu(const Shape& s, ssd_dtype dt, const void* x, c
 // bf16 MFMA kernels (gfx950 v_mfma_f32_16x16x32_bf16); *_supported says whether a shape
 // has an instantiation.
 bool chunk_state_mfma_supported(const Shape& s);
+// With Cm and gram given, where chunk_state_writes_gram(s) the same launch also writes the
+// chunk scan's C B^T blocks (else it ignores them).
+bool chunk_state_writes_gram(const Shape& s);
 hipError_t launch_chunk_state_mfma(const Shape& s, const void* x, const void* Bm,
                                    const float* dtc, const float* cs, float* states,
-                                   hipStream_t st);
+                                   const void* Cm, void* gram, hipStream_t st);
 bool chunk_scan_mfma_supported(const Shape& s);
 // bytes of the C B^T blocks the MFMA chunk scan reads (0 where the shape has no MFMA scan)
 size_t chunk_gram_bytes(const Shape& s);

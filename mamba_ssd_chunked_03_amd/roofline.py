@@ -5,9 +5,9 @@ read once and every output written once per launch; the quadratic part counts on
 causal half of each Q x Q diagonal block (the method never needs the upper triangle),
 and C B^T is counted once per (batch, group, chunk) because the heads of a group share
 it.  Bytes use the dtype sizes of the boundary (x, B, C, y in the input dtype; dt, cs
-and the states in fp32).  Where the chunk scan takes C B^T from a separate chunk_gram
-launch (gram_bytes > 0: the bf16 matrix-core path), that launch reads B and C and writes
-the gram blocks once, and the scan reads them once in place of B.
+and the states in fp32).  Where the chunk scan takes C B^T from a gram buffer (gram_bytes > 0:
+the bf16 matrix-core path), the chunk_state stage also computes it (reading C, writing
+the blocks once) and the scan reads the blocks once in place of B.
 """
 from dataclasses import dataclass
 
@@ -35,23 +35,23 @@ def kernel_costs(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len, dty
     io_bc = B * T * G * N * e               # B or C
     st1 = B * H * N * P * 4                 # init or final state
     cumsum = KernelCost("chunk_cumsum", B * T * H * 4 + H * 4 + 2 * chunk_f32, 2.0 * B * T * H)
-    state = KernelCost("chunk_state", io_xy + io_bc + 2 * chunk_f32 + state_f32,
-                       2.0 * B * H * T * N * P)
+    full, rem = divmod(T, Q)
+    tri = full * Q * (Q + 1) + rem * (rem + 1)          # sum of 2*(j+1) over valid rows
+    gram_flops = B * G * tri * N
+    state = KernelCost("chunk_state", io_xy + io_bc + 2 * chunk_f32 + state_f32
+                       + (io_bc + gram_bytes if gram_bytes else 0),
+                       2.0 * B * H * T * N * P + (gram_flops if gram_bytes else 0))
     passing = KernelCost("state_passing",
                          state_f32 + entry + B * H * nC * 4 + (st1 if init_state else 0)
                          + (st1 if final_state else 0),
                          2.0 * B * H * nC * N * P)
     # intra-chunk: sum over rows j of (j+1) MACs x P, per (b, h, chunk); C B^T likewise
     # per (b, g, chunk) over N; off-chunk: Q x N x P MACs per (b, h, chunk)
-    full, rem = divmod(T, Q)
-    tri = full * Q * (Q + 1) + rem * (rem + 1)          # sum of 2*(j+1) over valid rows
-    gram_flops = B * G * tri * N
     if gram_bytes:
-        gram = KernelCost("chunk_gram", 2 * io_bc + gram_bytes, gram_flops)
         scan = KernelCost("chunk_scan",
                           2 * io_xy + io_bc + gram_bytes + 2 * chunk_f32 + entry + H * 4,
                           B * H * tri * P + 2.0 * B * H * T * N * P)
-        return [cumsum, state, passing, gram, scan]
+        return [cumsum, state, passing, scan]
     scan = KernelCost("chunk_scan",
                       2 * io_xy + 2 * io_bc + 2 * chunk_f32 + entry + H * 4,
                       B * H * tri * P + gram_flops + 2.0 * B * H * T * N * P)

@@ -100,7 +100,14 @@ def test_validation_errors_before_any_launch(lib):
     # stage entry points validate the same way
     assert lib.ssd_chunk_cumsum(ctypes.byref(D(p=40)), 64, None, None, None, None, None) == 3
     assert lib.ssd_chunk_cumsum(ctypes.byref(D()), 64, None, None, None, None, None) == 1
-    assert lib.ssd_chunk_state(ctypes.byref(D()), 1, 64, None, None, None, None, None, None) == 1
+    assert lib.ssd_chunk_state(ctypes.byref(D()), 1, 64, None, None, None, None, None, None,
+                               None, None) == 1
+    # a gram buffer needs C (bf16, a shape with a matrix-core scan)
+    ok5 = [ctypes.c_void_p(256)] * 5
+    assert lib.ssd_chunk_state(ctypes.byref(D(p=64, n=64)), 1, 64, *ok5, None,
+                               ctypes.c_void_p(256), None) == 1
+    assert lib.ssd_chunk_state(ctypes.byref(D(p=64, n=64)), 1, 64, *ok5, ctypes.c_void_p(256),
+                               ctypes.c_void_p(264), None) == 4
     assert lib.ssd_state_passing(ctypes.byref(D()), 0, 64, ctypes.c_void_p(64),
                                  ctypes.c_void_p(64), None, ctypes.c_void_p(64), None,
                                  None) == 2   # aliasing

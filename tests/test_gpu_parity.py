@@ -246,6 +246,7 @@ SWEEP = [  # (headdim P, dstate N, chunk Q, groups)
     (16, 64, 64, 1), (32, 32, 128, 2), (64, 256, 256, 1), (128, 128, 128, 2),
     (128, 256, 64, 1), (16, 256, 128, 2), (64, 64, 256, 2), (128, 32, 256, 1),
     (32, 128, 64, 1), (64, 128, 128, 1), (128, 64, 256, 2), (16, 16, 64, 1),
+    (16, 128, 256, 2),
 ]
 
 
@@ -263,3 +264,56 @@ def test_shape_sweep_matches_oracle(shape):
     ey, ef = rel_l2(np64(y), y_ref), rel_l2(np64(fin), f_ref)
     say(f"    rel_l2 y={ey:.3e} final={ef:.3e}")
     assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ persistent pipelines
+
+PIPE = [  # (batch, seqlen, heads, headdim P, dstate N, groups, chunk Q)
+    (2, 16384, 8, 64, 128, 4, 256),   # 4 items per workgroup, crossing units
+    (1, 32768, 4, 32, 128, 2, 128),
+    (2, 16384, 4, 128, 128, 2, 256),  # single-buffered scan
+    (1, 8192, 6, 16, 128, 3, 64),
+]
+
+
+@pytest.mark.parametrize("shape", PIPE, ids=[f"B{b}_T{t}_H{h}_P{p}_N{n}_G{g}_Q{q}"
+                                             for b, t, h, p, n, g, q in PIPE])
+def test_pipelined_runs_match_oracle(shape):
+    """Enough (unit, head) items that each persistent workgroup walks several of them,
+    across unit boundaries, so the prefetched copies and the register-resident per-unit
+    operands are all exercised; slow decay keeps every carried state visible."""
+    Bz, T, H, P, N, G, Q = shape
+    w = Workload(f"pipe_{Bz}_{T}_{H}_{P}_{N}_{G}_{Q}", Bz, T, H, P, N, G, Q, init_state=True,
+                 log_neg_a_range=(np.log(0.005), np.log(0.05)))
+    say(f"[pipeline] {w.describe()}")
+    cpu = generate(w)
+    y, fin = gpu_fwd(to_device(cpu), Q)
+    y_ref, f_ref = oracle_fwd(cpu)
+    ey, ef = rel_l2(np64(y), y_ref), rel_l2(np64(fin), f_ref)
+    say(f"    rel_l2 y={ey:.3e} final={ef:.3e}")
+    assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
+
+
+GRAM_CASES = [  # (batch, seqlen, heads, headdim P, dstate N, groups, chunk Q)
+    (2, 4096 + 77, 6, 64, 128, 3, 256),   # blocks written by the states kernel itself
+    (1, 8192, 16, 32, 128, 2, 256),       # several units per workgroup
+    (1, 1000, 4, 64, 64, 2, 128),         # separate launch after the states kernel
+]
+
+
+@pytest.mark.parametrize("shape", GRAM_CASES, ids=[f"B{b}_T{t}_H{h}_P{p}_N{n}_G{g}_Q{q}"
+                                                   for b, t, h, p, n, g, q in GRAM_CASES])
+def test_chunk_state_fills_the_same_gram_blocks(shape):
+    """ssd_chunk_state given a gram buffer writes exactly what ssd_chunk_gram writes."""
+    Bz, T, H, P, N, G, Q = shape
+    w = Workload(f"gram_{Bz}_{T}_{H}_{P}_{N}_{G}_{Q}", Bz, T, H, P, N, G, Q)
+    say(f"[gram via chunk_state] {w.describe()}")
+    dv = to_device(generate(w))
+    d = _dims(w)
+    dtc, cs = binding.ssd_chunk_cumsum(d, Q, dv["dt"], dv["A"])
+    ref = binding.ssd_chunk_gram(d, Q, dv["B"], dv["C"])
+    assert ref.numel() > 0
+    got = torch.full_like(ref, 0x5A)
+    binding.ssd_chunk_state(d, Q, dv["x"], dv["B"], dtc, cs, C=dv["C"], gram=got)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
