@@ -148,7 +148,7 @@ def main():
     cshape = (w.batch, w.nheads, nC, Q)
     sshape = (w.batch, w.nheads, nC, w.headdim, w.dstate)
     dtc, cs = view(offs[0], chunk_n, cshape), view(offs[1], chunk_n, cshape)
-    S = view(offs[2], state_n, sshape)
+    S = view(offs[2], state_n, sshape, d_in["x"].dtype)   # chunk states in the input dtype
     E = view(offs[3], state_n, sshape, d_in["x"].dtype)   # entry states in the input dtype
     gram = ws[offs[4]:offs[4] + gram_n]                     # C B^T blocks (bf16 path)
 

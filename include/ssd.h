@@ -41,8 +41,8 @@
  *   - Supported sizes: chunk_len in {64, 128, 256}; dstate N in {16, 32, 64, 128, 256};
  *     headdim P in {16, 32, 64, 128}; ngroups G >= 1 dividing nheads H; any seqlen
  *     T >= 0 (the last chunk may be partial); batch >= 0; B*T*H*P < 2^31 elements per
- *     tensor.  dtype SSD_F32 or SSD_BF16 for x, B, C and y; dt, A, D and the states are
- *     always fp32.
+ *     tensor.  dtype SSD_F32 or SSD_BF16 for x, B, C and y (and the stored chunk and
+ *     entry states); dt, A, D, init_state, final_state and cs are always fp32.
  *
  * Tensor layouts
  *   x, y           [batch][seqlen][nheads][headdim]       in `dtype`
@@ -51,9 +51,11 @@
  *   B, C           [batch][seqlen][ngroups][dstate]       in `dtype`
  *   init_state, final_state  [batch][nheads][dstate][headdim]   fp32
  *   dt_chunk, cs   [batch][nheads][nchunks][chunk_len]    fp32, nchunks = ceil(T/chunk_len)
- *   chunk states   [batch][nheads][nchunks][headdim][dstate]   fp32
+ *   chunk states   [batch][nheads][nchunks][headdim][dstate]   in `dtype`
  *   entry states   [batch][nheads][nchunks][headdim][dstate]   in `dtype` (the chunk scan
- *                  consumes them as operands of that dtype; the carried state is fp32)
+ *                  consumes them as operands of that dtype; the state carried from chunk
+ *                  to chunk is fp32, and each chunk's state is rounded to `dtype` once
+ *                  when it is stored)
  *     (state buffers are headdim-major: the transpose of the N x P state of the formulas)
  */
 #ifndef LIBSSD_SSD_H
@@ -122,25 +124,26 @@ ssd_status ssd_chunk_cumsum(const ssd_dims* dims, int chunk_len, const float* dt
  * chunk when the chunk starts from zero, i.e. from the chunk's own inputs only:
  *     states[b][h][c][p][n] = sum_i exp(cs[c][Q-1] - cs[c][i]) * dt_chunk[c][i]
  *                                   * B[b][cQ+i][g][n] * x[b][cQ+i][h][p]
- * (sum over the chunk's valid positions i).  dt_chunk and cs come from ssd_chunk_cumsum.
+ * (sum over the chunk's valid positions i), accumulated in fp32 and stored in `dtype`.
+ * dt_chunk and cs come from ssd_chunk_cumsum.
  * gram: NULL, or a buffer of ssd_chunk_gram_size bytes that is also filled exactly as
  * ssd_chunk_gram(dims, dtype, chunk_len, B, C, gram) would fill it (C is then required;
  * where ssd_chunk_gram_size is 0 both are ignored).  The states kernel already holds each
  * chunk's B, so for some shapes the blocks come from the same pass. */
 ssd_status ssd_chunk_state(const ssd_dims* dims, ssd_dtype dtype, int chunk_len,
                            const void* x, const void* B, const float* dt_chunk,
-                           const float* cs, float* states, const void* C, void* gram,
+                           const float* cs, void* states, const void* C, void* gram,
                            void* stream);
 
 /* Stage 3 (same section, "Propagate states between chunks"): the sequential 1-SS scan
  * over chunks.  With E_0 = init_state (zeros if NULL), carried in fp32,
  *     entry_states[c] = E_c,   E_{c+1} = exp(cs[c][Q-1]) * E_c + states[c]
  * and final_state = E_nchunks (the state after the last step, fp32; NULL to skip).
- * entry_states are written in `dtype` (bf16: rounded to nearest even).  entry_states may
- * not alias states (SSD_ERR_DIMS).  init_state/final_state use the [N][P] layout,
- * states/entry_states the [P][N] one. */
+ * states are read and entry_states written in `dtype` (bf16: rounded to nearest even).
+ * entry_states may not alias states (SSD_ERR_DIMS).  init_state/final_state use the
+ * [N][P] layout, states/entry_states the [P][N] one. */
 ssd_status ssd_state_passing(const ssd_dims* dims, ssd_dtype dtype, int chunk_len,
-                             const float* states, const float* cs, const float* init_state,
+                             const void* states, const float* cs, const float* init_state,
                              void* entry_states, float* final_state, void* stream);
 
 /* Bytes of the `gram` buffer that ssd_chunk_gram fills and ssd_chunk_scan reads for these

@@ -170,7 +170,7 @@ def ssd_chunk_state(dims, chunk_len, x, B, dt_chunk, cs, states=None, C=None, gr
     C B^T blocks that ssd_chunk_scan reads, as ssd_chunk_gram would."""
     dev = x.device
     if states is None:
-        states = torch.empty(_state_shape(dims, chunk_len), dtype=torch.float32, device=dev)
+        states = torch.empty(_state_shape(dims, chunk_len), dtype=x.dtype, device=dev)
     gp = _ptr(gram) if gram is not None and gram.numel() else None
     _check(library().ssd_chunk_state(ctypes.byref(dims), _DTYPE_CODE[x.dtype], int(chunk_len),
                                      _ptr(x), _ptr(B), _ptr(dt_chunk), _ptr(cs), _ptr(states),
@@ -179,11 +179,14 @@ def ssd_chunk_state(dims, chunk_len, x, B, dt_chunk, cs, states=None, C=None, gr
 
 
 def ssd_state_passing(dims, chunk_len, states, cs, init_state=None, entry_states=None,
-                      final_state=None, want_final=True, entry_dtype=torch.float32, stream=None):
-    """Entry states come back in entry_dtype (fp32 or bf16); final_state is fp32."""
+                      final_state=None, want_final=True, stream=None):
+    """Chunk states in, entry states out, both in the input dtype (fp32 or bf16);
+    final_state is fp32."""
     dev = cs.device
     if entry_states is None:
-        entry_states = torch.empty(_state_shape(dims, chunk_len), dtype=entry_dtype, device=dev)
+        entry_states = torch.empty(_state_shape(dims, chunk_len), dtype=states.dtype, device=dev)
+    if entry_states.dtype != states.dtype:
+        raise TypeError("states and entry_states must have the same dtype")
     if final_state is None and want_final:
         final_state = torch.empty((dims.batch, dims.nheads, dims.dstate, dims.headdim),
                                   dtype=torch.float32, device=dev)

@@ -39,10 +39,20 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const float* __restri
     const int Lc = min(Q, T - t0);
     const int tid = threadIdx.x;
     const float* src = dt + ((size_t)b * T + t0) * H + h0;
-#pragma unroll  // all loads in flight at once: the kernel is latency-bound
-    for (int e = tid; e < Q * kHB; e += 256) {
+    // element e = tid + 256 k of the Q x 16 tile: all loads are issued before any is used
+    // (the kernel is latency-bound)
+    constexpr int L = Q * kHB / 256;
+    float v_in[L];
+#pragma unroll
+    for (int k = 0; k < L; ++k) {
+        const int e = tid + 256 * k;
         const int t = e / kHB, hh = e % kHB;
-        tile[hh][t] = (t < Lc && hh < nh) ? src[(size_t)t * H + hh] : 0.0f;
+        v_in[k] = (t < Lc && hh < nh) ? src[(size_t)t * H + hh] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < L; ++k) {
+        const int e = tid + 256 * k;
+        tile[e % kHB][e / kHB] = v_in[k];
     }
     __syncthreads();
     const int wave = tid >> 6, lane = tid & 63;

@@ -99,7 +99,7 @@ __device__ __forceinline__ int gram_pair_base(int t) {
 template <int Q, int N, int P>
 __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ Bm, const float* __restrict__ dtc,
-    const float* __restrict__ cs, float* __restrict__ states, const __bf16* __restrict__ Cm,
+    const float* __restrict__ cs, __bf16* __restrict__ states, const __bf16* __restrict__ Cm,
     uint4* __restrict__ gram, int T, int H, int G, int nC, int nslots) {
     using C_ = StateCfg<Q, N, P>;
     constexpr int NB = C_::NB, PT = C_::PT, PPR = C_::PPR, NPR = C_::NPR;
@@ -242,11 +242,11 @@ __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_ker
         // lane holds S[n = wave*16 + 4*g4 + r][p = pt*16 + l16]; layout [p][n]
         const int c = unit % nC, g = (unit / nC) % G, b = unit / nC / G;
         const int h = g * hpg + sl % hpg;
-        float* out = states + ((size_t)(b * H + h) * nC + c) * P * N;
+        __bf16* out = states + ((size_t)(b * H + h) * nC + c) * P * N;
 #pragma unroll
         for (int p = 0; p < PT; ++p)
-            *reinterpret_cast<float4*>(out + (size_t)(p * 16 + l16) * N + wave * 16 + 4 * g4) =
-                make_float4(acc[p][0], acc[p][1], acc[p][2], acc[p][3]);
+            *reinterpret_cast<uint2*>(out + (size_t)(p * 16 + l16) * N + wave * 16 + 4 * g4) =
+                make_uint2(pack_bf16(acc[p][0], acc[p][1]), pack_bf16(acc[p][2], acc[p][3]));
     }
 }
 
@@ -255,7 +255,7 @@ __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_ker
 template <int Q, int N, int P>
 __global__ __launch_bounds__(256) void chunk_state_mfma_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ Bm, const float* __restrict__ dtc,
-    const float* __restrict__ cs, float* __restrict__ states, int T, int H, int G, int nC) {
+    const float* __restrict__ cs, __bf16* __restrict__ states, int T, int H, int G, int nC) {
     constexpr int NTH = 256;
     constexpr int NB = Q / KB;
     constexpr int PT = P / 16;
@@ -367,15 +367,15 @@ __global__ __launch_bounds__(256) void chunk_state_mfma_kernel(
         lds_barrier();
     }
     // lane holds S[n = tile*16 + 4*g4 + r][p = pt*16 + l16]; layout [p][n]
-    float* out = states + ((size_t)bh * nC + c) * P * N;
+    __bf16* out = states + ((size_t)bh * nC + c) * P * N;
 #pragma unroll
     for (int a = 0; a < NTW; ++a)
 #pragma unroll
         for (int p = 0; p < PT; ++p) {
             const int n0 = (wave * NTW + a) * 16 + 4 * g4;
             const int pp = p * 16 + l16;
-            *reinterpret_cast<float4*>(out + (size_t)pp * N + n0) =
-                make_float4(acc[a][p][0], acc[a][p][1], acc[a][p][2], acc[a][p][3]);
+            *reinterpret_cast<uint2*>(out + (size_t)pp * N + n0) =
+                make_uint2(pack_bf16(acc[a][p][0], acc[a][p][1]), pack_bf16(acc[a][p][2], acc[a][p][3]));
         }
 }
 
@@ -383,10 +383,10 @@ __global__ __launch_bounds__(256) void chunk_state_mfma_kernel(
 
 template <int Q, int N, int P>
 hipError_t launch_state_t(const Shape& s, const void* x, const void* Bm, const float* dtc,
-                          const float* cs, float* states, const void*, void*, hipStream_t st) {
+                          const float* cs, void* states, const void*, void*, hipStream_t st) {
     const unsigned blocks = (unsigned)((size_t)s.B * s.H * s.nC);
     chunk_state_mfma_kernel<Q, N, P><<<blocks, 256, 0, st>>>(
-        (const __bf16*)x, (const __bf16*)Bm, dtc, cs, states, s.T, s.H, s.G, s.nC);
+        (const __bf16*)x, (const __bf16*)Bm, dtc, cs, (__bf16*)states, s.T, s.H, s.G, s.nC);
     return hipGetLastError();
 }
 
@@ -400,7 +400,7 @@ hipError_t launch_state_t(const Shape& s, const void* x, const void* Bm, const f
     break;
 
 using StateFn = hipError_t (*)(const Shape&, const void*, const void*, const float*, const float*,
-                               float*, const void*, void*, hipStream_t);
+                               void*, const void*, void*, hipStream_t);
 
 template <int Q>
 StateFn pick_state_q(const Shape& s) {
@@ -414,7 +414,7 @@ StateFn pick_state_q(const Shape& s) {
 
 template <int Q, int N, int P>
 hipError_t launch_state_pipe_t(const Shape& s, const void* x, const void* Bm, const float* dtc,
-                               const float* cs, float* states, const void* Cm, void* gram,
+                               const float* cs, void* states, const void* Cm, void* gram,
                                hipStream_t st) {
     using C_ = StateCfg<Q, N, P>;
     const auto kern = chunk_state_pipe_kernel<Q, N, P>;
@@ -437,7 +437,7 @@ hipError_t launch_state_pipe_t(const Shape& s, const void* x, const void* Bm, co
     }
     const int nslots = s.B * s.G * s.nC * (s.H / s.G);
     kern<<<grid_of[dev], C_::NTH, C_::LDS, st>>>((const __bf16*)x, (const __bf16*)Bm, dtc, cs,
-                                                  states, (const __bf16*)Cm, (uint4*)gram, s.T,
+                                                  (__bf16*)states, (const __bf16*)Cm, (uint4*)gram, s.T,
                                                   s.H, s.G, s.nC, nslots);
     return hipGetLastError();
 }
@@ -486,7 +486,7 @@ bool chunk_state_writes_gram(const Shape& s) {
 }
 
 hipError_t launch_chunk_state_mfma(const Shape& s, const void* x, const void* Bm,
-                                   const float* dtc, const float* cs, float* states,
+                                   const float* dtc, const float* cs, void* states,
                                    const void* Cm, void* gram, hipStream_t st) {
     StateFn f = pick_state(s);
     if (!f) return hipErrorInvalidValue;

@@ -25,7 +25,7 @@ constexpr int kThreads = 256;
 template <typename Tin>
 __global__ __launch_bounds__(kThreads) void chunk_state_valu_kernel(
     const Tin* __restrict__ x, const Tin* __restrict__ Bm, const float* __restrict__ dtc,
-    const float* __restrict__ cs, float* __restrict__ states, int T, int H, int G, int P, int N,
+    const float* __restrict__ cs, Tin* __restrict__ states, int T, int H, int G, int P, int N,
     int Q, int nC, int tilesP, int tilesN) {
     __shared__ float xs[32][64 + 1];
     __shared__ float bs[32][64 + 1];
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_valu_kernel(
         }
         __syncthreads();
     }
-    float* out = states + ((size_t)(b * H + h) * nC + c) * P * N;
+    Tin* out = states + ((size_t)(b * H + h) * nC + c) * P * N;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
         const int p = p0 + ty * 4 + a;
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_valu_kernel(
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int n = n0 + tx * 4 + q;
-            if (n < N) out[(size_t)p * N + n] = acc[a][q];
+            if (n < N) out[(size_t)p * N + n] = from_f32<Tin>(acc[a][q]);
         }
     }
 }
@@ -151,19 +151,19 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_valu_kernel(
 }  // namespace
 
 hipError_t launch_chunk_state_valu(const Shape& s, ssd_dtype dt, const void* x, const void* Bm,
-                                   const float* dtc, const float* cs, float* states,
+                                   const float* dtc, const float* cs, void* states,
                                    hipStream_t st) {
     const int tilesP = (s.P + 63) / 64, tilesN = (s.N + 63) / 64;
     const unsigned blocks = (unsigned)((size_t)s.B * s.H * s.nC * tilesP * tilesN);
     if (blocks == 0) return hipSuccess;
     if (dt == SSD_F32)
         chunk_state_valu_kernel<float><<<blocks, kThreads, 0, st>>>(
-            (const float*)x, (const float*)Bm, dtc, cs, states, s.T, s.H, s.G, s.P, s.N, s.Q, s.nC,
-            tilesP, tilesN);
+            (const float*)x, (const float*)Bm, dtc, cs, (float*)states, s.T, s.H, s.G, s.P, s.N,
+            s.Q, s.nC, tilesP, tilesN);
     else
         chunk_state_valu_kernel<__bf16><<<blocks, kThreads, 0, st>>>(
-            (const __bf16*)x, (const __bf16*)Bm, dtc, cs, states, s.T, s.H, s.G, s.P, s.N, s.Q,
-            s.nC, tilesP, tilesN);
+            (const __bf16*)x, (const __bf16*)Bm, dtc, cs, (__bf16*)states, s.T, s.H, s.G, s.P,
+            s.N, s.Q, s.nC, tilesP, tilesN);
     return hipGetLastError();
 }
 

@@ -50,7 +50,8 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Workspace {
-    float *dtc, *cs, *states;
+    float *dtc, *cs;
+    void* states;  // chunk states, in the input dtype
     void* entry;  // entry states, in the input dtype
     void* gram;   // C B^T blocks of the MFMA chunk scan (empty where unused)
 };
@@ -96,7 +97,7 @@ bool uses_gram(const Shape& s, ssd_dtype dtype) {
 // chunk states; with C and gram given (and a gram buffer in use for the shape) also the
 // chunk scan's C B^T blocks, in the same launch where the kernel can, else right after
 ssd_status run_chunk_state(const Shape& s, ssd_dtype dtype, const void* x, const void* B,
-                           const float* dtc, const float* cs, float* states, const void* C,
+                           const float* dtc, const float* cs, void* states, const void* C,
                            void* gram, hipStream_t st) {
     const bool want_gram = C != nullptr && gram != nullptr && uses_gram(s, dtype);
     if (dtype == SSD_BF16 && ssd::chunk_state_mfma_supported(s)) {
@@ -152,7 +153,7 @@ ssd_status ssd_chunk_cumsum(const ssd_dims* dims, int chunk_len, const float* dt
 }
 
 ssd_status ssd_chunk_state(const ssd_dims* dims, ssd_dtype dtype, int chunk_len, const void* x,
-                           const void* B, const float* dt_chunk, const float* cs, float* states,
+                           const void* B, const float* dt_chunk, const float* cs, void* states,
                            const void* C, void* gram, void* stream) {
     Shape s;
     ssd_status r = make_shape(dims, chunk_len, &s);
@@ -167,7 +168,7 @@ ssd_status ssd_chunk_state(const ssd_dims* dims, ssd_dtype dtype, int chunk_len,
 }
 
 ssd_status ssd_state_passing(const ssd_dims* dims, ssd_dtype dtype, int chunk_len,
-                             const float* states, const float* cs, const float* init_state,
+                             const void* states, const float* cs, const float* init_state,
                              void* entry_states, float* final_state, void* stream) {
     Shape s;
     ssd_status r = make_shape(dims, chunk_len, &s);

@@ -25,14 +25,16 @@ template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float v) { return
 // ---- launchers (each returns the launch status) -------------------------------------
 hipError_t launch_chunk_cumsum(const Shape& s, const float* dt, const float* A, float* dtc,
                                float* cs, hipStream_t st);
-// entry states are written in entry_dtype (fp32 or bf16); the carried state is fp32
-hipError_t launch_state_passing(const Shape& s, ssd_dtype entry_dtype, const float* states,
+// chunk states are read and entry states written in dtype (fp32 or bf16); the carried
+// state is fp32
+hipError_t launch_state_passing(const Shape& s, ssd_dtype dtype, const void* states,
                                 const float* cs, const float* init, void* entry,
                                 float* final_state, hipStream_t st);
 
-// Plain fp32-accumulate VALU kernels: any supported size, fp32 or bf16 inputs.
+// Plain fp32-accumulate VALU kernels: any supported size, fp32 or bf16 inputs.  Chunk
+// states are written in the input dtype.
 hipError_t launch_chunk_state_valu(const Shape& s, ssd_dtype dt, const void* x, const void* Bm,
-                                   const float* dtc, const float* cs, float* states,
+                                   const float* dtc, const float* cs, void* states,
                                    hipStream_t st);
 // entry states are read in the input dtype
 hipError_t launch_chunk_scan_valu(const Shape& s, ssd_dtype dt, const void* x, const void* Bm,
@@ -46,7 +48,7 @@ bool chunk_state_mfma_supported(const Shape& s);
 // chunk scan's C B^T blocks (else it ignores them).
 bool chunk_state_writes_gram(const Shape& s);
 hipError_t launch_chunk_state_mfma(const Shape& s, const void* x, const void* Bm,
-                                   const float* dtc, const float* cs, float* states,
+                                   const float* dtc, const float* cs, void* states,
                                    const void* Cm, void* gram, hipStream_t st);
 bool chunk_scan_mfma_supported(const Shape& s);
 // bytes of the C B^T blocks the MFMA chunk scan reads (0 where the shape has no MFMA scan)

@@ -11,9 +11,9 @@
 //
 // Every (b, h, p, n) element is an independent lane of a length-nC sequential scan.  A
 // workgroup of 256 threads covers 1024 elements of one (b, h) state, four consecutive
-// elements (one 16-byte load) per thread.  The loads of kUnroll chunks are issued before
-// the dependent multiply-adds so that several requests per thread are in flight; the
-// kernel is bound by HBM (it reads S and writes E once each).
+// elements per thread.  The loads of kUnroll chunks are issued before the dependent
+// multiply-adds so that several requests per thread are in flight; the kernel is bound by
+// HBM (it reads S and writes E once each, both in the input dtype).
 #include "ssd_internal.h"
 
 namespace ssd {
@@ -24,6 +24,15 @@ constexpr int kUnroll = 8;
 
 __device__ __forceinline__ float4 fma4(float a, float4 s, float4 v) {
     return make_float4(fmaf(a, s.x, v.x), fmaf(a, s.y, v.y), fmaf(a, s.z, v.z), fmaf(a, s.w, v.w));
+}
+
+__device__ __forceinline__ float4 load4(const float* src) {
+    return *reinterpret_cast<const float4*>(src);
+}
+__device__ __forceinline__ float4 load4(const __bf16* src) {
+    const uint2 w = *reinterpret_cast<const uint2*>(src);
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
 }
 
 __device__ __forceinline__ void store4(float* dst, float4 v) {
@@ -39,12 +48,13 @@ __device__ __forceinline__ void store4(__bf16* dst, float4 v) {
     *reinterpret_cast<bf16x4*>(dst) = o;
 }
 
-// TE: element type of the entry states (fp32, or bf16 when the consumer is the bf16 MFMA
-// chunk scan, which rounds them to bf16 anyway); the running state stays fp32.
-template <typename TE>
+// T: element type of the chunk states read and of the entry states written (fp32, or bf16
+// on the bf16 path, where both are matrix-core operands or their source); the running
+// state stays fp32.
+template <typename T>
 __global__ __launch_bounds__(kThreads) void state_passing_kernel(
-    const float* __restrict__ states, const float* __restrict__ cs,
-    const float* __restrict__ init, TE* __restrict__ entry, float* __restrict__ final_state,
+    const T* __restrict__ states, const float* __restrict__ cs,
+    const float* __restrict__ init, T* __restrict__ entry, float* __restrict__ final_state,
     int nC, int Q, int P, int N, int tiles_per_state) {
     const int NP = N * P;
     const int bh = blockIdx.x / tiles_per_state;
@@ -68,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void state_passing_kernel(
         float a[kUnroll];
 #pragma unroll
         for (int k = 0; k < kUnroll; ++k) {
-            v[k] = *reinterpret_cast<const float4*>(states + base + (size_t)(c + k) * NP);
+            v[k] = load4(states + base + (size_t)(c + k) * NP);
             a[k] = csl[(size_t)(c + k) * Q];
         }
 #pragma unroll
@@ -78,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void state_passing_kernel(
         }
     }
     for (; c < nC; ++c) {
-        const float4 v = *reinterpret_cast<const float4*>(states + base + (size_t)c * NP);
+        const float4 v = load4(states + base + (size_t)c * NP);
         store4(entry + base + (size_t)c * NP, s);
         s = fma4(expf(csl[(size_t)c * Q]), s, v);
     }
@@ -93,19 +103,21 @@ __global__ __launch_bounds__(kThreads) void state_passing_kernel(
 
 }  // namespace
 
-hipError_t launch_state_passing(const Shape& s, ssd_dtype entry_dtype, const float* states,
+hipError_t launch_state_passing(const Shape& s, ssd_dtype dtype, const void* states,
                                 const float* cs, const float* init, void* entry,
                                 float* final_state, hipStream_t st) {
     const int NP = s.N * s.P;
     const int tiles = (NP + kThreads * 4 - 1) / (kThreads * 4);
     const unsigned blocks = (unsigned)((size_t)s.B * s.H * tiles);
     if (blocks == 0) return hipSuccess;
-    if (entry_dtype == SSD_BF16)
+    if (dtype == SSD_BF16)
         state_passing_kernel<__bf16><<<blocks, kThreads, 0, st>>>(
-            states, cs, init, (__bf16*)entry, final_state, s.nC, s.Q, s.P, s.N, tiles);
+            (const __bf16*)states, cs, init, (__bf16*)entry, final_state, s.nC, s.Q, s.P, s.N,
+            tiles);
     else
         state_passing_kernel<float><<<blocks, kThreads, 0, st>>>(
-            states, cs, init, (float*)entry, final_state, s.nC, s.Q, s.P, s.N, tiles);
+            (const float*)states, cs, init, (float*)entry, final_state, s.nC, s.Q, s.P, s.N,
+            tiles);
     return hipGetLastError();
 }
 

@@ -4,8 +4,8 @@
 read once and every output written once per launch; the quadratic part counts only the
 causal half of each Q x Q diagonal block (the method never needs the upper triangle),
 and C B^T is counted once per (batch, group, chunk) because the heads of a group share
-it.  Bytes use the dtype sizes of the boundary (x, B, C, y in the input dtype; dt, cs
-and the states in fp32).  Where the chunk scan takes C B^T from a gram buffer (gram_bytes > 0:
+it.  Bytes use the dtype sizes of the boundary (x, B, C, y and the stored chunk and
+entry states in the input dtype; dt, cs, init and final states in fp32).  Where the chunk scan takes C B^T from a gram buffer (gram_bytes > 0:
 the bf16 matrix-core path), the chunk_state stage also computes it (reading C, writing
 the blocks once) and the scan reads the blocks once in place of B.
 """
@@ -29,7 +29,7 @@ def kernel_costs(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len, dty
     e = 2 if dtype == "bf16" else 4
     nC = (T + Q - 1) // Q
     chunk_f32 = B * H * nC * Q * 4          # dt_chunk or cs
-    state_f32 = B * H * nC * P * N * 4      # chunk states (fp32)
+    state_e = B * H * nC * P * N * e      # chunk states, in the input dtype
     entry = B * H * nC * P * N * e          # entry states, in the input dtype
     io_xy = B * T * H * P * e               # x or y
     io_bc = B * T * G * N * e               # B or C
@@ -38,11 +38,11 @@ def kernel_costs(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len, dty
     full, rem = divmod(T, Q)
     tri = full * Q * (Q + 1) + rem * (rem + 1)          # sum of 2*(j+1) over valid rows
     gram_flops = B * G * tri * N
-    state = KernelCost("chunk_state", io_xy + io_bc + 2 * chunk_f32 + state_f32
+    state = KernelCost("chunk_state", io_xy + io_bc + 2 * chunk_f32 + state_e
                        + (io_bc + gram_bytes if gram_bytes else 0),
                        2.0 * B * H * T * N * P + (gram_flops if gram_bytes else 0))
     passing = KernelCost("state_passing",
-                         state_f32 + entry + B * H * nC * 4 + (st1 if init_state else 0)
+                         state_e + entry + B * H * nC * 4 + (st1 if init_state else 0)
                          + (st1 if final_state else 0),
                          2.0 * B * H * nC * N * P)
     # intra-chunk: sum over rows j of (j+1) MACs x P, per (b, h, chunk); C B^T likewise

@@ -126,18 +126,19 @@ def test_stage_state_passing(w):
     ent_ref, fin_ref = oracle.entry_states(c["x"], c["dt"], c["A"], c["B"], c["C"], c["D"],
                                            w.chunk_len, init_state=c["init_state"])
     dev = "cuda"
-    S_d = torch.from_numpy(S.swapaxes(-1, -2).copy()).float().to(dev)
+    # chunk states are stored in the input dtype
+    S_d = torch.from_numpy(S.swapaxes(-1, -2).copy()).float().to(cpu["x"].dtype).to(dev)
     cs_d = torch.from_numpy(cs).float().to(dev)
     init = None if cpu["init_state"] is None else cpu["init_state"].to(dev)
-    ent, fin = binding.ssd_state_passing(_dims(w), w.chunk_len, S_d, cs_d, init_state=init,
-                                         entry_dtype=cpu["x"].dtype)
+    ent, fin = binding.ssd_state_passing(_dims(w), w.chunk_len, S_d, cs_d, init_state=init)
     torch.cuda.synchronize()
     e1 = rel_l2(np64(ent).swapaxes(-1, -2), ent_ref)
     e2 = rel_l2(np64(fin), fin_ref)
     say(f"    rel_l2 entry={e1:.3e} final={e2:.3e}")
-    # entry states carried in fp32, stored in the input dtype (bf16 adds one rounding)
-    assert e1 <= (1e-5 if w.dtype == "fp32" else 4e-3)
-    assert e2 <= 1e-5
+    # carried in fp32; chunk states in and entry states out in the input dtype (with bf16,
+    # one rounding of each chunk state and one of each entry state)
+    assert e1 <= (1e-5 if w.dtype == "fp32" else 6e-3)
+    assert e2 <= (1e-5 if w.dtype == "fp32" else 4e-3)
 
 
 @pytest.mark.parametrize("w", STAGE_CASES, ids=[w.name for w in STAGE_CASES])
