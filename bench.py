@@ -118,7 +118,7 @@ def main():
         print(json.dumps({"copy_calibration_MiB": args.copy_calibration,
                           "read_bytes_per_copy": 4 * n, "write_bytes_per_copy": 4 * n}))
         return
-    from mamba_ssd_chunked_03_amd import binding, roofline
+    from mamba_ssd_chunked_03_amd import binding, roofline, traffic
     from mamba_ssd_chunked_03_amd.workloads import WORKLOADS, generate
 
     w = WORKLOADS[args.workload]
@@ -212,11 +212,16 @@ def main():
                       "hbm_frac": round(gbs / roofline.PEAK_HBM_GBPS, 4),
                       "mfma_TFLOPs": round(tfl, 2),
                       "mfma_frac": round(tfl / roofline.PEAK_MFMA_TFLOPS["bf16"], 4)}
+    # measured HBM bytes per launch, where recorded for the kernels as they are now built
+    rec = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                       f"hbm_traffic_{w.name}.md")
+    for n in names:
+        kernels[n]["hbm_traffic_bytes"] = traffic.current_traffic(rec, n)
     dom = max(names, key=lambda n: per[n])
     dk = kernels[dom]
     roof = {"bound": "hbm", "kernel": dom, "achieved": dk["hbm_GBps"],
             "peak": roofline.PEAK_HBM_GBPS, "unit": "GB/s", "frac": dk["hbm_frac"],
-            "traffic": None}
+            "traffic": dk["hbm_traffic_bytes"]}
 
     ms_step = elapsed / args.steps * 1e3
     tokens_per_s = w.tokens * args.steps / elapsed
