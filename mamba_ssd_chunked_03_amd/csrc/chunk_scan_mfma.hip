@@ -22,6 +22,8 @@
 //                positive exponent); blocks wholly below a tile factor it at the block end
 //                e as exp(cs_j - cs_e) exp(cs_e - cs_i), both factors <= 1, so they need
 //                one exp per lane instead of one per element.
+#include <type_traits>
+
 #include "mfma_common.h"
 #include "ssd_internal.h"
 
@@ -106,7 +108,7 @@ struct ScanCfg {
     static constexpr int PT = P / 16, NK = N / 32, PPR = P / 8, NPR = N / 8;
     static constexpr unsigned XB = Q * P * 2, EB = P * N * 2, FB = Q * 4;
     static constexpr unsigned ITEM = XB + EB + 2 * FB;  // x, entry state, cs, dt
-    static constexpr unsigned TAIL = 2 * FB;            // cs*log2(e), block-end weights
+    static constexpr unsigned TAIL = 3 * FB;  // cs*log2(e); weights to block and half-block ends
     // copy instructions per wave per item: PT for x (Q P / 512 over Q / 32 waves), the
     // entry state's share, and cs / dt on waves 0 / 1
     static constexpr int EI = P * NPR / 64;
@@ -168,7 +170,8 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
     extern __shared__ __align__(16) unsigned char smem[];
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
     float* s_c2 = reinterpret_cast<float*>(smem + C_::NBUF * C_::ITEM);
-    float* s_v = s_c2 + Q;  // exp(cs_e - cs_i) dt_i, e = end of i's block
+    float* s_v = s_c2 + Q;   // exp(cs_e - cs_i) dt_i, e = end of i's 32-step block
+    float* s_vh = s_v + Q;   // the same with e = end of i's 16-step half block
 
     // this workgroup's items: a contiguous run, neighbouring runs on the same XCD (the GPU
     // deals consecutive workgroups round-robin to its 8 XCDs)
@@ -251,20 +254,18 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
 #pragma unroll
         for (int p = 0; p < PT; ++p)
             xoff[p] = swz_off(4 * qg4 + (ql16 >> 2), p * 16 + 4 * (ql16 & 3), PPR);
-        // diagonal-block mask of each tile as 8 bits: k-slot k (steps 4 g4 + k and
-        // 16 + 4 g4 + k - 4 of the block) is at or below row j iff bit k is set
-        auto diag_bits = [&](int tile) {
-            const int jr = 16 * (tile & 1) + ql16 - 4 * qg4;
-            unsigned m = 0;
+        // Mask of the 16 x 16 block on the diagonal, as 4 bits: a tile's 16 rows j meet its
+        // diagonal 32-step block in one 16-step half (the first for an even tile, the
+        // second for an odd one); k-slot q of that half (step 4 g4 + q of it) is at or
+        // below row j iff bit q is set.  The same bits serve both tiles of the wave.
+        unsigned dq = 0;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) m |= (unsigned)((k < 4 ? k : 12 + k) <= jr) << k;
-            return m;
-        };
-        const unsigned db0 = diag_bits(tile0), db1 = diag_bits(tile1);
+        for (int q = 0; q < 4; ++q) dq |= (unsigned)(q <= ql16 - 4 * qg4) << q;
         if (tid < Q) {
             const float ci = b_cs[tid];
             s_c2[tid] = ci * kLog2e;
             s_v[tid] = exp2_fast((b_cs[tid | (KB - 1)] - ci) * kLog2e) * b_dt[tid];
+            s_vh[tid] = exp2_fast((b_cs[tid | 15] - ci) * kLog2e) * b_dt[tid];
         }
         if (unit != cur_unit) {  // C rows and Gram fragments of the new unit
             cur_unit = unit;
@@ -340,7 +341,39 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
             }
             const int i0 = ib * KB + 4 * g4;
             // masked, decayed Gram block of one tile -> MFMA operand
-            auto block = [&](const uint4 gv4, int nblk, unsigned dbits, float csj) -> bf16x8 {
+            // The tile's own block.  Its 16 x 16 quarter on the diagonal is masked through
+            // the exponent (-inf above the diagonal, selected bit by bit by the
+            // sign-extended mask bit); for an even tile the other half lies wholly above the
+            // rows (zero), for an odd tile wholly below them (the decay factored at the end
+            // of that half, like a block below).  ODD is the tile's parity (wave-uniform).
+            auto diag = [&](auto odd_tag, const uint4 gv4, float csj, float* m) {
+                constexpr bool ODD = decltype(odd_tag)::value;
+                constexpr int hd = ODD ? 16 : 0;  // the diagonal half
+                const float4 cd = *reinterpret_cast<const float4*>(&s_c2[i0 + hd]);
+                const float4 dd = *reinterpret_cast<const float4*>(&b_dt[i0 + hd]);
+                const float cdv[4] = {cd.x, cd.y, cd.z, cd.w};
+                const float ddv[4] = {dd.x, dd.y, dd.z, dd.w};
+                const uint32_t w0 = ODD ? gv4.z : gv4.x, w1 = ODD ? gv4.w : gv4.y;
+                const float gd[4] = {bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
+                const unsigned ninf = 0xff800000u;
+                unsigned dbl = dq;  // opaque here too: masks are made where used
+                asm volatile("" : "+v"(dbl));
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const unsigned mq = (unsigned)__builtin_amdgcn_sbfe((int)dbl, q, 1);
+                    const float e = __uint_as_float((__float_as_uint(csj - cdv[q]) & mq) | (ninf & ~mq));
+                    m[hd / 4 + q] = gd[q] * exp2_fast(e) * ddv[q];
+                }
+                if (ODD) {
+                    const float f = exp2_fast(csj - s_c2[ib * KB + 15]);
+                    const float4 vh = *reinterpret_cast<const float4*>(&s_vh[i0]);
+                    m[0] = bf16_lo(gv4.x) * (vh.x * f); m[1] = bf16_hi(gv4.x) * (vh.y * f);
+                    m[2] = bf16_lo(gv4.y) * (vh.z * f); m[3] = bf16_hi(gv4.y) * (vh.w * f);
+                } else {
+                    m[4] = m[5] = m[6] = m[7] = 0.f;
+                }
+            };
+            auto block = [&](const uint4 gv4, int nblk, bool odd, float csj) -> bf16x8 {
                 float m[8];
                 if (ib < nblk - 1) {  // wholly below the tile: decay factored at block end
                     const float f = exp2_fast(csj - s_c2[ib * KB + KB - 1]);
@@ -350,42 +383,22 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
                     m[2] = bf16_lo(gv4.y) * (va.z * f); m[3] = bf16_hi(gv4.y) * (va.w * f);
                     m[4] = bf16_lo(gv4.z) * (vb.x * f); m[5] = bf16_hi(gv4.z) * (vb.y * f);
                     m[6] = bf16_lo(gv4.w) * (vb.z * f); m[7] = bf16_hi(gv4.w) * (vb.w * f);
-                } else {  // the diagonal block: mask above the diagonal through the exponent
-                    const float4 ca = *reinterpret_cast<const float4*>(&s_c2[i0]);
-                    const float4 cb = *reinterpret_cast<const float4*>(&s_c2[i0 + 16]);
-                    const float4 da = *reinterpret_cast<const float4*>(&b_dt[i0]);
-                    const float4 db = *reinterpret_cast<const float4*>(&b_dt[i0 + 16]);
-                    const float cav[4] = {ca.x, ca.y, ca.z, ca.w}, cbv[4] = {cb.x, cb.y, cb.z, cb.w};
-                    const float dav[4] = {da.x, da.y, da.z, da.w}, dbv[4] = {db.x, db.y, db.z, db.w};
-                    const float gv[8] = {bf16_lo(gv4.x), bf16_hi(gv4.x), bf16_lo(gv4.y),
-                                         bf16_hi(gv4.y), bf16_lo(gv4.z), bf16_hi(gv4.z),
-                                         bf16_lo(gv4.w), bf16_hi(gv4.w)};
-                    // exponent -inf above the diagonal: bit k of dbits, sign-extended to a
-                    // full mask, selects between the exponent and -inf bit by bit
-                    const unsigned ninf = 0xff800000u;
-                    unsigned dbl = dbits;  // opaque here too: masks are made where used
-                    asm volatile("" : "+v"(dbl));
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const unsigned ma = (unsigned)__builtin_amdgcn_sbfe((int)dbl, q, 1);
-                        const unsigned mc = (unsigned)__builtin_amdgcn_sbfe((int)dbl, 4 + q, 1);
-                        const float ea = __uint_as_float((__float_as_uint(csj - cav[q]) & ma) | (ninf & ~ma));
-                        const float ec = __uint_as_float((__float_as_uint(csj - cbv[q]) & mc) | (ninf & ~mc));
-                        m[q] = gv[q] * exp2_fast(ea) * dav[q];
-                        m[4 + q] = gv[4 + q] * exp2_fast(ec) * dbv[q];
-                    }
+                } else if (odd) {
+                    diag(std::true_type{}, gv4, csj, m);
+                } else {
+                    diag(std::false_type{}, gv4, csj, m);
                 }
                 return __builtin_bit_cast(
                     bf16x8, make_uint4(pack_bf16(m[0], m[1]), pack_bf16(m[2], m[3]),
                                        pack_bf16(m[4], m[5]), pack_bf16(m[6], m[7])));
             };
             if (ib < NB0 && ib < nb0) {
-                const bf16x8 bm = block(gf0[ib < NB0 ? ib : 0], nb0, db0, csj0);
+                const bf16x8 bm = block(gf0[ib < NB0 ? ib : 0], nb0, (tile0 & 1) != 0, csj0);
 #pragma unroll
                 for (int p = 0; p < PT; ++p) acc0[p] = mfma16(xa[p], bm, acc0[p]);
             }
             {
-                const bf16x8 bm = block(gf1[ib], nb1, db1, csj1);
+                const bf16x8 bm = block(gf1[ib], nb1, (tile1 & 1) != 0, csj1);
 #pragma unroll
                 for (int p = 0; p < PT; ++p) acc1[p] = mfma16(xa[p], bm, acc1[p]);
             }
