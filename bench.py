@@ -35,6 +35,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="rough budget for the oracle CPU baseline")
+    ap.add_argument("--decode", default="", metavar="WORKLOAD",
+                    help="instead of the forward, time ssd_decode_step on a decode workload "
+                         "(one token per sequence per step) and print its own JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to calibrate the "
                          "HBM byte counters against a known traffic, and exit")
@@ -99,12 +102,54 @@ def cpu_baseline(w, inputs, budget_s):
                       f"sequences, {el:.2f} s each, mean of {reps} runs)"}
 
 
+def bench_decode(args, w, torch, binding, roofline, generate):
+    """Decode steps back to back on one batch of sequences: tokens/s = batch / step time.
+    The step is bound by HBM: it reads and writes the fp32 state once."""
+    dev = torch.device("cuda:0")
+    log(f"[bench decode] {w.describe()}")
+    cpu = generate(w)
+    x, dt = cpu["x"][:, 0].to(dev), cpu["dt"][:, 0].contiguous().to(dev)
+    Bm, Cm = cpu["B"][:, 0].contiguous().to(dev), cpu["C"][:, 0].contiguous().to(dev)
+    A, D = cpu["A"].to(dev), cpu["D"].to(dev)
+    state = cpu["init_state"].to(dev)
+    y = torch.empty_like(x)
+    step = lambda: binding.ssd_decode_step(x, dt, A, Bm, Cm, D, state, y=y)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    c = roofline.decode_cost(w.batch, w.nheads, w.headdim, w.dstate, w.ngroups, w.dtype)
+    gbs = c.bytes / (us * 1e-6) / 1e9
+    ms_step = elapsed / args.steps * 1e3
+    print(json.dumps({
+        "metric": "SSD decode-step tokens/sec on 1 MI355X", "value": round(w.batch / (ms_step * 1e-3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "nheads": w.nheads, "headdim": w.headdim,
+                   "dstate": w.dstate, "ngroups": w.ngroups, "input_dtype": w.dtype},
+        "roofline": {"bound": "hbm", "kernel": "decode_step", "achieved": round(gbs, 1),
+                     "peak": roofline.PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbs / roofline.PEAK_HBM_GBPS, 4), "traffic": None},
+        "kernels": {"decode_step": {"avg_us": round(us, 2), "alg_bytes": int(c.bytes)}},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(each GPU would run its own shard; see DESIGN.md). Use --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures one GPU: libssd has no multi-GPU path (several GPUs would "
+              "each run the same kernels on their own batch elements, heads or groups). "
+              "Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -119,7 +164,9 @@ def main():
                           "read_bytes_per_copy": 4 * n, "write_bytes_per_copy": 4 * n}))
         return
     from mamba_ssd_chunked_03_amd import binding, roofline, traffic
-    from mamba_ssd_chunked_03_amd.workloads import WORKLOADS, generate
+    from mamba_ssd_chunked_03_amd.workloads import DECODE, WORKLOADS, generate
+    if args.decode:
+        return bench_decode(args, DECODE[args.decode], torch, binding, roofline, generate)
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")

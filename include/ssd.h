@@ -177,6 +177,25 @@ ssd_status ssd_chunk_scan(const ssd_dims* dims, ssd_dtype dtype, int chunk_len,
                           const float* cs, const float* D, const void* entry_states,
                           const void* gram, void* y, void* stream);
 
+/* One recurrent step for a batch of sequences ("Mamba-2: Attention's Distant Cousin",
+ * section "Working Through Four Tokens": the recurrent form, the one generation uses, with
+ * a state of fixed size).  For every (b, h), g = h / (H / G):
+ *     state[b][h] <- exp(dt[b][h] * A[h]) * state[b][h] + dt[b][h] * B[b][g] x[b][h]^T
+ *     y[b][h]      = C[b][g]^T state[b][h] + D[h] * x[b][h]
+ * computed in fp32 -- exactly one step of the recurrence that ssd_fwd computes by chunks.
+ * dims->seqlen is ignored (one step); the other sizes are checked as for ssd_fwd.
+ *   x, y     [batch][nheads][headdim]            in `dtype`
+ *   dt       [batch][nheads]                     fp32
+ *   A, D     [nheads]                            fp32
+ *   B, C     [batch][ngroups][dstate]            in `dtype`
+ *   state    [batch][nheads][dstate][headdim]    fp32, read and updated in place (the
+ *            layout of init_state / final_state: ssd_fwd's final_state continues here)
+ * x and state must be 16-byte aligned, the others 4-byte aligned.  Errors as ssd_fwd;
+ * nothing needs a workspace. */
+ssd_status ssd_decode_step(const ssd_dims* dims, ssd_dtype dtype, const void* x,
+                           const float* dt, const float* A, const void* B, const void* C,
+                           const float* D, float* state, void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,7 +16,7 @@ SSD_F32, SSD_BF16 = 0, 1
 _DTYPE_CODE = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}
 EXPORTED = ("ssd_status_string", "ssd_fwd_workspace_size", "ssd_fwd", "ssd_chunk_cumsum",
             "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_gram_size", "ssd_chunk_gram",
-            "ssd_chunk_scan")
+            "ssd_chunk_scan", "ssd_decode_step")
 
 
 class SsdDims(ctypes.Structure):
@@ -64,6 +64,8 @@ def library(path=LIB_PATH):
     lib.ssd_chunk_gram_size.argtypes = [dims, i, i]
     lib.ssd_chunk_gram.restype = i
     lib.ssd_chunk_gram.argtypes = [dims, i, i, vp, vp, vp, vp]
+    lib.ssd_decode_step.restype = i
+    lib.ssd_decode_step.argtypes = [dims, i, vp, fp, fp, vp, vp, fp, fp, vp, vp]
     lib.ssd_chunk_scan.restype = i
     lib.ssd_chunk_scan.argtypes = [dims, i, i, vp, vp, vp, fp, fp, fp, vp, vp, vp, vp]
     if path == LIB_PATH:
@@ -224,4 +226,22 @@ def ssd_chunk_scan(dims, chunk_len, x, B, C, dt_chunk, cs, D, entry_states, gram
     _check(library().ssd_chunk_scan(ctypes.byref(dims), _DTYPE_CODE[x.dtype], int(chunk_len),
                                     _ptr(x), _ptr(B), _ptr(C), _ptr(dt_chunk), _ptr(cs), _ptr(D),
                                     _ptr(entry_states), gp, _ptr(y), _stream(dev, stream)))
+    return y
+
+
+def ssd_decode_step(x, dt, A, B, C, D, state, y=None, stream=None):
+    """One recurrent step: x [batch, nheads, headdim], dt [batch, nheads], B and C
+    [batch, ngroups, dstate], state [batch, nheads, dstate, headdim] fp32 (updated in
+    place).  Returns y [batch, nheads, headdim] in x's dtype."""
+    dev = x.device
+    bz, h, p = x.shape
+    dims = SsdDims(bz, 1, h, p, B.shape[2], B.shape[1])
+    for t, name in ((x, "x"), (dt, "dt"), (A, "A"), (B, "B"), (C, "C"), (D, "D"),
+                    (state, "state")):
+        _need(t, name, device=dev)
+    _need(state, "state", dtype=torch.float32)
+    y = torch.empty_like(x) if y is None else y
+    _check(library().ssd_decode_step(ctypes.byref(dims), _DTYPE_CODE[x.dtype], _ptr(x),
+                                     _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(state),
+                                     _ptr(y), _stream(dev, stream)))
     return y

@@ -248,4 +248,21 @@ ssd_status ssd_fwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const f
     return run_chunk_scan(s, dtype, x, B, C, ws.dtc, ws.cs, D, ws.entry, ws.gram, y, st);
 }
 
+ssd_status ssd_decode_step(const ssd_dims* dims, ssd_dtype dtype, const void* x, const float* dt,
+                           const float* A, const void* B, const void* C, const float* D,
+                           float* state, void* y, void* stream) {
+    if (!dims) return SSD_ERR_NULL;
+    ssd_dims one = *dims;
+    one.seqlen = 1;  // the sizes are checked as for a one-step sequence
+    Shape s;
+    ssd_status r = make_shape(&one, 64, &s);
+    if (r != SSD_OK) return r;
+    if (!valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
+    if (s.B == 0) return SSD_OK;
+    if (!x || !dt || !A || !B || !C || !D || !state || !y) return SSD_ERR_NULL;
+    if (any_misaligned({x, state}) || any_misaligned4({dt, A, B, C, D, y})) return SSD_ERR_ALIGN;
+    return hip_status(ssd::launch_decode_step(s, dtype, x, dt, A, B, C, D, state, y,
+                                              (hipStream_t)stream));
+}
+
 }  // extern "C"

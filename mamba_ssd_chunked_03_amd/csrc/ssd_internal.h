@@ -51,6 +51,11 @@ hipError_t launch_chunk_state_mfma(const Shape& s, const void* x, const void* Bm
                                    const float* dtc, const float* cs, void* states,
                                    const void* Cm, void* gram, hipStream_t st);
 bool chunk_scan_mfma_supported(const Shape& s);
+// one recurrent step for every (b, h): state [B][H][N][P] fp32 in place; x, y [B][H][P] and
+// B, C [B][G][N] in dtype (Shape's T and Q are not used)
+hipError_t launch_decode_step(const Shape& s, ssd_dtype dtype, const void* x, const float* dt,
+                              const float* A, const void* Bm, const void* Cm, const float* D,
+                              float* state, void* y, hipStream_t st);
 // bytes of the C B^T blocks the MFMA chunk scan reads (0 where the shape has no MFMA scan)
 size_t chunk_gram_bytes(const Shape& s);
 hipError_t launch_chunk_gram(const Shape& s, const void* Bm, const void* Cm, void* gram,

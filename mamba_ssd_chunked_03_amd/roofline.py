@@ -65,3 +65,12 @@ def compulsory_bytes(batch, seqlen, nheads, headdim, dstate, ngroups, dtype="bf1
     st1 = B * H * N * P * 4
     return (2 * B * T * H * P * e + 2 * B * T * G * N * e + B * T * H * 4 + 2 * H * 4
             + (st1 if init_state else 0) + (st1 if final_state else 0))
+
+
+def decode_cost(batch, nheads, headdim, dstate, ngroups, dtype="bf16"):
+    """One decode step: the fp32 state read and written once, plus the step's inputs and
+    output (x, y in the input dtype; B, C per group; dt per head; A, D)."""
+    e = 2 if dtype == "bf16" else 4
+    B, H, P, N, G = batch, nheads, headdim, dstate, ngroups
+    nbytes = 2 * B * H * N * P * 4 + 2 * B * H * P * e + 2 * B * G * N * e + B * H * 4 + 2 * H * 4
+    return KernelCost("decode_step", nbytes, 4.0 * B * H * N * P)

@@ -72,6 +72,13 @@ LONG_CTX = Workload("long_ctx_65k", 1, 65536, 80, 64, 128, 8, 256, init_state=Tr
 
 WORKLOADS = {w.name: w for w in (TINY_FP32, MAMBA2_130M, MAMBA2_2P7B, *NSWEEP, LONG_CTX)}
 
+# Decode workloads: one token per sequence per step, continuing a state (seqlen 1, with
+# init_state the state the step starts from).  Shapes of the model layers above.
+DECODE = {w.name: w for w in (
+    Workload("decode_2p7b", 64, 1, 80, 64, 128, 1, 256, init_state=True),
+    Workload("decode_130m", 256, 1, 24, 64, 128, 1, 256, init_state=True),
+)}
+
 # Stress cases: the model-shaped distributions decay by about e^-254 per 256-step chunk,
 # which hides mistakes in the carried state; these make the carry visible.
 STRESS = {

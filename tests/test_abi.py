@@ -134,3 +134,15 @@ def test_validation_errors_before_any_launch(lib):
                               None) == 0
     assert lib.ssd_fwd(None, 0, None, None, None, None, None, None, 64, None, None, None, None,
                        0, None) == 1
+    # the decode step: sizes checked as for ssd_fwd (seqlen ignored), then pointers
+    assert lib.ssd_decode_step(ctypes.byref(D(t=0)), 1, None, None, None, None, None, None,
+                               None, None, None) == 1
+    assert lib.ssd_decode_step(ctypes.byref(D(p=48)), 1, *[ctypes.c_void_p(256)] * 8,
+                               None) == 3
+    assert lib.ssd_decode_step(ctypes.byref(D(h=3, g=2)), 1, *[ctypes.c_void_p(256)] * 8,
+                               None) == 2
+    assert lib.ssd_decode_step(ctypes.byref(D(b=0)), 1, None, None, None, None, None, None,
+                               None, None, None) == 0
+    assert lib.ssd_decode_step(ctypes.byref(D()), 1, *[ctypes.c_void_p(264)] * 8, None) == 4
+    assert lib.ssd_decode_step(None, 1, None, None, None, None, None, None, None, None,
+                               None) == 1

@@ -1,0 +1,97 @@
+"""The single-token decode step against the oracle (GPU).
+
+One step of ssd_decode_step is one step of the oracle's token recurrence with the given
+state as init_state ("Mamba-2: Attention's Distant Cousin", section "Working Through Four
+Tokens", recurrent form).  Steps that continue ssd_fwd's final_state must match the
+oracle run over the whole sequence.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mamba_ssd_chunked_03_amd import binding
+from mamba_ssd_chunked_03_amd.workloads import Workload, generate
+from parity import TOL, np64, rel_l2, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+CASES = [  # (batch, heads, headdim P, dstate N, groups, dtype)
+    (3, 4, 64, 128, 1, "bf16"),
+    (2, 6, 16, 16, 3, "fp32"),
+    (4, 2, 128, 256, 2, "bf16"),
+    (1, 8, 32, 64, 8, "fp32"),
+    (5, 3, 64, 32, 1, "bf16"),
+]
+
+
+def _step_inputs(w, cpu):
+    """Step 0 of a generated sequence as decode-step tensors."""
+    return dict(x=cpu["x"][:, 0], dt=cpu["dt"][:, 0].contiguous(), A=cpu["A"],
+                B=cpu["B"][:, 0].contiguous(), C=cpu["C"][:, 0].contiguous(), D=cpu["D"])
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"B{b}_H{h}_P{p}_N{n}_G{g}_{d}"
+                                             for b, h, p, n, g, d in CASES])
+def test_one_step_matches_oracle(case):
+    Bz, H, P, N, G, dt = case
+    w = Workload(f"dec_{Bz}_{H}_{P}_{N}_{G}", Bz, 1, H, P, N, G, 64, dtype=dt, init_state=True,
+                 log_neg_a_range=(np.log(0.01), np.log(1.0)))
+    say(f"[decode one step] {w.describe()}")
+    cpu = generate(w)
+    y_ref, f_ref, _ = oracle.ssd_ref(*(np64(cpu[k]) for k in ("x", "dt", "A", "B", "C", "D")),
+                                     init_state=np64(cpu["init_state"]))
+    dv = {k: v.cuda() for k, v in _step_inputs(w, cpu).items()}
+    state = cpu["init_state"].clone().cuda()
+    y = binding.ssd_decode_step(dv["x"], dv["dt"], dv["A"], dv["B"], dv["C"], dv["D"], state)
+    torch.cuda.synchronize()
+    ey = rel_l2(np64(y), y_ref[:, 0])
+    es = rel_l2(np64(state), f_ref)
+    say(f"    rel_l2 y={ey:.3e} state={es:.3e}")
+    # fp32 arithmetic on exact inputs: only y's rounding to bf16 is visible
+    assert es <= 1e-5
+    assert ey <= (1e-5 if dt == "fp32" else 4e-3)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_decode_continues_the_chunked_forward(dt):
+    """ssd_fwd over the first T1 tokens, then T2 decode steps from its final_state: every
+    output and the state after the last step match the oracle over all T1 + T2 tokens."""
+    T1, T2 = 300, 24
+    w = Workload(f"dec_cont_{dt}", 2, T1 + T2, 4, 64, 64, 2, 128, dtype=dt, init_state=True,
+                 log_neg_a_range=(np.log(0.005), np.log(0.05)))
+    say(f"[decode after fwd] {w.describe()}")
+    cpu = generate(w)
+    y_ref, f_ref, _ = oracle.ssd_ref(*(np64(cpu[k]) for k in ("x", "dt", "A", "B", "C", "D")),
+                                     init_state=np64(cpu["init_state"]))
+    dv = to_device(cpu)
+    head = {k: (None if v is None else (v[:, :T1].contiguous() if k in ("x", "dt", "B", "C")
+                                        else v)) for k, v in dv.items()}
+    y1, state = binding.ssd_fwd(head["x"], head["dt"], head["A"], head["B"], head["C"],
+                                head["D"], 128, init_state=head["init_state"])
+    ys = []
+    for t in range(T1, T1 + T2):
+        ys.append(binding.ssd_decode_step(dv["x"][:, t].contiguous(), dv["dt"][:, t].contiguous(),
+                                          dv["A"], dv["B"][:, t].contiguous(),
+                                          dv["C"][:, t].contiguous(), dv["D"], state))
+    torch.cuda.synchronize()
+    y = torch.cat([y1, torch.stack(ys, dim=1)], dim=1)
+    ey, ef = rel_l2(np64(y), y_ref), rel_l2(np64(state), f_ref)
+    say(f"    rel_l2 y={ey:.3e} final={ef:.3e}")
+    assert ey <= TOL[dt] and ef <= TOL[dt]
+
+
+def test_decode_bad_arguments():
+    x = torch.zeros((2, 4, 64), dtype=torch.bfloat16, device="cuda")
+    dt = torch.zeros((2, 4), device="cuda")
+    A = torch.zeros(4, device="cuda")
+    B = torch.zeros((2, 1, 128), dtype=torch.bfloat16, device="cuda")
+    state = torch.zeros((2, 4, 128, 64), device="cuda")
+    with pytest.raises(binding.SsdError):  # headdim 48 is not supported
+        binding.ssd_decode_step(torch.zeros((2, 4, 48), dtype=torch.bfloat16, device="cuda"),
+                                dt, A, B, B, A, torch.zeros((2, 4, 128, 48), device="cuda"))
+    with pytest.raises(TypeError):  # the state is fp32
+        binding.ssd_decode_step(x, dt, A, B, B, A, state.to(torch.bfloat16))
+    # an empty batch does nothing
+    y = binding.ssd_decode_step(x[:0], dt[:0], A, B[:0], B[:0], A, state[:0])
+    assert y.shape == (0, 4, 64)
