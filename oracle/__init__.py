@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the SSD layer forward.
+"""fp64 CPU oracle for the SSD layer, forward and backward.
 
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg are the only code allowed to import this package.  It shares no
@@ -6,10 +6,12 @@ code with the HIP library and never imports it.
 
 Contents
   ssd_ref          token-by-token recurrence (C, fp64, threads over (batch, head))
+  ssd_bwd_ref      gradients by reverse-mode differentiation of the recurrence (C, fp64)
   ssd_quadratic    the dual quadratic form y = (L o C B^T) (dt x) + ...  (numpy, tiny sizes)
   chunk_cumsum     chunk-local inclusive prefix sums of dt*A
   chunk_states     per-chunk states that start from zero (the chunk's own input only)
   entry_states     the state entering every chunk (init for chunk 0)
+  chunk_entry_grads  dL/d(entry state of a chunk) through that chunk's own outputs only
 
 Sources: "Mamba-2: Attention's Distant Cousin" (docsaid.org), sections "Writing an SSM
 as a Matrix", "Reducing A to a Single Number", "Working Through Four Tokens"; and the
@@ -49,6 +51,9 @@ def load_library(path):
     lib.ssd_ref.restype = ctypes.c_int
     lib.ssd_ref.argtypes = [ctypes.POINTER(_Dims), dp, dp, dp, dp, dp, dp, dp,
                             ctypes.c_int64, dp, dp, dp, ctypes.c_int]
+    lib.ssd_bwd_ref.restype = ctypes.c_int
+    lib.ssd_bwd_ref.argtypes = [ctypes.POINTER(_Dims), dp, dp, dp, dp, dp, dp, dp, dp, dp,
+                                ctypes.c_int64, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
     lib.ssd_ref_threads_used.restype = ctypes.c_int
     lib.ssd_ref_threads_used.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int]
     return lib
@@ -102,6 +107,58 @@ def ssd_ref(x, dt, A, B, C, D, init_state=None, chunk_len=0, nthreads=0, lib=Non
     return y, final, bound
 
 
+def ssd_bwd_ref(x, dt, A, B, C, D, dy, init_state=None, d_final=None, chunk_len=0,
+                nthreads=0, lib=None):
+    """Gradients of a scalar loss L through the recurrence, in fp64.
+
+    Inputs as for ssd_ref, plus dy = dL/dy [B,T,H,P] and d_final = dL/d final_state
+    [B,H,N,P] (None: zero).  Returns a dict with
+      dx [B,T,H,P], ddt [B,T,H], dA [H], dB [B,T,G,N], dC [B,T,G,N], dD [H],
+      d_init [B,H,N,P] (zeros-init gradient when init_state is None, still returned),
+      dB_heads / dC_heads [B,T,H,N] (each head's share of dB / dC),
+      boundary_grads [B,H,nC,N,P] or None (only when chunk_len > 0): for every chunk,
+        dL/d(state after the chunk's last step) through the later steps only.
+    A group's dB and dC are the sums of its heads' shares, dA and dD the sums over batch.
+    """
+    lib = lib or library()
+    x, dt, A, B, C, D, dy = (_f64(v) for v in (x, dt, A, B, C, D, dy))
+    init = None if init_state is None else _f64(init_state)
+    dfin = None if d_final is None else _f64(d_final)
+    bsz, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if dt.shape != (bsz, T, H) or A.shape != (H,) or D.shape != (H,):
+        raise ValueError("dt/A/D shapes do not match x")
+    if B.shape != (bsz, T, G, N) or C.shape != B.shape:
+        raise ValueError("B/C shapes do not match x")
+    if dy.shape != x.shape:
+        raise ValueError("dy must have the shape of x")
+    for name, v in (("init_state", init), ("d_final", dfin)):
+        if v is not None and v.shape != (bsz, H, N, P):
+            raise ValueError(f"{name} shape must be [B,H,N,P]")
+    dx = np.empty_like(x)
+    ddt = np.empty((bsz, T, H))
+    dBh = np.empty((bsz, T, H, N))
+    dCh = np.empty((bsz, T, H, N))
+    dAp = np.empty((bsz, H))
+    dDp = np.empty((bsz, H))
+    d_init = np.empty((bsz, H, N, P))
+    bgr = None
+    if chunk_len > 0:
+        bgr = np.empty((bsz, H, (T + chunk_len - 1) // chunk_len, N, P))
+    d = dims_of(x, B)
+    rc = lib.ssd_bwd_ref(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                         _ptr(init), _ptr(dy), _ptr(dfin), int(chunk_len), _ptr(dx), _ptr(ddt),
+                         _ptr(dBh), _ptr(dCh), _ptr(dAp), _ptr(dDp), _ptr(d_init), _ptr(bgr),
+                         int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"ssd_bwd_ref failed with code {rc}")
+    hpg = H // G
+    return dict(dx=dx, ddt=ddt, dA=dAp.sum(axis=0), dD=dDp.sum(axis=0),
+                dB=dBh.reshape(bsz, T, G, hpg, N).sum(axis=3),
+                dC=dCh.reshape(bsz, T, G, hpg, N).sum(axis=3),
+                d_init=d_init, dB_heads=dBh, dC_heads=dCh, boundary_grads=bgr)
+
+
 def threads_used(batch, nheads, nthreads=0):
     d = _Dims(batch, 1, nheads, 1, 1, 1)
     return library().ssd_ref_threads_used(ctypes.byref(d), int(nthreads))
@@ -153,3 +210,25 @@ def entry_states(x, dt, A, B, C, D, chunk_len, init_state=None, nthreads=0):
     ent[:, :, 0] = 0.0 if init_state is None else _f64(init_state)
     ent[:, :, 1:] = bound[:, :, :-1]
     return ent, final
+
+
+def chunk_entry_grads(x, dt, A, B, C, D, dy, chunk_len, init_state=None, nthreads=0):
+    """For every chunk c, the gradient of L = <y, dy> with respect to the state entering
+    chunk c through the outputs of chunk c alone (the later chunks' use of it excluded):
+    the init-state gradient of a run over chunk c's steps, started from its true entry
+    state, with dy restricted to the chunk and no final-state gradient.
+    Returns [B,H,nC,N,P]."""
+    x = _f64(x)
+    bsz, T, H, P = x.shape
+    N = np.asarray(B).shape[3]
+    Q = int(chunk_len)
+    nC = (T + Q - 1) // Q
+    ent, _ = entry_states(x, dt, A, B, C, D, Q, init_state=init_state, nthreads=nthreads)
+    out = np.empty((bsz, H, nC, N, P))
+    dy = _f64(dy)
+    for c in range(nC):
+        sl = slice(c * Q, min(T, (c + 1) * Q))
+        g = ssd_bwd_ref(x[:, sl], _f64(dt)[:, sl], A, _f64(B)[:, sl], _f64(C)[:, sl], D,
+                        dy[:, sl], init_state=ent[:, :, c], nthreads=nthreads)
+        out[:, :, c] = g["d_init"]
+    return out

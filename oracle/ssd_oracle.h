@@ -1,5 +1,6 @@
 /*
- * ssd_oracle.h -- fp64 CPU oracle for the SSD layer forward (test infrastructure only).
+ * ssd_oracle.h -- fp64 CPU oracle for the SSD layer forward and backward (test
+ * infrastructure only).
  *
  * Only the test suite, the smoke check and the benchmark's CPU-baseline leg use this
  * library.  It is independent of the HIP library: no shared code or headers.
@@ -39,6 +40,24 @@ int ssd_ref(const ssd_ref_dims* d, const double* x, const double* dt, const doub
             const double* B, const double* C, const double* D, const double* init_state,
             int64_t chunk_len, double* y, double* final_state, double* boundary_states,
             int nthreads);
+
+/*
+ * ssd_bwd_ref: gradients of a scalar loss through the same recurrence, by reverse-mode
+ * differentiation step by step (fp64).  Inputs as for ssd_ref plus dy [B][T][H][P]
+ * (dL/dy) and d_final [B][H][N][P] (dL/d final state) or NULL (zero).  Outputs:
+ *   dx [B][T][H][P], ddt [B][T][H]
+ *   dB_heads, dC_heads [B][T][H][N]: each head's share of dL/dB_t, dL/dC_t (the
+ *     gradient of a group's B or C is the sum over the heads of that group)
+ *   dA_parts, dD_parts [B][H]: each (batch, head)'s share of dL/dA[h], dL/dD[h]
+ *   d_init [B][H][N][P] or NULL: dL/d init_state
+ *   boundary_grads [B][H][ceil(T/chunk_len)][N][P] or NULL (then chunk_len may be 0):
+ *     for every chunk, dL/d(state after its last step) through the later steps only
+ */
+int ssd_bwd_ref(const ssd_ref_dims* d, const double* x, const double* dt, const double* A,
+                const double* B, const double* C, const double* D, const double* init_state,
+                const double* dy, const double* d_final, int64_t chunk_len, double* dx,
+                double* ddt, double* dB_heads, double* dC_heads, double* dA_parts,
+                double* dD_parts, double* d_init, double* boundary_grads, int nthreads);
 
 /* The number of threads ssd_ref runs with for these dims and this request. */
 int ssd_ref_threads_used(const ssd_ref_dims* d, int nthreads);
