@@ -1,5 +1,6 @@
 /*
- * ssd.h -- libssd: the Mamba-2 SSD (state space dual) layer forward on AMD MI355X (gfx950).
+ * ssd.h -- libssd: the Mamba-2 SSD (state space dual) layer on AMD MI355X (gfx950): the
+ * forward, its backward and the single-token recurrent step.
  *
  * The operation ("Mamba-2: Attention's Distant Cousin", docsaid.org, sections "Writing an
  * SSM as a Matrix" and "Reducing A to a Single Number"; structured summary of arXiv
@@ -176,6 +177,43 @@ ssd_status ssd_chunk_scan(const ssd_dims* dims, ssd_dtype dtype, int chunk_len,
                           const void* x, const void* B, const void* C, const float* dt_chunk,
                           const float* cs, const float* D, const void* entry_states,
                           const void* gram, void* y, void* stream);
+
+/* ---- backward ----------------------------------------------------------------------
+ * The pages' headline claim is training speed (structured summary of arXiv 2405.21060,
+ * section "1. Executive Summary": 2-8x faster training than Mamba's selective scan), and
+ * training needs the gradient of the layer.  The pages define only the forward; the
+ * backward here is its exact derivative, computed with the same block decomposition run in
+ * reverse: the chunk states and entry states are recomputed, each chunk's entry-state
+ * gradient through its own outputs (Z_c = sum_i exp(cs_i) C_i dy_i^T) is carried from the
+ * last chunk to the first (dE_c = Z_c + exp(cs[c][Q-1]) dE_{c+1}, dE_nchunks = d_final),
+ * and inside each chunk the transposed quadratic form gives dx, dB, dC and the gradients of
+ * the log decays, from which ddt and dA follow by suffix sums over the chunk. */
+
+/* Bytes of device workspace ssd_bwd needs for these sizes, for either dtype (0 if the
+ * sizes are invalid). */
+size_t ssd_bwd_workspace_size(const ssd_dims* dims, int chunk_len);
+
+/* Gradients of a scalar loss L through ssd_fwd with the same inputs, given
+ *   dy       dL/dy        [batch][seqlen][nheads][headdim]        in `dtype`
+ *   d_final  dL/d final_state [batch][nheads][dstate][headdim] fp32, NULL for zero
+ * (x, dt, A, B, C, D, chunk_len and init_state exactly as passed to ssd_fwd).  Writes
+ *   dx [B][T][H][P] and dB, dC [B][T][G][N] in `dtype` (dB, dC summed over the heads of
+ *     each group, in fp32, then rounded once),
+ *   ddt [B][T][H], dA [H], dD [H] fp32 (dA and dD summed over batch and time),
+ *   d_init [B][H][N][P] fp32 (dL/d init_state; NULL to skip -- with a NULL init_state it is
+ *     still the gradient with respect to the zero initial state).
+ * The result does not depend on chunk_len beyond rounding.  Every output is written in
+ * full; dA and dD even when batch or seqlen is 0 (then zero), and d_init = d_final (or
+ * zero) when seqlen is 0.  Reductions run in a fixed order: results are bitwise
+ * reproducible run to run.  Alignment: x, B, C, dy, dx, dB, dC and workspace 16 bytes;
+ * the fp32 arguments 4 bytes.  workspace: ssd_bwd_workspace_size bytes, contents
+ * unspecified on return.  Errors as ssd_fwd. */
+ssd_status ssd_bwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const float* dt,
+                   const float* A, const void* B, const void* C, const float* D,
+                   int chunk_len, const float* init_state, const void* dy,
+                   const float* d_final, void* dx, float* ddt, float* dA, void* dB, void* dC,
+                   float* dD, float* d_init, void* workspace, size_t workspace_bytes,
+                   void* stream);
 
 /* One recurrent step for a batch of sequences ("Mamba-2: Attention's Distant Cousin",
  * section "Working Through Four Tokens": the recurrent form, the one generation uses, with

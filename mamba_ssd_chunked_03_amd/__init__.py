@@ -1,4 +1,5 @@
-"""libssd: the Mamba-2 SSD layer forward on MI355X (gfx950), behind a C ABI.
+"""libssd: the Mamba-2 SSD layer (forward, backward, recurrent step) on MI355X (gfx950),
+behind a C ABI.
 
 The compute path is the HIP library `libssd.so` in this package directory (built by
 `build.py`); `binding` is a thin ctypes layer over it.  Importing the package does not

@@ -16,7 +16,7 @@ SSD_F32, SSD_BF16 = 0, 1
 _DTYPE_CODE = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}
 EXPORTED = ("ssd_status_string", "ssd_fwd_workspace_size", "ssd_fwd", "ssd_chunk_cumsum",
             "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_gram_size", "ssd_chunk_gram",
-            "ssd_chunk_scan", "ssd_decode_step")
+            "ssd_chunk_scan", "ssd_decode_step", "ssd_bwd_workspace_size", "ssd_bwd")
 
 
 class SsdDims(ctypes.Structure):
@@ -68,6 +68,11 @@ def library(path=LIB_PATH):
     lib.ssd_decode_step.argtypes = [dims, i, vp, fp, fp, vp, vp, fp, fp, vp, vp]
     lib.ssd_chunk_scan.restype = i
     lib.ssd_chunk_scan.argtypes = [dims, i, i, vp, vp, vp, fp, fp, fp, vp, vp, vp, vp]
+    lib.ssd_bwd_workspace_size.restype = sz
+    lib.ssd_bwd_workspace_size.argtypes = [dims, i]
+    lib.ssd_bwd.restype = i
+    lib.ssd_bwd.argtypes = [dims, i, vp, fp, fp, vp, vp, fp, i, fp, vp, fp, vp, fp, fp, vp, vp,
+                            fp, fp, vp, sz, vp]
     if path == LIB_PATH:
         _LIB = lib
     return lib
@@ -245,3 +250,50 @@ def ssd_decode_step(x, dt, A, B, C, D, state, y=None, stream=None):
                                      _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(state),
                                      _ptr(y), _stream(dev, stream)))
     return y
+
+
+def ssd_bwd_workspace_size(dims, chunk_len):
+    return int(library().ssd_bwd_workspace_size(ctypes.byref(dims), int(chunk_len)))
+
+
+def ssd_bwd(x, dt, A, B, C, D, chunk_len, dy, init_state=None, d_final=None, want_d_init=True,
+            out=None, workspace=None, stream=None):
+    """Gradients through ssd_fwd (libssd.ssd_bwd): inputs as for ssd_fwd plus dy (x's shape
+    and dtype) and d_final ([B,H,N,P] fp32 or None).  Returns a dict with dx, ddt, dA, dB,
+    dC, dD and d_init (None when want_d_init is False).  `out` may hold preallocated output
+    tensors under those names."""
+    dev = x.device
+    f32 = torch.float32
+    _need(x, "x", device=dev)
+    code = _DTYPE_CODE.get(x.dtype)
+    if code is None:
+        raise TypeError(f"x must be fp32 or bf16, got {x.dtype}")
+    for t, n in ((B, "B"), (C, "C"), (dy, "dy")):
+        _need(t, n, x.dtype, dev)
+    for t, n in ((dt, "dt"), (A, "A"), (D, "D")):
+        _need(t, n, f32, dev)
+    for t, n in ((init_state, "init_state"), (d_final, "d_final")):
+        if t is not None:
+            _need(t, n, f32, dev)
+    d = dims_of(x, B)
+    o = dict(out or {})
+    o.setdefault("dx", torch.empty_like(x))
+    o.setdefault("ddt", torch.empty_like(dt))
+    o.setdefault("dA", torch.empty_like(A))
+    o.setdefault("dB", torch.empty_like(B))
+    o.setdefault("dC", torch.empty_like(C))
+    o.setdefault("dD", torch.empty_like(D))
+    if want_d_init:
+        o.setdefault("d_init", torch.empty((d.batch, d.nheads, d.dstate, d.headdim), dtype=f32,
+                                           device=dev))
+    else:
+        o["d_init"] = None
+    if workspace is None:
+        ws = ssd_bwd_workspace_size(d, chunk_len)
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+    _check(library().ssd_bwd(ctypes.byref(d), code, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                             _ptr(D), int(chunk_len), _ptr(init_state), _ptr(dy), _ptr(d_final),
+                             _ptr(o["dx"]), _ptr(o["ddt"]), _ptr(o["dA"]), _ptr(o["dB"]),
+                             _ptr(o["dC"]), _ptr(o["dD"]), _ptr(o["d_init"]), _ptr(workspace),
+                             workspace.numel(), _stream(dev, stream)))
+    return o

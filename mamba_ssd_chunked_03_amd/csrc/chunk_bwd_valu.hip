@@ -1,0 +1,387 @@
+// chunk_bwd_valu.hip -- the backward pass inside each chunk, and the per-step and
+// per-head parameter gradients, in plain fp32 vector arithmetic (any supported size,
+// fp32 or bf16 inputs).
+//
+// The forward is the block decomposition of the SSD layer (structured summary of arXiv
+// 2405.21060, section "The Block-Decomposition SSD Algorithm"): inside chunk c, with cs the
+// chunk-local inclusive prefix sums of dt*A and E the state entering the chunk,
+//     y_j = sum_{i<=j} (C_j.B_i) exp(cs_j - cs_i) dt_i x_i + exp(cs_j) E^T C_j + D x_j
+//     S_c = sum_i exp(cs_last - cs_i) dt_i B_i x_i^T,    E_next = exp(cs_last) E + S_c.
+// Its gradient, given dy and F = dL/dE_next (the carried gradient of the chunk's end state,
+// from the reverse inter-chunk pass), with M[t][i] = dy_t . x_i and G[t][i] = C_t . B_i:
+//     dx_j  = D dy_j + dt_j [ sum_{t>=j} exp(cs_t - cs_j) G[t][j] dy_t
+//                            + exp(cs_last - cs_j) F^T B_j ]
+//     dC_j += sum_{i<=j} dt_i exp(cs_j - cs_i) M[j][i] B_i + exp(cs_j) E dy_j
+//     dB_j += dt_j [ sum_{t>=j} exp(cs_t - cs_j) M[t][j] C_t + exp(cs_last - cs_j) F x_j ]
+// summed over the heads of the group for dB and dC.  The step sizes enter through dt_j
+// directly and through every cs_k with k >= j (cs_k = A sum_{m<=k} dt_m), so
+//     ddt_j = direct_j + A R_j,   R_j = sum_{k>=j} dL/dcs_k,   dA = sum_j dt_j R_j,
+// where direct_j = B_j . (dL/dS_j) x_j is the explicit derivative and, per head,
+//     dL/dcs_k = C_k . dC_k(head) - B_k . dB_k(head)   (+ <E_next, F> at the chunk's end)
+// because cs_k enters every term as exp(+cs_k) where C_k reads and exp(-cs_k) where B_k
+// writes.  These identities follow from differentiating the decomposition term by term;
+// the fp64 oracle differentiates the token recurrence instead, and the two agree.
+//
+// Kernels
+//   chunk_bwd_valu_kernel: one workgroup per (b, g, chunk, 16-row tile J), looping over
+//     the heads of the group so that dB and dC are summed in registers with no atomics.
+//     Per head it forms the row strip W[j][i] (i <= j) and the column strip V[t][j]
+//     (t >= j) of the decayed M for j in J, the dx weights U[t][j] = exp(cs_t - cs_j) G[t][j],
+//     and from them dx (written per head), the dB/dC contributions and dL/dcs, direct.
+//   bwd_ddt_kernel: one wave per (b, h, chunk): the suffix sums R, ddt and dA's share.
+//   bwd_param_kernel: one workgroup per head: dA and dD summed over batch and chunks in a
+//     fixed order (results do not depend on scheduling).
+#include "ssd_internal.h"
+
+namespace ssd {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRows = 16;   // rows of a tile
+constexpr int kMaxNQ = 16;  // N / 16 for N <= 256
+
+template <typename Tin>
+__device__ __forceinline__ float ld(const Tin* p, size_t i) { return to_f32(p[i]); }
+
+// sum over the 16 lanes of an aligned group (every lane gets the total)
+__device__ __forceinline__ float sum16(float v) {
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 16);
+    return v;
+}
+__device__ __forceinline__ float sum64(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+template <typename Tin>
+__global__ __launch_bounds__(kThreads) void chunk_bwd_valu_kernel(
+    const Tin* __restrict__ x, const Tin* __restrict__ Bm, const Tin* __restrict__ Cm,
+    const float* __restrict__ dtc, const float* __restrict__ cs, const float* __restrict__ D,
+    const Tin* __restrict__ entry, const Tin* __restrict__ exitg, const Tin* __restrict__ dy,
+    Tin* __restrict__ dx, Tin* __restrict__ dB, Tin* __restrict__ dC, float* __restrict__ dcs,
+    float* __restrict__ direct, float* __restrict__ lt_part, float* __restrict__ dd_part,
+    int T, int H, int G, int P, int N, int Q, int nC) {
+    extern __shared__ float sm[];
+    float* Grow = sm;               // [16][Q]  G[j0 + r][i]
+    float* Gcol = Grow + kRows * Q; // [Q][16]  G[t][j0 + r]
+    float* Wrow = Gcol + kRows * Q; // [16][Q]  dt_i exp(cs_j - cs_i) M[j][i], i <= j
+    float* Vcol = Wrow + kRows * Q; // [Q][16]  exp(cs_t - cs_j) M[t][j], t >= j
+    float* Ucol = Vcol + kRows * Q; // [Q][16]  exp(cs_t - cs_j) G[t][j], t >= j
+    float* xJ = Ucol + kRows * Q;   // [16][P]
+    float* dyJ = xJ + kRows * P;    // [16][P]
+    float* red = dyJ + kRows * P;   // [2][4] wave partials
+
+    const int ntiles = Q / kRows;
+    int k = blockIdx.x;
+    const int rt = k % ntiles; k /= ntiles;
+    const int c = k % nC; k /= nC;
+    const int g = k % G;
+    const int b = k / G;
+    const int j0 = rt * kRows, t0 = c * Q;
+    if (t0 + j0 >= T) return;  // no valid row: nothing of this tile is read back
+    const int Lc = min(Q, T - t0);  // valid rows of the chunk
+    const int iend = j0 + kRows;
+    const int hpg = H / G;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ro = tid / 16, l16 = tid % 16;  // owned row of the tile and lane in its group
+    const int jo = j0 + ro;
+    const bool vrow = jo < Lc;
+    const int NQ = N / 16;
+
+    auto brow = [&](int i) { return Bm + ((size_t)(b * T + t0 + i) * G + g) * N; };
+    auto crow = [&](int i) { return Cm + ((size_t)(b * T + t0 + i) * G + g) * N; };
+
+    // the group's C_j . B_i strips, shared by every head
+    for (int e = tid; e < kRows * iend; e += kThreads) {
+        const int i = e / kRows, r = e % kRows;
+        float v = 0.f;
+        if (j0 + r < Lc && i < Lc) {
+            const Tin* cr = crow(j0 + r);
+            const Tin* br = brow(i);
+            for (int n = 0; n < N; ++n) v = fmaf(ld(cr, n), ld(br, n), v);
+        }
+        Grow[r * Q + i] = v;
+    }
+    for (int e = tid; e < (Q - j0) * kRows; e += kThreads) {
+        const int t = j0 + e / kRows, r = e % kRows;
+        float v = 0.f;
+        if (t < Lc && j0 + r < Lc) {
+            const Tin* cr = crow(t);
+            const Tin* br = brow(j0 + r);
+            for (int n = 0; n < N; ++n) v = fmaf(ld(cr, n), ld(br, n), v);
+        }
+        Gcol[t * kRows + r] = v;
+    }
+    float accB[kMaxNQ], accC[kMaxNQ], bj[kMaxNQ], cj[kMaxNQ];
+#pragma unroll
+    for (int q = 0; q < kMaxNQ; ++q) {
+        accB[q] = accC[q] = 0.f;
+        const int n = l16 + 16 * q;
+        bj[q] = (q < NQ && vrow) ? ld(brow(jo), n) : 0.f;
+        cj[q] = (q < NQ && vrow) ? ld(crow(jo), n) : 0.f;
+    }
+    __syncthreads();
+
+    for (int hh = 0; hh < hpg; ++hh) {
+        const int h = g * hpg + hh;
+        const size_t cb = ((size_t)(b * H + h) * nC + c) * Q;
+        const float* csh = cs + cb;
+        const float* dth = dtc + cb;
+        const float cs_last = csh[Q - 1];
+        auto xrow = [&](int i) { return x + ((size_t)(b * T + t0 + i) * H + h) * P; };
+        auto dyrow = [&](int i) { return dy + ((size_t)(b * T + t0 + i) * H + h) * P; };
+
+        for (int e = tid; e < kRows * P; e += kThreads) {
+            const int r = e / P, p = e % P;
+            const bool v = j0 + r < Lc;
+            xJ[e] = v ? ld(xrow(j0 + r), p) : 0.f;
+            dyJ[e] = v ? ld(dyrow(j0 + r), p) : 0.f;
+        }
+        __syncthreads();
+        for (int e = tid; e < kRows * iend; e += kThreads) {
+            const int i = e / kRows, r = e % kRows;
+            const int j = j0 + r;
+            float w = 0.f;
+            if (i <= j && j < Lc) {
+                const Tin* xi = xrow(i);
+                float m = 0.f;
+                for (int p = 0; p < P; ++p) m = fmaf(dyJ[r * P + p], ld(xi, p), m);
+                w = dth[i] * expf(csh[j] - csh[i]) * m;
+            }
+            Wrow[r * Q + i] = w;
+        }
+        for (int e = tid; e < (Q - j0) * kRows; e += kThreads) {
+            const int t = j0 + e / kRows, r = e % kRows;
+            const int j = j0 + r;
+            float v = 0.f, u = 0.f;
+            if (t >= j && t < Lc) {
+                const Tin* dyt = dyrow(t);
+                float m = 0.f;
+                for (int p = 0; p < P; ++p) m = fmaf(ld(dyt, p), xJ[r * P + p], m);
+                const float dec = expf(csh[t] - csh[j]);
+                v = dec * m;
+                u = dec * Gcol[t * kRows + r];
+            }
+            Vcol[t * kRows + r] = v;
+            Ucol[t * kRows + r] = u;
+        }
+        __syncthreads();
+
+        const float cs_j = vrow ? csh[jo] : cs_last;
+        const float dtj = vrow ? dth[jo] : 0.f;
+        const float e_j = expf(cs_j), f_j = expf(cs_last - cs_j);
+        float rs = 0.f, ccol = 0.f, oc = 0.f, ob = 0.f;
+        for (int i = l16; i < iend; i += 16) rs = fmaf(Wrow[ro * Q + i], Grow[ro * Q + i], rs);
+        for (int t = j0 + l16; t < Q; t += 16)
+            ccol = fmaf(Vcol[t * kRows + ro], Gcol[t * kRows + ro], ccol);
+        const Tin* E = entry + ((size_t)(b * H + h) * nC + c) * P * N;  // [P][N]
+        const Tin* F = exitg + ((size_t)(b * H + h) * nC + c) * P * N;  // [P][N]
+        const int imax = min(iend, Lc);
+#pragma unroll
+        for (int q = 0; q < kMaxNQ; ++q) {
+            if (q >= NQ) break;
+            const int n = l16 + 16 * q;
+            float sC = 0.f, sB = 0.f, edy = 0.f, fx = 0.f;
+            for (int i = 0; i < imax; ++i) sC = fmaf(Wrow[ro * Q + i], ld(brow(i), n), sC);
+            for (int t = j0; t < Lc; ++t) sB = fmaf(Vcol[t * kRows + ro], ld(crow(t), n), sB);
+            for (int p = 0; p < P; ++p) {
+                edy = fmaf(ld(E, (size_t)p * N + n), dyJ[ro * P + p], edy);
+                fx = fmaf(ld(F, (size_t)p * N + n), xJ[ro * P + p], fx);
+            }
+            accC[q] += sC + e_j * edy;
+            accB[q] += dtj * (sB + f_j * fx);
+            oc = fmaf(cj[q], e_j * edy, oc);
+            ob = fmaf(bj[q], f_j * fx, ob);
+        }
+        rs = sum16(rs);
+        ccol = sum16(ccol);
+        oc = sum16(oc);
+        ob = sum16(ob);
+
+        const float dh = D[h];
+        for (int p = l16; p < P; p += 16) {
+            float sx = 0.f, bf = 0.f;
+            for (int t = jo; t < Lc; ++t) sx = fmaf(Ucol[t * kRows + ro], ld(dyrow(t), p), sx);
+            if (vrow) {
+                const Tin* bjr = brow(jo);
+                for (int n = 0; n < N; ++n) bf = fmaf(ld(bjr, n), ld(F, (size_t)p * N + n), bf);
+                dx[((size_t)(b * T + t0 + jo) * H + h) * P + p] =
+                    from_f32<Tin>(dh * dyJ[ro * P + p] + dtj * (sx + f_j * bf));
+            }
+        }
+        if (l16 == 0 && vrow) {
+            direct[cb + jo] = ccol + ob;
+            dcs[cb + jo] = rs + oc - dtj * (ccol + ob);
+        }
+
+        // this tile's shares of the chunk-end term and of dD
+        float lt = (l16 == 0 && vrow) ? dtj * ob : 0.f;
+        if (rt == 0) {
+            float ef = 0.f;
+            for (int e = tid; e < N * P; e += kThreads) ef = fmaf(ld(E, e), ld(F, e), ef);
+            lt = fmaf(expf(cs_last), ef, lt);
+        }
+        float dd = 0.f;
+        for (int p = l16; p < P; p += 16) dd = fmaf(xJ[ro * P + p], dyJ[ro * P + p], dd);
+        lt = sum64(lt);
+        dd = sum64(dd);
+        if (lane == 0) {
+            red[wave] = lt;
+            red[4 + wave] = dd;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            const size_t pi = ((size_t)(b * H + h) * nC + c) * ntiles + rt;
+            lt_part[pi] = (red[0] + red[1]) + (red[2] + red[3]);
+            dd_part[pi] = (red[4] + red[5]) + (red[6] + red[7]);
+        }
+        // next head overwrites the strips and the staged rows
+        __syncthreads();
+    }
+    if (vrow) {
+        Tin* db = dB + ((size_t)(b * T + t0 + jo) * G + g) * N;
+        Tin* dc = dC + ((size_t)(b * T + t0 + jo) * G + g) * N;
+#pragma unroll
+        for (int q = 0; q < kMaxNQ; ++q) {
+            if (q >= NQ) break;
+            db[l16 + 16 * q] = from_f32<Tin>(accB[q]);
+            dc[l16 + 16 * q] = from_f32<Tin>(accC[q]);
+        }
+    }
+}
+
+// One wave per (b, h, chunk).  R_j = sum_{k >= j} dL/dcs_k within the chunk, plus the
+// chunk-end term (summed from the row tiles' shares); ddt_j = direct_j + A R_j and this
+// chunk's share of dA, sum_j dt_j R_j.  rows: rows per tile of the kernel that wrote the
+// shares.
+__global__ __launch_bounds__(kThreads) void bwd_ddt_kernel(
+    const float* __restrict__ dcs, const float* __restrict__ direct,
+    const float* __restrict__ lt_part, const float* __restrict__ dtc, const float* __restrict__ A,
+    float* __restrict__ ddt, float* __restrict__ dA_part, int T, int H, int Q, int nC,
+    int rows, int items) {
+    const int item = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (item >= items) return;
+    const int lane = threadIdx.x & 63;
+    const int c = item % nC, bh = item / nC;
+    const int h = bh % H, b = bh / H;
+    const size_t cb = (size_t)item * Q;
+    const int Lc = min(Q, T - c * Q);
+    const int ntiles = Q / rows;
+    const int nvalid = (Lc + rows - 1) / rows;
+    float lt = 0.f;
+    for (int k = 0; k < nvalid; ++k) lt += lt_part[(size_t)item * ntiles + k];
+
+    const int L = Q / 64;  // positions per lane, consecutive
+    const int k0 = lane * L;
+    float v[4];
+    float seg = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        v[m] = (m < L && k0 + m < Lc) ? dcs[cb + k0 + m] : 0.f;
+        seg += v[m];
+    }
+    // inclusive suffix sum of the lanes' segment sums
+    float suf = seg;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float up = __shfl_down(suf, o, 64);
+        if (lane + o < 64) suf += up;
+    }
+    float r = (suf - seg) + lt;
+    const float Ah = A[h];
+    float da = 0.f;
+#pragma unroll
+    for (int m = 3; m >= 0; --m) {
+        if (m >= L) continue;
+        r += v[m];
+        const int j = k0 + m;
+        if (j < Lc) {
+            ddt[((size_t)b * T + c * Q + j) * H + h] = direct[cb + j] + Ah * r;
+            da = fmaf(dtc[cb + j], r, da);
+        }
+    }
+    da = sum64(da);
+    if (lane == 0) dA_part[item] = da;
+}
+
+// One workgroup per head: dA[h] and dD[h] summed over every (b, chunk) in a fixed order.
+__global__ __launch_bounds__(kThreads) void bwd_param_kernel(
+    const float* __restrict__ dA_part, const float* __restrict__ dd_part, float* __restrict__ dA,
+    float* __restrict__ dD, int Bsz, int T, int H, int Q, int nC, int rows) {
+    __shared__ float red[2][kThreads];
+    const int h = blockIdx.x;
+    const int ntiles = Q / rows;
+    const int items = Bsz * nC;
+    float sa = 0.f, sd = 0.f;
+    for (int k = threadIdx.x; k < items; k += kThreads) {
+        const int b = k / nC, c = k % nC;
+        const size_t item = (size_t)(b * H + h) * nC + c;
+        sa += dA_part[item];
+        const int Lc = min(Q, T - c * Q);
+        const int nvalid = (Lc + rows - 1) / rows;
+        for (int t = 0; t < nvalid; ++t) sd += dd_part[item * ntiles + t];
+    }
+    red[0][threadIdx.x] = sa;
+    red[1][threadIdx.x] = sd;
+    __syncthreads();
+    for (int o = kThreads / 2; o > 0; o >>= 1) {
+        if (threadIdx.x < o) {
+            red[0][threadIdx.x] += red[0][threadIdx.x + o];
+            red[1][threadIdx.x] += red[1][threadIdx.x + o];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        dA[h] = red[0][0];
+        dD[h] = red[1][0];
+    }
+}
+
+size_t bwd_valu_lds(const Shape& s) {
+    return (size_t)(5 * kRows * s.Q + 2 * kRows * s.P + 8) * sizeof(float);
+}
+
+template <typename Tin>
+hipError_t launch_bwd_valu_t(const Shape& s, const BwdArgs& a, hipStream_t st) {
+    const auto kern = chunk_bwd_valu_kernel<Tin>;
+    const size_t lds = bwd_valu_lds(s);
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    const unsigned blocks = (unsigned)((size_t)s.B * s.G * s.nC * (s.Q / kRows));
+    kern<<<blocks, kThreads, lds, st>>>(
+        (const Tin*)a.x, (const Tin*)a.Bm, (const Tin*)a.Cm, a.dtc, a.cs, a.D, (const Tin*)a.entry,
+        (const Tin*)a.exitg, (const Tin*)a.dy, (Tin*)a.dx, (Tin*)a.dB, (Tin*)a.dC, a.dcs,
+        a.direct, a.lt_part, a.dd_part, s.T, s.H, s.G, s.P, s.N, s.Q, s.nC);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int chunk_bwd_valu_rows() { return kRows; }
+
+hipError_t launch_chunk_bwd_valu(const Shape& s, ssd_dtype dtype, const BwdArgs& a,
+                                 hipStream_t st) {
+    if ((size_t)s.B * s.nC == 0) return hipSuccess;
+    return dtype == SSD_F32 ? launch_bwd_valu_t<float>(s, a, st)
+                            : launch_bwd_valu_t<__bf16>(s, a, st);
+}
+
+hipError_t launch_bwd_finalize(const Shape& s, const BwdArgs& a, int rows, hipStream_t st) {
+    const int items = s.B * s.H * s.nC;
+    if (items > 0) {
+        const unsigned blocks = (unsigned)((items + 3) / 4);
+        bwd_ddt_kernel<<<blocks, kThreads, 0, st>>>(a.dcs, a.direct, a.lt_part, a.dtc, a.A,
+                                                    a.ddt, a.dA_part, s.T, s.H, s.Q, s.nC, rows,
+                                                    items);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    bwd_param_kernel<<<s.H, kThreads, 0, st>>>(a.dA_part, a.dd_part, a.dA, a.dD, s.B, s.T, s.H,
+                                               s.Q, s.nC, rows);
+    return hipGetLastError();
+}
+
+}  // namespace ssd

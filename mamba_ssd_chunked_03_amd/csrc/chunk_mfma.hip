@@ -21,6 +21,12 @@
 //   chunk_state_mfma_kernel (other shapes): one workgroup per (b, h, chunk); 32-step slices
 //     of B and x are transposed through registers into LDS ([feature][time], two time
 //     steps per 32-bit word) and double-buffered; x' is formed in fp32 and rounded once.
+//
+// With REV set, the same kernels compute the backward pass's mirror of stage 2: the
+// gradient of the entry state of every chunk through the chunk's own outputs,
+//     Z[n][p] = sum_i C[i][n] exp(cs_i) dy[i][p]
+// (y_i reads the entry state through exp(cs_i) C_i, so dL/dE = sum_i exp(cs_i) C_i dy_i^T):
+// C takes the place of B, dy that of x, and the per-step weight is exp(cs_i).
 #include "mfma_common.h"
 #include "ssd_internal.h"
 
@@ -96,7 +102,7 @@ __device__ __forceinline__ int gram_pair_base(int t) {
     return (t & 1) ? (t / 2 + 1) * (t / 2 + 1) : (t / 2) * (t / 2 + 1);
 }
 
-template <int Q, int N, int P>
+template <int Q, int N, int P, bool REV>
 __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ Bm, const float* __restrict__ dtc,
     const float* __restrict__ cs, __bf16* __restrict__ states, const __bf16* __restrict__ Cm,
@@ -157,7 +163,7 @@ __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_ker
                 const uint2 hi2 = lds_read_tr16(bp + BHALF);
                 bt[ib] = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
             }
-            constexpr bool kGram = (Q == 256 && N == 128);
+            constexpr bool kGram = (Q == 256 && N == 128 && !REV);
             if (kGram && gram != nullptr && sl == unit * hpg) {
                 // C B^T blocks of this unit (this workgroup holds its first head): wave w
                 // takes row tiles w and 15 - w and every block at or below them
@@ -208,7 +214,8 @@ __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_ker
         }
         if (tid < Q) {
             const float ci = b_cs[tid];
-            s_w[tid] = exp2_fast((b_cs[Q - 1] - ci) * kLog2e) * b_dt[tid];
+            s_w[tid] = REV ? exp2_fast(ci * kLog2e)
+                           : exp2_fast((b_cs[Q - 1] - ci) * kLog2e) * b_dt[tid];
         }
         lds_barrier();
         if (sl + 1 < hi)
@@ -252,7 +259,7 @@ __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_ker
 
 // ============================================================================ chunk_state
 
-template <int Q, int N, int P>
+template <int Q, int N, int P, bool REV>
 __global__ __launch_bounds__(256) void chunk_state_mfma_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ Bm, const float* __restrict__ dtc,
     const float* __restrict__ cs, __bf16* __restrict__ states, int T, int H, int G, int nC) {
@@ -283,7 +290,8 @@ __global__ __launch_bounds__(256) void chunk_state_mfma_kernel(
 
     // decay to the chunk end times dt, per step (fp32)
     const float cs_last = cs[cbase + Q - 1];
-    for (int i = tid; i < Q; i += NTH) s_w[i] = expf(cs_last - cs[cbase + i]) * dtc[cbase + i];
+    for (int i = tid; i < Q; i += NTH)
+        s_w[i] = REV ? expf(cs[cbase + i]) : expf(cs_last - cs[cbase + i]) * dtc[cbase + i];
 
     uint4 rb[BPT][2], rx[XPT][2];
     auto load = [&](int ib) {
@@ -381,28 +389,28 @@ __global__ __launch_bounds__(256) void chunk_state_mfma_kernel(
 
 // ---------------------------------------------------------------- dispatch tables
 
-template <int Q, int N, int P>
+template <int Q, int N, int P, bool REV>
 hipError_t launch_state_t(const Shape& s, const void* x, const void* Bm, const float* dtc,
                           const float* cs, void* states, const void*, void*, hipStream_t st) {
     const unsigned blocks = (unsigned)((size_t)s.B * s.H * s.nC);
-    chunk_state_mfma_kernel<Q, N, P><<<blocks, 256, 0, st>>>(
+    chunk_state_mfma_kernel<Q, N, P, REV><<<blocks, 256, 0, st>>>(
         (const __bf16*)x, (const __bf16*)Bm, dtc, cs, (__bf16*)states, s.T, s.H, s.G, s.nC);
     return hipGetLastError();
 }
 
 #define SSD_FOR_P(F, Q, N)                                   \
     switch (s.P) {                                           \
-        case 16: return F<Q, N, 16>;                         \
-        case 32: return F<Q, N, 32>;                         \
-        case 64: return F<Q, N, 64>;                         \
-        case 128: return F<Q, N, 128>;                       \
+        case 16: return F<Q, N, 16, REV>;                    \
+        case 32: return F<Q, N, 32, REV>;                    \
+        case 64: return F<Q, N, 64, REV>;                    \
+        case 128: return F<Q, N, 128, REV>;                  \
     }                                                        \
     break;
 
 using StateFn = hipError_t (*)(const Shape&, const void*, const void*, const float*, const float*,
                                void*, const void*, void*, hipStream_t);
 
-template <int Q>
+template <int Q, bool REV>
 StateFn pick_state_q(const Shape& s) {
     switch (s.N) {
         case 64: SSD_FOR_P(launch_state_t, Q, 64)
@@ -412,12 +420,12 @@ StateFn pick_state_q(const Shape& s) {
     return nullptr;
 }
 
-template <int Q, int N, int P>
+template <int Q, int N, int P, bool REV>
 hipError_t launch_state_pipe_t(const Shape& s, const void* x, const void* Bm, const float* dtc,
                                const float* cs, void* states, const void* Cm, void* gram,
                                hipStream_t st) {
     using C_ = StateCfg<Q, N, P>;
-    const auto kern = chunk_state_pipe_kernel<Q, N, P>;
+    const auto kern = chunk_state_pipe_kernel<Q, N, P, REV>;
     static int grid_of[64];  // per device: resident workgroups, a multiple of 8
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -442,13 +450,13 @@ hipError_t launch_state_pipe_t(const Shape& s, const void* x, const void* Bm, co
     return hipGetLastError();
 }
 
-template <int Q>
+template <int Q, bool REV>
 StateFn pick_state_pipe_q(const Shape& s) {
     if (s.N != 128) return nullptr;
     switch (s.P) {
-        case 16: return launch_state_pipe_t<Q, 128, 16>;
-        case 32: return launch_state_pipe_t<Q, 128, 32>;
-        case 64: return launch_state_pipe_t<Q, 128, 64>;
+        case 16: return launch_state_pipe_t<Q, 128, 16, REV>;
+        case 32: return launch_state_pipe_t<Q, 128, 32, REV>;
+        case 64: return launch_state_pipe_t<Q, 128, 64, REV>;
     }
     return nullptr;
 }
@@ -459,40 +467,51 @@ bool state_offsets_fit(const Shape& s) {
            (size_t)s.Q * s.G * s.N * 2 < ((size_t)1 << 31);
 }
 
+template <bool REV>
 StateFn pick_state(const Shape& s) {
     if (state_offsets_fit(s)) {
         StateFn f = nullptr;
         switch (s.Q) {
-            case 64: f = pick_state_pipe_q<64>(s); break;
-            case 128: f = pick_state_pipe_q<128>(s); break;
-            case 256: f = pick_state_pipe_q<256>(s); break;
+            case 64: f = pick_state_pipe_q<64, REV>(s); break;
+            case 128: f = pick_state_pipe_q<128, REV>(s); break;
+            case 256: f = pick_state_pipe_q<256, REV>(s); break;
         }
         if (f) return f;
     }
     switch (s.Q) {
-        case 64: return pick_state_q<64>(s);
-        case 128: return pick_state_q<128>(s);
-        case 256: return pick_state_q<256>(s);
+        case 64: return pick_state_q<64, REV>(s);
+        case 128: return pick_state_q<128, REV>(s);
+        case 256: return pick_state_q<256, REV>(s);
     }
     return nullptr;
 }
 
 }  // namespace
 
-bool chunk_state_mfma_supported(const Shape& s) { return pick_state(s) != nullptr; }
+bool chunk_state_mfma_supported(const Shape& s) { return pick_state<false>(s) != nullptr; }
 
 bool chunk_state_writes_gram(const Shape& s) {
-    return state_offsets_fit(s) && s.Q == 256 && s.N == 128 && pick_state_pipe_q<256>(s) != nullptr;
+    return state_offsets_fit(s) && s.Q == 256 && s.N == 128 &&
+           pick_state_pipe_q<256, false>(s) != nullptr;
 }
 
 hipError_t launch_chunk_state_mfma(const Shape& s, const void* x, const void* Bm,
                                    const float* dtc, const float* cs, void* states,
                                    const void* Cm, void* gram, hipStream_t st) {
-    StateFn f = pick_state(s);
+    StateFn f = pick_state<false>(s);
     if (!f) return hipErrorInvalidValue;
     if ((size_t)s.B * s.H * s.nC == 0) return hipSuccess;
     const bool fuse = gram != nullptr && Cm != nullptr && chunk_state_writes_gram(s);
     return f(s, x, Bm, dtc, cs, states, fuse ? Cm : nullptr, fuse ? gram : nullptr, st);
+}
+
+hipError_t launch_chunk_dstate_mfma(const Shape& s, const void* dy, const void* Cm,
+                                    const float* cs, void* dstates, hipStream_t st) {
+    StateFn f = pick_state<true>(s);
+    if (!f) return hipErrorInvalidValue;
+    if ((size_t)s.B * s.H * s.nC == 0) return hipSuccess;
+    // the weights need only cs; the step sizes are not read (cs stands in for them)
+    return f(s, dy, Cm, cs, cs, dstates, nullptr, nullptr, st);
 }
 
 }  // namespace ssd

@@ -22,7 +22,8 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <typename Tin>
+// REV: the backward pass's mirror (C for B, dy for x, weight exp(cs_i)), see chunk_mfma.hip
+template <typename Tin, bool REV>
 __global__ __launch_bounds__(kThreads) void chunk_state_valu_kernel(
     const Tin* __restrict__ x, const Tin* __restrict__ Bm, const float* __restrict__ dtc,
     const float* __restrict__ cs, Tin* __restrict__ states, int T, int H, int G, int P, int N,
@@ -46,7 +47,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_valu_kernel(
     for (int i0 = 0; i0 < Q; i0 += 32) {
         if (threadIdx.x < 32) {
             const int i = i0 + threadIdx.x;
-            ws[threadIdx.x] = expf(cs_last - cs[cbase + i]) * dtc[cbase + i];
+            ws[threadIdx.x] =
+                REV ? expf(cs[cbase + i]) : expf(cs_last - cs[cbase + i]) * dtc[cbase + i];
         }
         __syncthreads();
         for (int e = threadIdx.x; e < 32 * 64; e += kThreads) {
@@ -148,23 +150,34 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_valu_kernel(
     }
 }
 
+template <bool REV>
+hipError_t launch_state_valu_t(const Shape& s, ssd_dtype dt, const void* x, const void* Bm,
+                               const float* dtc, const float* cs, void* states, hipStream_t st) {
+    const int tilesP = (s.P + 63) / 64, tilesN = (s.N + 63) / 64;
+    const unsigned blocks = (unsigned)((size_t)s.B * s.H * s.nC * tilesP * tilesN);
+    if (blocks == 0) return hipSuccess;
+    if (dt == SSD_F32)
+        chunk_state_valu_kernel<float, REV><<<blocks, kThreads, 0, st>>>(
+            (const float*)x, (const float*)Bm, dtc, cs, (float*)states, s.T, s.H, s.G, s.P, s.N,
+            s.Q, s.nC, tilesP, tilesN);
+    else
+        chunk_state_valu_kernel<__bf16, REV><<<blocks, kThreads, 0, st>>>(
+            (const __bf16*)x, (const __bf16*)Bm, dtc, cs, (__bf16*)states, s.T, s.H, s.G, s.P,
+            s.N, s.Q, s.nC, tilesP, tilesN);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_chunk_state_valu(const Shape& s, ssd_dtype dt, const void* x, const void* Bm,
                                    const float* dtc, const float* cs, void* states,
                                    hipStream_t st) {
-    const int tilesP = (s.P + 63) / 64, tilesN = (s.N + 63) / 64;
-    const unsigned blocks = (unsigned)((size_t)s.B * s.H * s.nC * tilesP * tilesN);
-    if (blocks == 0) return hipSuccess;
-    if (dt == SSD_F32)
-        chunk_state_valu_kernel<float><<<blocks, kThreads, 0, st>>>(
-            (const float*)x, (const float*)Bm, dtc, cs, (float*)states, s.T, s.H, s.G, s.P, s.N,
-            s.Q, s.nC, tilesP, tilesN);
-    else
-        chunk_state_valu_kernel<__bf16><<<blocks, kThreads, 0, st>>>(
-            (const __bf16*)x, (const __bf16*)Bm, dtc, cs, (__bf16*)states, s.T, s.H, s.G, s.P,
-            s.N, s.Q, s.nC, tilesP, tilesN);
-    return hipGetLastError();
+    return launch_state_valu_t<false>(s, dt, x, Bm, dtc, cs, states, st);
+}
+
+hipError_t launch_chunk_dstate_valu(const Shape& s, ssd_dtype dt, const void* dy, const void* Cm,
+                                    const float* cs, void* dstates, hipStream_t st) {
+    return launch_state_valu_t<true>(s, dt, dy, Cm, cs, cs, dstates, st);
 }
 
 hipError_t launch_chunk_scan_valu(const Shape& s, ssd_dtype dt, const void* x, const void* Bm,

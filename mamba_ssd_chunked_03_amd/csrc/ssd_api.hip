@@ -111,6 +111,40 @@ ssd_status run_chunk_state(const Shape& s, ssd_dtype dtype, const void* x, const
     return hip_status(ssd::launch_chunk_gram(s, B, C, gram, st));
 }
 
+// Backward workspace: the forward intermediates it recomputes (dt_chunk, cs, chunk states --
+// reused for the chunk entry-state gradients --, entry states), the exit gradients, and
+// the per-step / per-tile / per-chunk shares the finishing kernels reduce.
+struct BwdWorkspace {
+    float *dtc, *cs;
+    void *states, *entry, *exitg;
+    float *dcs, *direct, *lt_part, *dd_part, *dA_part;
+};
+
+size_t bwd_workspace_bytes(const Shape& s, BwdWorkspace* w, char* base) {
+    const size_t chunk_elems = (size_t)s.B * s.H * s.nC * s.Q;
+    const size_t state_elems = (size_t)s.B * s.H * s.nC * s.P * s.N;
+    const size_t tile_elems = (size_t)s.B * s.H * s.nC * (s.Q / ssd::chunk_bwd_valu_rows());
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char* p = base ? base + off : nullptr;
+        off += round_up(bytes);
+        return (float*)p;
+    };
+    BwdWorkspace ws;
+    ws.dtc = take(chunk_elems * sizeof(float));
+    ws.cs = take(chunk_elems * sizeof(float));
+    ws.states = take(state_elems * sizeof(float));  // fp32 size: enough for either dtype
+    ws.entry = take(state_elems * sizeof(float));
+    ws.exitg = take(state_elems * sizeof(float));
+    ws.dcs = take(chunk_elems * sizeof(float));
+    ws.direct = take(chunk_elems * sizeof(float));
+    ws.lt_part = take(tile_elems * sizeof(float));
+    ws.dd_part = take(tile_elems * sizeof(float));
+    ws.dA_part = take((size_t)s.B * s.H * s.nC * sizeof(float));
+    if (w) *w = ws;
+    return off;
+}
+
 ssd_status run_chunk_scan(const Shape& s, ssd_dtype dtype, const void* x, const void* B,
                           const void* C, const float* dtc, const float* cs, const float* D,
                           const void* entry, const void* gram, void* y, hipStream_t st) {
@@ -246,6 +280,70 @@ ssd_status ssd_fwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const f
                                              final_state, st));
     if (r != SSD_OK || !has_tokens) return r;
     return run_chunk_scan(s, dtype, x, B, C, ws.dtc, ws.cs, D, ws.entry, ws.gram, y, st);
+}
+
+size_t ssd_bwd_workspace_size(const ssd_dims* dims, int chunk_len) {
+    Shape s;
+    if (make_shape(dims, chunk_len, &s) != SSD_OK) return 0;
+    return bwd_workspace_bytes(s, nullptr, nullptr);
+}
+
+ssd_status ssd_bwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const float* dt,
+                   const float* A, const void* B, const void* C, const float* D, int chunk_len,
+                   const float* init_state, const void* dy, const float* d_final, void* dx,
+                   float* ddt, float* dA, void* dB, void* dC, float* dD, float* d_init,
+                   void* workspace, size_t workspace_bytes_given, void* stream) {
+    Shape s;
+    ssd_status r = make_shape(dims, chunk_len, &s);
+    if (r != SSD_OK) return r;
+    if (!valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
+    const bool has_tokens = (size_t)s.B * s.T > 0;
+    if (!dA || !dD) return SSD_ERR_NULL;
+    if (has_tokens && (!x || !dt || !A || !B || !C || !D || !dy || !dx || !ddt || !dB || !dC))
+        return SSD_ERR_NULL;
+    if (any_misaligned({x, B, C, dy, dx, dB, dC, workspace}) ||
+        any_misaligned4({dt, A, D, init_state, d_final, ddt, dA, dD, d_init}))
+        return SSD_ERR_ALIGN;
+    BwdWorkspace ws;
+    const size_t need = bwd_workspace_bytes(s, &ws, (char*)workspace);
+    if (need > 0 && (!workspace || workspace_bytes_given < need)) return SSD_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    const bool mfma_state = dtype == SSD_BF16 && ssd::chunk_state_mfma_supported(s);
+    if (has_tokens) {
+        // the forward intermediates: log decays, chunk states, entry states
+        r = hip_status(ssd::launch_chunk_cumsum(s, dt, A, ws.dtc, ws.cs, st));
+        if (r != SSD_OK) return r;
+        r = run_chunk_state(s, dtype, x, B, ws.dtc, ws.cs, ws.states, nullptr, nullptr, st);
+        if (r != SSD_OK) return r;
+        r = hip_status(ssd::launch_state_passing(s, dtype, ws.states, ws.cs, init_state,
+                                                 ws.entry, nullptr, st));
+        if (r != SSD_OK) return r;
+        // the entry-state gradient of every chunk through its own outputs (into the chunk
+        // state buffer, no longer needed)
+        r = hip_status(mfma_state
+                           ? ssd::launch_chunk_dstate_mfma(s, dy, C, ws.cs, ws.states, st)
+                           : ssd::launch_chunk_dstate_valu(s, dtype, dy, C, ws.cs, ws.states, st));
+        if (r != SSD_OK) return r;
+    }
+    // carried backwards over the chunks; with T == 0 this copies d_final (or zeros) to d_init
+    r = hip_status(ssd::launch_state_passing_rev(s, dtype, ws.states, ws.cs, d_final, ws.exitg,
+                                                 d_init, st));
+    if (r != SSD_OK) return r;
+    ssd::BwdArgs a;
+    a.x = x; a.Bm = B; a.Cm = C; a.dy = dy;
+    a.dtc = ws.dtc; a.cs = ws.cs; a.A = A; a.D = D;
+    a.entry = ws.entry; a.exitg = ws.exitg;
+    a.dx = dx; a.dB = dB; a.dC = dC;
+    a.ddt = ddt; a.dA = dA; a.dD = dD;
+    a.dcs = ws.dcs; a.direct = ws.direct;
+    a.lt_part = ws.lt_part; a.dd_part = ws.dd_part; a.dA_part = ws.dA_part;
+    const int rows = ssd::chunk_bwd_valu_rows();
+    if (has_tokens) {
+        r = hip_status(ssd::launch_chunk_bwd_valu(s, dtype, a, st));
+        if (r != SSD_OK) return r;
+    }
+    // dA and dD are written even with no tokens (zeros)
+    return hip_status(ssd::launch_bwd_finalize(s, a, rows, st));
 }
 
 ssd_status ssd_decode_step(const ssd_dims* dims, ssd_dtype dtype, const void* x, const float* dt,

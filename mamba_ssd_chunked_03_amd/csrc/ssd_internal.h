@@ -64,4 +64,35 @@ hipError_t launch_chunk_scan_mfma(const Shape& s, const void* x, const void* Cm,
                                   const float* cs, const float* D, const void* entry,
                                   const void* gram, void* y, hipStream_t st);
 
+// ---- backward ------------------------------------------------------------------------
+// The gradient of every chunk's entry state through that chunk's own outputs,
+// Z[c][p][n] = sum_i exp(cs_i) C_i[n] dy_i[p] (the chunk_state kernels with C for B, dy for
+// x and weight exp(cs_i)); [B][H][nC][P][N] in dtype.
+hipError_t launch_chunk_dstate_valu(const Shape& s, ssd_dtype dt, const void* dy, const void* Cm,
+                                    const float* cs, void* dstates, hipStream_t st);
+hipError_t launch_chunk_dstate_mfma(const Shape& s, const void* dy, const void* Cm,
+                                    const float* cs, void* dstates, hipStream_t st);
+// the inter-chunk carry run last chunk first: exit_grads[c] = dL/d(end state of chunk c),
+// d_init = dL/d init_state ([N][P] fp32, may be NULL), from d_final (NULL = zero)
+hipError_t launch_state_passing_rev(const Shape& s, ssd_dtype dtype, const void* dstates,
+                                    const float* cs, const float* d_final, void* exit_grads,
+                                    float* d_init, hipStream_t st);
+
+// Everything the in-chunk backward and its finishing kernels read and write.
+struct BwdArgs {
+    const void *x, *Bm, *Cm, *dy;          // inputs, dtype
+    const float *dtc, *cs, *A, *D;         // fp32
+    const void *entry, *exitg;             // entry states and exit gradients, [P][N], dtype
+    void *dx, *dB, *dC;                    // outputs, dtype
+    float *ddt, *dA, *dD;                  // outputs, fp32
+    float *dcs, *direct;                   // [B][H][nC][Q]: dL/dcs and the explicit dL/ddt
+    float *lt_part, *dd_part;              // [B][H][nC][Q / rows]: per row tile
+    float* dA_part;                        // [B][H][nC]
+};
+int chunk_bwd_valu_rows();
+hipError_t launch_chunk_bwd_valu(const Shape& s, ssd_dtype dtype, const BwdArgs& a,
+                                 hipStream_t st);
+// ddt and dA, dD from the per-chunk and per-tile shares (rows: rows per tile)
+hipError_t launch_bwd_finalize(const Shape& s, const BwdArgs& a, int rows, hipStream_t st);
+
 }  // namespace ssd

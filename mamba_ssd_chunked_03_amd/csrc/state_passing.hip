@@ -51,7 +51,10 @@ __device__ __forceinline__ void store4(__bf16* dst, float4 v) {
 // T: element type of the chunk states read and of the entry states written (fp32, or bf16
 // on the bf16 path, where both are matrix-core operands or their source); the running
 // state stays fp32.
-template <typename T>
+// REV walks the chunks last to first: the backward pass carries the entry-state gradients
+// the same way, dE_c = Z_c + exp(cs[c][Q-1]) dE_{c+1} from dE_nC = dL/d final state, and
+// stores dE_{c+1} (the gradient of chunk c's end state) for chunk c.
+template <typename T, bool REV>
 __global__ __launch_bounds__(kThreads) void state_passing_kernel(
     const T* __restrict__ states, const float* __restrict__ cs,
     const float* __restrict__ init, T* __restrict__ entry, float* __restrict__ final_state,
@@ -71,6 +74,8 @@ __global__ __launch_bounds__(kThreads) void state_passing_kernel(
     }
     const size_t base = (size_t)bh * nC * NP + e;
     const float* csl = cs + (size_t)bh * nC * Q + (Q - 1);  // each chunk's total log decay
+    // k-th chunk visited
+    auto at = [&](int k) { return REV ? nC - 1 - k : k; };
 
     int c = 0;
     for (; c + kUnroll <= nC; c += kUnroll) {
@@ -78,19 +83,19 @@ __global__ __launch_bounds__(kThreads) void state_passing_kernel(
         float a[kUnroll];
 #pragma unroll
         for (int k = 0; k < kUnroll; ++k) {
-            v[k] = load4(states + base + (size_t)(c + k) * NP);
-            a[k] = csl[(size_t)(c + k) * Q];
+            v[k] = load4(states + base + (size_t)at(c + k) * NP);
+            a[k] = csl[(size_t)at(c + k) * Q];
         }
 #pragma unroll
         for (int k = 0; k < kUnroll; ++k) {
-            store4(entry + base + (size_t)(c + k) * NP, s);
+            store4(entry + base + (size_t)at(c + k) * NP, s);
             s = fma4(expf(a[k]), s, v[k]);
         }
     }
     for (; c < nC; ++c) {
-        const float4 v = load4(states + base + (size_t)c * NP);
-        store4(entry + base + (size_t)c * NP, s);
-        s = fma4(expf(csl[(size_t)c * Q]), s, v);
+        const float4 v = load4(states + base + (size_t)at(c) * NP);
+        store4(entry + base + (size_t)at(c) * NP, s);
+        s = fma4(expf(csl[(size_t)at(c) * Q]), s, v);
     }
     if (final_state) {
         float* out = final_state + (size_t)bh * NP;  // [N][P]
@@ -101,24 +106,36 @@ __global__ __launch_bounds__(kThreads) void state_passing_kernel(
     }
 }
 
-}  // namespace
-
-hipError_t launch_state_passing(const Shape& s, ssd_dtype dtype, const void* states,
-                                const float* cs, const float* init, void* entry,
-                                float* final_state, hipStream_t st) {
+template <bool REV>
+hipError_t launch_passing_t(const Shape& s, ssd_dtype dtype, const void* states, const float* cs,
+                            const float* init, void* entry, float* final_state, hipStream_t st) {
     const int NP = s.N * s.P;
     const int tiles = (NP + kThreads * 4 - 1) / (kThreads * 4);
     const unsigned blocks = (unsigned)((size_t)s.B * s.H * tiles);
     if (blocks == 0) return hipSuccess;
     if (dtype == SSD_BF16)
-        state_passing_kernel<__bf16><<<blocks, kThreads, 0, st>>>(
+        state_passing_kernel<__bf16, REV><<<blocks, kThreads, 0, st>>>(
             (const __bf16*)states, cs, init, (__bf16*)entry, final_state, s.nC, s.Q, s.P, s.N,
             tiles);
     else
-        state_passing_kernel<float><<<blocks, kThreads, 0, st>>>(
+        state_passing_kernel<float, REV><<<blocks, kThreads, 0, st>>>(
             (const float*)states, cs, init, (float*)entry, final_state, s.nC, s.Q, s.P, s.N,
             tiles);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_state_passing(const Shape& s, ssd_dtype dtype, const void* states,
+                                const float* cs, const float* init, void* entry,
+                                float* final_state, hipStream_t st) {
+    return launch_passing_t<false>(s, dtype, states, cs, init, entry, final_state, st);
+}
+
+hipError_t launch_state_passing_rev(const Shape& s, ssd_dtype dtype, const void* dstates,
+                                    const float* cs, const float* d_final, void* exit_grads,
+                                    float* d_init, hipStream_t st) {
+    return launch_passing_t<true>(s, dtype, dstates, cs, d_final, exit_grads, d_init, st);
 }
 
 }  // namespace ssd

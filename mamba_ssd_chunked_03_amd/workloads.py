@@ -141,6 +141,24 @@ def generate(w, device="cpu"):
     return out
 
 
+def generate_grads(w, device="cpu", with_final=True):
+    """Upstream gradients for the backward of workload `w`, from their own generator
+    (seeded with seed + 1, drawn in fp32 in the order dy, d_final):
+      dy      ~ N(0, 1), [B,T,H,P], cast to the workload dtype
+      d_final ~ N(0, 1), [B,H,N,P] fp32, or None when with_final is False."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(w.seed) + 1)
+    Bz, T, H, P, N = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate
+    dy = torch.randn((Bz, T, H, P), generator=g, dtype=torch.float32).to(_torch_dtype(w.dtype))
+    d_final = None
+    if with_final:
+        d_final = torch.randn((Bz, H, N, P), generator=g, dtype=torch.float32)
+    out = dict(dy=dy, d_final=d_final)
+    if device != "cpu":
+        out = {k: (None if v is None else v.to(device)) for k, v in out.items()}
+    return out
+
+
 def head_slice(inputs, w, b, h):
     """The inputs of the single sequence (batch b, head h) as a B=1, H=1, G=1 problem.
     Every (batch, head) pair is independent, so the full outputs for that pair can be

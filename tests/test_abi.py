@@ -146,3 +146,49 @@ def test_validation_errors_before_any_launch(lib):
     assert lib.ssd_decode_step(ctypes.byref(D()), 1, *[ctypes.c_void_p(264)] * 8, None) == 4
     assert lib.ssd_decode_step(None, 1, None, None, None, None, None, None, None, None,
                                None) == 1
+
+
+def test_bwd_workspace_size(lib):
+    d = D(4, 4096, 80, 64, 128, 1)
+    nC = 16
+    chunk = 4 * 80 * nC * 256 * 4
+    state = 4 * 80 * nC * 64 * 128 * 4
+    tiles = 4 * 80 * nC * (256 // 16) * 4
+    per_chunk = 4 * 80 * nC * 4
+    # dt_chunk, cs, chunk states (reused for the entry-state gradients), entry states, exit
+    # gradients, dL/dcs, the explicit dL/ddt, two per-tile shares and dA's per-chunk share
+    assert binding.ssd_bwd_workspace_size(d, 256) == \
+        4 * chunk + 3 * state + 2 * tiles + per_chunk
+    assert binding.ssd_bwd_workspace_size(D(h=3, g=2), 64) == 0
+    assert binding.ssd_bwd_workspace_size(D(t=0), 64) == 0
+
+
+def _bwd(lib, d, dtype=0, q=64, ptrs=None, ws_bytes=1 << 30):
+    names = ("x", "dt", "A", "B", "C", "D", "init", "dy", "dfin", "dx", "ddt", "dA", "dB", "dC",
+             "dD", "dinit", "ws")
+    p = {k: 256 for k in names}
+    p.update(init=None, dfin=None, dinit=None)
+    p.update(ptrs or {})
+    v = {k: (None if val is None else ctypes.c_void_p(val)) for k, val in p.items()}
+    return lib.ssd_bwd(ctypes.byref(d), dtype, v["x"], v["dt"], v["A"], v["B"], v["C"], v["D"], q,
+                       v["init"], v["dy"], v["dfin"], v["dx"], v["ddt"], v["dA"], v["dB"],
+                       v["dC"], v["dD"], v["dinit"], v["ws"], ws_bytes, None)
+
+
+def test_bwd_validation_errors_before_any_launch(lib):
+    assert _bwd(lib, D(h=3, g=2)) == 2
+    assert _bwd(lib, D(p=48)) == 3
+    assert _bwd(lib, D(), q=32) == 3
+    assert _bwd(lib, D(), dtype=3) == 3
+    for k in ("x", "dt", "A", "B", "C", "D", "dy", "dx", "ddt", "dB", "dC"):
+        assert _bwd(lib, D(), ptrs={k: None}) == 1, k
+    # dA and dD are written even for an empty problem, so they are always required
+    assert _bwd(lib, D(b=0), ptrs=dict(dA=None)) == 1
+    assert _bwd(lib, D(t=0), ptrs=dict(dD=None)) == 1
+    assert _bwd(lib, D(), ptrs=dict(dy=264)) == 4
+    assert _bwd(lib, D(), ptrs=dict(dB=264)) == 4
+    assert _bwd(lib, D(), ptrs=dict(ddt=258)) == 4
+    assert _bwd(lib, D(), ptrs=dict(dfin=258)) == 4
+    assert _bwd(lib, D(), ptrs=dict(ws=None)) == 5
+    assert _bwd(lib, D(), ws_bytes=100) == 5
+    assert lib.ssd_bwd(None, 0, *[None] * 6, 64, *[None] * 11, 0, None) == 1
