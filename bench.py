@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--decode", default="", metavar="WORKLOAD",
                     help="instead of the forward, time ssd_decode_step on a decode workload "
                          "(one token per sequence per step) and print its own JSON line")
+    ap.add_argument("--bwd", default="", metavar="WORKLOAD",
+                    help="instead of the forward, time the backward (ssd_bwd) on a workload and "
+                         "print its own JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to calibrate the "
                          "HBM byte counters against a known traffic, and exit")
@@ -144,6 +147,63 @@ def bench_decode(args, w, torch, binding, roofline, generate):
     }), flush=True)
 
 
+def bench_bwd(args, w, torch, binding, roofline, generate, generate_grads):
+    """Whole ssd_bwd calls back to back (the forward intermediates it recomputes
+    included): tokens/s = B*T / call time.  The call's kernels are listed with their
+    algorithmic bytes and FLOPs; their durations come from a kernel trace."""
+    dev = torch.device("cuda:0")
+    log(f"[bench bwd] {w.describe()}")
+    cpu = generate(w)
+    up = generate_grads(w)
+    d = {k: (None if v is None else v.to(dev)) for k, v in cpu.items()}
+    u = {k: (None if v is None else v.to(dev)) for k, v in up.items()}
+    dims = binding.SsdDims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups)
+    ws = torch.empty(binding.ssd_bwd_workspace_size(dims, w.chunk_len), dtype=torch.uint8,
+                     device=dev)
+    out = dict(dx=torch.empty_like(d["x"]), ddt=torch.empty_like(d["dt"]),
+               dA=torch.empty_like(d["A"]), dB=torch.empty_like(d["B"]),
+               dC=torch.empty_like(d["C"]), dD=torch.empty_like(d["D"]),
+               d_init=torch.empty((w.batch, w.nheads, w.dstate, w.headdim), device=dev))
+    step = lambda: binding.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], w.chunk_len,
+                                   u["dy"], init_state=d["init_state"], d_final=u["d_final"],
+                                   out=out, workspace=ws)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    costs = roofline.bwd_costs(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups,
+                               w.chunk_len, w.dtype, init_state=w.init_state)
+    tot_bytes = sum(c.bytes for c in costs)
+    tot_flops = sum(c.flops for c in costs)
+    gbs = tot_bytes / (us * 1e-6) / 1e9
+    ms_step = elapsed / args.steps * 1e3
+    print(json.dumps({
+        "metric": "SSD bwd tokens/sec on 1 MI355X", "value": round(w.tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen,
+                   "nheads": w.nheads, "headdim": w.headdim, "dstate": w.dstate,
+                   "ngroups": w.ngroups, "chunk_len": w.chunk_len, "input_dtype": w.dtype,
+                   "init_state": w.init_state},
+        "roofline": {"bound": "hbm", "kernel": "ssd_bwd (all kernels)", "achieved": round(gbs, 1),
+                     "peak": roofline.PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbs / roofline.PEAK_HBM_GBPS, 4), "traffic": None},
+        "call_us": round(us, 2),
+        "kernels": {c.name: {"alg_bytes": int(c.bytes), "alg_flops": int(c.flops)} for c in costs},
+        "alg_bytes_total": int(tot_bytes), "alg_flops_total": int(tot_flops),
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -164,9 +224,12 @@ def main():
                           "read_bytes_per_copy": 4 * n, "write_bytes_per_copy": 4 * n}))
         return
     from mamba_ssd_chunked_03_amd import binding, roofline, traffic
-    from mamba_ssd_chunked_03_amd.workloads import DECODE, WORKLOADS, generate
+    from mamba_ssd_chunked_03_amd.workloads import DECODE, WORKLOADS, generate, generate_grads
     if args.decode:
         return bench_decode(args, DECODE[args.decode], torch, binding, roofline, generate)
+    if args.bwd:
+        return bench_bwd(args, WORKLOADS[args.bwd], torch, binding, roofline, generate,
+                         generate_grads)
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")

@@ -1,0 +1,531 @@
+// chunk_bwd_mfma.hip -- the in-chunk backward on gfx950 bf16 MFMA (headdim 64, dstate 64 or
+// 128, any supported chunk length).
+//
+// It computes what chunk_bwd_valu.hip computes (the formulas are stated there): dx, the
+// head-summed dB and dC, and per head the explicit step-size gradient and dL/dcs.
+//
+// One workgroup of four waves per (batch, group, chunk, block J of 64 rows), looping over
+// the heads of the group.  Wave w owns the 16 columns j = j0 + 16 w + (0..15) of J.  With
+// M = dy x^T, W[t][i] = dt_i exp(cs_t - cs_i) M[t][i] (t >= i) is the matrix whose
+// head sum gives both diagonal-block products, dC_j += sum_i W[j][i] B_i and
+// dB_j += sum_t W[t][j] C_t.  For its columns a wave needs
+//   the row strip  W^T[i][j], i <= j   (rows i of W^T, from M^T = x dy^T)  -> dC_j
+//   the column strip W[t][j],  t >= j  (rows t, from M = dy x^T)          -> dB_j, dx_j
+// i.e. Q / 16 + 1 tiles of 16 x 16 (the diagonal tile twice), padded to whole 32-row
+// blocks: Q / 16 + 2 tiles for every wave and every J.  W is accumulated over the heads
+// in registers (fp32), so dB and dC cost two products per workgroup rather than per head.
+//
+// Everything is computed transposed so that the output rows (j) are MFMA columns: a lane
+// holds 4 consecutive p (or n) of one row j, which makes every per-row scalar a column sum
+// over the four lane groups and every store an 8-byte run:
+//   dx^T[p][j]  = D dy + dt_j (sum_t dy[t][p] U[t][j] + exp(cs_last - cs_j) (F B_j)[p])
+//                 with U[t][j] = exp(cs_t - cs_j) (C_t . B_j)
+//   dB^T[n][j] += sum_p F[p][n] (dt_j exp(cs_last - cs_j) x_j[p])   (+ sum_t C[t][n] W[t][j])
+//   dC^T[n][j] += sum_p E[p][n] (exp(cs_j) dy_j[p])                  (+ sum_i B[i][n] W^T[i][j])
+// MFMA operand layouts are those of mfma_common.h: contractions over time (t, i) and over
+// p use the 8-slot relabelling so that accumulator tiles feed the next product directly;
+// contractions over n (the C B^T tiles, F B_j, E C_j) read natural 8-element runs.
+//
+// Per head the x rows [0, j0 + 64) and dy rows [j0, Q) (one array of Q + 64 rows), E, F,
+// cs and dt are copied into LDS straight from HBM (buffer_load ... lds), double-buffered
+// so that the next head's copy runs under this head's products.  The group's B and C
+// chunks pass through the same LDS before the loop (for C B^T and the B_j, C_j operands)
+// and after it (for the two W products).
+#include "mfma_common.h"
+#include "ssd_internal.h"
+
+namespace ssd {
+namespace {
+
+using namespace mfma;
+
+template <int Q, int N, int P>
+struct BwdCfg {
+    static constexpr int NTH = 256;
+    static constexpr int NJ = Q / 64;               // row blocks per chunk
+    static constexpr int PAIRS = (Q / 16 + 2) / 2;  // 32-row blocks of strip per wave
+    static constexpr int PPR = P / 8, NPR = N / 8;  // 16-byte pieces per row
+    static constexpr int NKB = N / 32, PKB = P / 32;
+    static constexpr int NT = N / 16, PT = P / 16;
+    static constexpr unsigned XYB = (Q + 64) * P * 2;  // x rows [0, j0+64), dy rows [j0, Q)
+    static constexpr unsigned EB = P * N * 2;          // E or F, [p][n]
+    static constexpr unsigned FB = Q * 4;              // cs or dt
+    static constexpr unsigned ITEM = XYB + 2 * EB + 2 * FB;
+    static constexpr unsigned BCB = Q * N * 2;         // one B or C chunk
+    static constexpr unsigned LDS = 2 * ITEM + 64;     // + the per-head workgroup shares
+    static_assert(P == 64 && (N == 64 || N == 128), "shape");
+    static_assert(2 * BCB <= 2 * ITEM && (Q + 64) * N * 2 <= 2 * ITEM, "B/C staging fits");
+};
+
+// 8 bf16 at the relabelled k-slots {32kb + 4g .. +3, 32kb + 16 + 4g .. +3} of LDS row `row`
+__device__ __forceinline__ bf16x8 frag_rl(const unsigned char* base, int row, int kb, int g4,
+                                         int ppr) {
+    const uint2 lo = *reinterpret_cast<const uint2*>(base + swz_off(row, 32 * kb + 4 * g4, ppr));
+    const uint2 hi =
+        *reinterpret_cast<const uint2*>(base + swz_off(row, 32 * kb + 16 + 4 * g4, ppr));
+    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+// 8 bf16 at the natural k-slots 32kb + 8g .. +7
+__device__ __forceinline__ bf16x8 frag_nat(const unsigned char* base, int row, int kb, int g4,
+                                          int ppr) {
+    return *reinterpret_cast<const bf16x8*>(base + swz_off(row, 32 * kb + 8 * g4, ppr));
+}
+// transpose read: A operand (row = feature f0 + l16, k = data rows r0 + {4g..4g+3, 16+4g..})
+__device__ __forceinline__ bf16x8 frag_tr(const unsigned char* base, int r0, int f0, int l16,
+                                         int g4, int ppr) {
+    const unsigned off = swz_off(r0 + 4 * g4 + (l16 >> 2), f0 + 4 * (l16 & 3), ppr);
+    const uint2 lo = lds_read_tr16(base + off);
+    const uint2 hi = lds_read_tr16(base + off + 16u * ppr * 16u);  // rows + 16 (ppr <= 16)
+    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+__device__ __forceinline__ bf16x8 scale8(bf16x8 v, float s) {
+    const uint4 r = __builtin_bit_cast(uint4, v);
+    return __builtin_bit_cast(
+        bf16x8, make_uint4(pack_bf16(bf16_lo(r.x) * s, bf16_hi(r.x) * s),
+                           pack_bf16(bf16_lo(r.y) * s, bf16_hi(r.y) * s),
+                           pack_bf16(bf16_lo(r.z) * s, bf16_hi(r.z) * s),
+                           pack_bf16(bf16_lo(r.w) * s, bf16_hi(r.w) * s)));
+}
+__device__ __forceinline__ float dot8(bf16x8 a, bf16x8 b) {
+    const uint4 x = __builtin_bit_cast(uint4, a), y = __builtin_bit_cast(uint4, b);
+    float s = bf16_lo(x.x) * bf16_lo(y.x);
+    s = fmaf(bf16_hi(x.x), bf16_hi(y.x), s);
+    s = fmaf(bf16_lo(x.y), bf16_lo(y.y), s);
+    s = fmaf(bf16_hi(x.y), bf16_hi(y.y), s);
+    s = fmaf(bf16_lo(x.z), bf16_lo(y.z), s);
+    s = fmaf(bf16_hi(x.z), bf16_hi(y.z), s);
+    s = fmaf(bf16_lo(x.w), bf16_lo(y.w), s);
+    return fmaf(bf16_hi(x.w), bf16_hi(y.w), s);
+}
+__device__ __forceinline__ float colsum(float v) {  // over the four lane groups
+    v += __shfl_xor(v, 16, 64);
+    return v + __shfl_xor(v, 32, 64);
+}
+__device__ __forceinline__ float wavesum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// nrows rows of a [rows][feat] bf16 matrix (row stride rowb bytes in HBM, from row
+// src_row0) into LDS rows dst_row0.. (PPRX 16-byte pieces per row), swizzled.  Each
+// instruction fills 64 consecutive 16-byte LDS slots (lane L at its base + 16 L), so the
+// swizzle is applied on the source side: slot `sl` of LDS row dr receives piece
+// sl ^ (dr % PPRX).  nrows * PPRX is a multiple of 64.
+template <int PPRX>
+__device__ __forceinline__ void issue_rows(u32x4 rsrc, unsigned rowb, int src_row0, uint32_t lds,
+                                           int dst_row0, int nrows, int wave, int lane) {
+    const int ninst = nrows * PPRX / 64;
+    const uint32_t base = lds + (unsigned)dst_row0 * PPRX * 16u;
+    for (int k = wave; k < ninst; k += 4) {
+        const int m = k * 64 + lane;
+        const int r = m / PPRX, sl = m % PPRX;
+        const int dr = dst_row0 + r;
+        dma16(rsrc, base + (unsigned)k * 1024u,
+              (unsigned)(src_row0 + r) * rowb + (unsigned)(sl ^ (dr & (PPRX - 1))) * 16u);
+    }
+}
+
+template <int Q, int N, int P>
+__device__ __forceinline__ void issue_item(const __bf16* x, const __bf16* dy, const __bf16* entry,
+                                           const __bf16* exitg, const float* cs, const float* dtc,
+                                           int b, int h, int c, int j0, int Lc, int T, int H,
+                                           int nC, uint32_t lds, int wave, int lane) {
+    using C_ = BwdCfg<Q, N, P>;
+    const unsigned rowb = (unsigned)(H * P * 2);
+    const size_t xo = ((size_t)(b * T + c * Q) * H + h) * P;
+    const u32x4 xr = raw_rsrc(x + xo, (unsigned)Lc * rowb);
+    const u32x4 yr = raw_rsrc(dy + xo, (unsigned)Lc * rowb);
+    // x rows [0, j0 + 64) at LDS rows 0.., dy rows [j0, Q) at LDS rows j0 + 64..
+    issue_rows<C_::PPR>(xr, rowb, 0, lds, 0, j0 + 64, wave, lane);
+    issue_rows<C_::PPR>(yr, rowb, j0, lds, j0 + 64, Q - j0, wave, lane);
+    const size_t so = ((size_t)(b * H + h) * nC + c) * P * N;
+    issue_rows<C_::NPR>(raw_rsrc(entry + so, C_::EB), N * 2, 0, lds + C_::XYB, 0, P, wave, lane);
+    issue_rows<C_::NPR>(raw_rsrc(exitg + so, C_::EB), N * 2, 0, lds + C_::XYB + C_::EB, 0, P,
+                        wave, lane);
+    const size_t cb = ((size_t)(b * H + h) * nC + c) * Q;
+    if (wave == 0 && lane < Q / 4)
+        dma16(raw_rsrc(cs + cb, C_::FB), lds + C_::XYB + 2 * C_::EB, lane * 16u);
+    if (wave == 1 && lane < Q / 4)
+        dma16(raw_rsrc(dtc + cb, C_::FB), lds + C_::XYB + 2 * C_::EB + C_::FB, lane * 16u);
+}
+
+template <int Q, int N, int P>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void chunk_bwd_mfma_kernel(
+    const __bf16* __restrict__ x, const __bf16* __restrict__ Bm, const __bf16* __restrict__ Cm,
+    const float* __restrict__ dtc, const float* __restrict__ cs, const float* __restrict__ D,
+    const __bf16* __restrict__ entry, const __bf16* __restrict__ exitg,
+    const __bf16* __restrict__ dy, __bf16* __restrict__ dx, __bf16* __restrict__ dB,
+    __bf16* __restrict__ dC, float* __restrict__ dcs, float* __restrict__ direct,
+    float* __restrict__ lt_part, float* __restrict__ dd_part, int T, int H, int G, int nC) {
+    using C_ = BwdCfg<Q, N, P>;
+    constexpr int NJ = C_::NJ, PAIRS = C_::PAIRS, PPR = C_::PPR, NPR = C_::NPR;
+    constexpr int NKB = C_::NKB, PKB = C_::PKB, NT = C_::NT, PT = C_::PT;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const uint32_t lds0 = lds_addr(smem);
+    float* const shares = reinterpret_cast<float*>(smem + 2 * C_::ITEM);  // [2][4][2]
+
+    // neighbouring row blocks and chunks on the same XCD (its L2 holds their shared data)
+    const int nwg = gridDim.x, blk = blockIdx.x;
+    const int wp = (nwg % 8 == 0) ? (blk & 7) * (nwg >> 3) + (blk >> 3) : blk;
+    const int unit = wp / NJ, rj = wp % NJ;
+    const int c = unit % nC, g = (unit / nC) % G, b = unit / (nC * G);
+    const int j0 = rj * 64, t0 = c * Q;
+    const int Lc = min(Q, T - t0);
+    if (j0 >= Lc) return;  // no valid row
+    const int hpg = H / G;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int jtile = j0 / 16 + wave;                // the wave's column tile (16 rows j)
+    const int rsp = (j0 / 16 + (wave | 1) + 1) / 2;  // row-strip blocks: rows i < 32 rsp
+    const int tbase = j0 + 16 * (wave & ~1);        // column strip: rows t >= tbase
+
+    // ---------------------------------------------------------------- B and C chunks
+    {
+        const unsigned rowb = (unsigned)(G * N * 2);
+        const size_t bo = ((size_t)(b * T + t0) * G + g) * N;
+        issue_rows<NPR>(raw_rsrc(Bm + bo, (unsigned)Lc * rowb), rowb, 0, lds0, 0, Q, wave, lane);
+        issue_rows<NPR>(raw_rsrc(Cm + bo, (unsigned)Lc * rowb), rowb, 0, lds0 + C_::BCB, 0, Q,
+                        wave, lane);
+    }
+    dma_barrier();
+    const unsigned char* sBc = smem;
+    const unsigned char* sCc = smem + C_::BCB;
+    bf16x8 bj[NKB], cj[NKB];  // B_j, C_j over n (natural slots)
+    uint2 gt[2 * PAIRS];      // C B^T on the strips (bf16), accumulator layout
+    {
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int jl = j0 + 16 * wave + l16;  // the lane's column j (chunk row)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+        bj[kb] = frag_nat(sBc, jl, kb, g4, NPR);
+        cj[kb] = frag_nat(sCc, jl, kb, g4, NPR);
+    }
+    // C B^T on the strips, rounded to bf16: G^T[i][j] = B_i . C_j and G[t][j] = C_t . B_j
+#pragma unroll
+    for (int k = 0; k < PAIRS; ++k) {
+        const bool isrs = k < rsp;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int row = (isrs ? 32 * k : tbase + 32 * (k - rsp)) + 16 * u + l16;
+            const unsigned char* src = isrs ? sBc : sCc;
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+                acc = mfma16(frag_nat(src, row, kb, g4, NPR), isrs ? cj[kb] : bj[kb], acc);
+            gt[2 * k + u] = make_uint2(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]));
+        }
+    }
+    }
+    lds_barrier();  // B and C are no longer read: the item buffers are free
+
+    f32x4 wacc[2 * PAIRS];  // W over the strips, summed over the heads
+#pragma unroll
+    for (int s = 0; s < 2 * PAIRS; ++s) wacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 dbacc[NT], dcacc[NT];  // dB^T, dC^T [n][j]
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) dbacc[nt] = dcacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    issue_item<Q, N, P>(x, dy, entry, exitg, cs, dtc, b, g * hpg, c, j0, Lc, T, H, nC, lds0, wave,
+                        lane);
+#pragma unroll 1
+    for (int hh = 0; hh < hpg; ++hh) {
+        const int h = g * hpg + hh;
+        const int buf = hh & 1;
+        dma_barrier();  // this head's copies have landed; the other buffer is free
+        if (hh > 0 && tid == 0) {
+            const float* sh = shares + (buf ^ 1) * 8;
+            const size_t pi = ((size_t)(b * H + h - 1) * nC + c) * NJ + rj;
+            lt_part[pi] = (sh[0] + sh[2]) + (sh[4] + sh[6]);
+            dd_part[pi] = (sh[1] + sh[3]) + (sh[5] + sh[7]);
+        }
+        if (hh + 1 < hpg)
+            issue_item<Q, N, P>(x, dy, entry, exitg, cs, dtc, b, h + 1, c, j0, Lc, T, H, nC,
+                                lds0 + (buf ^ 1) * C_::ITEM, wave, lane);
+        // lane-dependent values are re-derived every head from an opaque copy of the lane
+        // index, so the compiler recomputes the LDS addresses instead of keeping them all
+        // live across the loop
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int l16 = ln & 15, g4 = ln >> 4;
+        const int jl = j0 + 16 * wave + l16;
+        const bool vj = jl < Lc;
+        const unsigned char* sXY = smem + buf * C_::ITEM;
+        const unsigned char* sE = sXY + C_::XYB;
+        const unsigned char* sF = sE + C_::EB;
+        const float* s_cs = reinterpret_cast<const float*>(sF + C_::EB);
+        const float* s_dt = s_cs + Q;
+        const float cs_last = s_cs[Q - 1];
+        const float csj = s_cs[jl], dtj = s_dt[jl];
+        const float ej = exp2_fast(csj * kLog2e), fj = exp2_fast((cs_last - csj) * kLog2e);
+
+        bf16x8 xj[PKB], yj[PKB];  // x_j, dy_j over p (relabelled slots)
+#pragma unroll
+        for (int kb = 0; kb < PKB; ++kb) {
+            xj[kb] = frag_rl(sXY, jl, kb, g4, PPR);
+            yj[kb] = frag_rl(sXY, jl + 64, kb, g4, PPR);
+        }
+
+        // ---- the strips: M, W, and the diagonal-block part of dx
+        float rs = 0.f, ccol = 0.f;
+        f32x4 dxa[PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) dxa[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < PAIRS; ++k) {
+            const bool isrs = k < rsp;
+            const int rbase = isrs ? 32 * k : tbase + 32 * (k - rsp);  // chunk row of the block
+            const int rho = isrs ? rbase : rbase + 64;                 // its LDS row
+            uint32_t ub[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                // the tile's place against the wave's column tile: every element kept, the
+                // diagonal tile (kept on one side of it), or none (a padding tile)
+                const int ti = rbase / 16 + u;
+                const int mode = isrs ? (ti < jtile ? 0 : ti == jtile ? 1 : 2)
+                                      : (ti > jtile ? 0 : ti == jtile ? 1 : 2);
+                if (mode == 2) continue;
+                f32x4 m = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < PKB; ++kb)
+                    m = mfma16(frag_rl(sXY, rho + 16 * u + l16, kb, g4, PPR),
+                               isrs ? yj[kb] : xj[kb], m);
+                const int r0 = rbase + 16 * u + 4 * g4;  // chunk row of element q = 0
+                const float4 csr = *reinterpret_cast<const float4*>(&s_cs[r0]);
+                const float4 dtr = *reinterpret_cast<const float4*>(&s_dt[r0]);
+                const uint2 gg = gt[2 * k + u];
+                const float gq[4] = {bf16_lo(gg.x), bf16_hi(gg.x), bf16_lo(gg.y), bf16_hi(gg.y)};
+                const float cr[4] = {csr.x, csr.y, csr.z, csr.w};
+                const float dr[4] = {dtr.x, dtr.y, dtr.z, dtr.w};
+                float uq[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int rq = 4 * g4 + q;  // row within the tile; the column is l16
+                    if (isrs) {  // W^T[i][j] = dt_i exp(cs_j - cs_i) M^T[i][j], i <= j
+                        const bool keep = mode == 0 || rq <= l16;
+                        const float e = keep ? exp2_fast((csj - cr[q]) * kLog2e) : 0.f;
+                        const float w = dr[q] * e * m[q];
+                        wacc[2 * k + u][q] += w;
+                        rs = fmaf(w, gq[q], rs);
+                        uq[q] = 0.f;
+                    } else {  // V[t][j] = exp(cs_t - cs_j) M[t][j], t >= j; W = dt_j V
+                        const bool keep = mode == 0 || rq >= l16;
+                        const float e = keep ? exp2_fast((cr[q] - csj) * kLog2e) : 0.f;
+                        const float v = e * m[q];
+                        wacc[2 * k + u][q] = fmaf(dtj, v, wacc[2 * k + u][q]);
+                        ccol = fmaf(v, gq[q], ccol);
+                        uq[q] = e * gq[q];
+                    }
+                }
+                ub[2 * u] = pack_bf16(uq[0], uq[1]);
+                ub[2 * u + 1] = pack_bf16(uq[2], uq[3]);
+            }
+            if (!isrs) {  // dx^T[p][j] += sum_t dy[t][p] U[t][j]
+                const bf16x8 bu = __builtin_bit_cast(bf16x8, make_uint4(ub[0], ub[1], ub[2], ub[3]));
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt)
+                    dxa[pt] = mfma16(frag_tr(sXY, rho, 16 * pt, l16, g4, PPR), bu, dxa[pt]);
+            }
+        }
+
+        // ---- off-diagonal terms through the carried states
+        f32x4 bfm[PT], cem[PT];  // (F B_j)[p], (E C_j)[p] as [p][j] tiles
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            bfm[pt] = cem[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                bfm[pt] = mfma16(frag_nat(sF, 16 * pt + l16, kb, g4, NPR), bj[kb], bfm[pt]);
+                cem[pt] = mfma16(frag_nat(sE, 16 * pt + l16, kb, g4, NPR), cj[kb], cem[pt]);
+            }
+        }
+        float ob = 0.f, oc = 0.f;
+        uint2 dyq[PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            const uint2 xq = *reinterpret_cast<const uint2*>(sXY + swz_off(jl, 16 * pt + 4 * g4, PPR));
+            dyq[pt] = *reinterpret_cast<const uint2*>(sXY + swz_off(jl + 64, 16 * pt + 4 * g4, PPR));
+            ob = fmaf(bf16_lo(xq.x), bfm[pt][0], ob);
+            ob = fmaf(bf16_hi(xq.x), bfm[pt][1], ob);
+            ob = fmaf(bf16_lo(xq.y), bfm[pt][2], ob);
+            ob = fmaf(bf16_hi(xq.y), bfm[pt][3], ob);
+            oc = fmaf(bf16_lo(dyq[pt].x), cem[pt][0], oc);
+            oc = fmaf(bf16_hi(dyq[pt].x), cem[pt][1], oc);
+            oc = fmaf(bf16_lo(dyq[pt].y), cem[pt][2], oc);
+            oc = fmaf(bf16_hi(dyq[pt].y), cem[pt][3], oc);
+        }
+        {
+            bf16x8 xs8[PKB], ys8[PKB];
+#pragma unroll
+            for (int kb = 0; kb < PKB; ++kb) {
+                xs8[kb] = scale8(xj[kb], dtj * fj);
+                ys8[kb] = scale8(yj[kb], ej);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int kb = 0; kb < PKB; ++kb) {
+                    dbacc[nt] = mfma16(frag_tr(sF, 32 * kb, 16 * nt, l16, g4, NPR), xs8[kb], dbacc[nt]);
+                    dcacc[nt] = mfma16(frag_tr(sE, 32 * kb, 16 * nt, l16, g4, NPR), ys8[kb], dcacc[nt]);
+                }
+        }
+
+        // ---- per-row results of this head
+        rs = colsum(rs);
+        ccol = colsum(ccol);
+        ob = colsum(ob) * fj;
+        oc = colsum(oc) * ej;
+        if (g4 == 0 && vj) {
+            const size_t cb = ((size_t)(b * H + h) * nC + c) * Q;
+            direct[cb + jl] = ccol + ob;
+            dcs[cb + jl] = rs + oc - dtj * (ccol + ob);
+        }
+        if (vj) {
+            const float dh = D[h];
+            __bf16* dxr = dx + ((size_t)(b * T + t0 + jl) * H + h) * P + 4 * g4;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                const float y0 = bf16_lo(dyq[pt].x), y1 = bf16_hi(dyq[pt].x);
+                const float y2 = bf16_lo(dyq[pt].y), y3 = bf16_hi(dyq[pt].y);
+                const float v0 = fmaf(dh, y0, dtj * fmaf(fj, bfm[pt][0], dxa[pt][0]));
+                const float v1 = fmaf(dh, y1, dtj * fmaf(fj, bfm[pt][1], dxa[pt][1]));
+                const float v2 = fmaf(dh, y2, dtj * fmaf(fj, bfm[pt][2], dxa[pt][2]));
+                const float v3 = fmaf(dh, y3, dtj * fmaf(fj, bfm[pt][3], dxa[pt][3]));
+                *reinterpret_cast<uint2*>(dxr + 16 * pt) = make_uint2(pack_bf16(v0, v1), pack_bf16(v2, v3));
+            }
+        }
+        // this block's shares of the chunk-end term (dt_j ob_j, and exp(cs_last) <E, F> on
+        // the first block) and of dD (x_j . dy_j)
+        float lt = (g4 == 0 && vj) ? dtj * ob : 0.f;
+        if (j0 == 0) {
+            float ef = 0.f;
+            for (int m = tid; m < P * NPR; m += 256)
+                ef += dot8(*reinterpret_cast<const bf16x8*>(sE + 16 * m),
+                           *reinterpret_cast<const bf16x8*>(sF + 16 * m));
+            lt = fmaf(exp2_fast(cs_last * kLog2e), ef, lt);
+        }
+        float dd = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < PKB; ++kb) dd += dot8(xj[kb], yj[kb]);
+        lt = wavesum(lt);
+        dd = wavesum(dd);
+        if (lane == 0) {
+            shares[buf * 8 + 2 * wave] = lt;
+            shares[buf * 8 + 2 * wave + 1] = dd;
+        }
+    }
+    dma_barrier();
+    if (tid == 0) {
+        const float* sh = shares + ((hpg - 1) & 1) * 8;
+        const size_t pi = ((size_t)(b * H + g * hpg + hpg - 1) * nC + c) * NJ + rj;
+        lt_part[pi] = (sh[0] + sh[2]) + (sh[4] + sh[6]);
+        dd_part[pi] = (sh[1] + sh[3]) + (sh[5] + sh[7]);
+    }
+
+    // ---------------------------------------------------------------- W products
+    {
+        const unsigned rowb = (unsigned)(G * N * 2);
+        const size_t bo = ((size_t)(b * T + t0) * G + g) * N;
+        // B rows [0, j0 + 64) at LDS rows 0.., C rows [j0, Q) at LDS rows j0 + 64..
+        issue_rows<NPR>(raw_rsrc(Bm + bo, (unsigned)Lc * rowb), rowb, 0, lds0, 0, j0 + 64, wave,
+                        lane);
+        issue_rows<NPR>(raw_rsrc(Cm + bo, (unsigned)Lc * rowb), rowb, j0, lds0, j0 + 64, Q - j0,
+                        wave, lane);
+    }
+    dma_barrier();
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int jl = j0 + 16 * wave + l16;
+    const bool vj = jl < Lc;
+#pragma unroll
+    for (int k = 0; k < PAIRS; ++k) {
+        const bool isrs = k < rsp;
+        const int rho = isrs ? 32 * k : tbase + 32 * (k - rsp) + 64;
+        const bf16x8 w8 = __builtin_bit_cast(
+            bf16x8, make_uint4(pack_bf16(wacc[2 * k][0], wacc[2 * k][1]),
+                               pack_bf16(wacc[2 * k][2], wacc[2 * k][3]),
+                               pack_bf16(wacc[2 * k + 1][0], wacc[2 * k + 1][1]),
+                               pack_bf16(wacc[2 * k + 1][2], wacc[2 * k + 1][3])));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const bf16x8 a = frag_tr(smem, rho, 16 * nt, l16, g4, NPR);
+            if (isrs)
+                dcacc[nt] = mfma16(a, w8, dcacc[nt]);  // dC^T[n][j] += B[i][n] W^T[i][j]
+            else
+                dbacc[nt] = mfma16(a, w8, dbacc[nt]);  // dB^T[n][j] += C[t][n] W[t][j]
+        }
+    }
+    if (vj) {
+        const size_t ro = ((size_t)(b * T + t0 + jl) * G + g) * N + 4 * g4;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            *reinterpret_cast<uint2*>(dB + ro + 16 * nt) =
+                make_uint2(pack_bf16(dbacc[nt][0], dbacc[nt][1]), pack_bf16(dbacc[nt][2], dbacc[nt][3]));
+            *reinterpret_cast<uint2*>(dC + ro + 16 * nt) =
+                make_uint2(pack_bf16(dcacc[nt][0], dcacc[nt][1]), pack_bf16(dcacc[nt][2], dcacc[nt][3]));
+        }
+    }
+}
+
+template <int Q, int N, int P>
+hipError_t launch_bwd_mfma_t(const Shape& s, const BwdArgs& a, hipStream_t st) {
+    using C_ = BwdCfg<Q, N, P>;
+    const auto kern = chunk_bwd_mfma_kernel<Q, N, P>;
+    static bool attr_set[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!attr_set[dev]) {
+        e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)C_::LDS);
+        if (e != hipSuccess) return e;
+        attr_set[dev] = true;
+    }
+    const unsigned blocks = (unsigned)((size_t)s.B * s.G * s.nC * C_::NJ);
+    kern<<<blocks, C_::NTH, C_::LDS, st>>>(
+        (const __bf16*)a.x, (const __bf16*)a.Bm, (const __bf16*)a.Cm, a.dtc, a.cs, a.D,
+        (const __bf16*)a.entry, (const __bf16*)a.exitg, (const __bf16*)a.dy, (__bf16*)a.dx,
+        (__bf16*)a.dB, (__bf16*)a.dC, a.dcs, a.direct, a.lt_part, a.dd_part, s.T, s.H, s.G, s.nC);
+    return hipGetLastError();
+}
+
+using BwdFn = hipError_t (*)(const Shape&, const BwdArgs&, hipStream_t);
+
+template <int Q>
+BwdFn pick_bwd_q(const Shape& s) {
+    if (s.P != 64) return nullptr;
+    switch (s.N) {
+        case 64: return launch_bwd_mfma_t<Q, 64, 64>;
+        case 128: return launch_bwd_mfma_t<Q, 128, 64>;
+    }
+    return nullptr;
+}
+
+BwdFn pick_bwd(const Shape& s) {
+    // buffer resources address one chunk of x / dy and of B / C with 32-bit byte offsets
+    if ((size_t)s.Q * s.H * s.P * 2 >= ((size_t)1 << 31) ||
+        (size_t)s.Q * s.G * s.N * 2 >= ((size_t)1 << 31))
+        return nullptr;
+    switch (s.Q) {
+        case 64: return pick_bwd_q<64>(s);
+        case 128: return pick_bwd_q<128>(s);
+        case 256: return pick_bwd_q<256>(s);
+    }
+    return nullptr;
+}
+
+}  // namespace
+
+bool chunk_bwd_mfma_supported(const Shape& s) { return pick_bwd(s) != nullptr; }
+int chunk_bwd_mfma_rows() { return 64; }
+
+hipError_t launch_chunk_bwd_mfma(const Shape& s, const BwdArgs& a, hipStream_t st) {
+    BwdFn f = pick_bwd(s);
+    if (!f) return hipErrorInvalidValue;
+    if ((size_t)s.B * s.nC == 0) return hipSuccess;
+    return f(s, a, st);
+}
+
+}  // namespace ssd

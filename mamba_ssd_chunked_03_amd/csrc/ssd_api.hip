@@ -337,9 +337,11 @@ ssd_status ssd_bwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const f
     a.ddt = ddt; a.dA = dA; a.dD = dD;
     a.dcs = ws.dcs; a.direct = ws.direct;
     a.lt_part = ws.lt_part; a.dd_part = ws.dd_part; a.dA_part = ws.dA_part;
-    const int rows = ssd::chunk_bwd_valu_rows();
+    const bool mfma_bwd = dtype == SSD_BF16 && ssd::chunk_bwd_mfma_supported(s);
+    const int rows = mfma_bwd ? ssd::chunk_bwd_mfma_rows() : ssd::chunk_bwd_valu_rows();
     if (has_tokens) {
-        r = hip_status(ssd::launch_chunk_bwd_valu(s, dtype, a, st));
+        r = hip_status(mfma_bwd ? ssd::launch_chunk_bwd_mfma(s, a, st)
+                                : ssd::launch_chunk_bwd_valu(s, dtype, a, st));
         if (r != SSD_OK) return r;
     }
     // dA and dD are written even with no tokens (zeros)

@@ -92,6 +92,10 @@ struct BwdArgs {
 int chunk_bwd_valu_rows();
 hipError_t launch_chunk_bwd_valu(const Shape& s, ssd_dtype dtype, const BwdArgs& a,
                                  hipStream_t st);
+// bf16 MFMA in-chunk backward (headdim 64, dstate 64 or 128), same outputs; rows per tile 64
+bool chunk_bwd_mfma_supported(const Shape& s);
+int chunk_bwd_mfma_rows();
+hipError_t launch_chunk_bwd_mfma(const Shape& s, const BwdArgs& a, hipStream_t st);
 // ddt and dA, dD from the per-chunk and per-tile shares (rows: rows per tile)
 hipError_t launch_bwd_finalize(const Shape& s, const BwdArgs& a, int rows, hipStream_t st);
 

@@ -74,3 +74,37 @@ def decode_cost(batch, nheads, headdim, dstate, ngroups, dtype="bf16"):
     B, H, P, N, G = batch, nheads, headdim, dstate, ngroups
     nbytes = 2 * B * H * N * P * 4 + 2 * B * H * P * e + 2 * B * G * N * e + B * H * 4 + 2 * H * 4
     return KernelCost("decode_step", nbytes, 4.0 * B * H * N * P)
+
+
+def bwd_costs(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len, dtype="bf16",
+              init_state=False, final_grad=True):
+    """The kernels of the backward pass (ssd_bwd), in launch order: the forward stages it
+    recomputes (cumsum, chunk states, entry states), the entry-state gradients of every
+    chunk through its own outputs (bwd_dstate), their reverse carry (bwd_passing), the
+    in-chunk gradients (bwd_chunk) and the ddt / dA / dD reductions (bwd_finalize).
+
+    Counts follow the forward's conventions.  In-chunk FLOPs per (b, h): the causal
+    dy x^T and the transposed masked product for dx (each Q(Q+1)/2 x P MACs per chunk),
+    and three Q x N x P contractions (B F, F x, E dy); per (b, g): C B^T and the two
+    head-summed products W^T C and W B for dB and dC (each causal, over N)."""
+    B, T, H, P, N, G, Q = batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len
+    e = 2 if dtype == "bf16" else 4
+    nC = (T + Q - 1) // Q
+    chunk_f32 = B * H * nC * Q * 4
+    state_e = B * H * nC * P * N * e
+    io_xy = B * T * H * P * e
+    io_bc = B * T * G * N * e
+    st1 = B * H * N * P * 4
+    full, rem = divmod(T, Q)
+    tri = full * Q * (Q + 1) + rem * (rem + 1)
+    fwd = kernel_costs(B, T, H, P, N, G, Q, dtype, init_state=init_state, final_state=False)
+    cumsum, state, passing = fwd[0], fwd[1], fwd[2]
+    dstate = KernelCost("bwd_dstate", io_xy + io_bc + chunk_f32 + state_e, 2.0 * B * H * T * N * P)
+    rpass = KernelCost("bwd_passing",
+                       2 * state_e + B * H * nC * 4 + (st1 if final_grad else 0) + st1,
+                       2.0 * B * H * nC * N * P)
+    chunk = KernelCost("bwd_chunk",
+                       3 * io_xy + 4 * io_bc + 4 * chunk_f32 + 2 * state_e + H * 4,
+                       B * H * (2.0 * tri * P + 6.0 * T * N * P) + 3.0 * B * G * tri * N)
+    fin = KernelCost("bwd_finalize", 3 * chunk_f32 + B * T * H * 4 + 2 * H * 4, 4.0 * B * T * H)
+    return [cumsum, state, passing, dstate, rpass, chunk, fin]
