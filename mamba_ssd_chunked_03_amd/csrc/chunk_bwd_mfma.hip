@@ -4,8 +4,14 @@
 // It computes what chunk_bwd_valu.hip computes (the formulas are stated there): dx, the
 // head-summed dB and dC, and per head the explicit step-size gradient and dL/dcs.
 //
-// One workgroup of four waves per (batch, group, chunk, block J of 64 rows), looping over
-// the heads of the group.  Wave w owns the 16 columns j = j0 + 16 w + (0..15) of J.  With
+// One workgroup of eight waves per (batch, group, chunk, block J of 64 rows), looping over
+// the heads of the group.  Waves w and w + 4 own the 16 columns j = j0 + 16 w + (0..15) of
+// J and share a SIMD: wave w (a "strip" wave) does the products inside the chunk, wave w + 4
+// (a "state" wave) those through the carried states, and they meet in LDS once per head
+// (the state wave's (F B_j) tiles and per-row sums go to the strip wave, which finishes dx)
+// and once per workgroup (the strip wave's W goes to the state wave, which holds dB, dC).
+// The two roles run in separate branches with the same barriers, so neither role's
+// registers are held while the other's code runs.  With
 // M = dy x^T, W[t][i] = dt_i exp(cs_t - cs_i) M[t][i] (t >= i) is the matrix whose
 // head sum gives both diagonal-block products, dC_j += sum_i W[j][i] B_i and
 // dB_j += sum_t W[t][j] C_t.  For its columns a wave needs
@@ -38,24 +44,6 @@ namespace ssd {
 namespace {
 
 using namespace mfma;
-
-template <int Q, int N, int P>
-struct BwdCfg {
-    static constexpr int NTH = 256;
-    static constexpr int NJ = Q / 64;               // row blocks per chunk
-    static constexpr int PAIRS = (Q / 16 + 2) / 2;  // 32-row blocks of strip per wave
-    static constexpr int PPR = P / 8, NPR = N / 8;  // 16-byte pieces per row
-    static constexpr int NKB = N / 32, PKB = P / 32;
-    static constexpr int NT = N / 16, PT = P / 16;
-    static constexpr unsigned XYB = (Q + 64) * P * 2;  // x rows [0, j0+64), dy rows [j0, Q)
-    static constexpr unsigned EB = P * N * 2;          // E or F, [p][n]
-    static constexpr unsigned FB = Q * 4;              // cs or dt
-    static constexpr unsigned ITEM = XYB + 2 * EB + 2 * FB;
-    static constexpr unsigned BCB = Q * N * 2;         // one B or C chunk
-    static constexpr unsigned LDS = 2 * ITEM + 64;     // + the per-head workgroup shares
-    static_assert(P == 64 && (N == 64 || N == 128), "shape");
-    static_assert(2 * BCB <= 2 * ITEM && (Q + 64) * N * 2 <= 2 * ITEM, "B/C staging fits");
-};
 
 // 8 bf16 at the relabelled k-slots {32kb + 4g .. +3, 32kb + 16 + 4g .. +3} of LDS row `row`
 __device__ __forceinline__ bf16x8 frag_rl(const unsigned char* base, int row, int kb, int g4,
@@ -112,12 +100,12 @@ __device__ __forceinline__ float wavesum(float v) {
 // instruction fills 64 consecutive 16-byte LDS slots (lane L at its base + 16 L), so the
 // swizzle is applied on the source side: slot `sl` of LDS row dr receives piece
 // sl ^ (dr % PPRX).  nrows * PPRX is a multiple of 64.
-template <int PPRX>
+template <int PPRX, int NW>
 __device__ __forceinline__ void issue_rows(u32x4 rsrc, unsigned rowb, int src_row0, uint32_t lds,
                                            int dst_row0, int nrows, int wave, int lane) {
     const int ninst = nrows * PPRX / 64;
     const uint32_t base = lds + (unsigned)dst_row0 * PPRX * 16u;
-    for (int k = wave; k < ninst; k += 4) {
+    for (int k = wave; k < ninst; k += NW) {
         const int m = k * 64 + lane;
         const int r = m / PPRX, sl = m % PPRX;
         const int dr = dst_row0 + r;
@@ -127,22 +115,51 @@ __device__ __forceinline__ void issue_rows(u32x4 rsrc, unsigned rowb, int src_ro
 }
 
 template <int Q, int N, int P>
+struct BwdCfg {
+    static constexpr int NW = 8, NTH = 512;         // 4 strip waves + 4 state waves
+    static constexpr int NJ = Q / 64;               // row blocks per chunk
+    static constexpr int PAIRS = (Q / 16 + 2) / 2;  // 32-row blocks of strip per wave
+    static constexpr int PPR = P / 8, NPR = N / 8;  // 16-byte pieces per row
+    static constexpr int NKB = N / 32, PKB = P / 32;
+    static constexpr int NT = N / 16, PT = P / 16;
+    static constexpr unsigned XYB = (Q + 64) * P * 2;  // x rows [0, j0+64), dy rows [j0, Q)
+    static constexpr unsigned EB = P * N * 2;          // E or F, [p][n]
+    static constexpr unsigned FB = Q * 4;              // cs or dt
+    static constexpr unsigned ITEM = XYB + 2 * EB + 2 * FB;
+    static constexpr unsigned BCB = Q * N * 2;         // one B or C chunk
+    // exchange from the state waves to the strip waves, after the two item buffers
+    static constexpr unsigned X_BF = 2 * ITEM;                // (F B_j) tiles, bf16 [4][PT][64]
+    static constexpr unsigned X_OB = X_BF + 4 * PT * 64 * 8;  // ob, oc per column [2][64]
+    static constexpr unsigned X_EF = X_OB + 2 * 64 * 4;       // <E, F> share per wave [4]
+    static constexpr unsigned X_SH = X_EF + 16;               // workgroup shares [2][4][2]
+    static constexpr unsigned LDS = X_SH + 64;
+    // the W accumulators (bf16) travel from the strip waves after the B/C rows at the end
+    static constexpr unsigned X_W = (Q + 64) * N * 2;
+    static_assert(P == 64 && (N == 64 || N == 128), "shape");
+    static_assert(2 * BCB <= 2 * ITEM, "B and C chunks fit the item buffers");
+    static_assert(X_W + 4u * PAIRS * 64 * 16 <= 2 * ITEM, "end-of-loop staging fits");
+    static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+template <int Q, int N, int P>
 __device__ __forceinline__ void issue_item(const __bf16* x, const __bf16* dy, const __bf16* entry,
                                            const __bf16* exitg, const float* cs, const float* dtc,
                                            int b, int h, int c, int j0, int Lc, int T, int H,
                                            int nC, uint32_t lds, int wave, int lane) {
     using C_ = BwdCfg<Q, N, P>;
+    constexpr int NW = C_::NW;
     const unsigned rowb = (unsigned)(H * P * 2);
     const size_t xo = ((size_t)(b * T + c * Q) * H + h) * P;
     const u32x4 xr = raw_rsrc(x + xo, (unsigned)Lc * rowb);
     const u32x4 yr = raw_rsrc(dy + xo, (unsigned)Lc * rowb);
     // x rows [0, j0 + 64) at LDS rows 0.., dy rows [j0, Q) at LDS rows j0 + 64..
-    issue_rows<C_::PPR>(xr, rowb, 0, lds, 0, j0 + 64, wave, lane);
-    issue_rows<C_::PPR>(yr, rowb, j0, lds, j0 + 64, Q - j0, wave, lane);
+    issue_rows<C_::PPR, NW>(xr, rowb, 0, lds, 0, j0 + 64, wave, lane);
+    issue_rows<C_::PPR, NW>(yr, rowb, j0, lds, j0 + 64, Q - j0, wave, lane);
     const size_t so = ((size_t)(b * H + h) * nC + c) * P * N;
-    issue_rows<C_::NPR>(raw_rsrc(entry + so, C_::EB), N * 2, 0, lds + C_::XYB, 0, P, wave, lane);
-    issue_rows<C_::NPR>(raw_rsrc(exitg + so, C_::EB), N * 2, 0, lds + C_::XYB + C_::EB, 0, P,
-                        wave, lane);
+    issue_rows<C_::NPR, NW>(raw_rsrc(entry + so, C_::EB), N * 2, 0, lds + C_::XYB, 0, P, wave,
+                            lane);
+    issue_rows<C_::NPR, NW>(raw_rsrc(exitg + so, C_::EB), N * 2, 0, lds + C_::XYB + C_::EB, 0, P,
+                            wave, lane);
     const size_t cb = ((size_t)(b * H + h) * nC + c) * Q;
     if (wave == 0 && lane < Q / 4)
         dma16(raw_rsrc(cs + cb, C_::FB), lds + C_::XYB + 2 * C_::EB, lane * 16u);
@@ -151,115 +168,113 @@ __device__ __forceinline__ void issue_item(const __bf16* x, const __bf16* dy, co
 }
 
 template <int Q, int N, int P>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void chunk_bwd_mfma_kernel(
-    const __bf16* __restrict__ x, const __bf16* __restrict__ Bm, const __bf16* __restrict__ Cm,
-    const float* __restrict__ dtc, const float* __restrict__ cs, const float* __restrict__ D,
-    const __bf16* __restrict__ entry, const __bf16* __restrict__ exitg,
-    const __bf16* __restrict__ dy, __bf16* __restrict__ dx, __bf16* __restrict__ dB,
-    __bf16* __restrict__ dC, float* __restrict__ dcs, float* __restrict__ direct,
-    float* __restrict__ lt_part, float* __restrict__ dd_part, int T, int H, int G, int nC) {
+__device__ __forceinline__ void issue_bc(const __bf16* Bm, const __bf16* Cm, int b, int g, int t0,
+                                         int Lc, int T, int G, int j0, bool rows_only,
+                                         uint32_t lds, int wave, int lane) {
+    using C_ = BwdCfg<Q, N, P>;
+    const unsigned rowb = (unsigned)(G * N * 2);
+    const size_t bo = ((size_t)(b * T + t0) * G + g) * N;
+    const u32x4 br = raw_rsrc(Bm + bo, (unsigned)Lc * rowb);
+    const u32x4 cr = raw_rsrc(Cm + bo, (unsigned)Lc * rowb);
+    if (!rows_only) {  // whole chunks: B at 0, C at BCB
+        issue_rows<C_::NPR, C_::NW>(br, rowb, 0, lds, 0, Q, wave, lane);
+        issue_rows<C_::NPR, C_::NW>(cr, rowb, 0, lds + C_::BCB, 0, Q, wave, lane);
+    } else {  // B rows [0, j0 + 64) at rows 0.., C rows [j0, Q) at rows j0 + 64..
+        issue_rows<C_::NPR, C_::NW>(br, rowb, 0, lds, 0, j0 + 64, wave, lane);
+        issue_rows<C_::NPR, C_::NW>(cr, rowb, j0, lds, j0 + 64, Q - j0, wave, lane);
+    }
+}
+
+// Everything both roles need to know about their workgroup
+struct BwdCtx {
+    int b, g, c, rj, j0, t0, Lc, hpg, T, H, G, nC;
+    int wave, cw, lane;   // wave 0..7, column tile 0..3 of the block, lane
+    int jtile, rsp, tbase;
+    uint32_t lds0;
+};
+
+// ------------------------------------------------------------------ strip waves
+// M strips, W accumulated over heads, C B^T on the strips, rs / ccol, the diagonal part
+// of dx; they finish dx and the per-row results of every head.
+template <int Q, int N, int P>
+__device__ __forceinline__ void bwd_strip_role(
+    const BwdCtx& k_, unsigned char* smem, const __bf16* x, const __bf16* Bm, const __bf16* Cm,
+    const float* dtc, const float* cs, const float* D, const __bf16* entry, const __bf16* exitg,
+    const __bf16* dy, __bf16* dx, float* dcs, float* direct, float* lt_part, float* dd_part) {
     using C_ = BwdCfg<Q, N, P>;
     constexpr int NJ = C_::NJ, PAIRS = C_::PAIRS, PPR = C_::PPR, NPR = C_::NPR;
-    constexpr int NKB = C_::NKB, PKB = C_::PKB, NT = C_::NT, PT = C_::PT;
-    extern __shared__ __align__(16) unsigned char smem[];
-    const uint32_t lds0 = lds_addr(smem);
-    float* const shares = reinterpret_cast<float*>(smem + 2 * C_::ITEM);  // [2][4][2]
+    constexpr int NKB = C_::NKB, PKB = C_::PKB, PT = C_::PT;
+    const int b = k_.b, g = k_.g, c = k_.c, j0 = k_.j0, t0 = k_.t0, Lc = k_.Lc;
+    const int hpg = k_.hpg, T = k_.T, H = k_.H, G = k_.G, nC = k_.nC;
+    const int wave = k_.wave, cw = k_.cw, lane = k_.lane;
+    const int jtile = k_.jtile, rsp = k_.rsp, tbase = k_.tbase;
+    float* const shares = reinterpret_cast<float*>(smem + C_::X_SH);
 
-    // neighbouring row blocks and chunks on the same XCD (its L2 holds their shared data)
-    const int nwg = gridDim.x, blk = blockIdx.x;
-    const int wp = (nwg % 8 == 0) ? (blk & 7) * (nwg >> 3) + (blk >> 3) : blk;
-    const int unit = wp / NJ, rj = wp % NJ;
-    const int c = unit % nC, g = (unit / nC) % G, b = unit / (nC * G);
-    const int j0 = rj * 64, t0 = c * Q;
-    const int Lc = min(Q, T - t0);
-    if (j0 >= Lc) return;  // no valid row
-    const int hpg = H / G;
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
-    const int jtile = j0 / 16 + wave;                // the wave's column tile (16 rows j)
-    const int rsp = (j0 / 16 + (wave | 1) + 1) / 2;  // row-strip blocks: rows i < 32 rsp
-    const int tbase = j0 + 16 * (wave & ~1);        // column strip: rows t >= tbase
-
-    // ---------------------------------------------------------------- B and C chunks
-    {
-        const unsigned rowb = (unsigned)(G * N * 2);
-        const size_t bo = ((size_t)(b * T + t0) * G + g) * N;
-        issue_rows<NPR>(raw_rsrc(Bm + bo, (unsigned)Lc * rowb), rowb, 0, lds0, 0, Q, wave, lane);
-        issue_rows<NPR>(raw_rsrc(Cm + bo, (unsigned)Lc * rowb), rowb, 0, lds0 + C_::BCB, 0, Q,
-                        wave, lane);
-    }
+    issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, false, k_.lds0, wave, lane);
     dma_barrier();
-    const unsigned char* sBc = smem;
-    const unsigned char* sCc = smem + C_::BCB;
-    bf16x8 bj[NKB], cj[NKB];  // B_j, C_j over n (natural slots)
-    uint2 gt[2 * PAIRS];      // C B^T on the strips (bf16), accumulator layout
-    {
-    const int l16 = lane & 15, g4 = lane >> 4;
-    const int jl = j0 + 16 * wave + l16;  // the lane's column j (chunk row)
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-        bj[kb] = frag_nat(sBc, jl, kb, g4, NPR);
-        cj[kb] = frag_nat(sCc, jl, kb, g4, NPR);
-    }
     // C B^T on the strips, rounded to bf16: G^T[i][j] = B_i . C_j and G[t][j] = C_t . B_j
+    uint2 gt[2 * PAIRS];
+    {
+        const int l16 = lane & 15, g4 = lane >> 4;
+        const int jl = j0 + 16 * cw + l16;
+        const unsigned char* sBc = smem;
+        const unsigned char* sCc = smem + C_::BCB;
+        bf16x8 bj[NKB], cj[NKB];
 #pragma unroll
-    for (int k = 0; k < PAIRS; ++k) {
-        const bool isrs = k < rsp;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int row = (isrs ? 32 * k : tbase + 32 * (k - rsp)) + 16 * u + l16;
-            const unsigned char* src = isrs ? sBc : sCc;
-            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-                acc = mfma16(frag_nat(src, row, kb, g4, NPR), isrs ? cj[kb] : bj[kb], acc);
-            gt[2 * k + u] = make_uint2(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]));
+        for (int kb = 0; kb < NKB; ++kb) {
+            bj[kb] = frag_nat(sBc, jl, kb, g4, NPR);
+            cj[kb] = frag_nat(sCc, jl, kb, g4, NPR);
         }
-    }
+#pragma unroll
+        for (int k = 0; k < PAIRS; ++k) {
+            const bool isrs = k < rsp;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int row = (isrs ? 32 * k : tbase + 32 * (k - rsp)) + 16 * u + l16;
+                const unsigned char* src = isrs ? sBc : sCc;
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+                    acc = mfma16(frag_nat(src, row, kb, g4, NPR), isrs ? cj[kb] : bj[kb], acc);
+                gt[2 * k + u] = make_uint2(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]));
+            }
+        }
     }
     lds_barrier();  // B and C are no longer read: the item buffers are free
 
     f32x4 wacc[2 * PAIRS];  // W over the strips, summed over the heads
 #pragma unroll
     for (int s = 0; s < 2 * PAIRS; ++s) wacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 dbacc[NT], dcacc[NT];  // dB^T, dC^T [n][j]
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) dbacc[nt] = dcacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    issue_item<Q, N, P>(x, dy, entry, exitg, cs, dtc, b, g * hpg, c, j0, Lc, T, H, nC, lds0, wave,
-                        lane);
+    issue_item<Q, N, P>(x, dy, entry, exitg, cs, dtc, b, g * hpg, c, j0, Lc, T, H, nC, k_.lds0,
+                        wave, lane);
 #pragma unroll 1
     for (int hh = 0; hh < hpg; ++hh) {
         const int h = g * hpg + hh;
         const int buf = hh & 1;
         dma_barrier();  // this head's copies have landed; the other buffer is free
-        if (hh > 0 && tid == 0) {
+        if (hh > 0 && wave == 0 && lane == 0) {
             const float* sh = shares + (buf ^ 1) * 8;
-            const size_t pi = ((size_t)(b * H + h - 1) * nC + c) * NJ + rj;
+            const size_t pi = ((size_t)(b * H + h - 1) * nC + c) * NJ + k_.rj;
             lt_part[pi] = (sh[0] + sh[2]) + (sh[4] + sh[6]);
             dd_part[pi] = (sh[1] + sh[3]) + (sh[5] + sh[7]);
         }
         if (hh + 1 < hpg)
             issue_item<Q, N, P>(x, dy, entry, exitg, cs, dtc, b, h + 1, c, j0, Lc, T, H, nC,
-                                lds0 + (buf ^ 1) * C_::ITEM, wave, lane);
-        // lane-dependent values are re-derived every head from an opaque copy of the lane
-        // index, so the compiler recomputes the LDS addresses instead of keeping them all
-        // live across the loop
+                                k_.lds0 + (buf ^ 1) * C_::ITEM, wave, lane);
+        // lane-dependent values re-derived every head from an opaque copy of the lane
+        // index: the compiler recomputes the LDS addresses instead of keeping them live
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int l16 = ln & 15, g4 = ln >> 4;
-        const int jl = j0 + 16 * wave + l16;
+        const int jl = j0 + 16 * cw + l16;
         const bool vj = jl < Lc;
         const unsigned char* sXY = smem + buf * C_::ITEM;
-        const unsigned char* sE = sXY + C_::XYB;
-        const unsigned char* sF = sE + C_::EB;
-        const float* s_cs = reinterpret_cast<const float*>(sF + C_::EB);
+        const float* s_cs = reinterpret_cast<const float*>(sXY + C_::XYB + 2 * C_::EB);
         const float* s_dt = s_cs + Q;
         const float cs_last = s_cs[Q - 1];
         const float csj = s_cs[jl], dtj = s_dt[jl];
-        const float ej = exp2_fast(csj * kLog2e), fj = exp2_fast((cs_last - csj) * kLog2e);
+        const float fj = exp2_fast((cs_last - csj) * kLog2e);
 
         bf16x8 xj[PKB], yj[PKB];  // x_j, dy_j over p (relabelled slots)
 #pragma unroll
@@ -267,8 +282,6 @@ void chunk_bwd_mfma_kernel(
             xj[kb] = frag_rl(sXY, jl, kb, g4, PPR);
             yj[kb] = frag_rl(sXY, jl + 64, kb, g4, PPR);
         }
-
-        // ---- the strips: M, W, and the diagonal-block part of dx
         float rs = 0.f, ccol = 0.f;
         f32x4 dxa[PT];
 #pragma unroll
@@ -281,8 +294,8 @@ void chunk_bwd_mfma_kernel(
             uint32_t ub[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                // the tile's place against the wave's column tile: every element kept, the
-                // diagonal tile (kept on one side of it), or none (a padding tile)
+                // the tile against the wave's column tile: every element kept, the diagonal
+                // tile (kept on one side), or none (a padding tile)
                 const int ti = rbase / 16 + u;
                 const int mode = isrs ? (ti < jtile ? 0 : ti == jtile ? 1 : 2)
                                       : (ti > jtile ? 0 : ti == jtile ? 1 : 2);
@@ -329,54 +342,13 @@ void chunk_bwd_mfma_kernel(
                     dxa[pt] = mfma16(frag_tr(sXY, rho, 16 * pt, l16, g4, PPR), bu, dxa[pt]);
             }
         }
-
-        // ---- off-diagonal terms through the carried states
-        f32x4 bfm[PT], cem[PT];  // (F B_j)[p], (E C_j)[p] as [p][j] tiles
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            bfm[pt] = cem[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                bfm[pt] = mfma16(frag_nat(sF, 16 * pt + l16, kb, g4, NPR), bj[kb], bfm[pt]);
-                cem[pt] = mfma16(frag_nat(sE, 16 * pt + l16, kb, g4, NPR), cj[kb], cem[pt]);
-            }
-        }
-        float ob = 0.f, oc = 0.f;
-        uint2 dyq[PT];
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            const uint2 xq = *reinterpret_cast<const uint2*>(sXY + swz_off(jl, 16 * pt + 4 * g4, PPR));
-            dyq[pt] = *reinterpret_cast<const uint2*>(sXY + swz_off(jl + 64, 16 * pt + 4 * g4, PPR));
-            ob = fmaf(bf16_lo(xq.x), bfm[pt][0], ob);
-            ob = fmaf(bf16_hi(xq.x), bfm[pt][1], ob);
-            ob = fmaf(bf16_lo(xq.y), bfm[pt][2], ob);
-            ob = fmaf(bf16_hi(xq.y), bfm[pt][3], ob);
-            oc = fmaf(bf16_lo(dyq[pt].x), cem[pt][0], oc);
-            oc = fmaf(bf16_hi(dyq[pt].x), cem[pt][1], oc);
-            oc = fmaf(bf16_lo(dyq[pt].y), cem[pt][2], oc);
-            oc = fmaf(bf16_hi(dyq[pt].y), cem[pt][3], oc);
-        }
-        {
-            bf16x8 xs8[PKB], ys8[PKB];
-#pragma unroll
-            for (int kb = 0; kb < PKB; ++kb) {
-                xs8[kb] = scale8(xj[kb], dtj * fj);
-                ys8[kb] = scale8(yj[kb], ej);
-            }
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int kb = 0; kb < PKB; ++kb) {
-                    dbacc[nt] = mfma16(frag_tr(sF, 32 * kb, 16 * nt, l16, g4, NPR), xs8[kb], dbacc[nt]);
-                    dcacc[nt] = mfma16(frag_tr(sE, 32 * kb, 16 * nt, l16, g4, NPR), ys8[kb], dcacc[nt]);
-                }
-        }
-
-        // ---- per-row results of this head
         rs = colsum(rs);
         ccol = colsum(ccol);
-        ob = colsum(ob) * fj;
-        oc = colsum(oc) * ej;
+
+        lds_barrier();  // the state waves' (F B_j) tiles, ob, oc and <E, F> shares are in LDS
+        const uint2* xbf = reinterpret_cast<const uint2*>(smem + C_::X_BF) + (cw * PT) * 64 + ln;
+        const float* xob = reinterpret_cast<const float*>(smem + C_::X_OB);
+        const float ob = xob[16 * cw + l16], oc = xob[64 + 16 * cw + l16];
         if (g4 == 0 && vj) {
             const size_t cb = ((size_t)(b * H + h) * nC + c) * Q;
             direct[cb + jl] = ccol + ob;
@@ -387,76 +359,189 @@ void chunk_bwd_mfma_kernel(
             __bf16* dxr = dx + ((size_t)(b * T + t0 + jl) * H + h) * P + 4 * g4;
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
-                const float y0 = bf16_lo(dyq[pt].x), y1 = bf16_hi(dyq[pt].x);
-                const float y2 = bf16_lo(dyq[pt].y), y3 = bf16_hi(dyq[pt].y);
-                const float v0 = fmaf(dh, y0, dtj * fmaf(fj, bfm[pt][0], dxa[pt][0]));
-                const float v1 = fmaf(dh, y1, dtj * fmaf(fj, bfm[pt][1], dxa[pt][1]));
-                const float v2 = fmaf(dh, y2, dtj * fmaf(fj, bfm[pt][2], dxa[pt][2]));
-                const float v3 = fmaf(dh, y3, dtj * fmaf(fj, bfm[pt][3], dxa[pt][3]));
+                const uint2 yq = *reinterpret_cast<const uint2*>(sXY + swz_off(jl + 64, 16 * pt + 4 * g4, PPR));
+                const uint2 bq = xbf[pt * 64];
+                const float v0 = fmaf(dh, bf16_lo(yq.x), dtj * fmaf(fj, bf16_lo(bq.x), dxa[pt][0]));
+                const float v1 = fmaf(dh, bf16_hi(yq.x), dtj * fmaf(fj, bf16_hi(bq.x), dxa[pt][1]));
+                const float v2 = fmaf(dh, bf16_lo(yq.y), dtj * fmaf(fj, bf16_lo(bq.y), dxa[pt][2]));
+                const float v3 = fmaf(dh, bf16_hi(yq.y), dtj * fmaf(fj, bf16_hi(bq.y), dxa[pt][3]));
                 *reinterpret_cast<uint2*>(dxr + 16 * pt) = make_uint2(pack_bf16(v0, v1), pack_bf16(v2, v3));
             }
         }
         // this block's shares of the chunk-end term (dt_j ob_j, and exp(cs_last) <E, F> on
         // the first block) and of dD (x_j . dy_j)
         float lt = (g4 == 0 && vj) ? dtj * ob : 0.f;
-        if (j0 == 0) {
-            float ef = 0.f;
-            for (int m = tid; m < P * NPR; m += 256)
-                ef += dot8(*reinterpret_cast<const bf16x8*>(sE + 16 * m),
-                           *reinterpret_cast<const bf16x8*>(sF + 16 * m));
-            lt = fmaf(exp2_fast(cs_last * kLog2e), ef, lt);
-        }
+        if (j0 == 0 && ln == 0)
+            lt = fmaf(exp2_fast(cs_last * kLog2e),
+                      reinterpret_cast<const float*>(smem + C_::X_EF)[cw], lt);
         float dd = 0.f;
 #pragma unroll
         for (int kb = 0; kb < PKB; ++kb) dd += dot8(xj[kb], yj[kb]);
         lt = wavesum(lt);
         dd = wavesum(dd);
         if (lane == 0) {
-            shares[buf * 8 + 2 * wave] = lt;
-            shares[buf * 8 + 2 * wave + 1] = dd;
+            shares[buf * 8 + 2 * cw] = lt;
+            shares[buf * 8 + 2 * cw + 1] = dd;
         }
     }
     dma_barrier();
-    if (tid == 0) {
+    if (wave == 0 && lane == 0) {
         const float* sh = shares + ((hpg - 1) & 1) * 8;
-        const size_t pi = ((size_t)(b * H + g * hpg + hpg - 1) * nC + c) * NJ + rj;
+        const size_t pi = ((size_t)(b * H + g * hpg + hpg - 1) * nC + c) * NJ + k_.rj;
         lt_part[pi] = (sh[0] + sh[2]) + (sh[4] + sh[6]);
         dd_part[pi] = (sh[1] + sh[3]) + (sh[5] + sh[7]);
     }
-
-    // ---------------------------------------------------------------- W products
-    {
-        const unsigned rowb = (unsigned)(G * N * 2);
-        const size_t bo = ((size_t)(b * T + t0) * G + g) * N;
-        // B rows [0, j0 + 64) at LDS rows 0.., C rows [j0, Q) at LDS rows j0 + 64..
-        issue_rows<NPR>(raw_rsrc(Bm + bo, (unsigned)Lc * rowb), rowb, 0, lds0, 0, j0 + 64, wave,
-                        lane);
-        issue_rows<NPR>(raw_rsrc(Cm + bo, (unsigned)Lc * rowb), rowb, j0, lds0, j0 + 64, Q - j0,
-                        wave, lane);
-    }
+    issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, true, k_.lds0, wave, lane);
+    // hand W (bf16, as the B operand of the two products) to the state waves
+    uint4* xw = reinterpret_cast<uint4*>(smem + C_::X_W) + (cw * PAIRS) * 64 + lane;
+#pragma unroll
+    for (int k = 0; k < PAIRS; ++k)
+        xw[k * 64] = make_uint4(pack_bf16(wacc[2 * k][0], wacc[2 * k][1]),
+                                pack_bf16(wacc[2 * k][2], wacc[2 * k][3]),
+                                pack_bf16(wacc[2 * k + 1][0], wacc[2 * k + 1][1]),
+                                pack_bf16(wacc[2 * k + 1][2], wacc[2 * k + 1][3]));
     dma_barrier();
-    const int l16 = lane & 15, g4 = lane >> 4;
-    const int jl = j0 + 16 * wave + l16;
-    const bool vj = jl < Lc;
+}
+
+// ------------------------------------------------------------------ state waves
+// The off-diagonal terms through the carried states E and F: (F B_j), (E C_j) for dx and
+// the per-row sums ob, oc; the dB and dC accumulators; the two W products at the end.
+template <int Q, int N, int P>
+__device__ __forceinline__ void bwd_state_role(
+    const BwdCtx& k_, unsigned char* smem, const __bf16* x, const __bf16* Bm, const __bf16* Cm,
+    const float* dtc, const float* cs, const __bf16* entry, const __bf16* exitg, const __bf16* dy,
+    __bf16* dB, __bf16* dC) {
+    using C_ = BwdCfg<Q, N, P>;
+    constexpr int PAIRS = C_::PAIRS, PPR = C_::PPR, NPR = C_::NPR;
+    constexpr int NKB = C_::NKB, PKB = C_::PKB, NT = C_::NT, PT = C_::PT;
+    const int b = k_.b, g = k_.g, c = k_.c, j0 = k_.j0, t0 = k_.t0, Lc = k_.Lc;
+    const int hpg = k_.hpg, T = k_.T, H = k_.H, G = k_.G, nC = k_.nC;
+    const int wave = k_.wave, cw = k_.cw, lane = k_.lane;
+    const int rsp = k_.rsp, tbase = k_.tbase;
+
+    issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, false, k_.lds0, wave, lane);
+    dma_barrier();
+    bf16x8 bj[NKB], cj[NKB];  // B_j, C_j over n (natural slots)
+    {
+        const int l16 = lane & 15, g4 = lane >> 4;
+        const int jl = j0 + 16 * cw + l16;
 #pragma unroll
-    for (int k = 0; k < PAIRS; ++k) {
-        const bool isrs = k < rsp;
-        const int rho = isrs ? 32 * k : tbase + 32 * (k - rsp) + 64;
-        const bf16x8 w8 = __builtin_bit_cast(
-            bf16x8, make_uint4(pack_bf16(wacc[2 * k][0], wacc[2 * k][1]),
-                               pack_bf16(wacc[2 * k][2], wacc[2 * k][3]),
-                               pack_bf16(wacc[2 * k + 1][0], wacc[2 * k + 1][1]),
-                               pack_bf16(wacc[2 * k + 1][2], wacc[2 * k + 1][3])));
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const bf16x8 a = frag_tr(smem, rho, 16 * nt, l16, g4, NPR);
-            if (isrs)
-                dcacc[nt] = mfma16(a, w8, dcacc[nt]);  // dC^T[n][j] += B[i][n] W^T[i][j]
-            else
-                dbacc[nt] = mfma16(a, w8, dbacc[nt]);  // dB^T[n][j] += C[t][n] W[t][j]
+        for (int kb = 0; kb < NKB; ++kb) {
+            bj[kb] = frag_nat(smem, jl, kb, g4, NPR);
+            cj[kb] = frag_nat(smem + C_::BCB, jl, kb, g4, NPR);
         }
     }
-    if (vj) {
+    lds_barrier();
+
+    f32x4 dbacc[NT], dcacc[NT];  // dB^T, dC^T [n][j]
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) dbacc[nt] = dcacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    issue_item<Q, N, P>(x, dy, entry, exitg, cs, dtc, b, g * hpg, c, j0, Lc, T, H, nC, k_.lds0,
+                        wave, lane);
+#pragma unroll 1
+    for (int hh = 0; hh < hpg; ++hh) {
+        const int h = g * hpg + hh;
+        const int buf = hh & 1;
+        dma_barrier();
+        if (hh + 1 < hpg)
+            issue_item<Q, N, P>(x, dy, entry, exitg, cs, dtc, b, h + 1, c, j0, Lc, T, H, nC,
+                                k_.lds0 + (buf ^ 1) * C_::ITEM, wave, lane);
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int l16 = ln & 15, g4 = ln >> 4;
+        const int jl = j0 + 16 * cw + l16;
+        const unsigned char* sXY = smem + buf * C_::ITEM;
+        const unsigned char* sE = sXY + C_::XYB;
+        const unsigned char* sF = sE + C_::EB;
+        const float* s_cs = reinterpret_cast<const float*>(sF + C_::EB);
+        const float* s_dt = s_cs + Q;
+        const float cs_last = s_cs[Q - 1];
+        const float csj = s_cs[jl], dtj = s_dt[jl];
+        const float ej = exp2_fast(csj * kLog2e), fj = exp2_fast((cs_last - csj) * kLog2e);
+
+        // dC^T[n][j] += sum_p E[p][n] (exp(cs_j) dy_j[p])
+#pragma unroll
+        for (int kb = 0; kb < PKB; ++kb) {
+            const bf16x8 ys8 = scale8(frag_rl(sXY, jl + 64, kb, g4, PPR), ej);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                dcacc[nt] = mfma16(frag_tr(sE, 32 * kb, 16 * nt, l16, g4, NPR), ys8, dcacc[nt]);
+        }
+        // (F B_j)[p] and (E C_j)[p] as [p][j] tiles; ob_j = exp(cs_last - cs_j) x_j . (F B_j),
+        // oc_j = exp(cs_j) dy_j . (E C_j)
+        float ob = 0.f, oc = 0.f;
+        uint2* xbf = reinterpret_cast<uint2*>(smem + C_::X_BF) + (cw * PT) * 64 + ln;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            f32x4 bfm = f32x4{0.f, 0.f, 0.f, 0.f}, cem = bfm;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                bfm = mfma16(frag_nat(sF, 16 * pt + l16, kb, g4, NPR), bj[kb], bfm);
+                cem = mfma16(frag_nat(sE, 16 * pt + l16, kb, g4, NPR), cj[kb], cem);
+            }
+            const uint2 xq = *reinterpret_cast<const uint2*>(sXY + swz_off(jl, 16 * pt + 4 * g4, PPR));
+            const uint2 yq = *reinterpret_cast<const uint2*>(sXY + swz_off(jl + 64, 16 * pt + 4 * g4, PPR));
+            ob = fmaf(bf16_lo(xq.x), bfm[0], ob);
+            ob = fmaf(bf16_hi(xq.x), bfm[1], ob);
+            ob = fmaf(bf16_lo(xq.y), bfm[2], ob);
+            ob = fmaf(bf16_hi(xq.y), bfm[3], ob);
+            oc = fmaf(bf16_lo(yq.x), cem[0], oc);
+            oc = fmaf(bf16_hi(yq.x), cem[1], oc);
+            oc = fmaf(bf16_lo(yq.y), cem[2], oc);
+            oc = fmaf(bf16_hi(yq.y), cem[3], oc);
+            xbf[pt * 64] = make_uint2(pack_bf16(bfm[0], bfm[1]), pack_bf16(bfm[2], bfm[3]));
+        }
+        ob = colsum(ob) * fj;
+        oc = colsum(oc) * ej;
+        float* xob = reinterpret_cast<float*>(smem + C_::X_OB);
+        if (g4 == 0) {
+            xob[16 * cw + l16] = ob;
+            xob[64 + 16 * cw + l16] = oc;
+        }
+        if (j0 == 0) {  // <E, F>, a quarter per state wave
+            float ef = 0.f;
+            for (int m = cw * 64 + ln; m < P * NPR; m += 256)
+                ef += dot8(*reinterpret_cast<const bf16x8*>(sE + 16 * m),
+                           *reinterpret_cast<const bf16x8*>(sF + 16 * m));
+            ef = wavesum(ef);
+            if (ln == 0) reinterpret_cast<float*>(smem + C_::X_EF)[cw] = ef;
+        }
+        lds_barrier();  // hand-off to the strip waves
+        // dB^T[n][j] += sum_p F[p][n] (dt_j exp(cs_last - cs_j) x_j[p])
+#pragma unroll
+        for (int kb = 0; kb < PKB; ++kb) {
+            const bf16x8 xs8 = scale8(frag_rl(sXY, jl, kb, g4, PPR), dtj * fj);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                dbacc[nt] = mfma16(frag_tr(sF, 32 * kb, 16 * nt, l16, g4, NPR), xs8, dbacc[nt]);
+        }
+    }
+    dma_barrier();
+    issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, true, k_.lds0, wave, lane);
+    dma_barrier();  // B / C rows and the strip waves' W are in LDS
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int jl = j0 + 16 * cw + l16;
+    const uint4* xw = reinterpret_cast<const uint4*>(smem + C_::X_W) + (cw * PAIRS) * 64 + lane;
+    // dC^T[n][j] += sum_i B[i][n] W^T[i][j] over the row-strip blocks, then
+    // dB^T[n][j] += sum_t C[t][n] W[t][j] over the column-strip blocks (two loops, so that
+    // no accumulator is chosen per block at run time)
+#pragma unroll 1
+    for (int k = 0; k < rsp; ++k) {
+        const bf16x8 w8 = __builtin_bit_cast(bf16x8, xw[k * 64]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            dcacc[nt] = mfma16(frag_tr(smem, 32 * k, 16 * nt, l16, g4, NPR), w8, dcacc[nt]);
+    }
+#pragma unroll 1
+    for (int k = rsp; k < PAIRS; ++k) {
+        const bf16x8 w8 = __builtin_bit_cast(bf16x8, xw[k * 64]);
+        const int rho = tbase + 32 * (k - rsp) + 64;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            dbacc[nt] = mfma16(frag_tr(smem, rho, 16 * nt, l16, g4, NPR), w8, dbacc[nt]);
+    }
+    if (jl < Lc) {
         const size_t ro = ((size_t)(b * T + t0 + jl) * G + g) * N + 4 * g4;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -466,6 +551,49 @@ void chunk_bwd_mfma_kernel(
                 make_uint2(pack_bf16(dcacc[nt][0], dcacc[nt][1]), pack_bf16(dcacc[nt][2], dcacc[nt][3]));
         }
     }
+}
+
+template <int Q, int N, int P>
+__global__ __launch_bounds__(512) void chunk_bwd_mfma_kernel(
+    const __bf16* __restrict__ x, const __bf16* __restrict__ Bm, const __bf16* __restrict__ Cm,
+    const float* __restrict__ dtc, const float* __restrict__ cs, const float* __restrict__ D,
+    const __bf16* __restrict__ entry, const __bf16* __restrict__ exitg,
+    const __bf16* __restrict__ dy, __bf16* __restrict__ dx, __bf16* __restrict__ dB,
+    __bf16* __restrict__ dC, float* __restrict__ dcs, float* __restrict__ direct,
+    float* __restrict__ lt_part, float* __restrict__ dd_part, int T, int H, int G, int nC) {
+    using C_ = BwdCfg<Q, N, P>;
+    extern __shared__ __align__(16) unsigned char smem[];
+    BwdCtx k_;
+    // neighbouring row blocks and chunks on the same XCD (its L2 holds their shared data)
+    const int nwg = gridDim.x, blk = blockIdx.x;
+    const int wp = (nwg % 8 == 0) ? (blk & 7) * (nwg >> 3) + (blk >> 3) : blk;
+    const int unit = wp / C_::NJ;
+    k_.rj = wp % C_::NJ;
+    k_.c = unit % nC;
+    k_.g = (unit / nC) % G;
+    k_.b = unit / (nC * G);
+    k_.j0 = k_.rj * 64;
+    k_.t0 = k_.c * Q;
+    k_.Lc = min(Q, T - k_.t0);
+    if (k_.j0 >= k_.Lc) return;  // no valid row
+    k_.hpg = H / G;
+    k_.T = T;
+    k_.H = H;
+    k_.G = G;
+    k_.nC = nC;
+    k_.wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    k_.cw = k_.wave & 3;
+    k_.lane = threadIdx.x & 63;
+    k_.jtile = k_.j0 / 16 + k_.cw;
+    k_.rsp = (k_.j0 / 16 + (k_.cw | 1) + 1) / 2;  // row-strip blocks: rows i < 32 rsp
+    k_.tbase = k_.j0 + 16 * (k_.cw & ~1);         // column strip: rows t >= tbase
+    k_.lds0 = lds_addr(smem);
+    // the two roles run the same sequence of barriers
+    if (k_.wave < 4)
+        bwd_strip_role<Q, N, P>(k_, smem, x, Bm, Cm, dtc, cs, D, entry, exitg, dy, dx, dcs,
+                                direct, lt_part, dd_part);
+    else
+        bwd_state_role<Q, N, P>(k_, smem, x, Bm, Cm, dtc, cs, entry, exitg, dy, dB, dC);
 }
 
 template <int Q, int N, int P>
