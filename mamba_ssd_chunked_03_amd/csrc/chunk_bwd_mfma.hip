@@ -17,9 +17,11 @@
 // dB_j += sum_t W[t][j] C_t.  For its columns a wave needs
 //   the row strip  W^T[i][j], i <= j   (rows i of W^T, from M^T = x dy^T)  -> dC_j
 //   the column strip W[t][j],  t >= j  (rows t, from M = dy x^T)          -> dB_j, dx_j
-// i.e. Q / 16 + 1 tiles of 16 x 16 (the diagonal tile twice), padded to whole 32-row
-// blocks: Q / 16 + 2 tiles for every wave and every J.  W is accumulated over the heads
-// in registers (fp32), so dB and dC cost two products per workgroup rather than per head.
+// taken as whole 32-row blocks covering rows [0, j0 + 64) and [j0, Q): Q / 16 + 4 tiles of
+// 16 x 16 for every wave and every J.  W is accumulated over the heads in registers (fp32),
+// so dB and dC cost two products per workgroup rather than per head.  Outside J the decays
+// are folded into the rows (prescale_rows), so only the four blocks inside J need work per
+// element.
 //
 // Everything is computed transposed so that the output rows (j) are MFMA columns: a lane
 // holds 4 consecutive p (or n) of one row j, which makes every per-row scalar a column sum
@@ -64,6 +66,30 @@ __device__ __forceinline__ bf16x8 frag_tr(const unsigned char* base, int r0, int
     const unsigned off = swz_off(r0 + 4 * g4 + (l16 >> 2), f0 + 4 * (l16 & 3), ppr);
     const uint2 lo = lds_read_tr16(base + off);
     const uint2 hi = lds_read_tr16(base + off + 16u * ppr * 16u);  // rows + 16 (ppr <= 16)
+    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+// Row rb + rl of a swizzled [rows][8 ppr] bf16 matrix, with rb a multiple of 16 (so of
+// ppr): the swizzle depends only on rl, so a lane's part of the byte offset is computed once
+// per head and the row base is a uniform offset (an immediate where it is a constant).
+__device__ __forceinline__ unsigned lane_part(int rl, int col, int ppr) {
+    return (unsigned)(rl * ppr + ((col >> 3) ^ (rl & (ppr - 1)))) * 16u + (unsigned)(col & 7) * 2u;
+}
+__device__ __forceinline__ const unsigned char* rows_at(const unsigned char* base, int rb, int ppr) {
+    return base + rb * ppr * 16;
+}
+// relabelled k-slots (two 8-byte halves at lane parts lo, hi)
+__device__ __forceinline__ bf16x8 ld_rl(const unsigned char* p, unsigned lo, unsigned hi) {
+    const uint2 a = *reinterpret_cast<const uint2*>(p + lo);
+    const uint2 b = *reinterpret_cast<const uint2*>(p + hi);
+    return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+__device__ __forceinline__ bf16x8 ld_nat(const unsigned char* p, unsigned off) {
+    return *reinterpret_cast<const bf16x8*>(p + off);
+}
+// transpose read of a 32-row block: rows 0..15 at p + off, rows 16..31 at p + off + plus16
+__device__ __forceinline__ bf16x8 ld_tr(const unsigned char* p, unsigned off, unsigned plus16) {
+    const uint2 lo = lds_read_tr16(p + off);
+    const uint2 hi = lds_read_tr16(p + off + plus16);
     return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 __device__ __forceinline__ bf16x8 scale8(bf16x8 v, float s) {
@@ -114,11 +140,23 @@ __device__ __forceinline__ void issue_rows(u32x4 rsrc, unsigned rowb, int src_ro
     }
 }
 
+// Makes an accumulator update happen where it is written: otherwise the compiler sinks
+// the updates of a head to the end of the loop and keeps every product they use live
+// across the rest of the head.
+__device__ __forceinline__ void pin(f32x4& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
+
+// bounds how far the scheduler moves the reads of one 32-row block ahead of the previous
+// block's products (each block's fragments would otherwise all be live at once)
+#ifndef SSD_FENCE
+#define SSD_FENCE() __builtin_amdgcn_sched_barrier(0)
+#endif
+
 template <int Q, int N, int P>
 struct BwdCfg {
     static constexpr int NW = 8, NTH = 512;         // 4 strip waves + 4 state waves
     static constexpr int NJ = Q / 64;               // row blocks per chunk
-    static constexpr int PAIRS = (Q / 16 + 2) / 2;  // 32-row blocks of strip per wave
+    static constexpr int PAIRS = Q / 32 + 2;        // 32-row blocks of strip per wave
     static constexpr int PPR = P / 8, NPR = N / 8;  // 16-byte pieces per row
     static constexpr int NKB = N / 32, PKB = P / 32;
     static constexpr int NT = N / 16, PT = P / 16;
@@ -189,14 +227,49 @@ __device__ __forceinline__ void issue_bc(const __bf16* Bm, const __bf16* Cm, int
 struct BwdCtx {
     int b, g, c, rj, j0, t0, Lc, hpg, T, H, G, nC;
     int wave, cw, lane;   // wave 0..7, column tile 0..3 of the block, lane
-    int jtile, rsp, tbase;
     uint32_t lds0;
 };
 
+// ------------------------------------------------------------------ decays folded into rows
+// Outside J the causal decay factors through a fixed row of the chunk: for i < j0 <= j,
+// exp(cs_j - cs_i) = exp(cs_j - cs_j0) exp(cs_j0 - cs_i), and for t > j0 + 63 >= j,
+// exp(cs_t - cs_j) = exp(cs_t - cs_j0+63) exp(cs_j0+63 - cs_j), every factor <= 1.  The
+// row factors (with dt_i for the row strip) are applied once per head to the x rows before
+// J and the dy rows after J in LDS, so that plain products of those rows give the decayed
+// W and the decayed (C B^T) product for dx; only the blocks inside J need per-element work.
+template <int Q, int N, int P>
+__device__ __forceinline__ void prescale_rows(unsigned char* sXY, const float* s_cs,
+                                              const float* s_dt, int j0, int tid) {
+    constexpr int PPR = P / 8;
+    const float cs_a = s_cs[j0], cs_b = s_cs[j0 + 63];
+    auto scale_piece = [&](unsigned char* p, float f) {
+        uint4 v = *reinterpret_cast<uint4*>(p);
+        v = make_uint4(pack_bf16(bf16_lo(v.x) * f, bf16_hi(v.x) * f),
+                       pack_bf16(bf16_lo(v.y) * f, bf16_hi(v.y) * f),
+                       pack_bf16(bf16_lo(v.z) * f, bf16_hi(v.z) * f),
+                       pack_bf16(bf16_lo(v.w) * f, bf16_hi(v.w) * f));
+        *reinterpret_cast<uint4*>(p) = v;
+    };
+    // x rows i < j0 (LDS rows i): dt_i exp(cs_j0 - cs_i)
+    for (int m = tid; m < j0 * PPR; m += 512) {
+        const int i = m / PPR;
+        scale_piece(sXY + 16 * m, s_dt[i] * exp2_fast((cs_a - s_cs[i]) * kLog2e));
+    }
+    // dy rows t >= j0 + 64 (LDS rows t + 64): exp(cs_t - cs_j0+63)
+    unsigned char* yb = sXY + (j0 + 128) * PPR * 16;
+    for (int m = tid; m < (Q - j0 - 64) * PPR; m += 512) {
+        const int t = j0 + 64 + m / PPR;
+        scale_piece(yb + 16 * m, exp2_fast((s_cs[t] - cs_b) * kLog2e));
+    }
+}
+
 // ------------------------------------------------------------------ strip waves
 // M strips, W accumulated over heads, C B^T on the strips, rs / ccol, the diagonal part
-// of dx; they finish dx and the per-row results of every head.
-template <int Q, int N, int P>
+// of dx; they finish dx and the per-row results of every head.  Instantiated per row block
+// (RJ), so that the block layout is known at compile time:
+//   row strip  blocks k < RSP: x rows [32k, 32k + 32), the last two inside J
+//   column strip blocks k < CSP: dy rows [j0 + 32k, +32), the first two inside J
+template <int Q, int N, int P, int RJ>
 __device__ __forceinline__ void bwd_strip_role(
     const BwdCtx& k_, unsigned char* smem, const __bf16* x, const __bf16* Bm, const __bf16* Cm,
     const float* dtc, const float* cs, const float* D, const __bf16* entry, const __bf16* exitg,
@@ -204,10 +277,13 @@ __device__ __forceinline__ void bwd_strip_role(
     using C_ = BwdCfg<Q, N, P>;
     constexpr int NJ = C_::NJ, PAIRS = C_::PAIRS, PPR = C_::PPR, NPR = C_::NPR;
     constexpr int NKB = C_::NKB, PKB = C_::PKB, PT = C_::PT;
-    const int b = k_.b, g = k_.g, c = k_.c, j0 = k_.j0, t0 = k_.t0, Lc = k_.Lc;
+    constexpr int j0 = 64 * RJ;
+    constexpr int RSO = 2 * RJ, RSP = RSO + 2;   // row strip: blocks before J, all
+    constexpr int CSP = (Q - j0) / 32;           // column strip blocks
+    static_assert(RSP + CSP == PAIRS, "layout");
+    const int b = k_.b, g = k_.g, c = k_.c, t0 = k_.t0, Lc = k_.Lc;
     const int hpg = k_.hpg, T = k_.T, H = k_.H, G = k_.G, nC = k_.nC;
     const int wave = k_.wave, cw = k_.cw, lane = k_.lane;
-    const int jtile = k_.jtile, rsp = k_.rsp, tbase = k_.tbase;
     float* const shares = reinterpret_cast<float*>(smem + C_::X_SH);
 
     issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, false, k_.lds0, wave, lane);
@@ -227,10 +303,10 @@ __device__ __forceinline__ void bwd_strip_role(
         }
 #pragma unroll
         for (int k = 0; k < PAIRS; ++k) {
-            const bool isrs = k < rsp;
+            const bool isrs = k < RSP;
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                const int row = (isrs ? 32 * k : tbase + 32 * (k - rsp)) + 16 * u + l16;
+                const int row = (isrs ? 32 * k : j0 + 32 * (k - RSP)) + 16 * u + l16;
                 const unsigned char* src = isrs ? sBc : sCc;
                 f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -255,55 +331,122 @@ __device__ __forceinline__ void bwd_strip_role(
         dma_barrier();  // this head's copies have landed; the other buffer is free
         if (hh > 0 && wave == 0 && lane == 0) {
             const float* sh = shares + (buf ^ 1) * 8;
-            const size_t pi = ((size_t)(b * H + h - 1) * nC + c) * NJ + k_.rj;
+            const size_t pi = ((size_t)(b * H + h - 1) * nC + c) * NJ + RJ;
             lt_part[pi] = (sh[0] + sh[2]) + (sh[4] + sh[6]);
             dd_part[pi] = (sh[1] + sh[3]) + (sh[5] + sh[7]);
         }
         if (hh + 1 < hpg)
             issue_item<Q, N, P>(x, dy, entry, exitg, cs, dtc, b, h + 1, c, j0, Lc, T, H, nC,
                                 k_.lds0 + (buf ^ 1) * C_::ITEM, wave, lane);
+        unsigned char* sXY = smem + buf * C_::ITEM;
+        const float* s_cs = reinterpret_cast<const float*>(sXY + C_::XYB + 2 * C_::EB);
+        const float* s_dt = s_cs + Q;
+        prescale_rows<Q, N, P>(sXY, s_cs, s_dt, j0, (int)threadIdx.x);
+        lds_barrier();
         // lane-dependent values re-derived every head from an opaque copy of the lane
         // index: the compiler recomputes the LDS addresses instead of keeping them live
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int l16 = ln & 15, g4 = ln >> 4;
-        const int jl = j0 + 16 * cw + l16;
+        const int jb = j0 + 16 * cw, jl = jb + l16;
         const bool vj = jl < Lc;
-        const unsigned char* sXY = smem + buf * C_::ITEM;
-        const float* s_cs = reinterpret_cast<const float*>(sXY + C_::XYB + 2 * C_::EB);
-        const float* s_dt = s_cs + Q;
         const float cs_last = s_cs[Q - 1];
         const float csj = s_cs[jl], dtj = s_dt[jl];
         const float fj = exp2_fast((cs_last - csj) * kLog2e);
-
-        bf16x8 xj[PKB], yj[PKB];  // x_j, dy_j over p (relabelled slots)
+        const float k1 = exp2_fast((csj - s_cs[j0]) * kLog2e);       // exp(cs_j - cs_j0)
+        const float k2 = exp2_fast((s_cs[j0 + 63] - csj) * kLog2e);  // exp(cs_j0+63 - cs_j)
+        // the lane's parts of its LDS offsets (see lane_part)
+        unsigned prl[PKB][2], ptp[PT], pac[PT];
 #pragma unroll
         for (int kb = 0; kb < PKB; ++kb) {
-            xj[kb] = frag_rl(sXY, jl, kb, g4, PPR);
-            yj[kb] = frag_rl(sXY, jl + 64, kb, g4, PPR);
+            prl[kb][0] = lane_part(l16, 32 * kb + 4 * g4, PPR);
+            prl[kb][1] = lane_part(l16, 32 * kb + 16 + 4 * g4, PPR);
         }
-        float rs = 0.f, ccol = 0.f;
-        f32x4 dxa[PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            ptp[pt] = lane_part(4 * g4 + (l16 >> 2), 16 * pt + 4 * (l16 & 3), PPR);
+            pac[pt] = lane_part(l16, 16 * pt + 4 * g4, PPR);
+        }
+        constexpr unsigned R16 = 16u * PPR * 16u;  // 16 rows of x / dy
+
+        bf16x8 xj[PKB], yj[PKB];  // x_j, dy_j over p (relabelled slots), unscaled rows of J
+#pragma unroll
+        for (int kb = 0; kb < PKB; ++kb) {
+            xj[kb] = ld_rl(rows_at(sXY, jb, PPR), prl[kb][0], prl[kb][1]);
+            yj[kb] = ld_rl(rows_at(sXY, jb + 64, PPR), prl[kb][0], prl[kb][1]);
+        }
+        float rs = 0.f;
+        f32x4 dxa[PT];  // sum_t dy[t][p] U[t][j], first as the part after J without k2
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) dxa[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // column strip after J: W[t][j] straight into the accumulators, and (C B^T) dy
+        {
+            bf16x8 xk[PKB];
 #pragma unroll
-        for (int k = 0; k < PAIRS; ++k) {
-            const bool isrs = k < rsp;
-            const int rbase = isrs ? 32 * k : tbase + 32 * (k - rsp);  // chunk row of the block
-            const int rho = isrs ? rbase : rbase + 64;                 // its LDS row
-            uint32_t ub[4] = {0u, 0u, 0u, 0u};
+            for (int kb = 0; kb < PKB; ++kb) xk[kb] = scale8(xj[kb], dtj * k2);
+#pragma unroll
+            for (int k = RSP + 2; k < PAIRS; ++k) {
+                const int rho = j0 + 32 * (k - RSP) + 64;
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int kb = 0; kb < PKB; ++kb)
+                        wacc[2 * k + u] = mfma16(
+                            ld_rl(rows_at(sXY, rho, PPR) + u * R16, prl[kb][0], prl[kb][1]),
+                            xk[kb], wacc[2 * k + u]);
+                pin(wacc[2 * k]);
+                pin(wacc[2 * k + 1]);
+                const uint2 g0 = gt[2 * k], g1 = gt[2 * k + 1];
+                const bf16x8 gb = __builtin_bit_cast(bf16x8, make_uint4(g0.x, g0.y, g1.x, g1.y));
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    dxa[pt] = mfma16(ld_tr(rows_at(sXY, rho, PPR), ptp[pt], R16), gb, dxa[pt]);
+                    pin(dxa[pt]);
+                }
+                SSD_FENCE();
+            }
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) dxa[pt] *= k2;
+        }
+        // row strip before J: W^T[i][j] from the scaled rows, its rs share elementwise
+        {
+            bf16x8 yk[PKB];
+#pragma unroll
+            for (int kb = 0; kb < PKB; ++kb) yk[kb] = scale8(yj[kb], k1);
+#pragma unroll
+            for (int k = 0; k < RSO; ++k)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    f32x4 w = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kb = 0; kb < PKB; ++kb)
+                        w = mfma16(ld_rl(rows_at(sXY, 32 * k, PPR) + u * R16, prl[kb][0], prl[kb][1]),
+                                   yk[kb], w);
+                    const uint2 gg = gt[2 * k + u];
+                    wacc[2 * k + u] += w;
+                    pin(wacc[2 * k + u]);
+                    rs = fmaf(w[0], bf16_lo(gg.x), rs);
+                    rs = fmaf(w[1], bf16_hi(gg.x), rs);
+                    rs = fmaf(w[2], bf16_lo(gg.y), rs);
+                    rs = fmaf(w[3], bf16_hi(gg.y), rs);
+                    pin(rs);
+                    if (u == 1) SSD_FENCE();
+                }
+        }
+        // the four blocks inside J, element by element (exact decays, causal mask)
+#pragma unroll
+        for (int k = RSO; k < RSP + 2; ++k) {
+            const bool isrs = k < RSP;
+            const int rbase = isrs ? 32 * k : j0 + 32 * (k - RSP);  // chunk row of the block
+            const int rho = isrs ? rbase : rbase + 64;              // its LDS row (unscaled)
+            uint32_t ub[4];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                // the tile against the wave's column tile: every element kept, the diagonal
-                // tile (kept on one side), or none (a padding tile)
-                const int ti = rbase / 16 + u;
-                const int mode = isrs ? (ti < jtile ? 0 : ti == jtile ? 1 : 2)
-                                      : (ti > jtile ? 0 : ti == jtile ? 1 : 2);
-                if (mode == 2) continue;
                 f32x4 m = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < PKB; ++kb)
-                    m = mfma16(frag_rl(sXY, rho + 16 * u + l16, kb, g4, PPR),
+                    m = mfma16(ld_rl(rows_at(sXY, rho, PPR) + u * R16, prl[kb][0], prl[kb][1]),
                                isrs ? yj[kb] : xj[kb], m);
                 const int r0 = rbase + 16 * u + 4 * g4;  // chunk row of element q = 0
                 const float4 csr = *reinterpret_cast<const float4*>(&s_cs[r0]);
@@ -315,32 +458,43 @@ __device__ __forceinline__ void bwd_strip_role(
                 float uq[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int rq = 4 * g4 + q;  // row within the tile; the column is l16
                     if (isrs) {  // W^T[i][j] = dt_i exp(cs_j - cs_i) M^T[i][j], i <= j
-                        const bool keep = mode == 0 || rq <= l16;
-                        const float e = keep ? exp2_fast((csj - cr[q]) * kLog2e) : 0.f;
+                        const float e = (jl - (r0 + q) >= 0) ? exp2_fast((csj - cr[q]) * kLog2e) : 0.f;
                         const float w = dr[q] * e * m[q];
                         wacc[2 * k + u][q] += w;
                         rs = fmaf(w, gq[q], rs);
-                        uq[q] = 0.f;
                     } else {  // V[t][j] = exp(cs_t - cs_j) M[t][j], t >= j; W = dt_j V
-                        const bool keep = mode == 0 || rq >= l16;
-                        const float e = keep ? exp2_fast((cr[q] - csj) * kLog2e) : 0.f;
-                        const float v = e * m[q];
-                        wacc[2 * k + u][q] = fmaf(dtj, v, wacc[2 * k + u][q]);
-                        ccol = fmaf(v, gq[q], ccol);
+                        const float e = ((r0 + q) - jl >= 0) ? exp2_fast((cr[q] - csj) * kLog2e) : 0.f;
+                        wacc[2 * k + u][q] = fmaf(dtj, e * m[q], wacc[2 * k + u][q]);
                         uq[q] = e * gq[q];
                     }
                 }
-                ub[2 * u] = pack_bf16(uq[0], uq[1]);
-                ub[2 * u + 1] = pack_bf16(uq[2], uq[3]);
+                pin(wacc[2 * k + u]);
+                pin(rs);
+                if (!isrs) {
+                    ub[2 * u] = pack_bf16(uq[0], uq[1]);
+                    ub[2 * u + 1] = pack_bf16(uq[2], uq[3]);
+                }
             }
             if (!isrs) {  // dx^T[p][j] += sum_t dy[t][p] U[t][j]
                 const bf16x8 bu = __builtin_bit_cast(bf16x8, make_uint4(ub[0], ub[1], ub[2], ub[3]));
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt)
-                    dxa[pt] = mfma16(frag_tr(sXY, rho, 16 * pt, l16, g4, PPR), bu, dxa[pt]);
+                for (int pt = 0; pt < PT; ++pt) {
+                    dxa[pt] = mfma16(ld_tr(rows_at(sXY, rho, PPR), ptp[pt], R16), bu, dxa[pt]);
+                    pin(dxa[pt]);
+                }
             }
+            SSD_FENCE();
+        }
+        // ccol_j = sum_t V[t][j] G[t][j] = x_j . (sum_t U[t][j] dy_t)
+        float ccol = 0.f;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            const uint2 xq = *reinterpret_cast<const uint2*>(rows_at(sXY, jb, PPR) + pac[pt]);
+            ccol = fmaf(bf16_lo(xq.x), dxa[pt][0], ccol);
+            ccol = fmaf(bf16_hi(xq.x), dxa[pt][1], ccol);
+            ccol = fmaf(bf16_lo(xq.y), dxa[pt][2], ccol);
+            ccol = fmaf(bf16_hi(xq.y), dxa[pt][3], ccol);
         }
         rs = colsum(rs);
         ccol = colsum(ccol);
@@ -359,7 +513,7 @@ __device__ __forceinline__ void bwd_strip_role(
             __bf16* dxr = dx + ((size_t)(b * T + t0 + jl) * H + h) * P + 4 * g4;
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
-                const uint2 yq = *reinterpret_cast<const uint2*>(sXY + swz_off(jl + 64, 16 * pt + 4 * g4, PPR));
+                const uint2 yq = *reinterpret_cast<const uint2*>(rows_at(sXY, jb + 64, PPR) + pac[pt]);
                 const uint2 bq = xbf[pt * 64];
                 const float v0 = fmaf(dh, bf16_lo(yq.x), dtj * fmaf(fj, bf16_lo(bq.x), dxa[pt][0]));
                 const float v1 = fmaf(dh, bf16_hi(yq.x), dtj * fmaf(fj, bf16_hi(bq.x), dxa[pt][1]));
@@ -417,7 +571,7 @@ __device__ __forceinline__ void bwd_state_role(
     const int b = k_.b, g = k_.g, c = k_.c, j0 = k_.j0, t0 = k_.t0, Lc = k_.Lc;
     const int hpg = k_.hpg, T = k_.T, H = k_.H, G = k_.G, nC = k_.nC;
     const int wave = k_.wave, cw = k_.cw, lane = k_.lane;
-    const int rsp = k_.rsp, tbase = k_.tbase;
+    const int rsp = (j0 + 64) / 32;  // row-strip blocks (rows 32 k), then column-strip blocks
 
     issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, false, k_.lds0, wave, lane);
     dma_barrier();
@@ -447,10 +601,30 @@ __device__ __forceinline__ void bwd_state_role(
         if (hh + 1 < hpg)
             issue_item<Q, N, P>(x, dy, entry, exitg, cs, dtc, b, h + 1, c, j0, Lc, T, H, nC,
                                 k_.lds0 + (buf ^ 1) * C_::ITEM, wave, lane);
+        {
+            unsigned char* it = smem + buf * C_::ITEM;
+            const float* ic = reinterpret_cast<const float*>(it + C_::XYB + 2 * C_::EB);
+            prescale_rows<Q, N, P>(it, ic, ic + Q, j0, (int)threadIdx.x);
+        }
+        lds_barrier();
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int l16 = ln & 15, g4 = ln >> 4;
-        const int jl = j0 + 16 * cw + l16;
+        const int jb = j0 + 16 * cw, jl = jb + l16;
+        unsigned prl[PKB][2], pac[PT], ptn[NT], pnat[NKB];
+#pragma unroll
+        for (int kb = 0; kb < PKB; ++kb) {
+            prl[kb][0] = lane_part(l16, 32 * kb + 4 * g4, PPR);
+            prl[kb][1] = lane_part(l16, 32 * kb + 16 + 4 * g4, PPR);
+        }
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) pac[pt] = lane_part(l16, 16 * pt + 4 * g4, PPR);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            ptn[nt] = lane_part(4 * g4 + (l16 >> 2), 16 * nt + 4 * (l16 & 3), NPR);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) pnat[kb] = lane_part(l16, 32 * kb + 8 * g4, NPR);
+        constexpr unsigned N16 = 16u * NPR * 16u;  // 16 rows of E / F
         const unsigned char* sXY = smem + buf * C_::ITEM;
         const unsigned char* sE = sXY + C_::XYB;
         const unsigned char* sF = sE + C_::EB;
@@ -463,10 +637,11 @@ __device__ __forceinline__ void bwd_state_role(
         // dC^T[n][j] += sum_p E[p][n] (exp(cs_j) dy_j[p])
 #pragma unroll
         for (int kb = 0; kb < PKB; ++kb) {
-            const bf16x8 ys8 = scale8(frag_rl(sXY, jl + 64, kb, g4, PPR), ej);
+            const bf16x8 ys8 =
+                scale8(ld_rl(rows_at(sXY, jb + 64, PPR), prl[kb][0], prl[kb][1]), ej);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
-                dcacc[nt] = mfma16(frag_tr(sE, 32 * kb, 16 * nt, l16, g4, NPR), ys8, dcacc[nt]);
+                dcacc[nt] = mfma16(ld_tr(rows_at(sE, 32 * kb, NPR), ptn[nt], N16), ys8, dcacc[nt]);
         }
         // (F B_j)[p] and (E C_j)[p] as [p][j] tiles; ob_j = exp(cs_last - cs_j) x_j . (F B_j),
         // oc_j = exp(cs_j) dy_j . (E C_j)
@@ -477,11 +652,11 @@ __device__ __forceinline__ void bwd_state_role(
             f32x4 bfm = f32x4{0.f, 0.f, 0.f, 0.f}, cem = bfm;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                bfm = mfma16(frag_nat(sF, 16 * pt + l16, kb, g4, NPR), bj[kb], bfm);
-                cem = mfma16(frag_nat(sE, 16 * pt + l16, kb, g4, NPR), cj[kb], cem);
+                bfm = mfma16(ld_nat(rows_at(sF, 16 * pt, NPR), pnat[kb]), bj[kb], bfm);
+                cem = mfma16(ld_nat(rows_at(sE, 16 * pt, NPR), pnat[kb]), cj[kb], cem);
             }
-            const uint2 xq = *reinterpret_cast<const uint2*>(sXY + swz_off(jl, 16 * pt + 4 * g4, PPR));
-            const uint2 yq = *reinterpret_cast<const uint2*>(sXY + swz_off(jl + 64, 16 * pt + 4 * g4, PPR));
+            const uint2 xq = *reinterpret_cast<const uint2*>(rows_at(sXY, jb, PPR) + pac[pt]);
+            const uint2 yq = *reinterpret_cast<const uint2*>(rows_at(sXY, jb + 64, PPR) + pac[pt]);
             ob = fmaf(bf16_lo(xq.x), bfm[0], ob);
             ob = fmaf(bf16_hi(xq.x), bfm[1], ob);
             ob = fmaf(bf16_lo(xq.y), bfm[2], ob);
@@ -511,10 +686,11 @@ __device__ __forceinline__ void bwd_state_role(
         // dB^T[n][j] += sum_p F[p][n] (dt_j exp(cs_last - cs_j) x_j[p])
 #pragma unroll
         for (int kb = 0; kb < PKB; ++kb) {
-            const bf16x8 xs8 = scale8(frag_rl(sXY, jl, kb, g4, PPR), dtj * fj);
+            const bf16x8 xs8 =
+                scale8(ld_rl(rows_at(sXY, jb, PPR), prl[kb][0], prl[kb][1]), dtj * fj);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
-                dbacc[nt] = mfma16(frag_tr(sF, 32 * kb, 16 * nt, l16, g4, NPR), xs8, dbacc[nt]);
+                dbacc[nt] = mfma16(ld_tr(rows_at(sF, 32 * kb, NPR), ptn[nt], N16), xs8, dbacc[nt]);
         }
     }
     dma_barrier();
@@ -523,6 +699,11 @@ __device__ __forceinline__ void bwd_state_role(
     const int l16 = lane & 15, g4 = lane >> 4;
     const int jl = j0 + 16 * cw + l16;
     const uint4* xw = reinterpret_cast<const uint4*>(smem + C_::X_W) + (cw * PAIRS) * 64 + lane;
+    unsigned ptn[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+        ptn[nt] = lane_part(4 * g4 + (l16 >> 2), 16 * nt + 4 * (l16 & 3), NPR);
+    constexpr unsigned N16 = 16u * NPR * 16u;
     // dC^T[n][j] += sum_i B[i][n] W^T[i][j] over the row-strip blocks, then
     // dB^T[n][j] += sum_t C[t][n] W[t][j] over the column-strip blocks (two loops, so that
     // no accumulator is chosen per block at run time)
@@ -531,15 +712,15 @@ __device__ __forceinline__ void bwd_state_role(
         const bf16x8 w8 = __builtin_bit_cast(bf16x8, xw[k * 64]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-            dcacc[nt] = mfma16(frag_tr(smem, 32 * k, 16 * nt, l16, g4, NPR), w8, dcacc[nt]);
+            dcacc[nt] = mfma16(ld_tr(rows_at(smem, 32 * k, NPR), ptn[nt], N16), w8, dcacc[nt]);
     }
 #pragma unroll 1
     for (int k = rsp; k < PAIRS; ++k) {
         const bf16x8 w8 = __builtin_bit_cast(bf16x8, xw[k * 64]);
-        const int rho = tbase + 32 * (k - rsp) + 64;
+        const int rho = j0 + 32 * (k - rsp) + 64;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-            dbacc[nt] = mfma16(frag_tr(smem, rho, 16 * nt, l16, g4, NPR), w8, dbacc[nt]);
+            dbacc[nt] = mfma16(ld_tr(rows_at(smem, rho, NPR), ptn[nt], N16), w8, dbacc[nt]);
     }
     if (jl < Lc) {
         const size_t ro = ((size_t)(b * T + t0 + jl) * G + g) * N + 4 * g4;
@@ -584,15 +765,24 @@ __global__ __launch_bounds__(512) void chunk_bwd_mfma_kernel(
     k_.wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     k_.cw = k_.wave & 3;
     k_.lane = threadIdx.x & 63;
-    k_.jtile = k_.j0 / 16 + k_.cw;
-    k_.rsp = (k_.j0 / 16 + (k_.cw | 1) + 1) / 2;  // row-strip blocks: rows i < 32 rsp
-    k_.tbase = k_.j0 + 16 * (k_.cw & ~1);         // column strip: rows t >= tbase
     k_.lds0 = lds_addr(smem);
-    // the two roles run the same sequence of barriers
-    if (k_.wave < 4)
-        bwd_strip_role<Q, N, P>(k_, smem, x, Bm, Cm, dtc, cs, D, entry, exitg, dy, dx, dcs,
-                                direct, lt_part, dd_part);
-    else
+    // the two roles run the same sequence of barriers; the strip role is instantiated per
+    // row block
+    if (k_.wave < 4) {
+        switch (k_.rj) {
+#define SSD_STRIP(RJ)                                                                        \
+    case RJ:                                                                                 \
+        if constexpr (RJ < C_::NJ)                                                           \
+            bwd_strip_role<Q, N, P, RJ>(k_, smem, x, Bm, Cm, dtc, cs, D, entry, exitg, dy, dx, \
+                                        dcs, direct, lt_part, dd_part);                      \
+        break;
+            SSD_STRIP(0)
+            SSD_STRIP(1)
+            SSD_STRIP(2)
+            SSD_STRIP(3)
+#undef SSD_STRIP
+        }
+    } else
         bwd_state_role<Q, N, P>(k_, smem, x, Bm, Cm, dtc, cs, entry, exitg, dy, dB, dC);
 }
 
