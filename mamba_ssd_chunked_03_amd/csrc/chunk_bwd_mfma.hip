@@ -146,12 +146,6 @@ __device__ __forceinline__ void issue_rows(u32x4 rsrc, unsigned rowb, int src_ro
 __device__ __forceinline__ void pin(f32x4& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
 
-// bounds how far the scheduler moves the reads of one 32-row block ahead of the previous
-// block's products (each block's fragments would otherwise all be live at once)
-#ifndef SSD_FENCE
-#define SSD_FENCE() __builtin_amdgcn_sched_barrier(0)
-#endif
-
 template <int Q, int N, int P>
 struct BwdCfg {
     static constexpr int NW = 8, NTH = 512;         // 4 strip waves + 4 state waves
@@ -223,13 +217,6 @@ __device__ __forceinline__ void issue_bc(const __bf16* Bm, const __bf16* Cm, int
     }
 }
 
-// Everything both roles need to know about their workgroup
-struct BwdCtx {
-    int b, g, c, rj, j0, t0, Lc, hpg, T, H, G, nC;
-    int wave, cw, lane;   // wave 0..7, column tile 0..3 of the block, lane
-    uint32_t lds0;
-};
-
 // ------------------------------------------------------------------ decays folded into rows
 // Outside J the causal decay factors through a fixed row of the chunk: for i < j0 <= j,
 // exp(cs_j - cs_i) = exp(cs_j - cs_j0) exp(cs_j0 - cs_i), and for t > j0 + 63 >= j,
@@ -238,8 +225,10 @@ struct BwdCtx {
 // J and the dy rows after J in LDS, so that plain products of those rows give the decayed
 // W and the decayed (C B^T) product for dx; only the blocks inside J need per-element work.
 template <int Q, int N, int P>
-__device__ __forceinline__ void prescale_rows(unsigned char* sXY, const float* s_cs,
-                                              const float* s_dt, int j0, int tid) {
+__device__ __forceinline__ void prescale_rows(unsigned char* sXY, int j0, int tid, int nth) {
+    const float* s_cs = reinterpret_cast<const float*>(sXY + BwdCfg<Q, N, P>::XYB +
+                                                       2 * BwdCfg<Q, N, P>::EB);
+    const float* s_dt = s_cs + Q;
     constexpr int PPR = P / 8;
     const float cs_a = s_cs[j0], cs_b = s_cs[j0 + 63];
     auto scale_piece = [&](unsigned char* p, float f) {
@@ -251,17 +240,24 @@ __device__ __forceinline__ void prescale_rows(unsigned char* sXY, const float* s
         *reinterpret_cast<uint4*>(p) = v;
     };
     // x rows i < j0 (LDS rows i): dt_i exp(cs_j0 - cs_i)
-    for (int m = tid; m < j0 * PPR; m += 512) {
+    for (int m = tid; m < j0 * PPR; m += nth) {
         const int i = m / PPR;
         scale_piece(sXY + 16 * m, s_dt[i] * exp2_fast((cs_a - s_cs[i]) * kLog2e));
     }
     // dy rows t >= j0 + 64 (LDS rows t + 64): exp(cs_t - cs_j0+63)
     unsigned char* yb = sXY + (j0 + 128) * PPR * 16;
-    for (int m = tid; m < (Q - j0 - 64) * PPR; m += 512) {
+    for (int m = tid; m < (Q - j0 - 64) * PPR; m += nth) {
         const int t = j0 + 64 + m / PPR;
         scale_piece(yb + 16 * m, exp2_fast((s_cs[t] - cs_b) * kLog2e));
     }
 }
+
+// Everything both roles need to know about their workgroup
+struct BwdCtx {
+    int b, g, c, rj, j0, t0, Lc, hpg, T, H, G, nC;
+    int wave, cw, lane;   // wave 0..7, column tile 0..3 of the block, lane
+    uint32_t lds0;
+};
 
 // ------------------------------------------------------------------ strip waves
 // M strips, W accumulated over heads, C B^T on the strips, rs / ccol, the diagonal part
@@ -324,11 +320,13 @@ __device__ __forceinline__ void bwd_strip_role(
 
     issue_item<Q, N, P>(x, dy, entry, exitg, cs, dtc, b, g * hpg, c, j0, Lc, T, H, nC, k_.lds0,
                         wave, lane);
+    dma_barrier();  // the first head's rows have landed
+    lds_barrier();  // ... and are scaled (by the state waves)
 #pragma unroll 1
     for (int hh = 0; hh < hpg; ++hh) {
         const int h = g * hpg + hh;
         const int buf = hh & 1;
-        dma_barrier();  // this head's copies have landed; the other buffer is free
+        lds_barrier();  // this head's rows are scaled; the other buffer is free
         if (hh > 0 && wave == 0 && lane == 0) {
             const float* sh = shares + (buf ^ 1) * 8;
             const size_t pi = ((size_t)(b * H + h - 1) * nC + c) * NJ + RJ;
@@ -341,8 +339,6 @@ __device__ __forceinline__ void bwd_strip_role(
         unsigned char* sXY = smem + buf * C_::ITEM;
         const float* s_cs = reinterpret_cast<const float*>(sXY + C_::XYB + 2 * C_::EB);
         const float* s_dt = s_cs + Q;
-        prescale_rows<Q, N, P>(sXY, s_cs, s_dt, j0, (int)threadIdx.x);
-        lds_barrier();
         // lane-dependent values re-derived every head from an opaque copy of the lane
         // index: the compiler recomputes the LDS addresses instead of keeping them live
         int ln = lane;
@@ -356,12 +352,11 @@ __device__ __forceinline__ void bwd_strip_role(
         const float k1 = exp2_fast((csj - s_cs[j0]) * kLog2e);       // exp(cs_j - cs_j0)
         const float k2 = exp2_fast((s_cs[j0 + 63] - csj) * kLog2e);  // exp(cs_j0+63 - cs_j)
         // the lane's parts of its LDS offsets (see lane_part)
-        unsigned prl[PKB][2], ptp[PT], pac[PT];
+        // contractions over p feed no further product, so they read 8 consecutive p
+        // (natural slots: one 16-byte read per fragment)
+        unsigned pnp[PKB], ptp[PT], pac[PT];
 #pragma unroll
-        for (int kb = 0; kb < PKB; ++kb) {
-            prl[kb][0] = lane_part(l16, 32 * kb + 4 * g4, PPR);
-            prl[kb][1] = lane_part(l16, 32 * kb + 16 + 4 * g4, PPR);
-        }
+        for (int kb = 0; kb < PKB; ++kb) pnp[kb] = lane_part(l16, 32 * kb + 8 * g4, PPR);
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
             ptp[pt] = lane_part(4 * g4 + (l16 >> 2), 16 * pt + 4 * (l16 & 3), PPR);
@@ -369,11 +364,11 @@ __device__ __forceinline__ void bwd_strip_role(
         }
         constexpr unsigned R16 = 16u * PPR * 16u;  // 16 rows of x / dy
 
-        bf16x8 xj[PKB], yj[PKB];  // x_j, dy_j over p (relabelled slots), unscaled rows of J
+        bf16x8 xj[PKB], yj[PKB];  // x_j, dy_j over p, unscaled rows of J
 #pragma unroll
         for (int kb = 0; kb < PKB; ++kb) {
-            xj[kb] = ld_rl(rows_at(sXY, jb, PPR), prl[kb][0], prl[kb][1]);
-            yj[kb] = ld_rl(rows_at(sXY, jb + 64, PPR), prl[kb][0], prl[kb][1]);
+            xj[kb] = ld_nat(rows_at(sXY, jb, PPR), pnp[kb]);
+            yj[kb] = ld_nat(rows_at(sXY, jb + 64, PPR), pnp[kb]);
         }
         float rs = 0.f;
         f32x4 dxa[PT];  // sum_t dy[t][p] U[t][j], first as the part after J without k2
@@ -392,9 +387,8 @@ __device__ __forceinline__ void bwd_strip_role(
                 for (int u = 0; u < 2; ++u)
 #pragma unroll
                     for (int kb = 0; kb < PKB; ++kb)
-                        wacc[2 * k + u] = mfma16(
-                            ld_rl(rows_at(sXY, rho, PPR) + u * R16, prl[kb][0], prl[kb][1]),
-                            xk[kb], wacc[2 * k + u]);
+                        wacc[2 * k + u] = mfma16(ld_nat(rows_at(sXY, rho, PPR) + u * R16, pnp[kb]),
+                                                 xk[kb], wacc[2 * k + u]);
                 pin(wacc[2 * k]);
                 pin(wacc[2 * k + 1]);
                 const uint2 g0 = gt[2 * k], g1 = gt[2 * k + 1];
@@ -404,7 +398,6 @@ __device__ __forceinline__ void bwd_strip_role(
                     dxa[pt] = mfma16(ld_tr(rows_at(sXY, rho, PPR), ptp[pt], R16), gb, dxa[pt]);
                     pin(dxa[pt]);
                 }
-                SSD_FENCE();
             }
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) dxa[pt] *= k2;
@@ -421,8 +414,7 @@ __device__ __forceinline__ void bwd_strip_role(
                     f32x4 w = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kb = 0; kb < PKB; ++kb)
-                        w = mfma16(ld_rl(rows_at(sXY, 32 * k, PPR) + u * R16, prl[kb][0], prl[kb][1]),
-                                   yk[kb], w);
+                        w = mfma16(ld_nat(rows_at(sXY, 32 * k, PPR) + u * R16, pnp[kb]), yk[kb], w);
                     const uint2 gg = gt[2 * k + u];
                     wacc[2 * k + u] += w;
                     pin(wacc[2 * k + u]);
@@ -431,10 +423,19 @@ __device__ __forceinline__ void bwd_strip_role(
                     rs = fmaf(w[2], bf16_lo(gg.y), rs);
                     rs = fmaf(w[3], bf16_hi(gg.y), rs);
                     pin(rs);
-                    if (u == 1) SSD_FENCE();
                 }
         }
-        // the four blocks inside J, element by element (exact decays, causal mask)
+        // the four blocks inside J, element by element (exact decays, causal mask); x_j and
+        // dy_j are read again here (through an opaque zero offset) rather than kept live
+        {
+            unsigned z = 0;
+            asm volatile("" : "+v"(z));
+#pragma unroll
+            for (int kb = 0; kb < PKB; ++kb) {
+                xj[kb] = ld_nat(rows_at(sXY, jb, PPR) + z, pnp[kb]);
+                yj[kb] = ld_nat(rows_at(sXY, jb + 64, PPR) + z, pnp[kb]);
+            }
+        }
 #pragma unroll
         for (int k = RSO; k < RSP + 2; ++k) {
             const bool isrs = k < RSP;
@@ -446,7 +447,7 @@ __device__ __forceinline__ void bwd_strip_role(
                 f32x4 m = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < PKB; ++kb)
-                    m = mfma16(ld_rl(rows_at(sXY, rho, PPR) + u * R16, prl[kb][0], prl[kb][1]),
+                    m = mfma16(ld_nat(rows_at(sXY, rho, PPR) + u * R16, pnp[kb]),
                                isrs ? yj[kb] : xj[kb], m);
                 const int r0 = rbase + 16 * u + 4 * g4;  // chunk row of element q = 0
                 const float4 csr = *reinterpret_cast<const float4*>(&s_cs[r0]);
@@ -484,7 +485,6 @@ __device__ __forceinline__ void bwd_strip_role(
                     pin(dxa[pt]);
                 }
             }
-            SSD_FENCE();
         }
         // ccol_j = sum_t V[t][j] G[t][j] = x_j . (sum_t U[t][j] dy_t)
         float ccol = 0.f;
@@ -499,7 +499,9 @@ __device__ __forceinline__ void bwd_strip_role(
         rs = colsum(rs);
         ccol = colsum(ccol);
 
-        lds_barrier();  // the state waves' (F B_j) tiles, ob, oc and <E, F> shares are in LDS
+        // the state waves' (F B_j) tiles, ob, oc and <E, F> shares are in LDS; every wave's
+        // copies of the next head have landed (the state waves scale them meanwhile)
+        dma_barrier();
         const uint2* xbf = reinterpret_cast<const uint2*>(smem + C_::X_BF) + (cw * PT) * 64 + ln;
         const float* xob = reinterpret_cast<const float*>(smem + C_::X_OB);
         const float ob = xob[16 * cw + l16], oc = xob[64 + 16 * cw + l16];
@@ -528,15 +530,8 @@ __device__ __forceinline__ void bwd_strip_role(
         if (j0 == 0 && ln == 0)
             lt = fmaf(exp2_fast(cs_last * kLog2e),
                       reinterpret_cast<const float*>(smem + C_::X_EF)[cw], lt);
-        float dd = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < PKB; ++kb) dd += dot8(xj[kb], yj[kb]);
         lt = wavesum(lt);
-        dd = wavesum(dd);
-        if (lane == 0) {
-            shares[buf * 8 + 2 * cw] = lt;
-            shares[buf * 8 + 2 * cw + 1] = dd;
-        }
+        if (lane == 0) shares[buf * 8 + 2 * cw] = lt;
     }
     dma_barrier();
     if (wave == 0 && lane == 0) {
@@ -593,20 +588,17 @@ __device__ __forceinline__ void bwd_state_role(
 
     issue_item<Q, N, P>(x, dy, entry, exitg, cs, dtc, b, g * hpg, c, j0, Lc, T, H, nC, k_.lds0,
                         wave, lane);
+    dma_barrier();
+    prescale_rows<Q, N, P>(smem, j0, (int)threadIdx.x - 256, 256);
+    lds_barrier();
 #pragma unroll 1
     for (int hh = 0; hh < hpg; ++hh) {
         const int h = g * hpg + hh;
         const int buf = hh & 1;
-        dma_barrier();
+        lds_barrier();
         if (hh + 1 < hpg)
             issue_item<Q, N, P>(x, dy, entry, exitg, cs, dtc, b, h + 1, c, j0, Lc, T, H, nC,
                                 k_.lds0 + (buf ^ 1) * C_::ITEM, wave, lane);
-        {
-            unsigned char* it = smem + buf * C_::ITEM;
-            const float* ic = reinterpret_cast<const float*>(it + C_::XYB + 2 * C_::EB);
-            prescale_rows<Q, N, P>(it, ic, ic + Q, j0, (int)threadIdx.x);
-        }
-        lds_barrier();
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int l16 = ln & 15, g4 = ln >> 4;
@@ -645,7 +637,7 @@ __device__ __forceinline__ void bwd_state_role(
         }
         // (F B_j)[p] and (E C_j)[p] as [p][j] tiles; ob_j = exp(cs_last - cs_j) x_j . (F B_j),
         // oc_j = exp(cs_j) dy_j . (E C_j)
-        float ob = 0.f, oc = 0.f;
+        float ob = 0.f, oc = 0.f, dd = 0.f;
         uint2* xbf = reinterpret_cast<uint2*>(smem + C_::X_BF) + (cw * PT) * 64 + ln;
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
@@ -665,10 +657,16 @@ __device__ __forceinline__ void bwd_state_role(
             oc = fmaf(bf16_hi(yq.x), cem[1], oc);
             oc = fmaf(bf16_lo(yq.y), cem[2], oc);
             oc = fmaf(bf16_hi(yq.y), cem[3], oc);
+            dd = fmaf(bf16_lo(xq.x), bf16_lo(yq.x), dd);
+            dd = fmaf(bf16_hi(xq.x), bf16_hi(yq.x), dd);
+            dd = fmaf(bf16_lo(xq.y), bf16_lo(yq.y), dd);
+            dd = fmaf(bf16_hi(xq.y), bf16_hi(yq.y), dd);
             xbf[pt * 64] = make_uint2(pack_bf16(bfm[0], bfm[1]), pack_bf16(bfm[2], bfm[3]));
         }
         ob = colsum(ob) * fj;
         oc = colsum(oc) * ej;
+        dd = wavesum(dd);  // this wave's 16 rows of x_j . dy_j (the dD share)
+        if (ln == 0) reinterpret_cast<float*>(smem + C_::X_SH)[buf * 8 + 2 * cw + 1] = dd;
         float* xob = reinterpret_cast<float*>(smem + C_::X_OB);
         if (g4 == 0) {
             xob[16 * cw + l16] = ob;
@@ -682,7 +680,9 @@ __device__ __forceinline__ void bwd_state_role(
             ef = wavesum(ef);
             if (ln == 0) reinterpret_cast<float*>(smem + C_::X_EF)[cw] = ef;
         }
-        lds_barrier();  // hand-off to the strip waves
+        dma_barrier();  // hand-off to the strip waves; the next head's copies have landed
+        if (hh + 1 < hpg)
+            prescale_rows<Q, N, P>(smem + (buf ^ 1) * C_::ITEM, j0, (int)threadIdx.x - 256, 256);
         // dB^T[n][j] += sum_p F[p][n] (dt_j exp(cs_last - cs_j) x_j[p])
 #pragma unroll
         for (int kb = 0; kb < PKB; ++kb) {
