@@ -260,7 +260,7 @@ struct BwdCtx {
 };
 
 // ------------------------------------------------------------------ strip waves
-// M strips, W accumulated over heads, C B^T on the strips, rs / ccol, the diagonal part
+// M strips, W accumulated over heads, C B^T on the strips, the W.G sums, the diagonal part
 // of dx; they finish dx and the per-row results of every head.  Instantiated per row block
 // (RJ), so that the block layout is known at compile time:
 //   row strip  blocks k < RSP: x rows [32k, 32k + 32), the last two inside J
@@ -269,7 +269,8 @@ template <int Q, int N, int P, int RJ>
 __device__ __forceinline__ void bwd_strip_role(
     const BwdCtx& k_, unsigned char* smem, const __bf16* x, const __bf16* Bm, const __bf16* Cm,
     const float* dtc, const float* cs, const float* D, const __bf16* entry, const __bf16* exitg,
-    const __bf16* dy, __bf16* dx, float* dcs, float* direct, float* lt_part, float* dd_part) {
+    const __bf16* dy, __bf16* dx, float* dcs, float* direct, float* xs, float* lt_part,
+    float* dd_part) {
     using C_ = BwdCfg<Q, N, P>;
     constexpr int NJ = C_::NJ, PAIRS = C_::PAIRS, PPR = C_::PPR, NPR = C_::NPR;
     constexpr int NKB = C_::NKB, PKB = C_::PKB, PT = C_::PT;
@@ -370,7 +371,18 @@ __device__ __forceinline__ void bwd_strip_role(
             xj[kb] = ld_nat(rows_at(sXY, jb, PPR), pnp[kb]);
             yj[kb] = ld_nat(rows_at(sXY, jb + 64, PPR), pnp[kb]);
         }
-        float rs = 0.f;
+        // per-column sums of W.G (W[t][i] G[t][i], i.e. the terms of dL/dcs):
+        //   rsb[s]  row j's pairs with columns i in the 64-row block s before J
+        //   rs_in   row j's pairs with columns i in J (fp32 from unscaled operands)
+        //   csu     column j's pairs with rows t in J, without the factor dt_j (likewise)
+        //   cpx     column j's pairs with rows t after J, without dt_j
+        // A pair inside J enters dL/dcs twice with opposite signs (row t and column i), so
+        // both of its copies are formed to fp32 accuracy and cancel; pairs across a block
+        // boundary are kept apart (xs) and summed once.
+        float rsb[RJ > 0 ? RJ : 1];
+#pragma unroll
+        for (int s2 = 0; s2 < (RJ > 0 ? RJ : 1); ++s2) rsb[s2] = 0.f;
+        float rs_in = 0.f, csu = 0.f;
         f32x4 dxa[PT];  // sum_t dy[t][p] U[t][j], first as the part after J without k2
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) dxa[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -402,7 +414,17 @@ __device__ __forceinline__ void bwd_strip_role(
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) dxa[pt] *= k2;
         }
-        // row strip before J: W^T[i][j] from the scaled rows, its rs share elementwise
+        // cpx_j = x_j . (sum over t after J of U[t][j] dy_t)
+        float cpx = 0.f;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            const uint2 xq = *reinterpret_cast<const uint2*>(rows_at(sXY, jb, PPR) + pac[pt]);
+            cpx = fmaf(bf16_lo(xq.x), dxa[pt][0], cpx);
+            cpx = fmaf(bf16_hi(xq.x), dxa[pt][1], cpx);
+            cpx = fmaf(bf16_lo(xq.y), dxa[pt][2], cpx);
+            cpx = fmaf(bf16_hi(xq.y), dxa[pt][3], cpx);
+        }
+        // row strip before J: W^T[i][j] from the scaled rows, its W.G sums per 64-row block
         {
             bf16x8 yk[PKB];
 #pragma unroll
@@ -418,11 +440,12 @@ __device__ __forceinline__ void bwd_strip_role(
                     const uint2 gg = gt[2 * k + u];
                     wacc[2 * k + u] += w;
                     pin(wacc[2 * k + u]);
-                    rs = fmaf(w[0], bf16_lo(gg.x), rs);
-                    rs = fmaf(w[1], bf16_hi(gg.x), rs);
-                    rs = fmaf(w[2], bf16_lo(gg.y), rs);
-                    rs = fmaf(w[3], bf16_hi(gg.y), rs);
-                    pin(rs);
+                    float& r_ = rsb[k >> 1];
+                    r_ = fmaf(w[0], bf16_lo(gg.x), r_);
+                    r_ = fmaf(w[1], bf16_hi(gg.x), r_);
+                    r_ = fmaf(w[2], bf16_lo(gg.y), r_);
+                    r_ = fmaf(w[3], bf16_hi(gg.y), r_);
+                    pin(r_);
                 }
         }
         // the four blocks inside J, element by element (exact decays, causal mask); x_j and
@@ -463,15 +486,18 @@ __device__ __forceinline__ void bwd_strip_role(
                         const float e = (jl - (r0 + q) >= 0) ? exp2_fast((csj - cr[q]) * kLog2e) : 0.f;
                         const float w = dr[q] * e * m[q];
                         wacc[2 * k + u][q] += w;
-                        rs = fmaf(w, gq[q], rs);
+                        rs_in = fmaf(w, gq[q], rs_in);
                     } else {  // V[t][j] = exp(cs_t - cs_j) M[t][j], t >= j; W = dt_j V
                         const float e = ((r0 + q) - jl >= 0) ? exp2_fast((cr[q] - csj) * kLog2e) : 0.f;
-                        wacc[2 * k + u][q] = fmaf(dtj, e * m[q], wacc[2 * k + u][q]);
+                        const float v = e * m[q];
+                        wacc[2 * k + u][q] = fmaf(dtj, v, wacc[2 * k + u][q]);
+                        csu = fmaf(v, gq[q], csu);
                         uq[q] = e * gq[q];
                     }
                 }
                 pin(wacc[2 * k + u]);
-                pin(rs);
+                pin(rs_in);
+                pin(csu);
                 if (!isrs) {
                     ub[2 * u] = pack_bf16(uq[0], uq[1]);
                     ub[2 * u + 1] = pack_bf16(uq[2], uq[3]);
@@ -486,18 +512,11 @@ __device__ __forceinline__ void bwd_strip_role(
                 }
             }
         }
-        // ccol_j = sum_t V[t][j] G[t][j] = x_j . (sum_t U[t][j] dy_t)
-        float ccol = 0.f;
+        rs_in = colsum(rs_in);
+        csu = colsum(csu);
+        cpx = colsum(cpx);
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            const uint2 xq = *reinterpret_cast<const uint2*>(rows_at(sXY, jb, PPR) + pac[pt]);
-            ccol = fmaf(bf16_lo(xq.x), dxa[pt][0], ccol);
-            ccol = fmaf(bf16_hi(xq.x), dxa[pt][1], ccol);
-            ccol = fmaf(bf16_lo(xq.y), dxa[pt][2], ccol);
-            ccol = fmaf(bf16_hi(xq.y), dxa[pt][3], ccol);
-        }
-        rs = colsum(rs);
-        ccol = colsum(ccol);
+        for (int s2 = 0; s2 < RJ; ++s2) rsb[s2] = colsum(rsb[s2]);
 
         // the state waves' (F B_j) tiles, ob, oc and <E, F> shares are in LDS; every wave's
         // copies of the next head have landed (the state waves scale them meanwhile)
@@ -506,9 +525,14 @@ __device__ __forceinline__ void bwd_strip_role(
         const float* xob = reinterpret_cast<const float*>(smem + C_::X_OB);
         const float ob = xob[16 * cw + l16], oc = xob[64 + 16 * cw + l16];
         if (g4 == 0 && vj) {
-            const size_t cb = ((size_t)(b * H + h) * nC + c) * Q;
-            direct[cb + jl] = ccol + ob;
-            dcs[cb + jl] = rs + oc - dtj * (ccol + ob);
+            const size_t item = (size_t)(b * H + h) * nC + c;
+            const size_t cb = item * Q;
+            direct[cb + jl] = (cpx + csu) + ob;
+            dcs[cb + jl] = (rs_in - dtj * csu) + (oc - dtj * ob);
+            float* xr = xs + item * NJ * Q + jl;
+            xr[0] = dtj * cpx;
+#pragma unroll
+            for (int s2 = 0; s2 < RJ; ++s2) xr[(1 + s2) * Q] = rsb[s2];
         }
         if (vj) {
             const float dh = D[h];
@@ -741,7 +765,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_mfma_kernel(
     const __bf16* __restrict__ entry, const __bf16* __restrict__ exitg,
     const __bf16* __restrict__ dy, __bf16* __restrict__ dx, __bf16* __restrict__ dB,
     __bf16* __restrict__ dC, float* __restrict__ dcs, float* __restrict__ direct,
-    float* __restrict__ lt_part, float* __restrict__ dd_part, int T, int H, int G, int nC) {
+    float* __restrict__ xs, float* __restrict__ lt_part, float* __restrict__ dd_part, int T,
+    int H, int G, int nC) {
     using C_ = BwdCfg<Q, N, P>;
     extern __shared__ __align__(16) unsigned char smem[];
     BwdCtx k_;
@@ -774,7 +799,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_mfma_kernel(
     case RJ:                                                                                 \
         if constexpr (RJ < C_::NJ)                                                           \
             bwd_strip_role<Q, N, P, RJ>(k_, smem, x, Bm, Cm, dtc, cs, D, entry, exitg, dy, dx, \
-                                        dcs, direct, lt_part, dd_part);                      \
+                                        dcs, direct, xs, lt_part, dd_part);                  \
         break;
             SSD_STRIP(0)
             SSD_STRIP(1)
@@ -805,7 +830,8 @@ hipError_t launch_bwd_mfma_t(const Shape& s, const BwdArgs& a, hipStream_t st) {
     kern<<<blocks, C_::NTH, C_::LDS, st>>>(
         (const __bf16*)a.x, (const __bf16*)a.Bm, (const __bf16*)a.Cm, a.dtc, a.cs, a.D,
         (const __bf16*)a.entry, (const __bf16*)a.exitg, (const __bf16*)a.dy, (__bf16*)a.dx,
-        (__bf16*)a.dB, (__bf16*)a.dC, a.dcs, a.direct, a.lt_part, a.dd_part, s.T, s.H, s.G, s.nC);
+        (__bf16*)a.dB, (__bf16*)a.dC, a.dcs, a.direct, a.xs, a.lt_part, a.dd_part, s.T, s.H, s.G,
+        s.nC);
     return hipGetLastError();
 }
 

@@ -256,9 +256,18 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_valu_kernel(
 // chunk-end term (summed from the row tiles' shares); ddt_j = direct_j + A R_j and this
 // chunk's share of dA, sum_j dt_j R_j.  rows: rows per tile of the kernel that wrote the
 // shares.
+// R_j = sum_{k >= j} dL/dcs_k is a sum over the chunk's pairs (t, i) with i < j <= t of
+// W[t][i] G[t][i] (each pair enters dL/dcs_t with + and dL/dcs_i with -), plus the terms
+// through the carried states.  dcs holds what a plain suffix sum takes: the state terms, and
+// pair terms whose two copies are formed to fp32 accuracy.  With xs (64-row blocks Jb), the
+// pairs across a block boundary arrive apart and are summed once each:
+//   R_j += sum_{k in Jb, k >= j} (rp_k - cp_k) + CP[Jb] + K[Jb],
+// rp_k = sum_{s < blk(k)} xs[1 + s][k]   (row k with the columns of earlier blocks)
+// cp_k = xs[0][k], CP[Jb] = sum_{k in Jb} cp_k   (column k with the rows of later blocks)
+// K[Jb] = sum_{s < Jb} sum_{k >= 64 (Jb + 1)} xs[1 + s][k]   (later rows, earlier columns)
 __global__ __launch_bounds__(kThreads) void bwd_ddt_kernel(
     const float* __restrict__ dcs, const float* __restrict__ direct,
-    const float* __restrict__ lt_part, const float* __restrict__ dtc, const float* __restrict__ A,
+    const float* __restrict__ xs, const float* __restrict__ lt_part, const float* __restrict__ dtc, const float* __restrict__ A,
     float* __restrict__ ddt, float* __restrict__ dA_part, int T, int H, int Q, int nC,
     int rows, int items) {
     const int item = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
@@ -290,12 +299,59 @@ __global__ __launch_bounds__(kThreads) void bwd_ddt_kernel(
         if (lane + o < 64) suf += up;
     }
     float r = (suf - seg) + lt;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (xs) {
+        const int NJ = Q / 64, lpb = 64 / L;  // blocks, lanes per block
+        const int blk = lane / lpb;
+        const float* xr = xs + (size_t)item * NJ * Q;
+        float segb = 0.f, segcp = 0.f, ks = 0.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int k = k0 + m;
+            if (m < L && k < Lc) {
+                const float cp = xr[k];
+                float rp = 0.f;
+                for (int s = 0; s < blk; ++s) rp += xr[(size_t)(1 + s) * Q + k];
+                bv[m] = rp - cp;
+                segb += bv[m];
+                segcp += cp;
+            }
+        }
+        // suffix of rp - cp within the block, and the block's total of cp
+        float sufb = segb;
+        const int bend = (blk + 1) * lpb;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float up = __shfl_down(sufb, o, 64);
+            if (lane + o < bend) sufb += up;
+        }
+        for (int o = 1; o < lpb; o <<= 1) segcp += __shfl_xor(segcp, o, 64);
+        // K: for each plane s, the suffix over the lanes after this block
+        for (int s = 0; s + 1 < NJ; ++s) {
+            float ps = 0.f;
+            if (blk > s) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int k = k0 + m;
+                    if (m < L && k < Lc) ps += xr[(size_t)(1 + s) * Q + k];
+                }
+            }
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const float up = __shfl_down(ps, o, 64);
+                if (lane + o < 64) ps += up;
+            }
+            const float after = __shfl(ps, bend < 64 ? bend : 63, 64);
+            if (s < blk && bend < 64) ks += after;
+        }
+        r += (sufb - segb) + segcp + ks;
+    }
     const float Ah = A[h];
     float da = 0.f;
 #pragma unroll
     for (int m = 3; m >= 0; --m) {
         if (m >= L) continue;
-        r += v[m];
+        r += v[m] + bv[m];
         const int j = k0 + m;
         if (j < Lc) {
             ddt[((size_t)b * T + c * Q + j) * H + h] = direct[cb + j] + Ah * r;
@@ -373,7 +429,7 @@ hipError_t launch_bwd_finalize(const Shape& s, const BwdArgs& a, int rows, hipSt
     const int items = s.B * s.H * s.nC;
     if (items > 0) {
         const unsigned blocks = (unsigned)((items + 3) / 4);
-        bwd_ddt_kernel<<<blocks, kThreads, 0, st>>>(a.dcs, a.direct, a.lt_part, a.dtc, a.A,
+        bwd_ddt_kernel<<<blocks, kThreads, 0, st>>>(a.dcs, a.direct, a.xs, a.lt_part, a.dtc, a.A,
                                                     a.ddt, a.dA_part, s.T, s.H, s.Q, s.nC, rows,
                                                     items);
         hipError_t e = hipGetLastError();

@@ -117,7 +117,7 @@ ssd_status run_chunk_state(const Shape& s, ssd_dtype dtype, const void* x, const
 struct BwdWorkspace {
     float *dtc, *cs;
     void *states, *entry, *exitg;
-    float *dcs, *direct, *lt_part, *dd_part, *dA_part;
+    float *dcs, *direct, *xs, *lt_part, *dd_part, *dA_part;
 };
 
 size_t bwd_workspace_bytes(const Shape& s, BwdWorkspace* w, char* base) {
@@ -138,6 +138,7 @@ size_t bwd_workspace_bytes(const Shape& s, BwdWorkspace* w, char* base) {
     ws.exitg = take(state_elems * sizeof(float));
     ws.dcs = take(chunk_elems * sizeof(float));
     ws.direct = take(chunk_elems * sizeof(float));
+    ws.xs = take(chunk_elems * (size_t)(s.Q / 64 > 0 ? s.Q / 64 : 1) * sizeof(float));
     ws.lt_part = take(tile_elems * sizeof(float));
     ws.dd_part = take(tile_elems * sizeof(float));
     ws.dA_part = take((size_t)s.B * s.H * s.nC * sizeof(float));
@@ -338,6 +339,7 @@ ssd_status ssd_bwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const f
     a.dcs = ws.dcs; a.direct = ws.direct;
     a.lt_part = ws.lt_part; a.dd_part = ws.dd_part; a.dA_part = ws.dA_part;
     const bool mfma_bwd = dtype == SSD_BF16 && ssd::chunk_bwd_mfma_supported(s);
+    a.xs = mfma_bwd ? ws.xs : nullptr;
     const int rows = mfma_bwd ? ssd::chunk_bwd_mfma_rows() : ssd::chunk_bwd_valu_rows();
     if (has_tokens) {
         r = hip_status(mfma_bwd ? ssd::launch_chunk_bwd_mfma(s, a, st)

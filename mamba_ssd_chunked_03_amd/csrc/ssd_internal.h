@@ -86,6 +86,11 @@ struct BwdArgs {
     void *dx, *dB, *dC;                    // outputs, dtype
     float *ddt, *dA, *dD;                  // outputs, fp32
     float *dcs, *direct;                   // [B][H][nC][Q]: dL/dcs and the explicit dL/ddt
+    // [B][H][nC][Q / 64][Q], MFMA path only (null otherwise): the in-chunk pair terms that
+    // cross a 64-row block boundary, kept apart from dcs so that no pair is summed twice
+    // (plane 0: per column, its pairs with rows in later blocks; plane 1 + s: per row, its
+    // pairs with columns in block s)
+    float* xs;
     float *lt_part, *dd_part;              // [B][H][nC][Q / rows]: per row tile
     float* dA_part;                        // [B][H][nC]
 };

@@ -11,8 +11,8 @@ import torch
 
 import oracle
 from mamba_ssd_chunked_03_amd import binding
-from mamba_ssd_chunked_03_amd.workloads import (STRESS, TINY_FP32, Workload, generate,
-                                                generate_grads, variants)
+from mamba_ssd_chunked_03_amd.workloads import (STRESS, TINY_FP32, WORKLOADS, Workload,
+                                                generate, generate_grads, variants)
 from parity import TOL, np64, rel_l2, say, to_device
 
 pytestmark = pytest.mark.gpu
@@ -115,3 +115,16 @@ def test_bwd_is_deterministic():
     b = gpu_bwd(w, cpu, up)
     for k in GRADS:
         assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("name", ["mamba2_2p7b", "mamba2_130m", "nsweep_n64"])
+def test_bwd_full_size_workloads(name):
+    """The model-shaped backward workloads at full size, with the launch configuration that
+    bench.py --bwd times (bf16, Q = 256, MFMA in-chunk kernel), compared whole-tensor with
+    the oracle's reverse-mode pass over every (b, h) sequence."""
+    w = WORKLOADS[name]
+    say(f"[bwd full] {w.describe()}")
+    cpu = generate(w)
+    up = generate_grads(w)
+    g = gpu_bwd(w, cpu, up)
+    compare(w, g, oracle_bwd(cpu, up))
