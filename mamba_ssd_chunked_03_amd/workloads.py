@@ -171,3 +171,66 @@ def head_slice(inputs, w, b, h):
     if inputs["init_state"] is not None:
         out["init_state"] = inputs["init_state"][b:b + 1, h:h + 1]
     return out
+
+
+# ---------------------------------------------------------------- the block around the layer
+@dataclass(frozen=True)
+class BlockCfg:
+    """The block's own sizes: conv width, normalisation groups (contiguous channel groups
+    of the H*P gated channels, per token), RMS instead of mean/variance, epsilon."""
+    conv_k: int = 4
+    norm_groups: int = 1
+    rms: bool = False
+    eps: float = 1e-5
+
+
+# Model-shaped blocks: the layer shapes above with a width-4 convolution and one
+# normalisation group over the H*P channels of a token.
+BLOCKS = {
+    "block_2p7b": (MAMBA2_2P7B, BlockCfg()),
+    "block_130m": (MAMBA2_130M, BlockCfg()),
+}
+
+
+def proj_width(w):
+    """Channels per token of the projection output [z | x | B | C | dt_raw]."""
+    d = w.nheads * w.headdim
+    return 2 * d + 2 * w.ngroups * w.dstate + w.nheads
+
+
+def generate_block(w, cfg, device="cpu"):
+    """Inputs of the block between the projections, from their own generator (seeded with
+    seed + 2, drawn in fp32 in this order):
+      zxbcdt  ~ N(0, 1), [B, T, proj_width], cast to the workload dtype
+      conv_w  ~ U(-1/sqrt(K), 1/sqrt(K)), [H*P + 2*G*N, K] fp32
+      conv_b  ~ U(-1/sqrt(K), 1/sqrt(K)), [H*P + 2*G*N] fp32
+      dt_bias ~ U(-3, -1), [H] fp32
+      A_h     = -exp(U(lo, hi)) as for the layer;  D ~ N(0, 1);  init ~ N(0, 0.1) if asked
+      norm_w  ~ 1 + N(0, 0.01), [H*P] fp32 (variance 0.01)
+      norm_b  ~ N(0, 0.01), [H*P] fp32."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(w.seed) + 2)
+    Bz, T, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    d = H * P
+    cdim = d + 2 * G * N
+    K = cfg.conv_k
+    bound = 1.0 / math.sqrt(K)
+    zxbcdt = torch.randn((Bz, T, proj_width(w)), generator=g, dtype=torch.float32)
+    conv_w = (torch.rand((cdim, K), generator=g, dtype=torch.float32) * 2 - 1) * bound
+    conv_b = (torch.rand((cdim,), generator=g, dtype=torch.float32) * 2 - 1) * bound
+    dt_bias = torch.rand((H,), generator=g, dtype=torch.float32) * 2 - 3
+    lo, hi = w.log_neg_a_range
+    A = -torch.exp(torch.rand((H,), generator=g, dtype=torch.float32) * (hi - lo) + lo)
+    D = torch.randn((H,), generator=g, dtype=torch.float32)
+    init = None
+    if w.init_state:
+        init = torch.randn((Bz, H, N, P), generator=g, dtype=torch.float32) * math.sqrt(0.1)
+    norm_w = 1 + torch.randn((d,), generator=g, dtype=torch.float32) * 0.1
+    norm_b = torch.randn((d,), generator=g, dtype=torch.float32) * 0.1
+    if w.a_zero:
+        A = torch.zeros_like(A)
+    out = dict(zxbcdt=zxbcdt.to(_torch_dtype(w.dtype)), conv_w=conv_w, conv_b=conv_b,
+               dt_bias=dt_bias, A=A, D=D, init_state=init, norm_w=norm_w, norm_b=norm_b)
+    if device != "cpu":
+        out = {k: (None if v is None else v.to(device)) for k, v in out.items()}
+    return out
