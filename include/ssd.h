@@ -1,6 +1,7 @@
 /*
  * ssd.h -- libssd: the Mamba-2 SSD (state space dual) layer on AMD MI355X (gfx950): the
- * forward, its backward and the single-token recurrent step.
+ * forward, its backward, the single-token recurrent step, and the block's prologue and
+ * epilogue around the layer (convolution, step sizes, gate, normalisation).
  *
  * The operation ("Mamba-2: Attention's Distant Cousin", docsaid.org, sections "Writing an
  * SSM as a Matrix" and "Reducing A to a Single Number"; structured summary of arXiv
@@ -233,6 +234,72 @@ ssd_status ssd_bwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const f
 ssd_status ssd_decode_step(const ssd_dims* dims, ssd_dtype dtype, const void* x,
                            const float* dt, const float* A, const void* B, const void* C,
                            const float* D, float* state, void* y, void* stream);
+
+/* ---- the block around the layer ----------------------------------------------------
+ * The Mamba-2 block between its input and output projections ("Mamba-2: Attention's
+ * Distant Cousin", section "The Mamba-2 Block", Figure 6; structured summary of arXiv
+ * 2405.21060, section "The Mamba-2 Architecture" and section 6.4): one projection yields,
+ * per token, the rows [z | x | B | C | dt_raw] of widths H*P, H*P, G*N, G*N, H.  The x, B, C
+ * channels pass through a depthwise causal convolution of width K (3-4 on the pages) and
+ * SiLU (the activation after the convolution, and the default feature map on B and C); the
+ * step size is made positive by softplus after a per-head bias.  After the layer, y is
+ * gated by SiLU(z) and normalised per token over contiguous channel groups (GroupNorm,
+ * the default extra normalisation, or its RMS variant).  The projections themselves are
+ * plain GEMMs and not part of this library.  Computation in fp32; x, B, C, z, y and out in
+ * `dtype`. */
+
+/* Prologue.  With Cd = H*P + 2*G*N, for every b, t < T and channel c < Cd:
+ *   v[b][t][c] = SiLU(conv_b[c] + sum_{k<K} conv_w[c*K + k] * xbc[b][t-(K-1)+k][c])
+ *   (xbc = 0 before t = 0; conv_w[c*K + K-1] weights the current step), and
+ *   x[b][t][h][p] = v[b][t][h*P + p],  B[b][t][g][n] = v[b][t][H*P + g*N + n],
+ *   C[b][t][g][n] = v[b][t][H*P + G*N + g*N + n],
+ *   dt[b][t][h] = softplus(dt_raw[b][t][h] + dt_bias[h]) = log(1 + exp(.)).
+ *   xbc     device, rows of Cd channels in `dtype`, row r = b*T + t at r * xbc_stride
+ *           elements (xbc_stride >= Cd); rows may sit inside a wider projection output
+ *   conv_w  [Cd][K] fp32, conv_b [Cd] fp32 or NULL (zero); conv_k = K in 1..8
+ *   dt_raw  rows of H values in `dtype` at dt_stride elements (>= H); dt_bias [H] or NULL
+ *   x, B, C [B][T][H][P], [B][T][G][N], [B][T][G][N] in `dtype` (16-byte aligned), and
+ *   dt      [B][T][H] fp32: the inputs ssd_fwd takes.
+ * xbc and dt_raw need only element alignment (16-byte alignment of xbc and a row stride
+ * that is a multiple of 16 bytes take the vector path).  Errors as ssd_fwd; SSD_ERR_DIMS
+ * for a stride below the row width; SSD_ERR_UNSUPPORTED for K outside 1..8. */
+ssd_status ssd_block_prologue(const ssd_dims* dims, ssd_dtype dtype, const void* xbc,
+                              int64_t xbc_stride, const float* conv_w, const float* conv_b,
+                              int conv_k, const void* dt_raw, int64_t dt_stride,
+                              const float* dt_bias, void* x, void* B, void* C, float* dt,
+                              void* stream);
+
+/* Epilogue.  With D = H*P channels split into norm_groups contiguous groups of S = D /
+ * norm_groups, for every b, t and group q, over its channels c:
+ *   v[c] = y[b][t][c] * SiLU(z[b][t][c])
+ *   GroupNorm (rms = 0): m = mean(v), s2 = mean((v - m)^2),
+ *                        out[c] = (v[c] - m) / sqrt(s2 + eps) * norm_w[c] + norm_b[c]
+ *   RMS (rms != 0):      out[c] = v[c] / sqrt(mean(v^2) + eps) * norm_w[c]   (no norm_b)
+ *   y    [B][T][H][P] in `dtype` (16-byte aligned: ssd_fwd's output)
+ *   z    rows of D values in `dtype` at z_stride elements (>= D)
+ *   norm_w [D] fp32, norm_b [D] fp32 or NULL (zero); eps >= 0
+ *   out  [B][T][H*P] in `dtype`, 16-byte aligned (may alias y).
+ * Errors as ssd_fwd; SSD_ERR_DIMS if norm_groups does not divide H*P. */
+ssd_status ssd_block_epilogue(const ssd_dims* dims, ssd_dtype dtype, const void* y,
+                              const void* z, int64_t z_stride, const float* norm_w,
+                              const float* norm_b, int norm_groups, int rms, float eps,
+                              void* out, void* stream);
+
+/* Bytes of workspace ssd_block_fwd needs (0 if the sizes are invalid): x, y, B, C, dt of
+ * the layer and ssd_fwd's own workspace. */
+size_t ssd_block_fwd_workspace_size(const ssd_dims* dims, ssd_dtype dtype, int chunk_len);
+
+/* The block between the projections: ssd_block_prologue on the x|B|C and dt_raw columns of
+ * zxbcdt ([B][T] rows of 2*H*P + 2*G*N + H values, [z | x | B | C | dt_raw], contiguous,
+ * 16-byte aligned), ssd_fwd (A, D, chunk_len, init_state, final_state as there), then
+ * ssd_block_epilogue with z from the first H*P columns; out [B][T][H*P] in `dtype`.
+ * Errors as the three calls, all checked before the first launch. */
+ssd_status ssd_block_fwd(const ssd_dims* dims, ssd_dtype dtype, const void* zxbcdt,
+                         const float* conv_w, const float* conv_b, int conv_k,
+                         const float* dt_bias, const float* A, const float* D, int chunk_len,
+                         const float* init_state, const float* norm_w, const float* norm_b,
+                         int norm_groups, int rms, float eps, void* out, float* final_state,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -16,7 +16,9 @@ SSD_F32, SSD_BF16 = 0, 1
 _DTYPE_CODE = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}
 EXPORTED = ("ssd_status_string", "ssd_fwd_workspace_size", "ssd_fwd", "ssd_chunk_cumsum",
             "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_gram_size", "ssd_chunk_gram",
-            "ssd_chunk_scan", "ssd_decode_step", "ssd_bwd_workspace_size", "ssd_bwd")
+            "ssd_chunk_scan", "ssd_decode_step", "ssd_bwd_workspace_size", "ssd_bwd",
+            "ssd_block_prologue", "ssd_block_epilogue", "ssd_block_fwd_workspace_size",
+            "ssd_block_fwd")
 
 
 class SsdDims(ctypes.Structure):
@@ -73,6 +75,17 @@ def library(path=LIB_PATH):
     lib.ssd_bwd.restype = i
     lib.ssd_bwd.argtypes = [dims, i, vp, fp, fp, vp, vp, fp, i, fp, vp, fp, vp, fp, fp, vp, vp,
                             fp, fp, vp, sz, vp]
+    i64, f = ctypes.c_int64, ctypes.c_float
+    lib.ssd_block_prologue.restype = i
+    lib.ssd_block_prologue.argtypes = [dims, i, vp, i64, fp, fp, i, vp, i64, fp, vp, vp, vp, fp,
+                                       vp]
+    lib.ssd_block_epilogue.restype = i
+    lib.ssd_block_epilogue.argtypes = [dims, i, vp, vp, i64, fp, fp, i, i, f, vp, vp]
+    lib.ssd_block_fwd_workspace_size.restype = sz
+    lib.ssd_block_fwd_workspace_size.argtypes = [dims, i, i]
+    lib.ssd_block_fwd.restype = i
+    lib.ssd_block_fwd.argtypes = [dims, i, vp, fp, fp, i, fp, fp, fp, i, fp, fp, fp, i, i, f, vp,
+                                  fp, vp, sz, vp]
     if path == LIB_PATH:
         _LIB = lib
     return lib
@@ -297,3 +310,123 @@ def ssd_bwd(x, dt, A, B, C, D, chunk_len, dy, init_state=None, d_final=None, wan
                              _ptr(o["dC"]), _ptr(o["dD"]), _ptr(o["d_init"]), _ptr(workspace),
                              workspace.numel(), _stream(dev, stream)))
     return o
+
+
+# ---------------------------------------------------------------- the block around the layer
+def _row_stride(t, name, dtype=None, device=None):
+    """Elements between consecutive [B*T] rows of a [B, T, width] view whose last dim is
+    contiguous and whose rows are evenly spaced (a column range of a wider tensor)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.dim() != 3 or (t.shape[2] > 1 and t.stride(2) != 1):
+        raise ValueError(f"{name} must be [B, T, width] with contiguous rows")
+    rs = t.stride(1)
+    if t.shape[0] > 1 and t.stride(0) != t.shape[1] * rs:
+        raise ValueError(f"{name}: rows must be evenly spaced over batch and time")
+    return rs
+
+
+def ssd_block_prologue(xbc, conv_w, conv_b, dt_raw, dt_bias, nheads, headdim, dstate, ngroups,
+                       x=None, B=None, C=None, dt=None, stream=None):
+    """x, B, C, dt = prologue(xbc, dt_raw) on the GPU through libssd.ssd_block_prologue.
+
+    xbc [B, T, H*P + 2*G*N] and dt_raw [B, T, H] in fp32 or bf16 (views with evenly spaced
+    rows, e.g. column ranges of the projection output); conv_w [H*P+2GN, K], conv_b, dt_bias
+    fp32 (biases may be None)."""
+    dev = xbc.device
+    code = _DTYPE_CODE.get(xbc.dtype)
+    if code is None:
+        raise TypeError(f"xbc must be fp32 or bf16, got {xbc.dtype}")
+    xs = _row_stride(xbc, "xbc", device=dev)
+    ds = _row_stride(dt_raw, "dt_raw", xbc.dtype, dev)
+    _need(conv_w, "conv_w", torch.float32, dev)
+    for t, n in ((conv_b, "conv_b"), (dt_bias, "dt_bias")):
+        if t is not None:
+            _need(t, n, torch.float32, dev)
+    bz, T = xbc.shape[0], xbc.shape[1]
+    d = SsdDims(bz, T, nheads, headdim, dstate, ngroups)
+    x = torch.empty((bz, T, nheads, headdim), dtype=xbc.dtype, device=dev) if x is None else x
+    B = torch.empty((bz, T, ngroups, dstate), dtype=xbc.dtype, device=dev) if B is None else B
+    C = torch.empty((bz, T, ngroups, dstate), dtype=xbc.dtype, device=dev) if C is None else C
+    dt = torch.empty((bz, T, nheads), dtype=torch.float32, device=dev) if dt is None else dt
+    _check(library().ssd_block_prologue(ctypes.byref(d), code, _ptr(xbc), xs, _ptr(conv_w),
+                                        _ptr(conv_b), int(conv_w.shape[1]), _ptr(dt_raw), ds,
+                                        _ptr(dt_bias), _ptr(x), _ptr(B), _ptr(C), _ptr(dt),
+                                        _stream(dev, stream)))
+    return dict(x=x, B=B, C=C, dt=dt)
+
+
+def ssd_block_epilogue(y, z, norm_w, norm_b, norm_groups, rms=False, eps=1e-5, dstate=16,
+                       ngroups=1, out=None, stream=None):
+    """out = norm(y * silu(z)) per token on the GPU through libssd.ssd_block_epilogue.
+
+    y [B, T, H, P] contiguous; z [B, T, H*P] (a view with evenly spaced rows); norm_w,
+    norm_b [H*P] fp32 (norm_b may be None).  dstate and ngroups only complete the layer's
+    sizes for validation.  Returns out [B, T, H*P]."""
+    dev = y.device
+    code = _DTYPE_CODE.get(y.dtype)
+    if code is None:
+        raise TypeError(f"y must be fp32 or bf16, got {y.dtype}")
+    _need(y, "y", device=dev)
+    zs = _row_stride(z, "z", y.dtype, dev)
+    _need(norm_w, "norm_w", torch.float32, dev)
+    if norm_b is not None:
+        _need(norm_b, "norm_b", torch.float32, dev)
+    bz, T, H, P = y.shape
+    d = SsdDims(bz, T, H, P, dstate, ngroups)
+    if out is None:
+        out = torch.empty((bz, T, H * P), dtype=y.dtype, device=dev)
+    _check(library().ssd_block_epilogue(ctypes.byref(d), code, _ptr(y), _ptr(z), zs,
+                                        _ptr(norm_w), _ptr(norm_b), int(norm_groups),
+                                        int(bool(rms)), float(eps), _ptr(out),
+                                        _stream(dev, stream)))
+    return out
+
+
+def ssd_block_fwd_workspace_size(dims, dtype, chunk_len):
+    return int(library().ssd_block_fwd_workspace_size(ctypes.byref(dims), int(dtype),
+                                                      int(chunk_len)))
+
+
+def ssd_block_fwd(zxbcdt, conv_w, conv_b, dt_bias, A, D, chunk_len, norm_w, norm_b,
+                  norm_groups, headdim, dstate, ngroups, rms=False, eps=1e-5, init_state=None,
+                  out=None, final_state=None, workspace=None, want_final=True, stream=None):
+    """out, final_state = block(zxbcdt) on the GPU through libssd.ssd_block_fwd.
+
+    zxbcdt [B, T, 2*H*P + 2*G*N + H] contiguous ([z | x | B | C | dt_raw] per token), H from
+    A.  Returns (out [B, T, H*P], final_state [B, H, N, P] or None)."""
+    dev = zxbcdt.device
+    code = _DTYPE_CODE.get(zxbcdt.dtype)
+    if code is None:
+        raise TypeError(f"zxbcdt must be fp32 or bf16, got {zxbcdt.dtype}")
+    _need(zxbcdt, "zxbcdt", device=dev)
+    f32 = torch.float32
+    for t, n in ((conv_w, "conv_w"), (A, "A"), (D, "D"), (norm_w, "norm_w")):
+        _need(t, n, f32, dev)
+    for t, n in ((conv_b, "conv_b"), (dt_bias, "dt_bias"), (norm_b, "norm_b"),
+                 (init_state, "init_state")):
+        if t is not None:
+            _need(t, n, f32, dev)
+    H = A.shape[0]
+    bz, T = zxbcdt.shape[0], zxbcdt.shape[1]
+    if zxbcdt.shape[2] != 2 * H * headdim + 2 * ngroups * dstate + H:
+        raise ValueError("zxbcdt width must be 2*H*P + 2*G*N + H")
+    d = SsdDims(bz, T, H, headdim, dstate, ngroups)
+    if out is None:
+        out = torch.empty((bz, T, H * headdim), dtype=zxbcdt.dtype, device=dev)
+    if final_state is None and want_final:
+        final_state = torch.empty((bz, H, dstate, headdim), dtype=f32, device=dev)
+    if workspace is None:
+        ws = ssd_block_fwd_workspace_size(d, code, chunk_len)
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+    _check(library().ssd_block_fwd(ctypes.byref(d), code, _ptr(zxbcdt), _ptr(conv_w),
+                                   _ptr(conv_b), int(conv_w.shape[1]), _ptr(dt_bias), _ptr(A),
+                                   _ptr(D), int(chunk_len), _ptr(init_state), _ptr(norm_w),
+                                   _ptr(norm_b), int(norm_groups), int(bool(rms)), float(eps),
+                                   _ptr(out), _ptr(final_state), _ptr(workspace),
+                                   workspace.numel(), _stream(dev, stream)))
+    return out, final_state

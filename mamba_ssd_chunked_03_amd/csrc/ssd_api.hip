@@ -367,4 +367,137 @@ ssd_status ssd_decode_step(const ssd_dims* dims, ssd_dtype dtype, const void* x,
                                               (hipStream_t)stream));
 }
 
+// ---- the block around the layer -----------------------------------------------------
+
+static bool aligned_elem(const void* p, ssd_dtype dtype) {
+    return ((uintptr_t)p & (dtype == SSD_BF16 ? 1u : 3u)) == 0;
+}
+
+ssd_status ssd_block_prologue(const ssd_dims* dims, ssd_dtype dtype, const void* xbc,
+                              int64_t xbc_stride, const float* conv_w, const float* conv_b,
+                              int conv_k, const void* dt_raw, int64_t dt_stride,
+                              const float* dt_bias, void* x, void* B, void* C, float* dt,
+                              void* stream) {
+    Shape s;
+    ssd_status r = make_shape(dims, 64, &s);
+    if (r != SSD_OK) return r;
+    if (!valid_dtype(dtype) || conv_k < 1 || conv_k > 8) return SSD_ERR_UNSUPPORTED;
+    const int64_t cdim = (int64_t)s.H * s.P + 2 * (int64_t)s.G * s.N;
+    if (xbc_stride < cdim || dt_stride < s.H) return SSD_ERR_DIMS;
+    if ((int64_t)s.B * s.T * xbc_stride >= ((int64_t)1 << 31) ||
+        (int64_t)s.B * s.T * dt_stride >= ((int64_t)1 << 31))
+        return SSD_ERR_DIMS;
+    if ((size_t)s.B * s.T == 0) return SSD_OK;
+    if (!xbc || !conv_w || !dt_raw || !x || !B || !C || !dt) return SSD_ERR_NULL;
+    if (any_misaligned({x, B, C}) || any_misaligned4({conv_w, conv_b, dt_bias, dt}) ||
+        !aligned_elem(xbc, dtype) || !aligned_elem(dt_raw, dtype))
+        return SSD_ERR_ALIGN;
+    ssd::BlockPrologueArgs a;
+    a.xbc = xbc; a.xbc_stride = xbc_stride;
+    a.conv_w = conv_w; a.conv_b = conv_b; a.conv_k = conv_k;
+    a.dt_raw = dt_raw; a.dt_stride = dt_stride; a.dt_bias = dt_bias;
+    a.x = x; a.Bm = B; a.Cm = C; a.dt = dt;
+    return hip_status(ssd::launch_block_prologue(s, dtype, a, (hipStream_t)stream));
+}
+
+ssd_status ssd_block_epilogue(const ssd_dims* dims, ssd_dtype dtype, const void* y,
+                              const void* z, int64_t z_stride, const float* norm_w,
+                              const float* norm_b, int norm_groups, int rms, float eps,
+                              void* out, void* stream) {
+    Shape s;
+    ssd_status r = make_shape(dims, 64, &s);
+    if (r != SSD_OK) return r;
+    if (!valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
+    const int64_t d = (int64_t)s.H * s.P;
+    if (norm_groups < 1 || d % norm_groups != 0 || z_stride < d || !(eps >= 0.f) ||
+        (int64_t)s.B * s.T * z_stride >= ((int64_t)1 << 31))
+        return SSD_ERR_DIMS;
+    if ((size_t)s.B * s.T == 0) return SSD_OK;
+    if (!y || !z || !norm_w || !out) return SSD_ERR_NULL;
+    if (any_misaligned({y, out}) || any_misaligned4({norm_w, norm_b}) ||
+        !aligned_elem(z, dtype))
+        return SSD_ERR_ALIGN;
+    ssd::BlockEpilogueArgs a;
+    a.y = y; a.z = z; a.z_stride = z_stride;
+    a.norm_w = norm_w; a.norm_b = norm_b;
+    a.groups = norm_groups; a.rms = rms ? 1 : 0; a.eps = eps;
+    a.out = out;
+    return hip_status(ssd::launch_block_epilogue(s, dtype, a, (hipStream_t)stream));
+}
+
+namespace {
+struct BlockWorkspace {
+    void *x, *B, *C, *y;
+    float* dt;
+    char* fwd;
+    size_t fwd_bytes;
+};
+
+size_t block_workspace_bytes(const Shape& s, ssd_dtype dtype, BlockWorkspace* w, char* base) {
+    const size_t e = dtype == SSD_BF16 ? 2 : 4;
+    const size_t bt = (size_t)s.B * s.T;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char* p = base ? base + off : nullptr;
+        off += round_up(bytes);
+        return p;
+    };
+    BlockWorkspace ws;
+    ws.x = take(bt * s.H * s.P * e);
+    ws.y = take(bt * s.H * s.P * e);
+    ws.B = take(bt * s.G * s.N * e);
+    ws.C = take(bt * s.G * s.N * e);
+    ws.dt = (float*)take(bt * s.H * sizeof(float));
+    ws.fwd_bytes = workspace_bytes(s, nullptr, nullptr);
+    ws.fwd = take(ws.fwd_bytes);
+    if (w) *w = ws;
+    return off;
+}
+}  // namespace
+
+size_t ssd_block_fwd_workspace_size(const ssd_dims* dims, ssd_dtype dtype, int chunk_len) {
+    Shape s;
+    if (make_shape(dims, chunk_len, &s) != SSD_OK || !valid_dtype(dtype)) return 0;
+    return block_workspace_bytes(s, dtype, nullptr, nullptr);
+}
+
+ssd_status ssd_block_fwd(const ssd_dims* dims, ssd_dtype dtype, const void* zxbcdt,
+                         const float* conv_w, const float* conv_b, int conv_k,
+                         const float* dt_bias, const float* A, const float* D, int chunk_len,
+                         const float* init_state, const float* norm_w, const float* norm_b,
+                         int norm_groups, int rms, float eps, void* out, float* final_state,
+                         void* workspace, size_t workspace_bytes_given, void* stream) {
+    Shape s;
+    ssd_status r = make_shape(dims, chunk_len, &s);
+    if (r != SSD_OK) return r;
+    if (!valid_dtype(dtype) || conv_k < 1 || conv_k > 8) return SSD_ERR_UNSUPPORTED;
+    const int64_t d = (int64_t)s.H * s.P, gn = (int64_t)s.G * s.N;
+    const int64_t width = 2 * d + 2 * gn + s.H;
+    if (norm_groups < 1 || d % norm_groups != 0 || !(eps >= 0.f) ||
+        (int64_t)s.B * s.T * width >= ((int64_t)1 << 31))
+        return SSD_ERR_DIMS;
+    const bool has_tokens = (size_t)s.B * s.T > 0;
+    if (has_tokens && (!zxbcdt || !conv_w || !A || !D || !norm_w || !out)) return SSD_ERR_NULL;
+    if (any_misaligned({zxbcdt, out, workspace}) ||
+        any_misaligned4({conv_w, conv_b, dt_bias, A, D, init_state, norm_w, norm_b,
+                         final_state}))
+        return SSD_ERR_ALIGN;
+    BlockWorkspace ws;
+    const size_t need = block_workspace_bytes(s, dtype, &ws, (char*)workspace);
+    if (need > 0 && (!workspace || workspace_bytes_given < need)) return SSD_ERR_WORKSPACE;
+    const size_t e = dtype == SSD_BF16 ? 2 : 4;
+    const char* zx = (const char*)zxbcdt;
+    if (has_tokens) {
+        r = ssd_block_prologue(dims, dtype, zx + d * e, width, conv_w, conv_b, conv_k,
+                               zx + (2 * d + 2 * gn) * e, width, dt_bias, ws.x, ws.B, ws.C,
+                               ws.dt, stream);
+        if (r != SSD_OK) return r;
+    }
+    r = ssd_fwd(dims, dtype, ws.x, ws.dt, A, ws.B, ws.C, D, chunk_len, init_state, ws.y,
+                final_state, ws.fwd, ws.fwd_bytes, stream);
+    if (r != SSD_OK || !has_tokens) return r;
+    return ssd_block_epilogue(dims, dtype, ws.y, zxbcdt, width, norm_w, norm_b, norm_groups,
+                              rms, eps, out, stream);
+}
+
 }  // extern "C"

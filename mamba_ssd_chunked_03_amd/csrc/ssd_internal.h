@@ -104,4 +104,30 @@ hipError_t launch_chunk_bwd_mfma(const Shape& s, const BwdArgs& a, hipStream_t s
 // ddt and dA, dD from the per-chunk and per-tile shares (rows: rows per tile)
 hipError_t launch_bwd_finalize(const Shape& s, const BwdArgs& a, int rows, hipStream_t st);
 
+// ---- the block around the layer (block.hip) -------------------------------------------
+struct BlockPrologueArgs {
+    const void* xbc;            // [B][T] rows of H*P + 2*G*N channels, in dtype
+    long long xbc_stride;       // elements between rows
+    const float *conv_w, *conv_b;  // [H*P + 2GN][conv_k], [H*P + 2GN] (conv_b may be null)
+    int conv_k;                 // 1..8
+    const void* dt_raw;         // [B][T] rows of H, in dtype
+    long long dt_stride;
+    const float* dt_bias;       // [H] or null
+    void *x, *Bm, *Cm;          // [B][T][H][P], [B][T][G][N] x2, in dtype
+    float* dt;                  // [B][T][H]
+};
+hipError_t launch_block_prologue(const Shape& s, ssd_dtype dtype, const BlockPrologueArgs& a,
+                                 hipStream_t st);
+struct BlockEpilogueArgs {
+    const void* y;              // [B][T][H*P], in dtype
+    const void* z;              // [B][T] rows of H*P, in dtype
+    long long z_stride;
+    const float *norm_w, *norm_b;  // [H*P] (norm_b may be null)
+    int groups, rms;
+    float eps;
+    void* out;                  // [B][T][H*P], in dtype
+};
+hipError_t launch_block_epilogue(const Shape& s, ssd_dtype dtype, const BlockEpilogueArgs& a,
+                                 hipStream_t st);
+
 }  // namespace ssd

@@ -156,9 +156,10 @@ def test_bwd_workspace_size(lib):
     tiles = 4 * 80 * nC * (256 // 16) * 4
     per_chunk = 4 * 80 * nC * 4
     # dt_chunk, cs, chunk states (reused for the entry-state gradients), entry states, exit
-    # gradients, dL/dcs, the explicit dL/ddt, two per-tile shares and dA's per-chunk share
+    # gradients, dL/dcs, the explicit dL/ddt, the cross-block pair sums (Q/64 planes), two
+    # per-tile shares and dA's per-chunk share
     assert binding.ssd_bwd_workspace_size(d, 256) == \
-        4 * chunk + 3 * state + 2 * tiles + per_chunk
+        4 * chunk + 3 * state + (256 // 64) * chunk + 2 * tiles + per_chunk
     assert binding.ssd_bwd_workspace_size(D(h=3, g=2), 64) == 0
     assert binding.ssd_bwd_workspace_size(D(t=0), 64) == 0
 
@@ -192,3 +193,58 @@ def test_bwd_validation_errors_before_any_launch(lib):
     assert _bwd(lib, D(), ptrs=dict(ws=None)) == 5
     assert _bwd(lib, D(), ws_bytes=100) == 5
     assert lib.ssd_bwd(None, 0, *[None] * 6, 64, *[None] * 11, 0, None) == 1
+
+
+def test_block_fwd_workspace_size(lib):
+    d = D(4, 4096, 80, 64, 128, 1)
+    bt = 4 * 4096
+
+    def r(v):
+        return (v + 255) // 256 * 256
+    # x, y, B, C (bf16), dt (fp32), then ssd_fwd's workspace
+    fwd = binding.ssd_fwd_workspace_size(d, 256)
+    assert binding.ssd_block_fwd_workspace_size(d, binding.SSD_BF16, 256) == \
+        2 * r(bt * 80 * 64 * 2) + 2 * r(bt * 128 * 2) + r(bt * 80 * 4) + r(fwd)
+    assert binding.ssd_block_fwd_workspace_size(d, binding.SSD_F32, 256) == \
+        2 * r(bt * 80 * 64 * 4) + 2 * r(bt * 128 * 4) + r(bt * 80 * 4) + r(fwd)
+    assert binding.ssd_block_fwd_workspace_size(D(h=3, g=2), 0, 64) == 0
+    assert binding.ssd_block_fwd_workspace_size(d, 9, 256) == 0
+
+
+def test_block_validation_errors_before_any_launch(lib):
+    ok = ctypes.c_void_p(256)
+    dm = D(p=16, n=16, h=2)          # Cd = 2*16 + 2*16 = 64, width 2*32 + 32 + 2 = 98
+
+    def pro(d=dm, dtype=1, xs=64, k=4, ds=2, **p):
+        a = dict(xbc=ok, w=ok, b=None, dt=ok, bias=None, x=ok, B=ok, C=ok, dto=ok)
+        a.update({n: (None if v is None else ctypes.c_void_p(v)) for n, v in p.items()})
+        return lib.ssd_block_prologue(ctypes.byref(d), dtype, a["xbc"], xs, a["w"], a["b"], k,
+                                      a["dt"], ds, a["bias"], a["x"], a["B"], a["C"], a["dto"],
+                                      None)
+    assert pro(k=0) == 3 and pro(k=9) == 3 and pro(dtype=4) == 3
+    assert pro(xs=63) == 2 and pro(ds=1) == 2
+    assert pro(xbc=None) == 1 and pro(dto=None) == 1
+    assert pro(x=264) == 4 and pro(dto=258) == 4 and pro(xbc=257) == 4   # element alignment
+    assert pro(d=D(b=0)) == 0 and pro(d=D(t=0), xbc=None) == 0            # nothing to do
+    assert pro(d=D(h=3, g=2)) == 2
+
+    def epi(d=dm, dtype=1, zs=32, groups=1, rms=0, eps=1e-5, **p):
+        a = dict(y=ok, z=ok, w=ok, b=None, out=ok)
+        a.update({n: (None if v is None else ctypes.c_void_p(v)) for n, v in p.items()})
+        return lib.ssd_block_epilogue(ctypes.byref(d), dtype, a["y"], a["z"], zs, a["w"], a["b"],
+                                      groups, rms, ctypes.c_float(eps), a["out"], None)
+    assert epi(groups=0) == 2 and epi(groups=3) == 2 and epi(zs=31) == 2
+    assert epi(eps=-1.0) == 2 and epi(eps=float("nan")) == 2
+    assert epi(y=None) == 1 and epi(w=None) == 1
+    assert epi(out=264) == 4 and epi(z=257) == 4 and epi(w=258) == 4
+    assert epi(d=D(t=0), y=None) == 0
+
+    def blk(d=dm, dtype=1, k=4, q=64, groups=1, ws_bytes=1 << 30, **p):
+        a = dict(zx=ok, w=ok, A=ok, Dp=ok, nw=ok, out=ok, ws=ok)
+        a.update({n: (None if v is None else ctypes.c_void_p(v)) for n, v in p.items()})
+        return lib.ssd_block_fwd(ctypes.byref(d), dtype, a["zx"], a["w"], None, k, None, a["A"],
+                                 a["Dp"], q, None, a["nw"], None, groups, 0,
+                                 ctypes.c_float(1e-5), a["out"], None, a["ws"], ws_bytes, None)
+    assert blk(k=0) == 3 and blk(q=100) == 3 and blk(groups=5) == 2
+    assert blk(zx=None) == 1 and blk(A=None) == 1
+    assert blk(zx=264) == 4 and blk(ws=None) == 5 and blk(ws_bytes=100) == 5

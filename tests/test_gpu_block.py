@@ -1,0 +1,197 @@
+"""Parity of the block prologue, epilogue and whole block (through the C ABI) with the
+fp64 block oracle (oracle/block.py), on the GPU.
+
+Outputs are compared whole-tensor by rel-L2 at the layer's bounds: 1e-4 for fp32, 2e-2 for
+bf16 (fp32 arithmetic, outputs rounded once).  The cases cover:
+- conv widths 1..8;
+- ragged step counts across the 64-step tiles, and T = 1;
+- rows inside the wider projection output (strided) and contiguous rows;
+- head counts whose rows are not a multiple of 16 bytes (the element-wise path);
+- every register-residency variant of the normalisation, and the streaming one;
+- GroupNorm and RMS;
+- the whole block at small sizes and at the full model-shaped sizes.
+"""
+import numpy as np
+import pytest
+import torch
+
+from mamba_ssd_chunked_03_amd import binding
+from mamba_ssd_chunked_03_amd.workloads import (BLOCKS, STRESS, TINY_FP32, BlockCfg, Workload,
+                                                generate_block, variants)
+from oracle import block as ob
+from parity import TOL, np64, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    binding.library()
+    torch.cuda.init()
+    return torch.device("cuda:0")
+
+
+def _split(w, zx):
+    d = w.nheads * w.headdim
+    gn = w.ngroups * w.dstate
+    return zx[:, :, :d], zx[:, :, d:2 * d + 2 * gn], zx[:, :, 2 * d + 2 * gn:]
+
+
+def _check(name, got, ref, dtype):
+    e = rel_l2(np64(got), ref)
+    say(f"    {name}: rel_l2 {e:.2e}")
+    assert e <= TOL[dtype], f"{name}: rel_l2 {e:.3e} > {TOL[dtype]}"
+
+
+PRO_CASES = [
+    (variants(TINY_FP32, name="pro_fp32_k4", seqlen=130), 4, True),
+    (variants(TINY_FP32, name="pro_fp32_k1", seqlen=17), 1, False),
+    (Workload("pro_bf16_k3", 2, 200, 4, 64, 64, 2, 64), 3, True),
+    (Workload("pro_bf16_k8_h3", 1, 70, 3, 32, 32, 1, 64), 8, True),    # rows not 16-byte
+    (Workload("pro_bf16_t1", 3, 1, 8, 64, 128, 1, 64), 4, True),
+    (Workload("pro_bf16_k2", 1, 129, 8, 16, 16, 4, 64), 2, False),
+]
+
+
+@pytest.mark.parametrize("w,k,strided", PRO_CASES, ids=[c[0].name for c in PRO_CASES])
+def test_prologue_matches_oracle(w, k, strided):
+    say(f"[prologue] {w.describe()} K={k} strided={strided}")
+    cpu = generate_block(w, BlockCfg(conv_k=k))
+    z, xbc, dtr = _split(w, cpu["zxbcdt"])
+    dev = "cuda"
+    if strided:  # column ranges of the projection output, as the block passes them
+        zxd = cpu["zxbcdt"].to(dev)
+        _, xbc_d, dtr_d = _split(w, zxd)
+    else:
+        xbc_d, dtr_d = xbc.contiguous().to(dev), dtr.contiguous().to(dev)
+    g = binding.ssd_block_prologue(xbc_d, cpu["conv_w"].to(dev), cpu["conv_b"].to(dev), dtr_d,
+                                   cpu["dt_bias"].to(dev), w.nheads, w.headdim, w.dstate,
+                                   w.ngroups)
+    torch.cuda.synchronize()
+    ref = ob.block_prologue(np64(xbc), np64(cpu["conv_w"]), np64(cpu["conv_b"]), np64(dtr),
+                            np64(cpu["dt_bias"]), w.nheads, w.headdim, w.dstate, w.ngroups)
+    for n in ("x", "B", "C", "dt"):
+        _check(n, g[n], ref[n], w.dtype)
+
+
+def test_prologue_without_biases():
+    w = Workload("pro_nobias", 2, 100, 4, 32, 16, 2, 64)
+    cpu = generate_block(w, BlockCfg(conv_k=4))
+    _, xbc, dtr = _split(w, cpu["zxbcdt"])
+    dev = "cuda"
+    g = binding.ssd_block_prologue(xbc.contiguous().to(dev), cpu["conv_w"].to(dev), None,
+                                   dtr.contiguous().to(dev), None, w.nheads, w.headdim,
+                                   w.dstate, w.ngroups)
+    torch.cuda.synchronize()
+    ref = ob.block_prologue(np64(xbc), np64(cpu["conv_w"]), None, np64(dtr), None, w.nheads,
+                            w.headdim, w.dstate, w.ngroups)
+    for n in ("x", "B", "C", "dt"):
+        _check(n, g[n], ref[n], w.dtype)
+
+
+# (name, dtype, B, T, H, P, groups, rms, z row padding): group sizes reach every residency
+# variant (nv = 1, 2, 4, 8, 16 and streaming) and the element-wise path
+EPI_CASES = [
+    ("epi_bf16_g1", "bf16", 2, 37, 8, 64, 1, False, 0),       # gs 512: lpg 64, nv 1
+    ("epi_bf16_g1_rms", "bf16", 2, 37, 8, 64, 1, True, 0),
+    ("epi_bf16_h80", "bf16", 1, 9, 80, 64, 1, False, 0),      # gs 5120: nv 10 (16)
+    ("epi_bf16_stream", "bf16", 1, 5, 136, 64, 1, False, 0),  # gs 8704: nv 17, streaming
+    ("epi_bf16_g8", "bf16", 2, 33, 8, 64, 8, False, 0),       # gs 64: lpg 8
+    ("epi_bf16_g4_rms", "bf16", 1, 20, 12, 32, 4, True, 0),   # gs 96: lpg 4, nv 3 (4)
+    ("epi_bf16_hp_g2", "bf16", 1, 11, 16, 64, 2, False, 0),   # gs 512
+    ("epi_bf16_pad", "bf16", 2, 21, 4, 32, 2, False, 3),      # z rows not 16-byte
+    ("epi_fp32_g1", "fp32", 2, 19, 4, 64, 1, False, 0),       # gs 256: V 4, nv 1
+    ("epi_fp32_g2_rms", "fp32", 1, 40, 8, 64, 2, True, 0),
+    ("epi_fp32_pad", "fp32", 1, 13, 2, 16, 1, False, 1),      # element-wise path
+    ("epi_fp32_big", "fp32", 1, 4, 80, 64, 1, False, 0),      # gs 5120, V 4: nv 20, streaming
+]
+
+
+@pytest.mark.parametrize("case", EPI_CASES, ids=[c[0] for c in EPI_CASES])
+def test_epilogue_matches_oracle(case):
+    name, dtype, bz, T, H, P, groups, rms, pad = case
+    say(f"[epilogue] {case}")
+    d = H * P
+    g = torch.Generator().manual_seed(7)
+    td = torch.float32 if dtype == "fp32" else torch.bfloat16
+    y = torch.randn((bz, T, H, P), generator=g).to(td)
+    zw = torch.randn((bz, T, d + pad), generator=g).to(td)
+    z = zw[:, :, :d]
+    nw = 1 + 0.1 * torch.randn(d, generator=g)
+    nb = 0.1 * torch.randn(d, generator=g)
+    dev = "cuda"
+    out = binding.ssd_block_epilogue(y.to(dev), zw.to(dev)[:, :, :d], nw.to(dev), nb.to(dev),
+                                     groups, rms=rms, eps=1e-5)
+    torch.cuda.synchronize()
+    ref = ob.gate_norm(np64(y), np64(z), np64(nw), np64(nb), groups, rms=rms, eps=1e-5)
+    _check("out", out, ref, dtype)
+
+
+BLOCK_CASES = [
+    (variants(TINY_FP32, name="blk_fp32", seqlen=200), BlockCfg(conv_k=4, norm_groups=2)),
+    (variants(STRESS["slow_decay"], name="blk_bf16_slow"), BlockCfg(conv_k=4, norm_groups=1)),
+    (Workload("blk_bf16_g2_rms", 2, 300, 8, 64, 64, 2, 128, init_state=True),
+     BlockCfg(conv_k=3, norm_groups=4, rms=True)),
+    (Workload("blk_bf16_h2", 1, 77, 2, 64, 128, 1, 64), BlockCfg(conv_k=4)),  # rows not 16B
+]
+
+
+def _run_block(w, cfg, cpu):
+    dev = "cuda"
+    d = {k: (None if v is None else v.to(dev)) for k, v in cpu.items()}
+    out, fin = binding.ssd_block_fwd(d["zxbcdt"], d["conv_w"], d["conv_b"], d["dt_bias"],
+                                     d["A"], d["D"], w.chunk_len, d["norm_w"], d["norm_b"],
+                                     cfg.norm_groups, w.headdim, w.dstate, w.ngroups,
+                                     rms=cfg.rms, eps=cfg.eps, init_state=d["init_state"])
+    torch.cuda.synchronize()
+    return out, fin
+
+
+def _oracle_block(w, cfg, cpu):
+    return ob.block_fwd(np64(cpu["zxbcdt"]), np64(cpu["conv_w"]), np64(cpu["conv_b"]),
+                        np64(cpu["dt_bias"]), np64(cpu["A"]), np64(cpu["D"]),
+                        np64(cpu["norm_w"]), np64(cpu["norm_b"]), w.nheads, w.headdim,
+                        w.dstate, w.ngroups, cfg.norm_groups, rms=cfg.rms, eps=cfg.eps,
+                        init_state=np64(cpu["init_state"]))
+
+
+@pytest.mark.parametrize("w,cfg", BLOCK_CASES, ids=[c[0].name for c in BLOCK_CASES])
+def test_block_matches_oracle(w, cfg):
+    say(f"[block] {w.describe()} {cfg}")
+    cpu = generate_block(w, cfg)
+    out, fin = _run_block(w, cfg, cpu)
+    ref_out, ref_fin = _oracle_block(w, cfg, cpu)
+    _check("out", out, ref_out, w.dtype)
+    _check("final_state", fin, ref_fin, w.dtype)
+
+
+@pytest.mark.parametrize("name", list(BLOCKS))
+def test_block_full_size(name):
+    """The model-shaped blocks at full size, in the launch configuration that
+    bench.py --block times, compared whole-tensor."""
+    w, cfg = BLOCKS[name]
+    say(f"[block full] {w.describe()} {cfg}")
+    cpu = generate_block(w, cfg)
+    out, fin = _run_block(w, cfg, cpu)
+    ref_out, ref_fin = _oracle_block(w, cfg, cpu)
+    _check("out", out, ref_out, w.dtype)
+    _check("final_state", fin, ref_fin, w.dtype)
+
+
+def test_block_empty_sequence():
+    """T = 0: nothing to compute; final_state = init_state."""
+    w = Workload("blk_empty", 2, 0, 4, 32, 16, 1, 64, init_state=True)
+    cfg = BlockCfg()
+    cpu = generate_block(w, cfg)
+    out, fin = _run_block(w, cfg, cpu)
+    assert out.shape == (2, 0, 128)
+    assert torch.equal(fin.cpu(), cpu["init_state"])
+
+
+def test_block_is_deterministic():
+    w, cfg = BLOCK_CASES[2]
+    cpu = generate_block(w, cfg)
+    a, fa = _run_block(w, cfg, cpu)
+    b, fb = _run_block(w, cfg, cpu)
+    assert torch.equal(a, b) and torch.equal(fa, fb)
