@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--decode", default="", metavar="WORKLOAD",
                     help="instead of the forward, time ssd_decode_step on a decode workload "
                          "(one token per sequence per step) and print its own JSON line")
+    ap.add_argument("--block", default="", metavar="BLOCK",
+                    help="time the block between the projections (ssd_block_fwd: prologue, "
+                         "ssd_fwd, epilogue) on a model-shaped block (block_2p7b, block_130m)")
     ap.add_argument("--bwd", default="", metavar="WORKLOAD",
                     help="instead of the forward, time the backward (ssd_bwd) on a workload and "
                          "print its own JSON line")
@@ -203,6 +206,98 @@ def bench_bwd(args, w, torch, binding, roofline, generate, generate_grads):
         "alg_bytes_total": int(tot_bytes), "alg_flops_total": int(tot_flops),
     }), flush=True)
 
+def bench_block(args, w, cfg, torch, binding, roofline, generate_block):
+    """Whole ssd_block_fwd calls back to back: tokens/s = B*T / call time.  A staged pass
+    makes the same three calls (prologue, ssd_fwd, epilogue) with HIP events between them
+    for the block kernels' durations; the roofline is the slower block kernel's (the SSD
+    layer's own kernels have theirs in the default run)."""
+    dev = torch.device("cuda:0")
+    log(f"[bench block] {w.describe()} {cfg}")
+    cpu = generate_block(w, cfg)
+    d = {k: (None if v is None else v.to(dev)) for k, v in cpu.items()}
+    dims = binding.SsdDims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups)
+    code = binding.SSD_BF16 if w.dtype == "bf16" else binding.SSD_F32
+    ws = torch.empty(binding.ssd_block_fwd_workspace_size(dims, code, w.chunk_len),
+                     dtype=torch.uint8, device=dev)
+    H, P, N, G = w.nheads, w.headdim, w.dstate, w.ngroups
+    hp, gn = H * P, G * N
+    out = torch.empty((w.batch, w.seqlen, hp), dtype=d["zxbcdt"].dtype, device=dev)
+    fin = torch.empty((w.batch, H, N, P), dtype=torch.float32, device=dev)
+
+    def step():
+        binding.ssd_block_fwd(d["zxbcdt"], d["conv_w"], d["conv_b"], d["dt_bias"], d["A"],
+                              d["D"], w.chunk_len, d["norm_w"], d["norm_b"], cfg.norm_groups,
+                              P, N, G, rms=cfg.rms, eps=cfg.eps, init_state=d["init_state"],
+                              out=out, final_state=fin, workspace=ws)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # staged: the same three calls with events between them
+    zx = d["zxbcdt"]
+    x = torch.empty((w.batch, w.seqlen, H, P), dtype=zx.dtype, device=dev)
+    Bm = torch.empty((w.batch, w.seqlen, G, N), dtype=zx.dtype, device=dev)
+    Cm = torch.empty_like(Bm)
+    dt = torch.empty((w.batch, w.seqlen, H), dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    fws = torch.empty(binding.ssd_fwd_workspace_size(dims, w.chunk_len), dtype=torch.uint8,
+                      device=dev)
+    out2 = torch.empty_like(out)
+    names = ["block_prologue", "ssd_fwd", "block_epilogue"]
+    per = {n: 0.0 for n in names}
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for ev in evs:  # back to back, one synchronisation at the end
+        ev[0].record()
+        binding.ssd_block_prologue(zx[:, :, hp:2 * hp + 2 * gn], d["conv_w"], d["conv_b"],
+                                   zx[:, :, 2 * hp + 2 * gn:], d["dt_bias"], H, P, N, G,
+                                   x=x, B=Bm, C=Cm, dt=dt)
+        ev[1].record()
+        binding.ssd_fwd(x, dt, d["A"], Bm, Cm, d["D"], w.chunk_len, init_state=d["init_state"],
+                        y=y, final_state=fin, workspace=fws)
+        ev[2].record()
+        binding.ssd_block_epilogue(y, zx[:, :, :hp], d["norm_w"], d["norm_b"], cfg.norm_groups,
+                                   rms=cfg.rms, eps=cfg.eps, dstate=N, ngroups=G, out=out2)
+        ev[3].record()
+    torch.cuda.synchronize()
+    for ev in evs:
+        for i, n in enumerate(names):
+            per[n] += ev[i].elapsed_time(ev[i + 1]) / args.steps
+    if not torch.equal(out2, ref):
+        log("[bench block] WARNING: staged calls and ssd_block_fwd differ")
+    costs = {c.name: c for c in roofline.block_costs(w.batch, w.seqlen, H, P, N, G, cfg.conv_k,
+                                                     w.dtype, norm_bias=not cfg.rms)}
+    kernels = {}
+    for n in names:
+        kernels[n] = {"avg_us": round(per[n] * 1e3, 2)}
+        if n in costs:
+            t = per[n] * 1e-3
+            gbs = costs[n].bytes / t / 1e9
+            kernels[n].update(alg_bytes=int(costs[n].bytes), alg_flops=int(costs[n].flops),
+                              hbm_GBps=round(gbs, 1),
+                              hbm_frac=round(gbs / roofline.PEAK_HBM_GBPS, 4))
+    dom = max(costs, key=lambda n: per[n])
+    ms_step = elapsed / args.steps * 1e3
+    print(json.dumps({
+        "metric": "Mamba-2 block (between the projections) tokens/sec on 1 MI355X",
+        "value": round(w.tokens / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": args.block, "batch": w.batch, "seqlen": w.seqlen, "nheads": H,
+                   "headdim": P, "dstate": N, "ngroups": G, "chunk_len": w.chunk_len,
+                   "conv_k": cfg.conv_k, "norm_groups": cfg.norm_groups, "rms": cfg.rms,
+                   "input_dtype": w.dtype},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["hbm_GBps"],
+                     "peak": roofline.PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": kernels[dom]["hbm_frac"], "traffic": None},
+        "kernels": kernels,
+    }), flush=True)
+
 
 def main():
     args = parse()
@@ -224,7 +319,11 @@ def main():
                           "read_bytes_per_copy": 4 * n, "write_bytes_per_copy": 4 * n}))
         return
     from mamba_ssd_chunked_03_amd import binding, roofline, traffic
-    from mamba_ssd_chunked_03_amd.workloads import DECODE, WORKLOADS, generate, generate_grads
+    from mamba_ssd_chunked_03_amd.workloads import (BLOCKS, DECODE, WORKLOADS, generate,
+                                                    generate_block, generate_grads)
+    if args.block:
+        w, cfg = BLOCKS[args.block]
+        return bench_block(args, w, cfg, torch, binding, roofline, generate_block)
     if args.decode:
         return bench_decode(args, DECODE[args.decode], torch, binding, roofline, generate)
     if args.bwd:

@@ -10,13 +10,14 @@
 // depthwise, one-dimensional, of width 3-4.
 //
 // Both kernels are HBM-bound streams (a few flops per byte):
-//   block_prologue_kernel: one thread per 16-byte vector of channels and 64 consecutive
-//     steps of one sequence.  It walks the steps in batches of 8 loads, keeps the K - 1
-//     previous inputs in registers (the causal window), and writes the SiLU'd result
+//   block_prologue_kernel: one thread per 16-byte vector of channels and 32 consecutive
+//     steps of one sequence.  It walks the steps in batches of 8 loads (the next batch in
+//     flight while the current one is computed), keeps the K - 1 previous inputs in
+//     registers (the causal window), and writes the SiLU'd result
 //     straight into x, B or C (a vector never straddles two of them: H*P and G*N are
-//     multiples of 16).  One extra workgroup column turns dt_raw into softplus(dt_raw +
-//     bias) for the same steps.  Every input byte is read once (plus the K - 1 step halo of
-//     each 64-step tile) and every output byte written once.
+//     multiples of 16).  The tile's threads also turn dt_raw into softplus(dt_raw + bias)
+//     for the same steps, a few independent elements each.  Every input byte is read once
+//     (plus the K - 1 step halo of each 32-step tile) and every output byte written once.
 //   block_epilogue_kernel: a team of lanes (a power of two up to a wave) per (token,
 //     normalisation group).  Its lanes read consecutive 16-byte vectors of y and z, form
 //     y * silu(z) in registers, reduce the mean and then the squared deviations across the
@@ -34,7 +35,7 @@ using mfma::exp2_fast;
 using mfma::kLog2e;
 using mfma::pack_bf16;
 
-constexpr int kPrologueTile = 64;  // steps per prologue thread
+constexpr int kPrologueTile = 32;  // steps per prologue thread
 
 __device__ __forceinline__ float sigmoid_fast(float v) {
     // 1 / (1 + exp(-v)); exp overflows to +inf for v < -88 and the reciprocal gives 0
@@ -56,9 +57,12 @@ __device__ __forceinline__ void load_vec(const T* p, float (&o)[V]) {
             o[2 * i] = bf16_lo(w[i]);
             o[2 * i + 1] = bf16_hi(w[i]);
         }
-    } else if constexpr (V == 4 && sizeof(T) == 4) {
-        const float4 u = *reinterpret_cast<const float4*>(p);
-        o[0] = u.x; o[1] = u.y; o[2] = u.z; o[3] = u.w;
+    } else if constexpr (V % 4 == 0 && sizeof(T) == 4) {
+#pragma unroll
+        for (int q = 0; q < V / 4; ++q) {
+            const float4 u = *reinterpret_cast<const float4*>(p + 4 * q);
+            o[4 * q] = u.x; o[4 * q + 1] = u.y; o[4 * q + 2] = u.z; o[4 * q + 3] = u.w;
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < V; ++i) o[i] = to_f32(p[i]);
@@ -77,37 +81,112 @@ __device__ __forceinline__ void store_vec(T* p, const float (&o)[V]) {
     }
 }
 
-// grid: x = ceil(ncv / 64) conv columns + 1 step-size column, y = B * ceil(T / 64)
-template <typename T, int V, int K>
-__global__ __launch_bounds__(64) void block_prologue_kernel(
-    const T* __restrict__ xbc, long long xstride, const float* __restrict__ w,
-    const float* __restrict__ cb, const T* __restrict__ dt_raw, long long dstride,
-    const float* __restrict__ dt_bias, T* __restrict__ xo, T* __restrict__ bo,
-    T* __restrict__ co, float* __restrict__ dto, int Tn, int H, int d, int gn, int ntile) {
-    const int b = blockIdx.y / ntile;
-    const int t0 = (blockIdx.y % ntile) * kPrologueTile;
-    const int tend = min(t0 + kPrologueTile, Tn);
-    if ((int)blockIdx.x == (int)gridDim.x - 1) {  // the step sizes of these steps
-        const int n = (tend - t0) * H;
-        for (int e = threadIdx.x; e < n; e += 64) {
-            const int t = t0 + e / H, h = e % H;
-            float v = to_f32(dt_raw[((long long)b * Tn + t) * dstride + h]);
-            if (dt_bias) v += dt_bias[h];
-            dto[((long long)b * Tn + t) * H + h] = softplus_f(v);
+// The raw 16-byte (or element) load of V values, unpacked to floats when used
+template <typename T, int V>
+struct Raw {
+    T v[V];
+};
+template <>
+struct Raw<__bf16, 8> {
+    uint4 u;
+};
+template <>
+struct Raw<float, 4> {
+    float4 u;
+};
+template <typename T, int V>
+__device__ __forceinline__ Raw<T, V> load_raw(const T* p) {
+    Raw<T, V> r;
+    if constexpr (V == 8 && sizeof(T) == 2) {
+        r.u = *reinterpret_cast<const uint4*>(p);
+    } else if constexpr (V == 4 && sizeof(T) == 4) {
+        r.u = *reinterpret_cast<const float4*>(p);
+    } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) r.v[i] = p[i];
+    }
+    return r;
+}
+template <typename T, int V>
+__device__ __forceinline__ void unpack(const Raw<T, V>& r, float (&o)[V]) {
+    if constexpr (V == 8 && sizeof(T) == 2) {
+        const uint32_t w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = bf16_lo(w[i]);
+            o[2 * i + 1] = bf16_hi(w[i]);
         }
-        return;
-    }
-    const int ncv = (d + 2 * gn) / V;
-    const int cv = blockIdx.x * 64 + threadIdx.x;
-    if (cv >= ncv) return;
-    const int c0 = cv * V;
-    float wr[K][V], bias[V];
+    } else if constexpr (V == 4 && sizeof(T) == 4) {
+        o[0] = r.u.x; o[1] = r.u.y; o[2] = r.u.z; o[3] = r.u.w;
+    } else {
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-        bias[i] = cb ? cb[c0 + i] : 0.f;
-#pragma unroll
-        for (int k = 0; k < K; ++k) wr[k][i] = w[(c0 + i) * K + k];
+        for (int i = 0; i < V; ++i) o[i] = to_f32(r.v[i]);
     }
+}
+
+// One thread's steps [t0, tend) of one channel vector: batches of 8 steps, the loads of
+// batch i + 1 issued before batch i is computed, in two buffers whose roles alternate at
+// compile time (the batch loop is unrolled, so no register copies make a batch wait for
+// its successor's loads).  FULL: tend - t0 == kPrologueTile, no bounds tests.
+template <typename T, int V, int K, bool FULL>
+__device__ __forceinline__ void prologue_tile(const T* src, long long xstride, T* dst,
+                                              int dstride_o, int t0, int tend,
+                                              const float (&wr)[K][V], const float (&bias)[V]) {
+    constexpr int NB = kPrologueTile / 8;
+    Raw<T, V> buf[2][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (FULL || t0 + j < tend) buf[0][j] = load_raw<T, V>(src + (long long)(t0 + j) * xstride);
+    // win[0 .. K-2]: the K - 1 steps before the next output step; win[K-1]: that step
+    float win[K][V];
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k) {
+        const int t = t0 - (K - 1) + k;
+        if (t >= 0) {
+            unpack<T, V>(load_raw<T, V>(src + (long long)t * xstride), win[k]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < V; ++i) win[k][i] = 0.f;
+        }
+    }
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi) {
+        const int tb = t0 + 8 * bi;
+        if (!FULL && tb >= tend) break;
+        if (bi + 1 < NB) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (FULL || tb + 8 + j < tend)
+                    buf[(bi + 1) & 1][j] = load_raw<T, V>(src + (long long)(tb + 8 + j) * xstride);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (FULL || tb + j < tend) {
+                unpack<T, V>(buf[bi & 1][j], win[K - 1]);
+                float o[V];
+#pragma unroll
+                for (int i = 0; i < V; ++i) {
+                    float a = bias[i];
+#pragma unroll
+                    for (int k = 0; k < K; ++k) a = fmaf(wr[k][i], win[k][i], a);
+                    o[i] = silu_f(a);
+                }
+                store_vec<T, V>(dst + (long long)(tb + j) * dstride_o, o);
+#pragma unroll
+                for (int k = 0; k < K - 1; ++k)
+#pragma unroll
+                    for (int i = 0; i < V; ++i) win[k][i] = win[k + 1][i];
+            }
+        }
+    }
+}
+
+template <typename T, int V, int K>
+__device__ __forceinline__ void prologue_conv(const T* __restrict__ xbc, long long xstride,
+                                              const float* __restrict__ w,
+                                              const float* __restrict__ cb, T* __restrict__ xo,
+                                              T* __restrict__ bo, T* __restrict__ co, int b,
+                                              int Tn, int d, int gn, int t0, int tend, int c0) {
     T* dst;
     int dstride_o;
     if (c0 < d) {
@@ -122,46 +201,52 @@ __global__ __launch_bounds__(64) void block_prologue_kernel(
     }
     const T* src = xbc + (long long)b * Tn * xstride + c0;
     dst += (long long)b * Tn * dstride_o;
-    // ext[0 .. K-2]: the K - 1 steps before the batch; ext[K-1 + i]: step tb + i
-    float ext[K - 1 + 8][V];
+    float wr[K][V], bias[V];
 #pragma unroll
-    for (int k = 0; k < K - 1; ++k) {
-        const int t = t0 - (K - 1) + k;
-        if (t >= 0) {
-            load_vec<T, V>(src + (long long)t * xstride, ext[k]);
-        } else {
+    for (int i = 0; i < V; ++i) {
+        bias[i] = cb ? cb[c0 + i] : 0.f;
 #pragma unroll
-            for (int i = 0; i < V; ++i) ext[k][i] = 0.f;
-        }
+        for (int k = 0; k < K; ++k) wr[k][i] = w[(c0 + i) * K + k];
     }
-    for (int tb = t0; tb < tend; tb += 8) {
+    if (tend - t0 == kPrologueTile)
+        prologue_tile<T, V, K, true>(src, xstride, dst, dstride_o, t0, tend, wr, bias);
+    else
+        prologue_tile<T, V, K, false>(src, xstride, dst, dstride_o, t0, tend, wr, bias);
+}
+
+// grid: x = ceil(ncv / 64) conv columns, y = B * ceil(T / kPrologueTile); the step sizes
+// of a tile are spread over all of its threads (a few independent loads each).
+template <typename T, int V, int K>
+__global__ __launch_bounds__(64) void block_prologue_kernel(
+    const T* __restrict__ xbc, long long xstride, const float* __restrict__ w,
+    const float* __restrict__ cb, const T* __restrict__ dt_raw, long long dstride,
+    const float* __restrict__ dt_bias, T* __restrict__ xo, T* __restrict__ bo,
+    T* __restrict__ co, float* __restrict__ dto, int Tn, int H, int d, int gn, int ntile) {
+    const int b = blockIdx.y / ntile;
+    const int t0 = (blockIdx.y % ntile) * kPrologueTile;
+    const int tend = min(t0 + kPrologueTile, Tn);
+    const int ncv = (d + 2 * gn) / V;
+    const int cv = blockIdx.x * 64 + threadIdx.x;
+    if (cv < ncv)
+        prologue_conv<T, V, K>(xbc, xstride, w, cb, xo, bo, co, b, Tn, d, gn, t0, tend, cv * V);
+    // the step sizes of these steps, spread over the tile's threads: all loads first
+    const int n = (tend - t0) * H, nthr = gridDim.x * 64;
+    for (int e0 = cv; e0 < n; e0 += 8 * nthr) {
+        float v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (tb + j < tend) {
-                load_vec<T, V>(src + (long long)(tb + j) * xstride, ext[K - 1 + j]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < V; ++i) ext[K - 1 + j][i] = 0.f;
-            }
+        for (int q = 0; q < 8; ++q) {
+            const int e = e0 + q * nthr;
+            v[q] = e < n ? to_f32(dt_raw[((long long)b * Tn + t0 + e / H) * dstride + e % H]) : 0.f;
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (tb + j < tend) {
-                float o[V];
-#pragma unroll
-                for (int i = 0; i < V; ++i) {
-                    float a = bias[i];
-#pragma unroll
-                    for (int k = 0; k < K; ++k) a = fmaf(wr[k][i], ext[j + k][i], a);
-                    o[i] = silu_f(a);
-                }
-                store_vec<T, V>(dst + (long long)(tb + j) * dstride_o, o);
+        for (int q = 0; q < 8; ++q) {
+            const int e = e0 + q * nthr;
+            if (e < n) {
+                const int h = e % H;
+                const float u = dt_bias ? v[q] + dt_bias[h] : v[q];
+                dto[((long long)b * Tn + t0 + e / H) * H + h] = softplus_f(u);
             }
         }
-#pragma unroll
-        for (int k = 0; k < K - 1; ++k)
-#pragma unroll
-            for (int i = 0; i < V; ++i) ext[k][i] = ext[8 + k][i];
     }
 }
 
@@ -199,14 +284,20 @@ __global__ __launch_bounds__(256) void block_epilogue_kernel(
 #pragma unroll
         for (int k = 0; k < V; ++k) v[k] *= silu_f(zv[k]);
     };
+    const bool shift = nb && !rms;
     auto emit = [&](int i, const float (&v)[V], float mean, float rstd) {
         const int c = (i * lpg + tl) * V;
+        float wv[V], bv[V];
+        load_vec<float, V>(nw + cbase + c, wv);
+        if (shift) {
+            load_vec<float, V>(nb + cbase + c, bv);
+        } else {
+#pragma unroll
+            for (int k = 0; k < V; ++k) bv[k] = 0.f;
+        }
         float o[V];
 #pragma unroll
-        for (int k = 0; k < V; ++k) {
-            o[k] = (v[k] - mean) * rstd * nw[cbase + c + k];
-            if (nb && !rms) o[k] += nb[cbase + c + k];
-        }
+        for (int k = 0; k < V; ++k) o[k] = fmaf((v[k] - mean) * rstd, wv[k], bv[k]);
         store_vec<T, V>(orow + c, o);
     };
     if constexpr (NVMAX > 0) {
@@ -266,7 +357,7 @@ hipError_t launch_prologue_k(const Shape& s, const BlockPrologueArgs& a, hipStre
     const int d = s.H * s.P, gn = s.G * s.N;
     const int ncv = (d + 2 * gn) / V;
     const int ntile = (s.T + kPrologueTile - 1) / kPrologueTile;
-    const dim3 grid((unsigned)((ncv + 63) / 64 + 1), (unsigned)(s.B * ntile));
+    const dim3 grid((unsigned)((ncv + 63) / 64), (unsigned)(s.B * ntile));
     block_prologue_kernel<T, V, K><<<grid, 64, 0, st>>>(
         (const T*)a.xbc, a.xbc_stride, a.conv_w, a.conv_b, (const T*)a.dt_raw, a.dt_stride,
         a.dt_bias, (T*)a.x, (T*)a.Bm, (T*)a.Cm, a.dt, s.T, s.H, d, gn, ntile);
@@ -310,7 +401,10 @@ hipError_t launch_epilogue_v(const Shape& s, const BlockEpilogueArgs& a, hipStre
     if (nv <= 1) return launch_epilogue_n<T, V, 1>(s, a, lpg, nv, st);
     if (nv <= 2) return launch_epilogue_n<T, V, 2>(s, a, lpg, nv, st);
     if (nv <= 4) return launch_epilogue_n<T, V, 4>(s, a, lpg, nv, st);
+    if (nv <= 6) return launch_epilogue_n<T, V, 6>(s, a, lpg, nv, st);
     if (nv <= 8) return launch_epilogue_n<T, V, 8>(s, a, lpg, nv, st);
+    if (nv <= 10) return launch_epilogue_n<T, V, 10>(s, a, lpg, nv, st);
+    if (nv <= 12) return launch_epilogue_n<T, V, 12>(s, a, lpg, nv, st);
     if (nv <= 16) return launch_epilogue_n<T, V, 16>(s, a, lpg, nv, st);
     return launch_epilogue_n<T, V, 0>(s, a, lpg, nv, st);
 }

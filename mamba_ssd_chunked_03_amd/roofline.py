@@ -108,3 +108,27 @@ def bwd_costs(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len, dtype=
                        B * H * (2.0 * tri * P + 6.0 * T * N * P) + 3.0 * B * G * tri * N)
     fin = KernelCost("bwd_finalize", 3 * chunk_f32 + B * T * H * 4 + 2 * H * 4, 4.0 * B * T * H)
     return [cumsum, state, passing, dstate, rpass, chunk, fin]
+
+
+def block_costs(batch, seqlen, nheads, headdim, dstate, ngroups, conv_k, dtype="bf16",
+                norm_bias=True):
+    """The block's own kernels around the layer.
+
+    block_prologue: reads the x|B|C columns (Cd = H*P + 2*G*N per token) and dt_raw of the
+      projection output plus the filters; writes x, B, C in dtype and dt in fp32.  FLOPs per
+      channel element: 2K for the filter and 4 for SiLU (exp, add, reciprocal, multiply);
+      per step size 4 (softplus and the bias).
+    block_epilogue: reads y and z (H*P per token) and the scale/shift; writes out.  FLOPs
+      per element: 5 for the gate (SiLU and the product), 3 for the two reductions, 3 to
+      normalise and scale (4 with the shift)."""
+    e = 2 if dtype == "bf16" else 4
+    bt = batch * seqlen
+    d = nheads * headdim
+    cd = d + 2 * ngroups * dstate
+    pro = KernelCost("block_prologue",
+                     bt * cd * e * 2 + bt * nheads * (e + 4) + cd * (conv_k + 1) * 4 + nheads * 4,
+                     bt * cd * (2.0 * conv_k + 4) + 4.0 * bt * nheads)
+    epi = KernelCost("block_epilogue",
+                     3 * bt * d * e + (2 if norm_bias else 1) * d * 4,
+                     bt * d * (11.0 + (1 if norm_bias else 0)))
+    return [pro, epi]
