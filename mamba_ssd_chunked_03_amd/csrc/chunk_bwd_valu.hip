@@ -28,7 +28,8 @@
 //     Per head it forms the row strip W[j][i] (i <= j) and the column strip V[t][j]
 //     (t >= j) of the decayed M for j in J, the dx weights U[t][j] = exp(cs_t - cs_j) G[t][j],
 //     and from them dx (written per head), the dB/dC contributions and dL/dcs, direct.
-//   bwd_ddt_kernel: one wave per (b, h, chunk): the suffix sums R, ddt and dA's share.
+//   bwd_ddt_kernel: one wave per (b, h, chunk), a workgroup per 16 heads of a (b, chunk):
+//     the suffix sums R, ddt (written as runs of consecutive heads) and dA's share.
 //   bwd_param_kernel: one workgroup per head: dA and dD summed over batch and chunks in a
 //     fixed order (results do not depend on scheduling).
 #include "ssd_internal.h"
@@ -265,101 +266,140 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_valu_kernel(
 // rp_k = sum_{s < blk(k)} xs[1 + s][k]   (row k with the columns of earlier blocks)
 // cp_k = xs[0][k], CP[Jb] = sum_{k in Jb} cp_k   (column k with the rows of later blocks)
 // K[Jb] = sum_{s < Jb} sum_{k >= 64 (Jb + 1)} xs[1 + s][k]   (later rows, earlier columns)
-__global__ __launch_bounds__(kThreads) void bwd_ddt_kernel(
+// L consecutive floats (L = 1, 2, 4) at a 4L-byte aligned address
+template <int L>
+__device__ __forceinline__ void load_run(const float* p, float (&o)[4]) {
+    if constexpr (L == 4) {
+        const float4 u = *reinterpret_cast<const float4*>(p);
+        o[0] = u.x; o[1] = u.y; o[2] = u.z; o[3] = u.w;
+    } else if constexpr (L == 2) {
+        const float2 u = *reinterpret_cast<const float2*>(p);
+        o[0] = u.x; o[1] = u.y; o[2] = o[3] = 0.f;
+    } else {
+        o[0] = p[0]; o[1] = o[2] = o[3] = 0.f;
+    }
+}
+
+constexpr int kDdtHeads = 16;  // heads per workgroup of the ddt kernel, one wave each
+constexpr int kDdtThreads = 64 * kDdtHeads;
+
+// One workgroup per (b, chunk, block of 16 heads); a wave per head, a lane L = Q/64
+// consecutive positions (each wave's work is a chain of dependent cross-lane scans: many
+// waves hide it).  The ddt rows of the block's heads are staged in LDS and
+// written as 64-byte runs of consecutive heads ([B][T][H] is head-minor).
+template <int Q>
+__global__ __launch_bounds__(kDdtThreads) void bwd_ddt_kernel(
     const float* __restrict__ dcs, const float* __restrict__ direct,
-    const float* __restrict__ xs, const float* __restrict__ lt_part, const float* __restrict__ dtc, const float* __restrict__ A,
-    float* __restrict__ ddt, float* __restrict__ dA_part, int T, int H, int Q, int nC,
-    int rows, int items) {
-    const int item = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-    if (item >= items) return;
-    const int lane = threadIdx.x & 63;
-    const int c = item % nC, bh = item / nC;
-    const int h = bh % H, b = bh / H;
-    const size_t cb = (size_t)item * Q;
+    const float* __restrict__ xs, const float* __restrict__ lt_part,
+    const float* __restrict__ dtc, const float* __restrict__ A, float* __restrict__ ddt,
+    float* __restrict__ dA_part, int T, int H, int nC, int rows) {
+    constexpr int L = Q / 64;           // positions per lane, consecutive
+    constexpr int NJ = Q / 64, lpb = 64 / L;  // 64-row blocks, lanes per block
+    __shared__ float tile[Q][kDdtHeads + 1];
+    const int hblocks = (H + kDdtHeads - 1) / kDdtHeads;
+    const int hb = blockIdx.x % hblocks;
+    const int bc = blockIdx.x / hblocks;
+    const int c = bc % nC, b = bc / nC;
+    const int h0 = hb * kDdtHeads, nh = min(kDdtHeads, H - h0);
     const int Lc = min(Q, T - c * Q);
     const int ntiles = Q / rows;
     const int nvalid = (Lc + rows - 1) / rows;
-    float lt = 0.f;
-    for (int k = 0; k < nvalid; ++k) lt += lt_part[(size_t)item * ntiles + k];
-
-    const int L = Q / 64;  // positions per lane, consecutive
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int k0 = lane * L;
-    float v[4];
-    float seg = 0.f;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        v[m] = (m < L && k0 + m < Lc) ? dcs[cb + k0 + m] : 0.f;
-        seg += v[m];
-    }
-    // inclusive suffix sum of the lanes' segment sums
-    float suf = seg;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const float up = __shfl_down(suf, o, 64);
-        if (lane + o < 64) suf += up;
-    }
-    float r = (suf - seg) + lt;
-    float bv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (xs) {
-        const int NJ = Q / 64, lpb = 64 / L;  // blocks, lanes per block
-        const int blk = lane / lpb;
-        const float* xr = xs + (size_t)item * NJ * Q;
-        float segb = 0.f, segcp = 0.f, ks = 0.f;
+    const int blk = lane / lpb, bend = (blk + 1) * lpb;
+    for (int hh = wave; hh < nh; hh += kDdtThreads / 64) {
+        const int h = h0 + hh;
+        const size_t item = ((size_t)b * H + h) * nC + c;
+        const size_t cb = item * Q;
+        float lt = 0.f;
+        for (int k = 0; k < nvalid; ++k) lt += lt_part[item * ntiles + k];
+        // positions past the chunk's end hold no results: zero them
+        auto valid = [&](int m) { return m < L && k0 + m < Lc; };
+        float v[4], dv[4], tv[4];
+        load_run<L>(dcs + cb + k0, v);
+        load_run<L>(direct + cb + k0, dv);
+        load_run<L>(dtc + cb + k0, tv);
+        float seg = 0.f;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const int k = k0 + m;
-            if (m < L && k < Lc) {
-                const float cp = xr[k];
-                float rp = 0.f;
-                for (int s = 0; s < blk; ++s) rp += xr[(size_t)(1 + s) * Q + k];
-                bv[m] = rp - cp;
-                segb += bv[m];
-                segcp += cp;
-            }
+            if (!valid(m)) v[m] = 0.f;
+            seg += v[m];
         }
-        // suffix of rp - cp within the block, and the block's total of cp
-        float sufb = segb;
-        const int bend = (blk + 1) * lpb;
+        // inclusive suffix sum of the lanes' segment sums
+        float suf = seg;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
-            const float up = __shfl_down(sufb, o, 64);
-            if (lane + o < bend) sufb += up;
+            const float up = __shfl_down(suf, o, 64);
+            if (lane + o < 64) suf += up;
         }
-        for (int o = 1; o < lpb; o <<= 1) segcp += __shfl_xor(segcp, o, 64);
-        // K: for each plane s, the suffix over the lanes after this block
-        for (int s = 0; s + 1 < NJ; ++s) {
-            float ps = 0.f;
-            if (blk > s) {
+        float r = (suf - seg) + lt;
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (xs) {
+            const float* xr = xs + item * NJ * Q;
+            float pl[NJ][4];  // plane 0: cp; plane 1 + s: row sums over block s
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int k = k0 + m;
-                    if (m < L && k < Lc) ps += xr[(size_t)(1 + s) * Q + k];
-                }
+            for (int s2 = 0; s2 < NJ; ++s2) load_run<L>(xr + (size_t)s2 * Q + k0, pl[s2]);
+            float segb = 0.f, segcp = 0.f;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                if (!valid(m)) continue;
+                float rp = 0.f;
+#pragma unroll
+                for (int s2 = 0; s2 + 1 < NJ; ++s2)
+                    if (s2 < blk) rp += pl[1 + s2][m];
+                bv[m] = rp - pl[0][m];
+                segb += bv[m];
+                segcp += pl[0][m];
             }
+            // suffix of rp - cp within the block, and the block's total of cp
+            float sufb = segb;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
-                const float up = __shfl_down(ps, o, 64);
-                if (lane + o < 64) ps += up;
+                const float up = __shfl_down(sufb, o, 64);
+                if (lane + o < bend) sufb += up;
             }
-            const float after = __shfl(ps, bend < 64 ? bend : 63, 64);
-            if (s < blk && bend < 64) ks += after;
-        }
-        r += (sufb - segb) + segcp + ks;
-    }
-    const float Ah = A[h];
-    float da = 0.f;
 #pragma unroll
-    for (int m = 3; m >= 0; --m) {
-        if (m >= L) continue;
-        r += v[m] + bv[m];
-        const int j = k0 + m;
-        if (j < Lc) {
-            ddt[((size_t)b * T + c * Q + j) * H + h] = direct[cb + j] + Ah * r;
-            da = fmaf(dtc[cb + j], r, da);
+            for (int o = 1; o < lpb; o <<= 1) segcp += __shfl_xor(segcp, o, 64);
+            // K: for each plane s, the suffix over the lanes after this block
+            float ks = 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 + 1 < NJ; ++s2) {
+                float ps = 0.f;
+                if (blk > s2) {
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        if (valid(m)) ps += pl[1 + s2][m];
+                }
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const float up = __shfl_down(ps, o, 64);
+                    if (lane + o < 64) ps += up;
+                }
+                const float after = __shfl(ps, bend < 64 ? bend : 63, 64);
+                if (s2 < blk && bend < 64) ks += after;
+            }
+            r += (sufb - segb) + segcp + ks;
         }
+        const float Ah = A[h];
+        float da = 0.f;
+#pragma unroll
+        for (int m = 3; m >= 0; --m) {
+            if (m >= L) continue;
+            r += v[m] + bv[m];
+            if (valid(m)) {
+                tile[k0 + m][hh] = dv[m] + Ah * r;
+                da = fmaf(tv[m], r, da);
+            }
+        }
+        da = sum64(da);
+        if (lane == 0) dA_part[item] = da;
     }
-    da = sum64(da);
-    if (lane == 0) dA_part[item] = da;
+    __syncthreads();
+    // rows of nh consecutive heads
+    for (int e = threadIdx.x; e < Lc * nh; e += kDdtThreads) {
+        const int j = e / nh, hh = e % nh;
+        ddt[((size_t)b * T + c * Q + j) * H + h0 + hh] = tile[j][hh];
+    }
 }
 
 // One workgroup per head: dA[h] and dD[h] summed over every (b, chunk) in a fixed order.
@@ -428,10 +468,22 @@ hipError_t launch_chunk_bwd_valu(const Shape& s, ssd_dtype dtype, const BwdArgs&
 hipError_t launch_bwd_finalize(const Shape& s, const BwdArgs& a, int rows, hipStream_t st) {
     const int items = s.B * s.H * s.nC;
     if (items > 0) {
-        const unsigned blocks = (unsigned)((items + 3) / 4);
-        bwd_ddt_kernel<<<blocks, kThreads, 0, st>>>(a.dcs, a.direct, a.xs, a.lt_part, a.dtc, a.A,
-                                                    a.ddt, a.dA_part, s.T, s.H, s.Q, s.nC, rows,
-                                                    items);
+        const unsigned blocks =
+            (unsigned)((size_t)s.B * s.nC * ((s.H + kDdtHeads - 1) / kDdtHeads));
+        switch (s.Q) {
+#define SSD_DDT(QV)                                                                          \
+    case QV:                                                                                 \
+        bwd_ddt_kernel<QV><<<blocks, kDdtThreads, 0, st>>>(a.dcs, a.direct, a.xs, a.lt_part, \
+                                                        a.dtc, a.A, a.ddt, a.dA_part, s.T,   \
+                                                        s.H, s.nC, rows);                    \
+        break;
+            SSD_DDT(64)
+            SSD_DDT(128)
+            SSD_DDT(256)
+#undef SSD_DDT
+            default:
+                return hipErrorInvalidValue;
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
