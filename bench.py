@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--bwd", default="", metavar="WORKLOAD",
                     help="instead of the forward, time the backward (ssd_bwd) on a workload and "
                          "print its own JSON line")
+    ap.add_argument("--peaks", action="store_true",
+                    help="measure practical peaks on this GPU: a 1 GiB device copy (HBM GB/s) "
+                         "and a bf16 8192^3 GEMM through torch (MFMA TFLOP/s)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to calibrate the "
                          "HBM byte counters against a known traffic, and exit")
@@ -102,10 +105,49 @@ def cpu_baseline(w, inputs, budget_s):
         el = sum(timed(nb, nh) for _ in range(reps)) / reps
     used = oracle.threads_used(nb, nh, nthreads)
     tokens = w.seqlen * nb * nh / w.nheads
+    # one thread, on the first group's heads of batch element 0 (a few seconds at most)
+    nh1 = min(w.nheads, hpg)
+    s1 = sample(1, nh1)
+    t0 = time.perf_counter()
+    oracle.ssd_ref(**s1, nthreads=1)
+    el1 = time.perf_counter() - t0
     return {"value": round(tokens / el, 1), "unit": "tokens/s", "cores": used, "kind": "oracle",
             "sample": f"batch elements 0..{nb - 1} of {w.batch}, heads 0..{nh - 1} of "
                       f"{w.nheads}, full T={w.seqlen} ({nb * nh} fp64 token-recurrence "
-                      f"sequences, {el:.2f} s each, mean of {reps} runs)"}
+                      f"sequences, {el:.2f} s each, mean of {reps} runs)",
+            "single_thread_value": round(w.seqlen * nh1 / w.nheads / el1, 1),
+            "single_thread_sample": f"batch element 0, heads 0..{nh1 - 1}, {el1:.2f} s",
+            "host": host_info()}
+
+
+def host_info():
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "threads_allowed": host_threads()}
+
+
+def step_stats(torch, fn, steps, flush=None):
+    """Per-step GPU times (HIP events on the current stream) of `steps` calls of fn, in us:
+    median, p10, p90.  With `flush`, an untimed flush runs before each timed call."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        if flush is not None:
+            flush()
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+    q = lambda f: t[min(len(t) - 1, int(f * (len(t) - 1) + 0.5))]
+    return {"median": round(q(0.5), 2), "p10": round(q(0.1), 2), "p90": round(q(0.9), 2)}
 
 
 def bench_decode(args, w, torch, binding, roofline, generate):
@@ -299,6 +341,29 @@ def bench_block(args, w, cfg, torch, binding, roofline, generate_block):
     }), flush=True)
 
 
+def measure_peaks(torch):
+    """Practical peaks next to the spec ones: HBM bandwidth from a 1 GiB device-to-device
+    copy (read + write bytes over time), MFMA throughput from a bf16 GEMM (hipBLASLt)."""
+    from mamba_ssd_chunked_03_amd import roofline
+    dev = torch.device("cuda:0")
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    copy = step_stats(torch, lambda: dst.copy_(src), 20)
+    m = 8192
+    a = torch.randn((m, m), device=dev).to(torch.bfloat16)
+    b = torch.randn((m, m), device=dev).to(torch.bfloat16)
+    for _ in range(3):
+        a @ b
+    gemm = step_stats(torch, lambda: a @ b, 20)
+    print(json.dumps({
+        "hbm_copy_GBps": round(2 * 4 * n / (copy["median"] * 1e-6) / 1e9, 1),
+        "hbm_spec_GBps": roofline.PEAK_HBM_GBPS,
+        "bf16_gemm_TFLOPs": round(2 * m ** 3 / (gemm["median"] * 1e-6) / 1e12, 1),
+        "bf16_spec_TFLOPs": roofline.PEAK_MFMA_TFLOPS["bf16"],
+        "copy_us": copy, "gemm_us": gemm}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -308,6 +373,8 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.peaks:
+        return measure_peaks(torch)
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda:0")
@@ -399,6 +466,12 @@ def main():
     torch.cuda.synchronize()
     if not torch.equal(y, y_ref):
         log("[bench] WARNING: staged calls and ssd_fwd differ")
+    # per-step times: warm (back to back) and cold (the 256 MB Infinity Cache flushed by an
+    # untimed 1 GiB write before each step)
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    step_us = {"warm": step_stats(torch, fwd, args.steps),
+               "cold": step_stats(torch, fwd, args.steps, flush=lambda: scratch.fill_(1.0))}
+    del scratch
     if not torch.isfinite(y.float()).all():
         log("[bench] WARNING: non-finite output")
 
@@ -445,6 +518,7 @@ def main():
                    "init_state": w.init_state, "parallelism": "single_gpu"},
         "roofline": roof,
         "kernels": kernels,
+        "step_us": step_us,
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle)")
