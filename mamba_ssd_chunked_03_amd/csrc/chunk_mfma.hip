@@ -7,7 +7,8 @@
 // the slow (row) dimension of B and x in HBM, so both operands pass through LDS.
 //
 // Two kernels:
-//   chunk_state_pipe_kernel (N = 128, P <= 64): persistent and pipelined.  A workgroup per
+//   chunk_state_pipe_kernel (N = 128, P <= 64; N = 64, P in {32, 64}): persistent and
+//     pipelined.  A workgroup per
 //     CU walks a run of (unit, head) items, a unit being one (batch, group, chunk).  The
 //     unit's B chunk is copied into LDS once and read out through transpose reads into
 //     register fragments (one 16-row n-tile per wave, all 32-step blocks), after which
@@ -163,17 +164,20 @@ __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_ker
                 const uint2 hi2 = lds_read_tr16(bp + BHALF);
                 bt[ib] = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
             }
-            constexpr bool kGram = (Q == 256 && N == 128 && !REV);
+            constexpr bool kGram = (Q == 256 && (N == 64 || N == 128) && !REV);
             if (kGram && gram != nullptr && sl == unit * hpg) {
                 // C B^T blocks of this unit (this workgroup holds its first head): wave w
-                // takes row tiles w and 15 - w and every block at or below them
+                // takes the row tile pairs (tp, 15 - tp), tp = w, w + NW, ..., and every
+                // block at or below them
                 const int c = unit % nC, g = (unit / nC) % G, b = unit / nC / G;
                 const int Lc = min(Q, T - c * Q);
                 const unsigned crow = (unsigned)(G * N * 2);
                 const __amdgpu_buffer_rsrc_t cr =
                     make_rsrc(Cm + ((size_t)(b * T + c * Q) * G + g) * N, (unsigned)Lc * crow);
                 constexpr int NK = N / 32, NPAIR = 72;
-                const int ta = wave, tb = 15 - wave;
+#pragma unroll 1
+                for (int tp = wave; tp < 8; tp += C_::NW) {
+                const int ta = tp, tb = 15 - tp;
                 const int na = ta / 2 + 1, nb = tb / 2 + 1;
                 bf16x8 ca[NK], cb[NK];
 #pragma unroll
@@ -206,6 +210,7 @@ __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_ker
                     };
                     if (ib < na) emit(ca, ta);
                     emit(cb, tb);
+                }
                 }
             }
             lds_barrier();  // every wave holds its fragments: the region is free
@@ -452,11 +457,17 @@ hipError_t launch_state_pipe_t(const Shape& s, const void* x, const void* Bm, co
 
 template <int Q, bool REV>
 StateFn pick_state_pipe_q(const Shape& s) {
-    if (s.N != 128) return nullptr;
-    switch (s.P) {
-        case 16: return launch_state_pipe_t<Q, 128, 16, REV>;
-        case 32: return launch_state_pipe_t<Q, 128, 32, REV>;
-        case 64: return launch_state_pipe_t<Q, 128, 64, REV>;
+    if (s.N == 128) {
+        switch (s.P) {
+            case 16: return launch_state_pipe_t<Q, 128, 16, REV>;
+            case 32: return launch_state_pipe_t<Q, 128, 32, REV>;
+            case 64: return launch_state_pipe_t<Q, 128, 64, REV>;
+        }
+    } else if (s.N == 64) {  // four waves: P up to 64 keeps the copy counts per wave even
+        switch (s.P) {
+            case 32: return launch_state_pipe_t<Q, 64, 32, REV>;
+            case 64: return launch_state_pipe_t<Q, 64, 64, REV>;
+        }
     }
     return nullptr;
 }
@@ -491,7 +502,7 @@ StateFn pick_state(const Shape& s) {
 bool chunk_state_mfma_supported(const Shape& s) { return pick_state<false>(s) != nullptr; }
 
 bool chunk_state_writes_gram(const Shape& s) {
-    return state_offsets_fit(s) && s.Q == 256 && s.N == 128 &&
+    return state_offsets_fit(s) && s.Q == 256 && (s.N == 64 || s.N == 128) &&
            pick_state_pipe_q<256, false>(s) != nullptr;
 }
 
