@@ -89,7 +89,9 @@ __global__ __launch_bounds__(256) void chunk_gram_kernel(const __bf16* __restric
 
 // ============================================================================ chunk_scan
 // Persistent and software-pipelined: each workgroup walks a contiguous run of (unit, head)
-// items, consecutive heads of one unit first.  Wave w of the NT/2 waves owns the 16-row
+// items, consecutive heads of one unit first, from the run's end to its start (the chunk
+// state kernel walks the same runs forwards, so the x rows it read last, the likeliest to
+// still sit in the Infinity Cache, are read first).  Wave w of the NT/2 waves owns the 16-row
 // tiles w and NT-1-w (the same share of the causal triangle for every wave).  While the
 // unit stays the same, a wave keeps its tiles' C rows and Gram fragments in registers, so
 // the compute needs no global loads at all; meanwhile the next item's x, entry state, cs
@@ -198,13 +200,13 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
     uint4 gf0[NB0], gf1[NB];  // Gram fragments of (tile0, ib), (tile1, ib)
     int cur_unit = -1;
 
-    issue_item<Q, N, P>(x, E, cs, dtc, lo, hpg, T, H, G, nC, lds0, wave, lane);
+    issue_item<Q, N, P>(x, E, cs, dtc, hi - 1, hpg, T, H, G, nC, lds0, wave, lane);
     if (C_::NBUF == 3 && lo + 1 < hi)
-        issue_item<Q, N, P>(x, E, cs, dtc, lo + 1, hpg, T, H, G, nC, lds0 + C_::ITEM, wave, lane);
+        issue_item<Q, N, P>(x, E, cs, dtc, hi - 2, hpg, T, H, G, nC, lds0 + C_::ITEM, wave, lane);
     int buf = 0;  // buffer of the current item
 #pragma unroll 1
-    for (int sl = lo; sl < hi; ++sl) {
-        const int n = sl - lo;
+    for (int n = 0; n < hi - lo; ++n) {
+        const int sl = hi - 1 - n;
         unsigned char* bx = smem + buf * C_::ITEM;
         const float* b_cs = reinterpret_cast<const float*>(bx + C_::XB + C_::EB);
         const float* b_dt = b_cs + Q;
@@ -212,7 +214,7 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
         // with three buffers the next item's copies and the previous item's stores, with
         // two the previous item's stores.
         if (C_::NBUF == 3) {
-            const bool more = sl + 1 < hi;
+            const bool more = n + 1 < hi - lo;
             if (n == 0 && !more)
                 asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
             else if (n == 0 && wave < 2)
@@ -293,13 +295,13 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
             __builtin_amdgcn_s_waitcnt(0x0F70);
         }
         lds_barrier();
-        if (C_::NBUF == 3 && sl + 2 < hi) {  // into the buffer of the previous item
+        if (C_::NBUF == 3 && n + 2 < hi - lo) {  // into the buffer of the previous item
             const int b2 = buf == 0 ? 2 : buf - 1;
-            issue_item<Q, N, P>(x, E, cs, dtc, sl + 2, hpg, T, H, G, nC, lds0 + b2 * C_::ITEM,
+            issue_item<Q, N, P>(x, E, cs, dtc, sl - 2, hpg, T, H, G, nC, lds0 + b2 * C_::ITEM,
                                 wave, lane);
         }
-        if (C_::NBUF == 2 && sl + 1 < hi)
-            issue_item<Q, N, P>(x, E, cs, dtc, sl + 1, hpg, T, H, G, nC,
+        if (C_::NBUF == 2 && n + 1 < hi - lo)
+            issue_item<Q, N, P>(x, E, cs, dtc, sl - 1, hpg, T, H, G, nC,
                                 lds0 + (buf ^ 1) * C_::ITEM, wave, lane);
 
         // stage 4: the entry state read out by C, then decayed from the chunk start
@@ -422,9 +424,9 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
         };
         store_tile(acc0, j0);
         store_tile(acc1, j1);
-        if (C_::NBUF == 1 && sl + 1 < hi) {
+        if (C_::NBUF == 1 && n + 1 < hi - lo) {
             lds_barrier();  // every wave is done with the buffer
-            issue_item<Q, N, P>(x, E, cs, dtc, sl + 1, hpg, T, H, G, nC, lds0, wave, lane);
+            issue_item<Q, N, P>(x, E, cs, dtc, sl - 1, hpg, T, H, G, nC, lds0, wave, lane);
         }
         buf = (C_::NBUF == 1) ? 0 : (buf + 1 == C_::NBUF ? 0 : buf + 1);
     }
