@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--block", default="", metavar="BLOCK",
                     help="time the block between the projections (ssd_block_fwd: prologue, "
                          "ssd_fwd, epilogue) on a model-shaped block (block_2p7b, block_130m)")
+    ap.add_argument("--varlen", action="store_true",
+                    help="time ssd_fwd_varlen on the 2.7B layer's 16384 tokens packed as one row "
+                         "of seeded sequence lengths (64 to 4096 steps)")
     ap.add_argument("--bwd", default="", metavar="WORKLOAD",
                     help="instead of the forward, time the backward (ssd_bwd) on a workload and "
                          "print its own JSON line")
@@ -341,6 +344,51 @@ def bench_block(args, w, cfg, torch, binding, roofline, generate_block):
     }), flush=True)
 
 
+def bench_varlen(args, torch, binding, generate, Workload):
+    """ssd_fwd_varlen calls back to back on one packed row: tokens/s = T / call time, next
+    to ssd_fwd on the same tokens as one unbroken sequence."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    T = 16384
+    rng = np.random.default_rng(11)
+    cuts = [0]
+    while cuts[-1] < T:
+        cuts.append(min(T, cuts[-1] + int(rng.integers(64, 4097))))
+    w = Workload("packed_2p7b", 1, T, 80, 64, 128, 1, 256)
+    log(f"[bench varlen] {w.describe()} {len(cuts) - 1} sequences")
+    d = {k: (None if v is None else v.to(dev)) for k, v in generate(w).items()}
+    cu = torch.tensor(cuts, dtype=torch.int32, device=dev)
+    dims = binding.SsdDims(1, T, w.nheads, w.headdim, w.dstate, w.ngroups)
+    ws = torch.empty(binding.ssd_fwd_varlen_workspace_size(dims, 256), dtype=torch.uint8,
+                     device=dev)
+    y = torch.empty_like(d["x"])
+    fins = torch.empty((len(cuts) - 1, w.nheads, w.dstate, w.headdim), device=dev)
+    step = lambda: binding.ssd_fwd_varlen(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], 256,
+                                          cu, y=y, final_states=fins, workspace=ws)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    fws = torch.empty(binding.ssd_fwd_workspace_size(dims, 256), dtype=torch.uint8, device=dev)
+    one = step_stats(torch, lambda: binding.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"],
+                                                    d["D"], 256, y=y, workspace=fws),
+                     args.steps)
+    print(json.dumps({
+        "metric": "SSD fwd (packed variable-length row) tokens/sec on 1 MI355X",
+        "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "seqlen": T, "nheads": w.nheads, "headdim": w.headdim,
+                   "dstate": w.dstate, "chunk_len": 256, "sequences": len(cuts) - 1,
+                   "final_states": True},
+        "ssd_fwd_same_tokens_us": one}), flush=True)
+
+
 def measure_peaks(torch):
     """Practical peaks next to the spec ones: HBM bandwidth from a 1 GiB device-to-device
     copy (read + write bytes over time), MFMA throughput from a bf16 GEMM (hipBLASLt)."""
@@ -386,8 +434,10 @@ def main():
                           "read_bytes_per_copy": 4 * n, "write_bytes_per_copy": 4 * n}))
         return
     from mamba_ssd_chunked_03_amd import binding, roofline, traffic
-    from mamba_ssd_chunked_03_amd.workloads import (BLOCKS, DECODE, WORKLOADS, generate,
-                                                    generate_block, generate_grads)
+    from mamba_ssd_chunked_03_amd.workloads import (BLOCKS, DECODE, WORKLOADS, Workload,
+                                                    generate, generate_block, generate_grads)
+    if args.varlen:
+        return bench_varlen(args, torch, binding, generate, Workload)
     if args.block:
         w, cfg = BLOCKS[args.block]
         return bench_block(args, w, cfg, torch, binding, roofline, generate_block)

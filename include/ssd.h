@@ -235,6 +235,38 @@ ssd_status ssd_decode_step(const ssd_dims* dims, ssd_dtype dtype, const void* x,
                            const float* dt, const float* A, const void* B, const void* C,
                            const float* D, float* state, void* y, void* stream);
 
+/* ---- packed variable-length rows -------------------------------------------------------
+ * Several independent sequences laid end to end in one row of steps (batch 1), sequence s
+ * covering steps cu_seqlens[s] .. cu_seqlens[s+1]-1.  Each starts from a zero state and no
+ * state passes from one into the next ("Mamba-2: Attention's Distant Cousin", section
+ * "Working Through Four Tokens": a sequence starts from zero; the reproduction page for
+ * arXiv 2405.21060 (citeark.co), reported claims: context parallelism passes a state
+ * between contiguous pieces of one sequence).  The four forward stages run unchanged:
+ * ssd_chunk_cumsum's running log-decay sum drops by a gap of 120 at every sequence start,
+ * which makes every decay across a start exactly zero in fp32.  The gaps cost some
+ * precision inside a chunk that holds several starts: with k starts in one chunk the
+ * log-decays reach about -(120 k + 254), and each decay carries a relative error of
+ * about ulp(120 k + 254), e.g. 6e-5 for k = 3. */
+
+/* Bytes of workspace ssd_fwd_varlen needs: ssd_fwd's for these sizes, then seqlen ints
+ * (0 if the sizes are invalid or batch != 1). */
+size_t ssd_fwd_varlen_workspace_size(const ssd_dims* dims, int chunk_len);
+
+/* y [1][T][H][P] for a packed row, and optionally every sequence's final state.
+ *   dims         batch must be 1 (else SSD_ERR_DIMS); T = total steps
+ *   cu_seqlens   device int32 [nseq + 1], rising from 0 to T (not checked: the caller's
+ *                contract, like dt >= 0); empty sequences are allowed
+ *   nseq         number of sequences, >= 1
+ *   final_states NULL, or [nseq][H][N][P] fp32: the state after each sequence's last step
+ *                (zero for an empty sequence)
+ * x, dt, A, B, C, D, chunk_len, y and the alignment rules as for ssd_fwd (no init_state:
+ * every sequence starts from zero); workspace of ssd_fwd_varlen_workspace_size bytes. */
+ssd_status ssd_fwd_varlen(const ssd_dims* dims, ssd_dtype dtype, const void* x, const float* dt,
+                          const float* A, const void* B, const void* C, const float* D,
+                          int chunk_len, const int32_t* cu_seqlens, int64_t nseq, void* y,
+                          float* final_states, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* ---- the block around the layer ----------------------------------------------------
  * The Mamba-2 block between its input and output projections ("Mamba-2: Attention's
  * Distant Cousin", section "The Mamba-2 Block", Figure 6; structured summary of arXiv

@@ -18,7 +18,7 @@ EXPORTED = ("ssd_status_string", "ssd_fwd_workspace_size", "ssd_fwd", "ssd_chunk
             "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_gram_size", "ssd_chunk_gram",
             "ssd_chunk_scan", "ssd_decode_step", "ssd_bwd_workspace_size", "ssd_bwd",
             "ssd_block_prologue", "ssd_block_epilogue", "ssd_block_fwd_workspace_size",
-            "ssd_block_fwd")
+            "ssd_block_fwd", "ssd_fwd_varlen_workspace_size", "ssd_fwd_varlen")
 
 
 class SsdDims(ctypes.Structure):
@@ -86,6 +86,11 @@ def library(path=LIB_PATH):
     lib.ssd_block_fwd.restype = i
     lib.ssd_block_fwd.argtypes = [dims, i, vp, fp, fp, i, fp, fp, fp, i, fp, fp, fp, i, i, f, vp,
                                   fp, vp, sz, vp]
+    lib.ssd_fwd_varlen_workspace_size.restype = sz
+    lib.ssd_fwd_varlen_workspace_size.argtypes = [dims, i]
+    lib.ssd_fwd_varlen.restype = i
+    lib.ssd_fwd_varlen.argtypes = [dims, i, vp, fp, fp, vp, vp, fp, i, vp, i64, vp, fp, vp, sz,
+                                   vp]
     if path == LIB_PATH:
         _LIB = lib
     return lib
@@ -430,3 +435,41 @@ def ssd_block_fwd(zxbcdt, conv_w, conv_b, dt_bias, A, D, chunk_len, norm_w, norm
                                    _ptr(out), _ptr(final_state), _ptr(workspace),
                                    workspace.numel(), _stream(dev, stream)))
     return out, final_state
+
+
+# ---------------------------------------------------------------- packed variable-length rows
+def ssd_fwd_varlen_workspace_size(dims, chunk_len):
+    return int(library().ssd_fwd_varlen_workspace_size(ctypes.byref(dims), int(chunk_len)))
+
+
+def ssd_fwd_varlen(x, dt, A, B, C, D, chunk_len, cu_seqlens, y=None, final_states=None,
+                   want_final=True, workspace=None, stream=None):
+    """y, final_states = SSD over a packed row through libssd.ssd_fwd_varlen.
+
+    x [1,T,H,P], B/C [1,T,G,N] in fp32 or bf16; dt [1,T,H], A, D [H] fp32; cu_seqlens int32
+    [nseq+1] on the device (0 .. T).  Returns (y, final_states [nseq,H,N,P] fp32 or None)."""
+    dev = x.device
+    code = _DTYPE_CODE.get(x.dtype)
+    if code is None:
+        raise TypeError(f"x must be fp32 or bf16, got {x.dtype}")
+    _need(x, "x", device=dev)
+    for t, n in ((B, "B"), (C, "C")):
+        _need(t, n, x.dtype, dev)
+    for t, n in ((dt, "dt"), (A, "A"), (D, "D")):
+        _need(t, n, torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    nseq = cu_seqlens.numel() - 1
+    d = dims_of(x, B)
+    if y is None:
+        y = torch.empty_like(x)
+    if final_states is None and want_final:
+        final_states = torch.empty((nseq, d.nheads, d.dstate, d.headdim), dtype=torch.float32,
+                                   device=dev)
+    if workspace is None:
+        ws = ssd_fwd_varlen_workspace_size(d, chunk_len)
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+    _check(library().ssd_fwd_varlen(ctypes.byref(d), code, _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                    _ptr(C), _ptr(D), int(chunk_len), _ptr(cu_seqlens), nseq,
+                                    _ptr(y), _ptr(final_states), _ptr(workspace),
+                                    workspace.numel(), _stream(dev, stream)))
+    return y, final_states

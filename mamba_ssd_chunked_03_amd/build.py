@@ -20,7 +20,7 @@ ARCH = "gfx950"
 
 SOURCES = ["ssd_api.hip", "chunk_cumsum.hip", "state_passing.hip", "chunk_valu.hip",
            "chunk_mfma.hip", "chunk_scan_mfma.hip", "decode_step.hip", "chunk_bwd_valu.hip",
-           "chunk_bwd_mfma.hip", "block.hip"]
+           "chunk_bwd_mfma.hip", "block.hip", "varlen.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

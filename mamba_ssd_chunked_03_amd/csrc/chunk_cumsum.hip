@@ -12,22 +12,35 @@
 // adds the carry of the lanes before it.  It writes the chunk-major copy
 // dt_chunk[b][h][c][i] that the later kernels read contiguously, and the inclusive prefix
 // sum cs of dt*A over the chunk, both as contiguous rows.
+//
+// Packed variable-length rows (starts != null): a step where a new sequence begins adds
+// -kSeqGap to the running sum.  Every decay exp(cs_j - cs_i) between two steps of
+// different sequences then carries a factor exp(-kSeqGap) or smaller, which is 0 in fp32,
+// while inside one sequence the offsets cancel.  The later stages thereby drop every
+// cross-sequence term with no change of their own: pair terms inside a chunk, a chunk
+// state's steps before the last sequence start, the carry across a chunk with a start in
+// it, and the entry state's read-out after a start.
 #include "ssd_internal.h"
 
 namespace ssd {
 namespace {
 
 constexpr int kHB = 16;  // heads per workgroup
+// log-decay gap at a packed sequence start: exp2(-kSeqGap log2 e) is below the smallest
+// fp32 subnormal, so every decay across a start is exactly zero
+constexpr float kSeqGap = 120.f;
 
 template <int Q>
 __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const float* __restrict__ dt,
                                                            const float* __restrict__ A,
+                                                           const int* __restrict__ starts,
                                                            float* __restrict__ dtc,
                                                            float* __restrict__ cs, int T, int H,
                                                            int nC) {
     constexpr int E = Q / 64;       // steps per lane
     constexpr int LD = Q + 4;       // padded row: 16-byte aligned, conflict-free writes
     __shared__ __align__(16) float tile[kHB][LD];
+    __shared__ float gap[Q];  // -kSeqGap where a packed sequence starts, else 0
     const int hblocks = (H + kHB - 1) / kHB;
     const int hb = blockIdx.x % hblocks;
     const int bc = blockIdx.x / hblocks;
@@ -54,6 +67,8 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const float* __restri
         const int e = tid + 256 * k;
         tile[e % kHB][e / kHB] = v_in[k];
     }
+    for (int i = tid; i < Q; i += 256)
+        gap[i] = (starts && i < Lc && starts[(size_t)b * T + t0 + i]) ? -kSeqGap : 0.f;
     __syncthreads();
     const int wave = tid >> 6, lane = tid & 63;
     for (int hh = wave; hh < nh; hh += 4) {
@@ -65,7 +80,7 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const float* __restri
         float acc = 0.0f;
 #pragma unroll
         for (int k = 0; k < E; ++k) {
-            acc += v[k] * a;
+            acc += fmaf(v[k], a, gap[lane * E + k]);
             run[k] = acc;
         }
         // exclusive carry from the lanes before this one
@@ -88,19 +103,22 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const float* __restri
 }  // namespace
 
 hipError_t launch_chunk_cumsum(const Shape& s, const float* dt, const float* A, float* dtc,
-                               float* cs, hipStream_t st) {
+                               float* cs, hipStream_t st, const int* starts) {
     const size_t hblocks = (size_t)(s.H + kHB - 1) / kHB;
     const unsigned blocks = (unsigned)((size_t)s.B * s.nC * hblocks);
     if (blocks == 0) return hipSuccess;
     switch (s.Q) {
         case 64:
-            chunk_cumsum_kernel<64><<<blocks, 256, 0, st>>>(dt, A, dtc, cs, s.T, s.H, s.nC);
+            chunk_cumsum_kernel<64><<<blocks, 256, 0, st>>>(dt, A, starts, dtc, cs, s.T, s.H,
+                                                             s.nC);
             break;
         case 128:
-            chunk_cumsum_kernel<128><<<blocks, 256, 0, st>>>(dt, A, dtc, cs, s.T, s.H, s.nC);
+            chunk_cumsum_kernel<128><<<blocks, 256, 0, st>>>(dt, A, starts, dtc, cs, s.T, s.H,
+                                                             s.nC);
             break;
         case 256:
-            chunk_cumsum_kernel<256><<<blocks, 256, 0, st>>>(dt, A, dtc, cs, s.T, s.H, s.nC);
+            chunk_cumsum_kernel<256><<<blocks, 256, 0, st>>>(dt, A, starts, dtc, cs, s.T, s.H,
+                                                             s.nC);
             break;
         default:
             return hipErrorInvalidValue;

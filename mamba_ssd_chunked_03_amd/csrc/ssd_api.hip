@@ -500,4 +500,53 @@ ssd_status ssd_block_fwd(const ssd_dims* dims, ssd_dtype dtype, const void* zxbc
                               rms, eps, out, stream);
 }
 
+// ---- packed variable-length rows ------------------------------------------------------
+
+size_t ssd_fwd_varlen_workspace_size(const ssd_dims* dims, int chunk_len) {
+    Shape s;
+    if (make_shape(dims, chunk_len, &s) != SSD_OK || dims->batch != 1) return 0;
+    return workspace_bytes(s, nullptr, nullptr) + round_up((size_t)s.T * sizeof(int));
+}
+
+ssd_status ssd_fwd_varlen(const ssd_dims* dims, ssd_dtype dtype, const void* x, const float* dt,
+                          const float* A, const void* B, const void* C, const float* D,
+                          int chunk_len, const int32_t* cu_seqlens, int64_t nseq, void* y,
+                          float* final_states, void* workspace, size_t workspace_bytes_given,
+                          void* stream) {
+    Shape s;
+    ssd_status r = make_shape(dims, chunk_len, &s);
+    if (r != SSD_OK) return r;
+    if (!valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
+    if (dims->batch != 1 || nseq < 1 || nseq >= ((int64_t)1 << 30)) return SSD_ERR_DIMS;
+    const bool has_tokens = s.T > 0;
+    if (!cu_seqlens) return SSD_ERR_NULL;
+    if (has_tokens && (!x || !dt || !A || !B || !C || !D || !y)) return SSD_ERR_NULL;
+    if (any_misaligned({x, B, C, y, workspace}) ||
+        any_misaligned4({dt, A, D, cu_seqlens, final_states}))
+        return SSD_ERR_ALIGN;
+    Workspace ws;
+    const size_t fwd = workspace_bytes(s, &ws, (char*)workspace);
+    const size_t need = fwd + round_up((size_t)s.T * sizeof(int));
+    if (need > 0 && (!workspace || workspace_bytes_given < need)) return SSD_ERR_WORKSPACE;
+    int* starts = (int*)((char*)workspace + fwd);
+    hipStream_t st = (hipStream_t)stream;
+    const int ns = (int)nseq;
+    if (has_tokens) {
+        r = hip_status(ssd::launch_seq_starts(cu_seqlens, ns, starts, s.T, st));
+        if (r != SSD_OK) return r;
+        r = hip_status(ssd::launch_chunk_cumsum(s, dt, A, ws.dtc, ws.cs, st, starts));
+        if (r != SSD_OK) return r;
+        r = run_chunk_state(s, dtype, x, B, ws.dtc, ws.cs, ws.states, C, ws.gram, st);
+        if (r != SSD_OK) return r;
+        r = hip_status(ssd::launch_state_passing(s, dtype, ws.states, ws.cs, nullptr, ws.entry,
+                                                 nullptr, st));
+        if (r != SSD_OK) return r;
+        r = run_chunk_scan(s, dtype, x, B, C, ws.dtc, ws.cs, D, ws.entry, ws.gram, y, st);
+        if (r != SSD_OK) return r;
+    }
+    if (!final_states) return SSD_OK;
+    return hip_status(ssd::launch_varlen_final(s, dtype, x, B, ws.dtc, ws.cs, ws.entry,
+                                               cu_seqlens, ns, final_states, st));
+}
+
 }  // extern "C"

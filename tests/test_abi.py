@@ -248,3 +248,23 @@ def test_block_validation_errors_before_any_launch(lib):
     assert blk(k=0) == 3 and blk(q=100) == 3 and blk(groups=5) == 2
     assert blk(zx=None) == 1 and blk(A=None) == 1
     assert blk(zx=264) == 4 and blk(ws=None) == 5 and blk(ws_bytes=100) == 5
+
+
+def test_varlen_validation_errors_before_any_launch(lib):
+    ok = ctypes.c_void_p(256)
+
+    def call(d, dtype=1, q=64, nseq=2, ws_bytes=1 << 30, **p):
+        a = dict(x=ok, dt=ok, A=ok, B=ok, C=ok, D=ok, cu=ok, y=ok, fin=None, ws=ok)
+        a.update({n: (None if v is None else ctypes.c_void_p(v)) for n, v in p.items()})
+        return lib.ssd_fwd_varlen(ctypes.byref(d), dtype, a["x"], a["dt"], a["A"], a["B"],
+                                  a["C"], a["D"], q, a["cu"], nseq, a["y"], a["fin"], a["ws"],
+                                  ws_bytes, None)
+    assert call(D(b=2)) == 2 and call(D(), nseq=0) == 2          # batch 1, nseq >= 1
+    assert call(D(), q=100) == 3 and call(D(), dtype=9) == 3
+    assert call(D(), cu=None) == 1 and call(D(), x=None) == 1
+    assert call(D(), cu=258) == 4 and call(D(), x=264) == 4
+    assert call(D(), ws=None) == 5 and call(D(), ws_bytes=16) == 5
+    d = D()
+    assert binding.ssd_fwd_varlen_workspace_size(d, 64) == \
+        binding.ssd_fwd_workspace_size(d, 64) + (256 * 4 + 255) // 256 * 256
+    assert binding.ssd_fwd_varlen_workspace_size(D(b=2), 64) == 0
