@@ -257,8 +257,9 @@ __device__ __forceinline__ float team_sum(float v, int lpg) {
 }
 
 // One team of lpg lanes per (row, group); a lane owns the vectors i * lpg + lane of its
-// group (nv of them).  NVMAX > 0: the gated values stay in registers (nv <= NVMAX);
-// NVMAX == 0: they are re-read for each pass.
+// group (nv of them).  NVMAX > 0: exactly NVMAX = nv vectors per lane, whose gated values
+// stay in registers (the count is a compile-time constant, so all loads are issued
+// before the first is used); NVMAX == 0: they are re-read for each pass.
 template <typename T, int V, int NVMAX>
 __global__ __launch_bounds__(256) void block_epilogue_kernel(
     const T* __restrict__ y, const T* __restrict__ z, long long zstride,
@@ -301,29 +302,38 @@ __global__ __launch_bounds__(256) void block_epilogue_kernel(
         store_vec<T, V>(orow + c, o);
     };
     if constexpr (NVMAX > 0) {
+        Raw<T, V> ry[NVMAX], rz[NVMAX];
+#pragma unroll
+        for (int i = 0; i < NVMAX; ++i) {
+            const int c = (i * lpg + tl) * V;
+            ry[i] = load_raw<T, V>(yr + c);
+            rz[i] = load_raw<T, V>(zr + c);
+        }
         float v[NVMAX][V];
         float s = 0.f;
 #pragma unroll
-        for (int i = 0; i < NVMAX; ++i)
-            if (i < nv) {
-                gated(i, v[i]);
+        for (int i = 0; i < NVMAX; ++i) {
+            float zv[V];
+            unpack<T, V>(ry[i], v[i]);
+            unpack<T, V>(rz[i], zv);
 #pragma unroll
-                for (int k = 0; k < V; ++k) s += v[i][k];
+            for (int k = 0; k < V; ++k) {
+                v[i][k] *= silu_f(zv[k]);
+                s += v[i][k];
             }
+        }
         const float mean = rms ? 0.f : team_sum(s, lpg) * inv_gs;
         float q = 0.f;
 #pragma unroll
         for (int i = 0; i < NVMAX; ++i)
-            if (i < nv)
 #pragma unroll
-                for (int k = 0; k < V; ++k) {
-                    const float dv = v[i][k] - mean;
-                    q = fmaf(dv, dv, q);
-                }
+            for (int k = 0; k < V; ++k) {
+                const float dv = v[i][k] - mean;
+                q = fmaf(dv, dv, q);
+            }
         const float rstd = rsqrtf(team_sum(q, lpg) * inv_gs + eps);
 #pragma unroll
-        for (int i = 0; i < NVMAX; ++i)
-            if (i < nv) emit(i, v[i], mean, rstd);
+        for (int i = 0; i < NVMAX; ++i) emit(i, v[i], mean, rstd);
     } else {
         float s = 0.f;
         for (int i = 0; i < nv; ++i) {
@@ -398,14 +408,13 @@ hipError_t launch_epilogue_v(const Shape& s, const BlockEpilogueArgs& a, hipStre
     int lpg = 64;
     while (nvec % lpg != 0) lpg >>= 1;  // the largest power of two up to 64 dividing nvec
     const int nv = nvec / lpg;
-    if (nv <= 1) return launch_epilogue_n<T, V, 1>(s, a, lpg, nv, st);
-    if (nv <= 2) return launch_epilogue_n<T, V, 2>(s, a, lpg, nv, st);
-    if (nv <= 4) return launch_epilogue_n<T, V, 4>(s, a, lpg, nv, st);
-    if (nv <= 6) return launch_epilogue_n<T, V, 6>(s, a, lpg, nv, st);
-    if (nv <= 8) return launch_epilogue_n<T, V, 8>(s, a, lpg, nv, st);
-    if (nv <= 10) return launch_epilogue_n<T, V, 10>(s, a, lpg, nv, st);
-    if (nv <= 12) return launch_epilogue_n<T, V, 12>(s, a, lpg, nv, st);
-    if (nv <= 16) return launch_epilogue_n<T, V, 16>(s, a, lpg, nv, st);
+    switch (nv) {  // exact counts up to 16 per lane, then the streaming variant
+#define SSD_NV(K) \
+    case K: return launch_epilogue_n<T, V, K>(s, a, lpg, nv, st);
+        SSD_NV(1) SSD_NV(2) SSD_NV(3) SSD_NV(4) SSD_NV(5) SSD_NV(6) SSD_NV(7) SSD_NV(8)
+        SSD_NV(9) SSD_NV(10) SSD_NV(11) SSD_NV(12) SSD_NV(13) SSD_NV(14) SSD_NV(15) SSD_NV(16)
+#undef SSD_NV
+    }
     return launch_epilogue_n<T, V, 0>(s, a, lpg, nv, st);
 }
 
