@@ -227,6 +227,16 @@ def bench_bwd(args, w, torch, binding, roofline, generate, generate_grads):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     us = e0.elapsed_time(e1) * 1e3 / args.steps
+    # the same gradients from the forward's own intermediates (ssd_bwd_saved), as a
+    # training step that has just run ssd_fwd would take them
+    fws = torch.empty(binding.ssd_fwd_workspace_size(dims, w.chunk_len), dtype=torch.uint8,
+                      device=dev)
+    binding.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], w.chunk_len,
+                    init_state=d["init_state"], workspace=fws)
+    saved = step_stats(torch, lambda: binding.ssd_bwd(
+        d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], w.chunk_len, u["dy"],
+        init_state=d["init_state"], d_final=u["d_final"], out=out, workspace=ws,
+        fwd_workspace=fws), args.steps)
     costs = roofline.bwd_costs(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups,
                                w.chunk_len, w.dtype, init_state=w.init_state)
     tot_bytes = sum(c.bytes for c in costs)
@@ -247,6 +257,7 @@ def bench_bwd(args, w, torch, binding, roofline, generate, generate_grads):
                      "peak": roofline.PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(gbs / roofline.PEAK_HBM_GBPS, 4), "traffic": None},
         "call_us": round(us, 2),
+        "saved_call_us": saved,
         "kernels": {c.name: {"alg_bytes": int(c.bytes), "alg_flops": int(c.flops)} for c in costs},
         "alg_bytes_total": int(tot_bytes), "alg_flops_total": int(tot_flops),
     }), flush=True)

@@ -216,6 +216,21 @@ ssd_status ssd_bwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const f
                    float* dD, float* d_init, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* ssd_bwd for training, where the forward has just run: the same gradients, reading the
+ * log decays (dt_chunk, cs) and the entry states from the workspace of the ssd_fwd call
+ * instead of recomputing them (three of ssd_bwd's launches fewer).
+ *   fwd_workspace  the workspace passed to ssd_fwd with the same dims, dtype, chunk_len and
+ *                  inputs (x, dt, A, B, C, init_state), not modified since; read only;
+ *                  16-byte aligned; NULL is SSD_ERR_NULL
+ * Every other argument and the result are as for ssd_bwd (bit-identical: the same kernels
+ * produce the same intermediates). */
+ssd_status ssd_bwd_saved(const ssd_dims* dims, ssd_dtype dtype, const void* x, const float* dt,
+                         const float* A, const void* B, const void* C, const float* D,
+                         int chunk_len, const float* init_state, const void* dy,
+                         const float* d_final, const void* fwd_workspace, void* dx, float* ddt,
+                         float* dA, void* dB, void* dC, float* dD, float* d_init,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* One recurrent step for a batch of sequences ("Mamba-2: Attention's Distant Cousin",
  * section "Working Through Four Tokens": the recurrent form, the one generation uses, with
  * a state of fixed size).  For every (b, h), g = h / (H / G):
@@ -248,8 +263,8 @@ ssd_status ssd_decode_step(const ssd_dims* dims, ssd_dtype dtype, const void* x,
  * log-decays reach about -(120 k + 254), and each decay carries a relative error of
  * about ulp(120 k + 254), e.g. 6e-5 for k = 3. */
 
-/* Bytes of workspace ssd_fwd_varlen needs: ssd_fwd's for these sizes, then seqlen ints
- * (0 if the sizes are invalid or batch != 1). */
+/* Bytes of workspace ssd_fwd_varlen needs: ssd_fwd's for these sizes (0 if the sizes are
+ * invalid or batch != 1). */
 size_t ssd_fwd_varlen_workspace_size(const ssd_dims* dims, int chunk_len);
 
 /* y [1][T][H][P] for a packed row, and optionally every sequence's final state.

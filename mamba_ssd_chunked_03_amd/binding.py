@@ -18,7 +18,8 @@ EXPORTED = ("ssd_status_string", "ssd_fwd_workspace_size", "ssd_fwd", "ssd_chunk
             "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_gram_size", "ssd_chunk_gram",
             "ssd_chunk_scan", "ssd_decode_step", "ssd_bwd_workspace_size", "ssd_bwd",
             "ssd_block_prologue", "ssd_block_epilogue", "ssd_block_fwd_workspace_size",
-            "ssd_block_fwd", "ssd_fwd_varlen_workspace_size", "ssd_fwd_varlen")
+            "ssd_block_fwd", "ssd_fwd_varlen_workspace_size", "ssd_fwd_varlen",
+            "ssd_bwd_saved")
 
 
 class SsdDims(ctypes.Structure):
@@ -86,6 +87,9 @@ def library(path=LIB_PATH):
     lib.ssd_block_fwd.restype = i
     lib.ssd_block_fwd.argtypes = [dims, i, vp, fp, fp, i, fp, fp, fp, i, fp, fp, fp, i, i, f, vp,
                                   fp, vp, sz, vp]
+    lib.ssd_bwd_saved.restype = i
+    lib.ssd_bwd_saved.argtypes = [dims, i, vp, fp, fp, vp, vp, fp, i, fp, vp, fp, vp, vp, fp, fp,
+                                  vp, vp, fp, fp, vp, sz, vp]
     lib.ssd_fwd_varlen_workspace_size.restype = sz
     lib.ssd_fwd_varlen_workspace_size.argtypes = [dims, i]
     lib.ssd_fwd_varlen.restype = i
@@ -275,11 +279,13 @@ def ssd_bwd_workspace_size(dims, chunk_len):
 
 
 def ssd_bwd(x, dt, A, B, C, D, chunk_len, dy, init_state=None, d_final=None, want_d_init=True,
-            out=None, workspace=None, stream=None):
+            out=None, workspace=None, fwd_workspace=None, stream=None):
     """Gradients through ssd_fwd (libssd.ssd_bwd): inputs as for ssd_fwd plus dy (x's shape
     and dtype) and d_final ([B,H,N,P] fp32 or None).  Returns a dict with dx, ddt, dA, dB,
     dC, dD and d_init (None when want_d_init is False).  `out` may hold preallocated output
-    tensors under those names."""
+    tensors under those names.  With fwd_workspace (the workspace of an ssd_fwd call on the
+    same inputs) it calls libssd.ssd_bwd_saved, which reads the forward's intermediates
+    instead of recomputing them."""
     dev = x.device
     f32 = torch.float32
     _need(x, "x", device=dev)
@@ -309,6 +315,15 @@ def ssd_bwd(x, dt, A, B, C, D, chunk_len, dy, init_state=None, d_final=None, wan
     if workspace is None:
         ws = ssd_bwd_workspace_size(d, chunk_len)
         workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+    if fwd_workspace is not None:
+        _need(fwd_workspace, "fwd_workspace", torch.uint8, dev)
+        _check(library().ssd_bwd_saved(
+            ctypes.byref(d), code, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+            int(chunk_len), _ptr(init_state), _ptr(dy), _ptr(d_final), _ptr(fwd_workspace),
+            _ptr(o["dx"]), _ptr(o["ddt"]), _ptr(o["dA"]), _ptr(o["dB"]), _ptr(o["dC"]),
+            _ptr(o["dD"]), _ptr(o["d_init"]), _ptr(workspace), workspace.numel(),
+            _stream(dev, stream)))
+        return o
     _check(library().ssd_bwd(ctypes.byref(d), code, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
                              _ptr(D), int(chunk_len), _ptr(init_state), _ptr(dy), _ptr(d_final),
                              _ptr(o["dx"]), _ptr(o["ddt"]), _ptr(o["dA"]), _ptr(o["dB"]),

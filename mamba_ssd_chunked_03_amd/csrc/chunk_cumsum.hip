@@ -13,8 +13,8 @@
 // dt_chunk[b][h][c][i] that the later kernels read contiguously, and the inclusive prefix
 // sum cs of dt*A over the chunk, both as contiguous rows.
 //
-// Packed variable-length rows (starts != null): a step where a new sequence begins adds
-// -kSeqGap to the running sum.  Every decay exp(cs_j - cs_i) between two steps of
+// Packed variable-length rows (cu != null, batch 1): a step where a sequence s >= 1 begins
+// (cu[s]) adds -kSeqGap to the running sum.  Every decay exp(cs_j - cs_i) between two steps of
 // different sequences then carries a factor exp(-kSeqGap) or smaller, which is 0 in fp32,
 // while inside one sequence the offsets cancel.  The later stages thereby drop every
 // cross-sequence term with no change of their own: pair terms inside a chunk, a chunk
@@ -33,7 +33,7 @@ constexpr float kSeqGap = 120.f;
 template <int Q>
 __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const float* __restrict__ dt,
                                                            const float* __restrict__ A,
-                                                           const int* __restrict__ starts,
+                                                           const int* __restrict__ cu, int nseq,
                                                            float* __restrict__ dtc,
                                                            float* __restrict__ cs, int T, int H,
                                                            int nC) {
@@ -67,8 +67,17 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const float* __restri
         const int e = tid + 256 * k;
         tile[e % kHB][e / kHB] = v_in[k];
     }
-    for (int i = tid; i < Q; i += 256)
-        gap[i] = (starts && i < Lc && starts[(size_t)b * T + t0 + i]) ? -kSeqGap : 0.f;
+    for (int i = tid; i < Q; i += 256) gap[i] = 0.f;
+    __syncthreads();
+    if (cu && tid == 0) {  // the sequence starts inside this chunk (batch 1)
+        int lo = 1, hi = nseq;  // first s >= 1 with cu[s] >= t0 (cu is non-decreasing)
+        while (lo < hi) {
+            const int mid = (lo + hi) / 2;
+            if (cu[mid] < t0) lo = mid + 1;
+            else hi = mid;
+        }
+        for (int q = lo; q < nseq && cu[q] < t0 + Lc; ++q) gap[cu[q] - t0] = -kSeqGap;
+    }
     __syncthreads();
     const int wave = tid >> 6, lane = tid & 63;
     for (int hh = wave; hh < nh; hh += 4) {
@@ -103,22 +112,22 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const float* __restri
 }  // namespace
 
 hipError_t launch_chunk_cumsum(const Shape& s, const float* dt, const float* A, float* dtc,
-                               float* cs, hipStream_t st, const int* starts) {
+                               float* cs, hipStream_t st, const int* cu, int nseq) {
     const size_t hblocks = (size_t)(s.H + kHB - 1) / kHB;
     const unsigned blocks = (unsigned)((size_t)s.B * s.nC * hblocks);
     if (blocks == 0) return hipSuccess;
     switch (s.Q) {
         case 64:
-            chunk_cumsum_kernel<64><<<blocks, 256, 0, st>>>(dt, A, starts, dtc, cs, s.T, s.H,
-                                                             s.nC);
+            chunk_cumsum_kernel<64><<<blocks, 256, 0, st>>>(dt, A, cu, nseq, dtc, cs, s.T,
+                                                             s.H, s.nC);
             break;
         case 128:
-            chunk_cumsum_kernel<128><<<blocks, 256, 0, st>>>(dt, A, starts, dtc, cs, s.T, s.H,
-                                                             s.nC);
+            chunk_cumsum_kernel<128><<<blocks, 256, 0, st>>>(dt, A, cu, nseq, dtc, cs, s.T,
+                                                             s.H, s.nC);
             break;
         case 256:
-            chunk_cumsum_kernel<256><<<blocks, 256, 0, st>>>(dt, A, starts, dtc, cs, s.T, s.H,
-                                                             s.nC);
+            chunk_cumsum_kernel<256><<<blocks, 256, 0, st>>>(dt, A, cu, nseq, dtc, cs, s.T,
+                                                             s.H, s.nC);
             break;
         default:
             return hipErrorInvalidValue;

@@ -264,10 +264,18 @@ __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_ker
 
 // ============================================================================ chunk_state
 
-template <int Q, int N, int P, bool REV>
+// FIN: packed variable-length rows (batch 1); a workgroup per (sequence, head) takes the
+// state after the sequence's last step te, in chunk c = te / Q at offset off:
+//     exp(cs_off) E_c + sum_{i <= off} exp(cs_off - cs_i) dt_i B_i x_i^T
+// (E_c the chunk's entry state, [P][N] in bf16), written as fp32 [N][P] to `finals`; an
+// empty sequence gets zeros.  The log-decay gaps at sequence starts (chunk_cumsum.hip) drop
+// the entry state and the steps of earlier sequences by themselves.
+template <int Q, int N, int P, bool REV, bool FIN = false>
 __global__ __launch_bounds__(256) void chunk_state_mfma_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ Bm, const float* __restrict__ dtc,
-    const float* __restrict__ cs, __bf16* __restrict__ states, int T, int H, int G, int nC) {
+    const float* __restrict__ cs, __bf16* __restrict__ states, int T, int H, int G, int nC,
+    const int* __restrict__ cu = nullptr, const __bf16* __restrict__ entry = nullptr,
+    float* __restrict__ finals = nullptr) {
     constexpr int NTH = 256;
     constexpr int NB = Q / KB;
     constexpr int PT = P / 16;
@@ -282,8 +290,16 @@ __global__ __launch_bounds__(256) void chunk_state_mfma_kernel(
     __shared__ __align__(16) __bf16 Xt[2][P][LDT];
     __shared__ float s_w[Q];
 
-    const int c = blockIdx.x % nC;
-    const int bh = blockIdx.x / nC;
+    int c, bh, te = 0, sq = 0;
+    if constexpr (FIN) {
+        sq = blockIdx.x / H;
+        bh = blockIdx.x % H;  // batch 1
+        te = cu[sq + 1] - 1;  // the sequence's last step (beg > te: empty)
+        c = te >= 0 ? te / Q : 0;
+    } else {
+        c = blockIdx.x % nC;
+        bh = blockIdx.x / nC;
+    }
     const int h = bh % H;
     const int b = bh / H;
     const int g = h / (H / G);
@@ -292,11 +308,17 @@ __global__ __launch_bounds__(256) void chunk_state_mfma_kernel(
     const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     const size_t cbase = ((size_t)bh * nC + c) * Q;
     const int t0 = c * Q;
+    // FIN: steps t0 .. te (empty: none); else the whole chunk
+    const bool empty = FIN && cu[sq + 1] <= cu[sq];
+    const int off = FIN ? (empty ? -1 : te - t0) : Q - 1;
+    const int tlim = FIN ? t0 + off : T - 1;  // last step read
 
-    // decay to the chunk end times dt, per step (fp32)
-    const float cs_last = cs[cbase + Q - 1];
+    // decay to the last step times dt, per step (fp32)
+    const float cs_last = off >= 0 ? cs[cbase + off] : 0.f;
     for (int i = tid; i < Q; i += NTH)
-        s_w[i] = REV ? expf(cs[cbase + i]) : expf(cs_last - cs[cbase + i]) * dtc[cbase + i];
+        s_w[i] = i > off ? 0.f
+                 : REV   ? expf(cs[cbase + i])
+                         : expf(cs_last - cs[cbase + i]) * dtc[cbase + i];
 
     uint4 rb[BPT][2], rx[XPT][2];
     auto load = [&](int ib) {
@@ -308,8 +330,8 @@ __global__ __launch_bounds__(256) void chunk_state_mfma_kernel(
             rb[q][0] = rb[q][1] = make_uint4(0, 0, 0, 0);
             if (e < BTASK) {
                 const __bf16* src = Bm + ((size_t)(b * T + t) * G + g) * N + cg * 8;
-                if (t < T) rb[q][0] = *reinterpret_cast<const uint4*>(src);
-                if (t + 1 < T) rb[q][1] = *reinterpret_cast<const uint4*>(src + (size_t)G * N);
+                if (t <= tlim) rb[q][0] = *reinterpret_cast<const uint4*>(src);
+                if (t + 1 <= tlim) rb[q][1] = *reinterpret_cast<const uint4*>(src + (size_t)G * N);
             }
         }
 #pragma unroll
@@ -320,8 +342,8 @@ __global__ __launch_bounds__(256) void chunk_state_mfma_kernel(
             rx[q][0] = rx[q][1] = make_uint4(0, 0, 0, 0);
             if (e < XTASK) {
                 const __bf16* src = x + ((size_t)(b * T + t) * H + h) * P + cg * 8;
-                if (t < T) rx[q][0] = *reinterpret_cast<const uint4*>(src);
-                if (t + 1 < T) rx[q][1] = *reinterpret_cast<const uint4*>(src + (size_t)H * P);
+                if (t <= tlim) rx[q][0] = *reinterpret_cast<const uint4*>(src);
+                if (t + 1 <= tlim) rx[q][1] = *reinterpret_cast<const uint4*>(src + (size_t)H * P);
             }
         }
     };
@@ -357,14 +379,32 @@ __global__ __launch_bounds__(256) void chunk_state_mfma_kernel(
     for (int a = 0; a < NTW; ++a)
 #pragma unroll
         for (int p = 0; p < PT; ++p) acc[a][p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (FIN) {  // the entry state decayed to the last step
+        if (!empty) {
+            const float de = expf(cs_last);
+            const __bf16* E = entry + ((size_t)bh * nC + c) * P * N;
+#pragma unroll
+            for (int a = 0; a < NTW; ++a)
+#pragma unroll
+                for (int p = 0; p < PT; ++p) {
+                    const int n0 = (wave * NTW + a) * 16 + 4 * g4;
+                    const uint2 e2 =
+                        *reinterpret_cast<const uint2*>(E + (size_t)(p * 16 + l16) * N + n0);
+                    acc[a][p] = f32x4{de * bf16_lo(e2.x), de * bf16_hi(e2.x),
+                                      de * bf16_lo(e2.y), de * bf16_hi(e2.y)};
+                }
+        }
+    }
+    // 32-step blocks that hold a step to take
+    const int nbk = FIN ? (off + KB) / KB : NB;
 
     load(0);
     lds_barrier();  // s_w ready
     store(0, 0);
     lds_barrier();
-    for (int ib = 0; ib < NB; ++ib) {
+    for (int ib = 0; ib < nbk; ++ib) {
         const int buf = ib & 1;
-        if (ib + 1 < NB) load(ib + 1);
+        if (ib + 1 < nbk) load(ib + 1);
         bf16x8 bx[PT];
 #pragma unroll
         for (int p = 0; p < PT; ++p)
@@ -376,8 +416,21 @@ __global__ __launch_bounds__(256) void chunk_state_mfma_kernel(
 #pragma unroll
             for (int p = 0; p < PT; ++p) acc[a][p] = mfma16(ba, bx[p], acc[a][p]);
         }
-        if (ib + 1 < NB) store(buf ^ 1, ib + 1);
+        if (ib + 1 < nbk) store(buf ^ 1, ib + 1);
         lds_barrier();
+    }
+    if constexpr (FIN) {  // fp32 [N][P] per (sequence, head)
+        float* out = finals + ((size_t)sq * H + h) * N * P;
+#pragma unroll
+        for (int a = 0; a < NTW; ++a)
+#pragma unroll
+            for (int p = 0; p < PT; ++p) {
+                const int n0 = (wave * NTW + a) * 16 + 4 * g4;
+                const int pp = p * 16 + l16;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) out[(size_t)(n0 + r) * P + pp] = acc[a][p][r];
+            }
+        return;
     }
     // lane holds S[n = tile*16 + 4*g4 + r][p = pt*16 + l16]; layout [p][n]
     __bf16* out = states + ((size_t)bh * nC + c) * P * N;
@@ -393,6 +446,45 @@ __global__ __launch_bounds__(256) void chunk_state_mfma_kernel(
 }
 
 // ---------------------------------------------------------------- dispatch tables
+
+template <int Q, int N, int P>
+hipError_t launch_final_t(const Shape& s, const void* x, const void* Bm, const float* dtc,
+                          const float* cs, const void* entry, const int* cu, int nseq,
+                          float* finals, hipStream_t st) {
+    chunk_state_mfma_kernel<Q, N, P, false, true><<<(unsigned)((size_t)nseq * s.H), 256, 0, st>>>(
+        (const __bf16*)x, (const __bf16*)Bm, dtc, cs, nullptr, s.T, s.H, s.G, s.nC, cu,
+        (const __bf16*)entry, finals);
+    return hipGetLastError();
+}
+using FinalFn = hipError_t (*)(const Shape&, const void*, const void*, const float*,
+                               const float*, const void*, const int*, int, float*, hipStream_t);
+template <int Q>
+FinalFn pick_final_q(const Shape& s) {
+    switch (s.N) {
+#define SSD_FIN_N(NV)                                         \
+    case NV:                                                  \
+        switch (s.P) {                                        \
+            case 16: return launch_final_t<Q, NV, 16>;        \
+            case 32: return launch_final_t<Q, NV, 32>;        \
+            case 64: return launch_final_t<Q, NV, 64>;        \
+            case 128: return launch_final_t<Q, NV, 128>;      \
+        }                                                     \
+        break;
+        SSD_FIN_N(64)
+        SSD_FIN_N(128)
+        SSD_FIN_N(256)
+#undef SSD_FIN_N
+    }
+    return nullptr;
+}
+FinalFn pick_final(const Shape& s) {
+    switch (s.Q) {
+        case 64: return pick_final_q<64>(s);
+        case 128: return pick_final_q<128>(s);
+        case 256: return pick_final_q<256>(s);
+    }
+    return nullptr;
+}
 
 template <int Q, int N, int P, bool REV>
 hipError_t launch_state_t(const Shape& s, const void* x, const void* Bm, const float* dtc,
@@ -500,6 +592,17 @@ StateFn pick_state(const Shape& s) {
 }  // namespace
 
 bool chunk_state_mfma_supported(const Shape& s) { return pick_state<false>(s) != nullptr; }
+
+bool varlen_final_mfma_supported(const Shape& s) { return pick_final(s) != nullptr; }
+
+hipError_t launch_varlen_final_mfma(const Shape& s, const void* x, const void* Bm,
+                                    const float* dtc, const float* cs, const void* entry,
+                                    const int* cu, int nseq, float* finals, hipStream_t st) {
+    const FinalFn f = pick_final(s);
+    if (!f) return hipErrorInvalidValue;
+    if (nseq <= 0 || s.H <= 0) return hipSuccess;
+    return f(s, x, Bm, dtc, cs, entry, cu, nseq, finals, st);
+}
 
 bool chunk_state_writes_gram(const Shape& s) {
     return state_offsets_fit(s) && s.Q == 256 && (s.N == 64 || s.N == 128) &&

@@ -289,11 +289,17 @@ size_t ssd_bwd_workspace_size(const ssd_dims* dims, int chunk_len) {
     return bwd_workspace_bytes(s, nullptr, nullptr);
 }
 
-ssd_status ssd_bwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const float* dt,
-                   const float* A, const void* B, const void* C, const float* D, int chunk_len,
-                   const float* init_state, const void* dy, const float* d_final, void* dx,
-                   float* ddt, float* dA, void* dB, void* dC, float* dD, float* d_init,
-                   void* workspace, size_t workspace_bytes_given, void* stream) {
+}  // extern "C"
+
+namespace {
+// fwd_ws: the workspace of an ssd_fwd call on the same inputs (its log decays and entry
+// states are read instead of recomputed), or null
+ssd_status bwd_impl(const ssd_dims* dims, ssd_dtype dtype, const void* x, const float* dt,
+                    const float* A, const void* B, const void* C, const float* D, int chunk_len,
+                    const float* init_state, const void* dy, const float* d_final,
+                    const void* fwd_ws, void* dx, float* ddt, float* dA, void* dB, void* dC,
+                    float* dD, float* d_init, void* workspace, size_t workspace_bytes_given,
+                    void* stream) {
     Shape s;
     ssd_status r = make_shape(dims, chunk_len, &s);
     if (r != SSD_OK) return r;
@@ -302,23 +308,32 @@ ssd_status ssd_bwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const f
     if (!dA || !dD) return SSD_ERR_NULL;
     if (has_tokens && (!x || !dt || !A || !B || !C || !D || !dy || !dx || !ddt || !dB || !dC))
         return SSD_ERR_NULL;
-    if (any_misaligned({x, B, C, dy, dx, dB, dC, workspace}) ||
+    if (any_misaligned({x, B, C, dy, dx, dB, dC, workspace, fwd_ws}) ||
         any_misaligned4({dt, A, D, init_state, d_final, ddt, dA, dD, d_init}))
         return SSD_ERR_ALIGN;
     BwdWorkspace ws;
     const size_t need = bwd_workspace_bytes(s, &ws, (char*)workspace);
     if (need > 0 && (!workspace || workspace_bytes_given < need)) return SSD_ERR_WORKSPACE;
+    if (fwd_ws) {  // the forward's own log decays and entry states
+        Workspace fws;
+        workspace_bytes(s, &fws, (char*)const_cast<void*>(fwd_ws));
+        ws.dtc = fws.dtc;
+        ws.cs = fws.cs;
+        ws.entry = fws.entry;
+    }
     hipStream_t st = (hipStream_t)stream;
     const bool mfma_state = dtype == SSD_BF16 && ssd::chunk_state_mfma_supported(s);
     if (has_tokens) {
-        // the forward intermediates: log decays, chunk states, entry states
-        r = hip_status(ssd::launch_chunk_cumsum(s, dt, A, ws.dtc, ws.cs, st));
-        if (r != SSD_OK) return r;
-        r = run_chunk_state(s, dtype, x, B, ws.dtc, ws.cs, ws.states, nullptr, nullptr, st);
-        if (r != SSD_OK) return r;
-        r = hip_status(ssd::launch_state_passing(s, dtype, ws.states, ws.cs, init_state,
-                                                 ws.entry, nullptr, st));
-        if (r != SSD_OK) return r;
+        if (!fwd_ws) {
+            // the forward intermediates: log decays, chunk states, entry states
+            r = hip_status(ssd::launch_chunk_cumsum(s, dt, A, ws.dtc, ws.cs, st));
+            if (r != SSD_OK) return r;
+            r = run_chunk_state(s, dtype, x, B, ws.dtc, ws.cs, ws.states, nullptr, nullptr, st);
+            if (r != SSD_OK) return r;
+            r = hip_status(ssd::launch_state_passing(s, dtype, ws.states, ws.cs, init_state,
+                                                     ws.entry, nullptr, st));
+            if (r != SSD_OK) return r;
+        }
         // the entry-state gradient of every chunk through its own outputs (into the chunk
         // state buffer, no longer needed)
         r = hip_status(mfma_state
@@ -348,6 +363,30 @@ ssd_status ssd_bwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const f
     }
     // dA and dD are written even with no tokens (zeros)
     return hip_status(ssd::launch_bwd_finalize(s, a, rows, st));
+}
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_bwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const float* dt,
+                   const float* A, const void* B, const void* C, const float* D, int chunk_len,
+                   const float* init_state, const void* dy, const float* d_final, void* dx,
+                   float* ddt, float* dA, void* dB, void* dC, float* dD, float* d_init,
+                   void* workspace, size_t workspace_bytes_given, void* stream) {
+    return bwd_impl(dims, dtype, x, dt, A, B, C, D, chunk_len, init_state, dy, d_final, nullptr,
+                    dx, ddt, dA, dB, dC, dD, d_init, workspace, workspace_bytes_given, stream);
+}
+
+ssd_status ssd_bwd_saved(const ssd_dims* dims, ssd_dtype dtype, const void* x, const float* dt,
+                         const float* A, const void* B, const void* C, const float* D,
+                         int chunk_len, const float* init_state, const void* dy,
+                         const float* d_final, const void* fwd_workspace, void* dx, float* ddt,
+                         float* dA, void* dB, void* dC, float* dD, float* d_init,
+                         void* workspace, size_t workspace_bytes_given, void* stream) {
+    if (!fwd_workspace) return SSD_ERR_NULL;
+    return bwd_impl(dims, dtype, x, dt, A, B, C, D, chunk_len, init_state, dy, d_final,
+                    fwd_workspace, dx, ddt, dA, dB, dC, dD, d_init, workspace,
+                    workspace_bytes_given, stream);
 }
 
 ssd_status ssd_decode_step(const ssd_dims* dims, ssd_dtype dtype, const void* x, const float* dt,
@@ -505,7 +544,7 @@ ssd_status ssd_block_fwd(const ssd_dims* dims, ssd_dtype dtype, const void* zxbc
 size_t ssd_fwd_varlen_workspace_size(const ssd_dims* dims, int chunk_len) {
     Shape s;
     if (make_shape(dims, chunk_len, &s) != SSD_OK || dims->batch != 1) return 0;
-    return workspace_bytes(s, nullptr, nullptr) + round_up((size_t)s.T * sizeof(int));
+    return workspace_bytes(s, nullptr, nullptr);
 }
 
 ssd_status ssd_fwd_varlen(const ssd_dims* dims, ssd_dtype dtype, const void* x, const float* dt,
@@ -525,16 +564,12 @@ ssd_status ssd_fwd_varlen(const ssd_dims* dims, ssd_dtype dtype, const void* x, 
         any_misaligned4({dt, A, D, cu_seqlens, final_states}))
         return SSD_ERR_ALIGN;
     Workspace ws;
-    const size_t fwd = workspace_bytes(s, &ws, (char*)workspace);
-    const size_t need = fwd + round_up((size_t)s.T * sizeof(int));
+    const size_t need = workspace_bytes(s, &ws, (char*)workspace);
     if (need > 0 && (!workspace || workspace_bytes_given < need)) return SSD_ERR_WORKSPACE;
-    int* starts = (int*)((char*)workspace + fwd);
     hipStream_t st = (hipStream_t)stream;
     const int ns = (int)nseq;
     if (has_tokens) {
-        r = hip_status(ssd::launch_seq_starts(cu_seqlens, ns, starts, s.T, st));
-        if (r != SSD_OK) return r;
-        r = hip_status(ssd::launch_chunk_cumsum(s, dt, A, ws.dtc, ws.cs, st, starts));
+        r = hip_status(ssd::launch_chunk_cumsum(s, dt, A, ws.dtc, ws.cs, st, cu_seqlens, ns));
         if (r != SSD_OK) return r;
         r = run_chunk_state(s, dtype, x, B, ws.dtc, ws.cs, ws.states, C, ws.gram, st);
         if (r != SSD_OK) return r;
@@ -545,6 +580,9 @@ ssd_status ssd_fwd_varlen(const ssd_dims* dims, ssd_dtype dtype, const void* x, 
         if (r != SSD_OK) return r;
     }
     if (!final_states) return SSD_OK;
+    if (dtype == SSD_BF16 && has_tokens && ssd::varlen_final_mfma_supported(s))
+        return hip_status(ssd::launch_varlen_final_mfma(s, x, B, ws.dtc, ws.cs, ws.entry,
+                                                        cu_seqlens, ns, final_states, st));
     return hip_status(ssd::launch_varlen_final(s, dtype, x, B, ws.dtc, ws.cs, ws.entry,
                                                cu_seqlens, ns, final_states, st));
 }

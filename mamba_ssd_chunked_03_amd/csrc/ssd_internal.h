@@ -23,10 +23,11 @@ template <> __device__ __forceinline__ float from_f32<float>(float v) { return v
 template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float v) { return (__bf16)v; }
 
 // ---- launchers (each returns the launch status) -------------------------------------
-// starts (optional, [B][T] int): 1 where a packed sequence begins; the running sum then
-// drops by a gap that zeroes every decay across the start
+// cu (optional, device [nseq + 1], batch 1): packed sequence offsets; at every sequence
+// start the running sum drops by a gap that zeroes every decay across the start
 hipError_t launch_chunk_cumsum(const Shape& s, const float* dt, const float* A, float* dtc,
-                               float* cs, hipStream_t st, const int* starts = nullptr);
+                               float* cs, hipStream_t st, const int* cu = nullptr,
+                               int nseq = 0);
 // chunk states are read and entry states written in dtype (fp32 or bf16); the carried
 // state is fp32
 hipError_t launch_state_passing(const Shape& s, ssd_dtype dtype, const void* states,
@@ -107,8 +108,12 @@ hipError_t launch_chunk_bwd_mfma(const Shape& s, const BwdArgs& a, hipStream_t s
 hipError_t launch_bwd_finalize(const Shape& s, const BwdArgs& a, int rows, hipStream_t st);
 
 // ---- packed variable-length rows (varlen.hip) -------------------------------------------
-// starts[t] = 1 where sequence s >= 1 begins (cu_seqlens[s] == t), else 0
-hipError_t launch_seq_starts(const int* cu, int nseq, int* starts, int T, hipStream_t st);
+// the same on bf16 MFMA (the per-item chunk-state kernel in its final-state mode), for the
+// sizes it is instantiated for
+bool varlen_final_mfma_supported(const Shape& s);
+hipError_t launch_varlen_final_mfma(const Shape& s, const void* x, const void* Bm,
+                                    const float* dtc, const float* cs, const void* entry,
+                                    const int* cu, int nseq, float* finals, hipStream_t st);
 // each sequence's state after its last step, [nseq][H][N][P] fp32 (zeros for an empty one)
 hipError_t launch_varlen_final(const Shape& s, ssd_dtype dtype, const void* x, const void* Bm,
                                const float* dtc, const float* cs, const void* entry,

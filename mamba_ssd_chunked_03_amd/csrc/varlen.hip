@@ -4,10 +4,10 @@
 // reproduction page for arXiv 2405.21060 describes context parallelism as passing states
 // between contiguous pieces of one sequence).
 //
-// The forward stages run unchanged on the row: chunk_cumsum is given the sequence starts
-// and drops the running log-decay sum by a fixed gap at each, which zeroes every decay
-// across a start (see chunk_cumsum.hip).  Two small kernels live here:
-//   seq_starts_kernel   starts[t] = 1 where some sequence s >= 1 begins at step t
+// The forward stages run unchanged on the row: chunk_cumsum is given the sequence offsets
+// and drops the running log-decay sum by a fixed gap at each start, which zeroes every
+// decay across a start (see chunk_cumsum.hip).  Here, for fp32 and for the sizes without a
+// bf16 matrix-core instantiation (chunk_mfma.hip has the MFMA one):
 //   varlen_final_kernel the state after each sequence's last step t_s, in chunk c:
 //     final_s = exp(cs[t_s]) E_c + sum_{i <= t_s in chunk c} exp(cs[t_s] - cs_i) dt_i B_i x_i^T
 //     (E_c the chunk's entry state; with the gaps in cs, the entry state and the steps of
@@ -19,21 +19,6 @@ namespace ssd {
 namespace {
 
 constexpr int kThreads = 256;
-
-__global__ __launch_bounds__(kThreads) void seq_starts_kernel(const int* __restrict__ cu,
-                                                              int nseq, int* __restrict__ starts,
-                                                              int T) {
-    const int t = blockIdx.x * kThreads + threadIdx.x;
-    if (t >= T) return;
-    // first s in [1, nseq) with cu[s] >= t (cu is non-decreasing)
-    int lo = 1, hi = nseq;
-    while (lo < hi) {
-        const int mid = (lo + hi) / 2;
-        if (cu[mid] < t) lo = mid + 1;
-        else hi = mid;
-    }
-    starts[t] = (lo < nseq && cu[lo] == t) ? 1 : 0;
-}
 
 template <typename Tin>
 __global__ __launch_bounds__(kThreads) void varlen_final_kernel(
@@ -117,13 +102,6 @@ __global__ __launch_bounds__(kThreads) void varlen_final_kernel(
 }
 
 }  // namespace
-
-hipError_t launch_seq_starts(const int* cu, int nseq, int* starts, int T, hipStream_t st) {
-    if (T <= 0) return hipSuccess;
-    seq_starts_kernel<<<(unsigned)((T + kThreads - 1) / kThreads), kThreads, 0, st>>>(
-        cu, nseq, starts, T);
-    return hipGetLastError();
-}
 
 hipError_t launch_varlen_final(const Shape& s, ssd_dtype dtype, const void* x, const void* Bm,
                                const float* dtc, const float* cs, const void* entry,

@@ -265,6 +265,16 @@ def test_varlen_validation_errors_before_any_launch(lib):
     assert call(D(), cu=258) == 4 and call(D(), x=264) == 4
     assert call(D(), ws=None) == 5 and call(D(), ws_bytes=16) == 5
     d = D()
-    assert binding.ssd_fwd_varlen_workspace_size(d, 64) == \
-        binding.ssd_fwd_workspace_size(d, 64) + (256 * 4 + 255) // 256 * 256
+    assert binding.ssd_fwd_varlen_workspace_size(d, 64) == binding.ssd_fwd_workspace_size(d, 64)
     assert binding.ssd_fwd_varlen_workspace_size(D(b=2), 64) == 0
+
+
+def test_bwd_saved_needs_the_forward_workspace(lib):
+    ok = [ctypes.c_void_p(256)] * 6
+    # fwd_workspace NULL is an error before anything else is read
+    assert lib.ssd_bwd_saved(ctypes.byref(D()), 1, *ok, 64, None, ctypes.c_void_p(256), None,
+                             None, *[ctypes.c_void_p(256)] * 7, ctypes.c_void_p(256), 1 << 30,
+                             None) == 1
+    assert lib.ssd_bwd_saved(ctypes.byref(D()), 1, *ok, 64, None, ctypes.c_void_p(256), None,
+                             ctypes.c_void_p(264), *[ctypes.c_void_p(256)] * 7,
+                             ctypes.c_void_p(256), 1 << 30, None) == 4

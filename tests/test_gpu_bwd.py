@@ -128,3 +128,26 @@ def test_bwd_full_size_workloads(name):
     up = generate_grads(w)
     g = gpu_bwd(w, cpu, up)
     compare(w, g, oracle_bwd(cpu, up))
+
+
+@pytest.mark.parametrize("w", [STRESS["slow_decay"], CASES[0], CASES[-1]],
+                         ids=["slow_decay", "tiny_fp32", "bwd_g2_q256"])
+def test_bwd_saved_equals_recompute(w):
+    """ssd_bwd_saved (the forward's intermediates read from its workspace) gives the same
+    bits as ssd_bwd (which recomputes them)."""
+    cpu = generate(w)
+    up = generate_grads(w)
+    d = to_device(cpu)
+    u = to_device(up)
+    dims = binding.dims_of(d["x"], d["B"])
+    fws = torch.empty(max(1, binding.ssd_fwd_workspace_size(dims, w.chunk_len)),
+                      dtype=torch.uint8, device="cuda")
+    binding.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], w.chunk_len,
+                    init_state=d["init_state"], workspace=fws)
+    a = binding.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], w.chunk_len, u["dy"],
+                        init_state=d["init_state"], d_final=u["d_final"])
+    b = binding.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], w.chunk_len, u["dy"],
+                        init_state=d["init_state"], d_final=u["d_final"], fwd_workspace=fws)
+    torch.cuda.synchronize()
+    for k in GRADS:
+        assert torch.equal(a[k], b[k]), k
