@@ -5,13 +5,15 @@
 // "The 1-Semiseparable Matrix": entries a_j ... a_{i+1} become exp(cs_j - cs_i) with
 // cs the running sum of log a = dt*A inside the chunk.
 //
-// One workgroup of 256 threads per (b, chunk, block of 16 heads).  dt is [B][T][H], so a
+// One workgroup of 16 waves per (b, chunk, block of 16 heads).  dt is [B][T][H], so a
 // chunk's steps for a block of heads are Q rows of 64 contiguous bytes: the workgroup
-// reads them coalesced into an LDS tile [head][time], then each wave takes whole heads:
-// a lane holds Q/64 consecutive steps, scans them serially, and a 64-wide shuffle scan
-// adds the carry of the lanes before it.  It writes the chunk-major copy
-// dt_chunk[b][h][c][i] that the later kernels read contiguously, and the inclusive prefix
-// sum cs of dt*A over the chunk, both as contiguous rows.
+// reads them coalesced into an LDS tile [head][time], then wave w takes head w: a lane
+// holds Q/64 consecutive steps, scans them serially, and a 64-wide shuffle scan adds the
+// carry of the lanes before it.  It writes the chunk-major copy dt_chunk[b][h][c][i] that
+// the later kernels read contiguously, and the inclusive prefix sum cs of dt*A over the
+// chunk, both as contiguous rows (one vector store per lane each).  The kernel is
+// latency-bound: every load is issued before any is used, and all heads of the block are
+// scanned at once.
 //
 // Packed variable-length rows (cu != null, batch 1): a step where a sequence s >= 1 begins
 // (cu[s]) adds -kSeqGap to the running sum.  Every decay exp(cs_j - cs_i) between two steps of
@@ -25,13 +27,14 @@
 namespace ssd {
 namespace {
 
-constexpr int kHB = 16;  // heads per workgroup
+constexpr int kHB = 16;  // heads per workgroup, one wave each
+constexpr int kThreads = kHB * 64;
 // log-decay gap at a packed sequence start: exp2(-kSeqGap log2 e) is below the smallest
 // fp32 subnormal, so every decay across a start is exactly zero
 constexpr float kSeqGap = 120.f;
 
 template <int Q>
-__global__ __launch_bounds__(256) void chunk_cumsum_kernel(const float* __restrict__ dt,
+__global__ __launch_bounds__(kThreads) void chunk_cumsum_kernel(const float* __restrict__ dt,
                                                            const float* __restrict__ A,
                                                            const int* __restrict__ cu, int nseq,
                                                            float* __restrict__ dtc,
@@ -52,22 +55,21 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const float* __restri
     const int Lc = min(Q, T - t0);
     const int tid = threadIdx.x;
     const float* src = dt + ((size_t)b * T + t0) * H + h0;
-    // element e = tid + 256 k of the Q x 16 tile: all loads are issued before any is used
-    // (the kernel is latency-bound)
-    constexpr int L = Q * kHB / 256;
+    // element e = tid + kThreads k of the Q x 16 tile
+    constexpr int L = Q * kHB / kThreads;
     float v_in[L];
 #pragma unroll
     for (int k = 0; k < L; ++k) {
-        const int e = tid + 256 * k;
+        const int e = tid + kThreads * k;
         const int t = e / kHB, hh = e % kHB;
         v_in[k] = (t < Lc && hh < nh) ? src[(size_t)t * H + hh] : 0.0f;
     }
 #pragma unroll
     for (int k = 0; k < L; ++k) {
-        const int e = tid + 256 * k;
+        const int e = tid + kThreads * k;
         tile[e % kHB][e / kHB] = v_in[k];
     }
-    for (int i = tid; i < Q; i += 256) gap[i] = 0.f;
+    if (tid < Q) gap[tid] = 0.f;
     __syncthreads();
     if (cu && tid == 0) {  // the sequence starts inside this chunk (batch 1)
         int lo = 1, hi = nseq;  // first s >= 1 with cu[s] >= t0 (cu is non-decreasing)
@@ -79,32 +81,42 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const float* __restri
         for (int q = lo; q < nseq && cu[q] < t0 + Lc; ++q) gap[cu[q] - t0] = -kSeqGap;
     }
     __syncthreads();
-    const int wave = tid >> 6, lane = tid & 63;
-    for (int hh = wave; hh < nh; hh += 4) {
-        const int h = h0 + hh;
-        const float a = A[h];
-        float v[E], run[E];
+    const int hh = tid >> 6, lane = tid & 63;
+    if (hh >= nh) return;
+    const int h = h0 + hh;
+    const float a = A[h];
+    float v[E], run[E];
 #pragma unroll
-        for (int k = 0; k < E; ++k) v[k] = tile[hh][lane * E + k];
-        float acc = 0.0f;
+    for (int k = 0; k < E; ++k) v[k] = tile[hh][lane * E + k];
+    float acc = 0.0f;
 #pragma unroll
-        for (int k = 0; k < E; ++k) {
-            acc += fmaf(v[k], a, gap[lane * E + k]);
-            run[k] = acc;
-        }
-        // exclusive carry from the lanes before this one
-        float incl = acc;
+    for (int k = 0; k < E; ++k) {
+        acc += fmaf(v[k], a, gap[lane * E + k]);
+        run[k] = acc;
+    }
+    // exclusive carry from the lanes before this one
+    float incl = acc;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float o = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += o;
-        }
-        const float carry = incl - acc;
-        const size_t o = (((size_t)b * H + h) * nC + c) * Q + lane * E;
+    for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    const float carry = incl - acc;
+#pragma unroll
+    for (int k = 0; k < E; ++k) run[k] += carry;
+    // rows of Q floats: the lane's E steps are contiguous and 4 E-byte aligned
+    const size_t o = (((size_t)b * H + h) * nC + c) * Q + lane * E;
+    if constexpr (E == 4) {
+        *reinterpret_cast<float4*>(dtc + o) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(cs + o) = make_float4(run[0], run[1], run[2], run[3]);
+    } else if constexpr (E == 2) {
+        *reinterpret_cast<float2*>(dtc + o) = make_float2(v[0], v[1]);
+        *reinterpret_cast<float2*>(cs + o) = make_float2(run[0], run[1]);
+    } else {
 #pragma unroll
         for (int k = 0; k < E; ++k) {
             dtc[o + k] = v[k];
-            cs[o + k] = run[k] + carry;
+            cs[o + k] = run[k];
         }
     }
 }
@@ -118,15 +130,15 @@ hipError_t launch_chunk_cumsum(const Shape& s, const float* dt, const float* A, 
     if (blocks == 0) return hipSuccess;
     switch (s.Q) {
         case 64:
-            chunk_cumsum_kernel<64><<<blocks, 256, 0, st>>>(dt, A, cu, nseq, dtc, cs, s.T,
+            chunk_cumsum_kernel<64><<<blocks, kThreads, 0, st>>>(dt, A, cu, nseq, dtc, cs, s.T,
                                                              s.H, s.nC);
             break;
         case 128:
-            chunk_cumsum_kernel<128><<<blocks, 256, 0, st>>>(dt, A, cu, nseq, dtc, cs, s.T,
+            chunk_cumsum_kernel<128><<<blocks, kThreads, 0, st>>>(dt, A, cu, nseq, dtc, cs, s.T,
                                                              s.H, s.nC);
             break;
         case 256:
-            chunk_cumsum_kernel<256><<<blocks, 256, 0, st>>>(dt, A, cu, nseq, dtc, cs, s.T,
+            chunk_cumsum_kernel<256><<<blocks, kThreads, 0, st>>>(dt, A, cu, nseq, dtc, cs, s.T,
                                                              s.H, s.nC);
             break;
         default:
