@@ -7,12 +7,13 @@
 // the slow (row) dimension of B and x in HBM, so both operands pass through LDS.
 //
 // Two kernels:
-//   chunk_state_pipe_kernel (N = 128, P <= 64; N = 64, P in {32, 64}): persistent and
-//     pipelined.  A workgroup per
-//     CU walks a run of (unit, head) items, a unit being one (batch, group, chunk).  The
-//     unit's B chunk is copied into LDS once and read out through transpose reads into
-//     register fragments (one 16-row n-tile per wave, all 32-step blocks), after which
-//     the next unit's B is copied in behind it.  Each item's x, cs and dt are copied into
+//   chunk_state_pipe_kernel (N = 128 or 256, P <= 64; N = 64, P in {32, 64}): persistent
+//     and pipelined.  A workgroup per CU walks a run of (unit, head) items, a unit being
+//     one (batch, group, chunk).  The unit's B chunk is copied into LDS once and read out
+//     through transpose reads into register fragments (one 16-row n-tile per wave, two at
+//     N = 256, all 32-step blocks), after which the next unit's B is copied in behind it.
+//     At N = 256 the B chunk (128 KB at Q = 256) passes in two column slices of 128, the
+//     second copied when the unit begins, so that the LDS holds one slice and two items.  Each item's x, cs and dt are copied into
 //     a double-buffered LDS while the previous item computes.  The per-step weight
 //     exp(cs_last - cs_i) dt_i is applied to the B fragments (rounded to bf16 once per
 //     item), and x^T comes out of LDS through transpose reads.
@@ -47,14 +48,18 @@ __device__ __forceinline__ uint32_t bits_of(const uint4& v, int k) {
 // ============================================================================ pipelined
 template <int Q, int N, int P>
 struct StateCfg {
-    static constexpr int NW = N / 16;  // waves: one 16-row n-tile each
+    static constexpr int NW = N < 128 ? N / 16 : 8;  // waves
+    static constexpr int NTW = N / 16 / NW;           // 16-row n-tiles per wave
     static constexpr int NTH = NW * 64;
     static constexpr int NB = Q / KB;
-    static constexpr int PT = P / 16, PPR = P / 8, NPR = N / 8;
-    static constexpr unsigned XB = Q * P * 2, BB = Q * N * 2, FB = Q * 4;
+    static constexpr int PT = P / 16, PPR = P / 8;
+    // B passes through LDS in column slices of at most 128 (one slice per n-tile of a wave)
+    static constexpr int BW = N < 128 ? N : 128, NS = N / BW, BPR = BW / 8;
+    static constexpr unsigned XB = Q * P * 2, BB = Q * BW * 2, FB = Q * 4;
     static constexpr unsigned ITEM = XB + 2 * FB;  // x, cs, dt
     static constexpr unsigned LDS = BB + 2 * ITEM + FB;
-    static constexpr int STORES = PT;  // state stores per wave per item
+    static constexpr int STORES = PT * NTW;  // state stores per wave per item
+    static_assert(NS == NTW, "one B slice per n-tile of a wave");
 };
 
 template <int Q, int N, int P>
@@ -80,20 +85,23 @@ __device__ __forceinline__ void state_issue_x(const __bf16* x, const float* cs, 
     if (wave == 1 && lane < Q / 4) dma16(raw_rsrc(dtc + sb, C_::FB), lds + C_::XB + C_::FB, lane * 16u);
 }
 
+// columns [BW sl, BW sl + BW) of the unit's B chunk into the B region ([time][BW], swizzled)
 template <int Q, int N, int P>
-__device__ __forceinline__ void state_issue_b(const __bf16* Bm, int unit, int T, int G, int nC,
-                                              uint32_t lds, int wave, int lane) {
+__device__ __forceinline__ void state_issue_b(const __bf16* Bm, int unit, int slice, int T, int G,
+                                              int nC, uint32_t lds, int wave, int lane) {
     using C_ = StateCfg<Q, N, P>;
     const int c = unit % nC, g = (unit / nC) % G, b = unit / nC / G;
     const int Lc = min(Q, T - c * Q);
     const unsigned rowb = (unsigned)(G * N * 2);
     const u32x4 br = raw_rsrc(Bm + ((size_t)(b * T + c * Q) * G + g) * N, (unsigned)Lc * rowb);
-    constexpr int BI = Q * C_::NPR / 64;
+    const unsigned col0 = (unsigned)slice * C_::BW * 2u;
+    constexpr int BI = Q * C_::BPR / 64;
 #pragma unroll
     for (int k = wave; k < BI; k += C_::NW) {
         const int m = k * 64 + lane;
-        const int r = m / C_::NPR, sl = m % C_::NPR;
-        dma16(br, lds + k * 1024, (unsigned)r * rowb + (unsigned)(sl ^ (r & (C_::NPR - 1))) * 16u);
+        const int r = m / C_::BPR, sl = m % C_::BPR;
+        dma16(br, lds + k * 1024,
+              (unsigned)r * rowb + col0 + (unsigned)(sl ^ (r & (C_::BPR - 1))) * 16u);
     }
 }
 
@@ -109,10 +117,10 @@ __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_ker
     const float* __restrict__ cs, __bf16* __restrict__ states, const __bf16* __restrict__ Cm,
     uint4* __restrict__ gram, int T, int H, int G, int nC, int nslots) {
     using C_ = StateCfg<Q, N, P>;
-    constexpr int NB = C_::NB, PT = C_::PT, PPR = C_::PPR, NPR = C_::NPR;
+    constexpr int NB = C_::NB, PT = C_::PT, PPR = C_::PPR, BPR = C_::BPR, NTW = C_::NTW;
     extern __shared__ __align__(16) unsigned char smem[];
     const uint32_t lds0 = lds_addr(smem);
-    unsigned char* const sB = smem;                    // B chunk of the next unit, [time][n]
+    unsigned char* const sB = smem;                    // a B slice of the unit, [time][BW]
     unsigned char* const sX = smem + C_::BB;           // two item buffers: x, cs, dt
     float* const s_w = reinterpret_cast<float*>(smem + C_::BB + 2 * C_::ITEM);
 
@@ -129,18 +137,19 @@ __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_ker
     const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
 
     // transpose-read offsets (rows 4 g4 + l16 / 4 of a 32-step block, column 4 (l16 % 4)
-    // within a 16-wide tile); the swizzle depends only on the row mod pieces-per-row
-    const unsigned boff = swz_off(4 * g4 + (l16 >> 2), wave * 16 + 4 * (l16 & 3), NPR);
+    // within a 16-wide tile); the swizzle depends only on the row mod pieces-per-row.  The
+    // wave's n-tile k is wave + NW k, at the same columns of B slice k.
+    const unsigned boff = swz_off(4 * g4 + (l16 >> 2), wave * 16 + 4 * (l16 & 3), BPR);
     unsigned xoff[PT];
 #pragma unroll
     for (int p = 0; p < PT; ++p) xoff[p] = swz_off(4 * g4 + (l16 >> 2), p * 16 + 4 * (l16 & 3), PPR);
-    constexpr unsigned BBLK = KB * NPR * 16, BHALF = 16 * NPR * 16;
+    constexpr unsigned BBLK = KB * BPR * 16, BHALF = 16 * BPR * 16;
     constexpr unsigned XBLK = KB * PPR * 16, XHALF = 16 * PPR * 16;
 
-    bf16x8 bt[NB];  // B^T fragments of this wave's n-tile, every 32-step block
+    bf16x8 bt[NTW][NB];  // B^T fragments of this wave's n-tiles, every 32-step block
     int cur_unit = -1;
 
-    state_issue_b<Q, N, P>(Bm, lo / hpg, T, G, nC, lds0, wave, lane);
+    state_issue_b<Q, N, P>(Bm, lo / hpg, 0, T, G, nC, lds0, wave, lane);
     state_issue_x<Q, N, P>(x, cs, dtc, lo, hpg, T, H, G, nC, lds0 + C_::BB, wave, lane);
 #pragma unroll 1
     for (int sl = lo; sl < hi; ++sl) {
@@ -155,14 +164,22 @@ __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_ker
         else
             asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::STORES) : "memory");
         const int unit = sl / hpg;
-        if (unit != cur_unit) {  // the B region holds this unit: take this wave's fragments
+        if (unit != cur_unit) {  // the B region holds slice 0 of this unit
             cur_unit = unit;
 #pragma unroll
-            for (int ib = 0; ib < NB; ++ib) {
-                const unsigned char* bp = sB + boff + ib * BBLK;
-                const uint2 lo2 = lds_read_tr16(bp);
-                const uint2 hi2 = lds_read_tr16(bp + BHALF);
-                bt[ib] = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+            for (int k = 0; k < NTW; ++k) {
+                if (k > 0) {  // slice k: copy it in now and wait for it
+                    lds_barrier();  // every wave has read slice k - 1
+                    state_issue_b<Q, N, P>(Bm, unit, k, T, G, nC, lds0, wave, lane);
+                    dma_barrier();
+                }
+#pragma unroll
+                for (int ib = 0; ib < NB; ++ib) {
+                    const unsigned char* bp = sB + boff + ib * BBLK;
+                    const uint2 lo2 = lds_read_tr16(bp);
+                    const uint2 hi2 = lds_read_tr16(bp + BHALF);
+                    bt[k][ib] = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+                }
             }
             constexpr bool kGram = (Q == 256 && (N == 64 || N == 128) && !REV);
             if (kGram && gram != nullptr && sl == unit * hpg) {
@@ -193,9 +210,9 @@ __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_ker
 #pragma unroll
                     for (int kk = 0; kk < NK; ++kk) {
                         r0[kk] = *reinterpret_cast<const bf16x8*>(
-                            sB + swz_off(ib * KB + l16, 32 * kk + 8 * g4, NPR));
+                            sB + swz_off(ib * KB + l16, 32 * kk + 8 * g4, BPR));
                         r1[kk] = *reinterpret_cast<const bf16x8*>(
-                            sB + swz_off(ib * KB + 16 + l16, 32 * kk + 8 * g4, NPR));
+                            sB + swz_off(ib * KB + 16 + l16, 32 * kk + 8 * g4, BPR));
                     }
                     auto emit = [&](const bf16x8* cc, int t) {
                         f32x4 g0 = f32x4{0.f, 0.f, 0.f, 0.f}, g1 = g0;
@@ -215,7 +232,7 @@ __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_ker
             }
             lds_barrier();  // every wave holds its fragments: the region is free
             const int nxt = (unit + 1) * hpg;
-            if (nxt < hi) state_issue_b<Q, N, P>(Bm, unit + 1, T, G, nC, lds0, wave, lane);
+            if (nxt < hi) state_issue_b<Q, N, P>(Bm, unit + 1, 0, T, G, nC, lds0, wave, lane);
         }
         if (tid < Q) {
             const float ci = b_cs[tid];
@@ -227,38 +244,49 @@ __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_ker
             state_issue_x<Q, N, P>(x, cs, dtc, sl + 1, hpg, T, H, G, nC,
                                    lds0 + C_::BB + (buf ^ 1) * C_::ITEM, wave, lane);
 
-        f32x4 acc[PT];
+        f32x4 acc[NTW][PT];
 #pragma unroll
-        for (int p = 0; p < PT; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < NTW; ++k)
+#pragma unroll
+            for (int p = 0; p < PT; ++p) acc[k][p] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ib = 0; ib < NB; ++ib) {
-            // B^T fragment weighted by exp(cs_last - cs_i) dt_i over its k-slots
+            // B^T fragments weighted by exp(cs_last - cs_i) dt_i over their k-slots
             const int i0 = ib * KB + 4 * g4;
             const float4 wa = *reinterpret_cast<const float4*>(&s_w[i0]);
             const float4 wb = *reinterpret_cast<const float4*>(&s_w[i0 + 16]);
-            const uint4 r = __builtin_bit_cast(uint4, bt[ib]);
-            const bf16x8 a = __builtin_bit_cast(
-                bf16x8, make_uint4(pack_bf16(bf16_lo(r.x) * wa.x, bf16_hi(r.x) * wa.y),
-                                   pack_bf16(bf16_lo(r.y) * wa.z, bf16_hi(r.y) * wa.w),
-                                   pack_bf16(bf16_lo(r.z) * wb.x, bf16_hi(r.z) * wb.y),
-                                   pack_bf16(bf16_lo(r.w) * wb.z, bf16_hi(r.w) * wb.w)));
+            bf16x8 a[NTW];
+#pragma unroll
+            for (int k = 0; k < NTW; ++k) {
+                const uint4 r = __builtin_bit_cast(uint4, bt[k][ib]);
+                a[k] = __builtin_bit_cast(
+                    bf16x8, make_uint4(pack_bf16(bf16_lo(r.x) * wa.x, bf16_hi(r.x) * wa.y),
+                                       pack_bf16(bf16_lo(r.y) * wa.z, bf16_hi(r.y) * wa.w),
+                                       pack_bf16(bf16_lo(r.z) * wb.x, bf16_hi(r.z) * wb.y),
+                                       pack_bf16(bf16_lo(r.w) * wb.z, bf16_hi(r.w) * wb.w)));
+            }
 #pragma unroll
             for (int p = 0; p < PT; ++p) {
                 const unsigned char* xp = bx + xoff[p] + ib * XBLK;
                 const uint2 lo2 = lds_read_tr16(xp);
                 const uint2 hi2 = lds_read_tr16(xp + XHALF);
-                acc[p] = mfma16(a, __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y)),
-                                acc[p]);
+                const bf16x8 xf = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+#pragma unroll
+                for (int k = 0; k < NTW; ++k) acc[k][p] = mfma16(a[k], xf, acc[k][p]);
             }
         }
-        // lane holds S[n = wave*16 + 4*g4 + r][p = pt*16 + l16]; layout [p][n]
+        // lane holds S[n = (wave + NW k)*16 + 4*g4 + r][p = pt*16 + l16]; layout [p][n]
         const int c = unit % nC, g = (unit / nC) % G, b = unit / nC / G;
         const int h = g * hpg + sl % hpg;
         __bf16* out = states + ((size_t)(b * H + h) * nC + c) * P * N;
 #pragma unroll
-        for (int p = 0; p < PT; ++p)
-            *reinterpret_cast<uint2*>(out + (size_t)(p * 16 + l16) * N + wave * 16 + 4 * g4) =
-                make_uint2(pack_bf16(acc[p][0], acc[p][1]), pack_bf16(acc[p][2], acc[p][3]));
+        for (int k = 0; k < NTW; ++k)
+#pragma unroll
+            for (int p = 0; p < PT; ++p)
+                *reinterpret_cast<uint2*>(out + (size_t)(p * 16 + l16) * N +
+                                          (wave + C_::NW * k) * 16 + 4 * g4) =
+                    make_uint2(pack_bf16(acc[k][p][0], acc[k][p][1]),
+                               pack_bf16(acc[k][p][2], acc[k][p][3]));
     }
 }
 
@@ -559,6 +587,12 @@ StateFn pick_state_pipe_q(const Shape& s) {
         switch (s.P) {
             case 32: return launch_state_pipe_t<Q, 64, 32, REV>;
             case 64: return launch_state_pipe_t<Q, 64, 64, REV>;
+        }
+    } else if (s.N == 256) {  // two n-tiles per wave, B copied in two column slices
+        switch (s.P) {
+            case 16: return launch_state_pipe_t<Q, 256, 16, REV>;
+            case 32: return launch_state_pipe_t<Q, 256, 32, REV>;
+            case 64: return launch_state_pipe_t<Q, 256, 64, REV>;
         }
     }
     return nullptr;

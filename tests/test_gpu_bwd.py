@@ -69,6 +69,10 @@ CASES = [
              log_neg_a_range=(np.log(0.01), np.log(0.1))),
     Workload("bwd_g2_q256", 1, 700, 4, 64, 128, 2, 256, init_state=True,
              log_neg_a_range=(np.log(0.005), np.log(0.05))),
+    # N = 256: the recomputed states and the state gradients run the pipelined states
+    # kernel with B (C) in two column slices, two items per workgroup across units
+    Workload("bwd_n256_pipe", 2, 8192, 8, 64, 256, 2, 256, init_state=True,
+             log_neg_a_range=(np.log(0.005), np.log(0.05))),
 ]
 
 

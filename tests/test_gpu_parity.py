@@ -274,6 +274,8 @@ PIPE = [  # (batch, seqlen, heads, headdim P, dstate N, groups, chunk Q)
     (1, 32768, 4, 32, 128, 2, 128),
     (2, 16384, 4, 128, 128, 2, 256),  # single-buffered scan
     (1, 8192, 6, 16, 128, 3, 64),
+    (2, 16384, 8, 64, 256, 4, 256),   # N = 256: B in two column slices, crossing units
+    (1, 8192, 6, 32, 256, 3, 128),
 ]
 
 
