@@ -196,13 +196,29 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
     constexpr unsigned XBLK = KB * PPR * 16;   // bytes of 32 rows of x
     constexpr unsigned XHALF = 16 * PPR * 16;  // bytes of 16 rows
 
-    bf16x8 cf0[NK], cf1[NK];  // C rows j0, j1 of the current unit
+    // C rows j0, j1 of the current unit: held across items where they fit (N <= 128), else
+    // loaded for every item, at the end of the item before it
+    constexpr bool CRES = N <= 128;
+    bf16x8 cf0[NK], cf1[NK];
+    auto load_c = [&](int slot) {
+        const int u = slot / hpg;
+        const int cc = u % nC, gg = (u / nC) % G, bb = u / nC / G;
+        const __amdgpu_buffer_rsrc_t cr = make_rsrc(Cm + ((size_t)(bb * T + cc * Q) * G + gg) * N,
+                                                    (unsigned)min(Q, T - cc * Q) * crow);
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+            const unsigned col = (32 * kk + 8 * g4) * 2u;
+            cf0[kk] = __builtin_bit_cast(bf16x8, buf_load16(cr, (unsigned)j0 * crow + col));
+            cf1[kk] = __builtin_bit_cast(bf16x8, buf_load16(cr, (unsigned)j1 * crow + col));
+        }
+    };
     uint4 gf0[NB0], gf1[NB];  // Gram fragments of (tile0, ib), (tile1, ib)
     int cur_unit = -1;
 
     issue_item<Q, N, P>(x, E, cs, dtc, hi - 1, hpg, T, H, G, nC, lds0, wave, lane);
     if (C_::NBUF == 3 && lo + 1 < hi)
         issue_item<Q, N, P>(x, E, cs, dtc, hi - 2, hpg, T, H, G, nC, lds0 + C_::ITEM, wave, lane);
+    if constexpr (!CRES) load_c(hi - 1);
     int buf = 0;  // buffer of the current item
 #pragma unroll 1
     for (int n = 0; n < hi - lo; ++n) {
@@ -213,26 +229,28 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
         // This item's copies have landed once only what was issued after them is pending:
         // with three buffers the next item's copies and the previous item's stores, with
         // two the previous item's stores.
+        // (Where the C rows are not held, this item's were issued last, after all of that.)
+        constexpr int CX = CRES ? 0 : 2 * NK;
         if (C_::NBUF == 3) {
             const bool more = n + 1 < hi - lo;
             if (n == 0 && !more)
                 asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
             else if (n == 0 && wave < 2)
-                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::DMA_HI) : "memory");
+                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::DMA_HI + CX) : "memory");
             else if (n == 0)
-                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::DMA_LO) : "memory");
+                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::DMA_LO + CX) : "memory");
             else if (!more)
-                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::STORES) : "memory");
+                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::STORES + CX) : "memory");
             else if (wave < 2)
-                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::DMA_HI + C_::STORES)
+                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::DMA_HI + C_::STORES + CX)
                              : "memory");
             else
-                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::DMA_LO + C_::STORES)
+                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::DMA_LO + C_::STORES + CX)
                              : "memory");
         } else if (n == 0 || C_::NBUF == 1) {
             asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         } else {
-            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::STORES) : "memory");
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::STORES + CX) : "memory");
         }
 
         const int unit = sl / hpg;
@@ -271,14 +289,7 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
         }
         if (unit != cur_unit) {  // C rows and Gram fragments of the new unit
             cur_unit = unit;
-            const __amdgpu_buffer_rsrc_t cr =
-                make_rsrc(Cm + ((size_t)(b * T + t0) * G + g) * N, (unsigned)Lc * crow);
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
-                const unsigned col = (32 * kk + 8 * g4) * 2u;
-                cf0[kk] = __builtin_bit_cast(bf16x8, buf_load16(cr, (unsigned)j0 * crow + col));
-                cf1[kk] = __builtin_bit_cast(bf16x8, buf_load16(cr, (unsigned)j1 * crow + col));
-            }
+            if constexpr (CRES) load_c(sl);
             // fragments past a tile's last block read outside the buffer: zeros
             const __amdgpu_buffer_rsrc_t gr = make_rsrc(
                 gram + (size_t)unit * npairs(Q) * 64, (unsigned)(npairs(Q) * 64 * 16));
@@ -294,6 +305,7 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
             // where the wait would also cover the next item's copies issued below
             __builtin_amdgcn_s_waitcnt(0x0F70);
         }
+        if constexpr (!CRES) __builtin_amdgcn_s_waitcnt(0x0F70);  // C rows (issued earlier)
         lds_barrier();
         if (C_::NBUF == 3 && n + 2 < hi - lo) {  // into the buffer of the previous item
             const int b2 = buf == 0 ? 2 : buf - 1;
@@ -424,6 +436,8 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
         };
         store_tile(acc0, j0);
         store_tile(acc1, j1);
+        if constexpr (!CRES)
+            if (n + 1 < hi - lo) load_c(sl - 1);
         if (C_::NBUF == 1 && n + 1 < hi - lo) {
             lds_barrier();  // every wave is done with the buffer
             issue_item<Q, N, P>(x, E, cs, dtc, sl - 1, hpg, T, H, G, nC, lds0, wave, lane);
