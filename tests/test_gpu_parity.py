@@ -320,3 +320,42 @@ def test_chunk_state_fills_the_same_gram_blocks(shape):
     binding.ssd_chunk_state(d, Q, dv["x"], dv["B"], dtc, cs, C=dv["C"], gram=got)
     torch.cuda.synchronize()
     assert torch.equal(got, ref)
+
+
+# ------------------------------------------------------------------ ssd_fwd = its stages
+
+STAGED = [  # (batch, seqlen, heads, headdim P, dstate N, groups, chunk Q)
+    (2, 4096 + 77, 6, 64, 128, 3, 256),   # ragged last chunk, C B^T written by the same pass
+    (1, 8192, 16, 32, 128, 2, 128),
+    (2, 3000, 8, 64, 64, 2, 64),
+    (1, 5000, 4, 32, 256, 1, 256),
+]
+
+
+@pytest.mark.parametrize("shape", STAGED, ids=[f"B{b}_T{t}_H{h}_P{p}_N{n}_G{g}_Q{q}"
+                                               for b, t, h, p, n, g, q in STAGED])
+def test_fwd_equals_its_stages(shape):
+    """ssd_fwd leaves in its workspace exactly the dt_chunk and cs of ssd_chunk_cumsum, and
+    gives exactly the y and final state of the stage-by-stage calls (with the C B^T blocks
+    from their own launch)."""
+    Bz, T, H, P, N, G, Q = shape
+    w = Workload(f"staged_{Bz}_{T}_{H}_{P}_{N}_{G}_{Q}", Bz, T, H, P, N, G, Q, init_state=True)
+    say(f"[fwd = stages] {w.describe()}")
+    dv = to_device(generate(w))
+    d = _dims(w)
+    ws = torch.zeros(binding.ssd_fwd_workspace_size(d, Q), dtype=torch.uint8, device="cuda")
+    y, fin = binding.ssd_fwd(dv["x"], dv["dt"], dv["A"], dv["B"], dv["C"], dv["D"], Q,
+                             init_state=dv["init_state"], workspace=ws)
+    dtc, cs = binding.ssd_chunk_cumsum(d, Q, dv["dt"], dv["A"])
+    S = binding.ssd_chunk_state(d, Q, dv["x"], dv["B"], dtc, cs)
+    E, f2 = binding.ssd_state_passing(d, Q, S, cs, init_state=dv["init_state"])
+    gram = binding.ssd_chunk_gram(d, Q, dv["B"], dv["C"])
+    y2 = binding.ssd_chunk_scan(d, Q, dv["x"], dv["B"], dv["C"], dtc, cs, dv["D"], E, gram=gram)
+    torch.cuda.synchronize()
+    # the workspace begins with dt_chunk, then cs, each rounded up to 256 bytes
+    n = dtc.numel()
+    off = (n * 4 + 255) // 256 * 256
+    assert torch.equal(ws[:n * 4].view(torch.float32), dtc.reshape(-1))
+    assert torch.equal(ws[off:off + n * 4].view(torch.float32), cs.reshape(-1))
+    assert torch.equal(y, y2)
+    assert torch.equal(fin, f2)
