@@ -33,6 +33,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="mamba2_2p7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache step times (so that a kernel trace of the run "
+                         "holds warm launches only)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="rough budget for the oracle CPU baseline")
     ap.add_argument("--decode", default="", metavar="WORKLOAD",
@@ -530,8 +533,9 @@ def main():
     # per-step times: warm (back to back) and cold (the 256 MB Infinity Cache flushed by an
     # untimed 1 GiB write before each step)
     scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    step_us = {"warm": step_stats(torch, fwd, args.steps),
-               "cold": step_stats(torch, fwd, args.steps, flush=lambda: scratch.fill_(1.0))}
+    step_us = {"warm": step_stats(torch, fwd, args.steps)}
+    if not args.no_cold:
+        step_us["cold"] = step_stats(torch, fwd, args.steps, flush=lambda: scratch.fill_(1.0))
     del scratch
     if not torch.isfinite(y.float()).all():
         log("[bench] WARNING: non-finite output")
