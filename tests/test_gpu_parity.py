@@ -301,6 +301,7 @@ GRAM_CASES = [  # (batch, seqlen, heads, headdim P, dstate N, groups, chunk Q)
     (2, 4096 + 77, 6, 64, 128, 3, 256),   # blocks written by the states kernel itself
     (1, 8192, 16, 32, 128, 2, 256),       # several units per workgroup
     (1, 1000, 4, 64, 64, 2, 128),         # separate launch after the states kernel
+    (2, 2048 + 100, 6, 64, 256, 2, 256),  # N = 256: summed over the two B column slices
 ]
 
 
