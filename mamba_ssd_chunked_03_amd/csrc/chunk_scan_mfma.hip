@@ -42,49 +42,110 @@ __host__ __device__ constexpr int npairs(int Q) { return pair_base(Q / 16); }
 // ============================================================================ chunk_gram
 // gram[unit][pair][lane] (16 bytes): for lane l of tile t, block ib, column j = 16t + l%16
 // and g = l/16, the bf16 values C_j . B_i for i = 32ib + 4g + {0..3}, 32ib + 16 + 4g + {0..3}.
-// One wave per (unit, pair): all of its loads are independent and issued together.
+// One workgroup per unit.  B and C pass through LDS in column slices of up to 64
+// (double-buffered: the next slice is copied while this one is used), and wave w sums the
+// blocks of row tiles w and NT - 1 - w over the slices, so each unit's B and C are read from
+// HBM once.  The sum over n runs in 32-column steps in order, as in the states kernel's own
+// C B^T blocks.
 template <int Q, int N>
-__global__ __launch_bounds__(256) void chunk_gram_kernel(const __bf16* __restrict__ Bm,
-                                                         const __bf16* __restrict__ Cm,
-                                                         uint4* __restrict__ gram, int T, int G,
-                                                         int nC) {
-    constexpr int NK = N / 32;
-    constexpr int WPU = (npairs(Q) + 3) / 4;  // workgroups per unit
-    const int unit = blockIdx.x / WPU;
-    const int pr = (blockIdx.x % WPU) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (pr >= npairs(Q)) return;  // whole wave
-    int t = 0;
-    while (pair_base(t + 1) <= pr) ++t;
-    const int ib = pr - pair_base(t);
-    const int c = unit % nC;
-    const int b = unit / nC / G;
-    const int g = (unit / nC) % G;
-    const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
-    const int t0 = c * Q;
-    const int Lc = min(Q, T - t0);
+struct GramCfg {
+    static constexpr int NT = Q / 16, NW = NT / 2, NTH = NW * 64;
+    static constexpr int BW = N < 64 ? N : 64;          // columns per slice
+    static constexpr int NS = N / BW, SPR = BW / 8;     // slices; 16-byte pieces per row
+    static constexpr int KS = BW / 32;                  // MFMA k-steps per slice
+    static constexpr unsigned SB = Q * BW * 2;          // one slice of B (or of C)
+    static constexpr unsigned LDS = 4 * SB;             // (B, C) x two buffers
+    static constexpr int NI = Q * SPR / 64;             // copy instructions per slice matrix
+    static_assert(N % 32 == 0 && NI * 64 == Q * SPR, "slice shape");
+};
+
+template <int Q, int N>
+__global__ __launch_bounds__((GramCfg<Q, N>::NTH)) void chunk_gram_kernel(
+    const __bf16* __restrict__ Bm, const __bf16* __restrict__ Cm, uint4* __restrict__ gram,
+    int T, int G, int nC) {
+    using C_ = GramCfg<Q, N>;
+    constexpr int NT = C_::NT, KS = C_::KS, SPR = C_::SPR;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const uint32_t lds0 = lds_addr(smem);
+    const int unit = blockIdx.x;
+    const int c = unit % nC, g = (unit / nC) % G, b = unit / nC / G;
+    const int Lc = min(Q, T - c * Q);
     const unsigned rowb = (unsigned)(G * N * 2);
-    const size_t base = ((size_t)(b * T + t0) * G + g) * N;
-    const __amdgpu_buffer_rsrc_t br = make_rsrc(Bm + base, (unsigned)Lc * rowb);
-    const __amdgpu_buffer_rsrc_t cr = make_rsrc(Cm + base, (unsigned)Lc * rowb);
-    const unsigned jrow = (unsigned)(t * 16 + l16) * rowb;
-    const unsigned irow = (unsigned)(ib * KB + l16) * rowb;
-    bf16x8 cf[NK], b0[NK], b1[NK];
+    const size_t base = ((size_t)(b * T + c * Q) * G + g) * N;
+    const u32x4 br = raw_rsrc(Bm + base, (unsigned)Lc * rowb);
+    const u32x4 cr = raw_rsrc(Cm + base, (unsigned)Lc * rowb);
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
+    // slice k of B and C into buffer k & 1 (B at 2 SB u, C after it), swizzled rows
+    auto issue = [&](int k) {
+        const uint32_t lb = lds0 + (unsigned)(k & 1) * 2u * C_::SB;
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-        const unsigned col = (32 * kk + 8 * g4) * 2u;
-        cf[kk] = __builtin_bit_cast(bf16x8, buf_load16(cr, jrow + col));
-        b0[kk] = __builtin_bit_cast(bf16x8, buf_load16(br, irow + col));
-        b1[kk] = __builtin_bit_cast(bf16x8, buf_load16(br, irow + 16 * rowb + col));
-    }
-    f32x4 g0 = f32x4{0.f, 0.f, 0.f, 0.f}, g1 = g0;
+        for (int i = wave; i < C_::NI; i += C_::NW) {
+            const int m = i * 64 + lane;
+            const int r = m / SPR, sl = m % SPR;
+            const unsigned off =
+                (unsigned)r * rowb + (unsigned)(k * C_::BW) * 2u + (unsigned)(sl ^ (r & (SPR - 1))) * 16u;
+            dma16(br, lb + (unsigned)i * 1024u, off);
+            dma16(cr, lb + C_::SB + (unsigned)i * 1024u, off);
+        }
+    };
+    const int ta = wave, tb = NT - 1 - wave;
+    const int na = ta / 2 + 1, nb = tb / 2 + 1;
+    f32x4 ga[NT / 4][2], gb[NT / 2][2];
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-        g0 = mfma16(b0[kk], cf[kk], g0);
-        g1 = mfma16(b1[kk], cf[kk], g1);
+    for (int i = 0; i < NT / 4; ++i) ga[i][0] = ga[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NT / 2; ++i) gb[i][0] = gb[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    issue(0);
+#pragma unroll 1
+    for (int k = 0; k < C_::NS; ++k) {
+        // slice k has landed for every wave, and slice k - 1's buffer is no longer read
+        dma_barrier();
+        if (k + 1 < C_::NS) issue(k + 1);
+        const unsigned char* sb = smem + (unsigned)(k & 1) * 2u * C_::SB;
+        const unsigned char* sc = sb + C_::SB;
+        bf16x8 ca[KS], cb[KS];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            ca[kk] = *reinterpret_cast<const bf16x8*>(sc + swz_off(ta * 16 + l16, 32 * kk + 8 * g4, SPR));
+            cb[kk] = *reinterpret_cast<const bf16x8*>(sc + swz_off(tb * 16 + l16, 32 * kk + 8 * g4, SPR));
+        }
+#pragma unroll
+        for (int ib = 0; ib < NT / 2; ++ib) {
+            if (ib < nb) {
+                bf16x8 r0[KS], r1[KS];  // B rows 32 ib + l16 and + 16
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk) {
+                    r0[kk] = *reinterpret_cast<const bf16x8*>(sb + swz_off(ib * KB + l16, 32 * kk + 8 * g4, SPR));
+                    r1[kk] = *reinterpret_cast<const bf16x8*>(sb + swz_off(ib * KB + 16 + l16, 32 * kk + 8 * g4, SPR));
+                }
+                if (ib < NT / 4 && ib < na) {
+#pragma unroll
+                    for (int kk = 0; kk < KS; ++kk) {
+                        ga[ib < NT / 4 ? ib : 0][0] = mfma16(r0[kk], ca[kk], ga[ib < NT / 4 ? ib : 0][0]);
+                        ga[ib < NT / 4 ? ib : 0][1] = mfma16(r1[kk], ca[kk], ga[ib < NT / 4 ? ib : 0][1]);
+                    }
+                }
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk) {
+                    gb[ib][0] = mfma16(r0[kk], cb[kk], gb[ib][0]);
+                    gb[ib][1] = mfma16(r1[kk], cb[kk], gb[ib][1]);
+                }
+            }
+        }
     }
-    gram[((size_t)unit * npairs(Q) + pr) * 64 + lane] =
-        make_uint4(pack_bf16(g0[0], g0[1]), pack_bf16(g0[2], g0[3]), pack_bf16(g1[0], g1[1]),
-                   pack_bf16(g1[2], g1[3]));
+    uint4* gu = gram + (size_t)unit * npairs(Q) * 64 + lane;
+    auto put = [&](const f32x4* gg, int t, int ib) {
+        gu[(size_t)(pair_base(t) + ib) * 64] =
+            make_uint4(pack_bf16(gg[0][0], gg[0][1]), pack_bf16(gg[0][2], gg[0][3]),
+                       pack_bf16(gg[1][0], gg[1][1]), pack_bf16(gg[1][2], gg[1][3]));
+    };
+#pragma unroll
+    for (int ib = 0; ib < NT / 4; ++ib)
+        if (ib < na) put(ga[ib], ta, ib);
+#pragma unroll
+    for (int ib = 0; ib < NT / 2; ++ib)
+        if (ib < nb) put(gb[ib], tb, ib);
 }
 
 // ============================================================================ chunk_scan
@@ -482,9 +543,22 @@ hipError_t launch_scan_t(const Shape& s, const void* x, const void* Cm, const fl
 template <int Q, int N>
 hipError_t launch_gram_t(const Shape& s, const void* Bm, const void* Cm, void* gram,
                          hipStream_t st) {
-    const unsigned blocks = (unsigned)((size_t)s.B * s.G * s.nC * ((npairs(Q) + 3) / 4));
-    chunk_gram_kernel<Q, N><<<blocks, 256, 0, st>>>((const __bf16*)Bm, (const __bf16*)Cm,
-                                                     (uint4*)gram, s.T, s.G, s.nC);
+    using C_ = GramCfg<Q, N>;
+    const auto kern = chunk_gram_kernel<Q, N>;
+    static bool attr_set[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!attr_set[dev]) {
+        e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)C_::LDS);
+        if (e != hipSuccess) return e;
+        attr_set[dev] = true;
+    }
+    const unsigned blocks = (unsigned)((size_t)s.B * s.G * s.nC);
+    kern<<<blocks, C_::NTH, C_::LDS, st>>>((const __bf16*)Bm, (const __bf16*)Cm, (uint4*)gram,
+                                           s.T, s.G, s.nC);
     return hipGetLastError();
 }
 
