@@ -94,8 +94,14 @@ __device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
 // into LDS at lds + 16 * lane.  The compiler does not see these as writes to LDS, so it
 // never makes later LDS reads wait for them; callers wait explicitly (s_waitcnt vmcnt)
 // and barrier before reading what they copied.
+// The LDS address travels in M0, which the compiler writes with a scalar instruction just
+// before the asm block.  On gfx950 an LDS copy needs one wait state after an M0 write, or
+// it may still see the previous M0 and land at the previous copy's address; the compiler
+// inserts that wait for the copies it emits itself but does not look inside asm, so the
+// block begins with it.
 __device__ __forceinline__ void dma16(u32x4 r, uint32_t lds, uint32_t voff) {
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(lds)
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r),
+                 "{m0}"(lds)
                  : "memory");
 }
 // raw buffer resource words: base, stride 0, size in bytes (reads past it return zeros)
