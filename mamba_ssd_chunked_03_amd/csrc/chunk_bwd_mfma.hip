@@ -173,13 +173,17 @@ struct BwdCfg {
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
+// One head's rows, states and step sizes, copied by the four state waves (iw = 0..3): their
+// own vector-memory count then covers the whole copy, so they can wait for it without a
+// barrier with the strip waves.
 template <int Q, int N, int P>
 __device__ __forceinline__ void issue_item(const __bf16* x, const __bf16* dy, const __bf16* entry,
                                            const __bf16* exitg, const float* cs, const float* dtc,
                                            int b, int h, int c, int j0, int Lc, int T, int H,
-                                           int nC, uint32_t lds, int wave, int lane) {
+                                           int nC, uint32_t lds, int iw, int lane) {
     using C_ = BwdCfg<Q, N, P>;
-    constexpr int NW = C_::NW;
+    constexpr int NW = 4;
+    const int wave = iw;
     const unsigned rowb = (unsigned)(H * P * 2);
     const size_t xo = ((size_t)(b * T + c * Q) * H + h) * P;
     const u32x4 xr = raw_rsrc(x + xo, (unsigned)Lc * rowb);
@@ -319,9 +323,7 @@ __device__ __forceinline__ void bwd_strip_role(
 #pragma unroll
     for (int s = 0; s < 2 * PAIRS; ++s) wacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    issue_item<Q, N, P>(x, dy, entry, exitg, cs, dtc, b, g * hpg, c, j0, Lc, T, H, nC, k_.lds0,
-                        wave, lane);
-    dma_barrier();  // the first head's rows have landed
+    dma_barrier();  // the first head's rows have landed (copied by the state waves)
     lds_barrier();  // ... and are scaled (by the state waves)
 #pragma unroll 1
     for (int hh = 0; hh < hpg; ++hh) {
@@ -334,9 +336,6 @@ __device__ __forceinline__ void bwd_strip_role(
             lt_part[pi] = (sh[0] + sh[2]) + (sh[4] + sh[6]);
             dd_part[pi] = (sh[1] + sh[3]) + (sh[5] + sh[7]);
         }
-        if (hh + 1 < hpg)
-            issue_item<Q, N, P>(x, dy, entry, exitg, cs, dtc, b, h + 1, c, j0, Lc, T, H, nC,
-                                k_.lds0 + (buf ^ 1) * C_::ITEM, wave, lane);
         unsigned char* sXY = smem + buf * C_::ITEM;
         const float* s_cs = reinterpret_cast<const float*>(sXY + C_::XYB + 2 * C_::EB);
         const float* s_dt = s_cs + Q;
@@ -518,9 +517,8 @@ __device__ __forceinline__ void bwd_strip_role(
 #pragma unroll
         for (int s2 = 0; s2 < RJ; ++s2) rsb[s2] = colsum(rsb[s2]);
 
-        // the state waves' (F B_j) tiles, ob, oc and <E, F> shares are in LDS; every wave's
-        // copies of the next head have landed (the state waves scale them meanwhile)
-        dma_barrier();
+        // the state waves' (F B_j) tiles, ob, oc and <E, F> shares are in LDS
+        lds_barrier();
         const uint2* xbf = reinterpret_cast<const uint2*>(smem + C_::X_BF) + (cw * PT) * 64 + ln;
         const float* xob = reinterpret_cast<const float*>(smem + C_::X_OB);
         const float ob = xob[16 * cw + l16], oc = xob[64 + 16 * cw + l16];
@@ -556,6 +554,9 @@ __device__ __forceinline__ void bwd_strip_role(
                       reinterpret_cast<const float*>(smem + C_::X_EF)[cw], lt);
         lt = wavesum(lt);
         if (lane == 0) shares[buf * 8 + 2 * cw] = lt;
+        lds_barrier();  // every state wave's copies of the next head have landed
+        if (hh + 1 < hpg)
+            prescale_rows<Q, N, P>(smem + (buf ^ 1) * C_::ITEM, j0, (int)threadIdx.x, 512);
     }
     dma_barrier();
     if (wave == 0 && lane == 0) {
@@ -611,7 +612,7 @@ __device__ __forceinline__ void bwd_state_role(
     for (int nt = 0; nt < NT; ++nt) dbacc[nt] = dcacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     issue_item<Q, N, P>(x, dy, entry, exitg, cs, dtc, b, g * hpg, c, j0, Lc, T, H, nC, k_.lds0,
-                        wave, lane);
+                        wave - 4, lane);
     dma_barrier();
     prescale_rows<Q, N, P>(smem, j0, (int)threadIdx.x - 256, 256);
     lds_barrier();
@@ -622,7 +623,7 @@ __device__ __forceinline__ void bwd_state_role(
         lds_barrier();
         if (hh + 1 < hpg)
             issue_item<Q, N, P>(x, dy, entry, exitg, cs, dtc, b, h + 1, c, j0, Lc, T, H, nC,
-                                k_.lds0 + (buf ^ 1) * C_::ITEM, wave, lane);
+                                k_.lds0 + (buf ^ 1) * C_::ITEM, wave - 4, lane);
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int l16 = ln & 15, g4 = ln >> 4;
@@ -704,9 +705,7 @@ __device__ __forceinline__ void bwd_state_role(
             ef = wavesum(ef);
             if (ln == 0) reinterpret_cast<float*>(smem + C_::X_EF)[cw] = ef;
         }
-        dma_barrier();  // hand-off to the strip waves; the next head's copies have landed
-        if (hh + 1 < hpg)
-            prescale_rows<Q, N, P>(smem + (buf ^ 1) * C_::ITEM, j0, (int)threadIdx.x - 256, 256);
+        lds_barrier();  // hand-off to the strip waves
         // dB^T[n][j] += sum_p F[p][n] (dt_j exp(cs_last - cs_j) x_j[p])
 #pragma unroll
         for (int kb = 0; kb < PKB; ++kb) {
@@ -716,6 +715,13 @@ __device__ __forceinline__ void bwd_state_role(
             for (int nt = 0; nt < NT; ++nt)
                 dbacc[nt] = mfma16(ld_tr(rows_at(sF, 32 * kb, NPR), ptn[nt], N16), xs8, dbacc[nt]);
         }
+        // this wave's share of the next head's copies has landed; after the barrier every
+        // share has, and all eight waves scale the next head's rows (read after its first
+        // barrier).  A wave's vmcnt covers only its own copies, so the barrier is needed.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+        if (hh + 1 < hpg)
+            prescale_rows<Q, N, P>(smem + (buf ^ 1) * C_::ITEM, j0, (int)threadIdx.x, 512);
     }
     dma_barrier();
     issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, true, k_.lds0, wave, lane);
@@ -807,8 +813,13 @@ __global__ __launch_bounds__(512) void chunk_bwd_mfma_kernel(
             SSD_STRIP(3)
 #undef SSD_STRIP
         }
-    } else
+    } else {
+        // the state waves issue every copy and scale the next head's rows, which the strip
+        // waves wait on: they go first when both are ready to issue (the saved backward at
+        // 2.7B: 538 -> 519 us)
+        __builtin_amdgcn_s_setprio(3);
         bwd_state_role<Q, N, P>(k_, smem, x, Bm, Cm, dtc, cs, entry, exitg, dy, dB, dC);
+    }
 }
 
 template <int Q, int N, int P>
