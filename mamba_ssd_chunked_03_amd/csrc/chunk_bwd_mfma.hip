@@ -36,7 +36,9 @@
 //
 // Per head the x rows [0, j0 + 64) and dy rows [j0, Q) (one array of Q + 64 rows), E, F,
 // cs and dt are copied into LDS straight from HBM (buffer_load ... lds), double-buffered
-// so that the next head's copy runs under this head's products.  The group's B and C
+// so that the next head's copy runs under this head's products.  The state waves issue
+// the copy; at the end of a head each waits for its own share, a workgroup barrier
+// follows, and all eight waves then scale the next head's rows.  The group's B and C
 // chunks pass through the same LDS before the loop (for C B^T and the B_j, C_j operands)
 // and after it (for the two W products).
 #include "mfma_common.h"
