@@ -148,6 +148,21 @@ def test_validation_errors_before_any_launch(lib):
                                None) == 1
 
 
+def test_size_limit_is_exact(lib):
+    """Every tensor must hold fewer than 2^31 elements, with T rounded up to whole chunks.
+    At H = 80, P = 64, N = 256, Q = 256, 1638 chunks put both x and the chunk states at
+    2,146,959,360 elements: accepted (the call goes on to fail on the workspace size, after
+    the shape checks); one more step makes a 1639th chunk and is refused as a shape."""
+    assert 1638 * 256 * 80 * 64 < 1 << 31 <= 1639 * 256 * 80 * 64
+    assert _fwd(lib, D(1, 1638 * 256, 80, 64, 256, 1), dtype=1, q=256, ws_bytes=10) == 5
+    assert _fwd(lib, D(1, 1638 * 256 - 100, 80, 64, 256, 1), dtype=1, q=256, ws_bytes=10) == 5
+    assert _fwd(lib, D(1, 1638 * 256 + 1, 80, 64, 256, 1), dtype=1, q=256, ws_bytes=10) == 2
+    # the chunk states alone at the limit (Q = 64: four times the elements of x)
+    assert 6553 * 80 * 16 * 256 < 1 << 31 <= 6554 * 80 * 16 * 256
+    assert _fwd(lib, D(1, 6553 * 64, 80, 16, 256, 1), dtype=1, q=64, ws_bytes=10) == 5
+    assert _fwd(lib, D(1, 6553 * 64 + 1, 80, 16, 256, 1), dtype=1, q=64, ws_bytes=10) == 2
+
+
 def test_bwd_workspace_size(lib):
     d = D(4, 4096, 80, 64, 128, 1)
     nC = 16

@@ -56,6 +56,35 @@ def test_fwd_matches_oracle_full_size_sampled(w):
     assert ef <= TOL[w.dtype]
 
 
+# The largest shapes the library accepts: tensors just under 2^31 elements (T rounded up to
+# whole chunks), each with a ragged last chunk.  A 32-bit overflow of an element or byte
+# offset anywhere on the path would show here.  The first puts x, y and the chunk states
+# at the limit (4.3 GB each in bf16); the second the chunk states alone (Q = 64, N = 256:
+# four times the elements of x).  Both shapes also run at small sizes below.
+LIMIT = [
+    (Workload("limit_x_and_states", 1, 1638 * 256 - 100, 80, 64, 256, 1, 256, init_state=True), 2),
+    (Workload("limit_states", 1, 819 * 64 - 37, 80, 128, 256, 1, 64, init_state=True), 3),
+]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("w,count", LIMIT, ids=[w.name for w, _ in LIMIT])
+def test_fwd_at_the_size_limit_sampled(w, count):
+    say(f"[fwd size limit] {w.describe()}")
+    padded = w.nchunks * w.chunk_len
+    assert padded * w.nheads * w.headdim < 1 << 31
+    assert w.nchunks * w.nheads * w.headdim * w.dstate < 1 << 31
+    assert max(padded * w.nheads * w.headdim,
+               w.nchunks * w.nheads * w.headdim * w.dstate) > 0.99 * (1 << 31)
+    cpu = generate(w)
+    y, fin = gpu_fwd(to_device(cpu), w.chunk_len)
+    assert torch.isfinite(y).all()
+    ey, ef = check_sampled(w, cpu, y, fin, count=count)
+    say(f"    sampled rel_l2 y={ey:.3e} final={ef:.3e}")
+    assert ey <= TOL[w.dtype]
+    assert ef <= TOL[w.dtype]
+
+
 def test_tiny_fp32_whole_output():
     """The fp32 workload compared on every output, at the fp32 bound."""
     w = TINY_FP32
