@@ -34,6 +34,9 @@
  *     SSD_ERR_ALIGN).  The caller owns every buffer.  The
  *     library allocates nothing and keeps no state between calls, so calls on different
  *     streams are independent; calls that share output or workspace buffers race.
+ *   - No output or workspace may overlap an input, another output or the workspace of
+ *     the same call (not checked: kernels read inputs that other workgroups' outputs
+ *     would already have overwritten), except where an entry point states otherwise.
  *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.  Work is
  *     enqueued asynchronously; a return of SSD_OK means "enqueued".
  *   - Arguments are validated before any launch; on an error nothing is enqueued.
@@ -42,8 +45,9 @@
  *     dt*A sum inside a chunk can overflow exp.
  *   - Supported sizes: chunk_len in {64, 128, 256}; dstate N in {16, 32, 64, 128, 256};
  *     headdim P in {16, 32, 64, 128}; ngroups G >= 1 dividing nheads H; any seqlen
- *     T >= 0 (the last chunk may be partial); batch >= 0; B*T*H*P < 2^31 elements per
- *     tensor.  dtype SSD_F32 or SSD_BF16 for x, B, C and y (and the stored chunk and
+ *     T >= 0 (the last chunk may be partial); batch >= 0; fewer than 2^31 elements in
+ *     x, in B and in the chunk states, counting T rounded up to whole chunks (else
+ *     SSD_ERR_DIMS).  dtype SSD_F32 or SSD_BF16 for x, B, C and y (and the stored chunk and
  *     entry states); dt, A, D, init_state, final_state and cs are always fp32.
  *
  * Tensor layouts
