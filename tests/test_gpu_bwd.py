@@ -122,12 +122,14 @@ def test_bwd_is_deterministic():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["mamba2_2p7b", "mamba2_130m", "nsweep_n64", "long_ctx_65k"])
+@pytest.mark.parametrize("name", ["mamba2_2p7b", "mamba2_130m", "nsweep_n64", "nsweep_n128",
+                                  "nsweep_n256", "long_ctx_65k"])
 def test_bwd_full_size_workloads(name):
     """The model-shaped backward workloads at full size, with the launch configuration that
-    bench.py --bwd times (bf16, Q = 256, MFMA in-chunk kernel), compared whole-tensor with
-    the oracle's reverse-mode pass over every (b, h) sequence.  long_ctx_65k adds eight
-    groups of ten heads, an initial state and 256 chunks per sequence."""
+    bench.py --bwd times (bf16, Q = 256; the MFMA in-chunk kernel, and at N = 256 the fp32
+    VALU one), compared whole-tensor with the oracle's reverse-mode pass over every (b, h)
+    sequence.  long_ctx_65k adds eight groups of ten heads, an initial state and 256
+    chunks per sequence."""
     w = WORKLOADS[name]
     say(f"[bwd full] {w.describe()}")
     cpu = generate(w)
