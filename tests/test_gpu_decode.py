@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from mamba_ssd_chunked_03_amd import binding
-from mamba_ssd_chunked_03_amd.workloads import Workload, generate
+from mamba_ssd_chunked_03_amd.workloads import DECODE, Workload, generate
 from parity import TOL, np64, rel_l2, say, to_device
 
 pytestmark = pytest.mark.gpu
@@ -37,6 +37,18 @@ def test_one_step_matches_oracle(case):
     Bz, H, P, N, G, dt = case
     w = Workload(f"dec_{Bz}_{H}_{P}_{N}_{G}", Bz, 1, H, P, N, G, 64, dtype=dt, init_state=True,
                  log_neg_a_range=(np.log(0.01), np.log(1.0)))
+    _check_one_step(w)
+
+
+@pytest.mark.parametrize("name", sorted(DECODE))
+def test_model_shaped_decode_steps_match_oracle(name):
+    """The decode workloads bench.py --decode times, at full size and in its launch
+    configuration, compared whole-tensor with one step of the oracle's recurrence."""
+    _check_one_step(DECODE[name])
+
+
+def _check_one_step(w):
+    dt = w.dtype
     say(f"[decode one step] {w.describe()}")
     cpu = generate(w)
     y_ref, f_ref, _ = oracle.ssd_ref(*(np64(cpu[k]) for k in ("x", "dt", "A", "B", "C", "D")),
