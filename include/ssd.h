@@ -31,9 +31,12 @@
  *   - Pointers are device pointers (hipMalloc'd or equivalent), row-major and
  *     contiguous.  x, B, C, y, dt_chunk, cs, the state buffers and the workspace must be
  *     16-byte aligned; dt, A, D, init_state and final_state 4-byte aligned (else
- *     SSD_ERR_ALIGN).  The caller owns every buffer.  The
- *     library allocates nothing and keeps no state between calls, so calls on different
- *     streams are independent; calls that share output or workspace buffers race.
+ *     SSD_ERR_ALIGN).  The caller owns every buffer.  The library allocates nothing.  The
+ *     only state it keeps between calls is per device and per kernel: on a kernel's first
+ *     launch on a device it raises the kernel's LDS limit and notes how many of its
+ *     workgroups fit on the device at once (held in atomics, so concurrent first calls
+ *     from several host threads are safe).  Calls on different streams are therefore
+ *     independent; calls that share output or workspace buffers race.
  *   - No output or workspace may overlap an input, another output or the workspace of
  *     the same call (not checked: kernels read inputs that other workgroups' outputs
  *     would already have overwritten), except where an entry point states otherwise.

@@ -828,17 +828,9 @@ template <int Q, int N, int P>
 hipError_t launch_bwd_mfma_t(const Shape& s, const BwdArgs& a, hipStream_t st) {
     using C_ = BwdCfg<Q, N, P>;
     const auto kern = chunk_bwd_mfma_kernel<Q, N, P>;
-    static bool attr_set[64];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    static DeviceSlots attr_set;
+    const hipError_t e = allow_lds((const void*)kern, C_::LDS, attr_set);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (!attr_set[dev]) {
-        e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)C_::LDS);
-        if (e != hipSuccess) return e;
-        attr_set[dev] = true;
-    }
     const unsigned blocks = (unsigned)((size_t)s.B * s.G * s.nC * C_::NJ);
     kern<<<blocks, C_::NTH, C_::LDS, st>>>(
         (const __bf16*)a.x, (const __bf16*)a.Bm, (const __bf16*)a.Cm, a.dtc, a.cs, a.D,

@@ -551,25 +551,12 @@ hipError_t launch_state_pipe_t(const Shape& s, const void* x, const void* Bm, co
                                hipStream_t st) {
     using C_ = StateCfg<Q, N, P>;
     const auto kern = chunk_state_pipe_kernel<Q, N, P, REV>;
-    static int grid_of[64];  // per device: resident workgroups, a multiple of 8
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    static DeviceSlots grid_of;  // per device: resident workgroups, a multiple of 8
+    int grid = 0;
+    const hipError_t e = resident_grid((const void*)kern, C_::NTH, C_::LDS, grid_of, &grid);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (grid_of[dev] == 0) {
-        e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)C_::LDS);
-        if (e != hipSuccess) return e;
-        int ncu = 0, occ = 0;
-        e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, C_::NTH, C_::LDS);
-        if (e != hipSuccess) return e;
-        const int g8 = (ncu * (occ > 0 ? occ : 1)) / 8;
-        grid_of[dev] = (g8 > 0 ? g8 : 1) * 8;
-    }
     const int nslots = s.B * s.G * s.nC * (s.H / s.G);
-    kern<<<grid_of[dev], C_::NTH, C_::LDS, st>>>((const __bf16*)x, (const __bf16*)Bm, dtc, cs,
+    kern<<<grid, C_::NTH, C_::LDS, st>>>((const __bf16*)x, (const __bf16*)Bm, dtc, cs,
                                                   (__bf16*)states, (const __bf16*)Cm, (uint4*)gram, s.T,
                                                   s.H, s.G, s.nC, nslots);
     return hipGetLastError();

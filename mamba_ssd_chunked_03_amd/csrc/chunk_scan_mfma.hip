@@ -517,24 +517,12 @@ hipError_t launch_scan_t(const Shape& s, const void* x, const void* Cm, const fl
     const auto kern = chunk_scan_mfma_kernel<Q, N, P>;
     // per device: allow the dynamic LDS size, and size the persistent grid to what is
     // resident at once (a multiple of 8 workgroups, one run of items each)
-    static int grid_of[64];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    static DeviceSlots grid_of;
+    int grid = 0;
+    const hipError_t e = resident_grid((const void*)kern, C_::NTH, C_::LDS, grid_of, &grid);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (grid_of[dev] == 0) {
-        e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)C_::LDS);
-        if (e != hipSuccess) return e;
-        int ncu = 0, occ = 0;
-        e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, C_::NTH, C_::LDS);
-        if (e != hipSuccess) return e;
-        grid_of[dev] = ((ncu * (occ > 0 ? occ : 1)) / 8 > 0 ? (ncu * (occ > 0 ? occ : 1)) / 8 : 1) * 8;
-    }
     const int nslots = s.B * s.G * s.nC * (s.H / s.G);
-    kern<<<grid_of[dev], C_::NTH, C_::LDS, st>>>(
+    kern<<<grid, C_::NTH, C_::LDS, st>>>(
         (const __bf16*)x, (const __bf16*)Cm, dtc, cs, D, (const __bf16*)E, (const uint4*)gram,
         (__bf16*)y, s.T, s.H, s.G, s.nC, nslots);
     return hipGetLastError();
@@ -545,17 +533,9 @@ hipError_t launch_gram_t(const Shape& s, const void* Bm, const void* Cm, void* g
                          hipStream_t st) {
     using C_ = GramCfg<Q, N>;
     const auto kern = chunk_gram_kernel<Q, N>;
-    static bool attr_set[64];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    static DeviceSlots attr_set;
+    const hipError_t e = allow_lds((const void*)kern, C_::LDS, attr_set);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (!attr_set[dev]) {
-        e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)C_::LDS);
-        if (e != hipSuccess) return e;
-        attr_set[dev] = true;
-    }
     const unsigned blocks = (unsigned)((size_t)s.B * s.G * s.nC);
     kern<<<blocks, C_::NTH, C_::LDS, st>>>((const __bf16*)Bm, (const __bf16*)Cm, (uint4*)gram,
                                            s.T, s.G, s.nC);

@@ -6,6 +6,8 @@
 // fp32 VALU kernels.
 #include <string.h>
 
+#include <initializer_list>
+
 #include "ssd_internal.h"
 
 using ssd::Shape;
@@ -19,6 +21,19 @@ bool supported_dstate(int64_t n) { return n == 16 || n == 32 || n == 64 || n == 
 bool supported_headdim(int64_t p) { return p == 16 || p == 32 || p == 64 || p == 128; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Whether the product of non-negative factors is below kMaxElems.  Each factor is checked
+// against what is left of the budget by division, so no intermediate product can overflow.
+bool product_fits(std::initializer_list<int64_t> factors) {
+    for (int64_t f : factors)
+        if (f == 0) return true;
+    int64_t acc = 1;
+    for (int64_t f : factors) {
+        if (f > (kMaxElems - 1) / acc) return false;  // acc * f would reach kMaxElems
+        acc *= f;
+    }
+    return true;
+}
+
 ssd_status make_shape(const ssd_dims* d, int chunk_len, Shape* s) {
     if (!d) return SSD_ERR_NULL;
     if (d->batch < 0 || d->seqlen < 0 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 ||
@@ -27,11 +42,15 @@ ssd_status make_shape(const ssd_dims* d, int chunk_len, Shape* s) {
     if (!supported_chunk(chunk_len) || !supported_dstate(d->dstate) ||
         !supported_headdim(d->headdim))
         return SSD_ERR_UNSUPPORTED;
+    // every size below 2^31 first (so that the int casts and the chunk count cannot
+    // overflow), then every tensor below 2^31 elements; ngroups <= nheads since it divides it
+    if (d->batch >= kMaxElems || d->seqlen >= kMaxElems || d->nheads > 65536)
+        return SSD_ERR_DIMS;
     const int64_t nC = (d->seqlen + chunk_len - 1) / chunk_len;
-    const int64_t bt = d->batch * (nC * chunk_len);
-    if (d->batch > kMaxElems || d->seqlen > kMaxElems || d->nheads > 65536 ||
-        bt * d->nheads * d->headdim >= kMaxElems || bt * d->ngroups * d->dstate >= kMaxElems ||
-        d->batch * d->nheads * nC * d->headdim * d->dstate >= kMaxElems)
+    const int64_t tpad = nC * chunk_len;
+    if (!product_fits({d->batch, tpad, d->nheads, d->headdim}) ||
+        !product_fits({d->batch, tpad, d->ngroups, d->dstate}) ||
+        !product_fits({d->batch, d->nheads, nC, d->headdim, d->dstate}))
         return SSD_ERR_DIMS;
     s->B = (int)d->batch;
     s->T = (int)d->seqlen;
@@ -423,8 +442,7 @@ ssd_status ssd_block_prologue(const ssd_dims* dims, ssd_dtype dtype, const void*
     if (!valid_dtype(dtype) || conv_k < 1 || conv_k > 8) return SSD_ERR_UNSUPPORTED;
     const int64_t cdim = (int64_t)s.H * s.P + 2 * (int64_t)s.G * s.N;
     if (xbc_stride < cdim || dt_stride < s.H) return SSD_ERR_DIMS;
-    if ((int64_t)s.B * s.T * xbc_stride >= ((int64_t)1 << 31) ||
-        (int64_t)s.B * s.T * dt_stride >= ((int64_t)1 << 31))
+    if (!product_fits({s.B, s.T, xbc_stride}) || !product_fits({s.B, s.T, dt_stride}))
         return SSD_ERR_DIMS;
     if ((size_t)s.B * s.T == 0) return SSD_OK;
     if (!xbc || !conv_w || !dt_raw || !x || !B || !C || !dt) return SSD_ERR_NULL;
@@ -449,7 +467,7 @@ ssd_status ssd_block_epilogue(const ssd_dims* dims, ssd_dtype dtype, const void*
     if (!valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
     const int64_t d = (int64_t)s.H * s.P;
     if (norm_groups < 1 || d % norm_groups != 0 || z_stride < d || !(eps >= 0.f) ||
-        (int64_t)s.B * s.T * z_stride >= ((int64_t)1 << 31))
+        !product_fits({s.B, s.T, z_stride}))
         return SSD_ERR_DIMS;
     if ((size_t)s.B * s.T == 0) return SSD_OK;
     if (!y || !z || !norm_w || !out) return SSD_ERR_NULL;
@@ -513,7 +531,7 @@ ssd_status ssd_block_fwd(const ssd_dims* dims, ssd_dtype dtype, const void* zxbc
     const int64_t d = (int64_t)s.H * s.P, gn = (int64_t)s.G * s.N;
     const int64_t width = 2 * d + 2 * gn + s.H;
     if (norm_groups < 1 || d % norm_groups != 0 || !(eps >= 0.f) ||
-        (int64_t)s.B * s.T * width >= ((int64_t)1 << 31))
+        !product_fits({s.B, s.T, width}))
         return SSD_ERR_DIMS;
     const bool has_tokens = (size_t)s.B * s.T > 0;
     if (has_tokens && (!zxbcdt || !conv_w || !A || !D || !norm_w || !out)) return SSD_ERR_NULL;

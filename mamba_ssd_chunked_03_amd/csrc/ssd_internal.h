@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "ssd.h"
 
 namespace ssd {
@@ -14,6 +16,56 @@ struct Shape {
     int B, T, H, P, N, G, Q, nC;
     int heads_per_group() const { return H / G; }
 };
+
+// ---- per-device launch state --------------------------------------------------------
+// The only state the library keeps between calls: per kernel instantiation and device,
+// whether the kernel's dynamic-LDS limit has been raised and how many of its workgroups
+// are resident at once.  Both are computed on the kernel's first launch on a device.  Two
+// threads making that first launch together both compute the same value; the slots are
+// atomics, and a slot is published only after the attribute is set, so a thread that reads
+// a nonzero slot launches after the attribute call of the thread that wrote it.
+constexpr int kMaxDevices = 64;
+using DeviceSlots = std::atomic<int>[kMaxDevices];
+
+// Raise kern's dynamic LDS limit to `lds` bytes on the current device (once per device) and
+// return in *grid the number of workgroups of `threads` threads resident at once, rounded
+// down to a multiple of 8 (at least 8): the grid of a persistent kernel.
+inline hipError_t resident_grid(const void* kern, int threads, unsigned lds,
+                                DeviceSlots& slots, int* grid) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    int g = slots[dev].load(std::memory_order_acquire);
+    if (g == 0) {
+        e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        int ncu = 0, occ = 0;
+        e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, threads, lds);
+        if (e != hipSuccess) return e;
+        const int g8 = (ncu * (occ > 0 ? occ : 1)) / 8;
+        g = (g8 > 0 ? g8 : 1) * 8;
+        slots[dev].store(g, std::memory_order_release);
+    }
+    *grid = g;
+    return hipSuccess;
+}
+
+// Raise kern's dynamic LDS limit to `lds` bytes on the current device, once per device.
+inline hipError_t allow_lds(const void* kern, unsigned lds, DeviceSlots& slots) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (slots[dev].load(std::memory_order_acquire) == 0) {
+        e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        slots[dev].store(1, std::memory_order_release);
+    }
+    return hipSuccess;
+}
 
 // ---- element access ---------------------------------------------------------------
 __device__ __forceinline__ float to_f32(float v) { return v; }

@@ -97,6 +97,15 @@ def test_validation_errors_before_any_launch(lib):
     assert _fwd(lib, D(), ptrs=dict(ws=None)) == 5
     assert _fwd(lib, D(), ws_bytes=10) == 5
     assert _fwd(lib, D(b=1 << 20, t=1 << 20)) == 2          # index range
+    # products that overflow int64, and sizes of exactly 2^31, are refused as shapes before
+    # any pointer or workspace check
+    assert _fwd(lib, D(b=1 << 20, t=1 << 30, h=1 << 16, p=16, n=16, g=1 << 16)) == 2
+    assert _fwd(lib, D(b=1 << 31, t=1 << 31, h=1, p=16, n=16, g=1)) == 2
+    assert _fwd(lib, D(b=1 << 31, t=1, h=1, p=16, n=16, g=1)) == 2
+    assert _fwd(lib, D(b=1, t=1 << 31, h=1, p=16, n=16, g=1)) == 2
+    assert _fwd(lib, D(b=(1 << 62), t=4, h=1, p=16, n=16, g=1)) == 2
+    assert binding.ssd_fwd_workspace_size(D(b=1 << 20, t=1 << 30, h=1 << 16, p=16, n=16,
+                                            g=1 << 16), 64) == 0
     # stage entry points validate the same way
     assert lib.ssd_chunk_cumsum(ctypes.byref(D(p=40)), 64, None, None, None, None, None) == 3
     assert lib.ssd_chunk_cumsum(ctypes.byref(D()), 64, None, None, None, None, None) == 1
