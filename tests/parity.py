@@ -7,7 +7,6 @@ import torch
 
 import oracle
 from mamba_ssd_chunked_03_amd import binding
-from mamba_ssd_chunked_03_amd.workloads import head_slice
 
 # Tolerances on rel-L2 = ||gpu - oracle||_2 / ||oracle||_2 over a whole tensor, as stated
 # for the SSD forward: 1e-4 with fp32 inputs, 2e-2 with bf16 inputs (fp32 accumulation).
@@ -51,25 +50,84 @@ def oracle_fwd(cpu_inputs, nthreads=0):
     return y, fin
 
 
-def sampled_pairs(w, count=4):
-    """(batch, head) pairs spread over the workload, always including the first and last."""
-    pairs = {(0, 0), (w.batch - 1, w.nheads - 1)}
-    rng = np.random.default_rng(1234)
-    while len(pairs) < min(count, w.batch * w.nheads):
-        pairs.add((int(rng.integers(w.batch)), int(rng.integers(w.nheads))))
-    return sorted(pairs)
+def seq_errors(u, ref, axes):
+    """Squared error and squared reference norm summed over `axes`: one entry per
+    remaining index (per sequence, when the remaining axes are batch and head)."""
+    u = np.asarray(u, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert u.shape == ref.shape, (u.shape, ref.shape)
+    assert np.isfinite(u).all(), "non-finite values in the GPU result"
+    return ((u - ref) ** 2).sum(axis=axes), (ref ** 2).sum(axis=axes)
 
 
-def check_sampled(w, cpu_inputs, y_gpu, fin_gpu, count=4):
-    """Compare whole (b, h) sequences of the GPU output with the oracle run on just that
-    sequence.  Returns the worst rel-L2 of y and of the final state."""
-    worst_y = worst_f = 0.0
-    for b, h in sampled_pairs(w, count):
-        sl = head_slice(cpu_inputs, w, b, h)
-        y_ref, f_ref = oracle_fwd(sl)
-        ey = rel_l2(np64(y_gpu[b:b + 1, :, h:h + 1, :]), y_ref)
-        worst_y = max(worst_y, ey)
-        if fin_gpu is not None:
-            ef = rel_l2(np64(fin_gpu[b:b + 1, h:h + 1]), f_ref)
-            worst_f = max(worst_f, ef)
-    return worst_y, worst_f
+def per_seq_rel_l2(err2, ref2):
+    """rel-L2 of each slice from its summed squared error and reference norm (the absolute
+    error where the reference is all zeros)."""
+    err2 = np.asarray(err2, dtype=np.float64)
+    ref2 = np.asarray(ref2, dtype=np.float64)
+    return np.where(ref2 > 0, np.sqrt(err2 / np.where(ref2 > 0, ref2, 1.0)), np.sqrt(err2))
+
+
+class SeqReport:
+    """Whole-tensor and per-(b, h) rel-L2 of y and of the final state, accumulated over
+    blocks of sequences."""
+
+    def __init__(self, batch, nheads):
+        self.ey = np.zeros((batch, nheads))
+        self.ry = np.zeros((batch, nheads))
+        self.ef = np.zeros((batch, nheads))
+        self.rf = np.zeros((batch, nheads))
+
+    def add(self, b, h0, y_gpu, y_ref, f_gpu, f_ref):
+        h1 = h0 + y_ref.shape[2]
+        e, r = seq_errors(y_gpu, y_ref, (0, 1, 3))
+        self.ey[b, h0:h1], self.ry[b, h0:h1] = e, r
+        if f_gpu is not None:
+            e, r = seq_errors(f_gpu, f_ref, (0, 2, 3))
+            self.ef[b, h0:h1], self.rf[b, h0:h1] = e, r
+
+    def whole(self):
+        f = lambda e, r: np.sqrt(e.sum() / r.sum()) if r.sum() > 0 else np.sqrt(e.sum())
+        return f(self.ey, self.ry), f(self.ef, self.rf)
+
+    def worst(self):
+        """(worst y rel-L2, its (b, h)), (worst final-state rel-L2, its (b, h))."""
+        sy, sf = per_seq_rel_l2(self.ey, self.ry), per_seq_rel_l2(self.ef, self.rf)
+        iy = np.unravel_index(np.argmax(sy), sy.shape)
+        jf = np.unravel_index(np.argmax(sf), sf.shape)
+        return (float(sy[iy]), tuple(int(i) for i in iy)), (float(sf[jf]), tuple(int(i) for i in jf))
+
+
+def check_every_sequence(w, cpu_inputs, y_gpu, fin_gpu, heads_per_call=16):
+    """Compare every (b, h) sequence of the GPU output with the oracle.  The oracle runs
+    over all of them, a block of heads of one group at a time (which bounds host memory at
+    the largest sizes); each sequence's rel-L2 is recorded next to the whole-tensor one.
+    Returns the SeqReport."""
+    hpg = w.nheads // w.ngroups
+    step = max(1, min(heads_per_call, hpg))
+    rep = SeqReport(w.batch, w.nheads)
+    init = cpu_inputs["init_state"]
+    for b in range(w.batch):
+        for g in range(w.ngroups):
+            for h0 in range(g * hpg, (g + 1) * hpg, step):
+                h1 = min(h0 + step, (g + 1) * hpg)
+                sl = dict(x=cpu_inputs["x"][b:b + 1, :, h0:h1], dt=cpu_inputs["dt"][b:b + 1, :, h0:h1],
+                          A=cpu_inputs["A"][h0:h1], B=cpu_inputs["B"][b:b + 1, :, g:g + 1],
+                          C=cpu_inputs["C"][b:b + 1, :, g:g + 1], D=cpu_inputs["D"][h0:h1],
+                          init_state=None if init is None else init[b:b + 1, h0:h1])
+                y_ref, f_ref = oracle_fwd(sl)
+                fg = None if fin_gpu is None else np64(fin_gpu[b:b + 1, h0:h1])
+                rep.add(b, h0, np64(y_gpu[b:b + 1, :, h0:h1, :]), y_ref, fg, f_ref)
+    return rep
+
+
+def assert_every_sequence(w, rep, tol=None, label="fwd"):
+    """Whole-tensor and per-sequence bounds, with the worst sequence logged."""
+    tol = TOL[w.dtype] if tol is None else tol
+    wy, wf = rep.whole()
+    (sy, iy), (sf, jf) = rep.worst()
+    say(f"    [{label}] whole rel_l2 y={wy:.3e} final={wf:.3e}; worst sequence y={sy:.3e} "
+        f"at (b,h)={iy}, final={sf:.3e} at (b,h)={jf}")
+    assert wy <= tol and wf <= tol, (wy, wf)
+    assert sy <= tol, f"y of sequence (b,h)={iy}: rel_l2 {sy:.3e} > {tol}"
+    assert sf <= tol, f"final state of sequence (b,h)={jf}: rel_l2 {sf:.3e} > {tol}"

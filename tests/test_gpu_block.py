@@ -19,7 +19,7 @@ from mamba_ssd_chunked_03_amd import binding
 from mamba_ssd_chunked_03_amd.workloads import (BLOCKS, STRESS, TINY_FP32, BlockCfg, Workload,
                                                 generate_block, variants)
 from oracle import block as ob
-from parity import TOL, np64, rel_l2, say
+from parity import TOL, np64, per_seq_rel_l2, rel_l2, say, seq_errors
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +42,20 @@ def _check(name, got, ref, dtype):
     e = rel_l2(np64(got), ref)
     say(f"    {name}: rel_l2 {e:.2e}")
     assert e <= TOL[dtype], f"{name}: rel_l2 {e:.3e} > {TOL[dtype]}"
+
+
+def _check_per_head(w, out, ref_out, fin, ref_fin):
+    """Next to the whole tensors: every (b, h) slice on its own, the output's channels of
+    head h over all steps and head h's final state."""
+    tol = TOL[w.dtype]
+    shape = (w.batch, w.seqlen, w.nheads, w.headdim)
+    so = per_seq_rel_l2(*seq_errors(np64(out).reshape(shape), np.asarray(ref_out).reshape(shape),
+                                    (1, 3)))
+    sf = per_seq_rel_l2(*seq_errors(np64(fin), ref_fin, (2, 3)))
+    io = np.unravel_index(np.argmax(so), so.shape)
+    jf = np.unravel_index(np.argmax(sf), sf.shape)
+    say(f"    worst (b,h): out {so[io]:.2e} at {io}, final_state {sf[jf]:.2e} at {jf}")
+    assert so[io] <= tol and sf[jf] <= tol
 
 
 PRO_CASES = [
@@ -164,12 +178,13 @@ def test_block_matches_oracle(w, cfg):
     ref_out, ref_fin = _oracle_block(w, cfg, cpu)
     _check("out", out, ref_out, w.dtype)
     _check("final_state", fin, ref_fin, w.dtype)
+    _check_per_head(w, out, ref_out, fin, ref_fin)
 
 
 @pytest.mark.parametrize("name", list(BLOCKS))
 def test_block_full_size(name):
     """The model-shaped blocks at full size, in the launch configuration that
-    bench.py --block times, compared whole-tensor."""
+    bench.py --block times, compared whole-tensor and per (b, h)."""
     w, cfg = BLOCKS[name]
     say(f"[block full] {w.describe()} {cfg}")
     cpu = generate_block(w, cfg)
@@ -177,6 +192,7 @@ def test_block_full_size(name):
     ref_out, ref_fin = _oracle_block(w, cfg, cpu)
     _check("out", out, ref_out, w.dtype)
     _check("final_state", fin, ref_fin, w.dtype)
+    _check_per_head(w, out, ref_out, fin, ref_fin)
 
 
 def test_block_empty_sequence():

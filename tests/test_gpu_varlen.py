@@ -15,7 +15,7 @@ import torch
 from mamba_ssd_chunked_03_amd import binding
 from mamba_ssd_chunked_03_amd.workloads import Workload, generate
 from oracle.varlen import ssd_varlen_ref
-from parity import TOL, np64, rel_l2, say
+from parity import TOL, np64, per_seq_rel_l2, rel_l2, say, seq_errors
 
 pytestmark = pytest.mark.gpu
 
@@ -40,11 +40,32 @@ def _run(w, cu):
     return y, fin, ry, rf
 
 
-def _check(w, y, fin, ry, rf):
-    ey, ef = rel_l2(np64(y), ry), rel_l2(np64(fin), rf)
-    say(f"    y={ey:.2e} final={ef:.2e}")
-    assert ey <= TOL[w.dtype], f"y: {ey:.3e}"
-    assert ef <= TOL[w.dtype], f"final states: {ef:.3e}"
+def _check(w, y, fin, ry, rf, cu):
+    """Whole tensors, and every (sequence, head) on its own: y over the sequence's steps,
+    its final state."""
+    tol = TOL[w.dtype]
+    yg, fg = np64(y), np64(fin)
+    ey, ef = rel_l2(yg, ry), rel_l2(fg, rf)
+    # A sequence of one or a few steps has y = k x per head for a scalar k = dt C.B + D
+    # (one step), which can cancel to near zero: its own norm is then no scale for the
+    # rounding of the two terms.  Each (sequence, head) is measured against its own norm,
+    # or a quarter of the typical norm of that many outputs where its own is smaller.
+    ms = np.mean(ry ** 2, axis=(0, 1, 3))  # per head
+    sy = []
+    for s in range(len(cu) - 1):
+        if cu[s + 1] > cu[s]:
+            err2, ref2 = seq_errors(yg[:, cu[s]:cu[s + 1]], ry[:, cu[s]:cu[s + 1]], (0, 1, 3))
+            floor = (0.25 ** 2) * ms * (cu[s + 1] - cu[s]) * ry.shape[3]
+            sy.append(per_seq_rel_l2(err2, np.maximum(ref2, floor)).max())
+    err2, ref2 = seq_errors(fg, rf, (2, 3))
+    sf = per_seq_rel_l2(err2, ref2)
+    wy, wf = max(sy), sf.max()
+    say(f"    whole y={ey:.2e} final={ef:.2e}; worst (sequence, head) y={wy:.2e} "
+        f"final={wf:.2e}")
+    assert ey <= tol, f"y: {ey:.3e}"
+    assert ef <= tol, f"final states: {ef:.3e}"
+    assert wy <= tol, f"y of one (sequence, head): {wy:.3e}"
+    assert wf <= tol, f"final state of one (sequence, head): {wf:.3e}"
 
 
 LN = np.log
@@ -71,7 +92,7 @@ CASES = [
 def test_varlen_matches_oracle(w, cu):
     say(f"[varlen] {w.describe()} cu={cu}")
     y, fin, ry, rf = _run(w, cu)
-    _check(w, y, fin, ry, rf)
+    _check(w, y, fin, ry, rf, cu)
 
 
 def test_single_sequence_equals_ssd_fwd():
@@ -98,4 +119,4 @@ def test_varlen_full_size_packed_row():
     w = Workload("vl_2p7b_packed", 1, T, 80, 64, 128, 1, 256)
     say(f"[varlen full] {w.describe()} {len(cuts) - 1} sequences")
     y, fin, ry, rf = _run(w, cuts)
-    _check(w, y, fin, ry, rf)
+    _check(w, y, fin, ry, rf, cuts)
