@@ -120,6 +120,28 @@ ssd_status ssd_fwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const f
                    int chunk_len, const float* init_state, void* y, float* final_state,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the fixed device array ssd_fwd_noalloc keeps its stage buffers in (one per GPU). */
+#define SSD_NOALLOC_SCRATCH_BYTES (256u << 20)
+
+/* ssd_fwd for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The same computation and kernels
+ * as ssd_fwd (bit-identical y and final_state), with the stage buffers (dt_chunk, cs, chunk
+ * and entry states in `dtype`, C B^T blocks) taken from a fixed array of
+ * SSD_NOALLOC_SCRATCH_BYTES inside the library instead of a caller's workspace.  Nothing is
+ * allocated by the call: the runtime reserves the array on each GPU when the library's code
+ * is first loaded there, and it stays reserved until the process ends.  The first call on a
+ * device looks up the array's device address (hipGetSymbolAddress); later calls reuse it.
+ * Limit: the stage buffers, 8*B*H*ceil(T/Q)*Q + 2*B*H*ceil(T/Q)*P*N*sizeof(dtype) bytes plus
+ * the C B^T blocks (ssd_chunk_gram_size), each rounded up to 256 bytes, must fit the array
+ * (e.g. B=4, T=4096, H=80, P=64, N=128, Q=256 in bf16 needs 183 MB); larger problems return
+ * SSD_ERR_WORKSPACE before any launch.  Every call on one GPU shares its array: calls that
+ * overlap in time on one GPU (concurrent streams, or host threads) race and must not be
+ * issued.  Arguments and other errors as ssd_fwd. */
+ssd_status ssd_fwd_noalloc(const ssd_dims* dims, ssd_dtype dtype, const void* x, const float* dt,
+                           const float* A, const void* B, const void* C, const float* D,
+                           int chunk_len, const float* init_state, void* y, float* final_state,
+                           void* stream);
+
 /* Stage 0 (summary section "The Block-Decomposition SSD Algorithm", step 0, and the log
  * form of the 1-SS mask entries a_j ... a_{i+1}): for every (b, h, chunk c) and
  * position i < chunk_len, with t = c*chunk_len + i,

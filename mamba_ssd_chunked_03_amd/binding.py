@@ -19,7 +19,7 @@ EXPORTED = ("ssd_status_string", "ssd_fwd_workspace_size", "ssd_fwd", "ssd_chunk
             "ssd_chunk_scan", "ssd_decode_step", "ssd_bwd_workspace_size", "ssd_bwd",
             "ssd_block_prologue", "ssd_block_epilogue", "ssd_block_fwd_workspace_size",
             "ssd_block_fwd", "ssd_fwd_varlen_workspace_size", "ssd_fwd_varlen",
-            "ssd_bwd_saved")
+            "ssd_bwd_saved", "ssd_fwd_noalloc")
 
 
 class SsdDims(ctypes.Structure):
@@ -57,6 +57,8 @@ def library(path=LIB_PATH):
     lib.ssd_fwd_workspace_size.argtypes = [dims, i]
     lib.ssd_fwd.restype = i
     lib.ssd_fwd.argtypes = [dims, i, vp, fp, fp, vp, vp, fp, i, fp, vp, fp, vp, sz, vp]
+    lib.ssd_fwd_noalloc.restype = i
+    lib.ssd_fwd_noalloc.argtypes = [dims, i, vp, fp, fp, vp, vp, fp, i, fp, vp, fp, vp]
     lib.ssd_chunk_cumsum.restype = i
     lib.ssd_chunk_cumsum.argtypes = [dims, i, fp, fp, fp, fp, vp]
     lib.ssd_chunk_state.restype = i
@@ -222,6 +224,38 @@ def ssd_fwd(x, dt, A, B, C, D, chunk_len, init_state=None, y=None, final_state=N
                              _ptr(D), int(chunk_len), _ptr(init_state), _ptr(y),
                              _ptr(final_state), _ptr(workspace), _nbytes(workspace),
                              _stream(dev, stream)))
+    return y, final_state
+
+
+def ssd_fwd_noalloc(x, dt, A, B, C, D, chunk_len, init_state=None, y=None, final_state=None,
+                    want_final=True, stream=None):
+    """ssd_fwd with the stage buffers in the library's fixed device array (no workspace, no
+    allocation inside the call; y and final_state are allocated here only when not given).
+    Raises SsdError (SSD_ERR_WORKSPACE) when the problem does not fit the array."""
+    dev = x.device
+    f32 = torch.float32
+    _need(x, "x", device=dev)
+    code = _DTYPE_CODE.get(x.dtype)
+    if code is None:
+        raise TypeError(f"x must be fp32 or bf16, got {x.dtype}")
+    for t, n in ((B, "B"), (C, "C")):
+        _need(t, n, x.dtype, dev)
+    for t, n in ((dt, "dt"), (A, "A"), (D, "D")):
+        _need(t, n, f32, dev)
+    if init_state is not None:
+        _need(init_state, "init_state", f32, dev)
+    d = dims_of(x, B)
+    _layer_inputs(d, dt, A, C, D, init_state)
+    if y is None:
+        y = torch.empty_like(x)
+    _out(y, "y", x.dtype, dev, x.shape)
+    fshape = (d.batch, d.nheads, d.dstate, d.headdim)
+    if final_state is None and want_final:
+        final_state = torch.empty(fshape, dtype=f32, device=dev)
+    _out(final_state, "final_state", f32, dev, fshape)
+    _check(library().ssd_fwd_noalloc(ctypes.byref(d), code, _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                     _ptr(C), _ptr(D), int(chunk_len), _ptr(init_state), _ptr(y),
+                                     _ptr(final_state), _stream(dev, stream)))
     return y, final_state
 
 

@@ -6,6 +6,7 @@
 // fp32 VALU kernels.
 #include <string.h>
 
+#include <atomic>
 #include <initializer_list>
 
 #include "ssd_internal.h"
@@ -271,23 +272,38 @@ ssd_status ssd_chunk_scan(const ssd_dims* dims, ssd_dtype dtype, int chunk_len, 
                           (hipStream_t)stream);
 }
 
-ssd_status ssd_fwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const float* dt,
-                   const float* A, const void* B, const void* C, const float* D, int chunk_len,
-                   const float* init_state, void* y, float* final_state, void* workspace,
-                   size_t workspace_bytes_given, void* stream) {
-    Shape s;
-    ssd_status r = make_shape(dims, chunk_len, &s);
+}  // extern "C"
+
+// ssd_fwd_noalloc's stage buffers: one array per GPU, in the code object, allocated by the
+// runtime when the library's code is loaded on that GPU and held until the process ends.
+// On the host, `scratch` names only a stand-in: its device address comes from
+// hipGetSymbolAddress, once per device with that device current, and is kept per device
+// (scratch_of_current_device).  The stage kernels fully write every buffer before they read
+// it, so nothing in it needs clearing between calls.
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+// Arguments of ssd_fwd other than the workspace: checked, and the shape made.
+ssd_status fwd_check(const ssd_dims* dims, ssd_dtype dtype, const void* x, const float* dt,
+                     const float* A, const void* B, const void* C, const float* D, int chunk_len,
+                     const float* init_state, const void* y, const float* final_state, Shape* s) {
+    ssd_status r = make_shape(dims, chunk_len, s);
     if (r != SSD_OK) return r;
     if (!valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
-    const bool has_tokens = (size_t)s.B * s.T > 0;
+    const bool has_tokens = (size_t)s->B * s->T > 0;
     if (has_tokens && (!x || !dt || !A || !B || !C || !D || !y)) return SSD_ERR_NULL;
-    if (any_misaligned({x, B, C, y, workspace}) ||
-        any_misaligned4({dt, A, D, init_state, final_state}))
+    if (any_misaligned({x, B, C, y}) || any_misaligned4({dt, A, D, init_state, final_state}))
         return SSD_ERR_ALIGN;
-    Workspace ws;
-    const size_t need = workspace_bytes(s, &ws, (char*)workspace);
-    if (need > 0 && (!workspace || workspace_bytes_given < need)) return SSD_ERR_WORKSPACE;
-    hipStream_t st = (hipStream_t)stream;
+    return SSD_OK;
+}
+
+// The forward's launches, on the stage buffers of ws.
+ssd_status fwd_run(const Shape& s, ssd_dtype dtype, const void* x, const float* dt,
+                   const float* A, const void* B, const void* C, const float* D,
+                   const float* init_state, void* y, float* final_state, const Workspace& ws,
+                   hipStream_t st) {
+    ssd_status r;
+    const bool has_tokens = (size_t)s.B * s.T > 0;
     if (s.B == 0) return SSD_OK;
     if (has_tokens) {
         r = hip_status(ssd::launch_chunk_cumsum(s, dt, A, ws.dtc, ws.cs, st));
@@ -300,6 +316,82 @@ ssd_status ssd_fwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const f
                                              final_state, st));
     if (r != SSD_OK || !has_tokens) return r;
     return run_chunk_scan(s, dtype, x, B, C, ws.dtc, ws.cs, D, ws.entry, ws.gram, y, st);
+}
+
+// ---- scratch for callers that cannot allocate ------------------------------------------
+std::atomic<void*> scratch_addr[ssd::kMaxDevices];  // per device: the address of `scratch`
+
+ssd_status scratch_of_current_device(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SSD_ERR_HIP;
+    if (dev < 0 || dev >= ssd::kMaxDevices) return SSD_ERR_HIP;
+    void* p = scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SSD_ERR_HIP;
+        scratch_addr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return SSD_OK;
+}
+
+// The stage buffers packed tightly for the scratch array: the chunk and entry states take
+// the input dtype's size (ssd_fwd's workspace reserves fp32 for either dtype).
+size_t tight_workspace_bytes(const Shape& s, ssd_dtype dtype, Workspace* w, char* base) {
+    const size_t chunk_elems = (size_t)s.B * s.H * s.nC * s.Q;
+    const size_t state_bytes = (size_t)s.B * s.H * s.nC * s.P * s.N * (dtype == SSD_BF16 ? 2 : 4);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char* p = base ? base + off : nullptr;
+        off += round_up(bytes);
+        return (float*)p;
+    };
+    Workspace ws;
+    ws.dtc = take(chunk_elems * sizeof(float));
+    ws.cs = take(chunk_elems * sizeof(float));
+    ws.states = take(state_bytes);
+    ws.entry = take(state_bytes);
+    ws.gram = take(uses_gram(s, dtype) ? ssd::chunk_gram_bytes(s) : 0);
+    if (w) *w = ws;
+    return off;
+}
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_fwd(const ssd_dims* dims, ssd_dtype dtype, const void* x, const float* dt,
+                   const float* A, const void* B, const void* C, const float* D, int chunk_len,
+                   const float* init_state, void* y, float* final_state, void* workspace,
+                   size_t workspace_bytes_given, void* stream) {
+    Shape s;
+    ssd_status r = fwd_check(dims, dtype, x, dt, A, B, C, D, chunk_len, init_state, y,
+                             final_state, &s);
+    if (r != SSD_OK) return r;
+    if (any_misaligned({workspace})) return SSD_ERR_ALIGN;
+    Workspace ws;
+    const size_t need = workspace_bytes(s, &ws, (char*)workspace);
+    if (need > 0 && (!workspace || workspace_bytes_given < need)) return SSD_ERR_WORKSPACE;
+    return fwd_run(s, dtype, x, dt, A, B, C, D, init_state, y, final_state, ws,
+                   (hipStream_t)stream);
+}
+
+ssd_status ssd_fwd_noalloc(const ssd_dims* dims, ssd_dtype dtype, const void* x, const float* dt,
+                           const float* A, const void* B, const void* C, const float* D,
+                           int chunk_len, const float* init_state, void* y, float* final_state,
+                           void* stream) {
+    Shape s;
+    ssd_status r = fwd_check(dims, dtype, x, dt, A, B, C, D, chunk_len, init_state, y,
+                             final_state, &s);
+    if (r != SSD_OK) return r;
+    if (tight_workspace_bytes(s, dtype, nullptr, nullptr) > (size_t)SSD_NOALLOC_SCRATCH_BYTES)
+        return SSD_ERR_WORKSPACE;
+    if (s.B == 0) return SSD_OK;
+    void* base = nullptr;
+    r = scratch_of_current_device(&base);
+    if (r != SSD_OK) return r;
+    Workspace ws;
+    tight_workspace_bytes(s, dtype, &ws, (char*)base);
+    return fwd_run(s, dtype, x, dt, A, B, C, D, init_state, y, final_state, ws,
+                   (hipStream_t)stream);
 }
 
 size_t ssd_bwd_workspace_size(const ssd_dims* dims, int chunk_len) {

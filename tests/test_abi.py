@@ -157,6 +157,21 @@ def test_validation_errors_before_any_launch(lib):
                                None) == 1
 
 
+def test_noalloc_refuses_oversize_before_any_launch(lib):
+    """ssd_fwd_noalloc checks the problem against its fixed array before touching the GPU:
+    the long-context shape needs 2 x 671 MB of bf16 entry states and chunk states."""
+    def call(d, dtype=1, q=256):
+        p = [ctypes.c_void_p(256)] * 6
+        return lib.ssd_fwd_noalloc(ctypes.byref(d), dtype, *p, q, None, ctypes.c_void_p(256),
+                                   None, None)
+    assert call(D(1, 65536, 80, 64, 128, 8)) == 5
+    assert call(D(0, 65536, 80, 64, 128, 8)) == 0  # batch 0: nothing to do
+    assert call(D(1, 65536, 80, 64, 128, 8), dtype=7) == 3
+    assert call(D(h=3, g=2), q=64) == 2
+    assert lib.ssd_fwd_noalloc(ctypes.byref(D()), 0, None, None, None, None, None, None, 64, None,
+                               None, None, None) == 1
+
+
 def test_size_limit_is_exact(lib):
     """Every tensor must hold fewer than 2^31 elements, with T rounded up to whole chunks.
     At H = 80, P = 64, N = 256, Q = 256, 1638 chunks put both x and the chunk states at
