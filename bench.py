@@ -4,11 +4,13 @@ and the fp64 oracle timed on the host cores beside it.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mamba2_2p7b]
 
-One step is one pass of the whole forward (chunk_cumsum -> chunk_state -> state_passing
--> chunk_scan) over one batch of synthetic inputs already resident in HBM.  Inside the
-timed region each kernel is bracketed by HIP events on the stream it runs on, which
-gives every kernel's average duration; the step time itself comes from the host clock
-between two device synchronisations.  Prints one JSON line.
+One step is one ssd_fwd call: one pass of the whole forward (chunk_cumsum -> chunk_state
+-> state_passing -> chunk_scan) over one batch of synthetic inputs already resident in
+HBM.  The step time comes from the host clock between two device synchronisations around
+the K timed steps.  Right after them, K more steps run as the four stage calls with HIP
+events between stages on the launch stream, which gives every kernel's average duration.
+Before the warmup, a distribution pass times whole ssd_fwd calls one by one (warm, and
+cold after flushing the Infinity Cache).  Prints one JSON line.
 """
 import argparse
 import json
@@ -36,6 +38,9 @@ def parse():
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache step times (so that a kernel trace of the run "
                          "holds warm launches only)")
+    ap.add_argument("--stat-steps", type=int, default=0,
+                    help="ssd_fwd calls in each per-step distribution pass (warm, cold) run "
+                         "before the warmup; default max(steps, 200)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="rough budget for the oracle CPU baseline")
     ap.add_argument("--decode", default="", metavar="WORKLOAD",
@@ -476,50 +481,46 @@ def main():
     y = torch.empty_like(d_in["x"])
     fin = torch.empty((w.batch, w.nheads, w.dstate, w.headdim), dtype=torch.float32, device=dev)
 
-    # the stage buffers inside the workspace, exactly as ssd_fwd lays them out
-    nC = w.nchunks
-    f32 = torch.float32
-    chunk_n = w.batch * w.nheads * nC * Q
-    state_n = w.batch * w.nheads * nC * w.headdim * w.dstate
-    rnd = lambda b: (b + 255) // 256 * 256
-    offs = [0]
-    for nbytes in (chunk_n * 4, chunk_n * 4, state_n * 4, state_n * 4):
-        offs.append(offs[-1] + rnd(nbytes))
     gram_n = binding.ssd_chunk_gram_size(dims, d_in["x"].dtype, Q)
-    def view(off, n, shape, dtype=f32):
-        esz = torch.tensor([], dtype=dtype).element_size()
-        return ws[off:off + n * esz].view(dtype).view(shape)
-    cshape = (w.batch, w.nheads, nC, Q)
-    sshape = (w.batch, w.nheads, nC, w.headdim, w.dstate)
-    dtc, cs = view(offs[0], chunk_n, cshape), view(offs[1], chunk_n, cshape)
-    S = view(offs[2], state_n, sshape, d_in["x"].dtype)   # chunk states in the input dtype
-    E = view(offs[3], state_n, sshape, d_in["x"].dtype)   # entry states in the input dtype
-    gram = ws[offs[4]:offs[4] + gram_n]                     # C B^T blocks (bf16 path)
 
     def fwd():
         binding.ssd_fwd(d_in["x"], d_in["dt"], d_in["A"], d_in["B"], d_in["C"], d_in["D"], Q,
                         init_state=d_in["init_state"], y=y, final_state=fin, workspace=ws)
 
-    # the same calls ssd_fwd makes, one stage at a time, with an event between stages
-    def staged(ev):
-        ev[0].record()
-        binding.ssd_chunk_cumsum(dims, Q, d_in["dt"], d_in["A"], dtc, cs)
-        ev[1].record()
-        binding.ssd_chunk_state(dims, Q, d_in["x"], d_in["B"], dtc, cs, S, C=d_in["C"], gram=gram)
-        ev[2].record()
-        binding.ssd_state_passing(dims, Q, S, cs, init_state=d_in["init_state"],
-                                  entry_states=E, final_state=fin)
-        ev[3].record()
-        binding.ssd_chunk_scan(dims, Q, d_in["x"], d_in["B"], d_in["C"], dtc, cs, d_in["D"], E,
-                               gram=gram, y=y)
-        ev[4].record()
+    # the four stage calls ssd_fwd makes, on its workspace, marshalled once; run with a HIP
+    # event between stages (on torch's current stream, the launch stream) they give every
+    # kernel's duration
+    calls = binding.fwd_stage_calls(d_in["x"], d_in["dt"], d_in["A"], d_in["B"], d_in["C"],
+                                    d_in["D"], Q, d_in["init_state"], y, fin, ws)
+    names = [n for n, _ in calls]
+
+    def step(ev=None):
+        for i, (_, call) in enumerate(calls):
+            if ev is not None:
+                ev[i].record()
+            call()
+        if ev is not None:
+            ev[len(calls)].record()
+
+    # Per-step time distribution of whole ssd_fwd calls (HIP events per call): warm (back to
+    # back) and cold (the 256 MB Infinity Cache flushed by an untimed 1 GiB write before each
+    # call).  It runs first, so the GPU has been busy for a while when the timed steps begin.
+    nstat = args.stat_steps if args.stat_steps > 0 else max(args.steps, 200)
+    log(f"[bench] per-step times: {nstat} warm, {nstat} cold ssd_fwd calls")
+    fwd()
+    torch.cuda.synchronize()
+    y_ref, fin_ref = y.clone(), fin.clone()
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    step_us = {"warm": step_stats(torch, fwd, nstat), "steps": nstat}
+    if not args.no_cold:
+        step_us["cold"] = step_stats(torch, fwd, nstat, flush=lambda: scratch.fill_(1.0))
+    del scratch
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         fwd()
     torch.cuda.synchronize()
-    y_ref = y.clone()
-    # the timed steps: whole forward passes, back to back
+    # the timed steps: whole ssd_fwd calls, back to back
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -527,24 +528,20 @@ def main():
         fwd()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    # per-stage durations (HIP events on the launch stream), for the roofline
-    ev_steps = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # Right after, the same number of steps as the four stage calls with a HIP event between
+    # stages: every kernel's average duration.  (An event between two kernels keeps the next
+    # from starting while the last workgroups of the previous drain, so the staged steps run
+    # a little longer than the ssd_fwd steps above; the durations are each kernel's own.)
+    ev_steps = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+                for _ in range(args.steps)]
     for k in range(args.steps):
-        staged(ev_steps[k])
+        step(ev_steps[k])
     torch.cuda.synchronize()
-    if not torch.equal(y, y_ref):
-        log("[bench] WARNING: staged calls and ssd_fwd differ")
-    # per-step times: warm (back to back) and cold (the 256 MB Infinity Cache flushed by an
-    # untimed 1 GiB write before each step)
-    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    step_us = {"warm": step_stats(torch, fwd, args.steps)}
-    if not args.no_cold:
-        step_us["cold"] = step_stats(torch, fwd, args.steps, flush=lambda: scratch.fill_(1.0))
-    del scratch
+    if not (torch.equal(y, y_ref) and torch.equal(fin, fin_ref)):
+        log("[bench] WARNING: the stage calls and ssd_fwd differ")
     if not torch.isfinite(y.float()).all():
         log("[bench] WARNING: non-finite output")
 
-    names = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_scan"]
     per = {n: 0.0 for n in names}
     for ev in ev_steps:
         for i, n in enumerate(names):

@@ -361,15 +361,18 @@ ssd_status ssd_block_epilogue(const ssd_dims* dims, ssd_dtype dtype, const void*
                               const float* norm_b, int norm_groups, int rms, float eps,
                               void* out, void* stream);
 
-/* Bytes of workspace ssd_block_fwd needs (0 if the sizes are invalid): x, y, B, C, dt of
- * the layer and ssd_fwd's own workspace. */
+/* Bytes of workspace ssd_block_fwd needs (0 if the sizes are invalid): x, y, B, C of the
+ * layer and ssd_fwd's own workspace. */
 size_t ssd_block_fwd_workspace_size(const ssd_dims* dims, ssd_dtype dtype, int chunk_len);
 
 /* The block between the projections: ssd_block_prologue on the x|B|C and dt_raw columns of
  * zxbcdt ([B][T] rows of 2*H*P + 2*G*N + H values, [z | x | B | C | dt_raw], contiguous,
  * 16-byte aligned), ssd_fwd (A, D, chunk_len, init_state, final_state as there), then
- * ssd_block_epilogue with z from the first H*P columns; out [B][T][H*P] in `dtype`.
- * Errors as the three calls, all checked before the first launch. */
+ * ssd_block_epilogue with z from the first H*P columns; out [B][T][H*P] in `dtype`.  The
+ * step sizes softplus(dt_raw + dt_bias) are made inside the forward's cumsum pass, straight
+ * from the dt_raw columns (the same arithmetic as ssd_block_prologue's, so the result is
+ * that of the three calls bit for bit), and dt is never stored.  Errors as the three calls,
+ * all checked before the first launch. */
 ssd_status ssd_block_fwd(const ssd_dims* dims, ssd_dtype dtype, const void* zxbcdt,
                          const float* conv_w, const float* conv_b, int conv_k,
                          const float* dt_bias, const float* A, const float* D, int chunk_len,

@@ -259,6 +259,68 @@ def ssd_fwd_noalloc(x, dt, A, B, C, D, chunk_len, init_state=None, y=None, final
     return y, final_state
 
 
+def fwd_stage_calls(x, dt, A, B, C, D, chunk_len, init_state, y, final_state, workspace,
+                    stream=None):
+    """The four stage calls ssd_fwd makes, on the stage buffers of its workspace laid out as
+    ssd_fwd lays them: a list of (name, call) with every argument checked and marshalled
+    once here, so that each call(), a C-ABI call and a status check, costs little host time
+    (the benchmark records an event between stages).  Running the calls in order gives
+    exactly ssd_fwd's y, final state and workspace contents."""
+    dev = x.device
+    f32 = torch.float32
+    d = dims_of(x, B)
+    code = _DTYPE_CODE.get(x.dtype)
+    if code is None:
+        raise TypeError(f"x must be fp32 or bf16, got {x.dtype}")
+    for t, n in ((B, "B"), (C, "C")):
+        _need(t, n, x.dtype, dev)
+    for t, n in ((dt, "dt"), (A, "A"), (D, "D")):
+        _need(t, n, f32, dev)
+    _need(x, "x", device=dev)
+    if init_state is not None:
+        _need(init_state, "init_state", f32, dev)
+    _layer_inputs(d, dt, A, C, D, init_state)
+    _out(_need(y, "y", x.dtype, dev), "y", x.dtype, dev, x.shape)
+    _out(final_state, "final_state", f32, dev, (d.batch, d.nheads, d.dstate, d.headdim))
+    _need(workspace, "workspace", torch.uint8, dev)
+    if _nbytes(workspace) < ssd_fwd_workspace_size(d, chunk_len):
+        raise ValueError("workspace smaller than ssd_fwd_workspace_size")
+    sh = _stage_shapes(d, chunk_len)
+    nchunk = 1
+    for v in sh["chunk"]:
+        nchunk *= v
+    nstate = 1
+    for v in sh["state"]:
+        nstate *= v
+    rnd = lambda b: (b + 255) // 256 * 256
+    base = workspace.data_ptr()
+    offs = [0]
+    for nb in (nchunk * 4, nchunk * 4, nstate * 4, nstate * 4):
+        offs.append(offs[-1] + rnd(nb))
+    gram_n = ssd_chunk_gram_size(d, x.dtype, chunk_len)
+    dtc, cs, states, entry, gram = (ctypes.c_void_p(base + o) for o in offs)
+    lib = library()
+    st = _stream(dev, stream)
+    q = int(chunk_len)
+    dref = ctypes.byref(d)
+    gp = gram if gram_n else None
+
+    def call(fn, *args):
+        def run():
+            _check(fn(*args))
+        run.dims = d  # keeps the dims alive with the call
+        return run
+    return [
+        ("chunk_cumsum", call(lib.ssd_chunk_cumsum, dref, q, _ptr(dt), _ptr(A), dtc, cs, st)),
+        ("chunk_state", call(lib.ssd_chunk_state, dref, code, q, _ptr(x), _ptr(B), dtc, cs,
+                             states, _ptr(C) if gram_n else None, gp, st)),
+        ("state_passing", call(lib.ssd_state_passing, dref, code, q, states, cs,
+                               _ptr(init_state), entry, _ptr(final_state), st)),
+        ("chunk_scan", call(lib.ssd_chunk_scan, dref, code, q, _ptr(x), _ptr(B), _ptr(C), dtc,
+                            cs, _ptr(D), entry, gp, _ptr(y), st)),
+    ]
+
+
 def ssd_chunk_cumsum(dims, chunk_len, dt, A, dt_chunk=None, cs=None, stream=None):
     dev = dt.device
     sh = _stage_shapes(dims, chunk_len)

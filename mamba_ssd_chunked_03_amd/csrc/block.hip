@@ -42,9 +42,6 @@ __device__ __forceinline__ float sigmoid_fast(float v) {
     return __builtin_amdgcn_rcpf(1.f + exp2_fast(-v * kLog2e));
 }
 __device__ __forceinline__ float silu_f(float v) { return v * sigmoid_fast(v); }
-__device__ __forceinline__ float softplus_f(float v) {
-    return fmaxf(v, 0.f) + log1pf(expf(-fabsf(v)));
-}
 
 // V consecutive elements as floats (V = 8 for bf16 and 4 for fp32 are one 16-byte access)
 template <typename T, int V>
@@ -229,8 +226,9 @@ __global__ __launch_bounds__(64) void block_prologue_kernel(
     const int cv = blockIdx.x * 64 + threadIdx.x;
     if (cv < ncv)
         prologue_conv<T, V, K>(xbc, xstride, w, cb, xo, bo, co, b, Tn, d, gn, t0, tend, cv * V);
-    // the step sizes of these steps, spread over the tile's threads: all loads first
-    const int n = (tend - t0) * H, nthr = gridDim.x * 64;
+    // the step sizes of these steps, spread over the tile's threads: all loads first (none
+    // when the caller makes them elsewhere: dto null)
+    const int n = dto ? (tend - t0) * H : 0, nthr = gridDim.x * 64;
     for (int e0 = cv; e0 < n; e0 += 8 * nthr) {
         float v[8];
 #pragma unroll
@@ -244,7 +242,7 @@ __global__ __launch_bounds__(64) void block_prologue_kernel(
             if (e < n) {
                 const int h = e % H;
                 const float u = dt_bias ? v[q] + dt_bias[h] : v[q];
-                dto[((long long)b * Tn + t0 + e / H) * H + h] = softplus_f(u);
+                dto[((long long)b * Tn + t0 + e / H) * H + h] = softplus_step(u);
             }
         }
     }

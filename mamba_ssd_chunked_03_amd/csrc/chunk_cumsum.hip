@@ -15,6 +15,12 @@
 // latency-bound: every load is issued before any is used, and all heads of the block are
 // scanned at once.
 //
+// Step sizes fused in (the block path): instead of dt, the kernel can read the raw step
+// sizes straight from the rows of the block's projection output and make them positive
+// itself, softplus(raw + bias), the block prologue's map ("Mamba-2: Attention's Distant
+// Cousin", section "The Mamba-2 Block": the step size comes out of the input projection
+// with x, B and C).  The block then never writes or reads a dt tensor.
+//
 // Packed variable-length rows (cu != null, batch 1): a step where a sequence s >= 1 begins
 // (cu[s]) adds -kSeqGap to the running sum.  Every decay exp(cs_j - cs_i) between two steps of
 // different sequences then carries a factor exp(-kSeqGap) or smaller, which is 0 in fp32,
@@ -33,13 +39,31 @@ constexpr int kThreads = kHB * 64;
 // fp32 subnormal, so every decay across a start is exactly zero
 constexpr float kSeqGap = 120.f;
 
-template <int Q>
-__global__ __launch_bounds__(kThreads) void chunk_cumsum_kernel(const float* __restrict__ dt,
-                                                           const float* __restrict__ A,
-                                                           const int* __restrict__ cu, int nseq,
-                                                           float* __restrict__ dtc,
-                                                           float* __restrict__ cs, int T, int H,
-                                                           int nC) {
+// Where the step sizes come from: dt [B][T][H] fp32 as given, or raw rows of the block's
+// projection output (in bf16 or fp32), made positive here by softplus(raw + bias) -- the
+// block's step-size map fused into this pass, so that the block never writes dt.
+enum class DtSource { kF32, kRawBf16, kRawF32 };
+
+template <DtSource SRC>
+__device__ __forceinline__ float step_size(const float* dt, const void* raw, long long stride,
+                                           const float* bias, int b, int T, int H, int t,
+                                           int h) {
+    if constexpr (SRC == DtSource::kF32) {
+        return dt[((size_t)b * T + t) * H + h];
+    } else {
+        const long long at = ((long long)b * T + t) * stride + h;
+        const float v = SRC == DtSource::kRawBf16
+                            ? to_f32(reinterpret_cast<const __bf16*>(raw)[at])
+                            : reinterpret_cast<const float*>(raw)[at];
+        return softplus_step(bias ? v + bias[h] : v);
+    }
+}
+
+template <int Q, DtSource SRC>
+__global__ __launch_bounds__(kThreads) void chunk_cumsum_kernel(
+    const float* __restrict__ dt, const void* __restrict__ raw, long long raw_stride,
+    const float* __restrict__ bias, const float* __restrict__ A, const int* __restrict__ cu,
+    int nseq, float* __restrict__ dtc, float* __restrict__ cs, int T, int H, int nC) {
     constexpr int E = Q / 64;       // steps per lane
     constexpr int LD = Q + 4;       // padded row: 16-byte aligned, conflict-free writes
     __shared__ __align__(16) float tile[kHB][LD];
@@ -54,7 +78,6 @@ __global__ __launch_bounds__(kThreads) void chunk_cumsum_kernel(const float* __r
     const int t0 = c * Q;
     const int Lc = min(Q, T - t0);
     const int tid = threadIdx.x;
-    const float* src = dt + ((size_t)b * T + t0) * H + h0;
     // element e = tid + kThreads k of the Q x 16 tile
     constexpr int L = Q * kHB / kThreads;
     float v_in[L];
@@ -62,7 +85,9 @@ __global__ __launch_bounds__(kThreads) void chunk_cumsum_kernel(const float* __r
     for (int k = 0; k < L; ++k) {
         const int e = tid + kThreads * k;
         const int t = e / kHB, hh = e % kHB;
-        v_in[k] = (t < Lc && hh < nh) ? src[(size_t)t * H + hh] : 0.0f;
+        v_in[k] = (t < Lc && hh < nh)
+                      ? step_size<SRC>(dt, raw, raw_stride, bias, b, T, H, t0 + t, h0 + hh)
+                      : 0.0f;
     }
 #pragma unroll
     for (int k = 0; k < L; ++k) {
@@ -121,30 +146,40 @@ __global__ __launch_bounds__(kThreads) void chunk_cumsum_kernel(const float* __r
     }
 }
 
+
+template <int Q, DtSource SRC>
+void launch_q(unsigned blocks, const Shape& s, const float* dt, const DtRaw* raw, const float* A,
+              const int* cu, int nseq, float* dtc, float* cs, hipStream_t st) {
+    chunk_cumsum_kernel<Q, SRC><<<blocks, kThreads, 0, st>>>(
+        dt, raw ? raw->p : nullptr, raw ? raw->stride : 0, raw ? raw->bias : nullptr, A, cu,
+        nseq, dtc, cs, s.T, s.H, s.nC);
+}
+
+template <DtSource SRC>
+hipError_t launch_src(unsigned blocks, const Shape& s, const float* dt, const DtRaw* raw,
+                      const float* A, const int* cu, int nseq, float* dtc, float* cs,
+                      hipStream_t st) {
+    switch (s.Q) {
+        case 64: launch_q<64, SRC>(blocks, s, dt, raw, A, cu, nseq, dtc, cs, st); break;
+        case 128: launch_q<128, SRC>(blocks, s, dt, raw, A, cu, nseq, dtc, cs, st); break;
+        case 256: launch_q<256, SRC>(blocks, s, dt, raw, A, cu, nseq, dtc, cs, st); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_chunk_cumsum(const Shape& s, const float* dt, const float* A, float* dtc,
-                               float* cs, hipStream_t st, const int* cu, int nseq) {
+                               float* cs, hipStream_t st, const int* cu, int nseq,
+                               const DtRaw* raw) {
     const size_t hblocks = (size_t)(s.H + kHB - 1) / kHB;
     const unsigned blocks = (unsigned)((size_t)s.B * s.nC * hblocks);
     if (blocks == 0) return hipSuccess;
-    switch (s.Q) {
-        case 64:
-            chunk_cumsum_kernel<64><<<blocks, kThreads, 0, st>>>(dt, A, cu, nseq, dtc, cs, s.T,
-                                                             s.H, s.nC);
-            break;
-        case 128:
-            chunk_cumsum_kernel<128><<<blocks, kThreads, 0, st>>>(dt, A, cu, nseq, dtc, cs, s.T,
-                                                             s.H, s.nC);
-            break;
-        case 256:
-            chunk_cumsum_kernel<256><<<blocks, kThreads, 0, st>>>(dt, A, cu, nseq, dtc, cs, s.T,
-                                                             s.H, s.nC);
-            break;
-        default:
-            return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    if (!raw) return launch_src<DtSource::kF32>(blocks, s, dt, raw, A, cu, nseq, dtc, cs, st);
+    if (raw->dtype == SSD_BF16)
+        return launch_src<DtSource::kRawBf16>(blocks, s, dt, raw, A, cu, nseq, dtc, cs, st);
+    return launch_src<DtSource::kRawF32>(blocks, s, dt, raw, A, cu, nseq, dtc, cs, st);
 }
 
 }  // namespace ssd

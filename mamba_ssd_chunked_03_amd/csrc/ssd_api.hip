@@ -297,16 +297,17 @@ ssd_status fwd_check(const ssd_dims* dims, ssd_dtype dtype, const void* x, const
     return SSD_OK;
 }
 
-// The forward's launches, on the stage buffers of ws.
+// The forward's launches, on the stage buffers of ws.  raw (optional): the step sizes are
+// made from raw projection rows inside the cumsum pass instead of being read from dt.
 ssd_status fwd_run(const Shape& s, ssd_dtype dtype, const void* x, const float* dt,
                    const float* A, const void* B, const void* C, const float* D,
                    const float* init_state, void* y, float* final_state, const Workspace& ws,
-                   hipStream_t st) {
+                   hipStream_t st, const ssd::DtRaw* raw = nullptr) {
     ssd_status r;
     const bool has_tokens = (size_t)s.B * s.T > 0;
     if (s.B == 0) return SSD_OK;
     if (has_tokens) {
-        r = hip_status(ssd::launch_chunk_cumsum(s, dt, A, ws.dtc, ws.cs, st));
+        r = hip_status(ssd::launch_chunk_cumsum(s, dt, A, ws.dtc, ws.cs, st, nullptr, 0, raw));
         if (r != SSD_OK) return r;
         r = run_chunk_state(s, dtype, x, B, ws.dtc, ws.cs, ws.states, C, ws.gram, st);
         if (r != SSD_OK) return r;
@@ -577,7 +578,6 @@ ssd_status ssd_block_epilogue(const ssd_dims* dims, ssd_dtype dtype, const void*
 namespace {
 struct BlockWorkspace {
     void *x, *B, *C, *y;
-    float* dt;
     char* fwd;
     size_t fwd_bytes;
 };
@@ -596,7 +596,6 @@ size_t block_workspace_bytes(const Shape& s, ssd_dtype dtype, BlockWorkspace* w,
     ws.y = take(bt * s.H * s.P * e);
     ws.B = take(bt * s.G * s.N * e);
     ws.C = take(bt * s.G * s.N * e);
-    ws.dt = (float*)take(bt * s.H * sizeof(float));
     ws.fwd_bytes = workspace_bytes(s, nullptr, nullptr);
     ws.fwd = take(ws.fwd_bytes);
     if (w) *w = ws;
@@ -636,15 +635,24 @@ ssd_status ssd_block_fwd(const ssd_dims* dims, ssd_dtype dtype, const void* zxbc
     if (need > 0 && (!workspace || workspace_bytes_given < need)) return SSD_ERR_WORKSPACE;
     const size_t e = dtype == SSD_BF16 ? 2 : 4;
     const char* zx = (const char*)zxbcdt;
-    if (has_tokens) {
-        r = ssd_block_prologue(dims, dtype, zx + d * e, width, conv_w, conv_b, conv_k,
-                               zx + (2 * d + 2 * gn) * e, width, dt_bias, ws.x, ws.B, ws.C,
-                               ws.dt, stream);
-        if (r != SSD_OK) return r;
-    }
-    r = ssd_fwd(dims, dtype, ws.x, ws.dt, A, ws.B, ws.C, D, chunk_len, init_state, ws.y,
-                final_state, ws.fwd, ws.fwd_bytes, stream);
-    if (r != SSD_OK || !has_tokens) return r;
+    hipStream_t st = (hipStream_t)stream;
+    Workspace fws;
+    workspace_bytes(s, &fws, ws.fwd);
+    if (!has_tokens)  // only copies init_state (or zeros) to final_state
+        return fwd_run(s, dtype, nullptr, nullptr, A, nullptr, nullptr, D, init_state, nullptr,
+                       final_state, fws, st);
+    // the convolution and SiLU of x, B and C; the step sizes are made in the cumsum pass
+    ssd::BlockPrologueArgs pa;
+    pa.xbc = zx + d * e; pa.xbc_stride = width;
+    pa.conv_w = conv_w; pa.conv_b = conv_b; pa.conv_k = conv_k;
+    pa.dt_raw = nullptr; pa.dt_stride = width; pa.dt_bias = nullptr;
+    pa.x = ws.x; pa.Bm = ws.B; pa.Cm = ws.C; pa.dt = nullptr;
+    r = hip_status(ssd::launch_block_prologue(s, dtype, pa, st));
+    if (r != SSD_OK) return r;
+    const ssd::DtRaw raw{zx + (2 * d + 2 * gn) * e, width, dt_bias, dtype};
+    r = fwd_run(s, dtype, ws.x, nullptr, A, ws.B, ws.C, D, init_state, ws.y, final_state, fws, st,
+                &raw);
+    if (r != SSD_OK) return r;
     return ssd_block_epilogue(dims, dtype, ws.y, zxbcdt, width, norm_w, norm_b, norm_groups,
                               rms, eps, out, stream);
 }

@@ -74,12 +74,27 @@ template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float v) { return (__bf16)v; }
 
+// The step size's positivity map, softplus(v) = log(1 + exp(v)), written so that exp never
+// overflows; the block prologue and the chunk cumsum share it, so both give the same bits.
+__device__ __forceinline__ float softplus_step(float v) {
+    return fmaxf(v, 0.f) + log1pf(expf(-fabsf(v)));
+}
+
 // ---- launchers (each returns the launch status) -------------------------------------
+// Raw step sizes: rows of the projection output (row b*T + t at `stride` elements, H values
+// in dtype) plus a per-head bias (may be null); the step size is softplus(raw + bias).
+struct DtRaw {
+    const void* p;
+    long long stride;
+    const float* bias;
+    ssd_dtype dtype;
+};
 // cu (optional, device [nseq + 1], batch 1): packed sequence offsets; at every sequence
-// start the running sum drops by a gap that zeroes every decay across the start
+// start the running sum drops by a gap that zeroes every decay across the start.
+// raw (optional): take the step sizes from raw rows instead of dt (which is then unused).
 hipError_t launch_chunk_cumsum(const Shape& s, const float* dt, const float* A, float* dtc,
                                float* cs, hipStream_t st, const int* cu = nullptr,
-                               int nseq = 0);
+                               int nseq = 0, const DtRaw* raw = nullptr);
 // chunk states are read and entry states written in dtype (fp32 or bf16); the carried
 // state is fp32
 hipError_t launch_state_passing(const Shape& s, ssd_dtype dtype, const void* states,

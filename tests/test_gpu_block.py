@@ -195,6 +195,29 @@ def test_block_full_size(name):
     _check_per_head(w, out, ref_out, fin, ref_fin)
 
 
+@pytest.mark.parametrize("w,cfg", [BLOCK_CASES[1], BLOCK_CASES[2], BLOCK_CASES[0]],
+                         ids=["bf16_slow", "bf16_g2_rms", "fp32"])
+def test_block_fwd_equals_its_three_calls(w, cfg):
+    """ssd_block_fwd makes the step sizes inside the forward's cumsum pass (softplus fused,
+    dt never stored); it must give exactly what the prologue, ssd_fwd and the epilogue give
+    as three calls."""
+    say(f"[block = 3 calls] {w.describe()} {cfg}")
+    cpu = generate_block(w, cfg)
+    out, fin = _run_block(w, cfg, cpu)
+    d = {k: (None if v is None else v.to("cuda")) for k, v in cpu.items()}
+    H, P, N, G = w.nheads, w.headdim, w.dstate, w.ngroups
+    hp, gn = H * P, G * N
+    zx = d["zxbcdt"]
+    pro = binding.ssd_block_prologue(zx[:, :, hp:2 * hp + 2 * gn], d["conv_w"], d["conv_b"],
+                                     zx[:, :, 2 * hp + 2 * gn:], d["dt_bias"], H, P, N, G)
+    y, f2 = binding.ssd_fwd(pro["x"], pro["dt"], d["A"], pro["B"], pro["C"], d["D"],
+                            w.chunk_len, init_state=d["init_state"])
+    o2 = binding.ssd_block_epilogue(y, zx[:, :, :hp], d["norm_w"], d["norm_b"], cfg.norm_groups,
+                                    rms=cfg.rms, eps=cfg.eps, dstate=N, ngroups=G)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2) and torch.equal(fin, f2)
+
+
 def test_block_empty_sequence():
     """T = 0: nothing to compute; final_state = init_state."""
     w = Workload("blk_empty", 2, 0, 4, 32, 16, 1, 64, init_state=True)

@@ -58,6 +58,19 @@ def test_fwd_matches_oracle_full_size(w):
     assert_every_sequence(w, check_every_sequence(w, cpu, y, fin))
 
 
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("q", [64, 128], ids=["Q64", "Q128"])
+def test_fwd_130m_shape_at_other_chunk_lengths(q):
+    """The 130M-shaped layer at chunk lengths 64 and 128 (256 is the workload itself):
+    the chunk length is the block decomposition's tunable block size and leaves the result
+    unchanged, so every sequence must still match the oracle."""
+    w = variants(MAMBA2_130M, name=f"mamba2_130m_q{q}", chunk_len=q)
+    say(f"[fwd chunk length] {w.describe()}")
+    cpu = generate(w)
+    y, fin = gpu_fwd(to_device(cpu), w.chunk_len)
+    assert_every_sequence(w, check_every_sequence(w, cpu, y, fin))
+
+
 # The largest shapes the library accepts: tensors just under 2^31 elements (T rounded up to
 # whole chunks), each with a ragged last chunk.  A 32-bit overflow of an element or byte
 # offset anywhere on the path would show here.  The first puts x, y and the chunk states

@@ -120,3 +120,25 @@ def test_varlen_full_size_packed_row():
     say(f"[varlen full] {w.describe()} {len(cuts) - 1} sequences")
     y, fin, ry, rf = _run(w, cuts)
     _check(w, y, fin, ry, rf, cuts)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_dense_packing_of_short_sequences(dtype):
+    """Sequences of 1 to 4 steps packed at chunk length 256, about 100 starts per chunk.
+    Every start lowers the running log-decay sum by the gap, so the sums reach about
+    -120 k inside a chunk with k starts, and each decay carries a relative error of about
+    ulp(120 k): the documented precision limit of dense packing.  The bound checked here is
+    that limit (2e-3 in fp32); bf16 keeps the layer's own bar."""
+    rng = np.random.default_rng(5)
+    T = 1024
+    cuts = [0]
+    while cuts[-1] < T:
+        cuts.append(min(T, cuts[-1] + int(rng.integers(1, 5))))
+    w = Workload(f"vl_dense_{dtype}", 1, T, 4, 64, 64, 1, 256, dtype=dtype,
+                 log_neg_a_range=(LN(0.01), LN(0.1)))
+    say(f"[varlen dense] {w.describe()} {len(cuts) - 1} sequences")
+    y, fin, ry, rf = _run(w, cuts)
+    ey, ef = rel_l2(np64(y), ry), rel_l2(np64(fin), rf)
+    say(f"    whole y={ey:.2e} final={ef:.2e}")
+    bound = 2e-3 if dtype == "fp32" else TOL["bf16"]
+    assert ey <= bound and ef <= bound
