@@ -563,8 +563,14 @@ def main():
     # measured HBM bytes per launch, where recorded for the kernels as they are now built
     rec = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                        f"hbm_traffic_{w.name}.md")
+    sqrec = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                         "sq_counters_2p7b.md")
     for n in names:
         kernels[n]["hbm_traffic_bytes"] = traffic.current_traffic(rec, n)
+        if w.name == "mamba2_2p7b":  # the counter record is of this workload
+            busy = traffic.current_mfma_busy(sqrec, n)
+            if busy is not None:
+                kernels[n]["mfma_busy_counter"] = busy
     dom = max(names, key=lambda n: per[n])
     dk = kernels[dom]
     roof = {"bound": "hbm", "kernel": dom, "achieved": dk["hbm_GBps"],

@@ -97,6 +97,19 @@ def load(path):
     return out
 
 
+def current_mfma_busy(path, stage):
+    """The matrix-core busy fraction of `stage` in the forward run of the SQ-counter record
+    (profiles/sq_counters_*.md) if taken on the current sources, else None."""
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        m = re.match(r"\|\s*fwd\s*\|\s*(\w+)\s*\|[^|]*\|\s*([\d.]+)%\s*\|.*\|\s*([0-9a-f]+)\s*\|\s*$",
+                     line)
+        if m and m.group(1) == stage:
+            return round(float(m.group(2)) / 100, 4) if m.group(3) == source_hash(stage) else None
+    return None
+
+
 def current_traffic(path, stage):
     """HBM bytes per launch of `stage` if recorded for the current sources, else None."""
     rec = load(path).get(stage)
