@@ -49,30 +49,15 @@ namespace {
 
 using namespace mfma;
 
-// 8 bf16 at the relabelled k-slots {32kb + 4g .. +3, 32kb + 16 + 4g .. +3} of LDS row `row`
-__device__ __forceinline__ bf16x8 frag_rl(const unsigned char* base, int row, int kb, int g4,
-                                         int ppr) {
-    const uint2 lo = *reinterpret_cast<const uint2*>(base + swz_off(row, 32 * kb + 4 * g4, ppr));
-    const uint2 hi =
-        *reinterpret_cast<const uint2*>(base + swz_off(row, 32 * kb + 16 + 4 * g4, ppr));
-    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-}
 // 8 bf16 at the natural k-slots 32kb + 8g .. +7
 __device__ __forceinline__ bf16x8 frag_nat(const unsigned char* base, int row, int kb, int g4,
                                           int ppr) {
     return *reinterpret_cast<const bf16x8*>(base + swz_off(row, 32 * kb + 8 * g4, ppr));
 }
-// transpose read: A operand (row = feature f0 + l16, k = data rows r0 + {4g..4g+3, 16+4g..})
-__device__ __forceinline__ bf16x8 frag_tr(const unsigned char* base, int r0, int f0, int l16,
-                                         int g4, int ppr) {
-    const unsigned off = swz_off(r0 + 4 * g4 + (l16 >> 2), f0 + 4 * (l16 & 3), ppr);
-    const uint2 lo = lds_read_tr16(base + off);
-    const uint2 hi = lds_read_tr16(base + off + 16u * ppr * 16u);  // rows + 16 (ppr <= 16)
-    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-}
-// Row rb + rl of a swizzled [rows][8 ppr] bf16 matrix, with rb a multiple of 16 (so of
-// ppr): the swizzle depends only on rl, so a lane's part of the byte offset is computed once
-// per head and the row base is a uniform offset (an immediate where it is a constant).
+// Row rb + rl of a swizzled [rows][8 ppr] bf16 matrix, with rb a multiple of 16 and rl < 16:
+// the swizzle (by row % min(ppr, 16), as issue_rows writes it) depends only on rl, so a
+// lane's part of the byte offset is computed once per head and the row base is a uniform
+// offset (an immediate where it is a constant).
 __device__ __forceinline__ unsigned lane_part(int rl, int col, int ppr) {
     return (unsigned)(rl * ppr + ((col >> 3) ^ (rl & (ppr - 1)))) * 16u + (unsigned)(col & 7) * 2u;
 }
@@ -124,13 +109,17 @@ __device__ __forceinline__ float wavesum(float v) {
 }
 
 // nrows rows of a [rows][feat] bf16 matrix (row stride rowb bytes in HBM, from row
-// src_row0) into LDS rows dst_row0.. (PPRX 16-byte pieces per row), swizzled.  Each
-// instruction fills 64 consecutive 16-byte LDS slots (lane L at its base + 16 L), so the
-// swizzle is applied on the source side: slot `sl` of LDS row dr receives piece
-// sl ^ (dr % PPRX).  nrows * PPRX is a multiple of 64.
+// src_row0, from byte colb of each row) into LDS rows dst_row0.. (PPRX 16-byte pieces per
+// row), swizzled.  Each instruction fills 64 consecutive 16-byte LDS slots (lane L at its
+// base + 16 L), so the swizzle is applied on the source side: slot `sl` of LDS row dr
+// receives piece sl ^ (dr % 16) (dr % PPRX for rows of fewer than 16 pieces; the XOR keeps
+// a piece inside its aligned group of 16, and lane_part's row offset rl < 16 reads the
+// same swizzle).  nrows * PPRX is a multiple of 64.
 template <int PPRX, int NW>
 __device__ __forceinline__ void issue_rows(u32x4 rsrc, unsigned rowb, int src_row0, uint32_t lds,
-                                           int dst_row0, int nrows, int wave, int lane) {
+                                           int dst_row0, int nrows, int wave, int lane,
+                                           unsigned colb = 0) {
+    constexpr int SWM = (PPRX < 16 ? PPRX : 16) - 1;
     const int ninst = nrows * PPRX / 64;
     const uint32_t base = lds + (unsigned)dst_row0 * PPRX * 16u;
     for (int k = wave; k < ninst; k += NW) {
@@ -138,7 +127,7 @@ __device__ __forceinline__ void issue_rows(u32x4 rsrc, unsigned rowb, int src_ro
         const int r = m / PPRX, sl = m % PPRX;
         const int dr = dst_row0 + r;
         dma16(rsrc, base + (unsigned)k * 1024u,
-              (unsigned)(src_row0 + r) * rowb + (unsigned)(sl ^ (dr & (PPRX - 1))) * 16u);
+              (unsigned)(src_row0 + r) * rowb + colb + (unsigned)(sl ^ (dr & SWM)) * 16u);
     }
 }
 
@@ -156,23 +145,35 @@ struct BwdCfg {
     static constexpr int PPR = P / 8, NPR = N / 8;  // 16-byte pieces per row
     static constexpr int NKB = N / 32, PKB = P / 32;
     static constexpr int NT = N / 16, PT = P / 16;
+    // dstate 256: the terms through the carried states come from chunk_bwd_carried_kernel
+    // (E and F are not copied here), B and C pass through LDS in column slices for C B^T
+    // and in two halves of n for the W products, and the state waves' dB, dC accumulators
+    // start from that kernel's sums
+    static constexpr bool EXT = N > 128;
+    static constexpr int SLN = EXT ? 64 : N;        // columns of B / C per C B^T slice
+    static constexpr int NSL = N / SLN;
+    static constexpr int HN = EXT ? 128 : N;        // columns of B / C per W-product pass
+    static constexpr int NHP = N / HN;
     static constexpr unsigned XYB = (Q + 64) * P * 2;  // x rows [0, j0+64), dy rows [j0, Q)
-    static constexpr unsigned EB = P * N * 2;          // E or F, [p][n]
+    static constexpr unsigned EB = EXT ? 0 : P * N * 2;  // E or F, [p][n]
     static constexpr unsigned FB = Q * 4;              // cs or dt
     static constexpr unsigned ITEM = XYB + 2 * EB + 2 * FB;
-    static constexpr unsigned BCB = Q * N * 2;         // one B or C chunk
+    static constexpr unsigned BCB = Q * SLN * 2;       // one B or C chunk (slice)
     // exchange from the state waves to the strip waves, after the two item buffers
     static constexpr unsigned X_BF = 2 * ITEM;                // (F B_j) tiles, bf16 [4][PT][64]
     static constexpr unsigned X_OB = X_BF + 4 * PT * 64 * 8;  // ob, oc per column [2][64]
     static constexpr unsigned X_EF = X_OB + 2 * 64 * 4;       // <E, F> share per wave [4]
     static constexpr unsigned X_SH = X_EF + 16;               // workgroup shares [2][4][2]
-    static constexpr unsigned LDS = X_SH + 64;
     // the W accumulators (bf16) travel from the strip waves after the B/C rows at the end
-    static constexpr unsigned X_W = (Q + 64) * N * 2;
-    static_assert(P == 64 && (N == 64 || N == 128), "shape");
+    // (past the exchange area where those rows are a half of n)
+    static constexpr unsigned X_W =
+        EXT ? ((Q + 64) * HN * 2 > X_SH + 64 ? (Q + 64) * HN * 2 : X_SH + 64) : (Q + 64) * N * 2;
+    static constexpr unsigned WB = 4u * PAIRS * 64 * 16;
+    static constexpr unsigned LDS = EXT ? X_W + WB : X_SH + 64;
+    static_assert(P == 64 && (N == 64 || N == 128 || N == 256), "shape");
     static_assert(2 * BCB <= 2 * ITEM, "B and C chunks fit the item buffers");
-    static_assert(X_W + 4u * PAIRS * 64 * 16 <= 2 * ITEM, "end-of-loop staging fits");
-    static_assert(LDS <= 160 * 1024, "LDS");
+    static_assert(EXT || X_W + WB <= 2 * ITEM, "end-of-loop staging fits");
+    static_assert(X_W % 16 == 0 && LDS <= 160 * 1024, "LDS");
 };
 
 // One head's rows, states and step sizes, copied by the four state waves (iw = 0..3): their
@@ -193,11 +194,13 @@ __device__ __forceinline__ void issue_item(const __bf16* x, const __bf16* dy, co
     // x rows [0, j0 + 64) at LDS rows 0.., dy rows [j0, Q) at LDS rows j0 + 64..
     issue_rows<C_::PPR, NW>(xr, rowb, 0, lds, 0, j0 + 64, wave, lane);
     issue_rows<C_::PPR, NW>(yr, rowb, j0, lds, j0 + 64, Q - j0, wave, lane);
-    const size_t so = ((size_t)(b * H + h) * nC + c) * P * N;
-    issue_rows<C_::NPR, NW>(raw_rsrc(entry + so, C_::EB), N * 2, 0, lds + C_::XYB, 0, P, wave,
-                            lane);
-    issue_rows<C_::NPR, NW>(raw_rsrc(exitg + so, C_::EB), N * 2, 0, lds + C_::XYB + C_::EB, 0, P,
-                            wave, lane);
+    if constexpr (!C_::EXT) {
+        const size_t so = ((size_t)(b * H + h) * nC + c) * P * N;
+        issue_rows<C_::NPR, NW>(raw_rsrc(entry + so, C_::EB), N * 2, 0, lds + C_::XYB, 0, P,
+                                wave, lane);
+        issue_rows<C_::NPR, NW>(raw_rsrc(exitg + so, C_::EB), N * 2, 0, lds + C_::XYB + C_::EB,
+                                0, P, wave, lane);
+    }
     const size_t cb = ((size_t)(b * H + h) * nC + c) * Q;
     if (wave == 0 && lane < Q / 4)
         dma16(raw_rsrc(cs + cb, C_::FB), lds + C_::XYB + 2 * C_::EB, lane * 16u);
@@ -205,21 +208,26 @@ __device__ __forceinline__ void issue_item(const __bf16* x, const __bf16* dy, co
         dma16(raw_rsrc(dtc + cb, C_::FB), lds + C_::XYB + 2 * C_::EB + C_::FB, lane * 16u);
 }
 
+// B and C of the group's chunk, columns [part * cols, +cols) (cols = SLN for whole chunks,
+// HN for the rows of the W products; all of n below dstate 256)
 template <int Q, int N, int P>
 __device__ __forceinline__ void issue_bc(const __bf16* Bm, const __bf16* Cm, int b, int g, int t0,
                                          int Lc, int T, int G, int j0, bool rows_only,
-                                         uint32_t lds, int wave, int lane) {
+                                         uint32_t lds, int wave, int lane, int part = 0) {
     using C_ = BwdCfg<Q, N, P>;
+    constexpr int SPR = C_::SLN / 8, HPR = C_::HN / 8;  // pieces per staged row
     const unsigned rowb = (unsigned)(G * N * 2);
     const size_t bo = ((size_t)(b * T + t0) * G + g) * N;
     const u32x4 br = raw_rsrc(Bm + bo, (unsigned)Lc * rowb);
     const u32x4 cr = raw_rsrc(Cm + bo, (unsigned)Lc * rowb);
     if (!rows_only) {  // whole chunks: B at 0, C at BCB
-        issue_rows<C_::NPR, C_::NW>(br, rowb, 0, lds, 0, Q, wave, lane);
-        issue_rows<C_::NPR, C_::NW>(cr, rowb, 0, lds + C_::BCB, 0, Q, wave, lane);
+        const unsigned colb = (unsigned)part * C_::SLN * 2u;
+        issue_rows<SPR, C_::NW>(br, rowb, 0, lds, 0, Q, wave, lane, colb);
+        issue_rows<SPR, C_::NW>(cr, rowb, 0, lds + C_::BCB, 0, Q, wave, lane, colb);
     } else {  // B rows [0, j0 + 64) at rows 0.., C rows [j0, Q) at rows j0 + 64..
-        issue_rows<C_::NPR, C_::NW>(br, rowb, 0, lds, 0, j0 + 64, wave, lane);
-        issue_rows<C_::NPR, C_::NW>(cr, rowb, j0, lds, j0 + 64, Q - j0, wave, lane);
+        const unsigned colb = (unsigned)part * C_::HN * 2u;
+        issue_rows<HPR, C_::NW>(br, rowb, 0, lds, 0, j0 + 64, wave, lane, colb);
+        issue_rows<HPR, C_::NW>(cr, rowb, j0, lds, j0 + 64, Q - j0, wave, lane, colb);
     }
 }
 
@@ -289,11 +297,49 @@ __device__ __forceinline__ void bwd_strip_role(
     const int wave = k_.wave, cw = k_.cw, lane = k_.lane;
     float* const shares = reinterpret_cast<float*>(smem + C_::X_SH);
 
-    issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, false, k_.lds0, wave, lane);
-    dma_barrier();
     // C B^T on the strips, rounded to bf16: G^T[i][j] = B_i . C_j and G[t][j] = C_t . B_j
     uint2 gt[2 * PAIRS];
-    {
+    if constexpr (C_::EXT) {
+        // summed in fp32 over column slices of B and C
+        constexpr int SPR = C_::SLN / 8, SKB = C_::SLN / 32;
+        const int l16 = lane & 15, g4 = lane >> 4;
+        const int jl = j0 + 16 * cw + l16;
+        const unsigned char* sBc = smem;
+        const unsigned char* sCc = smem + C_::BCB;
+        f32x4 ga[2 * PAIRS];
+#pragma unroll
+        for (int s = 0; s < 2 * PAIRS; ++s) ga[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+        for (int sl = 0; sl < C_::NSL; ++sl) {
+            issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, false, k_.lds0, wave, lane, sl);
+            dma_barrier();
+            bf16x8 bj[SKB], cj[SKB];
+#pragma unroll
+            for (int kb = 0; kb < SKB; ++kb) {
+                bj[kb] = frag_nat(sBc, jl, kb, g4, SPR);
+                cj[kb] = frag_nat(sCc, jl, kb, g4, SPR);
+            }
+#pragma unroll
+            for (int k = 0; k < PAIRS; ++k) {
+                const bool isrs = k < RSP;
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int row = (isrs ? 32 * k : j0 + 32 * (k - RSP)) + 16 * u + l16;
+                    const unsigned char* src = isrs ? sBc : sCc;
+#pragma unroll
+                    for (int kb = 0; kb < SKB; ++kb)
+                        ga[2 * k + u] = mfma16(frag_nat(src, row, kb, g4, SPR),
+                                               isrs ? cj[kb] : bj[kb], ga[2 * k + u]);
+                }
+            }
+            lds_barrier();  // this slice is no longer read
+        }
+#pragma unroll
+        for (int s = 0; s < 2 * PAIRS; ++s)
+            gt[s] = make_uint2(pack_bf16(ga[s][0], ga[s][1]), pack_bf16(ga[s][2], ga[s][3]));
+    } else {
+        issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, false, k_.lds0, wave, lane);
+        dma_barrier();
         const int l16 = lane & 15, g4 = lane >> 4;
         const int jl = j0 + 16 * cw + l16;
         const unsigned char* sBc = smem;
@@ -318,8 +364,8 @@ __device__ __forceinline__ void bwd_strip_role(
                 gt[2 * k + u] = make_uint2(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]));
             }
         }
+        lds_barrier();  // B and C are no longer read: the item buffers are free
     }
-    lds_barrier();  // B and C are no longer read: the item buffers are free
 
     f32x4 wacc[2 * PAIRS];  // W over the strips, summed over the heads
 #pragma unroll
@@ -332,7 +378,7 @@ __device__ __forceinline__ void bwd_strip_role(
         const int h = g * hpg + hh;
         const int buf = hh & 1;
         lds_barrier();  // this head's rows are scaled; the other buffer is free
-        if (hh > 0 && wave == 0 && lane == 0) {
+        if (!C_::EXT && hh > 0 && wave == 0 && lane == 0) {
             const float* sh = shares + (buf ^ 1) * 8;
             const size_t pi = ((size_t)(b * H + h - 1) * nC + c) * NJ + RJ;
             lt_part[pi] = (sh[0] + sh[2]) + (sh[4] + sh[6]);
@@ -549,19 +595,22 @@ __device__ __forceinline__ void bwd_strip_role(
             }
         }
         // this block's shares of the chunk-end term (dt_j ob_j, and exp(cs_last) <E, F> on
-        // the first block) and of dD (x_j . dy_j)
-        float lt = (g4 == 0 && vj) ? dtj * ob : 0.f;
-        if (j0 == 0 && ln == 0)
-            lt = fmaf(exp2_fast(cs_last * kLog2e),
-                      reinterpret_cast<const float*>(smem + C_::X_EF)[cw], lt);
-        lt = wavesum(lt);
-        if (lane == 0) shares[buf * 8 + 2 * cw] = lt;
+        // the first block) and of dD (x_j . dy_j); at dstate 256 the carried-state kernel
+        // writes both
+        if constexpr (!C_::EXT) {
+            float lt = (g4 == 0 && vj) ? dtj * ob : 0.f;
+            if (j0 == 0 && ln == 0)
+                lt = fmaf(exp2_fast(cs_last * kLog2e),
+                          reinterpret_cast<const float*>(smem + C_::X_EF)[cw], lt);
+            lt = wavesum(lt);
+            if (lane == 0) shares[buf * 8 + 2 * cw] = lt;
+        }
         lds_barrier();  // every state wave's copies of the next head have landed
         if (hh + 1 < hpg)
             prescale_rows<Q, N, P>(smem + (buf ^ 1) * C_::ITEM, j0, (int)threadIdx.x, 512);
     }
     dma_barrier();
-    if (wave == 0 && lane == 0) {
+    if (!C_::EXT && wave == 0 && lane == 0) {
         const float* sh = shares + ((hpg - 1) & 1) * 8;
         const size_t pi = ((size_t)(b * H + g * hpg + hpg - 1) * nC + c) * NJ + k_.rj;
         lt_part[pi] = (sh[0] + sh[2]) + (sh[4] + sh[6]);
@@ -577,6 +626,13 @@ __device__ __forceinline__ void bwd_strip_role(
                                 pack_bf16(wacc[2 * k + 1][0], wacc[2 * k + 1][1]),
                                 pack_bf16(wacc[2 * k + 1][2], wacc[2 * k + 1][3]));
     dma_barrier();
+    // the other halves of n: the state waves have read the previous half's rows
+#pragma unroll 1
+    for (int part = 1; part < C_::NHP; ++part) {
+        lds_barrier();
+        issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, true, k_.lds0, wave, lane, part);
+        dma_barrier();
+    }
 }
 
 // ------------------------------------------------------------------ state waves
@@ -766,6 +822,120 @@ __device__ __forceinline__ void bwd_state_role(
     }
 }
 
+// The state waves at dstate 256.  chunk_bwd_carried_kernel has already formed the terms
+// through the carried states, so per head these waves hand its (F B_j) tile and ob, oc to
+// the strip waves and issue and scale the copies; after the loop they finish dB and dC from
+// that kernel's head sums, one half of n at a time.  The barriers are bwd_state_role's.
+template <int Q, int N, int P>
+__device__ __forceinline__ void bwd_state_role_ext(
+    const BwdCtx& k_, unsigned char* smem, const __bf16* x, const __bf16* Bm, const __bf16* Cm,
+    const float* dtc, const float* cs, const __bf16* dy, const __bf16* xfb, const float* direct,
+    const float* dcs, const float* dBs, const float* dCs, __bf16* dB, __bf16* dC) {
+    using C_ = BwdCfg<Q, N, P>;
+    constexpr int PAIRS = C_::PAIRS, PT = C_::PT, HN = C_::HN, HPR = HN / 8, HT = HN / 16;
+    const int b = k_.b, g = k_.g, c = k_.c, j0 = k_.j0, t0 = k_.t0, Lc = k_.Lc;
+    const int hpg = k_.hpg, T = k_.T, H = k_.H, G = k_.G, nC = k_.nC;
+    const int wave = k_.wave, cw = k_.cw, lane = k_.lane;
+    const int rsp = (j0 + 64) / 32;  // row-strip blocks (rows 32 k), then column-strip blocks
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int jl = j0 + 16 * cw + l16;
+    const bool vj = jl < Lc;
+
+#pragma unroll 1
+    for (int sl = 0; sl < C_::NSL; ++sl) {  // the strip waves' C B^T slices
+        issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, false, k_.lds0, wave, lane, sl);
+        dma_barrier();
+        lds_barrier();
+    }
+
+    issue_item<Q, N, P>(x, dy, nullptr, nullptr, cs, dtc, b, g * hpg, c, j0, Lc, T, H, nC,
+                        k_.lds0, wave - 4, lane);
+    dma_barrier();
+    prescale_rows<Q, N, P>(smem, j0, (int)threadIdx.x - 256, 256);
+    lds_barrier();
+#pragma unroll 1
+    for (int hh = 0; hh < hpg; ++hh) {
+        const int h = g * hpg + hh;
+        const int buf = hh & 1;
+        lds_barrier();
+        // (F B_j)[p] for p = 16 pt + 4 g4 .. + 3 of column j, and ob_j, oc_j
+        const size_t cb = ((size_t)(b * H + h) * nC + c) * Q;
+        const __bf16* fr = xfb + ((size_t)(b * T + t0 + jl) * H + h) * P + 4 * g4;
+        uint2 fb[PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+            fb[pt] = vj ? *reinterpret_cast<const uint2*>(fr + 16 * pt) : make_uint2(0u, 0u);
+        const float ob = direct[cb + jl], oc = dcs[cb + jl];
+        if (hh + 1 < hpg)
+            issue_item<Q, N, P>(x, dy, nullptr, nullptr, cs, dtc, b, h + 1, c, j0, Lc, T, H, nC,
+                                k_.lds0 + (buf ^ 1) * C_::ITEM, wave - 4, lane);
+        uint2* xbf = reinterpret_cast<uint2*>(smem + C_::X_BF) + (cw * PT) * 64 + lane;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) xbf[pt * 64] = fb[pt];
+        float* xob = reinterpret_cast<float*>(smem + C_::X_OB);
+        if (g4 == 0) {
+            xob[16 * cw + l16] = ob;
+            xob[64 + 16 * cw + l16] = oc;
+        }
+        lds_barrier();  // hand-off to the strip waves
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+        if (hh + 1 < hpg)
+            prescale_rows<Q, N, P>(smem + (buf ^ 1) * C_::ITEM, j0, (int)threadIdx.x, 512);
+    }
+    dma_barrier();
+    issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, true, k_.lds0, wave, lane);
+    dma_barrier();  // B / C rows (first half of n) and the strip waves' W are in LDS
+    const uint4* xw = reinterpret_cast<const uint4*>(smem + C_::X_W) + (cw * PAIRS) * 64 + lane;
+    unsigned ptn[HT];
+#pragma unroll
+    for (int nt = 0; nt < HT; ++nt)
+        ptn[nt] = lane_part(4 * g4 + (l16 >> 2), 16 * nt + 4 * (l16 & 3), HPR);
+    constexpr unsigned N16 = 16u * HPR * 16u;
+#pragma unroll 1
+    for (int part = 0; part < C_::NHP; ++part) {
+        if (part > 0) {
+            lds_barrier();
+            issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, true, k_.lds0, wave, lane, part);
+            dma_barrier();
+        }
+        // dB^T, dC^T [n][j] for n in this half, from the carried-state sums
+        const size_t ro = ((size_t)(b * T + t0 + jl) * G + g) * N + part * HN + 4 * g4;
+        f32x4 dbacc[HT], dcacc[HT];
+#pragma unroll
+        for (int nt = 0; nt < HT; ++nt) {
+            dbacc[nt] = vj ? *reinterpret_cast<const f32x4*>(dBs + ro + 16 * nt)
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
+            dcacc[nt] = vj ? *reinterpret_cast<const f32x4*>(dCs + ro + 16 * nt)
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll 1
+        for (int k = 0; k < rsp; ++k) {
+            const bf16x8 w8 = __builtin_bit_cast(bf16x8, xw[k * 64]);
+#pragma unroll
+            for (int nt = 0; nt < HT; ++nt)
+                dcacc[nt] = mfma16(ld_tr(rows_at(smem, 32 * k, HPR), ptn[nt], N16), w8, dcacc[nt]);
+        }
+#pragma unroll 1
+        for (int k = rsp; k < PAIRS; ++k) {
+            const bf16x8 w8 = __builtin_bit_cast(bf16x8, xw[k * 64]);
+            const int rho = j0 + 32 * (k - rsp) + 64;
+#pragma unroll
+            for (int nt = 0; nt < HT; ++nt)
+                dbacc[nt] = mfma16(ld_tr(rows_at(smem, rho, HPR), ptn[nt], N16), w8, dbacc[nt]);
+        }
+        if (vj) {
+#pragma unroll
+            for (int nt = 0; nt < HT; ++nt) {
+                *reinterpret_cast<uint2*>(dB + ro + 16 * nt) = make_uint2(
+                    pack_bf16(dbacc[nt][0], dbacc[nt][1]), pack_bf16(dbacc[nt][2], dbacc[nt][3]));
+                *reinterpret_cast<uint2*>(dC + ro + 16 * nt) = make_uint2(
+                    pack_bf16(dcacc[nt][0], dcacc[nt][1]), pack_bf16(dcacc[nt][2], dcacc[nt][3]));
+            }
+        }
+    }
+}
+
 template <int Q, int N, int P>
 __global__ __launch_bounds__(512) void chunk_bwd_mfma_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ Bm, const __bf16* __restrict__ Cm,
@@ -773,8 +943,9 @@ __global__ __launch_bounds__(512) void chunk_bwd_mfma_kernel(
     const __bf16* __restrict__ entry, const __bf16* __restrict__ exitg,
     const __bf16* __restrict__ dy, __bf16* __restrict__ dx, __bf16* __restrict__ dB,
     __bf16* __restrict__ dC, float* __restrict__ dcs, float* __restrict__ direct,
-    float* __restrict__ xs, float* __restrict__ lt_part, float* __restrict__ dd_part, int T,
-    int H, int G, int nC) {
+    float* __restrict__ xs, float* __restrict__ lt_part, float* __restrict__ dd_part,
+    const __bf16* __restrict__ xfb, const float* __restrict__ dBs, const float* __restrict__ dCs,
+    int T, int H, int G, int nC) {
     using C_ = BwdCfg<Q, N, P>;
     extern __shared__ __align__(16) unsigned char smem[];
     BwdCtx k_;
@@ -820,23 +991,294 @@ __global__ __launch_bounds__(512) void chunk_bwd_mfma_kernel(
         // waves wait on: they go first when both are ready to issue (the saved backward at
         // 2.7B: 538 -> 519 us)
         __builtin_amdgcn_s_setprio(3);
-        bwd_state_role<Q, N, P>(k_, smem, x, Bm, Cm, dtc, cs, entry, exitg, dy, dB, dC);
+        if constexpr (C_::EXT)
+            bwd_state_role_ext<Q, N, P>(k_, smem, x, Bm, Cm, dtc, cs, dy, xfb, direct, dcs, dBs,
+                                        dCs, dB, dC);
+        else
+            bwd_state_role<Q, N, P>(k_, smem, x, Bm, Cm, dtc, cs, entry, exitg, dy, dB, dC);
+    }
+}
+
+// ------------------------------------------------------------------ carried states, dstate 256
+// At dstate 256 the dB and dC accumulators of a 64-row block over all n (two 64 x 256 fp32
+// tiles) do not fit beside the strip products, and E, F (64 x 256 bf16 each) do not fit
+// double-buffered beside the x / dy rows.  The terms through the carried states therefore
+// run first, in this kernel: one workgroup of eight waves per (batch, group, chunk, block J
+// of 64 rows), looping over the heads of the group; wave w owns the 16 columns
+// j = j0 + 16 (w % 4) + (0..15) and the half w / 4 of n.  Per head it writes
+//   xfb[j][p] = (F B_j)[p] rounded to bf16 (the in-chunk kernel's operand for dx),
+//   direct_j = ob_j = exp(cs_last - cs_j) x_j . (F B_j),  dcs_j = oc_j = exp(cs_j) dy_j . (E C_j)
+//     (the in-chunk kernel reads both and completes them),
+//   the block's chunk-end share (sum_j dt_j ob_j, plus exp(cs_last) <E, F> on the first
+//     block) and dD share (sum_j x_j . dy_j),
+// and after the last head the head sums in fp32, where the in-chunk kernel's dB and dC
+// accumulators start:
+//   dBs^T[n][j] = sum_h dt_j exp(cs_last - cs_j) sum_p F[p][n] x_j[p]
+//   dCs^T[n][j] = sum_h exp(cs_j) sum_p E[p][n] dy_j[p].
+// The two halves of n meet in LDS once per head: the upper half's (F B_j) partial tiles
+// and dy_j . (E C_j) column sums go to the lower half's waves, which finish and store.
+// E, F, cs and dt are copied into LDS straight from HBM, double-buffered over the heads;
+// x_j and dy_j (8 bytes per lane and p-tile) are loaded to registers one head ahead.
+template <int Q>
+struct CarryCfg {
+    static constexpr int N = 256, P = 64, NPR = N / 8, NJ = Q / 64;
+    static constexpr int PT = P / 16, HT = N / 32, HKB = N / 64;  // per half of n
+    static constexpr unsigned EB = P * N * 2;   // E or F, [p][n]
+    static constexpr unsigned FB = Q * 4;       // cs or dt
+    static constexpr unsigned ITEM = 2 * EB + 2 * FB;
+    static constexpr unsigned X_BM = 2 * ITEM;                // upper-half (F B_j), f32x4 [4][PT][64]
+    static constexpr unsigned X_OC = X_BM + 4 * PT * 64 * 16;  // upper-half oc sums [64]
+    static constexpr unsigned X_EF = X_OC + 64 * 4;            // <E, F> per wave [8]
+    static constexpr unsigned X_SH = X_EF + 8 * 4;             // lt, dd per wave [2][4][2]
+    static constexpr unsigned LDS = X_SH + 16 * 4;
+    static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+template <int Q>
+__global__ __launch_bounds__(512) void chunk_bwd_carried_kernel(
+    const __bf16* __restrict__ x, const __bf16* __restrict__ Bm, const __bf16* __restrict__ Cm,
+    const float* __restrict__ dtc, const float* __restrict__ cs,
+    const __bf16* __restrict__ entry, const __bf16* __restrict__ exitg,
+    const __bf16* __restrict__ dy, __bf16* __restrict__ xfb, float* __restrict__ dBs,
+    float* __restrict__ dCs, float* __restrict__ dcs, float* __restrict__ direct,
+    float* __restrict__ lt_part, float* __restrict__ dd_part, int T, int H, int G, int nC) {
+    using K_ = CarryCfg<Q>;
+    constexpr int N = K_::N, P = K_::P, NPR = K_::NPR, NJ = K_::NJ;
+    constexpr int PT = K_::PT, HT = K_::HT, HKB = K_::HKB;
+    extern __shared__ __align__(16) unsigned char smem[];
+    // the row blocks of a chunk, and neighbouring chunks, on the same XCD
+    const int nwg = gridDim.x, blk = blockIdx.x;
+    const int wp = (nwg % 8 == 0) ? (blk & 7) * (nwg >> 3) + (blk >> 3) : blk;
+    const int unit = wp / NJ, rj = wp % NJ;
+    const int c = unit % nC, g = (unit / nC) % G, b = unit / (nC * G);
+    const int j0 = 64 * rj, t0 = c * Q;
+    const int Lc = min(Q, T - t0);
+    if (j0 >= Lc) return;  // no valid row
+    const int hpg = H / G;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int cw = wave & 3, nh = wave >> 2;
+    const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int jl = j0 + 16 * cw + l16;
+    const bool vj = jl < Lc;
+    const uint32_t lds0 = lds_addr(smem);
+    float* const shr = reinterpret_cast<float*>(smem + K_::X_SH);
+
+    // one head's E, F (swizzled rows of 32 pieces), cs and dt into item buffer `buf`
+    auto issue = [&](int h, int buf) {
+        const uint32_t base = lds0 + (unsigned)buf * K_::ITEM;
+        const size_t so = ((size_t)(b * H + h) * nC + c) * P * N;
+        const u32x4 er = raw_rsrc(entry + so, K_::EB), fr = raw_rsrc(exitg + so, K_::EB);
+        issue_rows<NPR, 8>(er, N * 2, 0, base, 0, P, wave, lane);
+        issue_rows<NPR, 8>(fr, N * 2, 0, base + K_::EB, 0, P, wave, lane);
+        const size_t cb = ((size_t)(b * H + h) * nC + c) * Q;
+        if (wave == 0 && lane < Q / 4)
+            dma16(raw_rsrc(cs + cb, K_::FB), base + 2 * K_::EB, lane * 16u);
+        if (wave == 1 && lane < Q / 4)
+            dma16(raw_rsrc(dtc + cb, K_::FB), base + 2 * K_::EB + K_::FB, lane * 16u);
+    };
+    // x_j and dy_j at p = 16 pt + 4 g4 .. + 3 (zeros past the chunk's end)
+    auto load_rows = [&](int h, uint2 (&xq)[PT], uint2 (&yq)[PT]) {
+        const size_t o = ((size_t)(b * T + t0 + jl) * H + h) * P + 4 * g4;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            xq[pt] = vj ? *reinterpret_cast<const uint2*>(x + o + 16 * pt) : make_uint2(0u, 0u);
+            yq[pt] = vj ? *reinterpret_cast<const uint2*>(dy + o + 16 * pt) : make_uint2(0u, 0u);
+        }
+    };
+
+    // B_j, C_j over this wave's half of n (natural slots)
+    bf16x8 bj[HKB], cj[HKB];
+    {
+        const size_t ro = ((size_t)(b * T + t0 + jl) * G + g) * N + 128 * nh + 8 * g4;
+        const bf16x8 z = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
+#pragma unroll
+        for (int kb = 0; kb < HKB; ++kb) {
+            bj[kb] = vj ? *reinterpret_cast<const bf16x8*>(Bm + ro + 32 * kb) : z;
+            cj[kb] = vj ? *reinterpret_cast<const bf16x8*>(Cm + ro + 32 * kb) : z;
+        }
+    }
+    // lane parts of the LDS offsets: transposed E / F reads for the [n][j] products, natural
+    // reads for the [p][j] ones
+    unsigned ptn[HT], pnat[HKB];
+#pragma unroll
+    for (int nt = 0; nt < HT; ++nt)
+        ptn[nt] = lane_part(4 * g4 + (l16 >> 2), 128 * nh + 16 * nt + 4 * (l16 & 3), NPR);
+#pragma unroll
+    for (int kb = 0; kb < HKB; ++kb) pnat[kb] = lane_part(l16, 128 * nh + 32 * kb + 8 * g4, NPR);
+    constexpr unsigned N16 = 16u * NPR * 16u;  // 16 rows of E / F
+
+    f32x4 dbacc[HT], dcacc[HT];
+#pragma unroll
+    for (int nt = 0; nt < HT; ++nt) dbacc[nt] = dcacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint2 xq[PT], yq[PT];
+    load_rows(g * hpg, xq, yq);
+    issue(g * hpg, 0);
+#pragma unroll 1
+    for (int hh = 0; hh < hpg; ++hh) {
+        const int h = g * hpg + hh;
+        const int buf = hh & 1;
+        // this head's copies and rows have landed (the wait is visible to the compiler, so it
+        // adds none of its own for the rows); the previous head's exchange has been read
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        dma_barrier();
+        if (hh > 0 && wave == 0 && lane == 0) {
+            const float* sh = shr + (buf ^ 1) * 8;
+            const size_t pi = ((size_t)(b * H + h - 1) * nC + c) * NJ + rj;
+            lt_part[pi] = (sh[0] + sh[2]) + (sh[4] + sh[6]);
+            dd_part[pi] = (sh[1] + sh[3]) + (sh[5] + sh[7]);
+        }
+        uint2 xn[PT], yn[PT];
+        if (hh + 1 < hpg) {
+            load_rows(h + 1, xn, yn);
+            issue(h + 1, buf ^ 1);
+        }
+        const unsigned char* sE = smem + buf * K_::ITEM;
+        const unsigned char* sF = sE + K_::EB;
+        const float* s_cs = reinterpret_cast<const float*>(sF + K_::EB);
+        const float* s_dt = s_cs + Q;
+        const float cs_last = s_cs[Q - 1];
+        const float csj = vj ? s_cs[jl] : cs_last, dtj = vj ? s_dt[jl] : 0.f;
+        const float ej = exp2_fast(csj * kLog2e), fj = exp2_fast((cs_last - csj) * kLog2e);
+
+        // dC^T[n][j] += sum_p E[p][n] (exp(cs_j) dy_j[p]); dB^T[n][j] += sum_p F[p][n]
+        // (dt_j exp(cs_last - cs_j) x_j[p]); operands over p in the relabelled slots
+#pragma unroll
+        for (int kb = 0; kb < P / 32; ++kb) {
+            const bf16x8 y8 = __builtin_bit_cast(
+                bf16x8, make_uint4(yq[2 * kb].x, yq[2 * kb].y, yq[2 * kb + 1].x, yq[2 * kb + 1].y));
+            const bf16x8 x8 = __builtin_bit_cast(
+                bf16x8, make_uint4(xq[2 * kb].x, xq[2 * kb].y, xq[2 * kb + 1].x, xq[2 * kb + 1].y));
+            const bf16x8 ys8 = scale8(y8, ej), xs8 = scale8(x8, dtj * fj);
+#pragma unroll
+            for (int nt = 0; nt < HT; ++nt) {
+                dcacc[nt] = mfma16(ld_tr(rows_at(sE, 32 * kb, NPR), ptn[nt], N16), ys8, dcacc[nt]);
+                dbacc[nt] = mfma16(ld_tr(rows_at(sF, 32 * kb, NPR), ptn[nt], N16), xs8, dbacc[nt]);
+            }
+        }
+        // (F B_j)[p] and (E C_j)[p] over this half of n, as [p][j] tiles
+        f32x4 bfm[PT];
+        float ocp = 0.f;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            f32x4 cem = f32x4{0.f, 0.f, 0.f, 0.f};
+            bfm[pt] = cem;
+#pragma unroll
+            for (int kb = 0; kb < HKB; ++kb) {
+                bfm[pt] = mfma16(ld_nat(rows_at(sF, 16 * pt, NPR), pnat[kb]), bj[kb], bfm[pt]);
+                cem = mfma16(ld_nat(rows_at(sE, 16 * pt, NPR), pnat[kb]), cj[kb], cem);
+            }
+            ocp = fmaf(bf16_lo(yq[pt].x), cem[0], ocp);
+            ocp = fmaf(bf16_hi(yq[pt].x), cem[1], ocp);
+            ocp = fmaf(bf16_lo(yq[pt].y), cem[2], ocp);
+            ocp = fmaf(bf16_hi(yq[pt].y), cem[3], ocp);
+        }
+        ocp = colsum(ocp);
+        f32x4* xbm = reinterpret_cast<f32x4*>(smem + K_::X_BM) + cw * PT * 64 + lane;
+        float* xoc = reinterpret_cast<float*>(smem + K_::X_OC);
+        float* xef = reinterpret_cast<float*>(smem + K_::X_EF);
+        if (nh == 1) {
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) xbm[pt * 64] = bfm[pt];
+            if (g4 == 0) xoc[16 * cw + l16] = ocp;
+        }
+        if (j0 == 0) {  // <E, F>, an eighth per wave
+            float ef = 0.f;
+            for (int m = (int)threadIdx.x; m < P * NPR; m += 512)
+                ef += dot8(*reinterpret_cast<const bf16x8*>(sE + 16 * m),
+                           *reinterpret_cast<const bf16x8*>(sF + 16 * m));
+            ef = wavesum(ef);
+            if (lane == 0) xef[wave] = ef;
+        }
+        lds_barrier();
+        if (nh == 0) {
+            float ob = 0.f, dd = 0.f;
+            __bf16* xo = xfb + ((size_t)(b * T + t0 + jl) * H + h) * P + 4 * g4;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                bfm[pt] += xbm[pt * 64];
+                const uint2 xv = xq[pt], yv = yq[pt];
+                ob = fmaf(bf16_lo(xv.x), bfm[pt][0], ob);
+                ob = fmaf(bf16_hi(xv.x), bfm[pt][1], ob);
+                ob = fmaf(bf16_lo(xv.y), bfm[pt][2], ob);
+                ob = fmaf(bf16_hi(xv.y), bfm[pt][3], ob);
+                dd = fmaf(bf16_lo(xv.x), bf16_lo(yv.x), dd);
+                dd = fmaf(bf16_hi(xv.x), bf16_hi(yv.x), dd);
+                dd = fmaf(bf16_lo(xv.y), bf16_lo(yv.y), dd);
+                dd = fmaf(bf16_hi(xv.y), bf16_hi(yv.y), dd);
+                if (vj)
+                    *reinterpret_cast<uint2*>(xo + 16 * pt) =
+                        make_uint2(pack_bf16(bfm[pt][0], bfm[pt][1]),
+                                   pack_bf16(bfm[pt][2], bfm[pt][3]));
+            }
+            ob = colsum(ob) * fj;
+            const float oc = (ocp + xoc[16 * cw + l16]) * ej;
+            const size_t cb = ((size_t)(b * H + h) * nC + c) * Q;
+            if (g4 == 0 && vj) {
+                direct[cb + jl] = ob;
+                dcs[cb + jl] = oc;
+            }
+            float lt = (g4 == 0 && vj) ? dtj * ob : 0.f;
+            if (j0 == 0 && lane == 0)
+                lt = fmaf(exp2_fast(cs_last * kLog2e), xef[cw] + xef[cw + 4], lt);
+            lt = wavesum(lt);
+            dd = wavesum(dd);  // this wave's 16 rows of x_j . dy_j
+            if (lane == 0) {
+                shr[buf * 8 + 2 * cw] = lt;
+                shr[buf * 8 + 2 * cw + 1] = dd;
+            }
+        }
+        if (hh + 1 < hpg) {
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                xq[pt] = xn[pt];
+                yq[pt] = yn[pt];
+            }
+        }
+    }
+    dma_barrier();
+    if (wave == 0 && lane == 0) {
+        const float* sh = shr + ((hpg - 1) & 1) * 8;
+        const size_t pi = ((size_t)(b * H + g * hpg + hpg - 1) * nC + c) * NJ + rj;
+        lt_part[pi] = (sh[0] + sh[2]) + (sh[4] + sh[6]);
+        dd_part[pi] = (sh[1] + sh[3]) + (sh[5] + sh[7]);
+    }
+    if (vj) {
+        const size_t ro = ((size_t)(b * T + t0 + jl) * G + g) * N + 128 * nh + 4 * g4;
+#pragma unroll
+        for (int nt = 0; nt < HT; ++nt) {
+            *reinterpret_cast<f32x4*>(dBs + ro + 16 * nt) = dbacc[nt];
+            *reinterpret_cast<f32x4*>(dCs + ro + 16 * nt) = dcacc[nt];
+        }
     }
 }
 
 template <int Q, int N, int P>
 hipError_t launch_bwd_mfma_t(const Shape& s, const BwdArgs& a, hipStream_t st) {
     using C_ = BwdCfg<Q, N, P>;
+    const unsigned blocks = (unsigned)((size_t)s.B * s.G * s.nC * C_::NJ);
+    hipError_t e;
+    if constexpr (C_::EXT) {
+        if (!a.xfb || !a.dBs || !a.dCs) return hipErrorInvalidValue;
+        const auto ck = chunk_bwd_carried_kernel<Q>;
+        static DeviceSlots carried_set;
+        e = allow_lds((const void*)ck, CarryCfg<Q>::LDS, carried_set);
+        if (e != hipSuccess) return e;
+        ck<<<blocks, 512, CarryCfg<Q>::LDS, st>>>(
+            (const __bf16*)a.x, (const __bf16*)a.Bm, (const __bf16*)a.Cm, a.dtc, a.cs,
+            (const __bf16*)a.entry, (const __bf16*)a.exitg, (const __bf16*)a.dy, (__bf16*)a.xfb,
+            a.dBs, a.dCs, a.dcs, a.direct, a.lt_part, a.dd_part, s.T, s.H, s.G, s.nC);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const auto kern = chunk_bwd_mfma_kernel<Q, N, P>;
     static DeviceSlots attr_set;
-    const hipError_t e = allow_lds((const void*)kern, C_::LDS, attr_set);
+    e = allow_lds((const void*)kern, C_::LDS, attr_set);
     if (e != hipSuccess) return e;
-    const unsigned blocks = (unsigned)((size_t)s.B * s.G * s.nC * C_::NJ);
     kern<<<blocks, C_::NTH, C_::LDS, st>>>(
         (const __bf16*)a.x, (const __bf16*)a.Bm, (const __bf16*)a.Cm, a.dtc, a.cs, a.D,
         (const __bf16*)a.entry, (const __bf16*)a.exitg, (const __bf16*)a.dy, (__bf16*)a.dx,
-        (__bf16*)a.dB, (__bf16*)a.dC, a.dcs, a.direct, a.xs, a.lt_part, a.dd_part, s.T, s.H, s.G,
-        s.nC);
+        (__bf16*)a.dB, (__bf16*)a.dC, a.dcs, a.direct, a.xs, a.lt_part, a.dd_part,
+        (const __bf16*)a.xfb, a.dBs, a.dCs, s.T, s.H, s.G, s.nC);
     return hipGetLastError();
 }
 
@@ -848,6 +1290,7 @@ BwdFn pick_bwd_q(const Shape& s) {
     switch (s.N) {
         case 64: return launch_bwd_mfma_t<Q, 64, 64>;
         case 128: return launch_bwd_mfma_t<Q, 128, 64>;
+        case 256: return launch_bwd_mfma_t<Q, 256, 64>;
     }
     return nullptr;
 }
@@ -868,6 +1311,7 @@ BwdFn pick_bwd(const Shape& s) {
 }  // namespace
 
 bool chunk_bwd_mfma_supported(const Shape& s) { return pick_bwd(s) != nullptr; }
+bool chunk_bwd_mfma_carried(const Shape& s) { return s.N > 128 && pick_bwd(s) != nullptr; }
 int chunk_bwd_mfma_rows() { return 64; }
 
 hipError_t launch_chunk_bwd_mfma(const Shape& s, const BwdArgs& a, hipStream_t st) {

@@ -138,6 +138,8 @@ struct BwdWorkspace {
     float *dtc, *cs;
     void *states, *entry, *exitg;
     float *dcs, *direct, *xs, *lt_part, *dd_part, *dA_part;
+    void* xfb;            // the carried-state terms at dstate 256 (null otherwise)
+    float *dBs, *dCs;
 };
 
 size_t bwd_workspace_bytes(const Shape& s, BwdWorkspace* w, char* base) {
@@ -162,6 +164,14 @@ size_t bwd_workspace_bytes(const Shape& s, BwdWorkspace* w, char* base) {
     ws.lt_part = take(tile_elems * sizeof(float));
     ws.dd_part = take(tile_elems * sizeof(float));
     ws.dA_part = take((size_t)s.B * s.H * s.nC * sizeof(float));
+    ws.xfb = nullptr;
+    ws.dBs = ws.dCs = nullptr;
+    if (ssd::chunk_bwd_mfma_carried(s)) {  // sized by shape: the dtype is not known here
+        const size_t tokens = (size_t)s.B * s.T;
+        ws.xfb = take(tokens * s.H * s.P * 2);
+        ws.dBs = take(tokens * s.G * s.N * sizeof(float));
+        ws.dCs = take(tokens * s.G * s.N * sizeof(float));
+    }
     if (w) *w = ws;
     return off;
 }
@@ -465,6 +475,7 @@ ssd_status bwd_impl(const ssd_dims* dims, ssd_dtype dtype, const void* x, const 
     a.ddt = ddt; a.dA = dA; a.dD = dD;
     a.dcs = ws.dcs; a.direct = ws.direct;
     a.lt_part = ws.lt_part; a.dd_part = ws.dd_part; a.dA_part = ws.dA_part;
+    a.xfb = ws.xfb; a.dBs = ws.dBs; a.dCs = ws.dCs;
     const bool mfma_bwd = dtype == SSD_BF16 && ssd::chunk_bwd_mfma_supported(s);
     a.xs = mfma_bwd ? ws.xs : nullptr;
     const int rows = mfma_bwd ? ssd::chunk_bwd_mfma_rows() : ssd::chunk_bwd_valu_rows();

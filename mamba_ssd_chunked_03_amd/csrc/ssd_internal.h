@@ -163,12 +163,19 @@ struct BwdArgs {
     float* xs;
     float *lt_part, *dd_part;              // [B][H][nC][Q / rows]: per row tile
     float* dA_part;                        // [B][H][nC]
+    // MFMA path at dstate 256 only (null otherwise): the terms through the carried states,
+    // formed by a kernel of their own before the in-chunk one -- (F B_j) per step and head
+    // ([B][T][H][P], bf16) and the head sums of the dB, dC terms ([B][T][G][N], fp32)
+    void* xfb;
+    float *dBs, *dCs;
 };
 int chunk_bwd_valu_rows();
 hipError_t launch_chunk_bwd_valu(const Shape& s, ssd_dtype dtype, const BwdArgs& a,
                                  hipStream_t st);
-// bf16 MFMA in-chunk backward (headdim 64, dstate 64 or 128), same outputs; rows per tile 64
+// bf16 MFMA in-chunk backward (headdim 64, dstate 64, 128 or 256), same outputs; rows per
+// tile 64.  At dstate 256 it also needs BwdArgs' xfb, dBs and dCs (chunk_bwd_mfma_carried).
 bool chunk_bwd_mfma_supported(const Shape& s);
+bool chunk_bwd_mfma_carried(const Shape& s);
 int chunk_bwd_mfma_rows();
 hipError_t launch_chunk_bwd_mfma(const Shape& s, const BwdArgs& a, hipStream_t st);
 // ddt and dA, dD from the per-chunk and per-tile shares (rows: rows per tile)

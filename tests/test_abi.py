@@ -199,6 +199,17 @@ def test_bwd_workspace_size(lib):
     # per-tile shares and dA's per-chunk share
     assert binding.ssd_bwd_workspace_size(d, 256) == \
         4 * chunk + 3 * state + (256 // 64) * chunk + 2 * tiles + per_chunk
+    # dstate 256 (headdim 64): the carried-state terms of the matrix-core path as well, (F B_j)
+    # per step and head in bf16 and the dB, dC head sums in fp32
+    d = D(2, 8192, 32, 64, 256, 1)
+    nC = 32
+    chunk = 2 * 32 * nC * 256 * 4
+    state = 2 * 32 * nC * 64 * 256 * 4
+    tiles = 2 * 32 * nC * (256 // 16) * 4
+    per_chunk = 2 * 32 * nC * 4
+    carried = 2 * 8192 * 32 * 64 * 2 + 2 * (2 * 8192 * 1 * 256 * 4)
+    assert binding.ssd_bwd_workspace_size(d, 256) == \
+        4 * chunk + 3 * state + (256 // 64) * chunk + 2 * tiles + per_chunk + carried
     assert binding.ssd_bwd_workspace_size(D(h=3, g=2), 64) == 0
     assert binding.ssd_bwd_workspace_size(D(t=0), 64) == 0
 

@@ -94,8 +94,15 @@ CASES = [
     Workload("bwd_g2_q256", 1, 700, 4, 64, 128, 2, 256, init_state=True,
              log_neg_a_range=(np.log(0.005), np.log(0.05))),
     # N = 256: the recomputed states and the state gradients run the pipelined states
-    # kernel with B (C) in two column slices, two items per workgroup across units
+    # kernel with B (C) in two column slices, two items per workgroup across units; the
+    # in-chunk part runs the carried-state kernel and then the in-chunk kernel
     Workload("bwd_n256_pipe", 2, 8192, 8, 64, 256, 2, 256, init_state=True,
+             log_neg_a_range=(np.log(0.005), np.log(0.05))),
+    # N = 256 at the other chunk lengths, each with a ragged last chunk (44 and 60 rows:
+    # row blocks past the end, and a block cut inside)
+    Workload("bwd_n256_q64", 1, 300, 4, 64, 256, 2, 64, init_state=True,
+             log_neg_a_range=(np.log(0.01), np.log(0.1))),
+    Workload("bwd_n256_q128", 2, 700, 6, 64, 256, 3, 128, init_state=True,
              log_neg_a_range=(np.log(0.005), np.log(0.05))),
 ]
 
@@ -150,9 +157,9 @@ def test_bwd_is_deterministic():
                                   "nsweep_n256", "long_ctx_65k"])
 def test_bwd_full_size_workloads(name):
     """The model-shaped backward workloads at full size, with the launch configuration that
-    bench.py --bwd times (bf16, Q = 256; the MFMA in-chunk kernel, and at N = 256 the fp32
-    VALU one), compared whole-tensor with the oracle's reverse-mode pass over every (b, h)
-    sequence.  long_ctx_65k adds eight groups of ten heads, an initial state and 256
+    bench.py --bwd times (bf16, Q = 256; the MFMA in-chunk kernel, preceded at N = 256 by
+    the carried-state kernel), compared with the oracle's reverse-mode pass over every
+    (b, h) sequence.  long_ctx_65k adds eight groups of ten heads, an initial state and 256
     chunks per sequence."""
     w = WORKLOADS[name]
     say(f"[bwd full] {w.describe()}")
@@ -162,8 +169,8 @@ def test_bwd_full_size_workloads(name):
     compare(w, g, oracle_bwd(cpu, up))
 
 
-@pytest.mark.parametrize("w", [STRESS["slow_decay"], CASES[0], CASES[-1]],
-                         ids=["slow_decay", "tiny_fp32", "bwd_g2_q256"])
+@pytest.mark.parametrize("w", [STRESS["slow_decay"], CASES[0], CASES[-4], CASES[-1]],
+                         ids=["slow_decay", "tiny_fp32", "bwd_g2_q256", "bwd_n256_q128"])
 def test_bwd_saved_equals_recompute(w):
     """ssd_bwd_saved (the forward's intermediates read from its workspace) gives the same
     bits as ssd_bwd (which recomputes them)."""
