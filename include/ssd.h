@@ -290,7 +290,10 @@ ssd_status ssd_decode_step(const ssd_dims* dims, ssd_dtype dtype, const void* x,
  * which makes every decay across a start exactly zero in fp32.  The gaps cost some
  * precision inside a chunk that holds several starts: with k starts in one chunk the
  * log-decays reach about -(120 k + 254), and each decay carries a relative error of
- * about ulp(120 k + 254), e.g. 6e-5 for k = 3. */
+ * about ulp(120 k + 254), e.g. 6e-5 for k = 3.  Measured with about 100 starts per chunk
+ * (sequences of 1-4 steps), rel-L2 against the fp64 oracle: in fp32 1.8e-5 on y and
+ * 2.5e-4 on the final states (above ssd_fwd's fp32 bound of 1e-4: this is that limit); in
+ * bf16 1.7e-3, within ssd_fwd's bf16 bound. */
 
 /* Bytes of workspace ssd_fwd_varlen needs: ssd_fwd's for these sizes (0 if the sizes are
  * invalid or batch != 1). */
