@@ -626,12 +626,14 @@ __device__ __forceinline__ void bwd_strip_role(
                                 pack_bf16(wacc[2 * k + 1][0], wacc[2 * k + 1][1]),
                                 pack_bf16(wacc[2 * k + 1][2], wacc[2 * k + 1][3]));
     dma_barrier();
-    // the other halves of n: the state waves have read the previous half's rows
+    if constexpr (C_::EXT) {
+        // the other halves of n: the state waves have read the previous half's rows
 #pragma unroll 1
-    for (int part = 1; part < C_::NHP; ++part) {
-        lds_barrier();
-        issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, true, k_.lds0, wave, lane, part);
-        dma_barrier();
+        for (int part = 1; part < C_::NHP; ++part) {
+            lds_barrier();
+            issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, true, k_.lds0, wave, lane, part);
+            dma_barrier();
+        }
     }
 }
 
@@ -892,14 +894,8 @@ __device__ __forceinline__ void bwd_state_role_ext(
     for (int nt = 0; nt < HT; ++nt)
         ptn[nt] = lane_part(4 * g4 + (l16 >> 2), 16 * nt + 4 * (l16 & 3), HPR);
     constexpr unsigned N16 = 16u * HPR * 16u;
-#pragma unroll 1
-    for (int part = 0; part < C_::NHP; ++part) {
-        if (part > 0) {
-            lds_barrier();
-            issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, true, k_.lds0, wave, lane, part);
-            dma_barrier();
-        }
-        // dB^T, dC^T [n][j] for n in this half, from the carried-state sums
+    // dB^T, dC^T [n][j] for n in one half, from the carried-state sums
+    auto finish_half = [&](int part) {
         const size_t ro = ((size_t)(b * T + t0 + jl) * G + g) * N + part * HN + 4 * g4;
         f32x4 dbacc[HT], dcacc[HT];
 #pragma unroll
@@ -933,6 +929,15 @@ __device__ __forceinline__ void bwd_state_role_ext(
                     pack_bf16(dcacc[nt][0], dcacc[nt][1]), pack_bf16(dcacc[nt][2], dcacc[nt][3]));
             }
         }
+    };
+    finish_half(0);
+    // the other halves of n: every state wave has read the previous half's rows
+#pragma unroll 1
+    for (int part = 1; part < C_::NHP; ++part) {
+        lds_barrier();
+        issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, true, k_.lds0, wave, lane, part);
+        dma_barrier();
+        finish_half(part);
     }
 }
 
@@ -1009,16 +1014,18 @@ __global__ __launch_bounds__(512) void chunk_bwd_mfma_kernel(
 //   xfb[j][p] = (F B_j)[p] rounded to bf16 (the in-chunk kernel's operand for dx),
 //   direct_j = ob_j = exp(cs_last - cs_j) x_j . (F B_j),  dcs_j = oc_j = exp(cs_j) dy_j . (E C_j)
 //     (the in-chunk kernel reads both and completes them),
-//   the block's chunk-end share (sum_j dt_j ob_j, plus exp(cs_last) <E, F> on the first
-//     block) and dD share (sum_j x_j . dy_j),
+//   the block's chunk-end share (sum_j dt_j ob_j, plus its share of exp(cs_last) <E, F>) and
+//     dD share (sum_j x_j . dy_j),
 // and after the last head the head sums in fp32, where the in-chunk kernel's dB and dC
 // accumulators start:
 //   dBs^T[n][j] = sum_h dt_j exp(cs_last - cs_j) sum_p F[p][n] x_j[p]
 //   dCs^T[n][j] = sum_h exp(cs_j) sum_p E[p][n] dy_j[p].
-// The two halves of n meet in LDS once per head: the upper half's (F B_j) partial tiles
-// and dy_j . (E C_j) column sums go to the lower half's waves, which finish and store.
-// E, F, cs and dt are copied into LDS straight from HBM, double-buffered over the heads;
-// x_j and dy_j (8 bytes per lane and p-tile) are loaded to registers one head ahead.
+// The two halves of n meet in LDS once per head and share the finishing: each half hands
+// the other the two p-tiles of its (F B_j) partial that the other finishes, and one of its
+// two column sums; the lower half then finishes p-tiles 0-1 and ob, the upper half p-tiles
+// 2-3 and oc.  E, F, cs and dt are copied into LDS straight from HBM, double-buffered over
+// the heads, the next head's E and F copies spread through this head's products; x_j and
+// dy_j (8 bytes per lane and p-tile) are loaded to registers one head ahead.
 template <int Q>
 struct CarryCfg {
     static constexpr int N = 256, P = 64, NPR = N / 8, NJ = Q / 64;
@@ -1026,12 +1033,13 @@ struct CarryCfg {
     static constexpr unsigned EB = P * N * 2;   // E or F, [p][n]
     static constexpr unsigned FB = Q * 4;       // cs or dt
     static constexpr unsigned ITEM = 2 * EB + 2 * FB;
-    static constexpr unsigned X_BM = 2 * ITEM;                // upper-half (F B_j), f32x4 [4][PT][64]
-    static constexpr unsigned X_OC = X_BM + 4 * PT * 64 * 16;  // upper-half oc sums [64]
-    static constexpr unsigned X_EF = X_OC + 64 * 4;            // <E, F> per wave [8]
-    static constexpr unsigned X_SH = X_EF + 8 * 4;             // lt, dd per wave [2][4][2]
+    static constexpr int NCI = P * NPR / 64 / 8;                // E (or F) copies per wave: 4
+    static constexpr unsigned X_BM = 2 * ITEM;                 // (F B_j) tiles for the other half, f32x4 [8][2][64]
+    static constexpr unsigned X_CS = X_BM + 8 * 2 * 64 * 16;   // column sums for the other half [2][64]
+    static constexpr unsigned X_EF = X_CS + 2 * 64 * 4;        // <E, F> shares per wave [8]
+    static constexpr unsigned X_SH = X_EF + 8 * 4;             // lt (lower), dd (upper) per wave [2][4][2]
     static constexpr unsigned LDS = X_SH + 16 * 4;
-    static_assert(LDS <= 160 * 1024, "LDS");
+    static_assert(NCI * 8 * 64 == P * NPR && LDS <= 160 * 1024, "layout");
 };
 
 template <int Q>
@@ -1044,7 +1052,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_carried_kernel(
     float* __restrict__ lt_part, float* __restrict__ dd_part, int T, int H, int G, int nC) {
     using K_ = CarryCfg<Q>;
     constexpr int N = K_::N, P = K_::P, NPR = K_::NPR, NJ = K_::NJ;
-    constexpr int PT = K_::PT, HT = K_::HT, HKB = K_::HKB;
+    constexpr int PT = K_::PT, HT = K_::HT, HKB = K_::HKB, NCI = K_::NCI;
     extern __shared__ __align__(16) unsigned char smem[];
     // the row blocks of a chunk, and neighbouring chunks, on the same XCD
     const int nwg = gridDim.x, blk = blockIdx.x;
@@ -1054,6 +1062,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_carried_kernel(
     const int j0 = 64 * rj, t0 = c * Q;
     const int Lc = min(Q, T - t0);
     if (j0 >= Lc) return;  // no valid row
+    const int nvb = (Lc + 63) / 64;  // row blocks with a valid row: they share <E, F>
     const int hpg = H / G;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int cw = wave & 3, nh = wave >> 2;
@@ -1063,18 +1072,27 @@ __global__ __launch_bounds__(512) void chunk_bwd_carried_kernel(
     const uint32_t lds0 = lds_addr(smem);
     float* const shr = reinterpret_cast<float*>(smem + K_::X_SH);
 
-    // one head's E, F (swizzled rows of 32 pieces), cs and dt into item buffer `buf`
-    auto issue = [&](int h, int buf) {
-        const uint32_t base = lds0 + (unsigned)buf * K_::ITEM;
-        const size_t so = ((size_t)(b * H + h) * nC + c) * P * N;
-        const u32x4 er = raw_rsrc(entry + so, K_::EB), fr = raw_rsrc(exitg + so, K_::EB);
-        issue_rows<NPR, 8>(er, N * 2, 0, base, 0, P, wave, lane);
-        issue_rows<NPR, 8>(fr, N * 2, 0, base + K_::EB, 0, P, wave, lane);
+    // one head's cs and dt into item buffer `buf` (waves 0 and 1)
+    auto issue_steps = [&](int h, int buf) {
+        const uint32_t base = lds0 + (unsigned)buf * K_::ITEM + 2 * K_::EB;
         const size_t cb = ((size_t)(b * H + h) * nC + c) * Q;
-        if (wave == 0 && lane < Q / 4)
-            dma16(raw_rsrc(cs + cb, K_::FB), base + 2 * K_::EB, lane * 16u);
-        if (wave == 1 && lane < Q / 4)
-            dma16(raw_rsrc(dtc + cb, K_::FB), base + 2 * K_::EB + K_::FB, lane * 16u);
+        if (wave == 0 && lane < Q / 4) dma16(raw_rsrc(cs + cb, K_::FB), base, lane * 16u);
+        if (wave == 1 && lane < Q / 4) dma16(raw_rsrc(dtc + cb, K_::FB), base + K_::FB, lane * 16u);
+    };
+    // copy k (0 .. 2 NCI - 1) of this wave's share of one head's E (k < NCI) and F: 64
+    // pieces of 16 bytes at LDS slots 64 (wave + 8 i) .., rows of 32 pieces swizzled as
+    // issue_rows writes them
+    auto issue_ef = [&](const u32x4& er, const u32x4& fr, int buf, int k) {
+        const int i = k % NCI, inst = wave + 8 * i;
+        const int m = inst * 64 + lane, r = m / NPR, sl = m % NPR;
+        const uint32_t dst = lds0 + (unsigned)buf * K_::ITEM + (k < NCI ? 0u : K_::EB) +
+                             (unsigned)inst * 1024u;
+        dma16(k < NCI ? er : fr, dst, (unsigned)r * (N * 2u) + (unsigned)(sl ^ (r & 15)) * 16u);
+    };
+    auto ef_rsrc = [&](int h, u32x4& er, u32x4& fr) {
+        const size_t so = ((size_t)(b * H + h) * nC + c) * P * N;
+        er = raw_rsrc(entry + so, K_::EB);
+        fr = raw_rsrc(exitg + so, K_::EB);
     };
     // x_j and dy_j at p = 16 pt + 4 g4 .. + 3 (zeros past the chunk's end)
     auto load_rows = [&](int h, uint2 (&xq)[PT], uint2 (&yq)[PT]) {
@@ -1112,11 +1130,18 @@ __global__ __launch_bounds__(512) void chunk_bwd_carried_kernel(
     for (int nt = 0; nt < HT; ++nt) dbacc[nt] = dcacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     uint2 xq[PT], yq[PT];
     load_rows(g * hpg, xq, yq);
-    issue(g * hpg, 0);
+    {
+        u32x4 er, fr;
+        ef_rsrc(g * hpg, er, fr);
+#pragma unroll
+        for (int k = 0; k < 2 * NCI; ++k) issue_ef(er, fr, 0, k);
+        issue_steps(g * hpg, 0);
+    }
 #pragma unroll 1
     for (int hh = 0; hh < hpg; ++hh) {
         const int h = g * hpg + hh;
         const int buf = hh & 1;
+        const bool more = hh + 1 < hpg;
         // this head's copies and rows have landed (the wait is visible to the compiler, so it
         // adds none of its own for the rows); the previous head's exchange has been read
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -1128,9 +1153,11 @@ __global__ __launch_bounds__(512) void chunk_bwd_carried_kernel(
             dd_part[pi] = (sh[1] + sh[3]) + (sh[5] + sh[7]);
         }
         uint2 xn[PT], yn[PT];
-        if (hh + 1 < hpg) {
+        u32x4 er, fr;
+        if (more) {
             load_rows(h + 1, xn, yn);
-            issue(h + 1, buf ^ 1);
+            ef_rsrc(h + 1, er, fr);
+            issue_steps(h + 1, buf ^ 1);
         }
         const unsigned char* sE = smem + buf * K_::ITEM;
         const unsigned char* sF = sE + K_::EB;
@@ -1141,7 +1168,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_carried_kernel(
         const float ej = exp2_fast(csj * kLog2e), fj = exp2_fast((cs_last - csj) * kLog2e);
 
         // dC^T[n][j] += sum_p E[p][n] (exp(cs_j) dy_j[p]); dB^T[n][j] += sum_p F[p][n]
-        // (dt_j exp(cs_last - cs_j) x_j[p]); operands over p in the relabelled slots
+        // (dt_j exp(cs_last - cs_j) x_j[p]); operands over p in the relabelled slots.  The
+        // next head's E and F copies are issued between the products, one per two tiles.
 #pragma unroll
         for (int kb = 0; kb < P / 32; ++kb) {
             const bf16x8 y8 = __builtin_bit_cast(
@@ -1153,11 +1181,13 @@ __global__ __launch_bounds__(512) void chunk_bwd_carried_kernel(
             for (int nt = 0; nt < HT; ++nt) {
                 dcacc[nt] = mfma16(ld_tr(rows_at(sE, 32 * kb, NPR), ptn[nt], N16), ys8, dcacc[nt]);
                 dbacc[nt] = mfma16(ld_tr(rows_at(sF, 32 * kb, NPR), ptn[nt], N16), xs8, dbacc[nt]);
+                if ((nt & 1) && more) issue_ef(er, fr, buf ^ 1, kb * (HT / 2) + nt / 2);
             }
         }
-        // (F B_j)[p] and (E C_j)[p] over this half of n, as [p][j] tiles
+        // (F B_j)[p] and (E C_j)[p] over this half of n, as [p][j] tiles; this half's parts
+        // of ob, oc (before their decays) and, in the upper half, x_j . dy_j
         f32x4 bfm[PT];
-        float ocp = 0.f;
+        float obp = 0.f, ocp = 0.f, dd = 0.f;
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
             f32x4 cem = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1167,67 +1197,64 @@ __global__ __launch_bounds__(512) void chunk_bwd_carried_kernel(
                 bfm[pt] = mfma16(ld_nat(rows_at(sF, 16 * pt, NPR), pnat[kb]), bj[kb], bfm[pt]);
                 cem = mfma16(ld_nat(rows_at(sE, 16 * pt, NPR), pnat[kb]), cj[kb], cem);
             }
-            ocp = fmaf(bf16_lo(yq[pt].x), cem[0], ocp);
-            ocp = fmaf(bf16_hi(yq[pt].x), cem[1], ocp);
-            ocp = fmaf(bf16_lo(yq[pt].y), cem[2], ocp);
-            ocp = fmaf(bf16_hi(yq[pt].y), cem[3], ocp);
-        }
-        ocp = colsum(ocp);
-        f32x4* xbm = reinterpret_cast<f32x4*>(smem + K_::X_BM) + cw * PT * 64 + lane;
-        float* xoc = reinterpret_cast<float*>(smem + K_::X_OC);
-        float* xef = reinterpret_cast<float*>(smem + K_::X_EF);
-        if (nh == 1) {
+            const uint2 xv = xq[pt], yv = yq[pt];
+            const float xs[4] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y)};
+            const float ys[4] = {bf16_lo(yv.x), bf16_hi(yv.x), bf16_lo(yv.y), bf16_hi(yv.y)};
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) xbm[pt * 64] = bfm[pt];
-            if (g4 == 0) xoc[16 * cw + l16] = ocp;
+            for (int q = 0; q < 4; ++q) {
+                obp = fmaf(xs[q], bfm[pt][q], obp);
+                ocp = fmaf(ys[q], cem[q], ocp);
+                if (nh == 1) dd = fmaf(xs[q], ys[q], dd);
+            }
         }
-        if (j0 == 0) {  // <E, F>, an eighth per wave
+        obp = colsum(obp);
+        ocp = colsum(ocp);
+        // hand the other half its two p-tiles and column sum (the lower half finishes
+        // p-tiles 0-1 and ob, the upper half p-tiles 2-3 and oc)
+        f32x4* xbm = reinterpret_cast<f32x4*>(smem + K_::X_BM);
+        float* xcs = reinterpret_cast<float*>(smem + K_::X_CS);
+        float* xef = reinterpret_cast<float*>(smem + K_::X_EF);
+        const int give = 2 * (1 - nh);
+        xbm[(wave * 2) * 64 + lane] = bfm[give];
+        xbm[(wave * 2 + 1) * 64 + lane] = bfm[give + 1];
+        if (g4 == 0) xcs[64 * nh + 16 * cw + l16] = nh == 0 ? ocp : obp;
+        // <E, F>: the valid row blocks of the chunk take a share each, an eighth per wave
+        {
             float ef = 0.f;
-            for (int m = (int)threadIdx.x; m < P * NPR; m += 512)
+            for (int m = rj * 512 + (int)threadIdx.x; m < P * NPR; m += 512 * nvb)
                 ef += dot8(*reinterpret_cast<const bf16x8*>(sE + 16 * m),
                            *reinterpret_cast<const bf16x8*>(sF + 16 * m));
             ef = wavesum(ef);
             if (lane == 0) xef[wave] = ef;
         }
         lds_barrier();
-        if (nh == 0) {
-            float ob = 0.f, dd = 0.f;
+        {
+            const int other = wave ^ 4, own = 2 * nh;
             __bf16* xo = xfb + ((size_t)(b * T + t0 + jl) * H + h) * P + 4 * g4;
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                bfm[pt] += xbm[pt * 64];
-                const uint2 xv = xq[pt], yv = yq[pt];
-                ob = fmaf(bf16_lo(xv.x), bfm[pt][0], ob);
-                ob = fmaf(bf16_hi(xv.x), bfm[pt][1], ob);
-                ob = fmaf(bf16_lo(xv.y), bfm[pt][2], ob);
-                ob = fmaf(bf16_hi(xv.y), bfm[pt][3], ob);
-                dd = fmaf(bf16_lo(xv.x), bf16_lo(yv.x), dd);
-                dd = fmaf(bf16_hi(xv.x), bf16_hi(yv.x), dd);
-                dd = fmaf(bf16_lo(xv.y), bf16_lo(yv.y), dd);
-                dd = fmaf(bf16_hi(xv.y), bf16_hi(yv.y), dd);
+            for (int u = 0; u < 2; ++u) {
+                const f32x4 v = bfm[own + u] + xbm[(other * 2 + u) * 64 + lane];
                 if (vj)
-                    *reinterpret_cast<uint2*>(xo + 16 * pt) =
-                        make_uint2(pack_bf16(bfm[pt][0], bfm[pt][1]),
-                                   pack_bf16(bfm[pt][2], bfm[pt][3]));
+                    *reinterpret_cast<uint2*>(xo + 16 * (own + u)) =
+                        make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
             }
-            ob = colsum(ob) * fj;
-            const float oc = (ocp + xoc[16 * cw + l16]) * ej;
             const size_t cb = ((size_t)(b * H + h) * nC + c) * Q;
-            if (g4 == 0 && vj) {
-                direct[cb + jl] = ob;
-                dcs[cb + jl] = oc;
+            float share;
+            if (nh == 0) {
+                const float ob = (obp + xcs[64 + 16 * cw + l16]) * fj;
+                if (g4 == 0 && vj) direct[cb + jl] = ob;
+                share = (g4 == 0 && vj) ? dtj * ob : 0.f;
+                if (lane == 0)
+                    share = fmaf(exp2_fast(cs_last * kLog2e), xef[cw] + xef[cw + 4], share);
+            } else {
+                const float oc = (ocp + xcs[16 * cw + l16]) * ej;
+                if (g4 == 0 && vj) dcs[cb + jl] = oc;
+                share = dd;  // this wave's 16 rows of x_j . dy_j
             }
-            float lt = (g4 == 0 && vj) ? dtj * ob : 0.f;
-            if (j0 == 0 && lane == 0)
-                lt = fmaf(exp2_fast(cs_last * kLog2e), xef[cw] + xef[cw + 4], lt);
-            lt = wavesum(lt);
-            dd = wavesum(dd);  // this wave's 16 rows of x_j . dy_j
-            if (lane == 0) {
-                shr[buf * 8 + 2 * cw] = lt;
-                shr[buf * 8 + 2 * cw + 1] = dd;
-            }
+            share = wavesum(share);
+            if (lane == 0) shr[buf * 8 + 2 * cw + nh] = share;
         }
-        if (hh + 1 < hpg) {
+        if (more) {
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
                 xq[pt] = xn[pt];
