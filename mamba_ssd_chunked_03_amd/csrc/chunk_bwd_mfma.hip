@@ -1,5 +1,5 @@
-// chunk_bwd_mfma.hip -- the in-chunk backward on gfx950 bf16 MFMA (headdim 64, dstate 64 or
-// 128, any supported chunk length).
+// chunk_bwd_mfma.hip -- the in-chunk backward on gfx950 bf16 MFMA (headdim 64 with dstate 64,
+// 128 or 256, headdim 32 with dstate 32, 64 or 128; any supported chunk length).
 //
 // It computes what chunk_bwd_valu.hip computes (the formulas are stated there): dx, the
 // head-summed dB and dC, and per head the explicit step-size gradient and dL/dcs.
@@ -150,29 +150,37 @@ struct BwdCfg {
     // and in two halves of n for the W products, and the state waves' dB, dC accumulators
     // start from that kernel's sums
     static constexpr bool EXT = N > 128;
-    static constexpr int SLN = EXT ? 64 : N;        // columns of B / C per C B^T slice
-    static constexpr int NSL = N / SLN;
     static constexpr int HN = EXT ? 128 : N;        // columns of B / C per W-product pass
     static constexpr int NHP = N / HN;
     static constexpr unsigned XYB = (Q + 64) * P * 2;  // x rows [0, j0+64), dy rows [j0, Q)
     static constexpr unsigned EB = EXT ? 0 : P * N * 2;  // E or F, [p][n]
     static constexpr unsigned FB = Q * 4;              // cs or dt
     static constexpr unsigned ITEM = XYB + 2 * EB + 2 * FB;
+    // columns of B / C per C B^T slice: whole chunks where both fit the two item buffers
+    // (all of n for headdim 64 below dstate 256)
+    static constexpr int SLN = EXT ? 64
+                               : 2u * Q * N * 2 <= 2 * ITEM ? N
+                               : 2u * Q * 64 * 2 <= 2 * ITEM ? 64 : 32;
+    static constexpr bool SLICED = SLN < N;
+    static constexpr int NSL = N / SLN;
     static constexpr unsigned BCB = Q * SLN * 2;       // one B or C chunk (slice)
     // exchange from the state waves to the strip waves, after the two item buffers
     static constexpr unsigned X_BF = 2 * ITEM;                // (F B_j) tiles, bf16 [4][PT][64]
     static constexpr unsigned X_OB = X_BF + 4 * PT * 64 * 8;  // ob, oc per column [2][64]
     static constexpr unsigned X_EF = X_OB + 2 * 64 * 4;       // <E, F> share per wave [4]
     static constexpr unsigned X_SH = X_EF + 16;               // workgroup shares [2][4][2]
-    // the W accumulators (bf16) travel from the strip waves after the B/C rows at the end
-    // (past the exchange area where those rows are a half of n)
-    static constexpr unsigned X_W =
-        EXT ? ((Q + 64) * HN * 2 > X_SH + 64 ? (Q + 64) * HN * 2 : X_SH + 64) : (Q + 64) * N * 2;
+    // the W accumulators (bf16) travel from the strip waves after the B/C rows at the end:
+    // inside the item buffers where they fit, else past the exchange area
     static constexpr unsigned WB = 4u * PAIRS * 64 * 16;
-    static constexpr unsigned LDS = EXT ? X_W + WB : X_SH + 64;
-    static_assert(P == 64 && (N == 64 || N == 128 || N == 256), "shape");
+    static constexpr bool W_IN_ITEMS = !EXT && (Q + 64) * N * 2 + WB <= 2 * ITEM;
+    static constexpr unsigned X_W =
+        W_IN_ITEMS ? (Q + 64) * N * 2
+                   : ((Q + 64) * HN * 2 > X_SH + 64 ? (Q + 64) * HN * 2 : X_SH + 64);
+    static constexpr unsigned LDS = W_IN_ITEMS ? X_SH + 64 : X_W + WB;
+    static_assert((P == 64 && (N == 64 || N == 128 || N == 256)) ||
+                      (P == 32 && (N == 32 || N == 64 || N == 128)),
+                  "shape");
     static_assert(2 * BCB <= 2 * ITEM, "B and C chunks fit the item buffers");
-    static_assert(EXT || X_W + WB <= 2 * ITEM, "end-of-loop staging fits");
     static_assert(X_W % 16 == 0 && LDS <= 160 * 1024, "LDS");
 };
 
@@ -299,7 +307,7 @@ __device__ __forceinline__ void bwd_strip_role(
 
     // C B^T on the strips, rounded to bf16: G^T[i][j] = B_i . C_j and G[t][j] = C_t . B_j
     uint2 gt[2 * PAIRS];
-    if constexpr (C_::EXT) {
+    if constexpr (C_::SLICED) {
         // summed in fp32 over column slices of B and C
         constexpr int SPR = C_::SLN / 8, SKB = C_::SLN / 32;
         const int l16 = lane & 15, g4 = lane >> 4;
@@ -653,10 +661,25 @@ __device__ __forceinline__ void bwd_state_role(
     const int wave = k_.wave, cw = k_.cw, lane = k_.lane;
     const int rsp = (j0 + 64) / 32;  // row-strip blocks (rows 32 k), then column-strip blocks
 
-    issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, false, k_.lds0, wave, lane);
-    dma_barrier();
     bf16x8 bj[NKB], cj[NKB];  // B_j, C_j over n (natural slots)
-    {
+    if constexpr (C_::SLICED) {  // the strip waves' C B^T slices, this wave's B_j, C_j parts
+        constexpr int SPR = C_::SLN / 8, SKB = C_::SLN / 32;
+        const int l16 = lane & 15, g4 = lane >> 4;
+        const int jl = j0 + 16 * cw + l16;
+#pragma unroll
+        for (int sl = 0; sl < C_::NSL; ++sl) {
+            issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, false, k_.lds0, wave, lane, sl);
+            dma_barrier();
+#pragma unroll
+            for (int kb = 0; kb < SKB; ++kb) {
+                bj[sl * SKB + kb] = frag_nat(smem, jl, kb, g4, SPR);
+                cj[sl * SKB + kb] = frag_nat(smem + C_::BCB, jl, kb, g4, SPR);
+            }
+            lds_barrier();
+        }
+    } else {
+        issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, false, k_.lds0, wave, lane);
+        dma_barrier();
         const int l16 = lane & 15, g4 = lane >> 4;
         const int jl = j0 + 16 * cw + l16;
 #pragma unroll
@@ -664,8 +687,8 @@ __device__ __forceinline__ void bwd_state_role(
             bj[kb] = frag_nat(smem, jl, kb, g4, NPR);
             cj[kb] = frag_nat(smem + C_::BCB, jl, kb, g4, NPR);
         }
+        lds_barrier();
     }
-    lds_barrier();
 
     f32x4 dbacc[NT], dcacc[NT];  // dB^T, dC^T [n][j]
 #pragma unroll
@@ -1313,11 +1336,18 @@ using BwdFn = hipError_t (*)(const Shape&, const BwdArgs&, hipStream_t);
 
 template <int Q>
 BwdFn pick_bwd_q(const Shape& s) {
-    if (s.P != 64) return nullptr;
-    switch (s.N) {
-        case 64: return launch_bwd_mfma_t<Q, 64, 64>;
-        case 128: return launch_bwd_mfma_t<Q, 128, 64>;
-        case 256: return launch_bwd_mfma_t<Q, 256, 64>;
+    if (s.P == 64) {
+        switch (s.N) {
+            case 64: return launch_bwd_mfma_t<Q, 64, 64>;
+            case 128: return launch_bwd_mfma_t<Q, 128, 64>;
+            case 256: return launch_bwd_mfma_t<Q, 256, 64>;
+        }
+    } else if (s.P == 32) {
+        switch (s.N) {
+            case 32: return launch_bwd_mfma_t<Q, 32, 32>;
+            case 64: return launch_bwd_mfma_t<Q, 64, 32>;
+            case 128: return launch_bwd_mfma_t<Q, 128, 32>;
+        }
     }
     return nullptr;
 }

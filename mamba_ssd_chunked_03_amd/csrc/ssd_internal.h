@@ -172,8 +172,9 @@ struct BwdArgs {
 int chunk_bwd_valu_rows();
 hipError_t launch_chunk_bwd_valu(const Shape& s, ssd_dtype dtype, const BwdArgs& a,
                                  hipStream_t st);
-// bf16 MFMA in-chunk backward (headdim 64, dstate 64, 128 or 256), same outputs; rows per
-// tile 64.  At dstate 256 it also needs BwdArgs' xfb, dBs and dCs (chunk_bwd_mfma_carried).
+// bf16 MFMA in-chunk backward (headdim 64 with dstate 64, 128 or 256; headdim 32 with
+// dstate 32, 64 or 128), same outputs; rows per tile 64.  At dstate 256 it also needs
+// BwdArgs' xfb, dBs and dCs (chunk_bwd_mfma_carried).
 bool chunk_bwd_mfma_supported(const Shape& s);
 bool chunk_bwd_mfma_carried(const Shape& s);
 int chunk_bwd_mfma_rows();

@@ -5,7 +5,7 @@ of the two roles (and the hardware gives no error for that).  This CPU test read
 kernel source and derives, for each role function, the sequence of barriers it executes:
 `lds_barrier()` (L) and `dma_barrier()` (D) in program order, with loops kept as
 (header: body) groups and `if constexpr` branches resolved for each configuration of the
-kernel.  The strip role must match the state role for dstate <= 128 and the dstate-256
+kernel (dstate 256 or not; B and C whole or in column slices).  The strip role must match the state role for dstate <= 128 and the dstate-256
 state role for dstate 256.  A barrier under a run-time `if`, or in a helper called from a
 role, is rejected: the check would not see whether both roles take it.
 """
@@ -140,29 +140,29 @@ def has_barrier(nodes):
     return False
 
 
-def sequence(nodes, ext):
-    """The barrier sequence with `if constexpr (C_::EXT)` resolved."""
+def sequence(nodes, flags):
+    """The barrier sequence with `if constexpr` on the configuration flags (C_::EXT,
+    C_::SLICED, or their negation) resolved by `flags`."""
     out = []
     for n in nodes:
         if n in ("L", "D"):
             out.append(n)
         elif n[0] == "block":
-            out.extend(sequence(n[1], ext))
+            out.extend(sequence(n[1], flags))
         elif n[0] == "for":
-            inner = sequence(n[2], ext)
+            inner = sequence(n[2], flags)
             if inner:
                 out.append((n[1], tuple(inner)))
         elif n[0] == "cif":
             cond = n[1]
-            if cond == "C_::EXT":
-                take = ext
-            elif cond == "!C_::EXT":
-                take = not ext
+            neg = cond.startswith("!")
+            if cond.lstrip("!") in flags:
+                take = flags[cond.lstrip("!")] != neg
             else:
                 assert not has_barrier(n[2]) and not has_barrier(n[3]), \
                     f"barrier under if constexpr ({cond})"
                 continue
-            out.extend(sequence(n[2] if take else n[3], ext))
+            out.extend(sequence(n[2] if take else n[3], flags))
         elif n[0] == "if":
             assert not has_barrier(n[2]), f"barrier under a run-time if ({n[1]})"
     return out
@@ -195,11 +195,17 @@ def test_parser_sees_every_barrier(src):
         assert count(parse(body)) == n_text, name
 
 
-@pytest.mark.parametrize("ext", [False, True], ids=["dstate_le_128", "dstate_256"])
-def test_roles_run_the_same_barriers(src, ext):
-    strip = sequence(parse(function_body(src, "bwd_strip_role")), ext)
+# (dstate 256, B / C in column slices for C B^T): every configuration the kernel has
+CONFIGS = [(False, False), (False, True), (True, True)]
+
+
+@pytest.mark.parametrize("ext,sliced", CONFIGS,
+                         ids=["whole_bc", "sliced_bc", "dstate_256"])
+def test_roles_run_the_same_barriers(src, ext, sliced):
+    flags = {"C_::EXT": ext, "C_::SLICED": sliced}
+    strip = sequence(parse(function_body(src, "bwd_strip_role")), flags)
     state_name = "bwd_state_role_ext" if ext else "bwd_state_role"
-    state = sequence(parse(function_body(src, state_name)), ext)
+    state = sequence(parse(function_body(src, state_name)), flags)
     assert strip, "no barriers found"
     assert strip == state, f"\nstrip: {strip}\nstate: {state}"
 
@@ -227,5 +233,6 @@ def test_check_catches_a_mismatch(src):
     body = function_body(src, "bwd_strip_role")
     i = body.index("lds_barrier();", body.index("for (int hh"))
     broken = body[:i] + body[i + len("lds_barrier();"):]
-    state = sequence(parse(function_body(src, "bwd_state_role")), False)
-    assert sequence(parse(broken), False) != state
+    flags = {"C_::EXT": False, "C_::SLICED": False}
+    state = sequence(parse(function_body(src, "bwd_state_role")), flags)
+    assert sequence(parse(broken), flags) != state

@@ -104,6 +104,14 @@ CASES = [
              log_neg_a_range=(np.log(0.01), np.log(0.1))),
     Workload("bwd_n256_q128", 2, 700, 6, 64, 256, 3, 128, init_state=True,
              log_neg_a_range=(np.log(0.005), np.log(0.05))),
+    # headdim 32 on the matrix cores (ragged_250_q64 and short_t17 above are too): B and C
+    # through LDS in 64- and 32-column slices for C B^T, W staged past the exchange area
+    Workload("bwd_p32_q256", 2, 1000, 8, 32, 128, 2, 256, init_state=True,
+             log_neg_a_range=(np.log(0.005), np.log(0.05))),
+    Workload("bwd_p32_n64_q256", 1, 600, 4, 32, 64, 1, 256, init_state=True,
+             log_neg_a_range=(np.log(0.01), np.log(0.1))),
+    Workload("bwd_p32_q128", 1, 500, 4, 32, 128, 1, 128, init_state=True,
+             log_neg_a_range=(np.log(0.005), np.log(0.05))),
 ]
 
 
@@ -169,8 +177,11 @@ def test_bwd_full_size_workloads(name):
     compare(w, g, oracle_bwd(cpu, up))
 
 
-@pytest.mark.parametrize("w", [STRESS["slow_decay"], CASES[0], CASES[-4], CASES[-1]],
-                         ids=["slow_decay", "tiny_fp32", "bwd_g2_q256", "bwd_n256_q128"])
+SAVED_CASES = ["slow_decay", "tiny_fp32", "bwd_g2_q256", "bwd_n256_q128", "bwd_p32_q256"]
+
+
+@pytest.mark.parametrize("w", [{c.name: c for c in CASES}[n] for n in SAVED_CASES],
+                         ids=SAVED_CASES)
 def test_bwd_saved_equals_recompute(w):
     """ssd_bwd_saved (the forward's intermediates read from its workspace) gives the same
     bits as ssd_bwd (which recomputes them)."""
