@@ -588,9 +588,10 @@ __device__ __forceinline__ void bwd_strip_role(
 #pragma unroll
             for (int s2 = 0; s2 < RJ; ++s2) xr[(1 + s2) * Q] = rsb[s2];
         }
-        if (vj) {
+        if (vj) {  // (the partner lane group of pair_runs has the same j)
             const float dh = D[h];
-            __bf16* dxr = dx + ((size_t)(b * T + t0 + jl) * H + h) * P + 4 * g4;
+            __bf16* dxr = dx + ((size_t)(b * T + t0 + jl) * H + h) * P;
+            uint2 o[PT];
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
                 const uint2 yq = *reinterpret_cast<const uint2*>(rows_at(sXY, jb + 64, PPR) + pac[pt]);
@@ -599,8 +600,12 @@ __device__ __forceinline__ void bwd_strip_role(
                 const float v1 = fmaf(dh, bf16_hi(yq.x), dtj * fmaf(fj, bf16_hi(bq.x), dxa[pt][1]));
                 const float v2 = fmaf(dh, bf16_lo(yq.y), dtj * fmaf(fj, bf16_lo(bq.y), dxa[pt][2]));
                 const float v3 = fmaf(dh, bf16_hi(yq.y), dtj * fmaf(fj, bf16_hi(bq.y), dxa[pt][3]));
-                *reinterpret_cast<uint2*>(dxr + 16 * pt) = make_uint2(pack_bf16(v0, v1), pack_bf16(v2, v3));
+                o[pt] = make_uint2(pack_bf16(v0, v1), pack_bf16(v2, v3));
             }
+#pragma unroll
+            for (int q = 0; q < PT / 2; ++q)  // 16-byte stores, p-tiles 2q and 2q + 1
+                *reinterpret_cast<uint4*>(dxr + 16 * (2 * q + (g4 & 1)) + 8 * (g4 >> 1)) =
+                    pair_runs(o[2 * q], o[2 * q + 1], (g4 & 1) != 0);
         }
         // this block's shares of the chunk-end term (dt_j ob_j, and exp(cs_last) <E, F> on
         // the first block) and of dD (x_j . dy_j); at dstate 256 the carried-state kernel
@@ -642,6 +647,24 @@ __device__ __forceinline__ void bwd_strip_role(
             issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, true, k_.lds0, wave, lane, part);
             dma_barrier();
         }
+    }
+}
+
+// dB^T and dC^T tiles [n][j] (lane: n = 16 nt + 4 g4 .. +3 of row j) rounded to bf16 and
+// stored as 16-byte runs of row j (pair_runs over n-tiles 2q, 2q + 1); row = the offset of
+// element 0 of row j in dB and dC
+template <int NTL>
+__device__ __forceinline__ void store_dbdc(__bf16* dB, __bf16* dC, size_t row, const f32x4* dbacc,
+                                           const f32x4* dcacc, int g4) {
+    const bool odd = (g4 & 1) != 0;
+#pragma unroll
+    for (int q = 0; q < NTL / 2; ++q) {
+        const size_t at = row + 16 * (2 * q + (g4 & 1)) + 8 * (g4 >> 1);
+        auto pk = [](const f32x4& a) {
+            return make_uint2(pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]));
+        };
+        *reinterpret_cast<uint4*>(dB + at) = pair_runs(pk(dbacc[2 * q]), pk(dbacc[2 * q + 1]), odd);
+        *reinterpret_cast<uint4*>(dC + at) = pair_runs(pk(dcacc[2 * q]), pk(dcacc[2 * q + 1]), odd);
     }
 }
 
@@ -835,16 +858,8 @@ __device__ __forceinline__ void bwd_state_role(
         for (int nt = 0; nt < NT; ++nt)
             dbacc[nt] = mfma16(ld_tr(rows_at(smem, rho, NPR), ptn[nt], N16), w8, dbacc[nt]);
     }
-    if (jl < Lc) {
-        const size_t ro = ((size_t)(b * T + t0 + jl) * G + g) * N + 4 * g4;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            *reinterpret_cast<uint2*>(dB + ro + 16 * nt) =
-                make_uint2(pack_bf16(dbacc[nt][0], dbacc[nt][1]), pack_bf16(dbacc[nt][2], dbacc[nt][3]));
-            *reinterpret_cast<uint2*>(dC + ro + 16 * nt) =
-                make_uint2(pack_bf16(dcacc[nt][0], dcacc[nt][1]), pack_bf16(dcacc[nt][2], dcacc[nt][3]));
-        }
-    }
+    if (jl < Lc)
+        store_dbdc<NT>(dB, dC, ((size_t)(b * T + t0 + jl) * G + g) * N, dbacc, dcacc, g4);
 }
 
 // The state waves at dstate 256.  chunk_bwd_carried_kernel has already formed the terms
@@ -943,15 +958,7 @@ __device__ __forceinline__ void bwd_state_role_ext(
             for (int nt = 0; nt < HT; ++nt)
                 dbacc[nt] = mfma16(ld_tr(rows_at(smem, rho, HPR), ptn[nt], N16), w8, dbacc[nt]);
         }
-        if (vj) {
-#pragma unroll
-            for (int nt = 0; nt < HT; ++nt) {
-                *reinterpret_cast<uint2*>(dB + ro + 16 * nt) = make_uint2(
-                    pack_bf16(dbacc[nt][0], dbacc[nt][1]), pack_bf16(dbacc[nt][2], dbacc[nt][3]));
-                *reinterpret_cast<uint2*>(dC + ro + 16 * nt) = make_uint2(
-                    pack_bf16(dcacc[nt][0], dcacc[nt][1]), pack_bf16(dcacc[nt][2], dcacc[nt][3]));
-            }
-        }
+        if (vj) store_dbdc<HT>(dB, dC, ro - 4 * g4, dbacc, dcacc, g4);
     };
     finish_half(0);
     // the other halves of n: every state wave has read the previous half's rows
@@ -1253,14 +1260,17 @@ __global__ __launch_bounds__(512) void chunk_bwd_carried_kernel(
         lds_barrier();
         {
             const int other = wave ^ 4, own = 2 * nh;
-            __bf16* xo = xfb + ((size_t)(b * T + t0 + jl) * H + h) * P + 4 * g4;
+            __bf16* xo = xfb + ((size_t)(b * T + t0 + jl) * H + h) * P;
+            uint2 o[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const f32x4 v = bfm[own + u] + xbm[(other * 2 + u) * 64 + lane];
-                if (vj)
-                    *reinterpret_cast<uint2*>(xo + 16 * (own + u)) =
-                        make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+                o[u] = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
             }
+            // one 16-byte store per lane (p-tiles own, own + 1; the partner group has the same j)
+            const uint4 pr = pair_runs(o[0], o[1], (g4 & 1) != 0);
+            if (vj)
+                *reinterpret_cast<uint4*>(xo + 16 * (own + (g4 & 1)) + 8 * (g4 >> 1)) = pr;
             const size_t cb = ((size_t)(b * H + h) * nC + c) * Q;
             float share;
             if (nh == 0) {

@@ -58,7 +58,9 @@ struct StateCfg {
     static constexpr unsigned XB = Q * P * 2, BB = Q * BW * 2, FB = Q * 4;
     static constexpr unsigned ITEM = XB + 2 * FB;  // x, cs, dt
     static constexpr unsigned LDS = BB + 2 * ITEM + FB;
-    static constexpr int STORES = PT * NTW;  // state stores per wave per item
+    // state stores per wave per item: PT / 2 16-byte stores per n-tile (PT 8-byte ones where
+    // PT is odd)
+    static constexpr int STORES = (PT % 2 == 0 ? PT / 2 : PT) * NTW;
     static_assert(NS == NTW, "one B slice per n-tile of a wave");
 };
 
@@ -280,13 +282,28 @@ __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_ker
         const int h = g * hpg + sl % hpg;
         __bf16* out = states + ((size_t)(b * H + h) * nC + c) * P * N;
 #pragma unroll
-        for (int k = 0; k < NTW; ++k)
+        for (int k = 0; k < NTW; ++k) {
+            uint2 o[PT];
 #pragma unroll
             for (int p = 0; p < PT; ++p)
-                *reinterpret_cast<uint2*>(out + (size_t)(p * 16 + l16) * N +
-                                          (wave + C_::NW * k) * 16 + 4 * g4) =
-                    make_uint2(pack_bf16(acc[k][p][0], acc[k][p][1]),
-                               pack_bf16(acc[k][p][2], acc[k][p][3]));
+                o[p] = make_uint2(pack_bf16(acc[k][p][0], acc[k][p][1]),
+                                  pack_bf16(acc[k][p][2], acc[k][p][3]));
+            if constexpr (PT % 2 == 0) {
+                // 16-byte stores (pair_runs over p-tiles 2q, 2q + 1): rows 16 (2q + g4 % 2)
+                // + l16, n-tile elements 8 (g4 / 2) .. +7
+                const bool odd = (g4 & 1) != 0;
+#pragma unroll
+                for (int q = 0; q < PT / 2; ++q)
+                    *reinterpret_cast<uint4*>(out + (size_t)((2 * q + (g4 & 1)) * 16 + l16) * N +
+                                              (wave + C_::NW * k) * 16 + 8 * (g4 >> 1)) =
+                        pair_runs(o[2 * q], o[2 * q + 1], odd);
+            } else {
+#pragma unroll
+                for (int p = 0; p < PT; ++p)
+                    *reinterpret_cast<uint2*>(out + (size_t)(p * 16 + l16) * N +
+                                              (wave + C_::NW * k) * 16 + 4 * g4) = o[p];
+            }
+        }
     }
 }
 

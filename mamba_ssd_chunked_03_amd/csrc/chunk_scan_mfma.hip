@@ -183,7 +183,9 @@ struct ScanCfg {
                               : (2 * ITEM + TAIL <= 160u * 1024u)         ? 2
                                                                           : 1;
     static constexpr unsigned LDS = NBUF * ITEM + TAIL;
-    static constexpr int STORES = 2 * PT;  // y stores per wave per item
+    // y stores per wave per item: two row tiles, each as PT / 2 16-byte stores per lane
+    // (PT 8-byte stores where PT is odd)
+    static constexpr int STORES = PT % 2 == 0 ? PT : 2 * PT;
 };
 
 template <int Q, int N, int P>
@@ -485,14 +487,28 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
         const __amdgpu_buffer_rsrc_t yr =
             make_rsrc(y + ((size_t)(b * T + t0) * H + h) * P, (unsigned)Lc * rowb);
         auto store_tile = [&](const f32x4* acc, int j) {
+            uint2 o[PT];
 #pragma unroll
             for (int p = 0; p < PT; ++p) {
                 const int p0 = p * 16 + 4 * g4;
                 const uint2 xv = *reinterpret_cast<const uint2*>(bx + swz_off(j, p0, PPR));
-                uint2 out;
-                out.x = pack_bf16(acc[p][0] + dh * bf16_lo(xv.x), acc[p][1] + dh * bf16_hi(xv.x));
-                out.y = pack_bf16(acc[p][2] + dh * bf16_lo(xv.y), acc[p][3] + dh * bf16_hi(xv.y));
-                buf_store8(yr, (unsigned)j * rowb + p0 * 2u, out);
+                o[p].x = pack_bf16(acc[p][0] + dh * bf16_lo(xv.x), acc[p][1] + dh * bf16_hi(xv.x));
+                o[p].y = pack_bf16(acc[p][2] + dh * bf16_lo(xv.y), acc[p][3] + dh * bf16_hi(xv.y));
+            }
+            if constexpr (PT % 2 == 0) {
+                // 16-byte stores (pair_runs over p-tiles 2q, 2q + 1): each writes 64
+                // contiguous bytes of 16 rows
+                const bool odd = (g4 & 1) != 0;
+#pragma unroll
+                for (int q = 0; q < PT / 2; ++q) {
+                    const int p0 = 32 * q + 16 * (g4 & 1) + 8 * (g4 >> 1);
+                    buf_store16(yr, (unsigned)j * rowb + p0 * 2u,
+                                pair_runs(o[2 * q], o[2 * q + 1], odd));
+                }
+            } else {
+#pragma unroll
+                for (int p = 0; p < PT; ++p)
+                    buf_store8(yr, (unsigned)j * rowb + (p * 16 + 4 * g4) * 2u, o[p]);
             }
         };
         store_tile(acc0, j0);

@@ -77,11 +77,28 @@ __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, unsigned of
     const u32x2 w = {v.x, v.y};
     __builtin_amdgcn_raw_buffer_store_b64(w, r, (int)off, 0, 0);
 }
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, unsigned off, uint4 v) {
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, 0);
+}
 // 16 bytes per lane from a buffer straight into LDS at lds_base + 16 * lane
 __device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds_base,
                                              unsigned off) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 0);
+}
+// Lane groups g = lane / 16 and g ^ 1 each hold, for two tiles a and b, a run of 4 bf16
+// (8 bytes) at element 4 g of a 16-element span.  After one exchange the even group holds
+// tile a's elements 8 (g / 2) .. +7 and the odd group tile b's, so each lane makes one
+// 16-byte store where it made two 8-byte ones (8-byte pieces spread over 16 rows write at
+// about 60% of the rate of 16-byte ones).  Returns the lane's 16 bytes, to be stored in tile
+// (odd ? b : a) at element 8 (g / 2).
+__device__ __forceinline__ uint4 pair_runs(uint2 ra, uint2 rb, bool odd) {
+    const uint2 keep = odd ? rb : ra, give = odd ? ra : rb;
+    const uint2 got = make_uint2((unsigned)__shfl_xor((int)give.x, 16, 64),
+                                 (unsigned)__shfl_xor((int)give.y, 16, 64));
+    return odd ? make_uint4(got.x, got.y, keep.x, keep.y)
+               : make_uint4(keep.x, keep.y, got.x, got.y);
 }
 // transpose read: see the header comment
 __device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
