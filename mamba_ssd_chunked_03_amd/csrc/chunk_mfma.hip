@@ -58,9 +58,11 @@ struct StateCfg {
     static constexpr unsigned XB = Q * P * 2, BB = Q * BW * 2, FB = Q * 4;
     static constexpr unsigned ITEM = XB + 2 * FB;  // x, cs, dt
     static constexpr unsigned LDS = BB + 2 * ITEM + FB;
-    // state stores per wave per item: PT / 2 16-byte stores per n-tile (PT 8-byte ones where
-    // PT is odd)
-    static constexpr int STORES = (PT % 2 == 0 ? PT / 2 : PT) * NTW;
+    // 16-byte state stores (PT / 2 per n-tile) in the forward; in the reverse-weight variant
+    // (the backward's state gradients) they measured slower (55.0 -> 59.1 us at 2.7B, the
+    // forward's 53.1 -> 51.4 us), so it keeps PT 8-byte stores per n-tile
+    static constexpr bool PAIRED(bool rev) { return PT % 2 == 0 && !rev; }
+    static constexpr int STORES(bool rev) { return (PAIRED(rev) ? PT / 2 : PT) * NTW; }
     static_assert(NS == NTW, "one B slice per n-tile of a wave");
 };
 
@@ -164,7 +166,7 @@ __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_ker
         if (n == 0)
             asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         else
-            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::STORES) : "memory");
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C_::STORES(REV)) : "memory");
         const int unit = sl / hpg;
         if (unit != cur_unit) {  // the B region holds slice 0 of this unit
             cur_unit = unit;
@@ -288,7 +290,7 @@ __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_ker
             for (int p = 0; p < PT; ++p)
                 o[p] = make_uint2(pack_bf16(acc[k][p][0], acc[k][p][1]),
                                   pack_bf16(acc[k][p][2], acc[k][p][3]));
-            if constexpr (PT % 2 == 0) {
+            if constexpr (C_::PAIRED(REV)) {
                 // 16-byte stores (pair_runs over p-tiles 2q, 2q + 1): rows 16 (2q + g4 % 2)
                 // + l16, n-tile elements 8 (g4 / 2) .. +7
                 const bool odd = (g4 & 1) != 0;
