@@ -25,7 +25,7 @@
 //
 // Everything is computed transposed so that the output rows (j) are MFMA columns: a lane
 // holds 4 consecutive p (or n) of one row j, which makes every per-row scalar a column sum
-// over the four lane groups and every store an 8-byte run:
+// over the four lane groups (stores pair two such runs into 16 bytes, pair_runs):
 //   dx^T[p][j]  = D dy + dt_j (sum_t dy[t][p] U[t][j] + exp(cs_last - cs_j) (F B_j)[p])
 //                 with U[t][j] = exp(cs_t - cs_j) (C_t . B_j)
 //   dB^T[n][j] += sum_p F[p][n] (dt_j exp(cs_last - cs_j) x_j[p])   (+ sum_t C[t][n] W[t][j])
@@ -39,8 +39,11 @@
 // so that the next head's copy runs under this head's products.  The state waves issue
 // the copy; at the end of a head each waits for its own share, a workgroup barrier
 // follows, and all eight waves then scale the next head's rows.  The group's B and C
-// chunks pass through the same LDS before the loop (for C B^T and the B_j, C_j operands)
-// and after it (for the two W products).
+// chunks pass through the same LDS before the loop (for C B^T and the B_j, C_j operands;
+// in column slices where whole chunks do not fit) and after it (for the two W products).
+//
+// At dstate 256 the terms through E and F are formed first, by chunk_bwd_carried_kernel
+// (at the end of this file), and this kernel takes them from HBM (BwdCfg::EXT).
 #include "mfma_common.h"
 #include "ssd_internal.h"
 
