@@ -502,18 +502,22 @@ def main():
         if ev is not None:
             ev[len(calls)].record()
 
-    # Per-step time distribution of whole ssd_fwd calls (HIP events per call): warm (back to
-    # back) and cold (the 256 MB Infinity Cache flushed by an untimed 1 GiB write before each
-    # call).  It runs first, so the GPU has been busy for a while when the timed steps begin.
+    # Per-step time distribution of whole ssd_fwd calls (HIP events per call): cold (the
+    # 256 MB Infinity Cache flushed by an untimed 1 GiB write before each call), then warm
+    # (back to back).  It runs first, so the GPU has been busy for a while when the timed
+    # steps begin.
     nstat = args.stat_steps if args.stat_steps > 0 else max(args.steps, 200)
-    log(f"[bench] per-step times: {nstat} warm, {nstat} cold ssd_fwd calls")
+    log(f"[bench] per-step times: {nstat} cold, {nstat} warm ssd_fwd calls")
     fwd()
     torch.cuda.synchronize()
     y_ref, fin_ref = y.clone(), fin.clone()
     scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    step_us = {"warm": step_stats(torch, fwd, nstat), "steps": nstat}
+    # cold first: the warm calls then run right before the warm-up and timed steps, so those
+    # start from the steady back-to-back state rather than from the flushes' aftermath
+    step_us = {"steps": nstat}
     if not args.no_cold:
         step_us["cold"] = step_stats(torch, fwd, nstat, flush=lambda: scratch.fill_(1.0))
+    step_us["warm"] = step_stats(torch, fwd, nstat)
     del scratch
 
     log(f"[bench] warmup {args.warmup}")
