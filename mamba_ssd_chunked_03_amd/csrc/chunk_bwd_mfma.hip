@@ -20,8 +20,8 @@
 // taken as whole 32-row blocks covering rows [0, j0 + 64) and [j0, Q): Q / 16 + 4 tiles of
 // 16 x 16 for every wave and every J.  W is accumulated over the heads in registers (fp32),
 // so dB and dC cost two products per workgroup rather than per head.  Outside J the decays
-// are folded into the rows (prescale_rows), so only the four blocks inside J need work per
-// element.
+// factor through a row of J (row_factors): the product tiles' rows are scaled by one
+// factor each, so only the four blocks inside J need work per element.
 //
 // Everything is computed transposed so that the output rows (j) are MFMA columns: a lane
 // holds 4 consecutive p (or n) of one row j, which makes every per-row scalar a column sum
@@ -32,13 +32,13 @@
 //   dC^T[n][j] += sum_p E[p][n] (exp(cs_j) dy_j[p])                  (+ sum_i B[i][n] W^T[i][j])
 // MFMA operand layouts are those of mfma_common.h: contractions over time (t, i) and over
 // p use the 8-slot relabelling so that accumulator tiles feed the next product directly;
-// contractions over n (the C B^T tiles, F B_j, E C_j) read natural 8-element runs.
+// contractions over n (the C B^T tiles, F B_j) read natural 8-element runs.
 //
 // Per head the x rows [0, j0 + 64) and dy rows [j0, Q) (one array of Q + 64 rows), E, F,
 // cs and dt are copied into LDS straight from HBM (buffer_load ... lds), double-buffered
 // so that the next head's copy runs under this head's products.  The state waves issue
 // the copy; at the end of a head each waits for its own share, a workgroup barrier
-// follows, and all eight waves then scale the next head's rows.  The group's B and C
+// follows, and the next head's row factors are formed from its cs and dt.  The group's B and C
 // chunks pass through the same LDS before the loop (for C B^T and the B_j, C_j operands;
 // in column slices where whole chunks do not fit) and after it (for the two W products).
 //
@@ -101,14 +101,33 @@ __device__ __forceinline__ float dot8(bf16x8 a, bf16x8 b) {
     s = fmaf(bf16_lo(x.w), bf16_lo(y.w), s);
     return fmaf(bf16_hi(x.w), bf16_hi(y.w), s);
 }
-__device__ __forceinline__ float colsum(float v) {  // over the four lane groups
-    v += __shfl_xor(v, 16, 64);
-    return v + __shfl_xor(v, 32, 64);
+// Sum over the four lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48), the same value in every
+// lane.  Two VALU exchanges instead of LDS-routed shuffles: v_permlane32_swap of v with
+// itself yields (lower half, upper half) in every lane, so their sum is v + (v at l ^ 32);
+// v_permlane16_swap likewise pairs the even and odd 16-lane rows.
+__device__ __forceinline__ float colsum(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+// v plus v from another lane of its 16-lane row, by a DPP row permutation
+template <int CTRL>
+__device__ __forceinline__ float add_dpp(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF,
+                                                          false));
+}
+// Sum over the wave, the same value in every lane: the lane groups, then inside a row the
+// pairs (quad_perm [1,0,3,2]), the quads' halves ([2,3,0,1]), the two quads of each half
+// row (row_half_mirror) and the two halves (row_mirror).
 __device__ __forceinline__ float wavesum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v = colsum(v);
+    v = add_dpp<0xB1>(v);
+    v = add_dpp<0x4E>(v);
+    v = add_dpp<0x141>(v);
+    return add_dpp<0x140>(v);
 }
 
 // nrows rows of a [rows][feat] bf16 matrix (row stride rowb bytes in HBM, from row
@@ -172,14 +191,16 @@ struct BwdCfg {
     static constexpr unsigned X_OB = X_BF + 4 * PT * 64 * 8;  // ob, oc per column [2][64]
     static constexpr unsigned X_EF = X_OB + 2 * 64 * 4;       // <E, F> share per wave [4]
     static constexpr unsigned X_SH = X_EF + 16;               // workgroup shares [2][4][2]
+    static constexpr unsigned X_RF = X_SH + 64;               // row factors of a head [Q]
+    static constexpr unsigned X_END = X_RF + Q * 4;
     // the W accumulators (bf16) travel from the strip waves after the B/C rows at the end:
     // inside the item buffers where they fit, else past the exchange area
     static constexpr unsigned WB = 4u * PAIRS * 64 * 16;
     static constexpr bool W_IN_ITEMS = !EXT && (Q + 64) * N * 2 + WB <= 2 * ITEM;
     static constexpr unsigned X_W =
         W_IN_ITEMS ? (Q + 64) * N * 2
-                   : ((Q + 64) * HN * 2 > X_SH + 64 ? (Q + 64) * HN * 2 : X_SH + 64);
-    static constexpr unsigned LDS = W_IN_ITEMS ? X_SH + 64 : X_W + WB;
+                   : ((Q + 64) * HN * 2 > X_END ? (Q + 64) * HN * 2 : X_END);
+    static constexpr unsigned LDS = W_IN_ITEMS ? X_END : X_W + WB;
     static_assert((P == 64 && (N == 64 || N == 128 || N == 256)) ||
                       (P == 32 && (N == 32 || N == 64 || N == 128)),
                   "shape");
@@ -242,39 +263,37 @@ __device__ __forceinline__ void issue_bc(const __bf16* Bm, const __bf16* Cm, int
     }
 }
 
-// ------------------------------------------------------------------ decays folded into rows
+// ------------------------------------------------------------------ decays factored per row
 // Outside J the causal decay factors through a fixed row of the chunk: for i < j0 <= j,
 // exp(cs_j - cs_i) = exp(cs_j - cs_j0) exp(cs_j0 - cs_i), and for t > j0 + 63 >= j,
-// exp(cs_t - cs_j) = exp(cs_t - cs_j0+63) exp(cs_j0+63 - cs_j), every factor <= 1.  The
-// row factors (with dt_i for the row strip) are applied once per head to the x rows before
-// J and the dy rows after J in LDS, so that plain products of those rows give the decayed
-// W and the decayed (C B^T) product for dx; only the blocks inside J need per-element work.
+// exp(cs_t - cs_j) = exp(cs_t - cs_j0+63) exp(cs_j0+63 - cs_j), every factor <= 1.  Per
+// head, the row factors (with dt_i for the row strip) are formed once into a vector of Q
+// floats, rf[i] = dt_i exp(cs_j0 - cs_i) for i < j0 and rf[t] = exp(cs_t - cs_j0+63) for
+// t > j0 + 63; the strip waves apply them to the rows of their product tiles (and to the
+// C B^T operand of dx), so only the blocks inside J need work per element.
 template <int Q, int N, int P>
-__device__ __forceinline__ void prescale_rows(unsigned char* sXY, int j0, int tid, int nth) {
+__device__ __forceinline__ void row_factors(const unsigned char* sXY, float* rf, int j0, int tid,
+                                            int nth) {
     const float* s_cs = reinterpret_cast<const float*>(sXY + BwdCfg<Q, N, P>::XYB +
                                                        2 * BwdCfg<Q, N, P>::EB);
     const float* s_dt = s_cs + Q;
-    constexpr int PPR = P / 8;
     const float cs_a = s_cs[j0], cs_b = s_cs[j0 + 63];
-    auto scale_piece = [&](unsigned char* p, float f) {
-        uint4 v = *reinterpret_cast<uint4*>(p);
-        v = make_uint4(pack_bf16(bf16_lo(v.x) * f, bf16_hi(v.x) * f),
-                       pack_bf16(bf16_lo(v.y) * f, bf16_hi(v.y) * f),
-                       pack_bf16(bf16_lo(v.z) * f, bf16_hi(v.z) * f),
-                       pack_bf16(bf16_lo(v.w) * f, bf16_hi(v.w) * f));
-        *reinterpret_cast<uint4*>(p) = v;
-    };
-    // x rows i < j0 (LDS rows i): dt_i exp(cs_j0 - cs_i)
-    for (int m = tid; m < j0 * PPR; m += nth) {
-        const int i = m / PPR;
-        scale_piece(sXY + 16 * m, s_dt[i] * exp2_fast((cs_a - s_cs[i]) * kLog2e));
+    for (int i = tid; i < Q; i += nth) {
+        if (i < j0)
+            rf[i] = s_dt[i] * exp2_fast((cs_a - s_cs[i]) * kLog2e);
+        else if (i >= j0 + 64)
+            rf[i] = exp2_fast((s_cs[i] - cs_b) * kLog2e);
     }
-    // dy rows t >= j0 + 64 (LDS rows t + 64): exp(cs_t - cs_j0+63)
-    unsigned char* yb = sXY + (j0 + 128) * PPR * 16;
-    for (int m = tid; m < (Q - j0 - 64) * PPR; m += nth) {
-        const int t = j0 + 64 + m / PPR;
-        scale_piece(yb + 16 * m, exp2_fast((s_cs[t] - cs_b) * kLog2e));
-    }
+}
+
+// the four row factors of rows r .. r + 3 (r a multiple of 4)
+__device__ __forceinline__ float4 rf4(const float* rf, int r) {
+    return *reinterpret_cast<const float4*>(rf + r);
+}
+// 4 bf16 (a uint2) times 4 factors, rounded back to bf16
+__device__ __forceinline__ uint2 scale4(uint2 v, float4 f) {
+    return make_uint2(pack_bf16(bf16_lo(v.x) * f.x, bf16_hi(v.x) * f.y),
+                      pack_bf16(bf16_lo(v.y) * f.z, bf16_hi(v.y) * f.w));
 }
 
 // Everything both roles need to know about their workgroup
@@ -383,12 +402,12 @@ __device__ __forceinline__ void bwd_strip_role(
     for (int s = 0; s < 2 * PAIRS; ++s) wacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     dma_barrier();  // the first head's rows have landed (copied by the state waves)
-    lds_barrier();  // ... and are scaled (by the state waves)
+    lds_barrier();  // ... and its row factors are formed (by the state waves)
 #pragma unroll 1
     for (int hh = 0; hh < hpg; ++hh) {
         const int h = g * hpg + hh;
         const int buf = hh & 1;
-        lds_barrier();  // this head's rows are scaled; the other buffer is free
+        lds_barrier();  // this head's row factors are formed; the other buffer is free
         if (!C_::EXT && hh > 0 && wave == 0 && lane == 0) {
             const float* sh = shares + (buf ^ 1) * 8;
             const size_t pi = ((size_t)(b * H + h - 1) * nC + c) * NJ + RJ;
@@ -398,6 +417,7 @@ __device__ __forceinline__ void bwd_strip_role(
         unsigned char* sXY = smem + buf * C_::ITEM;
         const float* s_cs = reinterpret_cast<const float*>(sXY + C_::XYB + 2 * C_::EB);
         const float* s_dt = s_cs + Q;
+        const float* s_rf = reinterpret_cast<const float*>(smem + C_::X_RF);
         // lane-dependent values re-derived every head from an opaque copy of the lane
         // index: the compiler recomputes the LDS addresses instead of keeping them live
         int ln = lane;
@@ -445,23 +465,31 @@ __device__ __forceinline__ void bwd_strip_role(
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) dxa[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // column strip after J: W[t][j] straight into the accumulators, and (C B^T) dy
+        // column strip after J: W[t][j] (rows scaled by their factors) into the
+        // accumulators, and (C B^T) dy with C B^T scaled by the same factors
         {
             bf16x8 xk[PKB];
 #pragma unroll
             for (int kb = 0; kb < PKB; ++kb) xk[kb] = scale8(xj[kb], dtj * k2);
 #pragma unroll
             for (int k = RSP + 2; k < PAIRS; ++k) {
-                const int rho = j0 + 32 * (k - RSP) + 64;
+                const int rt = j0 + 32 * (k - RSP);  // chunk row of the block
+                const int rho = rt + 64;              // its LDS row
+                float4 f[2];
 #pragma unroll
-                for (int u = 0; u < 2; ++u)
+                for (int u = 0; u < 2; ++u) {
+                    f[u] = rf4(s_rf, rt + 16 * u + 4 * g4);
+                    f32x4 w = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kb = 0; kb < PKB; ++kb)
-                        wacc[2 * k + u] = mfma16(ld_nat(rows_at(sXY, rho, PPR) + u * R16, pnp[kb]),
-                                                 xk[kb], wacc[2 * k + u]);
-                pin(wacc[2 * k]);
-                pin(wacc[2 * k + 1]);
-                const uint2 g0 = gt[2 * k], g1 = gt[2 * k + 1];
+                        w = mfma16(ld_nat(rows_at(sXY, rho, PPR) + u * R16, pnp[kb]), xk[kb], w);
+                    wacc[2 * k + u][0] = fmaf(f[u].x, w[0], wacc[2 * k + u][0]);
+                    wacc[2 * k + u][1] = fmaf(f[u].y, w[1], wacc[2 * k + u][1]);
+                    wacc[2 * k + u][2] = fmaf(f[u].z, w[2], wacc[2 * k + u][2]);
+                    wacc[2 * k + u][3] = fmaf(f[u].w, w[3], wacc[2 * k + u][3]);
+                    pin(wacc[2 * k + u]);
+                }
+                const uint2 g0 = scale4(gt[2 * k], f[0]), g1 = scale4(gt[2 * k + 1], f[1]);
                 const bf16x8 gb = __builtin_bit_cast(bf16x8, make_uint4(g0.x, g0.y, g1.x, g1.y));
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt) {
@@ -482,7 +510,8 @@ __device__ __forceinline__ void bwd_strip_role(
             cpx = fmaf(bf16_lo(xq.y), dxa[pt][2], cpx);
             cpx = fmaf(bf16_hi(xq.y), dxa[pt][3], cpx);
         }
-        // row strip before J: W^T[i][j] from the scaled rows, its W.G sums per 64-row block
+        // row strip before J: W^T[i][j] with its rows scaled by their factors, its W.G sums
+        // per 64-row block
         {
             bf16x8 yk[PKB];
 #pragma unroll
@@ -495,6 +524,11 @@ __device__ __forceinline__ void bwd_strip_role(
 #pragma unroll
                     for (int kb = 0; kb < PKB; ++kb)
                         w = mfma16(ld_nat(rows_at(sXY, 32 * k, PPR) + u * R16, pnp[kb]), yk[kb], w);
+                    const float4 f = rf4(s_rf, 32 * k + 16 * u + 4 * g4);
+                    w[0] *= f.x;
+                    w[1] *= f.y;
+                    w[2] *= f.z;
+                    w[3] *= f.w;
                     const uint2 gg = gt[2 * k + u];
                     wacc[2 * k + u] += w;
                     pin(wacc[2 * k + u]);
@@ -608,7 +642,7 @@ __device__ __forceinline__ void bwd_strip_role(
 #pragma unroll
             for (int q = 0; q < PT / 2; ++q)  // 16-byte stores, p-tiles 2q and 2q + 1
                 *reinterpret_cast<uint4*>(dxr + 16 * (2 * q + (g4 & 1)) + 8 * (g4 >> 1)) =
-                    pair_runs(o[2 * q], o[2 * q + 1], (g4 & 1) != 0);
+                    pair_runs(o[2 * q], o[2 * q + 1]);
         }
         // this block's shares of the chunk-end term (dt_j ob_j, and exp(cs_last) <E, F> on
         // the first block) and of dD (x_j . dy_j); at dstate 256 the carried-state kernel
@@ -623,7 +657,9 @@ __device__ __forceinline__ void bwd_strip_role(
         }
         lds_barrier();  // every state wave's copies of the next head have landed
         if (hh + 1 < hpg)
-            prescale_rows<Q, N, P>(smem + (buf ^ 1) * C_::ITEM, j0, (int)threadIdx.x, 512);
+            row_factors<Q, N, P>(smem + (buf ^ 1) * C_::ITEM,
+                                 reinterpret_cast<float*>(smem + C_::X_RF), j0,
+                                 (int)threadIdx.x, 512);
     }
     dma_barrier();
     if (!C_::EXT && wave == 0 && lane == 0) {
@@ -659,21 +695,22 @@ __device__ __forceinline__ void bwd_strip_role(
 template <int NTL>
 __device__ __forceinline__ void store_dbdc(__bf16* dB, __bf16* dC, size_t row, const f32x4* dbacc,
                                            const f32x4* dcacc, int g4) {
-    const bool odd = (g4 & 1) != 0;
 #pragma unroll
     for (int q = 0; q < NTL / 2; ++q) {
         const size_t at = row + 16 * (2 * q + (g4 & 1)) + 8 * (g4 >> 1);
         auto pk = [](const f32x4& a) {
             return make_uint2(pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]));
         };
-        *reinterpret_cast<uint4*>(dB + at) = pair_runs(pk(dbacc[2 * q]), pk(dbacc[2 * q + 1]), odd);
-        *reinterpret_cast<uint4*>(dC + at) = pair_runs(pk(dcacc[2 * q]), pk(dcacc[2 * q + 1]), odd);
+        *reinterpret_cast<uint4*>(dB + at) = pair_runs(pk(dbacc[2 * q]), pk(dbacc[2 * q + 1]));
+        *reinterpret_cast<uint4*>(dC + at) = pair_runs(pk(dcacc[2 * q]), pk(dcacc[2 * q + 1]));
     }
 }
 
 // ------------------------------------------------------------------ state waves
-// The off-diagonal terms through the carried states E and F: (F B_j), (E C_j) for dx and
-// the per-row sums ob, oc; the dB and dC accumulators; the two W products at the end.
+// The off-diagonal terms through the carried states E and F: (F B_j) for dx and the
+// per-row sums ob, oc (oc_j = exp(cs_j) dy_j . (E C_j) is taken as C_j . (the head's dC^T
+// column j), so E C_j itself is never formed); the dB and dC accumulators; the two W
+// products at the end.
 template <int Q, int N, int P>
 __device__ __forceinline__ void bwd_state_role(
     const BwdCtx& k_, unsigned char* smem, const __bf16* x, const __bf16* Bm, const __bf16* Cm,
@@ -687,9 +724,12 @@ __device__ __forceinline__ void bwd_state_role(
     const int wave = k_.wave, cw = k_.cw, lane = k_.lane;
     const int rsp = (j0 + 64) / 32;  // row-strip blocks (rows 32 k), then column-strip blocks
 
-    bf16x8 bj[NKB], cj[NKB];  // B_j, C_j over n (natural slots)
+    // B_j over n (natural slots, the operand of F B_j) and C_j[16 nt + 4 g4 .. +3] (the
+    // lane's n of the dC^T tiles)
+    bf16x8 bj[NKB];
+    uint2 cq[NT];
     if constexpr (C_::SLICED) {  // the strip waves' C B^T slices, this wave's B_j, C_j parts
-        constexpr int SPR = C_::SLN / 8, SKB = C_::SLN / 32;
+        constexpr int SPR = C_::SLN / 8, SKB = C_::SLN / 32, STL = C_::SLN / 16;
         const int l16 = lane & 15, g4 = lane >> 4;
         const int jl = j0 + 16 * cw + l16;
 #pragma unroll
@@ -697,10 +737,11 @@ __device__ __forceinline__ void bwd_state_role(
             issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, false, k_.lds0, wave, lane, sl);
             dma_barrier();
 #pragma unroll
-            for (int kb = 0; kb < SKB; ++kb) {
-                bj[sl * SKB + kb] = frag_nat(smem, jl, kb, g4, SPR);
-                cj[sl * SKB + kb] = frag_nat(smem + C_::BCB, jl, kb, g4, SPR);
-            }
+            for (int kb = 0; kb < SKB; ++kb) bj[sl * SKB + kb] = frag_nat(smem, jl, kb, g4, SPR);
+#pragma unroll
+            for (int nt = 0; nt < STL; ++nt)
+                cq[sl * STL + nt] = *reinterpret_cast<const uint2*>(
+                    smem + C_::BCB + swz_off(jl, 16 * nt + 4 * g4, SPR));
             lds_barrier();
         }
     } else {
@@ -709,10 +750,11 @@ __device__ __forceinline__ void bwd_state_role(
         const int l16 = lane & 15, g4 = lane >> 4;
         const int jl = j0 + 16 * cw + l16;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            bj[kb] = frag_nat(smem, jl, kb, g4, NPR);
-            cj[kb] = frag_nat(smem + C_::BCB, jl, kb, g4, NPR);
-        }
+        for (int kb = 0; kb < NKB; ++kb) bj[kb] = frag_nat(smem, jl, kb, g4, NPR);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            cq[nt] = *reinterpret_cast<const uint2*>(smem + C_::BCB +
+                                                     swz_off(jl, 16 * nt + 4 * g4, NPR));
         lds_barrier();
     }
 
@@ -723,7 +765,8 @@ __device__ __forceinline__ void bwd_state_role(
     issue_item<Q, N, P>(x, dy, entry, exitg, cs, dtc, b, g * hpg, c, j0, Lc, T, H, nC, k_.lds0,
                         wave - 4, lane);
     dma_barrier();
-    prescale_rows<Q, N, P>(smem, j0, (int)threadIdx.x - 256, 256);
+    row_factors<Q, N, P>(smem, reinterpret_cast<float*>(smem + C_::X_RF), j0,
+                         (int)threadIdx.x - 256, 256);
     lds_barrier();
 #pragma unroll 1
     for (int hh = 0; hh < hpg; ++hh) {
@@ -760,37 +803,45 @@ __device__ __forceinline__ void bwd_state_role(
         const float csj = s_cs[jl], dtj = s_dt[jl];
         const float ej = exp2_fast(csj * kLog2e), fj = exp2_fast((cs_last - csj) * kLog2e);
 
-        // dC^T[n][j] += sum_p E[p][n] (exp(cs_j) dy_j[p])
+        // this head's dC^T[n][j] term, sum_p E[p][n] (exp(cs_j) dy_j[p]), and from it
+        // oc_j = exp(cs_j) dy_j . (E C_j) = sum_n C_j[n] (that term)[n][j]
+        float oc = 0.f;
+        {
+            f32x4 dch[NT];
 #pragma unroll
-        for (int kb = 0; kb < PKB; ++kb) {
-            const bf16x8 ys8 =
-                scale8(ld_rl(rows_at(sXY, jb + 64, PPR), prl[kb][0], prl[kb][1]), ej);
+            for (int nt = 0; nt < NT; ++nt) dch[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                dcacc[nt] = mfma16(ld_tr(rows_at(sE, 32 * kb, NPR), ptn[nt], N16), ys8, dcacc[nt]);
+            for (int kb = 0; kb < PKB; ++kb) {
+                const bf16x8 ys8 =
+                    scale8(ld_rl(rows_at(sXY, jb + 64, PPR), prl[kb][0], prl[kb][1]), ej);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    dch[nt] = mfma16(ld_tr(rows_at(sE, 32 * kb, NPR), ptn[nt], N16), ys8, dch[nt]);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                oc = fmaf(bf16_lo(cq[nt].x), dch[nt][0], oc);
+                oc = fmaf(bf16_hi(cq[nt].x), dch[nt][1], oc);
+                oc = fmaf(bf16_lo(cq[nt].y), dch[nt][2], oc);
+                oc = fmaf(bf16_hi(cq[nt].y), dch[nt][3], oc);
+                dcacc[nt] += dch[nt];
+            }
         }
-        // (F B_j)[p] and (E C_j)[p] as [p][j] tiles; ob_j = exp(cs_last - cs_j) x_j . (F B_j),
-        // oc_j = exp(cs_j) dy_j . (E C_j)
-        float ob = 0.f, oc = 0.f, dd = 0.f;
+        // (F B_j)[p] as [p][j] tiles; ob_j = exp(cs_last - cs_j) x_j . (F B_j)
+        float ob = 0.f, dd = 0.f;
         uint2* xbf = reinterpret_cast<uint2*>(smem + C_::X_BF) + (cw * PT) * 64 + ln;
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
-            f32x4 bfm = f32x4{0.f, 0.f, 0.f, 0.f}, cem = bfm;
+            f32x4 bfm = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
+            for (int kb = 0; kb < NKB; ++kb)
                 bfm = mfma16(ld_nat(rows_at(sF, 16 * pt, NPR), pnat[kb]), bj[kb], bfm);
-                cem = mfma16(ld_nat(rows_at(sE, 16 * pt, NPR), pnat[kb]), cj[kb], cem);
-            }
             const uint2 xq = *reinterpret_cast<const uint2*>(rows_at(sXY, jb, PPR) + pac[pt]);
             const uint2 yq = *reinterpret_cast<const uint2*>(rows_at(sXY, jb + 64, PPR) + pac[pt]);
             ob = fmaf(bf16_lo(xq.x), bfm[0], ob);
             ob = fmaf(bf16_hi(xq.x), bfm[1], ob);
             ob = fmaf(bf16_lo(xq.y), bfm[2], ob);
             ob = fmaf(bf16_hi(xq.y), bfm[3], ob);
-            oc = fmaf(bf16_lo(yq.x), cem[0], oc);
-            oc = fmaf(bf16_hi(yq.x), cem[1], oc);
-            oc = fmaf(bf16_lo(yq.y), cem[2], oc);
-            oc = fmaf(bf16_hi(yq.y), cem[3], oc);
             dd = fmaf(bf16_lo(xq.x), bf16_lo(yq.x), dd);
             dd = fmaf(bf16_hi(xq.x), bf16_hi(yq.x), dd);
             dd = fmaf(bf16_lo(xq.y), bf16_lo(yq.y), dd);
@@ -798,7 +849,7 @@ __device__ __forceinline__ void bwd_state_role(
             xbf[pt * 64] = make_uint2(pack_bf16(bfm[0], bfm[1]), pack_bf16(bfm[2], bfm[3]));
         }
         ob = colsum(ob) * fj;
-        oc = colsum(oc) * ej;
+        oc = colsum(oc);
         dd = wavesum(dd);  // this wave's 16 rows of x_j . dy_j (the dD share)
         if (ln == 0) reinterpret_cast<float*>(smem + C_::X_SH)[buf * 8 + 2 * cw + 1] = dd;
         float* xob = reinterpret_cast<float*>(smem + C_::X_OB);
@@ -825,12 +876,15 @@ __device__ __forceinline__ void bwd_state_role(
                 dbacc[nt] = mfma16(ld_tr(rows_at(sF, 32 * kb, NPR), ptn[nt], N16), xs8, dbacc[nt]);
         }
         // this wave's share of the next head's copies has landed; after the barrier every
-        // share has, and all eight waves scale the next head's rows (read after its first
-        // barrier).  A wave's vmcnt covers only its own copies, so the barrier is needed.
+        // share has, and the next head's row factors are formed from its cs and dt (read
+        // after its first barrier).  A wave's vmcnt covers only its own copies, so the
+        // barrier is needed.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();
         if (hh + 1 < hpg)
-            prescale_rows<Q, N, P>(smem + (buf ^ 1) * C_::ITEM, j0, (int)threadIdx.x, 512);
+            row_factors<Q, N, P>(smem + (buf ^ 1) * C_::ITEM,
+                                 reinterpret_cast<float*>(smem + C_::X_RF), j0,
+                                 (int)threadIdx.x, 512);
     }
     dma_barrier();
     issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, true, k_.lds0, wave, lane);
@@ -867,7 +921,7 @@ __device__ __forceinline__ void bwd_state_role(
 
 // The state waves at dstate 256.  chunk_bwd_carried_kernel has already formed the terms
 // through the carried states, so per head these waves hand its (F B_j) tile and ob, oc to
-// the strip waves and issue and scale the copies; after the loop they finish dB and dC from
+// the strip waves and issue the copies; after the loop they finish dB and dC from
 // that kernel's head sums, one half of n at a time.  The barriers are bwd_state_role's.
 template <int Q, int N, int P>
 __device__ __forceinline__ void bwd_state_role_ext(
@@ -894,7 +948,8 @@ __device__ __forceinline__ void bwd_state_role_ext(
     issue_item<Q, N, P>(x, dy, nullptr, nullptr, cs, dtc, b, g * hpg, c, j0, Lc, T, H, nC,
                         k_.lds0, wave - 4, lane);
     dma_barrier();
-    prescale_rows<Q, N, P>(smem, j0, (int)threadIdx.x - 256, 256);
+    row_factors<Q, N, P>(smem, reinterpret_cast<float*>(smem + C_::X_RF), j0,
+                         (int)threadIdx.x - 256, 256);
     lds_barrier();
 #pragma unroll 1
     for (int hh = 0; hh < hpg; ++hh) {
@@ -924,7 +979,9 @@ __device__ __forceinline__ void bwd_state_role_ext(
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();
         if (hh + 1 < hpg)
-            prescale_rows<Q, N, P>(smem + (buf ^ 1) * C_::ITEM, j0, (int)threadIdx.x, 512);
+            row_factors<Q, N, P>(smem + (buf ^ 1) * C_::ITEM,
+                                 reinterpret_cast<float*>(smem + C_::X_RF), j0,
+                                 (int)threadIdx.x, 512);
     }
     dma_barrier();
     issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, true, k_.lds0, wave, lane);
@@ -1025,9 +1082,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_mfma_kernel(
 #undef SSD_STRIP
         }
     } else {
-        // the state waves issue every copy and scale the next head's rows, which the strip
-        // waves wait on: they go first when both are ready to issue (the saved backward at
-        // 2.7B: 538 -> 519 us)
+        // the state waves issue every copy, which the strip waves wait on: they go first
+        // when both are ready to issue (the saved backward at 2.7B: 538 -> 519 us)
         __builtin_amdgcn_s_setprio(3);
         if constexpr (C_::EXT)
             bwd_state_role_ext<Q, N, P>(k_, smem, x, Bm, Cm, dtc, cs, dy, xfb, direct, dcs, dBs,
@@ -1271,7 +1327,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_carried_kernel(
                 o[u] = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
             }
             // one 16-byte store per lane (p-tiles own, own + 1; the partner group has the same j)
-            const uint4 pr = pair_runs(o[0], o[1], (g4 & 1) != 0);
+            const uint4 pr = pair_runs(o[0], o[1]);
             if (vj)
                 *reinterpret_cast<uint4*>(xo + 16 * (own + (g4 & 1)) + 8 * (g4 >> 1)) = pr;
             const size_t cb = ((size_t)(b * H + h) * nC + c) * Q;

@@ -293,12 +293,11 @@ __global__ __launch_bounds__((StateCfg<Q, N, P>::NTH)) void chunk_state_pipe_ker
             if constexpr (C_::PAIRED(REV)) {
                 // 16-byte stores (pair_runs over p-tiles 2q, 2q + 1): rows 16 (2q + g4 % 2)
                 // + l16, n-tile elements 8 (g4 / 2) .. +7
-                const bool odd = (g4 & 1) != 0;
 #pragma unroll
                 for (int q = 0; q < PT / 2; ++q)
                     *reinterpret_cast<uint4*>(out + (size_t)((2 * q + (g4 & 1)) * 16 + l16) * N +
                                               (wave + C_::NW * k) * 16 + 8 * (g4 >> 1)) =
-                        pair_runs(o[2 * q], o[2 * q + 1], odd);
+                        pair_runs(o[2 * q], o[2 * q + 1]);
             } else {
 #pragma unroll
                 for (int p = 0; p < PT; ++p)

@@ -498,12 +498,11 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
             if constexpr (PT % 2 == 0) {
                 // 16-byte stores (pair_runs over p-tiles 2q, 2q + 1): each writes 64
                 // contiguous bytes of 16 rows
-                const bool odd = (g4 & 1) != 0;
 #pragma unroll
                 for (int q = 0; q < PT / 2; ++q) {
                     const int p0 = 32 * q + 16 * (g4 & 1) + 8 * (g4 >> 1);
                     buf_store16(yr, (unsigned)j * rowb + p0 * 2u,
-                                pair_runs(o[2 * q], o[2 * q + 1], odd));
+                                pair_runs(o[2 * q], o[2 * q + 1]));
                 }
             } else {
 #pragma unroll

@@ -92,13 +92,14 @@ __device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds
 // tile a's elements 8 (g / 2) .. +7 and the odd group tile b's, so each lane makes one
 // 16-byte store where it made two 8-byte ones (8-byte pieces spread over 16 rows write at
 // about 60% of the rate of 16-byte ones).  Returns the lane's 16 bytes, to be stored in tile
-// (odd ? b : a) at element 8 (g / 2).
-__device__ __forceinline__ uint4 pair_runs(uint2 ra, uint2 rb, bool odd) {
-    const uint2 keep = odd ? rb : ra, give = odd ? ra : rb;
-    const uint2 got = make_uint2((unsigned)__shfl_xor((int)give.x, 16, 64),
-                                 (unsigned)__shfl_xor((int)give.y, 16, 64));
-    return odd ? make_uint4(got.x, got.y, keep.x, keep.y)
-               : make_uint4(keep.x, keep.y, got.x, got.y);
+// (g odd ? b : a) at element 8 (g / 2).  The exchange is v_permlane16_swap, which trades
+// the odd 16-lane rows of its first operand for the even rows of its second: with (a, b) as
+// the operands, an even row gets (its a, the odd row's a) and an odd row (the even row's b,
+// its b), both in the order of the returned pair.
+__device__ __forceinline__ uint4 pair_runs(uint2 ra, uint2 rb) {
+    const auto x = __builtin_amdgcn_permlane16_swap(ra.x, rb.x, false, false);
+    const auto y = __builtin_amdgcn_permlane16_swap(ra.y, rb.y, false, false);
+    return make_uint4(x[0], y[0], x[1], y[1]);
 }
 // transpose read: see the header comment
 __device__ __forceinline__ uint2 lds_read_tr16(const void* p) {

@@ -214,7 +214,7 @@ def test_roles_call_no_barrier_helpers(src):
     """Barriers only appear in the role functions themselves and the kernels (no helper
     that a role calls issues one): the per-role count above would miss them."""
     barrier = re.compile(r"\b(?:lds|dma)_barrier\s*\(|__syncthreads|s_barrier")
-    helpers = ("issue_item", "issue_bc", "issue_rows", "prescale_rows")
+    helpers = ("issue_item", "issue_bc", "issue_rows", "row_factors")
     for h in helpers:
         assert not barrier.search(function_body(src, h)), h
     # nor a lambda inside a role (its body is parsed where it is defined, not called)
