@@ -37,8 +37,8 @@
 // Per head the x rows [0, j0 + 64) and dy rows [j0, Q) (one array of Q + 64 rows), E, F,
 // cs and dt are copied into LDS straight from HBM (buffer_load ... lds), double-buffered
 // so that the next head's copy runs under this head's products.  The state waves issue
-// the copy; at the end of a head each waits for its own share, a workgroup barrier
-// follows, and the next head's row factors are formed from its cs and dt.  The group's B and C
+// the copy; at the end of a head each waits for its own share and a workgroup barrier
+// follows (two barriers per head: this one and the hand-off).  The group's B and C
 // chunks pass through the same LDS before the loop (for C B^T and the B_j, C_j operands;
 // in column slices where whole chunks do not fit) and after it (for the two W products).
 //
@@ -191,8 +191,9 @@ struct BwdCfg {
     static constexpr unsigned X_OB = X_BF + 4 * PT * 64 * 8;  // ob, oc per column [2][64]
     static constexpr unsigned X_EF = X_OB + 2 * 64 * 4;       // <E, F> share per wave [4]
     static constexpr unsigned X_SH = X_EF + 16;               // workgroup shares [2][4][2]
-    static constexpr unsigned X_RF = X_SH + 64;               // row factors of a head [Q]
-    static constexpr unsigned X_END = X_RF + Q * 4;
+    // each strip wave's row factors of its head (the Q - 64 rows outside J) [4][Q - 64]
+    static constexpr unsigned X_RF = X_SH + 64;
+    static constexpr unsigned X_END = X_RF + 4 * (Q - 64) * 4;
     // the W accumulators (bf16) travel from the strip waves after the B/C rows at the end:
     // inside the item buffers where they fit, else past the exchange area
     static constexpr unsigned WB = 4u * PAIRS * 64 * 16;
@@ -267,22 +268,26 @@ __device__ __forceinline__ void issue_bc(const __bf16* Bm, const __bf16* Cm, int
 // Outside J the causal decay factors through a fixed row of the chunk: for i < j0 <= j,
 // exp(cs_j - cs_i) = exp(cs_j - cs_j0) exp(cs_j0 - cs_i), and for t > j0 + 63 >= j,
 // exp(cs_t - cs_j) = exp(cs_t - cs_j0+63) exp(cs_j0+63 - cs_j), every factor <= 1.  Per
-// head, the row factors (with dt_i for the row strip) are formed once into a vector of Q
-// floats, rf[i] = dt_i exp(cs_j0 - cs_i) for i < j0 and rf[t] = exp(cs_t - cs_j0+63) for
-// t > j0 + 63; the strip waves apply them to the rows of their product tiles (and to the
-// C B^T operand of dx), so only the blocks inside J need work per element.
+// head, each strip wave forms the row factors (with dt_i for the row strip) of the Q - 64
+// rows outside J in its own LDS slice, rf[i] = dt_i exp(cs_j0 - cs_i) for rows i < j0 and
+// rf[t - 64] = exp(cs_t - cs_j0+63) for rows t > j0 + 63, and applies them to the rows of
+// its product tiles (and to the C B^T operand of dx), so only the blocks inside J need work
+// per element.  The slice is the wave's own (a wave's LDS accesses complete in order), so
+// no workgroup barrier stands between forming and reading it.
 template <int Q, int N, int P>
-__device__ __forceinline__ void row_factors(const unsigned char* sXY, float* rf, int j0, int tid,
-                                            int nth) {
+__device__ __forceinline__ void row_factors(const unsigned char* sXY, float* rf, int j0,
+                                            int lane) {
     const float* s_cs = reinterpret_cast<const float*>(sXY + BwdCfg<Q, N, P>::XYB +
                                                        2 * BwdCfg<Q, N, P>::EB);
     const float* s_dt = s_cs + Q;
     const float cs_a = s_cs[j0], cs_b = s_cs[j0 + 63];
-    for (int i = tid; i < Q; i += nth) {
-        if (i < j0)
+    for (int i = lane; i < Q - 64; i += 64) {
+        if (i < j0) {
             rf[i] = s_dt[i] * exp2_fast((cs_a - s_cs[i]) * kLog2e);
-        else if (i >= j0 + 64)
-            rf[i] = exp2_fast((s_cs[i] - cs_b) * kLog2e);
+        } else {
+            const int t = i + 64;
+            rf[i] = exp2_fast((s_cs[t] - cs_b) * kLog2e);
+        }
     }
 }
 
@@ -402,12 +407,11 @@ __device__ __forceinline__ void bwd_strip_role(
     for (int s = 0; s < 2 * PAIRS; ++s) wacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     dma_barrier();  // the first head's rows have landed (copied by the state waves)
-    lds_barrier();  // ... and its row factors are formed (by the state waves)
 #pragma unroll 1
     for (int hh = 0; hh < hpg; ++hh) {
         const int h = g * hpg + hh;
         const int buf = hh & 1;
-        lds_barrier();  // this head's row factors are formed; the other buffer is free
+        // (this head's copies have landed: the barrier at the end of the previous head)
         if (!C_::EXT && hh > 0 && wave == 0 && lane == 0) {
             const float* sh = shares + (buf ^ 1) * 8;
             const size_t pi = ((size_t)(b * H + h - 1) * nC + c) * NJ + RJ;
@@ -417,7 +421,10 @@ __device__ __forceinline__ void bwd_strip_role(
         unsigned char* sXY = smem + buf * C_::ITEM;
         const float* s_cs = reinterpret_cast<const float*>(sXY + C_::XYB + 2 * C_::EB);
         const float* s_dt = s_cs + Q;
-        const float* s_rf = reinterpret_cast<const float*>(smem + C_::X_RF);
+        float* const rfw = reinterpret_cast<float*>(smem + C_::X_RF) + cw * (Q - 64);
+        row_factors<Q, N, P>(sXY, rfw, j0, lane);
+        asm volatile("" ::: "memory");  // the factors are read below by this wave only
+        const float* s_rf = rfw;
         // lane-dependent values re-derived every head from an opaque copy of the lane
         // index: the compiler recomputes the LDS addresses instead of keeping them live
         int ln = lane;
@@ -478,7 +485,7 @@ __device__ __forceinline__ void bwd_strip_role(
                 float4 f[2];
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    f[u] = rf4(s_rf, rt + 16 * u + 4 * g4);
+                    f[u] = rf4(s_rf, rt - 64 + 16 * u + 4 * g4);
                     f32x4 w = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kb = 0; kb < PKB; ++kb)
@@ -655,11 +662,8 @@ __device__ __forceinline__ void bwd_strip_role(
             lt = wavesum(lt);
             if (lane == 0) shares[buf * 8 + 2 * cw] = lt;
         }
-        lds_barrier();  // every state wave's copies of the next head have landed
-        if (hh + 1 < hpg)
-            row_factors<Q, N, P>(smem + (buf ^ 1) * C_::ITEM,
-                                 reinterpret_cast<float*>(smem + C_::X_RF), j0,
-                                 (int)threadIdx.x, 512);
+        lds_barrier();  // every state wave's copies of the next head have landed, and
+                        // every wave is done with this head's buffer and exchange
     }
     dma_barrier();
     if (!C_::EXT && wave == 0 && lane == 0) {
@@ -765,14 +769,11 @@ __device__ __forceinline__ void bwd_state_role(
     issue_item<Q, N, P>(x, dy, entry, exitg, cs, dtc, b, g * hpg, c, j0, Lc, T, H, nC, k_.lds0,
                         wave - 4, lane);
     dma_barrier();
-    row_factors<Q, N, P>(smem, reinterpret_cast<float*>(smem + C_::X_RF), j0,
-                         (int)threadIdx.x - 256, 256);
-    lds_barrier();
 #pragma unroll 1
     for (int hh = 0; hh < hpg; ++hh) {
         const int h = g * hpg + hh;
         const int buf = hh & 1;
-        lds_barrier();
+        // the other buffer (the previous head's) is free: the barrier at the end of that head
         if (hh + 1 < hpg)
             issue_item<Q, N, P>(x, dy, entry, exitg, cs, dtc, b, h + 1, c, j0, Lc, T, H, nC,
                                 k_.lds0 + (buf ^ 1) * C_::ITEM, wave - 4, lane);
@@ -876,15 +877,9 @@ __device__ __forceinline__ void bwd_state_role(
                 dbacc[nt] = mfma16(ld_tr(rows_at(sF, 32 * kb, NPR), ptn[nt], N16), xs8, dbacc[nt]);
         }
         // this wave's share of the next head's copies has landed; after the barrier every
-        // share has, and the next head's row factors are formed from its cs and dt (read
-        // after its first barrier).  A wave's vmcnt covers only its own copies, so the
-        // barrier is needed.
+        // share has (a wave's vmcnt covers only its own copies, so the barrier is needed)
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();
-        if (hh + 1 < hpg)
-            row_factors<Q, N, P>(smem + (buf ^ 1) * C_::ITEM,
-                                 reinterpret_cast<float*>(smem + C_::X_RF), j0,
-                                 (int)threadIdx.x, 512);
     }
     dma_barrier();
     issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, true, k_.lds0, wave, lane);
@@ -948,14 +943,10 @@ __device__ __forceinline__ void bwd_state_role_ext(
     issue_item<Q, N, P>(x, dy, nullptr, nullptr, cs, dtc, b, g * hpg, c, j0, Lc, T, H, nC,
                         k_.lds0, wave - 4, lane);
     dma_barrier();
-    row_factors<Q, N, P>(smem, reinterpret_cast<float*>(smem + C_::X_RF), j0,
-                         (int)threadIdx.x - 256, 256);
-    lds_barrier();
 #pragma unroll 1
     for (int hh = 0; hh < hpg; ++hh) {
         const int h = g * hpg + hh;
         const int buf = hh & 1;
-        lds_barrier();
         // (F B_j)[p] for p = 16 pt + 4 g4 .. + 3 of column j, and ob_j, oc_j
         const size_t cb = ((size_t)(b * H + h) * nC + c) * Q;
         const __bf16* fr = xfb + ((size_t)(b * T + t0 + jl) * H + h) * P + 4 * g4;
@@ -978,10 +969,6 @@ __device__ __forceinline__ void bwd_state_role_ext(
         lds_barrier();  // hand-off to the strip waves
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();
-        if (hh + 1 < hpg)
-            row_factors<Q, N, P>(smem + (buf ^ 1) * C_::ITEM,
-                                 reinterpret_cast<float*>(smem + C_::X_RF), j0,
-                                 (int)threadIdx.x, 512);
     }
     dma_barrier();
     issue_bc<Q, N, P>(Bm, Cm, b, g, t0, Lc, T, G, j0, true, k_.lds0, wave, lane);

@@ -8,7 +8,7 @@
 // One workgroup of 16 waves per (b, chunk, block of 16 heads).  dt is [B][T][H], so a
 // chunk's steps for a block of heads are Q rows of 64 contiguous bytes: the workgroup
 // reads them coalesced into an LDS tile [head][time], then wave w takes head w: a lane
-// holds Q/64 consecutive steps, scans them serially, and a 64-wide shuffle scan adds the
+// holds Q/64 consecutive steps, scans them serially, and a 64-wide DPP scan adds the
 // carry of the lanes before it.  It writes the chunk-major copy dt_chunk[b][h][c][i] that
 // the later kernels read contiguously, and the inclusive prefix sum cs of dt*A over the
 // chunk, both as contiguous rows (one vector store per lane each).  The kernel is
@@ -57,6 +57,15 @@ __device__ __forceinline__ float step_size(const float* dt, const void* raw, lon
                             : reinterpret_cast<const float*>(raw)[at];
         return softplus_step(bias ? v + bias[h] : v);
     }
+}
+
+// v moved by a DPP control CTRL (row_shr:n = 0x110 + n, row_bcast:15 = 0x142, row_bcast:31 =
+// 0x143) in the rows of ROWS (a 4-bit row mask); 0 in lanes without a source and in the
+// rows left out
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_or_zero(float v) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
 }
 
 template <int Q, DtSource SRC>
@@ -119,13 +128,17 @@ __global__ __launch_bounds__(kThreads) void chunk_cumsum_kernel(
         acc += fmaf(v[k], a, gap[lane * E + k]);
         run[k] = acc;
     }
-    // exclusive carry from the lanes before this one
+    // exclusive carry from the lanes before this one: an inclusive scan of the lane totals
+    // by DPP (VALU, no LDS round trips): shifts by 1, 2, 4, 8 inside each 16-lane row, then
+    // row 0's total into row 1 and row 2's into row 3 (row_bcast:15), then the first two
+    // rows' total into rows 2 and 3 (row_bcast:31)
     float incl = acc;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
-    }
+    incl += dpp_or_zero<0x111, 0xF>(incl);
+    incl += dpp_or_zero<0x112, 0xF>(incl);
+    incl += dpp_or_zero<0x114, 0xF>(incl);
+    incl += dpp_or_zero<0x118, 0xF>(incl);
+    incl += dpp_or_zero<0x142, 0xA>(incl);
+    incl += dpp_or_zero<0x143, 0xC>(incl);
     const float carry = incl - acc;
 #pragma unroll
     for (int k = 0; k < E; ++k) run[k] += carry;
