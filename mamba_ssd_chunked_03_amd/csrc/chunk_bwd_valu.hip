@@ -44,16 +44,80 @@ constexpr int kMaxNQ = 16;  // N / 16 for N <= 256
 template <typename Tin>
 __device__ __forceinline__ float ld(const Tin* p, size_t i) { return to_f32(p[i]); }
 
-// sum over the 16 lanes of an aligned group (every lane gets the total)
+// Cross-lane sums and scans in VALU operations (DPP row permutations and the gfx950 lane
+// swaps) rather than LDS-routed shuffles; a row is 16 aligned lanes.
+// v moved by the DPP control CTRL; 0 in lanes without a source
+template <int CTRL>
+__device__ __forceinline__ float dpp0(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_value(float v, int lane) {  // v of one lane, uniform
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+// sum over the lane's row (every lane of it gets the total): pairs (quad_perm [1,0,3,2]),
+// quad halves ([2,3,0,1]), the two quads of each half row (row_half_mirror), the halves
+// (row_mirror)
 __device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 16);
+    v += dpp0<0xB1>(v);
+    v += dpp0<0x4E>(v);
+    v += dpp0<0x141>(v);
+    return v + dpp0<0x140>(v);
+}
+// v plus v of the same lane in the other row of its pair (rows 0-1, 2-3): v_permlane16_swap
+// of v with itself gives the even row's v and the odd row's v in every lane of both
+__device__ __forceinline__ float add_row_pair(float v) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+// v plus v of the same lane in the other half of the wave (v_permlane32_swap likewise)
+__device__ __forceinline__ float add_half(float v) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float sum64(float v) { return add_half(add_row_pair(sum16(v))); }
+// inclusive suffix sum inside the lane's row (row_shl:1, 2, 4, 8)
+__device__ __forceinline__ float row_suffix(float v) {
+    v += dpp0<0x101>(v);
+    v += dpp0<0x102>(v);
+    v += dpp0<0x104>(v);
+    return v + dpp0<0x108>(v);
+}
+// inclusive suffix sum inside the lane's block of LPB lanes (16, 32 or 64)
+template <int LPB>
+__device__ __forceinline__ float block_suffix(float v, int lane) {
+    v = row_suffix(v);
+    if constexpr (LPB == 16) {
+        return v;
+    } else {
+        // the rows' totals sit in their first lanes
+        const float t1 = lane_value(v, 16), t2 = lane_value(v, 32), t3 = lane_value(v, 48);
+        const int row = lane >> 4;
+        if constexpr (LPB == 32) return v + (row == 0 ? t1 : row == 2 ? t3 : 0.f);
+        else return v + (row == 0 ? t1 + (t2 + t3) : row == 1 ? t2 + t3 : row == 2 ? t3 : 0.f);
+    }
+}
+// sum over the lane's block of LPB lanes
+template <int LPB>
+__device__ __forceinline__ float block_sum(float v) {
+    v = sum16(v);
+    if constexpr (LPB >= 32) v = add_row_pair(v);
+    if constexpr (LPB == 64) v = add_half(v);
     return v;
 }
-__device__ __forceinline__ float sum64(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+// sum of v over the lanes of the blocks (LPB lanes each) after the lane's block
+template <int LPB>
+__device__ __forceinline__ float later_blocks(float v, int lane) {
+    if constexpr (LPB == 64) {
+        return 0.f;
+    } else {
+        const float s = sum16(v);
+        const float r1 = lane_value(s, 16), r2 = lane_value(s, 32), r3 = lane_value(s, 48);
+        const int row = lane >> 4;
+        if constexpr (LPB == 32) return row < 2 ? r2 + r3 : 0.f;
+        else return row == 0 ? r1 + (r2 + r3) : row == 1 ? r2 + r3 : row == 2 ? r3 : 0.f;
+    }
 }
 
 template <typename Tin>
@@ -284,9 +348,9 @@ constexpr int kDdtHeads = 16;  // heads per workgroup of the ddt kernel, one wav
 constexpr int kDdtThreads = 64 * kDdtHeads;
 
 // One workgroup per (b, chunk, block of 16 heads); a wave per head, a lane L = Q/64
-// consecutive positions (each wave's work is a chain of dependent cross-lane scans: many
-// waves hide it).  The ddt rows of the block's heads are staged in LDS and
-// written as 64-byte runs of consecutive heads ([B][T][H] is head-minor).
+// consecutive positions (each wave's work is a chain of dependent cross-lane scans, in DPP
+// and lane-swap operations: many waves hide it).  The ddt rows of the block's heads are
+// staged in LDS and written as 64-byte runs of consecutive heads ([B][T][H] is head-minor).
 template <int Q>
 __global__ __launch_bounds__(kDdtThreads) void bwd_ddt_kernel(
     const float* __restrict__ dcs, const float* __restrict__ direct,
@@ -306,7 +370,7 @@ __global__ __launch_bounds__(kDdtThreads) void bwd_ddt_kernel(
     const int nvalid = (Lc + rows - 1) / rows;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int k0 = lane * L;
-    const int blk = lane / lpb, bend = (blk + 1) * lpb;
+    const int blk = lane / lpb;
     for (int hh = wave; hh < nh; hh += kDdtThreads / 64) {
         const int h = h0 + hh;
         const size_t item = ((size_t)b * H + h) * nC + c;
@@ -326,12 +390,7 @@ __global__ __launch_bounds__(kDdtThreads) void bwd_ddt_kernel(
             seg += v[m];
         }
         // inclusive suffix sum of the lanes' segment sums
-        float suf = seg;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const float up = __shfl_down(suf, o, 64);
-            if (lane + o < 64) suf += up;
-        }
+        const float suf = block_suffix<64>(seg, lane);
         float r = (suf - seg) + lt;
         float bv[4] = {0.f, 0.f, 0.f, 0.f};
         if (xs) {
@@ -352,14 +411,8 @@ __global__ __launch_bounds__(kDdtThreads) void bwd_ddt_kernel(
                 segcp += pl[0][m];
             }
             // suffix of rp - cp within the block, and the block's total of cp
-            float sufb = segb;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const float up = __shfl_down(sufb, o, 64);
-                if (lane + o < bend) sufb += up;
-            }
-#pragma unroll
-            for (int o = 1; o < lpb; o <<= 1) segcp += __shfl_xor(segcp, o, 64);
+            const float sufb = block_suffix<lpb>(segb, lane);
+            segcp = block_sum<lpb>(segcp);
             // K: for each plane s, the suffix over the lanes after this block
             float ks = 0.f;
 #pragma unroll
@@ -370,13 +423,8 @@ __global__ __launch_bounds__(kDdtThreads) void bwd_ddt_kernel(
                     for (int m = 0; m < 4; ++m)
                         if (valid(m)) ps += pl[1 + s2][m];
                 }
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const float up = __shfl_down(ps, o, 64);
-                    if (lane + o < 64) ps += up;
-                }
-                const float after = __shfl(ps, bend < 64 ? bend : 63, 64);
-                if (s2 < blk && bend < 64) ks += after;
+                const float after = later_blocks<lpb>(ps, lane);  // the later blocks
+                if (s2 < blk) ks += after;
             }
             r += (sufb - segb) + segcp + ks;
         }
