@@ -13,7 +13,10 @@
 // workgroup of 256 threads covers 1024 elements of one (b, h) state, four consecutive
 // elements per thread.  The loads of kUnroll chunks are issued before the dependent
 // multiply-adds so that several requests per thread are in flight; the kernel is bound by
-// HBM (it reads S and writes E once each, both in the input dtype).
+// HBM (it reads S and writes E once each, both in the input dtype).  The initial and final
+// states are [N][P] where the chunk states are [P][N]: where a workgroup's 1024 elements are
+// whole rows of p (N * P a multiple of 1024), they pass through LDS and are read and written
+// as 16-byte runs along p, instead of four 4-byte accesses 4P bytes apart per thread.
 #include "ssd_internal.h"
 
 namespace ssd {
@@ -59,18 +62,39 @@ __global__ __launch_bounds__(kThreads) void state_passing_kernel(
     const T* __restrict__ states, const float* __restrict__ cs,
     const float* __restrict__ init, T* __restrict__ entry, float* __restrict__ final_state,
     int nC, int Q, int P, int N, int tiles_per_state) {
+    constexpr int TILE = kThreads * 4;  // elements per workgroup
+    __shared__ __align__(16) float xs[TILE];
     const int NP = N * P;
     const int bh = blockIdx.x / tiles_per_state;
     const int tile = blockIdx.x % tiles_per_state;
     const int e = (tile * kThreads + threadIdx.x) * 4;  // element in the [P][N] state
-    if (e >= NP) return;
+    // whole rows of p per workgroup, and 16-byte aligned states (the same for every
+    // workgroup of the launch, so the barriers below are uniform)
+    const bool staged = NP % TILE == 0;
+    const bool stage_in = staged && init && ((uintptr_t)init & 15u) == 0;
+    const bool stage_out = staged && final_state && ((uintptr_t)final_state & 15u) == 0;
+    if (!staged && e >= NP) return;
     const int p = e / N, n = e % N;  // N % 4 == 0, so the four elements share p
+    // staged transfers: the workgroup's R = TILE / N rows of p from p0; thread t moves the
+    // 16-byte run at n = 4t / R, p = p0 + 4t % R of the [N][P] state (R is a multiple of 4)
+    const int R = TILE / N, p0 = tile * R;
+    const int tn = (int)(threadIdx.x * 4) / R, tr = (int)(threadIdx.x * 4) % R;
 
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     if (init) {
         const float* in = init + (size_t)bh * NP;  // [N][P]
-        s = make_float4(in[(n + 0) * P + p], in[(n + 1) * P + p], in[(n + 2) * P + p],
-                        in[(n + 3) * P + p]);
+        if (stage_in) {
+            const float4 v = *reinterpret_cast<const float4*>(in + (size_t)tn * P + p0 + tr);
+            xs[(tr + 0) * N + tn] = v.x;  // LDS in the workgroup's [p][n] order
+            xs[(tr + 1) * N + tn] = v.y;
+            xs[(tr + 2) * N + tn] = v.z;
+            xs[(tr + 3) * N + tn] = v.w;
+            __syncthreads();
+            s = *reinterpret_cast<const float4*>(xs + (e - tile * TILE));
+        } else {
+            s = make_float4(in[(n + 0) * P + p], in[(n + 1) * P + p], in[(n + 2) * P + p],
+                            in[(n + 3) * P + p]);
+        }
     }
     const size_t base = (size_t)bh * nC * NP + e;
     const float* csl = cs + (size_t)bh * nC * Q + (Q - 1);  // each chunk's total log decay
@@ -99,10 +123,19 @@ __global__ __launch_bounds__(kThreads) void state_passing_kernel(
     }
     if (final_state) {
         float* out = final_state + (size_t)bh * NP;  // [N][P]
-        out[(n + 0) * P + p] = s.x;
-        out[(n + 1) * P + p] = s.y;
-        out[(n + 2) * P + p] = s.z;
-        out[(n + 3) * P + p] = s.w;
+        if (stage_out) {
+            if (stage_in) __syncthreads();  // every thread has read its initial state
+            *reinterpret_cast<float4*>(xs + (e - tile * TILE)) = s;
+            __syncthreads();
+            *reinterpret_cast<float4*>(out + (size_t)tn * P + p0 + tr) =
+                make_float4(xs[(tr + 0) * N + tn], xs[(tr + 1) * N + tn], xs[(tr + 2) * N + tn],
+                            xs[(tr + 3) * N + tn]);
+        } else {
+            out[(n + 0) * P + p] = s.x;
+            out[(n + 1) * P + p] = s.y;
+            out[(n + 2) * P + p] = s.z;
+            out[(n + 3) * P + p] = s.w;
+        }
     }
 }
 

@@ -233,6 +233,40 @@ def test_deterministic_run_to_run():
     assert torch.equal(y1, y2) and torch.equal(f1, f2)
 
 
+def _at_4_byte_offset(t):
+    """A copy of t whose storage starts 4 bytes past a 16-byte boundary."""
+    buf = torch.empty(t.numel() + 4, dtype=t.dtype, device=t.device)
+    out = buf[1:1 + t.numel()].view(t.shape)
+    out.copy_(t)
+    assert out.data_ptr() % 16 == 4
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_states_at_4_byte_offsets_match_aligned(dtype):
+    """init_state and final_state need only 4-byte alignment.  The state kernel moves them
+    in 16-byte runs through LDS when they are 16-byte aligned and element by element
+    otherwise; both give the same bits, forward and backward (d_final, d_init)."""
+    w = variants(STRESS["slow_decay"], dtype=dtype)
+    dv = to_device(generate(w))
+    say(f"[state alignment] {dtype}")
+    args = (dv["x"], dv["dt"], dv["A"], dv["B"], dv["C"], dv["D"], w.chunk_len)
+    y0, f0 = binding.ssd_fwd(*args, init_state=dv["init_state"])
+    fin = _at_4_byte_offset(torch.zeros_like(f0))
+    y1, f1 = binding.ssd_fwd(*args, init_state=_at_4_byte_offset(dv["init_state"]),
+                             final_state=fin)
+    assert torch.equal(y0, y1) and torch.equal(f0, f1)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    dy = torch.randn(dv["x"].shape, generator=g).to(dv["x"])
+    dfin = torch.randn(f0.shape, generator=g).to(f0)
+    o0 = binding.ssd_bwd(*args, dy, init_state=dv["init_state"], d_final=dfin)
+    dinit = _at_4_byte_offset(torch.zeros_like(o0["d_init"]))
+    o1 = binding.ssd_bwd(*args, dy, init_state=_at_4_byte_offset(dv["init_state"]),
+                         d_final=_at_4_byte_offset(dfin), out={"d_init": dinit})
+    for k in o0:
+        assert torch.equal(o0[k], o1[k]), k
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_split_run_resumes_from_final_state(dtype):
     """Two segments, the second starting from the first's final state, reproduce one
