@@ -26,15 +26,22 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
 
-// EPT consecutive elements of a state row (EPT = 8 for bf16, 4 for fp32: one 16-byte access)
+// EPT consecutive elements of a state row, one access: 16 bytes (8 bf16 or 4 fp32) or, for
+// bf16 with EPT = 4, 8 bytes
 template <typename T, int EPT>
 __device__ __forceinline__ void load_run(const T* src, float (&v)[EPT]) {
     if constexpr (sizeof(T) == 2) {
-        static_assert(EPT == 8, "bf16 runs are 8 elements");
-        const uint4 w = *reinterpret_cast<const uint4*>(src);
-        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+        static_assert(EPT == 4 || EPT == 8, "bf16 runs are 4 or 8 elements");
+        uint32_t u[EPT / 2];
+        if constexpr (EPT == 8) {
+            const uint4 w = *reinterpret_cast<const uint4*>(src);
+            u[0] = w.x; u[1] = w.y; u[2] = w.z; u[3] = w.w;
+        } else {
+            const uint2 w = *reinterpret_cast<const uint2*>(src);
+            u[0] = w.x; u[1] = w.y;
+        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < EPT / 2; ++i) {
             v[2 * i] = __uint_as_float(u[i] << 16);
             v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
         }
@@ -47,11 +54,11 @@ __device__ __forceinline__ void load_run(const T* src, float (&v)[EPT]) {
 template <typename T, int EPT>
 __device__ __forceinline__ void store_run(T* dst, const float (&v)[EPT]) {
     if constexpr (sizeof(T) == 2) {
-        typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-        bf16x8_t o;
+        typedef __bf16 bf16xe_t __attribute__((ext_vector_type(EPT)));
+        bf16xe_t o;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = (__bf16)v[i];
-        *reinterpret_cast<bf16x8_t*>(dst) = o;
+        for (int i = 0; i < EPT; ++i) o[i] = (__bf16)v[i];
+        *reinterpret_cast<bf16xe_t*>(dst) = o;
     } else {
         *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
     }
@@ -59,17 +66,17 @@ __device__ __forceinline__ void store_run(T* dst, const float (&v)[EPT]) {
 
 // T: element type of the chunk states read and of the entry states written (fp32, or bf16
 // on the bf16 path, where both are matrix-core operands or their source); the running
-// state stays fp32.  A thread carries EPT consecutive elements of a row of p (16 bytes of
-// T per chunk).
+// state stays fp32.  A thread carries EPT consecutive elements of a row of p: 4, or 8 in
+// bf16 where the chunks are few (16-byte accesses; over long runs of chunks, with few
+// (b, h) states, the 8-byte form measured faster: twice the threads in flight).
 // REV walks the chunks last to first: the backward pass carries the entry-state gradients
 // the same way, dE_c = Z_c + exp(cs[c][Q-1]) dE_{c+1} from dE_nC = dL/d final state, and
 // stores dE_{c+1} (the gradient of chunk c's end state) for chunk c.
-template <typename T, bool REV>
+template <typename T, int EPT, bool REV>
 __global__ __launch_bounds__(kThreads) void state_passing_kernel(
     const T* __restrict__ states, const float* __restrict__ cs,
     const float* __restrict__ init, T* __restrict__ entry, float* __restrict__ final_state,
     int nC, int Q, int P, int N, int tiles_per_state) {
-    constexpr int EPT = 16 / (int)sizeof(T);
     constexpr int TILE = kThreads * EPT;  // elements per workgroup
     constexpr int RUNS = EPT / 4;         // 16-byte fp32 runs of a thread's elements
     __shared__ __align__(16) float xs[TILE];
@@ -163,23 +170,29 @@ __global__ __launch_bounds__(kThreads) void state_passing_kernel(
     }
 }
 
+// bf16 states over at most kLongRun chunks take 8 elements per thread, longer runs 4
+constexpr int kLongRun = 64;
+
+template <typename T, int EPT, bool REV>
+hipError_t launch_passing_e(const Shape& s, const void* states, const float* cs,
+                            const float* init, void* entry, float* final_state, hipStream_t st) {
+    const int NP = s.N * s.P;
+    const int tiles = (NP + kThreads * EPT - 1) / (kThreads * EPT);
+    const unsigned blocks = (unsigned)((size_t)s.B * s.H * tiles);
+    if (blocks == 0) return hipSuccess;
+    state_passing_kernel<T, EPT, REV><<<blocks, kThreads, 0, st>>>(
+        (const T*)states, cs, init, (T*)entry, final_state, s.nC, s.Q, s.P, s.N, tiles);
+    return hipGetLastError();
+}
+
 template <bool REV>
 hipError_t launch_passing_t(const Shape& s, ssd_dtype dtype, const void* states, const float* cs,
                             const float* init, void* entry, float* final_state, hipStream_t st) {
-    const int NP = s.N * s.P;
-    const int ept = dtype == SSD_BF16 ? 8 : 4;  // elements per thread
-    const int tiles = (NP + kThreads * ept - 1) / (kThreads * ept);
-    const unsigned blocks = (unsigned)((size_t)s.B * s.H * tiles);
-    if (blocks == 0) return hipSuccess;
-    if (dtype == SSD_BF16)
-        state_passing_kernel<__bf16, REV><<<blocks, kThreads, 0, st>>>(
-            (const __bf16*)states, cs, init, (__bf16*)entry, final_state, s.nC, s.Q, s.P, s.N,
-            tiles);
-    else
-        state_passing_kernel<float, REV><<<blocks, kThreads, 0, st>>>(
-            (const float*)states, cs, init, (float*)entry, final_state, s.nC, s.Q, s.P, s.N,
-            tiles);
-    return hipGetLastError();
+    if (dtype != SSD_BF16)
+        return launch_passing_e<float, 4, REV>(s, states, cs, init, entry, final_state, st);
+    if (s.nC <= kLongRun)
+        return launch_passing_e<__bf16, 8, REV>(s, states, cs, init, entry, final_state, st);
+    return launch_passing_e<__bf16, 4, REV>(s, states, cs, init, entry, final_state, st);
 }
 
 }  // namespace
