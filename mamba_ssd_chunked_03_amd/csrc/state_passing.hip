@@ -67,8 +67,8 @@ __device__ __forceinline__ void store_run(T* dst, const float (&v)[EPT]) {
 // T: element type of the chunk states read and of the entry states written (fp32, or bf16
 // on the bf16 path, where both are matrix-core operands or their source); the running
 // state stays fp32.  A thread carries EPT consecutive elements of a row of p: 4, or 8 in
-// bf16 where the chunks are few (16-byte accesses; over long runs of chunks, with few
-// (b, h) states, the 8-byte form measured faster: twice the threads in flight).
+// bf16 where the chunks are few (16-byte accesses; over runs of 64 chunks and more, with
+// few (b, h) states, the 8-byte form measured faster: twice the threads in flight).
 // REV walks the chunks last to first: the backward pass carries the entry-state gradients
 // the same way, dE_c = Z_c + exp(cs[c][Q-1]) dE_{c+1} from dE_nC = dL/d final state, and
 // stores dE_{c+1} (the gradient of chunk c's end state) for chunk c.
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void state_passing_kernel(
 }
 
 // bf16 states over at most kLongRun chunks take 8 elements per thread, longer runs 4
-constexpr int kLongRun = 64;
+constexpr int kLongRun = 32;
 
 template <typename T, int EPT, bool REV>
 hipError_t launch_passing_e(const Shape& s, const void* states, const float* cs,
