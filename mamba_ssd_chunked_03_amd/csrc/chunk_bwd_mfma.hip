@@ -1069,9 +1069,9 @@ __global__ __launch_bounds__(512) void chunk_bwd_mfma_kernel(
 #undef SSD_STRIP
         }
     } else {
-        // the state waves issue every copy, which the strip waves wait on: they go first
-        // when both are ready to issue (the saved backward at 2.7B: 538 -> 519 us)
-        __builtin_amdgcn_s_setprio(3);
+        // both roles at the default wave priority: the strip waves' products are the longer
+        // chain of every head, and raising the state waves (which issue the copies) above
+        // them measured slower
         if constexpr (C_::EXT)
             bwd_state_role_ext<Q, N, P>(k_, smem, x, Bm, Cm, dtc, cs, dy, xfb, direct, dcs, dBs,
                                         dCs, dB, dC);
