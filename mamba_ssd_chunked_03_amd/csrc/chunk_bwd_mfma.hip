@@ -136,20 +136,26 @@ __device__ __forceinline__ float wavesum(float v) {
 // base + 16 L), so the swizzle is applied on the source side: slot `sl` of LDS row dr
 // receives piece sl ^ (dr % 16) (dr % PPRX for rows of fewer than 16 pieces; the XOR keeps
 // a piece inside its aligned group of 16, and lane_part's row offset rl < 16 reads the
-// same swizzle).  nrows * PPRX is a multiple of 64.
+// same swizzle).  nrows * PPRX is a multiple of 64.  A wave's successive instructions
+// are NW * 64 / PPRX rows apart, a multiple of the swizzle period, so the lane's source
+// offset only advances by that many rows: it is formed once and then stepped.
 template <int PPRX, int NW>
 __device__ __forceinline__ void issue_rows(u32x4 rsrc, unsigned rowb, int src_row0, uint32_t lds,
                                            int dst_row0, int nrows, int wave, int lane,
                                            unsigned colb = 0) {
     constexpr int SWM = (PPRX < 16 ? PPRX : 16) - 1;
+    constexpr int RSTEP = NW * 64 / PPRX;  // rows between a wave's instructions
+    static_assert(NW * 64 % PPRX == 0 && RSTEP % (SWM + 1) == 0, "stepped offsets");
     const int ninst = nrows * PPRX / 64;
     const uint32_t base = lds + (unsigned)dst_row0 * PPRX * 16u;
+    const int m = wave * 64 + lane;
+    const int r = m / PPRX, sl = m % PPRX;
+    unsigned voff =
+        (unsigned)(src_row0 + r) * rowb + colb + (unsigned)(sl ^ ((dst_row0 + r) & SWM)) * 16u;
+    const unsigned vstep = (unsigned)RSTEP * rowb;
     for (int k = wave; k < ninst; k += NW) {
-        const int m = k * 64 + lane;
-        const int r = m / PPRX, sl = m % PPRX;
-        const int dr = dst_row0 + r;
-        dma16(rsrc, base + (unsigned)k * 1024u,
-              (unsigned)(src_row0 + r) * rowb + colb + (unsigned)(sl ^ (dr & SWM)) * 16u);
+        dma16(rsrc, base + (unsigned)k * 1024u, voff);
+        voff += vstep;
     }
 }
 
@@ -311,10 +317,11 @@ struct BwdCtx {
 // ------------------------------------------------------------------ strip waves
 // M strips, W accumulated over heads, C B^T on the strips, the W.G sums, the diagonal part
 // of dx; they finish dx and the per-row results of every head.  Instantiated per row block
-// (RJ), so that the block layout is known at compile time:
+// (RJ) and column tile (CW), so that the block layout and which tiles inside J are causal,
+// masked or diagonal are known at compile time:
 //   row strip  blocks k < RSP: x rows [32k, 32k + 32), the last two inside J
 //   column strip blocks k < CSP: dy rows [j0 + 32k, +32), the first two inside J
-template <int Q, int N, int P, int RJ>
+template <int Q, int N, int P, int RJ, int CW>
 __device__ __forceinline__ void bwd_strip_role(
     const BwdCtx& k_, unsigned char* smem, const __bf16* x, const __bf16* Bm, const __bf16* Cm,
     const float* dtc, const float* cs, const float* D, const __bf16* entry, const __bf16* exitg,
@@ -329,7 +336,8 @@ __device__ __forceinline__ void bwd_strip_role(
     static_assert(RSP + CSP == PAIRS, "layout");
     const int b = k_.b, g = k_.g, c = k_.c, t0 = k_.t0, Lc = k_.Lc;
     const int hpg = k_.hpg, T = k_.T, H = k_.H, G = k_.G, nC = k_.nC;
-    const int wave = k_.wave, cw = k_.cw, lane = k_.lane;
+    const int wave = k_.wave, lane = k_.lane;
+    constexpr int cw = CW;
     float* const shares = reinterpret_cast<float*>(smem + C_::X_SH);
 
     // C B^T on the strips, rounded to bf16: G^T[i][j] = B_i . C_j and G[t][j] = C_t . B_j
@@ -558,14 +566,23 @@ __device__ __forceinline__ void bwd_strip_role(
                 yj[kb] = ld_nat(rows_at(sXY, jb + 64, PPR) + z, pnp[kb]);
             }
         }
+        // The role is specialised per column tile: against the wave's 16 columns (tile CW of
+        // J), the 16-row tile t of J lies wholly before them (t < CW: every pair causal in
+        // W^T, none in V), on the diagonal (t == CW: masked per element) or wholly after
+        // (t > CW: the reverse).  Only the diagonal tile needs the mask, and the wholly
+        // masked halves (their products, exps and sums) are not formed at all.
 #pragma unroll
         for (int k = RSO; k < RSP + 2; ++k) {
             const bool isrs = k < RSP;
+            const int kk = isrs ? k - RSO : k - RSP;                 // 32-row block of J
             const int rbase = isrs ? 32 * k : j0 + 32 * (k - RSP);  // chunk row of the block
             const int rho = isrs ? rbase : rbase + 64;              // its LDS row (unscaled)
-            uint32_t ub[4];
+            uint32_t ub[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
+                const int t = 2 * kk + u;  // 16-row tile of J
+                if (isrs ? t > CW : t < CW) continue;  // wholly masked
+                const bool diag = t == CW;
                 f32x4 m = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < PKB; ++kb)
@@ -582,12 +599,14 @@ __device__ __forceinline__ void bwd_strip_role(
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     if (isrs) {  // W^T[i][j] = dt_i exp(cs_j - cs_i) M^T[i][j], i <= j
-                        const float e = (jl - (r0 + q) >= 0) ? exp2_fast((csj - cr[q]) * kLog2e) : 0.f;
+                        const float x_ = exp2_fast((csj - cr[q]) * kLog2e);
+                        const float e = (!diag || jl - (r0 + q) >= 0) ? x_ : 0.f;
                         const float w = dr[q] * e * m[q];
                         wacc[2 * k + u][q] += w;
                         rs_in = fmaf(w, gq[q], rs_in);
                     } else {  // V[t][j] = exp(cs_t - cs_j) M[t][j], t >= j; W = dt_j V
-                        const float e = ((r0 + q) - jl >= 0) ? exp2_fast((cr[q] - csj) * kLog2e) : 0.f;
+                        const float x_ = exp2_fast((cr[q] - csj) * kLog2e);
+                        const float e = (!diag || (r0 + q) - jl >= 0) ? x_ : 0.f;
                         const float v = e * m[q];
                         wacc[2 * k + u][q] = fmaf(dtj, v, wacc[2 * k + u][q]);
                         csu = fmaf(v, gq[q], csu);
@@ -602,8 +621,10 @@ __device__ __forceinline__ void bwd_strip_role(
                     ub[2 * u + 1] = pack_bf16(uq[2], uq[3]);
                 }
             }
-            if (!isrs) {  // dx^T[p][j] += sum_t dy[t][p] U[t][j]
-                const bf16x8 bu = __builtin_bit_cast(bf16x8, make_uint4(ub[0], ub[1], ub[2], ub[3]));
+            // dx^T[p][j] += sum_t dy[t][p] U[t][j], unless both halves are masked
+            if (!isrs && 2 * kk + 1 >= CW) {
+                const bf16x8 bu =
+                    __builtin_bit_cast(bf16x8, make_uint4(ub[0], ub[1], ub[2], ub[3]));
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt) {
                     dxa[pt] = mfma16(ld_tr(rows_at(sXY, rho, PPR), ptp[pt], R16), bu, dxa[pt]);
@@ -1053,19 +1074,21 @@ __global__ __launch_bounds__(512) void chunk_bwd_mfma_kernel(
     k_.lane = threadIdx.x & 63;
     k_.lds0 = lds_addr(smem);
     // the two roles run the same sequence of barriers; the strip role is instantiated per
-    // row block
+    // row block and column tile
     if (k_.wave < 4) {
-        switch (k_.rj) {
-#define SSD_STRIP(RJ)                                                                        \
-    case RJ:                                                                                 \
+        switch (k_.rj * 4 + k_.cw) {
+#define SSD_STRIP(RJ, CW)                                                                    \
+    case RJ * 4 + CW:                                                                        \
         if constexpr (RJ < C_::NJ)                                                           \
-            bwd_strip_role<Q, N, P, RJ>(k_, smem, x, Bm, Cm, dtc, cs, D, entry, exitg, dy, dx, \
-                                        dcs, direct, xs, lt_part, dd_part);                  \
+            bwd_strip_role<Q, N, P, RJ, CW>(k_, smem, x, Bm, Cm, dtc, cs, D, entry, exitg, dy, \
+                                            dx, dcs, direct, xs, lt_part, dd_part);          \
         break;
-            SSD_STRIP(0)
-            SSD_STRIP(1)
-            SSD_STRIP(2)
-            SSD_STRIP(3)
+#define SSD_STRIP4(RJ) SSD_STRIP(RJ, 0) SSD_STRIP(RJ, 1) SSD_STRIP(RJ, 2) SSD_STRIP(RJ, 3)
+            SSD_STRIP4(0)
+            SSD_STRIP4(1)
+            SSD_STRIP4(2)
+            SSD_STRIP4(3)
+#undef SSD_STRIP4
 #undef SSD_STRIP
         }
     } else {
