@@ -368,14 +368,25 @@ ssd_status ssd_block_epilogue(const ssd_dims* dims, ssd_dtype dtype, const void*
  * layer and ssd_fwd's own workspace. */
 size_t ssd_block_fwd_workspace_size(const ssd_dims* dims, ssd_dtype dtype, int chunk_len);
 
+/* 1 if ssd_block_fwd applies the gate and the norm inside the chunk scan for these sizes
+ * (bf16 on the matrix-core scan, headdim 32 or 64, every norm group inside one head: S =
+ * H*P / norm_groups channels, S a multiple of 16 that divides P, and 8-byte aligned
+ * projection rows), given 16-byte aligned norm_w and norm_b; 0 otherwise, also for invalid
+ * sizes.  Reads no device state. */
+int ssd_block_fwd_norm_in_scan(const ssd_dims* dims, ssd_dtype dtype, int chunk_len,
+                               int norm_groups);
+
 /* The block between the projections: ssd_block_prologue on the x|B|C and dt_raw columns of
  * zxbcdt ([B][T] rows of 2*H*P + 2*G*N + H values, [z | x | B | C | dt_raw], contiguous,
  * 16-byte aligned), ssd_fwd (A, D, chunk_len, init_state, final_state as there), then
  * ssd_block_epilogue with z from the first H*P columns; out [B][T][H*P] in `dtype`.  The
  * step sizes softplus(dt_raw + dt_bias) are made inside the forward's cumsum pass, straight
- * from the dt_raw columns (the same arithmetic as ssd_block_prologue's, so the result is
- * that of the three calls bit for bit), and dt is never stored.  Errors as the three calls,
- * all checked before the first launch. */
+ * from the dt_raw columns (the same arithmetic as ssd_block_prologue's), and dt is never
+ * stored.  Where ssd_block_fwd_norm_in_scan says so and norm_w, norm_b are 16-byte aligned,
+ * the gate and the norm run in the chunk scan's store (y is never stored, no epilogue pass):
+ * the result then differs from the three calls only by the rounding of y to `dtype` before
+ * the norm; otherwise it equals the three calls bit for bit.  Errors as the three calls, all
+ * checked before the first launch. */
 ssd_status ssd_block_fwd(const ssd_dims* dims, ssd_dtype dtype, const void* zxbcdt,
                          const float* conv_w, const float* conv_b, int conv_k,
                          const float* dt_bias, const float* A, const float* D, int chunk_len,

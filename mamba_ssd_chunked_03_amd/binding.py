@@ -19,7 +19,7 @@ EXPORTED = ("ssd_status_string", "ssd_fwd_workspace_size", "ssd_fwd", "ssd_chunk
             "ssd_chunk_scan", "ssd_decode_step", "ssd_bwd_workspace_size", "ssd_bwd",
             "ssd_block_prologue", "ssd_block_epilogue", "ssd_block_fwd_workspace_size",
             "ssd_block_fwd", "ssd_fwd_varlen_workspace_size", "ssd_fwd_varlen",
-            "ssd_bwd_saved", "ssd_fwd_noalloc")
+            "ssd_bwd_saved", "ssd_fwd_noalloc", "ssd_block_fwd_norm_in_scan")
 
 
 class SsdDims(ctypes.Structure):
@@ -86,6 +86,8 @@ def library(path=LIB_PATH):
     lib.ssd_block_epilogue.argtypes = [dims, i, vp, vp, i64, fp, fp, i, i, f, vp, vp]
     lib.ssd_block_fwd_workspace_size.restype = sz
     lib.ssd_block_fwd_workspace_size.argtypes = [dims, i, i]
+    lib.ssd_block_fwd_norm_in_scan.restype = i
+    lib.ssd_block_fwd_norm_in_scan.argtypes = [dims, i, i, i]
     lib.ssd_block_fwd.restype = i
     lib.ssd_block_fwd.argtypes = [dims, i, vp, fp, fp, i, fp, fp, fp, i, fp, fp, fp, i, i, f, vp,
                                   fp, vp, sz, vp]
@@ -638,6 +640,11 @@ def ssd_block_epilogue(y, z, norm_w, norm_b, norm_groups, rms=False, eps=1e-5, d
 def ssd_block_fwd_workspace_size(dims, dtype, chunk_len):
     return int(library().ssd_block_fwd_workspace_size(ctypes.byref(dims), int(dtype),
                                                       int(chunk_len)))
+
+
+def ssd_block_fwd_norm_in_scan(dims, dtype, chunk_len, norm_groups):
+    return bool(library().ssd_block_fwd_norm_in_scan(ctypes.byref(dims), int(dtype),
+                                                     int(chunk_len), int(norm_groups)))
 
 
 def ssd_block_fwd(zxbcdt, conv_w, conv_b, dt_bias, A, D, chunk_len, norm_w, norm_b,

@@ -101,18 +101,6 @@ __device__ __forceinline__ float dot8(bf16x8 a, bf16x8 b) {
     s = fmaf(bf16_lo(x.w), bf16_lo(y.w), s);
     return fmaf(bf16_hi(x.w), bf16_hi(y.w), s);
 }
-// Sum over the four lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48), the same value in every
-// lane.  Two VALU exchanges instead of LDS-routed shuffles: v_permlane32_swap of v with
-// itself yields (lower half, upper half) in every lane, so their sum is v + (v at l ^ 32);
-// v_permlane16_swap likewise pairs the even and odd 16-lane rows.
-__device__ __forceinline__ float colsum(float v) {
-    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
-                                                    false, false);
-    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
-                                                    false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
 // v plus v from another lane of its 16-lane row, by a DPP row permutation
 template <int CTRL>
 __device__ __forceinline__ float add_dpp(float v) {

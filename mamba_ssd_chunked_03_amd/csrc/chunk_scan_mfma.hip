@@ -222,12 +222,14 @@ __device__ __forceinline__ void issue_item(const __bf16* x, const __bf16* E, con
         dma16(raw_rsrc(dtc + sb * Q, C_::FB), lds + C_::XB + C_::EB + C_::FB, lane * 16u);
 }
 
-template <int Q, int N, int P>
+// With GATE set, the store applies the block's gate and normalisation (GateNorm) and
+// writes the block output in place of y.
+template <int Q, int N, int P, bool GATE = false>
 __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ Cm, const float* __restrict__ dtc,
     const float* __restrict__ cs, const float* __restrict__ D, const __bf16* __restrict__ E,
     const uint4* __restrict__ gram, __bf16* __restrict__ y, int T, int H, int G, int nC,
-    int nslots) {
+    int nslots, GateNorm gn) {
     using C_ = ScanCfg<Q, N, P>;
     constexpr int PT = C_::PT, NK = C_::NK, PPR = C_::PPR, NPR = C_::NPR, NB = C_::NB,
                   NB0 = C_::NB0;
@@ -275,6 +277,26 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
             cf1[kk] = __builtin_bit_cast(bf16x8, buf_load16(cr, (unsigned)j1 * crow + col));
         }
     };
+    // GATE: rows j0, j1 of the item's z (each lane's 4 channels of each p-tile), loaded at
+    // the end of the item before, after its stores
+    uint2 zq0[GATE ? PT : 1], zq1[GATE ? PT : 1];
+    const unsigned zrowb = (unsigned)(gn.z_stride * 2);
+    auto load_z = [&](int slot) {
+        const int u = slot / hpg;
+        const int cc = u % nC, gg = (u / nC) % G, bb = u / nC / G;
+        const int hh = gg * hpg + slot % hpg;
+        const int tt = cc * Q;
+        const __amdgpu_buffer_rsrc_t zr = make_rsrc(
+            reinterpret_cast<const __bf16*>(gn.z) + ((size_t)bb * T + tt) * gn.z_stride +
+                (size_t)hh * P,
+            (unsigned)min(Q, T - tt) * zrowb);
+#pragma unroll
+        for (int p = 0; p < PT; ++p) {
+            const unsigned col = (unsigned)(p * 16 + 4 * g4) * 2u;
+            zq0[p] = buf_load8(zr, (unsigned)j0 * zrowb + col);
+            zq1[p] = buf_load8(zr, (unsigned)j1 * zrowb + col);
+        }
+    };
     uint4 gf0[NB0], gf1[NB];  // Gram fragments of (tile0, ib), (tile1, ib)
     int cur_unit = -1;
 
@@ -282,6 +304,7 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
     if (C_::NBUF == 3 && lo + 1 < hi)
         issue_item<Q, N, P>(x, E, cs, dtc, hi - 2, hpg, T, H, G, nC, lds0 + C_::ITEM, wave, lane);
     if constexpr (!CRES) load_c(hi - 1);
+    if constexpr (GATE) load_z(hi - 1);
     int buf = 0;  // buffer of the current item
 #pragma unroll 1
     for (int n = 0; n < hi - lo; ++n) {
@@ -294,7 +317,15 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
         // two the previous item's stores.
         // (Where the C rows are not held, this item's were issued last, after all of that.)
         constexpr int CX = CRES ? 0 : 2 * NK;
-        if (C_::NBUF == 3) {
+        if constexpr (GATE) {
+            // the item's z rows were issued last: wait for everything, then mark them ready
+            // here, so that no later wait (the compiler's, at their use) also covers the
+            // copies issued during this item
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+            for (int p = 0; p < PT; ++p)
+                asm volatile("" ::"v"(zq0[p].x), "v"(zq0[p].y), "v"(zq1[p].x), "v"(zq1[p].y));
+        } else if (C_::NBUF == 3) {
             const bool more = n + 1 < hi - lo;
             if (n == 0 && !more)
                 asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
@@ -510,10 +541,98 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
                     buf_store8(yr, (unsigned)j * rowb + (p * 16 + 4 * g4) * 2u, o[p]);
             }
         };
-        store_tile(acc0, j0);
-        store_tile(acc1, j1);
+        if constexpr (GATE) {
+            // out = norm(y * SiLU(z)) per token over groups of S = P / gph channels: a row's
+            // P channels sit in the four lane groups of its lanes (p-tile p, channels
+            // p * 16 + 4 g4 + 0..3), so a group's sums are per-lane sums over its p-tiles,
+            // summed over the lane groups (colsum); mean, then the squared deviations
+            const int gph = gn.groups_per_head;
+            const int ppg = PT / gph;  // p-tiles per group
+            const float inv_s = 1.f / (float)(16 * ppg);
+            const float* wh = gn.w + (size_t)h * P;
+            const float* bh = gn.b ? gn.b + (size_t)h * P : nullptr;
+            auto gate_tile = [&](const f32x4* acc, const uint2* zt, int j) {
+                float v[PT][4];
+#pragma unroll
+                for (int p = 0; p < PT; ++p) {
+                    const int p0 = p * 16 + 4 * g4;
+                    const uint2 xv = *reinterpret_cast<const uint2*>(bx + swz_off(j, p0, PPR));
+                    const uint2 zq = zt[p];
+                    const float xs[4] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y)};
+                    const float zs[4] = {bf16_lo(zq.x), bf16_hi(zq.x), bf16_lo(zq.y), bf16_hi(zq.y)};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)  // SiLU(z) = z / (1 + exp(-z)), v_rcp_f32
+                        v[p][e] = fmaf(dh, xs[e], acc[p][e]) *
+                                  (zs[e] * __builtin_amdgcn_rcpf(1.f + __expf(-zs[e])));
+                }
+                // group sums over the tile's p-tiles (the group of p-tile p is p / ppg)
+                auto group_sum = [&](const float (&ps)[PT], float (&gs)[PT]) {
+#pragma unroll
+                    for (int p = 0; p < PT; ++p) {
+                        float t = 0.f;
+#pragma unroll
+                        for (int q2 = 0; q2 < PT; ++q2)
+                            t += (q2 / ppg == p / ppg) ? ps[q2] : 0.f;
+                        gs[p] = t;
+                    }
+                };
+                float ps[PT], mean[PT], var[PT];
+#pragma unroll
+                for (int p = 0; p < PT; ++p) {
+                    ps[p] = gn.rms ? 0.f : colsum((v[p][0] + v[p][1]) + (v[p][2] + v[p][3]));
+                }
+                group_sum(ps, mean);
+#pragma unroll
+                for (int p = 0; p < PT; ++p) {
+                    mean[p] *= inv_s;
+                    float sq = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float dv = v[p][e] - mean[p];
+                        sq = fmaf(dv, dv, sq);
+                    }
+                    ps[p] = colsum(sq);
+                }
+                group_sum(ps, var);
+                uint2 o[PT];
+#pragma unroll
+                for (int p = 0; p < PT; ++p) {
+                    const int p0 = p * 16 + 4 * g4;
+                    const float rstd = __builtin_amdgcn_rsqf(var[p] * inv_s + gn.eps);
+                    const float4 w4 = *reinterpret_cast<const float4*>(wh + p0);
+                    const float4 b4 = (bh && !gn.rms) ? *reinterpret_cast<const float4*>(bh + p0)
+                                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+                    const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+                    const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+                    float ov[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        ov[e] = fmaf((v[p][e] - mean[p]) * rstd, wv[e], bv[e]);
+                    o[p] = make_uint2(pack_bf16(ov[0], ov[1]), pack_bf16(ov[2], ov[3]));
+                }
+                if constexpr (PT % 2 == 0) {
+#pragma unroll
+                    for (int q = 0; q < PT / 2; ++q) {
+                        const int p0 = 32 * q + 16 * (g4 & 1) + 8 * (g4 >> 1);
+                        buf_store16(yr, (unsigned)j * rowb + p0 * 2u,
+                                    pair_runs(o[2 * q], o[2 * q + 1]));
+                    }
+                } else {
+#pragma unroll
+                    for (int p = 0; p < PT; ++p)
+                        buf_store8(yr, (unsigned)j * rowb + (p * 16 + 4 * g4) * 2u, o[p]);
+                }
+            };
+            gate_tile(acc0, zq0, j0);
+            gate_tile(acc1, zq1, j1);
+        } else {
+            store_tile(acc0, j0);
+            store_tile(acc1, j1);
+        }
         if constexpr (!CRES)
             if (n + 1 < hi - lo) load_c(sl - 1);
+        if constexpr (GATE)
+            if (n + 1 < hi - lo) load_z(sl - 1);
         if (C_::NBUF == 1 && n + 1 < hi - lo) {
             lds_barrier();  // every wave is done with the buffer
             issue_item<Q, N, P>(x, E, cs, dtc, sl - 1, hpg, T, H, G, nC, lds0, wave, lane);
@@ -524,12 +643,13 @@ __global__ __launch_bounds__((ScanCfg<Q, N, P>::NTH)) void chunk_scan_mfma_kerne
 
 // ---------------------------------------------------------------- dispatch
 
-template <int Q, int N, int P>
+template <int Q, int N, int P, bool GATE = false>
 hipError_t launch_scan_t(const Shape& s, const void* x, const void* Cm, const float* dtc,
                          const float* cs, const float* D, const void* E, const void* gram,
-                         void* y, hipStream_t st) {
+                         void* y, hipStream_t st, const GateNorm* gate) {
     using C_ = ScanCfg<Q, N, P>;
-    const auto kern = chunk_scan_mfma_kernel<Q, N, P>;
+    const auto kern = chunk_scan_mfma_kernel<Q, N, P, GATE>;
+    const GateNorm gn = gate ? *gate : GateNorm{nullptr, 0, nullptr, nullptr, 1, 0, 0.f};
     // per device: allow the dynamic LDS size, and size the persistent grid to what is
     // resident at once (a multiple of 8 workgroups, one run of items each)
     static DeviceSlots grid_of;
@@ -539,7 +659,7 @@ hipError_t launch_scan_t(const Shape& s, const void* x, const void* Cm, const fl
     const int nslots = s.B * s.G * s.nC * (s.H / s.G);
     kern<<<grid, C_::NTH, C_::LDS, st>>>(
         (const __bf16*)x, (const __bf16*)Cm, dtc, cs, D, (const __bf16*)E, (const uint4*)gram,
-        (__bf16*)y, s.T, s.H, s.G, s.nC, nslots);
+        (__bf16*)y, s.T, s.H, s.G, s.nC, nslots, gn);
     return hipGetLastError();
 }
 
@@ -558,7 +678,8 @@ hipError_t launch_gram_t(const Shape& s, const void* Bm, const void* Cm, void* g
 }
 
 using ScanFn = hipError_t (*)(const Shape&, const void*, const void*, const float*, const float*,
-                              const float*, const void*, const void*, void*, hipStream_t);
+                              const float*, const void*, const void*, void*, hipStream_t,
+                              const GateNorm*);
 using GramFn = hipError_t (*)(const Shape&, const void*, const void*, void*, hipStream_t);
 
 template <int Q, int N>
@@ -578,6 +699,25 @@ ScanFn pick_scan_q(const Shape& s) {
         case 64: return pick_scan_qn<Q, 64>(s);
         case 128: return pick_scan_qn<Q, 128>(s);
         case 256: return pick_scan_qn<Q, 256>(s);
+    }
+    return nullptr;
+}
+// the gated store: head sizes whose p-tiles split into 1, 2 or 4 groups of 16 channels or more
+template <int Q, int N>
+ScanFn pick_scan_gate_qn(const Shape& s) {
+    switch (s.P) {
+        case 32: return launch_scan_t<Q, N, 32, true>;
+        case 64: return launch_scan_t<Q, N, 64, true>;
+    }
+    return nullptr;
+}
+template <int Q>
+ScanFn pick_scan_gate_q(const Shape& s) {
+    switch (s.N) {
+        case 32: return pick_scan_gate_qn<Q, 32>(s);
+        case 64: return pick_scan_gate_qn<Q, 64>(s);
+        case 128: return pick_scan_gate_qn<Q, 128>(s);
+        case 256: return pick_scan_gate_qn<Q, 256>(s);
     }
     return nullptr;
 }
@@ -607,6 +747,15 @@ ScanFn pick_scan(const Shape& s) {
     }
     return nullptr;
 }
+ScanFn pick_scan_gate(const Shape& s) {
+    if (!scan_offsets_fit(s)) return nullptr;
+    switch (s.Q) {
+        case 64: return pick_scan_gate_q<64>(s);
+        case 128: return pick_scan_gate_q<128>(s);
+        case 256: return pick_scan_gate_q<256>(s);
+    }
+    return nullptr;
+}
 GramFn pick_gram(const Shape& s) {
     if (!scan_offsets_fit(s)) return nullptr;
     switch (s.Q) {
@@ -620,6 +769,12 @@ GramFn pick_gram(const Shape& s) {
 }  // namespace
 
 bool chunk_scan_mfma_supported(const Shape& s) { return pick_scan(s) != nullptr; }
+
+bool chunk_scan_gate_supported(const Shape& s, int groups_per_head) {
+    const int pt = s.P / 16;
+    return pick_scan_gate(s) != nullptr && groups_per_head >= 1 && groups_per_head <= pt &&
+           pt % groups_per_head == 0;
+}
 
 size_t chunk_gram_bytes(const Shape& s) {
     if (!chunk_scan_mfma_supported(s)) return 0;
@@ -636,11 +791,13 @@ hipError_t launch_chunk_gram(const Shape& s, const void* Bm, const void* Cm, voi
 
 hipError_t launch_chunk_scan_mfma(const Shape& s, const void* x, const void* Cm, const float* dtc,
                                   const float* cs, const float* D, const void* entry,
-                                  const void* gram, void* y, hipStream_t st) {
-    ScanFn f = pick_scan(s);
-    if (!f) return hipErrorInvalidValue;
+                                  const void* gram, void* y, hipStream_t st,
+                                  const GateNorm* gate) {
+    ScanFn f = gate ? pick_scan_gate(s) : pick_scan(s);
+    if (!f || (gate && !chunk_scan_gate_supported(s, gate->groups_per_head)))
+        return hipErrorInvalidValue;
     if ((size_t)s.B * s.G * s.nC == 0) return hipSuccess;
-    return f(s, x, Cm, dtc, cs, D, entry, gram, y, st);
+    return f(s, x, Cm, dtc, cs, D, entry, gram, y, st, gate);
 }
 
 }  // namespace ssd

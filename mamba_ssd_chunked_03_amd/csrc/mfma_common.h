@@ -102,6 +102,22 @@ __device__ __forceinline__ uint4 pair_runs(uint2 ra, uint2 rb) {
     return make_uint4(x[0], y[0], x[1], y[1]);
 }
 // transpose read: see the header comment
+// Sum over the four lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48), the same value in every
+// lane.  Two VALU exchanges instead of LDS-routed shuffles: v_permlane32_swap of v with
+// itself yields (lower half, upper half) in every lane, so their sum is v + (v at l ^ 32);
+// v_permlane16_swap likewise pairs the even and odd 16-lane rows.
+__device__ __forceinline__ float colsum(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    return make_uint2(v.x, v.y);
+}
 __device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
     const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) s16x4*)(p));

@@ -178,9 +178,12 @@ size_t bwd_workspace_bytes(const Shape& s, BwdWorkspace* w, char* base) {
 
 ssd_status run_chunk_scan(const Shape& s, ssd_dtype dtype, const void* x, const void* B,
                           const void* C, const float* dtc, const float* cs, const float* D,
-                          const void* entry, const void* gram, void* y, hipStream_t st) {
+                          const void* entry, const void* gram, void* y, hipStream_t st,
+                          const ssd::GateNorm* gate = nullptr) {
     if (uses_gram(s, dtype))
-        return hip_status(ssd::launch_chunk_scan_mfma(s, x, C, dtc, cs, D, entry, gram, y, st));
+        return hip_status(
+            ssd::launch_chunk_scan_mfma(s, x, C, dtc, cs, D, entry, gram, y, st, gate));
+    if (gate) return SSD_ERR_UNSUPPORTED;
     return hip_status(ssd::launch_chunk_scan_valu(s, dtype, x, B, C, dtc, cs, D, entry, y, st));
 }
 
@@ -312,7 +315,8 @@ ssd_status fwd_check(const ssd_dims* dims, ssd_dtype dtype, const void* x, const
 ssd_status fwd_run(const Shape& s, ssd_dtype dtype, const void* x, const float* dt,
                    const float* A, const void* B, const void* C, const float* D,
                    const float* init_state, void* y, float* final_state, const Workspace& ws,
-                   hipStream_t st, const ssd::DtRaw* raw = nullptr) {
+                   hipStream_t st, const ssd::DtRaw* raw = nullptr,
+                   const ssd::GateNorm* gate = nullptr) {
     ssd_status r;
     const bool has_tokens = (size_t)s.B * s.T > 0;
     if (s.B == 0) return SSD_OK;
@@ -326,7 +330,7 @@ ssd_status fwd_run(const Shape& s, ssd_dtype dtype, const void* x, const float* 
     r = hip_status(ssd::launch_state_passing(s, dtype, ws.states, ws.cs, init_state, ws.entry,
                                              final_state, st));
     if (r != SSD_OK || !has_tokens) return r;
-    return run_chunk_scan(s, dtype, x, B, C, ws.dtc, ws.cs, D, ws.entry, ws.gram, y, st);
+    return run_chunk_scan(s, dtype, x, B, C, ws.dtc, ws.cs, D, ws.entry, ws.gram, y, st, gate);
 }
 
 // ---- scratch for callers that cannot allocate ------------------------------------------
@@ -593,6 +597,21 @@ struct BlockWorkspace {
     size_t fwd_bytes;
 };
 
+// Norm groups per head where ssd_block_fwd applies the gate and the norm in the chunk scan
+// (each group S = H P / norm_groups channels inside one head, S a multiple of 16 dividing
+// P, bf16 on the matrix-core scan, 8-byte aligned projection rows), else 0.
+int norm_groups_per_head(const Shape& s, ssd_dtype dtype, int norm_groups) {
+    const int64_t d = (int64_t)s.H * s.P;
+    if (dtype != SSD_BF16 || norm_groups < 1 || d % norm_groups != 0) return 0;
+    const int64_t gsize = d / norm_groups;
+    if (gsize % 16 != 0 || s.P % gsize != 0) return 0;
+    const int gph = (int)(s.P / gsize);
+    const int64_t width = 2 * d + 2 * (int64_t)s.G * s.N + s.H;
+    if ((width * 2) % 8 != 0 || !uses_gram(s, dtype) || !ssd::chunk_scan_gate_supported(s, gph))
+        return 0;
+    return gph;
+}
+
 size_t block_workspace_bytes(const Shape& s, ssd_dtype dtype, BlockWorkspace* w, char* base) {
     const size_t e = dtype == SSD_BF16 ? 2 : 4;
     const size_t bt = (size_t)s.B * s.T;
@@ -613,6 +632,13 @@ size_t block_workspace_bytes(const Shape& s, ssd_dtype dtype, BlockWorkspace* w,
     return off;
 }
 }  // namespace
+
+int ssd_block_fwd_norm_in_scan(const ssd_dims* dims, ssd_dtype dtype, int chunk_len,
+                               int norm_groups) {
+    Shape s;
+    if (make_shape(dims, chunk_len, &s) != SSD_OK || !valid_dtype(dtype)) return 0;
+    return norm_groups_per_head(s, dtype, norm_groups) > 0 ? 1 : 0;
+}
 
 size_t ssd_block_fwd_workspace_size(const ssd_dims* dims, ssd_dtype dtype, int chunk_len) {
     Shape s;
@@ -661,6 +687,14 @@ ssd_status ssd_block_fwd(const ssd_dims* dims, ssd_dtype dtype, const void* zxbc
     r = hip_status(ssd::launch_block_prologue(s, dtype, pa, st));
     if (r != SSD_OK) return r;
     const ssd::DtRaw raw{zx + (2 * d + 2 * gn) * e, width, dt_bias, dtype};
+    // norm groups inside a head: the gate and the norm in the chunk scan's store, which
+    // writes `out` (y is never stored and no epilogue pass runs)
+    const int gph = norm_groups_per_head(s, dtype, norm_groups);
+    if (gph > 0 && !any_misaligned({norm_w, norm_b})) {
+        const ssd::GateNorm gate{zxbcdt, width, norm_w, norm_b, gph, rms, eps};
+        return fwd_run(s, dtype, ws.x, nullptr, A, ws.B, ws.C, D, init_state, out, final_state,
+                       fws, st, &raw, &gate);
+    }
     r = fwd_run(s, dtype, ws.x, nullptr, A, ws.B, ws.C, D, init_state, ws.y, final_state, fws, st,
                 &raw);
     if (r != SSD_OK) return r;

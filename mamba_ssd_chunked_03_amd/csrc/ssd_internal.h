@@ -121,6 +121,19 @@ hipError_t launch_chunk_state_mfma(const Shape& s, const void* x, const void* Bm
                                    const float* dtc, const float* cs, void* states,
                                    const void* Cm, void* gram, hipStream_t st);
 bool chunk_scan_mfma_supported(const Shape& s);
+// The block's gate and normalisation applied in the chunk scan's store, where every norm
+// group lies inside one head (S = H P / norm_groups channels, S a multiple of 16 dividing P):
+// out = norm(y * SiLU(z)) over each group of a token's channels, written where y would be.
+struct GateNorm {
+    const void* z;        // rows of z in the input dtype, z_stride elements apart
+    long long z_stride;
+    const float* w;       // [H P], 16-byte aligned
+    const float* b;       // [H P] or null (unused with rms), 16-byte aligned
+    int groups_per_head;  // P / S
+    int rms;
+    float eps;
+};
+bool chunk_scan_gate_supported(const Shape& s, int groups_per_head);
 // one recurrent step for every (b, h): state [B][H][N][P] fp32 in place; x, y [B][H][P] and
 // B, C [B][G][N] in dtype (Shape's T and Q are not used)
 hipError_t launch_decode_step(const Shape& s, ssd_dtype dtype, const void* x, const float* dt,
@@ -132,7 +145,8 @@ hipError_t launch_chunk_gram(const Shape& s, const void* Bm, const void* Cm, voi
                              hipStream_t st);
 hipError_t launch_chunk_scan_mfma(const Shape& s, const void* x, const void* Cm, const float* dtc,
                                   const float* cs, const float* D, const void* entry,
-                                  const void* gram, void* y, hipStream_t st);
+                                  const void* gram, void* y, hipStream_t st,
+                                  const GateNorm* gate = nullptr);
 
 // ---- backward ------------------------------------------------------------------------
 // The gradient of every chunk's entry state through that chunk's own outputs,

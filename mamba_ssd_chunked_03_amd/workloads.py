@@ -185,10 +185,12 @@ class BlockCfg:
 
 
 # Model-shaped blocks: the layer shapes above with a width-4 convolution and one
-# normalisation group over the H*P channels of a token.
+# normalisation group over the H*P channels of a token; and the 2.7B shape with one group
+# per head (the group inside a head: the gate and the norm run in the chunk scan's store).
 BLOCKS = {
     "block_2p7b": (MAMBA2_2P7B, BlockCfg()),
     "block_130m": (MAMBA2_130M, BlockCfg()),
+    "block_2p7b_headnorm": (MAMBA2_2P7B, BlockCfg(norm_groups=80)),
 }
 
 

@@ -329,3 +329,26 @@ def test_bwd_saved_needs_the_forward_workspace(lib):
     assert lib.ssd_bwd_saved(ctypes.byref(D()), 1, *ok, 64, None, ctypes.c_void_p(256), None,
                              ctypes.c_void_p(264), *[ctypes.c_void_p(256)] * 7,
                              ctypes.c_void_p(256), 1 << 30, None) == 4
+
+
+def test_block_norm_in_scan_query(lib):
+    """ssd_block_fwd_norm_in_scan: the gate and the norm run in the chunk scan exactly where
+    every norm group lies inside one head (S = H P / norm_groups a multiple of 16 dividing
+    P), in bf16, at head sizes 32 and 64; answered from the sizes alone (no GPU here)."""
+    q = binding.ssd_block_fwd_norm_in_scan
+    bf, f32 = binding.SSD_BF16, binding.SSD_F32
+    d = D(4, 4096, 80, 64, 128, 1)
+    assert q(d, bf, 256, 80)            # S = 64 = P: one group per head
+    assert q(d, bf, 256, 160)           # S = 32: two per head
+    assert q(d, bf, 256, 320)           # S = 16: four per head
+    assert not q(d, bf, 256, 640)       # S = 8: below a 16-channel p-tile
+    assert not q(d, bf, 256, 1)         # one group over all heads (the model default)
+    assert not q(d, bf, 256, 40)        # S = 128: a group spans two heads
+    assert not q(d, bf, 256, 3)         # does not divide H P
+    assert not q(d, f32, 256, 80)       # fp32 takes the VALU scan
+    assert q(D(2, 200, 4, 32, 128, 1), bf, 64, 8)       # P = 32, S = 16
+    assert not q(D(2, 200, 4, 16, 128, 1), bf, 64, 4)   # P = 16 has no gated scan
+    assert not q(D(1, 256, 3, 64, 16, 1), bf, 64, 3)    # rows of 2*192 + 32 + 3 bf16: not 8 B
+    assert not q(D(h=3, g=2), bf, 64, 3)                # invalid sizes
+    assert not q(d, bf, 100, 80)                        # unsupported chunk length
+    assert not q(d, 9, 256, 80)                         # unknown dtype

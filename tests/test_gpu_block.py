@@ -218,6 +218,52 @@ def test_block_fwd_equals_its_three_calls(w, cfg):
     assert torch.equal(out, o2) and torch.equal(fin, f2)
 
 
+# Norm groups inside one head (S = H P / norm_groups a multiple of 16 dividing P): the gate
+# and the norm run in the chunk scan's store, which writes the block output (y is never
+# stored).  One, two and four groups per head, GroupNorm and RMS, head sizes 64 and 32,
+# ragged lengths, init on and off.
+LN_ = np.log
+FUSED_CASES = [
+    (Workload("blk_fused_g1", 2, 300 + 77, 8, 64, 128, 2, 128, init_state=True,
+              log_neg_a_range=(LN_(0.005), LN_(0.05))), BlockCfg(conv_k=4, norm_groups=8)),
+    (Workload("blk_fused_g2_rms", 1, 500, 4, 64, 64, 1, 256),
+     BlockCfg(conv_k=4, norm_groups=8, rms=True)),
+    (Workload("blk_fused_g4", 1, 256 + 31, 4, 64, 128, 1, 256, init_state=True),
+     BlockCfg(conv_k=3, norm_groups=16)),
+    (Workload("blk_fused_p32_g2", 2, 200, 4, 32, 128, 1, 64, init_state=True,
+              log_neg_a_range=(LN_(0.01), LN_(0.1))), BlockCfg(conv_k=2, norm_groups=8)),
+]
+
+
+@pytest.mark.parametrize("w,cfg", FUSED_CASES, ids=[c[0].name for c in FUSED_CASES])
+def test_block_with_norm_groups_inside_a_head(w, cfg):
+    """The fused gate and norm against the oracle's block (the bf16 bar, whole tensor and per
+    (b, h)), and against the same block made by the three unfused calls (prologue, ssd_fwd,
+    epilogue), which differ only by the rounding of y to bf16 before the norm."""
+    say(f"[block fused norm] {w.describe()} {cfg}")
+    cpu = generate_block(w, cfg)
+    out, fin = _run_block(w, cfg, cpu)
+    ref_out, ref_fin = _oracle_block(w, cfg, cpu)
+    _check("out", out, ref_out, w.dtype)
+    _check("final_state", fin, ref_fin, w.dtype)
+    _check_per_head(w, out, ref_out, fin, ref_fin)
+    d = {k: (None if v is None else v.to("cuda")) for k, v in cpu.items()}
+    H, P, N, G = w.nheads, w.headdim, w.dstate, w.ngroups
+    hp, gn = H * P, G * N
+    zx = d["zxbcdt"]
+    pro = binding.ssd_block_prologue(zx[:, :, hp:2 * hp + 2 * gn], d["conv_w"], d["conv_b"],
+                                     zx[:, :, 2 * hp + 2 * gn:], d["dt_bias"], H, P, N, G)
+    y, f2 = binding.ssd_fwd(pro["x"], pro["dt"], d["A"], pro["B"], pro["C"], d["D"],
+                            w.chunk_len, init_state=d["init_state"])
+    o2 = binding.ssd_block_epilogue(y, zx[:, :, :hp], d["norm_w"], d["norm_b"], cfg.norm_groups,
+                                    rms=cfg.rms, eps=cfg.eps, dstate=N, ngroups=G)
+    torch.cuda.synchronize()
+    assert torch.equal(fin, f2)
+    e = rel_l2(np64(out), np64(o2))
+    say(f"    fused against three calls: rel_l2 {e:.3e}")
+    assert e <= 1e-2
+
+
 def test_block_empty_sequence():
     """T = 0: nothing to compute; final_state = init_state."""
     w = Workload("blk_empty", 2, 0, 4, 32, 16, 1, 64, init_state=True)
