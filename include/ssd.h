@@ -371,8 +371,8 @@ size_t ssd_block_fwd_workspace_size(const ssd_dims* dims, ssd_dtype dtype, int c
 /* 1 if ssd_block_fwd applies the gate and the norm inside the chunk scan for these sizes
  * (bf16 on the matrix-core scan, headdim 32 or 64, every norm group inside one head: S =
  * H*P / norm_groups channels, S a multiple of 16 that divides P, and 8-byte aligned
- * projection rows), given 16-byte aligned norm_w and norm_b; 0 otherwise, also for invalid
- * sizes.  Reads no device state. */
+ * projection rows of which chunk_len span under 2^31 bytes), given 16-byte aligned norm_w
+ * and norm_b; 0 otherwise, also for invalid sizes.  Reads no device state. */
 int ssd_block_fwd_norm_in_scan(const ssd_dims* dims, ssd_dtype dtype, int chunk_len,
                                int norm_groups);
 

@@ -607,7 +607,9 @@ int norm_groups_per_head(const Shape& s, ssd_dtype dtype, int norm_groups) {
     if (gsize % 16 != 0 || s.P % gsize != 0) return 0;
     const int gph = (int)(s.P / gsize);
     const int64_t width = 2 * d + 2 * (int64_t)s.G * s.N + s.H;
-    if ((width * 2) % 8 != 0 || !uses_gram(s, dtype) || !ssd::chunk_scan_gate_supported(s, gph))
+    // the scan addresses a chunk of z rows with 32-bit byte offsets
+    if ((width * 2) % 8 != 0 || (int64_t)s.Q * width * 2 >= ((int64_t)1 << 31) ||
+        !uses_gram(s, dtype) || !ssd::chunk_scan_gate_supported(s, gph))
         return 0;
     return gph;
 }

@@ -352,3 +352,6 @@ def test_block_norm_in_scan_query(lib):
     assert not q(D(h=3, g=2), bf, 64, 3)                # invalid sizes
     assert not q(d, bf, 100, 80)                        # unsupported chunk length
     assert not q(d, 9, 256, 80)                         # unknown dtype
+    # 64 rows of z span 2^31 bytes or more: the scan's 32-bit offsets would not reach them
+    big = D(1, 64, 1 << 17, 64, 128, 1)                 # H P = 2^23: rows of over 2^25 bytes
+    assert not q(big, bf, 64, 1 << 17)
