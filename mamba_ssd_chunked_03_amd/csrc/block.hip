@@ -435,7 +435,9 @@ hipError_t launch_block_epilogue(const Shape& s, ssd_dtype dtype, const BlockEpi
     if ((long long)s.B * s.T == 0) return hipSuccess;
     const int V = dtype == SSD_BF16 ? 8 : 4;
     const int gs = s.H * s.P / a.groups;
-    const bool vec = aligned16p(a.z) && a.z_stride % V == 0 && gs % V == 0;
+    // the vector path reads z, and the norm parameters, as 16-byte runs
+    const bool vec = aligned16p(a.z) && a.z_stride % V == 0 && gs % V == 0 &&
+                     aligned16p(a.norm_w) && (a.norm_b == nullptr || aligned16p(a.norm_b));
     if (dtype == SSD_BF16)
         return vec ? launch_epilogue_v<__bf16, 8>(s, a, st) : launch_epilogue_v<__bf16, 1>(s, a, st);
     return vec ? launch_epilogue_v<float, 4>(s, a, st) : launch_epilogue_v<float, 1>(s, a, st);

@@ -264,6 +264,46 @@ def test_block_with_norm_groups_inside_a_head(w, cfg):
     assert e <= 1e-2
 
 
+def test_block_with_unaligned_norm_params():
+    """Norm parameters 4 bytes past a 16-byte boundary (the ABI asks only for 4-byte
+    alignment): the fused store and the epilogue's vector path both need 16-byte runs, so
+    ssd_block_fwd takes the epilogue pass, and the epilogue its element-wise variant.  The
+    block must equal the three calls bit for bit and the three calls with aligned
+    parameters within the bf16 bar, on sizes that would otherwise take the fused path."""
+    w, cfg = FUSED_CASES[0]
+    say(f"[block unaligned norm params] {w.describe()} {cfg}")
+    d_ = binding.SsdDims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups)
+    assert binding.ssd_block_fwd_norm_in_scan(d_, binding.SSD_BF16, w.chunk_len, cfg.norm_groups)
+    cpu = generate_block(w, cfg)
+    d = {k: (None if v is None else v.to("cuda")) for k, v in cpu.items()}
+    H, P, N, G = w.nheads, w.headdim, w.dstate, w.ngroups
+    hp, gn = H * P, G * N
+    wbuf = torch.zeros(hp + 1, device="cuda")
+    bbuf = torch.zeros(hp + 1, device="cuda")
+    wbuf[1:].copy_(d["norm_w"])
+    bbuf[1:].copy_(d["norm_b"])
+    nw, nb = wbuf[1:], bbuf[1:]
+    assert nw.data_ptr() % 16 == 4 and nb.data_ptr() % 16 == 4
+    out, fin = binding.ssd_block_fwd(d["zxbcdt"], d["conv_w"], d["conv_b"], d["dt_bias"],
+                                     d["A"], d["D"], w.chunk_len, nw, nb, cfg.norm_groups,
+                                     P, N, G, rms=cfg.rms, eps=cfg.eps,
+                                     init_state=d["init_state"])
+    zx = d["zxbcdt"]
+    pro = binding.ssd_block_prologue(zx[:, :, hp:2 * hp + 2 * gn], d["conv_w"], d["conv_b"],
+                                     zx[:, :, 2 * hp + 2 * gn:], d["dt_bias"], H, P, N, G)
+    y, f2 = binding.ssd_fwd(pro["x"], pro["dt"], d["A"], pro["B"], pro["C"], d["D"],
+                            w.chunk_len, init_state=d["init_state"])
+    o2 = binding.ssd_block_epilogue(y, zx[:, :, :hp], nw, nb, cfg.norm_groups, rms=cfg.rms,
+                                    eps=cfg.eps, dstate=N, ngroups=G)
+    o3 = binding.ssd_block_epilogue(y, zx[:, :, :hp], d["norm_w"], d["norm_b"], cfg.norm_groups,
+                                    rms=cfg.rms, eps=cfg.eps, dstate=N, ngroups=G)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2) and torch.equal(fin, f2)
+    e = rel_l2(np64(o2), np64(o3))
+    say(f"    element-wise against vector epilogue: rel_l2 {e:.3e}")
+    assert e <= TOL["bf16"]
+
+
 def test_block_empty_sequence():
     """T = 0: nothing to compute; final_state = init_state."""
     w = Workload("blk_empty", 2, 0, 4, 32, 16, 1, 64, init_state=True)
